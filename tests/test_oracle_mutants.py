@@ -1,0 +1,71 @@
+"""Each plausible mistake planted in a copy of the oracle is caught by a pin.
+
+The mistakes are planted on the CPU only, in a temporary copy of oracle.cpp
+built into its own library; the real oracle is untouched.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import oracle.build as ob
+from tests import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.cpp")
+
+# (name, text in oracle.cpp, replacement)
+MUTANTS = [
+    ("drop_rank_1", "for (int32_t r = 1; r < N; ++r)", "for (int32_t r = 2; r < N; ++r)"),
+    ("inclusive_bound_divisor", "return s / (float)N;", "return s / (float)(N + 1);"),
+    ("sum_not_averaged", "return s / (float)N;", "return s;"),
+    ("reverse_rank_order", "s = s + widen(G[r][i]);", "s = s + widen(G[N - r][i]);"),
+    ("wrong_index", "s = s + widen(G[r][i]);", "s = s + widen(G[r][i > 0 ? i - 1 : i]);"),
+    ("swap_beta1_terms", "f.b1 * M[i] + f.c1 * g", "f.c1 * M[i] + f.b1 * g"),
+    ("v_uses_g_not_g2", "f.c2 * (g * g)", "f.c2 * g"),
+    ("v_from_m", "f.b2 * V[i]", "f.b2 * M[i]"),
+    ("eps_inside_sqrt", "std::sqrt(v1) * f.rb + f.e", "std::sqrt(v1 + f.e) * f.rb"),
+    ("rb_not_applied", "std::sqrt(v1) * f.rb + f.e", "std::sqrt(v1) + f.e"),
+    ("multiply_not_divide", "float u = m1 / d;", "float u = m1 * d;"),
+    ("ascent_sign", "f.dk * P[i] - f.ss * u", "f.dk * P[i] + f.ss * u"),
+    ("decay_on_update", "f.dk * P[i] - f.ss * u", "P[i] - f.ss * u * f.dk"),
+    ("bias1_off_by_one", "std::pow(hp.beta1, (double)t)", "std::pow(hp.beta1, (double)(t + 1))"),
+    ("no_bias1", "f.ss = (float)(hp.lr / (1.0 - std::pow(hp.beta1, (double)t)));", "f.ss = (float)hp.lr;"),
+    ("bias2_uses_beta1", "std::pow(hp.beta2, (double)t)", "std::pow(hp.beta1, (double)t)"),
+    ("decay_not_lr_scaled", "(1.0 - hp.lr * hp.weight_decay)", "(1.0 - hp.weight_decay)"),
+    ("fold_in_fp32", "f.c1 = (float)(1.0 - hp.beta1);", "f.c1 = 1.0f - (float)hp.beta1;"),
+    ("bf16_truncates", "return (uint16_t)((u + 0x7FFFu + lsb) >> 16);", "return (uint16_t)(u >> 16);"),
+    ("bf16_ties_up", "return (uint16_t)((u + 0x7FFFu + lsb) >> 16);", "return (uint16_t)((u + 0x8000u) >> 16);"),
+    ("bf16_nan_to_inf", "return 0x7FC0;  // NaN", "return (uint16_t)(u >> 16) & 0xFF80;  // NaN"),
+    ("copy_from_wrong_value", "B[i] = to_bf16(p1);", "B[i] = to_bf16(m1);"),
+    ("state_bytes_fp32_grad", "return 4 + 2 + 2 + 4 + 4;", "return 4 + 2 + 4 + 4 + 4;"),
+]
+
+
+def test_mutations_apply_once():
+    src = open(SRC, encoding="utf-8").read()
+    for name, old, _new in MUTANTS:
+        assert src.count(old) >= 1, f"mutant {name}: text not found in oracle.cpp"
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    src = open(SRC, encoding="utf-8").read()
+    mutated = src.replace(old, new)
+    assert mutated != src
+    with tempfile.TemporaryDirectory() as d:
+        cpp = os.path.join(d, "oracle_mutant.cpp")
+        with open(cpp, "w", encoding="utf-8") as f:
+            f.write(mutated)
+        lib = ob.build(src=cpp, out=os.path.join(d, "liboracle_mutant.so"))
+        o = oracle.Oracle(lib)
+        caught = []
+        for pin in pins.ALL:
+            try:
+                pin(o)
+            except AssertionError as e:
+                caught.append(f"{pin.__name__}: {str(e)[:80]}")
+            except (ValueError, FloatingPointError, ZeroDivisionError) as e:
+                caught.append(f"{pin.__name__}: {type(e).__name__}")
+        assert caught, f"mutant {name} passed every pin"

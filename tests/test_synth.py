@@ -1,0 +1,59 @@
+"""The seeded input generator: counter-based, position-addressable, right moments."""
+import numpy as np
+
+import synth
+from synth import workloads as W
+
+
+def test_slices_and_gathers_agree():
+    k = synth.key(0, synth.KIND_P)
+    full = synth.normal_f32(k, 0, 10_000, 0.02)
+    assert np.array_equal(full[4321:], synth.normal_f32(k, 4321, 10_000 - 4321, 0.02))
+    idx = np.array([0, 17, 9999, 5000, 5000], dtype=np.int64)
+    assert np.array_equal(synth.normal_f32_at(k, idx, 0.02), full[idx])
+    kg = synth.key(0, synth.KIND_GRAD, 3)
+    km = synth.key(0, synth.KIND_MASK)
+    th = synth.mask_threshold(0.01)
+    gb = synth.normal_bf16(kg, 0, 10_000, 1e-3, km, th)
+    assert np.array_equal(synth.normal_bf16_at(kg, idx, 1e-3, km, th), gb[idx])
+
+
+def test_streams_differ_and_repeat():
+    a = synth.normal_f32(synth.key(0, synth.KIND_GRAD, 0), 0, 1000, 1.0)
+    b = synth.normal_f32(synth.key(0, synth.KIND_GRAD, 1), 0, 1000, 1.0)
+    c = synth.normal_f32(synth.key(1, synth.KIND_GRAD, 0), 0, 1000, 1.0)
+    assert not np.array_equal(a, b) and not np.array_equal(a, c)
+    assert np.array_equal(a, synth.normal_f32(synth.key(0, synth.KIND_GRAD, 0), 0, 1000, 1.0))
+
+
+def test_moments():
+    x = synth.normal_f32(synth.key(7, synth.KIND_P), 0, 4_000_000, 0.02).astype(np.float64)
+    assert abs(x.mean()) < 1e-4 and abs(x.std() / 0.02 - 1) < 3e-3
+    assert np.max(np.abs(x)) <= 6 * 0.02 * (1 + 1e-6)
+    v = synth.normal_f32(synth.key(7, synth.KIND_V), 0, 1_000_000, 1e-6, absval=True)
+    assert np.all(v >= 0)
+    g = synth.normal_bf16(synth.key(7, synth.KIND_GRAD), 0, 2_000_000, 1e-3,
+                          synth.key(7, synth.KIND_MASK), synth.mask_threshold(0.001))
+    zero = np.mean(g == 0)
+    assert 0.0008 < zero < 0.0012
+    gf = (g.astype(np.uint32) << 16).view(np.float32)
+    assert abs(gf.std() / 1e-3 - 1) < 5e-3
+
+
+def test_workload_sizes():
+    c3 = W.C3()
+    assert len(c3.sizes) == 288 and c3.n_params == 809_533_440
+    c5 = W.C5()
+    assert len(c5.sizes) == 20_000 and min(c5.sizes) >= 64 and max(c5.sizes) <= 1 << 20
+    assert 2.0e9 < c5.n_params < 2.3e9       # log-uniform 64..2^20 has mean ~108k
+    offs, L = c5.layout()
+    assert np.all(offs % 8 == 0) and L >= c5.n_params
+    assert W.C4.n_params == 70_000_000_000 // 64
+
+
+def test_host_inputs_at_matches_slices():
+    w = W.C1.with_(warm=True, zero_frac=0.01)
+    a = W.host_inputs(w, 100, 300)
+    b = W.host_inputs_at(w, np.arange(100, 300))
+    for k in "GPMV":
+        assert np.array_equal(a[k], b[k])
