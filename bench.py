@@ -1,0 +1,238 @@
+"""Benchmark: one ZeRO rank's fused reduce + AdamW + bf16 re-cast step on one GPU.
+
+A step is one call of the library on the whole workload (default: the
+70B-parameter model's 1/64 shard, 1,093,750,000 parameters, 64 replica
+gradient chunks, warm state at step 5000, weight decay 0.1).  Inputs are
+seeded synthetic draws generated in device memory before timing.
+
+Prints one JSON line.  `value` is parameters updated per second; the roofline
+object prices the kernel's algorithmic bytes, (2N + 26) per parameter, against
+MI355X's 8 TB/s HBM peak.  The CPU oracle's throughput on a bounded sample of
+the same workload is reported beside it as `cpu_baseline`.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "params/s and achieved HBM GB/s (% of peak) for fused reduce+Adam shard step"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "sharded_mixed_precision_rank_amd", "csrc", "zs_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def workload(name: str):
+    from synth import workloads as W
+
+    return {"c1": W.C1, "c2": W.C2, "c3": W.C3(), "c4": W.C4, "c5": W.C5(1), "c5w": W.C5(10000)}[name]
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(w, n_launch_params: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary for
+    this workload, if it was taken on the current kernel source; else None."""
+    tag = w.name.replace("/", "-")
+    path = os.path.join(PROFILES, f"zs_kernel_{tag}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path, encoding="utf-8").read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def spot_check(w, d, samples: int, seed: int = 1234) -> dict:
+    """Sampled parity: outputs of the first step at random positions (plus both
+    ends) against the CPU oracle on the host-drawn inputs at those positions."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from synth import workloads as W
+    from tests import parity
+
+    L = d["arena_len"]
+    rng = np.random.default_rng(seed)
+    idx = np.unique(np.concatenate([rng.integers(0, L, samples), np.arange(min(L, 4096)),
+                                    np.arange(max(0, L - 4096), L)]))
+    if w.is_list:  # keep positions inside tensors; gaps are checked by the tests
+        offs, _ = w.layout()
+        sizes = np.asarray(w.sizes)
+        t = np.searchsorted(offs, idx, side="right") - 1
+        idx = idx[(t >= 0) & (idx < offs[np.maximum(t, 0)] + sizes[np.maximum(t, 0)])]
+    it = torch.from_numpy(idx).to(d["P"].device)
+    got = dict(P=d["P"][it].cpu().numpy(), M=d["M"][it].cpu().numpy(), V=d["V"][it].cpu().numpy(),
+               B=d["B"].view(torch.int16)[it].cpu().numpy().view(np.uint16))
+    h = W.host_inputs_at(w, idx)
+    P, M, V, B = oracle.load().step(h["G"], h["P"], h["M"], h["V"], w.hp(), w.step)
+    rep = parity.assert_step(got, dict(P=P, M=M, V=V, B=B), f"{w.name} sampled")
+    return dict(samples=int(idx.size), bit_identical=parity.bit_identical(got, dict(P=P, M=M, V=V, B=B)),
+                max_rel=max(rep[k]["max_rel"] for k in "PMV"), max_bf16_ulp=rep["B"]["max_ulp"])
+
+
+def copy_ceiling(gbytes: float = 8.0, reps: int = 5) -> float:
+    """Read+write GB/s of a plain 16-byte-per-lane copy kernel over `gbytes`."""
+    import torch
+
+    import synth
+
+    n = int(gbytes * 1e9) // 16 * 4
+    src = torch.empty(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    synth.dev_copy16(src, dst, blocks=256 * 8)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        synth.dev_copy16(src, dst, blocks=256 * 8)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / t / 1e9
+
+
+def cpu_baseline(w, target_s: float) -> dict:
+    """The CPU oracle, as it stands, timed on this host's cores over a bounded
+    slice of the workload (the first `n` parameters), repeated until about
+    `target_s` seconds of compute have run."""
+    import numpy as np
+
+    import oracle
+    from synth import workloads as W
+
+    cores = len(os.sched_getaffinity(0))
+    threads = min(cores, 16)
+    n = 2_000_000 if w.N >= 32 else 8_000_000
+    h = W.host_inputs(w, 0, n)
+    o = oracle.load()
+    P, M, V = h["P"].copy(), h["M"].copy(), h["V"].copy()
+    B = np.empty(n, dtype=np.uint16)
+    reps, spent = 0, 0.0
+    while spent < target_s or reps == 0:
+        t0 = time.perf_counter()
+        o.step_inplace(h["G"], P, M, V, B, w.hp(), w.step + reps, threads=threads)
+        spent += time.perf_counter() - t0
+        reps += 1
+    pps = n * reps / spent
+    return dict(value=pps, unit="params/s", cores=threads, kind="oracle",
+                gbps=pps * (2 * w.N + 26) / 1e9,
+                sample=f"first {n} params of {w.name} (N={w.N}), {reps} oracle steps in {spent:.1f} s on "
+                       f"{threads} threads of {cores} cores")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "c5w"])
+    ap.add_argument("--samples", type=int, default=200_000, help="sampled parity positions (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 = skip)")
+    ap.add_argument("--no-copy", action="store_true", help="skip the copy-kernel ceiling")
+    ap.add_argument("--blocks", type=int, default=0, help="workgroups per launch (0 = library default)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build runs one rank's shard step on a single MI355X and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import sharded_mixed_precision_rank_amd as zs
+    from synth import workloads as W
+
+    w = workload(args.workload)
+    zs.set_grid_blocks(args.blocks)
+    log(f"workload {w.name}: {w.n_params} params, N={w.N}, step={w.step}, wd={w.weight_decay}")
+    t0 = time.perf_counter()
+    d = W.device_inputs(w)
+    torch.cuda.synchronize()
+    log(f"inputs drawn in device memory in {time.perf_counter() - t0:.1f} s "
+        f"({torch.cuda.memory_allocated() / 1e9:.1f} GB)")
+
+    plan = None
+    if w.is_list:
+        offs, _ = w.layout()
+        plan = zs.ListPlan.from_arenas(w.sizes, offs, d["G"], d["P"], d["M"], d["V"], d["B"])
+
+    def step(t):
+        if plan is not None:
+            plan.step(w.hp(), t)
+        else:
+            zs.reduce_adam_flat(d["G"], d["P"], d["M"], d["V"], d["B"], w.hp(), t)
+
+    step(w.step)
+    torch.cuda.synchronize()
+    check = None
+    if args.samples > 0:
+        check = spot_check(w, d, args.samples)
+        log(f"sampled parity vs oracle: {check}")
+
+    for k in range(args.warmup):
+        step(w.step + 1 + k)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(args.steps):
+        step(w.step + 1 + args.warmup + k)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    n = w.n_params
+    bytes_per_launch = (2 * w.N + 26) * n
+    achieved = bytes_per_launch / (ms / 1e3) / 1e9
+    log(f"{ms:.3f} ms/step, {n / (ms / 1e3) / 1e9:.2f} G params/s, {achieved:.0f} GB/s")
+
+    del d, plan
+    torch.cuda.empty_cache()
+    ceiling = None if args.no_copy else copy_ceiling()
+    if ceiling:
+        log(f"copy-kernel ceiling {ceiling:.0f} GB/s")
+    traffic = counter_traffic(w, n)
+    base = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    if base:
+        log(f"cpu baseline {base['value'] / 1e6:.1f} M params/s ({base['sample']})")
+
+    rec = {
+        "metric": METRIC, "value": n / (ms / 1e3), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "n_params": n, "replicas": w.N, "adam_step": w.step,
+                   "weight_decay": w.weight_decay, "storage": "bf16 grads and working copy, fp32 master/m/v"},
+        "hbm_GBps": achieved, "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,
+        "copy_ceiling_GBps": ceiling,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "bytes_per_param": 2 * w.N + 26, "kernel": ("list_kernel" if w.is_list else "flat_kernel") + (
+                         f"<{w.N}>" if w.N in (1, 2, 4, 8, 16, 32, 64) else "<0>")},
+        "cpu_baseline": base,
+        "parity_sample": check,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

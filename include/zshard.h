@@ -1,0 +1,175 @@
+/*
+ * libzshard — one ZeRO rank's optimizer-side step on one MI355X (gfx950) GPU.
+ *
+ * The step, per parameter of the rank's shard (all arithmetic IEEE binary32,
+ * round to nearest even, one rounding per operation, no fused multiply-add, in
+ * exactly this order):
+ *
+ *   reduce   s = G_0[i]; s = s + G_r[i] for r = 1..N-1;  g = s / N
+ *            The reduce half of the gradient reduce-scatter: the rank keeps the
+ *            average of the N data-parallel replicas' gradients for the
+ *            parameters it owns ("Почему training 70B модели требует optimizer
+ *            sharding (ZeRO-3)?", §5, ZeRO-3 step algorithm, steps 2-3; the
+ *            average is the gradient-synchronisation equation of "Data
+ *            Parallelism 数据并行（二）", section 数据并行训练（DP）, read as N
+ *            terms).  Floating-point addition is not associative (same
+ *            section), so the order is fixed: rank 0 first, up to N-1.
+ *   update   m1 = b1*M + c1*g;  v1 = b2*V + c2*(g*g);  d = sqrt(v1)*rb + e
+ *            p1 = dk*P - ss*(m1/d)
+ *            Mixed-precision AdamW on the 16-byte-per-parameter state of the
+ *            Data Parallelism page's appendix (fp32 master, fp32 momentum, fp32
+ *            variance, bf16 working copy, bf16 gradient).  The pages print no
+ *            update equations: these are Kingma & Ba's Adam (Algorithm 1,
+ *            bias-corrected, eps after the square root) with Loshchilov &
+ *            Hutter's decoupled weight decay scaled by lr.  Scalars are folded
+ *            on the host in double and rounded once to fp32:
+ *              b1 = beta1, c1 = 1-beta1, b2 = beta2, c2 = 1-beta2, e = eps,
+ *              ss = lr/(1-beta1^t), rb = 1/sqrt(1-beta2^t), dk = 1-lr*weight_decay
+ *   re-cast  B = bf16_rne(p1): the working copy the next parameter all-gather
+ *            ships (ZeRO-3 page, §5).  NaN stays NaN (payload unspecified).
+ *
+ * Non-finite gradients propagate (no skipping, no clipping).
+ *
+ * Memory: every buffer is caller-owned device memory.  The library allocates
+ * device memory only for list-plan tables.  Host arrays passed in (grad_chunks,
+ * tensors) are read during the call and may be freed when it returns.
+ *
+ * Asynchrony: the step calls enqueue one kernel on `stream` and return; the
+ * caller keeps the buffers alive until the stream reaches the work.  Faults
+ * during execution surface at the caller's next synchronisation.  Setting the
+ * environment variable ZS_SYNC=1 makes every step call synchronise the stream
+ * and report kernel errors itself.
+ *
+ * Errors: arguments are checked before anything is enqueued; on failure nothing
+ * is launched, a status is returned and zs_last_error() gives a thread-local
+ * description.  No C++ exception crosses this interface.
+ */
+#ifndef ZSHARD_H
+#define ZSHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define ZS_API __attribute__((visibility("default")))
+#else
+#define ZS_API
+#endif
+
+#define ZS_ABI_VERSION 1
+/* Largest replica count N one call accepts (the N chunk pointers travel as
+   kernel arguments). */
+#define ZS_MAX_REPLICAS 256
+
+/* A hipStream_t, passed as an opaque pointer; NULL is the null stream. */
+typedef void* zs_stream;
+
+/* Adam/AdamW hyperparameters, as doubles.  Valid: all finite, lr >= 0,
+   0 <= beta1 < 1, 0 <= beta2 < 1, eps > 0, weight_decay >= 0 (decoupled,
+   applied as p *= 1 - lr*weight_decay). */
+typedef struct zs_adam_hp {
+  double lr, beta1, beta2, eps, weight_decay;
+} zs_adam_hp;
+
+typedef enum zs_status {
+  ZS_OK = 0,
+  ZS_ERR_NULL = 1,  /* a required pointer is NULL */
+  ZS_ERR_RANGE = 2, /* N, n, T, step or a hyperparameter out of range */
+  ZS_ERR_ALIAS = 3, /* an output overlaps another output or a gradient */
+  ZS_ERR_ALIGN = 4, /* a pointer is not naturally aligned (4 B fp32, 2 B bf16) */
+  ZS_ERR_HIP = 5,   /* the HIP runtime reported an error */
+  ZS_ERR_NOMEM = 6  /* a plan table could not be allocated */
+} zs_status;
+
+/* The fp32 scalars one step uses, as folded on the host. */
+typedef struct zs_folded {
+  float b1, c1, b2, c2, eps, ss, rb, dk;
+} zs_folded;
+
+/* ABI version of the loaded library (ZS_ABI_VERSION it was built with). */
+ZS_API int zs_abi_version(void);
+
+/* Static name of a status value. */
+ZS_API const char* zs_status_string(int status);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+ZS_API const char* zs_last_error(void);
+
+/* Folds the step's scalars exactly as the step calls do (host only, no GPU).
+   step is the 1-based index of the update.  Errors: ZS_ERR_NULL, ZS_ERR_RANGE. */
+ZS_API zs_status zs_fold(const zs_adam_hp* hp, int64_t step, zs_folded* out);
+
+/* The step on one flat shard of n parameters.
+     grad_chunks  host array of N device pointers; grad_chunks[r] holds replica
+                  r's n bf16 gradients (raw bf16 bits).  Read only; the same
+                  pointer may appear more than once.
+     N            replicas, 1..ZS_MAX_REPLICAS
+     n            parameters in the shard, >= 0 (0 is a no-op)
+     master, m, v device fp32 arrays of n, updated in place
+     param_bf16   device bf16 array of n, written (never read)
+     hp, step     hyperparameters; step >= 1 is the 1-based index of this
+                  update (the library keeps no state and never increments it)
+     stream       the stream the kernel is enqueued on
+   Layout: any natural alignment works; when every array can be brought to
+   16-byte alignment by the same element offset, the kernel uses 16-byte
+   vector accesses for all but at most 14 elements.
+   Errors: ZS_ERR_NULL, ZS_ERR_RANGE, ZS_ERR_ALIGN, ZS_ERR_ALIAS (outputs must
+   be pairwise disjoint and disjoint from every gradient range), ZS_ERR_HIP. */
+ZS_API zs_status zs_reduce_adam_flat(const uint16_t* const* grad_chunks, int32_t N, int64_t n, float* master,
+                                     float* m, float* v, uint16_t* param_bf16, const zs_adam_hp* hp, int64_t step,
+                                     zs_stream stream);
+
+/* One tensor of a ragged per-layer list (the per-layer parameter lists a
+   model's layers hand to the gradient hooks and the optimizer, "Data
+   Parallelism 数据并行（二）", section on integrating data parallelism into
+   backpropagation).  Same meaning as the flat call's arguments. */
+typedef struct zs_tensor {
+  int64_t n;
+  float* master;
+  float* m;
+  float* v;
+  uint16_t* param_bf16;
+  const uint16_t* const* grad_chunks; /* host array of N device pointers */
+} zs_tensor;
+
+/* A device-resident chunk table for a fixed list of tensors: built once,
+   then one launch per step covers every tensor. */
+typedef struct zs_list_plan* zs_list_plan_t;
+
+/* Validates the list (as the flat call, per tensor, plus: outputs of all
+   tensors pairwise disjoint and disjoint from every gradient range), splits
+   every tensor into chunks, and uploads the table on `stream`; returns after
+   the upload has completed.  T >= 0 tensors, 1 <= N <= ZS_MAX_REPLICAS.
+   Errors: ZS_ERR_NULL, ZS_ERR_RANGE, ZS_ERR_ALIGN, ZS_ERR_ALIAS, ZS_ERR_NOMEM,
+   ZS_ERR_HIP. */
+ZS_API zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_t N, zs_stream stream,
+                                     zs_list_plan_t* out);
+
+/* The step on every tensor of the plan: one kernel launch on `stream`. */
+ZS_API zs_status zs_reduce_adam_list_plan(zs_list_plan_t plan, const zs_adam_hp* hp, int64_t step,
+                                          zs_stream stream);
+
+/* One-shot form: create a plan, run it, wait for the step to finish on
+   `stream`, destroy the plan.  Blocks the calling thread. */
+ZS_API zs_status zs_reduce_adam_list(const zs_tensor* tensors, int32_t T, int32_t N, const zs_adam_hp* hp,
+                                     int64_t step, zs_stream stream);
+
+/* Waits for the device to go idle, then frees the plan's table.  NULL is a no-op. */
+ZS_API void zs_list_plan_destroy(zs_list_plan_t plan);
+
+/* Shape of a plan: total parameters, tensors and chunks (any output may be NULL). */
+ZS_API zs_status zs_list_plan_info(zs_list_plan_t plan, int64_t* n_params, int32_t* n_tensors, int32_t* n_chunks);
+
+/* Workgroups per launch for all later step calls in this process: 0 picks
+   automatically from the device's compute-unit count.  Results do not depend
+   on it (every element is computed by one thread with the same operations). */
+ZS_API zs_status zs_set_grid_blocks(int32_t blocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZSHARD_H */

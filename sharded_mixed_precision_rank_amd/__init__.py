@@ -1,0 +1,303 @@
+"""Python binding of libzshard (see include/zshard.h for the contract).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libzshard.so``.  PyTorch supplies device memory and streams.
+Importing this module fails if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzshard.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                      "(there is no fallback implementation)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+ZS_MAX_REPLICAS = 256
+STATUS = {0: "ZS_OK", 1: "ZS_ERR_NULL", 2: "ZS_ERR_RANGE", 3: "ZS_ERR_ALIAS", 4: "ZS_ERR_ALIGN", 5: "ZS_ERR_HIP",
+          6: "ZS_ERR_NOMEM"}
+
+
+class AdamHPStruct(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
+
+
+class FoldedStruct(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_float) for k in ("b1", "c1", "b2", "c2", "eps", "ss", "rb", "dk")]
+
+
+class TensorStruct(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("master", ctypes.c_void_p), ("m", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("param_bf16", ctypes.c_void_p), ("grad_chunks", ctypes.POINTER(ctypes.c_void_p))]
+
+
+_vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+_lib.zs_abi_version.restype = ctypes.c_int
+_lib.zs_status_string.restype = ctypes.c_char_p
+_lib.zs_status_string.argtypes = [ctypes.c_int]
+_lib.zs_last_error.restype = ctypes.c_char_p
+_lib.zs_fold.restype = ctypes.c_int
+_lib.zs_fold.argtypes = [ctypes.POINTER(AdamHPStruct), _i64, ctypes.POINTER(FoldedStruct)]
+_lib.zs_reduce_adam_flat.restype = ctypes.c_int
+_lib.zs_reduce_adam_flat.argtypes = [ctypes.POINTER(_vp), _i32, _i64, _vp, _vp, _vp, _vp,
+                                     ctypes.POINTER(AdamHPStruct), _i64, _vp]
+_lib.zs_list_plan_create.restype = ctypes.c_int
+_lib.zs_list_plan_create.argtypes = [ctypes.POINTER(TensorStruct), _i32, _i32, _vp, ctypes.POINTER(_vp)]
+_lib.zs_reduce_adam_list_plan.restype = ctypes.c_int
+_lib.zs_reduce_adam_list_plan.argtypes = [_vp, ctypes.POINTER(AdamHPStruct), _i64, _vp]
+_lib.zs_reduce_adam_list.restype = ctypes.c_int
+_lib.zs_reduce_adam_list.argtypes = [ctypes.POINTER(TensorStruct), _i32, _i32, ctypes.POINTER(AdamHPStruct), _i64,
+                                     _vp]
+_lib.zs_list_plan_destroy.restype = None
+_lib.zs_list_plan_destroy.argtypes = [_vp]
+_lib.zs_list_plan_info.restype = ctypes.c_int
+_lib.zs_list_plan_info.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+_lib.zs_set_grid_blocks.restype = ctypes.c_int
+_lib.zs_set_grid_blocks.argtypes = [_i32]
+
+
+class ZShardError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = STATUS.get(status, f"status {status}")
+        detail = _lib.zs_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {self.name}: {detail}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise ZShardError(status, where)
+
+
+@dataclass(frozen=True)
+class AdamHP:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+
+    def _c(self) -> AdamHPStruct:
+        return AdamHPStruct(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay)
+
+
+def _hp(hp) -> AdamHPStruct:
+    if isinstance(hp, AdamHP):
+        return hp._c()
+    if isinstance(hp, dict):
+        return AdamHP(**hp)._c()
+    raise TypeError("hp must be an AdamHP or a dict of lr, beta1, beta2, eps, weight_decay")
+
+
+def abi_version() -> int:
+    return int(_lib.zs_abi_version())
+
+
+def fold(hp, step: int) -> dict:
+    """The fp32 scalars the step uses (computed on the host, no GPU needed)."""
+    out = FoldedStruct()
+    h = _hp(hp)
+    _check(_lib.zs_fold(ctypes.byref(h), step, ctypes.byref(out)), "zs_fold")
+    return {k: getattr(out, k) for k, _ in FoldedStruct._fields_}
+
+
+def set_grid_blocks(blocks: int) -> None:
+    _check(_lib.zs_set_grid_blocks(blocks), "zs_set_grid_blocks")
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev_check(t, dtypes, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _bf16_types():
+    import torch
+
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _f32_types():
+    import torch
+
+    return (torch.float32,)
+
+
+def _tensor_args(grads, master, m, v, param):
+    n = master.numel()
+    _dev_check(master, _f32_types(), "master")
+    _dev_check(m, _f32_types(), "m")
+    _dev_check(v, _f32_types(), "v")
+    _dev_check(param, _bf16_types(), "param")
+    for name, t in (("m", m), ("v", v), ("param", param)):
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, master has {n}")
+    for r, g in enumerate(grads):
+        _dev_check(g, _bf16_types(), f"grads[{r}]")
+        if g.numel() != n:
+            raise ValueError(f"grads[{r}] has {g.numel()} elements, master has {n}")
+    return n
+
+
+def reduce_adam_flat(grads: Sequence, master, m, v, param, hp, step: int, stream=None) -> None:
+    """One shard step: average ``grads`` (N bf16 device tensors, rank order) and
+    apply AdamW to ``master``/``m``/``v`` in place, writing the bf16 copy to
+    ``param``.  Enqueued on ``stream`` (default: torch's current stream)."""
+    N = len(grads)
+    n = _tensor_args(grads, master, m, v, param)
+    tab = (_vp * max(N, 1))(*[g.data_ptr() for g in grads])
+    h = _hp(hp)
+    _check(_lib.zs_reduce_adam_flat(tab, N, n, master.data_ptr(), m.data_ptr(), v.data_ptr(), param.data_ptr(),
+                                    ctypes.byref(h), step, _stream_handle(stream)), "zs_reduce_adam_flat")
+
+
+def reduce_adam_flat_ptrs(grad_ptrs: Sequence[int], n: int, master: int, m: int, v: int, param: int, hp,
+                          step: int, stream) -> None:
+    """Raw-pointer form of :func:`reduce_adam_flat` (device addresses as ints)."""
+    N = len(grad_ptrs)
+    tab = (_vp * max(N, 1))(*grad_ptrs)
+    h = _hp(hp)
+    _check(_lib.zs_reduce_adam_flat(tab, N, n, master, m, v, param, ctypes.byref(h), step, _stream_handle(stream)),
+           "zs_reduce_adam_flat")
+
+
+@dataclass
+class ShardTensor:
+    """One tensor of a ragged list: its replicas' grads and its state."""
+    grads: Sequence
+    master: object
+    m: object
+    v: object
+    param: object
+
+
+def _tensor_table(tensors: Sequence[ShardTensor], N: int):
+    keep = []
+    tab = (TensorStruct * max(len(tensors), 1))()
+    for i, t in enumerate(tensors):
+        if len(t.grads) != N:
+            raise ValueError(f"tensor {i} has {len(t.grads)} grads, expected N={N}")
+        n = _tensor_args(t.grads, t.master, t.m, t.v, t.param)
+        g = (_vp * N)(*[x.data_ptr() for x in t.grads])
+        keep.append(g)
+        tab[i] = TensorStruct(n, t.master.data_ptr(), t.m.data_ptr(), t.v.data_ptr(), t.param.data_ptr(),
+                              ctypes.cast(g, ctypes.POINTER(_vp)))
+    return tab, keep
+
+
+class ListPlan:
+    """A device-resident chunk table for a fixed ragged list of tensors; each
+    :meth:`step` is one kernel launch covering every tensor."""
+
+    def __init__(self, tensors: Sequence[ShardTensor], N: int, stream=None):
+        tab, keep = _tensor_table(tensors, N)
+        h = _vp()
+        _check(_lib.zs_list_plan_create(tab, len(tensors), N, _stream_handle(stream), ctypes.byref(h)),
+               "zs_list_plan_create")
+        self._h = h
+        self.N = N
+        self._tensors = list(tensors)   # the plan holds their addresses: keep them alive
+
+    @classmethod
+    def from_arenas(cls, sizes, offsets, grads: Sequence, master, m, v, param, stream=None) -> "ListPlan":
+        """Plan over tensors laid out in per-array arenas: tensor t is elements
+        [offsets[t], offsets[t] + sizes[t]) of ``master``, ``m``, ``v``, ``param``
+        and of every replica's gradient arena in ``grads``."""
+        import numpy as np
+
+        N = len(grads)
+        L = master.numel()
+        _tensor_args(grads, master, m, v, param)
+        sizes = np.asarray(sizes, dtype=np.int64)
+        offsets = np.asarray(offsets, dtype=np.int64)
+        if sizes.shape != offsets.shape or (sizes.size and (offsets.min() < 0 or (offsets + sizes).max() > L)):
+            raise ValueError("tensor ranges must lie inside the arenas")
+        T = sizes.size
+        gtab = np.empty((max(T, 1), N), dtype=np.uint64)
+        for r, g in enumerate(grads):
+            gtab[:T, r] = np.uint64(g.data_ptr()) + (offsets * 2).astype(np.uint64)
+        rec = np.zeros((max(T, 1), 6), dtype=np.uint64)
+        rec[:T, 0] = sizes.astype(np.uint64)
+        rec[:T, 1] = np.uint64(master.data_ptr()) + (offsets * 4).astype(np.uint64)
+        rec[:T, 2] = np.uint64(m.data_ptr()) + (offsets * 4).astype(np.uint64)
+        rec[:T, 3] = np.uint64(v.data_ptr()) + (offsets * 4).astype(np.uint64)
+        rec[:T, 4] = np.uint64(param.data_ptr()) + (offsets * 2).astype(np.uint64)
+        rec[:T, 5] = np.uint64(gtab.ctypes.data) + np.arange(max(T, 1), dtype=np.uint64) * np.uint64(8 * N)
+        assert ctypes.sizeof(TensorStruct) == 48
+        self = cls.__new__(cls)
+        h = _vp()
+        _check(_lib.zs_list_plan_create(ctypes.cast(rec.ctypes.data, ctypes.POINTER(TensorStruct)), T, N,
+                                        _stream_handle(stream), ctypes.byref(h)), "zs_list_plan_create")
+        self._h = h
+        self.N = N
+        self._tensors = [grads, master, m, v, param]
+        return self
+
+    def step(self, hp, step: int, stream=None) -> None:
+        if not self._h:
+            raise ValueError("plan is closed")
+        h = _hp(hp)
+        _check(_lib.zs_reduce_adam_list_plan(self._h, ctypes.byref(h), step, _stream_handle(stream)),
+               "zs_reduce_adam_list_plan")
+
+    def info(self) -> dict:
+        n, t, c = _i64(), _i32(), _i32()
+        _check(_lib.zs_list_plan_info(self._h, ctypes.byref(n), ctypes.byref(t), ctypes.byref(c)),
+               "zs_list_plan_info")
+        return dict(n_params=n.value, n_tensors=t.value, n_chunks=c.value)
+
+    def close(self) -> None:
+        if self._h:
+            _lib.zs_list_plan_destroy(self._h)
+            self._h = _vp()
+            self._tensors = []
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def reduce_adam_list(tensors: Sequence[ShardTensor], N: int, hp, step: int, stream=None) -> None:
+    """One-shot list step (builds a plan, runs it, waits, frees it)."""
+    tab, keep = _tensor_table(tensors, N)
+    h = _hp(hp)
+    _check(_lib.zs_reduce_adam_list(tab, len(tensors), N, ctypes.byref(h), step, _stream_handle(stream)),
+           "zs_reduce_adam_list")
+
+
+def library():
+    """The loaded ctypes library (for tests of the raw ABI)."""
+    return _lib

@@ -1,0 +1,421 @@
+// C-ABI front end of libzshard: argument checks, scalar folding, list plans,
+// launches and error reporting.  The arithmetic contract is in include/zshard.h.
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "zs_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<int32_t> g_grid_blocks{0};
+
+zs_status fail(zs_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+zs_status hip_fail(hipError_t e, const char* what) {
+  return fail(ZS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool sync_mode() {
+  static const bool on = [] {
+    const char* s = std::getenv("ZS_SYNC");
+    return s && s[0] && std::strcmp(s, "0") != 0;
+  }();
+  return on;
+}
+
+zs_status check_hp(const zs_adam_hp* hp, int64_t step) {
+  if (!hp) return fail(ZS_ERR_NULL, "hp is NULL");
+  const double xs[5] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+  for (double x : xs)
+    if (!std::isfinite(x)) return fail(ZS_ERR_RANGE, "hyperparameters must be finite");
+  if (hp->lr < 0) return fail(ZS_ERR_RANGE, "lr must be >= 0 (got %g)", hp->lr);
+  if (!(hp->beta1 >= 0 && hp->beta1 < 1)) return fail(ZS_ERR_RANGE, "beta1 must be in [0, 1) (got %g)", hp->beta1);
+  if (!(hp->beta2 >= 0 && hp->beta2 < 1)) return fail(ZS_ERR_RANGE, "beta2 must be in [0, 1) (got %g)", hp->beta2);
+  if (!(hp->eps > 0)) return fail(ZS_ERR_RANGE, "eps must be > 0 (got %g)", hp->eps);
+  if (hp->weight_decay < 0) return fail(ZS_ERR_RANGE, "weight_decay must be >= 0 (got %g)", hp->weight_decay);
+  if (step < 1) return fail(ZS_ERR_RANGE, "step must be >= 1 (got %lld)", (long long)step);
+  return ZS_OK;
+}
+
+void fold_scalars(const zs_adam_hp& hp, int64_t step, zs_folded* f) {
+  const double t = (double)step;
+  f->b1 = (float)hp.beta1;
+  f->c1 = (float)(1.0 - hp.beta1);
+  f->b2 = (float)hp.beta2;
+  f->c2 = (float)(1.0 - hp.beta2);
+  f->eps = (float)hp.eps;
+  f->ss = (float)(hp.lr / (1.0 - std::pow(hp.beta1, t)));
+  f->rb = (float)(1.0 / std::sqrt(1.0 - std::pow(hp.beta2, t)));
+  f->dk = (float)(1.0 - hp.lr * hp.weight_decay);
+}
+
+zs::Scalars make_scalars(const zs_adam_hp& hp, int64_t step, int32_t N) {
+  zs_folded f;
+  fold_scalars(hp, step, &f);
+  zs::Scalars c;
+  c.b1 = f.b1;
+  c.c1 = f.c1;
+  c.b2 = f.b2;
+  c.c2 = f.c2;
+  c.e = f.eps;
+  c.ss = f.ss;
+  c.rb = f.rb;
+  c.dk = f.dk;
+  c.n_rep = N;
+  c.pow2 = (N & (N - 1)) == 0;
+  c.inv_n = (float)(1.0 / (double)N);
+  return c;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+  int kind;          // 0 = output, 1 = gradient
+  int64_t owner;
+};
+
+// Outputs pairwise disjoint; no gradient range overlaps an output.
+zs_status check_alias(std::vector<Range>& rs) {
+  std::vector<Range> outs, grads;
+  for (const Range& r : rs)
+    if (r.hi > r.lo) (r.kind == 0 ? outs : grads).push_back(r);
+  std::sort(outs.begin(), outs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t k = 1; k < outs.size(); ++k)
+    if (outs[k].lo < outs[k - 1].hi)
+      return fail(ZS_ERR_ALIAS, "output arrays overlap (tensors %lld and %lld)", (long long)outs[k - 1].owner,
+                  (long long)outs[k].owner);
+  // Sorted disjoint outputs also have sorted ends, so of the outputs that start
+  // below a gradient range's end, only the last can reach past its start.
+  for (const Range& g : grads) {
+    auto it = std::lower_bound(outs.begin(), outs.end(), g.hi, [](const Range& o, uintptr_t x) { return o.lo < x; });
+    if (it != outs.begin()) {
+      const Range& o = *(it - 1);
+      if (o.hi > g.lo)
+        return fail(ZS_ERR_ALIAS, "a gradient chunk overlaps an output array (tensor %lld)", (long long)g.owner);
+    }
+  }
+  return ZS_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Per-tensor checks shared by the flat call and the list plans; appends the
+// tensor's address ranges to `rs`.
+zs_status check_tensor(const uint16_t* const* g, int32_t N, int64_t n, const float* p, const float* m,
+                       const float* v, const uint16_t* b, int64_t owner, std::vector<Range>& rs) {
+  if (n < 0) return fail(ZS_ERR_RANGE, "n must be >= 0 (tensor %lld)", (long long)owner);
+  if (n > (int64_t(1) << 56)) return fail(ZS_ERR_RANGE, "n too large (tensor %lld)", (long long)owner);
+  if (n == 0) return ZS_OK;
+  if (!g) return fail(ZS_ERR_NULL, "grad_chunks is NULL (tensor %lld)", (long long)owner);
+  if (!p || !m || !v || !b) return fail(ZS_ERR_NULL, "master/m/v/param_bf16 is NULL (tensor %lld)", (long long)owner);
+  for (int32_t r = 0; r < N; ++r) {
+    if (!g[r]) return fail(ZS_ERR_NULL, "grad_chunks[%d] is NULL (tensor %lld)", r, (long long)owner);
+    if (!aligned(g[r], 2)) return fail(ZS_ERR_ALIGN, "grad_chunks[%d] not 2-byte aligned", r);
+  }
+  if (!aligned(p, 4) || !aligned(m, 4) || !aligned(v, 4))
+    return fail(ZS_ERR_ALIGN, "fp32 arrays must be 4-byte aligned (tensor %lld)", (long long)owner);
+  if (!aligned(b, 2)) return fail(ZS_ERR_ALIGN, "param_bf16 must be 2-byte aligned (tensor %lld)", (long long)owner);
+  const uintptr_t n4 = (uintptr_t)n * 4, n2 = (uintptr_t)n * 2;
+  rs.push_back({(uintptr_t)p, (uintptr_t)p + n4, 0, owner});
+  rs.push_back({(uintptr_t)m, (uintptr_t)m + n4, 0, owner});
+  rs.push_back({(uintptr_t)v, (uintptr_t)v + n4, 0, owner});
+  rs.push_back({(uintptr_t)b, (uintptr_t)b + n2, 0, owner});
+  for (int32_t r = 0; r < N; ++r) rs.push_back({(uintptr_t)g[r], (uintptr_t)g[r] + n2, 1, owner});
+  return ZS_OK;
+}
+
+zs::FlatShape shape_of(const uint16_t* const* g, int32_t N, int64_t n, float* p, float* m, float* v,
+                       uint16_t* b) {
+  zs::FlatShape s;
+  s.p = p;
+  s.m = m;
+  s.v = v;
+  s.b = b;
+  s.n = n;
+  const int64_t h = zs::common_peel(p, m, v, b, g, N);
+  if (h < 0 || n < h + 8) {
+    s.head = 0;
+    s.nvec = 0;
+    s.scalar_only = 1;
+  } else {
+    s.head = h;
+    s.nvec = (n - h) / 8;
+    s.scalar_only = 0;
+  }
+  return s;
+}
+
+int auto_blocks() {
+  const int32_t forced = g_grid_blocks.load(std::memory_order_relaxed);
+  if (forced > 0) return forced;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!cached[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached[dev] = cus * 8;
+  }
+  return cached[dev];
+}
+
+zs_status after_launch(hipError_t e, hipStream_t stream, const char* what) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (sync_mode()) {
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  return ZS_OK;
+}
+
+}  // namespace
+
+namespace zs {
+
+int64_t common_peel(const float* p, const float* m, const float* v, const uint16_t* b, const uint16_t* const* g,
+                    int32_t N) {
+  for (int64_t h = 0; h < 8; ++h) {
+    bool ok = aligned(p + h, 16) && aligned(m + h, 16) && aligned(v + h, 16) && aligned(b + h, 16);
+    for (int32_t r = 0; ok && r < N; ++r) ok = aligned(g[r] + h, 16);
+    if (ok) return h;
+  }
+  return -1;
+}
+
+}  // namespace zs
+
+struct zs_list_plan {
+  int device;
+  int32_t N;
+  int32_t T;
+  int32_t n_chunks;
+  int64_t n_params;
+  void* table;  // device: chunks | tensors | grad pointers
+  zs::ListChunk* chunks;
+  zs::ListTensor* tensors;
+  const uint16_t** gptrs;
+};
+
+extern "C" {
+
+int zs_abi_version(void) { return ZS_ABI_VERSION; }
+
+const char* zs_status_string(int status) {
+  switch (status) {
+    case ZS_OK: return "ZS_OK";
+    case ZS_ERR_NULL: return "ZS_ERR_NULL";
+    case ZS_ERR_RANGE: return "ZS_ERR_RANGE";
+    case ZS_ERR_ALIAS: return "ZS_ERR_ALIAS";
+    case ZS_ERR_ALIGN: return "ZS_ERR_ALIGN";
+    case ZS_ERR_HIP: return "ZS_ERR_HIP";
+    case ZS_ERR_NOMEM: return "ZS_ERR_NOMEM";
+    default: return "ZS_ERR_UNKNOWN";
+  }
+}
+
+const char* zs_last_error(void) { return g_last_error.c_str(); }
+
+zs_status zs_fold(const zs_adam_hp* hp, int64_t step, zs_folded* out) {
+  g_last_error.clear();
+  if (!out) return fail(ZS_ERR_NULL, "out is NULL");
+  zs_status st = check_hp(hp, step);
+  if (st) return st;
+  fold_scalars(*hp, step, out);
+  return ZS_OK;
+}
+
+zs_status zs_set_grid_blocks(int32_t blocks) {
+  if (blocks < 0 || blocks > (1 << 24)) return fail(ZS_ERR_RANGE, "blocks must be in [0, 2^24]");
+  g_grid_blocks.store(blocks, std::memory_order_relaxed);
+  return ZS_OK;
+}
+
+zs_status zs_reduce_adam_flat(const uint16_t* const* grad_chunks, int32_t N, int64_t n, float* master, float* m,
+                              float* v, uint16_t* param_bf16, const zs_adam_hp* hp, int64_t step,
+                              zs_stream stream) {
+  try {
+    g_last_error.clear();
+    zs_status st = check_hp(hp, step);
+    if (st) return st;
+    if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
+    std::vector<Range> rs;
+    st = check_tensor(grad_chunks, N, n, master, m, v, param_bf16, 0, rs);
+    if (st) return st;
+    if (n == 0) return ZS_OK;
+    st = check_alias(rs);
+    if (st) return st;
+    const zs::FlatShape s = shape_of(grad_chunks, N, n, master, m, v, param_bf16);
+    const zs::Scalars c = make_scalars(*hp, step, N);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return after_launch(zs::launch_flat(grad_chunks, s, c, auto_blocks(), hs), hs, "zs_reduce_adam_flat launch");
+  } catch (const std::bad_alloc&) {
+    return fail(ZS_ERR_NOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(ZS_ERR_HIP, "unexpected exception");
+  }
+}
+
+zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_t N, zs_stream stream,
+                              zs_list_plan_t* out) {
+  try {
+    g_last_error.clear();
+    if (!out) return fail(ZS_ERR_NULL, "out is NULL");
+    *out = nullptr;
+    if (T < 0) return fail(ZS_ERR_RANGE, "T must be >= 0 (got %d)", T);
+    if (T > 0 && !tensors) return fail(ZS_ERR_NULL, "tensors is NULL");
+    if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
+    std::vector<Range> rs;
+    int64_t total = 0;
+    for (int32_t t = 0; t < T; ++t) {
+      const zs_tensor& x = tensors[t];
+      zs_status st = check_tensor(x.grad_chunks, N, x.n, x.master, x.m, x.v, x.param_bf16, t, rs);
+      if (st) return st;
+      total += x.n;
+    }
+    zs_status st = check_alias(rs);
+    if (st) return st;
+
+    std::vector<zs::ListTensor> ht;
+    std::vector<zs::ListChunk> hc;
+    std::vector<const uint16_t*> hg;
+    ht.reserve(T);
+    hg.reserve((size_t)T * N);
+    for (int32_t t = 0; t < T; ++t) {
+      const zs_tensor& x = tensors[t];
+      zs::ListTensor d{};
+      if (x.n == 0) {
+        d.scalar_only = 1;
+      } else {
+        const zs::FlatShape s = shape_of(x.grad_chunks, N, x.n, x.master, x.m, x.v, x.param_bf16);
+        d.p = s.p;
+        d.m = s.m;
+        d.v = s.v;
+        d.b = s.b;
+        d.n = s.n;
+        d.head = s.head;
+        d.nvec = s.nvec;
+        d.scalar_only = s.scalar_only;
+        if (!s.scalar_only) {
+          const int64_t per = zs::kChunkElems / 8;
+          for (int64_t g0 = 0; g0 < s.nvec; g0 += per)
+            hc.push_back({t, g0 == 0 ? 1 : 0, g0, std::min(s.nvec, g0 + per), 0});
+        } else {
+          for (int64_t e0 = 0; e0 < s.n; e0 += zs::kChunkElems)
+            hc.push_back({t, 0, e0, std::min(s.n, e0 + zs::kChunkElems), 0});
+        }
+      }
+      ht.push_back(d);
+      for (int32_t r = 0; r < N; ++r) hg.push_back(x.n ? x.grad_chunks[r] : nullptr);
+    }
+    if (hc.size() > (size_t)INT32_MAX) return fail(ZS_ERR_RANGE, "too many chunks");
+
+    zs_list_plan* plan = new zs_list_plan();
+    plan->N = N;
+    plan->T = T;
+    plan->n_chunks = (int32_t)hc.size();
+    plan->n_params = total;
+    plan->table = nullptr;
+    if (hipGetDevice(&plan->device) != hipSuccess) plan->device = 0;
+    const size_t bc = hc.size() * sizeof(zs::ListChunk), bt = ht.size() * sizeof(zs::ListTensor),
+                 bg = hg.size() * sizeof(void*);
+    const size_t bytes = bc + bt + bg;
+    if (bytes > 0) {
+      hipError_t e = hipMalloc(&plan->table, bytes);
+      if (e != hipSuccess) {
+        delete plan;
+        (void)hipGetLastError();
+        return fail(ZS_ERR_NOMEM, "plan table of %zu bytes: %s", bytes, hipGetErrorString(e));
+      }
+      std::vector<unsigned char> host(bytes);
+      std::memcpy(host.data(), hc.data(), bc);
+      std::memcpy(host.data() + bc, ht.data(), bt);
+      std::memcpy(host.data() + bc + bt, hg.data(), bg);
+      hipStream_t hs = static_cast<hipStream_t>(stream);
+      e = hipMemcpyAsync(plan->table, host.data(), bytes, hipMemcpyHostToDevice, hs);
+      if (e == hipSuccess) e = hipStreamSynchronize(hs);
+      if (e != hipSuccess) {
+        (void)hipFree(plan->table);
+        delete plan;
+        return hip_fail(e, "plan table upload");
+      }
+    }
+    unsigned char* base = static_cast<unsigned char*>(plan->table);
+    plan->chunks = reinterpret_cast<zs::ListChunk*>(base);
+    plan->tensors = reinterpret_cast<zs::ListTensor*>(base + bc);
+    plan->gptrs = reinterpret_cast<const uint16_t**>(base + bc + bt);
+    *out = plan;
+    return ZS_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(ZS_ERR_NOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(ZS_ERR_HIP, "unexpected exception");
+  }
+}
+
+zs_status zs_reduce_adam_list_plan(zs_list_plan_t plan, const zs_adam_hp* hp, int64_t step, zs_stream stream) {
+  g_last_error.clear();
+  if (!plan) return fail(ZS_ERR_NULL, "plan is NULL");
+  zs_status st = check_hp(hp, step);
+  if (st) return st;
+  if (plan->n_chunks == 0) return ZS_OK;
+  const zs::Scalars c = make_scalars(*hp, step, plan->N);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  return after_launch(zs::launch_list(plan->chunks, plan->n_chunks, plan->tensors, plan->gptrs, c, auto_blocks(), hs),
+                      hs, "zs_reduce_adam_list launch");
+}
+
+void zs_list_plan_destroy(zs_list_plan_t plan) {
+  if (!plan) return;
+  if (plan->table) {
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(plan->device);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(plan->table);
+    (void)hipSetDevice(cur);
+  }
+  delete plan;
+}
+
+zs_status zs_reduce_adam_list(const zs_tensor* tensors, int32_t T, int32_t N, const zs_adam_hp* hp, int64_t step,
+                              zs_stream stream) {
+  zs_status st = check_hp(hp, step);
+  if (st) return st;
+  zs_list_plan_t plan = nullptr;
+  st = zs_list_plan_create(tensors, T, N, stream, &plan);
+  if (st) return st;
+  st = zs_reduce_adam_list_plan(plan, hp, step, stream);
+  if (st == ZS_OK) {
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) st = hip_fail(e, "zs_reduce_adam_list");
+  }
+  zs_list_plan_destroy(plan);
+  return st;
+}
+
+zs_status zs_list_plan_info(zs_list_plan_t plan, int64_t* n_params, int32_t* n_tensors, int32_t* n_chunks) {
+  if (!plan) return fail(ZS_ERR_NULL, "plan is NULL");
+  if (n_params) *n_params = plan->n_params;
+  if (n_tensors) *n_tensors = plan->T;
+  if (n_chunks) *n_chunks = plan->n_chunks;
+  return ZS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Internal interface between the C-ABI front end (zs_api.cpp) and the device
+// kernels (zs_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/zshard.h"
+
+namespace zs {
+
+// Scalars of one step, folded on the host (double -> fp32 once).
+struct Scalars {
+  float b1, c1, b2, c2, e, ss, rb, dk;
+  float inv_n;      // exactly 1/N when N is a power of two
+  int32_t n_rep;    // N
+  int32_t pow2;     // N is a power of two: s * inv_n is bit-identical to s / N
+};
+
+// Flat shard, as the kernel sees it.  Elements [0, head) and
+// [head + 8*nvec, n) go through the per-element path; the 8-element groups in
+// between through 16-byte vector accesses.  scalar_only = 1 means no common
+// alignment offset exists and every element takes the per-element path.
+struct FlatShape {
+  float* p;
+  float* m;
+  float* v;
+  uint16_t* b;
+  int64_t n;
+  int64_t head;
+  int64_t nvec;
+  int32_t scalar_only;
+};
+
+// One tensor of a list plan (64 bytes, device table).
+struct ListTensor {
+  float* p;
+  float* m;
+  float* v;
+  uint16_t* b;
+  int64_t n;
+  int64_t head;
+  int64_t nvec;
+  int32_t scalar_only;
+  int32_t pad_;
+};
+
+// One chunk of a list plan (device table): for a vector tensor, groups
+// [begin, end); for a scalar-only tensor, elements [begin, end).  The chunk
+// with first != 0 also handles its tensor's head and tail elements.
+struct ListChunk {
+  int32_t tensor;
+  int32_t first;
+  int64_t begin;
+  int64_t end;
+  int64_t pad_;
+};
+
+static_assert(sizeof(ListTensor) == 64, "ListTensor layout");
+static_assert(sizeof(ListChunk) == 32, "ListChunk layout");
+
+// Common alignment peel: the smallest h in [0, 8) such that every pointer
+// advanced by h elements is 16-byte aligned, or -1 if none exists.
+int64_t common_peel(const float* p, const float* m, const float* v, const uint16_t* b,
+                    const uint16_t* const* g, int32_t N);
+
+// Launches (host side, defined with the kernels).
+hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, int blocks,
+                       hipStream_t stream);
+hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
+                       const uint16_t* const* gptrs, const Scalars& c, int blocks, hipStream_t stream);
+
+// Elements per list chunk (vector tensors: groups of 8 per chunk = this / 8).
+constexpr int64_t kChunkElems = 65536;
+constexpr int kBlock = 256;
+
+}  // namespace zs

@@ -1,0 +1,415 @@
+// Device kernels of libzshard: the fused reduce + AdamW + bf16 re-cast step.
+//
+// The step is a pure stream: per parameter it reads N bf16 gradients and the
+// fp32 master/momentum/variance and writes those three back plus a bf16 copy,
+// (2N + 26) bytes with no reuse, against a handful of ALU operations per byte.
+// HBM bandwidth bounds it; there is no contraction, so no MFMA.  Design:
+//
+//  * One thread owns an 8-parameter group: one 16-byte load per replica
+//    (8 bf16), two 16-byte loads/stores per fp32 array, one 16-byte bf16
+//    store.  A wave touches 1 KiB contiguous per array per access, so every
+//    cache line is fully used and writes never need the line's old contents.
+//  * Replica pointers are wave-uniform.  For the flat call they sit in the
+//    kernel-argument segment and reach SGPRs through scalar loads; for lists
+//    they are staged through LDS per chunk and moved to SGPRs with
+//    readfirstlane.  Either way each global load is SGPR base + one shared
+//    VGPR offset.
+//  * Replicas are accumulated in fp32 registers strictly in rank order
+//    0..N-1; loads are issued in batches so that several are in flight per
+//    thread without holding all N in registers.
+//  * The master/momentum/variance loads are issued before the gradient
+//    stream so their latency overlaps it.
+//  * Every access is marked non-temporal: nothing is re-read, so nothing
+//    should displace useful lines in L2 or the Infinity Cache.
+//  * Elements outside the 16-byte-aligned middle (at most 7 at each end) and
+//    shards whose arrays share no common alignment go through a per-element
+//    path with the identical operation sequence (same inline function), so
+//    results do not depend on alignment, grid size or path.
+//
+// Arithmetic: see include/zshard.h.  Built with -ffp-contract=off (no FMA
+// contraction) and correctly rounded fp32 divide and sqrt; fp32 denormals are
+// kept.  Division by N is a multiply by 1/N only when N is a power of two,
+// where both are the same correctly rounded result.
+#include <type_traits>
+
+#include "zs_internal.h"
+
+namespace zs {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBatch = 8;  // replica loads in flight per thread per batch
+
+
+#define GLB __attribute__((address_space(1)))
+
+// A tile's base pointer: wave-uniform, in the global address space, pinned in
+// SGPRs and opaque to the optimizer.  Adding a lane's 32-bit byte offset then
+// stays the SGPR-base + VGPR-offset addressing form (one offset register for
+// every array) instead of being folded into a 64-bit per-lane address.
+template <class T>
+__device__ __forceinline__ GLB T* tile_base(T* p) {
+  GLB T* q = (GLB T*)p;
+  asm volatile("" : "+s"(q));
+  return q;
+}
+// A lane's 32-bit offset re-materialised in the current basic block:
+// instruction selection only recognises base + zero-extended 32-bit offset
+// when the extension is visible in the block of the access, and the loop
+// optimisers would otherwise hoist it out of the tile loop.
+__device__ __forceinline__ uint32_t here(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+template <class T>
+__device__ __forceinline__ GLB T* at(GLB T* base, uint32_t bytes) {
+  return (GLB T*)((GLB char*)base + bytes);
+}
+template <class T>
+__device__ __forceinline__ T ld_g(const GLB T* p) {
+  return __builtin_nontemporal_load(p);
+}
+template <class T>
+__device__ __forceinline__ void st_g(GLB T* p, T x) {
+  __builtin_nontemporal_store(x, p);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf_one(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);  // round to nearest even
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ uint16_t to_bf16(float a) { return __builtin_bit_cast(uint16_t, (__bf16)a); }
+
+// s / N.  For the replica counts the kernels are specialised on (powers of
+// two) this is a multiply by the exact reciprocal, the same correctly rounded
+// result; otherwise a correctly rounded divide.
+template <int NT>
+__device__ __forceinline__ float mean_of(float s, const Scalars& c) {
+  if constexpr (NT > 0 && (NT & (NT - 1)) == 0)
+    return s * (1.0f / (float)NT);
+  else
+    return s / (float)c.n_rep;
+}
+
+// The per-parameter AdamW update; every path calls this one function.
+__device__ __forceinline__ void adam(float g, float& p, float& m, float& v, const Scalars& c) {
+  const float m1 = c.b1 * m + c.c1 * g;
+  const float v1 = c.b2 * v + c.c2 * (g * g);
+  const float d = __builtin_sqrtf(v1) * c.rb + c.e;
+  const float u = m1 / d;
+  p = c.dk * p - c.ss * u;
+  m = m1;
+  v = v1;
+}
+
+__device__ __forceinline__ void accumulate(float (&acc)[8], const u32x4 w) {
+  acc[0] = acc[0] + bf_lo(w.x);
+  acc[1] = acc[1] + bf_hi(w.x);
+  acc[2] = acc[2] + bf_lo(w.y);
+  acc[3] = acc[3] + bf_hi(w.y);
+  acc[4] = acc[4] + bf_lo(w.z);
+  acc[5] = acc[5] + bf_hi(w.z);
+  acc[6] = acc[6] + bf_lo(w.w);
+  acc[7] = acc[7] + bf_hi(w.w);
+}
+
+// Replica pointer tables: each call of G(r) yields replica r's gradient base
+// already advanced to the current tile (wave-uniform, so it lives in SGPRs),
+// and every load adds the lane's 32-bit byte offset within the tile.
+template <class GP>
+__device__ __forceinline__ u32x4 ld_grad(GP G, int r, uint32_t lane) {
+  return ld_g((const GLB u32x4*)at(G(r), here(lane) * 2u));
+}
+
+template <class GP>
+__device__ __forceinline__ void load_batch(GP G, int r, int N, uint32_t lane, u32x4 (&w)[kBatch]) {
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j)
+    if (r + j < N) w[j] = ld_grad(G, r + j, lane);
+}
+
+__device__ __forceinline__ void add_batch(float (&acc)[8], const u32x4 (&w)[kBatch], int r, int N) {
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j)
+    if (r + j < N) accumulate(acc, w[j]);
+}
+
+// acc[k] = sum over replicas r = 0..N-1, in that order, of element lane+k.
+// Replicas 1..N-1 stream in batches of kBatch loads; the next batch is in
+// flight while the current one is added (two register buffers), and
+// scheduling barriers stop the compiler from hoisting later batches, which
+// would buy nothing but registers.
+template <int NT, class GP>
+__device__ __forceinline__ void reduce_replicas(GP G, int N, uint32_t lane, float (&acc)[8]) {
+  {
+    const u32x4 w = ld_grad(G, 0, lane);
+    acc[0] = bf_lo(w.x);
+    acc[1] = bf_hi(w.x);
+    acc[2] = bf_lo(w.y);
+    acc[3] = bf_hi(w.y);
+    acc[4] = bf_lo(w.z);
+    acc[5] = bf_hi(w.z);
+    acc[6] = bf_lo(w.w);
+    acc[7] = bf_hi(w.w);
+  }
+  if constexpr (NT > 0) {
+    // fully unrolled: batch k+1 is issued before batch k is added
+    constexpr int NB = (NT - 1 + kBatch - 1) / kBatch;
+    u32x4 w[2][kBatch];
+    if constexpr (NB > 0) load_batch(G, 1, NT, lane, w[0]);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (k + 1 < NB) load_batch(G, 1 + (k + 1) * kBatch, NT, lane, w[(k + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      add_batch(acc, w[k & 1], 1 + k * kBatch, NT);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    u32x4 wa[kBatch], wb[kBatch];
+    if (N > 1) load_batch(G, 1, N, lane, wa);
+#pragma unroll 1
+    for (int r0 = 1; r0 < N; r0 += 2 * kBatch) {
+      const int r1 = r0 + kBatch, r2 = r1 + kBatch;
+      if (r1 < N) load_batch(G, r1, N, lane, wb);
+      __builtin_amdgcn_sched_barrier(0);
+      add_batch(acc, wa, r0, N);
+      __builtin_amdgcn_sched_barrier(0);
+      if (r2 < N) load_batch(G, r2, N, lane, wa);
+      __builtin_amdgcn_sched_barrier(0);
+      if (r1 < N) add_batch(acc, wb, r1, N);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// One 8-parameter group: element e0 + lane of every array, where e0 is the
+// wave-uniform tile start (16-byte aligned in every array) and lane < 2^29 is
+// this thread's element offset within the tile.  G(r) returns replica r's
+// gradient pointer advanced to e0.
+template <int NT, class GP>
+__device__ __forceinline__ void group_step(GP G, int N, int64_t e0, uint32_t lane, const FlatShape& s,
+                                           const Scalars& c) {
+  f32x4 pa, pb, ma, mb, va, vb;
+  {
+    const uint32_t lb4 = here(lane) * 4u;  // byte offset in fp32 arrays
+    const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(s.p + e0), lb4);
+    const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(s.m + e0), lb4);
+    const GLB f32x4* V4 = (const GLB f32x4*)at(tile_base(s.v + e0), lb4);
+    pa = ld_g(P4);
+    pb = ld_g(P4 + 1);
+    ma = ld_g(M4);
+    mb = ld_g(M4 + 1);
+    va = ld_g(V4);
+    vb = ld_g(V4 + 1);
+  }
+
+  float acc[8];
+  reduce_replicas<NT>(G, N, lane, acc);
+
+  float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+  float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+  float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) adam(mean_of<NT>(acc[k], c), p[k], m[k], v[k], c);
+
+  // addresses recomputed here so they stay SGPR base + 32-bit lane offset
+  const uint32_t lb4 = here(lane) * 4u;
+  GLB f32x4* P4 = (GLB f32x4*)at(tile_base(s.p + e0), lb4);
+  GLB f32x4* M4 = (GLB f32x4*)at(tile_base(s.m + e0), lb4);
+  GLB f32x4* V4 = (GLB f32x4*)at(tile_base(s.v + e0), lb4);
+  st_g(P4, (f32x4){p[0], p[1], p[2], p[3]});
+  st_g(P4 + 1, (f32x4){p[4], p[5], p[6], p[7]});
+  st_g(M4, (f32x4){m[0], m[1], m[2], m[3]});
+  st_g(M4 + 1, (f32x4){m[4], m[5], m[6], m[7]});
+  st_g(V4, (f32x4){v[0], v[1], v[2], v[3]});
+  st_g(V4 + 1, (f32x4){v[4], v[5], v[6], v[7]});
+  st_g((GLB u32x4*)at(tile_base(s.b + e0), here(lane) * 2u),
+       (u32x4){pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])});
+}
+
+// Groups [g_begin, g_end) of a vector-path shard, one workgroup-wide tile of
+// kBlock groups at a time starting at tile index `tile0` and stepping by
+// `tstep` tiles.  G0(r) returns replica r's unadvanced base pointer.
+template <int NT, class GP0>
+__device__ __forceinline__ void tiles(GP0 G0, int N, int64_t g_begin, int64_t g_end, int64_t tile0, int64_t tstep,
+                                      const FlatShape& s, const Scalars& c) {
+  const uint32_t lane = threadIdx.x * 8u;
+  for (int64_t t = tile0;; t += tstep) {
+    const int64_t gt = g_begin + t * kBlock;  // first group of the tile
+    if (gt >= g_end) break;
+    const int64_t e0 = s.head + 8 * gt;
+    auto G = [&](int r) { return tile_base(G0(r) + e0); };
+    if (gt + threadIdx.x < g_end) group_step<NT>(G, N, e0, lane, s, c);
+  }
+}
+
+// One element, any alignment: the same operations as group_step.
+template <class GP>
+__device__ __forceinline__ void elem_step(GP G, int N, int64_t i, const FlatShape& s, const Scalars& c) {
+  float acc = bf_one(G(0)[i]);
+  for (int r = 1; r < N; ++r) acc = acc + bf_one(G(r)[i]);
+  float p = s.p[i], m = s.m[i], v = s.v[i];
+  adam(mean_of<0>(acc, c), p, m, v, c);
+  s.p[i] = p;
+  s.m[i] = m;
+  s.v[i] = v;
+  s.b[i] = to_bf16(p);
+}
+
+// Head and tail elements of a vector-path shard: thread t < head + tail.
+template <class GP>
+__device__ __forceinline__ void edge_step(GP G, int N, int t, const FlatShape& s, const Scalars& c) {
+  const int64_t tail = s.n - s.head - 8 * s.nvec;
+  if (t < s.head)
+    elem_step(G, N, t, s, c);
+  else if (t < s.head + tail)
+    elem_step(G, N, s.head + 8 * s.nvec + (t - s.head), s, c);
+}
+
+template <int NT>
+struct FlatArgs {
+  const uint16_t* g[NT > 0 ? NT : ZS_MAX_REPLICAS];
+  FlatShape s;
+  Scalars c;
+};
+
+template <int NT>
+__global__ __launch_bounds__(kBlock) void flat_kernel(const FlatArgs<NT> a) {
+  const int N = NT > 0 ? NT : a.c.n_rep;
+  if (!a.s.scalar_only) {
+    auto G0 = [&](int r) { return a.g[r]; };
+    tiles<NT>(G0, N, 0, a.s.nvec, blockIdx.x, gridDim.x, a.s, a.c);
+    auto G = [&](int r) { return a.g[r]; };
+    if (blockIdx.x == gridDim.x - 1) edge_step(G, N, threadIdx.x, a.s, a.c);
+  } else {
+    auto G = [&](int r) { return a.g[r]; };
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < a.s.n; i += stride) elem_step(G, N, i, a.s, a.c);
+  }
+}
+
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+}
+
+template <class T>
+__device__ __forceinline__ T* uniform_fptr(T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Ragged list: each workgroup takes chunks; per chunk it stages the owning
+// tensor's descriptor and its N replica pointers into LDS, then runs the same
+// group/element code as the flat kernel over the chunk.
+template <int NT>
+__global__ __launch_bounds__(kBlock) void list_kernel(const ListChunk* __restrict__ chunks, int32_t n_chunks,
+                                                      const ListTensor* __restrict__ tensors,
+                                                      const uint16_t* const* __restrict__ gptrs, const Scalars c) {
+  constexpr int kMaxN = NT > 0 ? NT : ZS_MAX_REPLICAS;
+  __shared__ int64_t s_tensor[8];
+  __shared__ const uint16_t* s_g[kMaxN];
+  const int N = NT > 0 ? NT : c.n_rep;
+  for (int32_t ci = blockIdx.x; ci < n_chunks; ci += gridDim.x) {
+    const ListChunk ch = chunks[ci];
+    const int32_t t = ch.tensor;
+    if (threadIdx.x < 8) s_tensor[threadIdx.x] = reinterpret_cast<const int64_t*>(tensors + t)[threadIdx.x];
+    for (int r = threadIdx.x; r < N; r += kBlock) s_g[r] = gptrs[(int64_t)t * N + r];
+    __syncthreads();
+    FlatShape s;
+    s.p = uniform_fptr(reinterpret_cast<float*>(s_tensor[0]));
+    s.m = uniform_fptr(reinterpret_cast<float*>(s_tensor[1]));
+    s.v = uniform_fptr(reinterpret_cast<float*>(s_tensor[2]));
+    s.b = uniform_fptr(reinterpret_cast<uint16_t*>(s_tensor[3]));
+    s.n = uniform_i64(s_tensor[4]);
+    s.head = uniform_i64(s_tensor[5]);
+    s.nvec = uniform_i64(s_tensor[6]);
+    s.scalar_only = (int32_t)uniform_i64(s_tensor[7] & 0xFFFFFFFF);
+    auto G = [&](int r) { return uniform_ptr(s_g[r]); };
+    if (!s.scalar_only) {
+      tiles<NT>(G, N, ch.begin, ch.end, 0, 1, s, c);
+      if (ch.first) edge_step(G, N, threadIdx.x, s, c);
+    } else {
+      for (int64_t i = ch.begin + threadIdx.x; i < ch.end; i += kBlock) elem_step(G, N, i, s, c);
+    }
+    __syncthreads();  // the next chunk overwrites the staged descriptor
+  }
+}
+
+int clamp_grid(int blocks, int64_t work) {
+  int64_t need = (work + kBlock - 1) / kBlock;
+  if (need < 1) need = 1;
+  return (int)(blocks < need ? blocks : need);
+}
+
+template <int NT>
+hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, int blocks,
+                   hipStream_t stream) {
+  FlatArgs<NT> a;
+  for (int r = 0; r < c.n_rep; ++r) a.g[r] = grads[r];
+  a.s = s;
+  a.c = c;
+  const int grid = clamp_grid(blocks, s.scalar_only ? s.n : s.nvec);
+  (void)hipGetLastError();
+  flat_kernel<NT><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int NT>
+hipError_t go_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
+                   const uint16_t* const* gptrs, const Scalars& c, int blocks, hipStream_t stream) {
+  const int grid = blocks < n_chunks ? blocks : n_chunks;
+  (void)hipGetLastError();
+  list_kernel<NT><<<dim3(grid), dim3(kBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, c);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, int blocks,
+                       hipStream_t stream) {
+  switch (c.n_rep) {
+    case 1: return go_flat<1>(grads, s, c, blocks, stream);
+    case 2: return go_flat<2>(grads, s, c, blocks, stream);
+    case 4: return go_flat<4>(grads, s, c, blocks, stream);
+    case 8: return go_flat<8>(grads, s, c, blocks, stream);
+    case 16: return go_flat<16>(grads, s, c, blocks, stream);
+    case 32: return go_flat<32>(grads, s, c, blocks, stream);
+    case 64: return go_flat<64>(grads, s, c, blocks, stream);
+    default: return go_flat<0>(grads, s, c, blocks, stream);
+  }
+}
+
+hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
+                       const uint16_t* const* gptrs, const Scalars& c, int blocks, hipStream_t stream) {
+  switch (c.n_rep) {
+    case 1: return go_list<1>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
+    case 2: return go_list<2>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
+    case 4: return go_list<4>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
+    case 8: return go_list<8>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
+    case 16: return go_list<16>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
+    case 32: return go_list<32>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
+    case 64: return go_list<64>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
+    default: return go_list<0>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
+  }
+}
+
+}  // namespace zs

@@ -13,10 +13,14 @@ def build(verbose: bool = False) -> None:
          "-o", os.path.join(HERE, "libsynth_host.so")],
         ["hipcc", *HIP_FLAGS, os.path.join(HERE, "synth_dev.hip"), "-o", os.path.join(HERE, "libsynth_dev.so")],
     ]
+    noise = "is not a recognized feature for this target"
     for cmd in cmds:
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True, stderr=subprocess.PIPE if not verbose else None)
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        msgs = [l for l in r.stdout.splitlines() if noise not in l]
+        if r.returncode != 0:
+            raise RuntimeError("build failed:\n" + "\n".join(msgs))
 
 
 if __name__ == "__main__":

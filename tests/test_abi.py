@@ -1,0 +1,147 @@
+"""The C-ABI library without a GPU: it loads, exports what the header
+declares, folds scalars exactly as specified, and rejects bad arguments before
+touching the HIP runtime."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sharded_mixed_precision_rank_amd as zs
+from tests import pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zshard.h")
+
+
+def declared_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    return sorted(set(re.findall(r"ZS_API\s+[\w\s\*]+?\b(zs_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("zs_reduce_adam_flat", "zs_reduce_adam_list", "zs_list_plan_create", "zs_reduce_adam_list_plan",
+                 "zs_list_plan_destroy", "zs_fold", "zs_last_error", "zs_status_string", "zs_abi_version"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(zs.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libzshard.so does not export {name}"
+
+
+def test_only_the_abi_is_exported():
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", zs.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
+    text_syms = [l.split()[-1] for l in out.splitlines() if " T " in l]
+    assert sorted(text_syms) == declared_functions()
+
+
+def test_abi_version():
+    assert zs.abi_version() == 1
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+@pytest.mark.parametrize("t", [1, 2, 100, 1000, 5000, 10000])
+def test_fold_matches_definition_and_oracle(orc, wd, t):
+    hp = dict(pins.HP, weight_decay=wd)
+    got = zs.fold(hp, t)
+    b1, b2 = hp["beta1"], hp["beta2"]
+    want = dict(b1=b1, c1=1.0 - b1, b2=b2, c2=1.0 - b2, eps=hp["eps"], ss=hp["lr"] / (1.0 - b1 ** t),
+                rb=1.0 / math.sqrt(1.0 - b2 ** t), dk=1.0 - hp["lr"] * wd)
+    for k, x in want.items():
+        assert got[k] == pins.f32(x), k
+    assert [got[k] for k in ("b1", "c1", "b2", "c2", "eps", "ss", "rb", "dk")] == [float(x) for x in orc.fold(hp, t)]
+
+
+def _flat(lib, ptrs, N, n, p, m, v, b, hp, step):
+    tab = (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
+    h = zs.AdamHPStruct(*[hp[k] for k in ("lr", "beta1", "beta2", "eps", "weight_decay")])
+    return lib.zs_reduce_adam_flat(tab, N, n, p, m, v, b, ctypes.byref(h), step, None)
+
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+# fake, never dereferenced: every call below fails validation before any HIP call
+A = 0x7F0000000000
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(N=0), "ZS_ERR_RANGE"),
+    (dict(N=257), "ZS_ERR_RANGE"),
+    (dict(n=-1), "ZS_ERR_RANGE"),
+    (dict(step=0), "ZS_ERR_RANGE"),
+    (dict(hp=dict(HP, beta1=1.0)), "ZS_ERR_RANGE"),
+    (dict(hp=dict(HP, beta2=-0.1)), "ZS_ERR_RANGE"),
+    (dict(hp=dict(HP, eps=0.0)), "ZS_ERR_RANGE"),
+    (dict(hp=dict(HP, lr=float("nan"))), "ZS_ERR_RANGE"),
+    (dict(hp=dict(HP, weight_decay=-1.0)), "ZS_ERR_RANGE"),
+    (dict(p=0), "ZS_ERR_NULL"),
+    (dict(ptrs=[A + 0x100000, 0]), "ZS_ERR_NULL"),
+    (dict(p=A + 2), "ZS_ERR_ALIGN"),
+    (dict(b=A + 0x300001), "ZS_ERR_ALIGN"),
+    (dict(ptrs=[A + 0x100001, A + 0x200000]), "ZS_ERR_ALIGN"),
+    (dict(m=A + 0x10), "ZS_ERR_ALIAS"),                       # m overlaps master
+    (dict(b=A + 0x100000 + 64), "ZS_ERR_ALIAS"),              # copy overlaps grad 0
+    (dict(v=A + 0x200000 - 16), "ZS_ERR_ALIAS"),              # v runs into grad 1
+])
+def test_flat_rejects_bad_arguments_without_gpu(case, status):
+    lib = zs.library()
+    n = 1024
+    args = dict(ptrs=[A + 0x100000, A + 0x200000], N=2, n=n, p=A, m=A + 0x10000, v=A + 0x20000, b=A + 0x30000,
+                hp=HP, step=1)
+    args.update(case)
+    if "ptrs" in case and "N" not in case:
+        args["N"] = len(case["ptrs"])
+    st = _flat(lib, args["ptrs"], args["N"], args["n"], args["p"], args["m"], args["v"], args["b"], args["hp"],
+               args["step"])
+    assert zs.STATUS[st] == status, zs.library().zs_last_error()
+    assert zs.library().zs_last_error()
+
+
+def test_n_zero_is_a_noop():
+    lib = zs.library()
+    assert _flat(lib, [0, 0], 2, 0, 0, 0, 0, 0, HP, 1) == 0
+
+
+def test_list_plan_rejects_overlaps_without_gpu():
+    lib = zs.library()
+    N = 2
+    g0 = (ctypes.c_void_p * 2)(A + 0x1000000, A + 0x2000000)
+    g1 = (ctypes.c_void_p * 2)(A + 0x1100000, A + 0x2100000)
+    T = (zs.TensorStruct * 2)()
+    T[0] = zs.TensorStruct(100, A, A + 0x1000, A + 0x2000, A + 0x3000, ctypes.cast(g0, ctypes.POINTER(ctypes.c_void_p)))
+    # tensor 1's master overlaps tensor 0's m
+    T[1] = zs.TensorStruct(100, A + 0x1000 + 8, A + 0x5000, A + 0x6000, A + 0x7000,
+                           ctypes.cast(g1, ctypes.POINTER(ctypes.c_void_p)))
+    plan = ctypes.c_void_p()
+    st = lib.zs_list_plan_create(T, 2, N, None, ctypes.byref(plan))
+    assert zs.STATUS[st] == "ZS_ERR_ALIAS" and not plan
+    # a gradient chunk of tensor 1 lying inside tensor 0's copy
+    T[1] = zs.TensorStruct(100, A + 0x8000, A + 0x9000, A + 0xA000, A + 0xB000,
+                           ctypes.cast((ctypes.c_void_p * 2)(A + 0x3000 + 20, A + 0x2100000),
+                                       ctypes.POINTER(ctypes.c_void_p)))
+    st = lib.zs_list_plan_create(T, 2, N, None, ctypes.byref(plan))
+    assert zs.STATUS[st] == "ZS_ERR_ALIAS"
+    st = lib.zs_list_plan_create(T, -1, N, None, ctypes.byref(plan))
+    assert zs.STATUS[st] == "ZS_ERR_RANGE"
+    st = lib.zs_list_plan_create(T, 2, 0, None, ctypes.byref(plan))
+    assert zs.STATUS[st] == "ZS_ERR_RANGE"
+
+
+def test_status_strings():
+    for k, v in zs.STATUS.items():
+        assert zs.library().zs_status_string(k).decode() == v
+
+
+def test_python_binding_refuses_host_tensors():
+    import torch
+
+    g = torch.zeros(8, dtype=torch.bfloat16)
+    p = torch.zeros(8)
+    with pytest.raises(ValueError):
+        zs.reduce_adam_flat([g], p, p.clone(), p.clone(), g.clone(), HP, 1)
