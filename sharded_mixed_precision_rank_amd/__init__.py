@@ -18,6 +18,11 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                       "(there is no fallback implementation)")
 
+# PyTorch-ROCm ships its own HIP runtime (same soname).  Load it first so the
+# library binds to the runtime that owns torch's devices, streams and memory;
+# loading the library first would bring in a second runtime.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 ZS_MAX_REPLICAS = 256

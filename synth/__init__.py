@@ -56,6 +56,8 @@ def _host_lib():
 def _dev_lib():
     global _dev
     if _dev is None:
+        import torch  # noqa: F401  (torch's HIP runtime must be the one in the process)
+
         if not os.path.exists(DEV_LIB):
             raise ImportError(f"{DEV_LIB} is not built; run __graft_entry__.build()")
         lib = ctypes.CDLL(DEV_LIB)
