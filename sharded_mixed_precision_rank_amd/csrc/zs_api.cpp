@@ -171,7 +171,7 @@ int auto_blocks() {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    cached[dev] = cus * 8;
+    cached[dev] = 1 << 30;  // one tile per workgroup: measured best; the loop covers any remainder
   }
   return cached[dev];
 }

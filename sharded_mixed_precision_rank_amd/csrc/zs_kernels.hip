@@ -38,6 +38,7 @@ namespace zs {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -121,36 +122,62 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], const u32x4 w) {
   acc[7] = acc[7] + bf_hi(w.w);
 }
 
-// Replica pointer tables: each call of G(r) yields replica r's gradient base
-// already advanced to the current tile (wave-uniform, so it lives in SGPRs),
-// and every load adds the lane's 32-bit byte offset within the tile.
-template <class GP>
-__device__ __forceinline__ u32x4 ld_grad(GP G, int r, uint32_t lane) {
-  return ld_g((const GLB u32x4*)at(G(r), here(lane) * 2u));
+// Lane layouts of an 8-parameter group inside a tile of kBlock groups.
+//  Split (full tiles): lane l of wave q owns the quads at tile elements
+//    512q + 4l and 512q + 256 + 4l.  Every access instruction of a wave then
+//    covers whole contiguous lines: 1 KiB per fp32 access, 512 B per bf16
+//    access (8 bytes per lane).  Writes in particular go out as full lines.
+//  Contiguous (the one partial tile of a shard): thread t owns the 8
+//    elements 8t..8t+7; used where only a prefix of the tile's groups exists.
+template <bool SPLIT>
+struct Layout {
+  static __device__ __forceinline__ uint32_t first() {
+    return SPLIT ? 512u * (threadIdx.x >> 6) + 4u * (threadIdx.x & 63u) : 8u * threadIdx.x;
+  }
+  static constexpr uint32_t kSecond = SPLIT ? 256u : 4u;  // element distance to the 2nd quad
+};
+
+// Replica r's 8 bf16 values of this lane's group.  G(r) is replica r's
+// gradient pointer advanced to the tile (wave-uniform, SGPRs); `e` is the
+// lane's first element in the tile.
+template <bool SPLIT, class GP>
+__device__ __forceinline__ u32x4 ld_grad(GP G, int r, uint32_t e) {
+  if constexpr (SPLIT) {
+    const GLB u32x2* a = (const GLB u32x2*)at(G(r), here(e) * 2u);
+    const u32x2 x = ld_g(a), y = ld_g(a + Layout<true>::kSecond / 4);
+    return (u32x4){x.x, x.y, y.x, y.y};
+  } else {
+    return ld_g((const GLB u32x4*)at(G(r), here(e) * 2u));
+  }
 }
 
-template <class GP>
-__device__ __forceinline__ void load_batch(GP G, int r, int N, uint32_t lane, u32x4 (&w)[kBatch]) {
+template <bool SPLIT, class GP>
+__device__ __forceinline__ void load_batch(GP G, int r, int N, uint32_t e, u32x4 (&w)[kBatch]) {
 #pragma unroll
   for (int j = 0; j < kBatch; ++j)
-    if (r + j < N) w[j] = ld_grad(G, r + j, lane);
+    if (r + j < N) w[j] = ld_grad<SPLIT>(G, r + j, e);
 }
 
+// Adds a batch, then pins the accumulators: the sums must be formed here, not
+// sunk towards their use after the last batch (which would keep every loaded
+// batch live at once).
 __device__ __forceinline__ void add_batch(float (&acc)[8], const u32x4 (&w)[kBatch], int r, int N) {
 #pragma unroll
   for (int j = 0; j < kBatch; ++j)
     if (r + j < N) accumulate(acc, w[j]);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(acc[k]));
 }
 
-// acc[k] = sum over replicas r = 0..N-1, in that order, of element lane+k.
-// Replicas 1..N-1 stream in batches of kBatch loads; the next batch is in
-// flight while the current one is added (two register buffers), and
-// scheduling barriers stop the compiler from hoisting later batches, which
-// would buy nothing but registers.
-template <int NT, class GP>
-__device__ __forceinline__ void reduce_replicas(GP G, int N, uint32_t lane, float (&acc)[8]) {
+// acc[k] = sum over replicas r = 0..N-1, in that order, of element k of the
+// lane's group.  Replicas 1..N-1 stream in batches of kBatch loads; the next
+// batch is in flight while the current one is added (two register buffers),
+// and scheduling barriers stop the compiler from hoisting later batches,
+// which would buy nothing but registers.
+template <int NT, bool SPLIT, class GP>
+__device__ __forceinline__ void reduce_replicas(GP G, int N, uint32_t e, float (&acc)[8]) {
   {
-    const u32x4 w = ld_grad(G, 0, lane);
+    const u32x4 w = ld_grad<SPLIT>(G, 0, e);
     acc[0] = bf_lo(w.x);
     acc[1] = bf_hi(w.x);
     acc[2] = bf_lo(w.y);
@@ -161,28 +188,27 @@ __device__ __forceinline__ void reduce_replicas(GP G, int N, uint32_t lane, floa
     acc[7] = bf_hi(w.w);
   }
   if constexpr (NT > 0) {
-    // fully unrolled: batch k+1 is issued before batch k is added
     constexpr int NB = (NT - 1 + kBatch - 1) / kBatch;
     u32x4 w[2][kBatch];
-    if constexpr (NB > 0) load_batch(G, 1, NT, lane, w[0]);
+    if constexpr (NB > 0) load_batch<SPLIT>(G, 1, NT, e, w[0]);
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      if (k + 1 < NB) load_batch(G, 1 + (k + 1) * kBatch, NT, lane, w[(k + 1) & 1]);
+      if (k + 1 < NB) load_batch<SPLIT>(G, 1 + (k + 1) * kBatch, NT, e, w[(k + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
       add_batch(acc, w[k & 1], 1 + k * kBatch, NT);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     u32x4 wa[kBatch], wb[kBatch];
-    if (N > 1) load_batch(G, 1, N, lane, wa);
+    if (N > 1) load_batch<SPLIT>(G, 1, N, e, wa);
 #pragma unroll 1
     for (int r0 = 1; r0 < N; r0 += 2 * kBatch) {
       const int r1 = r0 + kBatch, r2 = r1 + kBatch;
-      if (r1 < N) load_batch(G, r1, N, lane, wb);
+      if (r1 < N) load_batch<SPLIT>(G, r1, N, e, wb);
       __builtin_amdgcn_sched_barrier(0);
       add_batch(acc, wa, r0, N);
       __builtin_amdgcn_sched_barrier(0);
-      if (r2 < N) load_batch(G, r2, N, lane, wa);
+      if (r2 < N) load_batch<SPLIT>(G, r2, N, e, wa);
       __builtin_amdgcn_sched_barrier(0);
       if (r1 < N) add_batch(acc, wb, r1, N);
       __builtin_amdgcn_sched_barrier(0);
@@ -190,29 +216,29 @@ __device__ __forceinline__ void reduce_replicas(GP G, int N, uint32_t lane, floa
   }
 }
 
-// One 8-parameter group: element e0 + lane of every array, where e0 is the
-// wave-uniform tile start (16-byte aligned in every array) and lane < 2^29 is
-// this thread's element offset within the tile.  G(r) returns replica r's
-// gradient pointer advanced to e0.
-template <int NT, class GP>
-__device__ __forceinline__ void group_step(GP G, int N, int64_t e0, uint32_t lane, const FlatShape& s,
-                                           const Scalars& c) {
+// One 8-parameter group of the tile starting at element e0 (wave-uniform,
+// 16-byte aligned in every array).  G(r) returns replica r's gradient pointer
+// advanced to e0.
+template <int NT, bool SPLIT, class GP>
+__device__ __forceinline__ void group_step(GP G, int N, int64_t e0, const FlatShape& s, const Scalars& c) {
+  constexpr uint32_t q2 = Layout<SPLIT>::kSecond / 4;  // second quad, in f32x4 units
+  const uint32_t e = Layout<SPLIT>::first();
   f32x4 pa, pb, ma, mb, va, vb;
   {
-    const uint32_t lb4 = here(lane) * 4u;  // byte offset in fp32 arrays
-    const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(s.p + e0), lb4);
-    const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(s.m + e0), lb4);
-    const GLB f32x4* V4 = (const GLB f32x4*)at(tile_base(s.v + e0), lb4);
+    const uint32_t o = here(e) * 4u;  // byte offset in fp32 arrays
+    const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(s.p + e0), o);
+    const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(s.m + e0), o);
+    const GLB f32x4* V4 = (const GLB f32x4*)at(tile_base(s.v + e0), o);
     pa = ld_g(P4);
-    pb = ld_g(P4 + 1);
+    pb = ld_g(P4 + q2);
     ma = ld_g(M4);
-    mb = ld_g(M4 + 1);
+    mb = ld_g(M4 + q2);
     va = ld_g(V4);
-    vb = ld_g(V4 + 1);
+    vb = ld_g(V4 + q2);
   }
 
   float acc[8];
-  reduce_replicas<NT>(G, N, lane, acc);
+  reduce_replicas<NT, SPLIT>(G, N, e, acc);
 
   float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
   float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
@@ -221,33 +247,42 @@ __device__ __forceinline__ void group_step(GP G, int N, int64_t e0, uint32_t lan
   for (int k = 0; k < 8; ++k) adam(mean_of<NT>(acc[k], c), p[k], m[k], v[k], c);
 
   // addresses recomputed here so they stay SGPR base + 32-bit lane offset
-  const uint32_t lb4 = here(lane) * 4u;
-  GLB f32x4* P4 = (GLB f32x4*)at(tile_base(s.p + e0), lb4);
-  GLB f32x4* M4 = (GLB f32x4*)at(tile_base(s.m + e0), lb4);
-  GLB f32x4* V4 = (GLB f32x4*)at(tile_base(s.v + e0), lb4);
+  const uint32_t o = here(e) * 4u;
+  GLB f32x4* P4 = (GLB f32x4*)at(tile_base(s.p + e0), o);
+  GLB f32x4* M4 = (GLB f32x4*)at(tile_base(s.m + e0), o);
+  GLB f32x4* V4 = (GLB f32x4*)at(tile_base(s.v + e0), o);
   st_g(P4, (f32x4){p[0], p[1], p[2], p[3]});
-  st_g(P4 + 1, (f32x4){p[4], p[5], p[6], p[7]});
+  st_g(P4 + q2, (f32x4){p[4], p[5], p[6], p[7]});
   st_g(M4, (f32x4){m[0], m[1], m[2], m[3]});
-  st_g(M4 + 1, (f32x4){m[4], m[5], m[6], m[7]});
+  st_g(M4 + q2, (f32x4){m[4], m[5], m[6], m[7]});
   st_g(V4, (f32x4){v[0], v[1], v[2], v[3]});
-  st_g(V4 + 1, (f32x4){v[4], v[5], v[6], v[7]});
-  st_g((GLB u32x4*)at(tile_base(s.b + e0), here(lane) * 2u),
-       (u32x4){pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])});
+  st_g(V4 + q2, (f32x4){v[4], v[5], v[6], v[7]});
+  if constexpr (SPLIT) {
+    GLB u32x2* B2 = (GLB u32x2*)at(tile_base(s.b + e0), here(e) * 2u);
+    st_g(B2, (u32x2){pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])});
+    st_g(B2 + Layout<true>::kSecond / 4, (u32x2){pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])});
+  } else {
+    st_g((GLB u32x4*)at(tile_base(s.b + e0), here(e) * 2u),
+         (u32x4){pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])});
+  }
 }
 
 // Groups [g_begin, g_end) of a vector-path shard, one workgroup-wide tile of
 // kBlock groups at a time starting at tile index `tile0` and stepping by
-// `tstep` tiles.  G0(r) returns replica r's unadvanced base pointer.
+// `tstep` tiles.  G0(r) returns replica r's unadvanced base pointer.  Whole
+// tiles use the split layout; the last, partial tile the contiguous one.
 template <int NT, class GP0>
 __device__ __forceinline__ void tiles(GP0 G0, int N, int64_t g_begin, int64_t g_end, int64_t tile0, int64_t tstep,
                                       const FlatShape& s, const Scalars& c) {
-  const uint32_t lane = threadIdx.x * 8u;
   for (int64_t t = tile0;; t += tstep) {
     const int64_t gt = g_begin + t * kBlock;  // first group of the tile
     if (gt >= g_end) break;
     const int64_t e0 = s.head + 8 * gt;
     auto G = [&](int r) { return tile_base(G0(r) + e0); };
-    if (gt + threadIdx.x < g_end) group_step<NT>(G, N, e0, lane, s, c);
+    if (gt + kBlock <= g_end)
+      group_step<NT, true>(G, N, e0, s, c);
+    else if (gt + threadIdx.x < g_end)
+      group_step<NT, false>(G, N, e0, s, c);
   }
 }
 
