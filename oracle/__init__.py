@@ -22,6 +22,11 @@ class OracleHP(ctypes.Structure):
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
 
 
+class OracleScaler(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_double), ("min_scale", ctypes.c_double), ("window", ctypes.c_int64),
+                ("hysteresis", ctypes.c_int64), ("overflows", ctypes.c_int64), ("clean", ctypes.c_int64)]
+
+
 def _hp(hp: dict) -> OracleHP:
     return OracleHP(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp.get("weight_decay", 0.0))
 
@@ -47,6 +52,20 @@ class Oracle:
         lib.oracle_reduce_mean.argtypes = [vp, i32, i64, vp, i32]
         lib.oracle_reduce_adam.restype = ctypes.c_int
         lib.oracle_reduce_adam.argtypes = [vp, i32, i64, vp, vp, vp, vp, ctypes.POINTER(OracleHP), i64, i32]
+        lib.oracle_f32_to_f16_array.argtypes = [vp, vp, i64]
+        lib.oracle_f16_to_f32.restype = ctypes.c_float
+        lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.oracle_reduce_unscale.restype = ctypes.c_int
+        lib.oracle_reduce_unscale.argtypes = [vp, i32, i64, i32, ctypes.c_double, vp, i32]
+        lib.oracle_sqnorm.restype = ctypes.c_double
+        lib.oracle_sqnorm.argtypes = [vp, i64]
+        lib.oracle_clip_coef.restype = ctypes.c_float
+        lib.oracle_clip_coef.argtypes = [ctypes.c_double, ctypes.c_double]
+        lib.oracle_adam_from_gbar.restype = ctypes.c_int
+        lib.oracle_adam_from_gbar.argtypes = [vp, i64, vp, vp, vp, vp, i32, ctypes.POINTER(OracleHP), i64,
+                                              ctypes.c_double, ctypes.c_double, i32, i32]
+        lib.oracle_scaler_update.restype = ctypes.c_int
+        lib.oracle_scaler_update.argtypes = [ctypes.POINTER(OracleScaler), i32]
         lib.oracle_state_bytes_per_param.restype = i64
         lib.oracle_sharded_state_bytes.restype = ctypes.c_double
         lib.oracle_sharded_state_bytes.argtypes = [ctypes.c_double, i32]
@@ -97,6 +116,54 @@ class Oracle:
         B1 = np.empty(P1.size, dtype=np.uint16)
         self.step_inplace(G, P1, M1, V1, B1, hp, t, threads)
         return P1, M1, V1, B1
+
+    # ---- two-pass form (clipping, fp16 loss scaling)
+    def f16(self, x) -> np.ndarray:
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, dtype=np.uint16)
+        self.lib.oracle_f32_to_f16_array(x.ctypes.data, out.ctypes.data, x.size)
+        return out
+
+    def f16_to_f32(self, h) -> np.ndarray:
+        return np.array([self.lib.oracle_f16_to_f32(int(v)) for v in np.asarray(h).ravel()], dtype=np.float32)
+
+    def reduce_unscale(self, G, fmt: int = 0, loss_scale: float = 1.0, threads: int = 0) -> np.ndarray:
+        tab, rows = _ptr_table(G)
+        n = rows[0].size
+        out = np.empty(n, dtype=np.float32)
+        rc = self.lib.oracle_reduce_unscale(tab, len(rows), n, fmt, loss_scale, out.ctypes.data, threads)
+        if rc:
+            raise ValueError("oracle_reduce_unscale: bad arguments")
+        return out
+
+    def sqnorm(self, gbar) -> float:
+        g = np.ascontiguousarray(gbar, dtype=np.float32)
+        return float(self.lib.oracle_sqnorm(g.ctypes.data, g.size))
+
+    def clip_coef(self, total_sq: float, max_norm: float) -> float:
+        return float(self.lib.oracle_clip_coef(total_sq, max_norm))
+
+    def adam_from_gbar(self, gbar, P, M, V, hp: dict, t: int, total_sq: float, max_norm: float = 0.0,
+                       out_fmt: int = 0, skip_nonfinite: bool = True, threads: int = 0):
+        """Functional pass 2: returns (P1, M1, V1, B1, taken)."""
+        g = np.ascontiguousarray(gbar, dtype=np.float32)
+        P1 = np.array(P, dtype=np.float32, copy=True)
+        M1 = np.array(M, dtype=np.float32, copy=True)
+        V1 = np.array(V, dtype=np.float32, copy=True)
+        B1 = np.zeros(P1.size, dtype=np.uint16)
+        h = _hp(hp)
+        rc = self.lib.oracle_adam_from_gbar(g.ctypes.data, g.size, P1.ctypes.data, M1.ctypes.data, V1.ctypes.data,
+                                            B1.ctypes.data, out_fmt, ctypes.byref(h), t, total_sq, max_norm,
+                                            int(skip_nonfinite), threads)
+        if rc == 1:
+            raise ValueError("oracle_adam_from_gbar: bad arguments")
+        return P1, M1, V1, B1, rc == 0
+
+    def scaler(self, scale: float = 2.0 ** 16, min_scale: float = 1.0, window: int = 1000, hysteresis: int = 2):
+        return OracleScaler(scale, min_scale, window, hysteresis, 0, 0)
+
+    def scaler_update(self, st: "OracleScaler", overflow: bool) -> bool:
+        return bool(self.lib.oracle_scaler_update(ctypes.byref(st), int(overflow)))
 
     def state_bytes_per_param(self) -> int:
         return int(self.lib.oracle_state_bytes_per_param())

@@ -40,6 +40,22 @@
 //  3. bf16 re-cast of the new master (round to nearest even; NaN stays NaN):
 //     the working copy the next parameter all-gather would ship (ZeRO-3 page,
 //     §5, forward all-gather of every layer's shards).
+//
+// Two-pass form (global-norm gradient clipping and fp16 dynamic loss scaling,
+// both set in the ZeRO-3 page's §8 DeepSpeed config: gradient_clipping, and the
+// fp16 block with a dynamic loss scale):
+//  pass 1  g_i = (s_i / N) * u, s_i the rank-ordered sum above, u = f32(1/S)
+//          for loss scale S (1 when not scaling); gradients bf16 or fp16.
+//          total_sq = sum over i of (double)g_i^2, in double, index order.
+//  pass 2  if total_sq is not finite (overflow) the step is skipped: nothing
+//          changes.  Otherwise, with c = max_norm / (sqrt(total_sq) + 1e-6) in
+//          double and k = f32(min(c, 1)) (k = 1 without clipping), the update
+//          above runs on g_i * k (one fp32 multiply) and writes the working copy
+//          as bf16 or fp16 (round to nearest even).
+//  scaler  dynamic loss scale: on overflow the scale halves (not below the
+//          minimum) once `hysteresis` overflows have been seen since the last
+//          change, and the step is skipped; after `window` consecutive clean
+//          steps the scale doubles and the overflow count restarts.
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -70,6 +86,52 @@ uint16_t to_bf16(float x) {
   uint32_t lsb = (u >> 16) & 1u;
   return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
 }
+
+// IEEE binary16 -> binary32 (exact).
+float half_to_f32(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h >> 15) << 31;
+  const int exp = (h >> 10) & 0x1F;
+  const uint32_t man = h & 0x3FF;
+  uint32_t u;
+  if (exp == 0x1F) {
+    u = sign | 0x7F800000u | (man << 13);  // Inf or NaN
+  } else if (exp != 0) {
+    u = sign | ((uint32_t)(exp - 15 + 127) << 23) | (man << 13);
+  } else if (man == 0) {
+    u = sign;
+  } else {  // subnormal: value = man * 2^-24
+    float f = (float)man * 0x1p-24f;
+    std::memcpy(&u, &f, 4);
+    u |= sign;
+  }
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// binary32 -> binary16, round to nearest even (overflow to Inf, NaN stays NaN).
+uint16_t to_f16(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return (uint16_t)(sign | 0x7E00u);  // NaN
+  if (a >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u);  // rounds to >= 65520: Inf
+  if (a < 0x38800000u) {                                     // below 2^-14: subnormal or zero in binary16
+    // value / 2^-24, rounded to nearest even integer
+    float f;
+    std::memcpy(&f, &a, 4);
+    const float q = f * 0x1p24f;  // exact: a power-of-two scale of a normal or subnormal binary32
+    float r = std::nearbyint(q);  // default rounding mode: to nearest even
+    return (uint16_t)(sign | (uint16_t)r);
+  }
+  // normal binary16: drop 13 mantissa bits with round to nearest even, re-bias the exponent
+  const uint32_t lsb = (a >> 13) & 1u;
+  const uint32_t r = (a + 0xFFFu + lsb) >> 13;  // may carry into the exponent
+  return (uint16_t)(sign | (uint16_t)(r - ((uint32_t)(127 - 15) << 10)));
+}
+
+float widen_fmt(uint16_t h, int fmt) { return fmt ? half_to_f32(h) : widen(h); }
 
 struct Folded {
   float b1, c1, b2, c2, e, ss, rb, dk;
@@ -168,6 +230,94 @@ int oracle_reduce_adam(const uint16_t* const* G, int32_t N, int64_t n, float* P,
 // (the Data Parallelism page's appendix; the same 16 as the 2+2+4+4+4 of the
 // Distributed-training chapter's §2): fp32 master + bf16 working copy + bf16
 // gradient + fp32 momentum + fp32 variance.
+uint16_t oracle_f32_to_f16(float x) { return to_f16(x); }
+float oracle_f16_to_f32(uint16_t h) { return half_to_f32(h); }
+
+void oracle_f32_to_f16_array(const float* x, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = to_f16(x[i]);
+}
+
+// Pass 1: gbar[i] = (s_i / N) * f32(1/loss_scale); fmt 0 = bf16 grads, 1 = fp16.
+int oracle_reduce_unscale(const uint16_t* const* G, int32_t N, int64_t n, int32_t fmt, double loss_scale,
+                          float* gbar, int32_t threads) {
+  if (N < 1 || n < 0 || !(loss_scale > 0)) return 1;
+  const float inv = (float)(1.0 / loss_scale);
+  parallel_ranges(n, threads, [&](int64_t lo, int64_t hi) {
+    for (int64_t i = lo; i < hi; ++i) {
+      float s = widen_fmt(G[0][i], fmt);
+      for (int32_t r = 1; r < N; ++r) s = s + widen_fmt(G[r][i], fmt);
+      gbar[i] = (s / (float)N) * inv;
+    }
+  });
+  return 0;
+}
+
+// Squared L2 norm of gbar: sum of (double)gbar[i]^2 in double, in index order.
+double oracle_sqnorm(const float* gbar, int64_t n) {
+  double acc = 0.0;
+  for (int64_t i = 0; i < n; ++i) acc += (double)gbar[i] * (double)gbar[i];
+  return acc;
+}
+
+// Clip coefficient: f32(min(max_norm / (sqrt(total_sq) + 1e-6), 1)); 1 when max_norm <= 0.
+float oracle_clip_coef(double total_sq, double max_norm) {
+  if (!(max_norm > 0)) return 1.0f;
+  const double c = max_norm / (std::sqrt(total_sq) + 1e-6);
+  return (float)(c < 1.0 ? c : 1.0);
+}
+
+// Pass 2: the update on g_i * coef; out_fmt 0 = bf16 working copy, 1 = fp16.
+// Returns 2 (and changes nothing) when skip_nonfinite and total_sq is not finite.
+int oracle_adam_from_gbar(const float* gbar, int64_t n, float* P, float* M, float* V, uint16_t* B, int32_t out_fmt,
+                          const oracle_hp* hp, int64_t t, double total_sq, double max_norm, int32_t skip_nonfinite,
+                          int32_t threads) {
+  if (n < 0 || t < 1) return 1;
+  if (skip_nonfinite && !std::isfinite(total_sq)) return 2;
+  const Folded f = fold(*hp, t);
+  const float k = oracle_clip_coef(total_sq, max_norm);
+  parallel_ranges(n, threads, [&](int64_t lo, int64_t hi) {
+    for (int64_t i = lo; i < hi; ++i) {
+      const float g = gbar[i] * k;
+      float m1 = f.b1 * M[i] + f.c1 * g;
+      float v1 = f.b2 * V[i] + f.c2 * (g * g);
+      float d = std::sqrt(v1) * f.rb + f.e;
+      float u = m1 / d;
+      float p1 = f.dk * P[i] - f.ss * u;
+      P[i] = p1;
+      M[i] = m1;
+      V[i] = v1;
+      B[i] = out_fmt ? to_f16(p1) : to_bf16(p1);
+    }
+  });
+  return 0;
+}
+
+// Dynamic loss scale (fp16 training).  state: {scale, overflows since the last
+// change, clean steps since the last change}.  Returns 1 if the step is taken.
+typedef struct oracle_scaler {
+  double scale, min_scale;
+  int64_t window, hysteresis, overflows, clean;
+} oracle_scaler;
+
+int oracle_scaler_update(oracle_scaler* s, int32_t overflow) {
+  if (overflow) {
+    s->overflows += 1;
+    s->clean = 0;
+    if (s->overflows >= s->hysteresis) {
+      s->scale = s->scale / 2.0 < s->min_scale ? s->min_scale : s->scale / 2.0;
+      s->overflows = 0;
+    }
+    return 0;
+  }
+  s->clean += 1;
+  if (s->clean >= s->window) {
+    s->scale *= 2.0;
+    s->clean = 0;
+    s->overflows = 0;
+  }
+  return 1;
+}
+
 int64_t oracle_state_bytes_per_param(void) { return 4 + 2 + 2 + 4 + 4; }
 
 // Per-device model-state bytes when all of it is sharded over ndp ranks

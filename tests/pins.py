@@ -316,5 +316,151 @@ def pin_folded_scalars(o):
             assert [float(x) for x in got] == [f32(w) for w in want], f"P11: folded scalars wrong at t={t}, wd={wd}"
 
 
+# ---------------------------------------------------------------------- P12
+def pin_f16_casts(o):
+    """binary16 <-> binary32: every one of the 65536 encodings decodes as numpy's
+    float16 does; encoding matches numpy's round-to-nearest-even cast."""
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = allh.view(np.float16).astype(np.float32)
+    got = o.f16_to_f32(allh)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+    rng = np.random.default_rng(112)
+    r = rng.integers(0, 2 ** 32, 4_000_000, dtype=np.uint64).astype(np.uint32)
+    r = r[(r & 0x7F800000) != 0x7F800000]
+    specials = np.array([0x477FEFFF, 0x477FF000, 0x477FE000, 0x33000000, 0x33000001, 0x387FC000, 0x38800000,
+                         0x387FFFFF, 0x7F800000, 0xFF800000, 0x80000000, 0x00000001], dtype=np.uint32)
+    xs = np.concatenate([r, specials]).view(np.float32)
+    with np.errstate(over="ignore"):
+        ref = xs.astype(np.float16).view(np.uint16)
+    assert np.array_equal(o.f16(xs), ref), "P12: fp16 cast differs from numpy's"
+    nanh = o.f16(np.array([np.nan], dtype=np.float32))
+    assert (nanh[0] & 0x7C00) == 0x7C00 and (nanh[0] & 0x3FF)
+
+
+# ---------------------------------------------------------------------- P13
+def pin_two_pass_equals_fused(o):
+    """Without loss scaling or clipping, pass 1 + pass 2 is the fused step, bit for bit."""
+    rng = np.random.default_rng(113)
+    for N in (1, 3, 8):
+        G, P, M, V, hp, t = random_case(rng, N, 4096, True, 17, 0.1, hp=dict(HP, weight_decay=0.1))
+        g = o.reduce_unscale(G, 0, 1.0, threads=1)
+        assert np.array_equal(bits(g), bits(o.reduce_mean(G, threads=1)))
+        ts = o.sqnorm(g)
+        two = o.adam_from_gbar(g, P, M, V, hp, t, ts, 0.0, 0)
+        fused = o.step(G, P, M, V, hp, t, threads=1)
+        assert two[4] and all(np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
+                              for a, b in zip(two[:4], fused)), "P13: two-pass != fused"
+
+
+def pin_unscale_and_fp16_grads(o):
+    """Power-of-two loss scales unscale exactly; fp16 replicas average like bf16 ones."""
+    rng = np.random.default_rng(114)
+    xs = (rng.standard_normal((4, 4096)) * 1e-2).astype(np.float32)
+    H = o.f16(xs)
+    g1 = o.reduce_unscale(H, 1, 1.0, threads=1)
+    for k in (1, 8, 16, 24):
+        gk = o.reduce_unscale(H, 1, float(2 ** k), threads=1)
+        assert np.array_equal(bits(gk), bits(g1 * np.float32(2.0 ** -k))), f"P13: unscale by 2^{k} not exact"
+    dec = np.stack([o.f16_to_f32(h) for h in H]).astype(np.float64)
+    exact = dec.sum(axis=0) / 4                       # fp16 sums of 4 terms are exact in double
+    assert np.all(np.abs(g1 - exact) <= 4 * U * np.abs(dec).sum(axis=0) / 4 + 1e-45)
+    one = o.reduce_unscale([H[0]] * 5, 1, 1.0, threads=1)
+    assert np.array_equal(bits(one), bits(dec[0].astype(np.float32))), "P13: identical fp16 replicas"
+
+
+# ---------------------------------------------------------------------- P14
+def pin_sqnorm(o):
+    import math
+
+    rng = np.random.default_rng(115)
+    g = (rng.standard_normal(100_003) * 1e-3).astype(np.float32)
+    exact = math.fsum(float(x) * float(x) for x in g)      # correctly rounded sum of exact squares
+    got = o.sqnorm(g)
+    assert abs(got - exact) <= g.size * 2.0 ** -53 * exact, "P14: squared norm"
+    c = np.full(1000, np.float32(0.5))
+    assert o.sqnorm(c) == 250.0
+    assert math.isinf(o.sqnorm(np.array([1.0, np.inf], np.float32)))
+    assert math.isnan(o.sqnorm(np.array([1.0, np.nan], np.float32)))
+
+
+# ---------------------------------------------------------------------- P15
+def pin_clipping(o):
+    """Clipping by global norm: coefficient 1 below the threshold (the update is
+    then the unclipped one, bit for bit); above it, agreement with
+    torch.nn.utils.clip_grad_norm_ followed by AdamW, in float64."""
+    import torch
+
+    rng = np.random.default_rng(116)
+    G, P, M, V, hp, t = random_case(rng, 4, 4096, True, 100, 0.1, hp=dict(HP, weight_decay=0.1))
+    g = o.reduce_unscale(G, 0, 1.0, threads=1)
+    ts = o.sqnorm(g)
+    norm = ts ** 0.5
+    assert o.clip_coef(ts, 2 * norm) == 1.0 and o.clip_coef(ts, 0.0) == 1.0
+    a = o.adam_from_gbar(g, P, M, V, hp, t, ts, 2 * norm)
+    b = o.adam_from_gbar(g, P, M, V, hp, t, ts, 0.0)
+    assert all(np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8)) for x, y in zip(a[:4], b[:4]))
+    max_norm = norm / 7
+    k = o.clip_coef(ts, max_norm)
+    want = max_norm / (norm + 1e-6)
+    assert abs(k - want) <= U * want, "P15: clip coefficient"
+    out = o.adam_from_gbar(g, P, M, V, hp, t, ts, max_norm)
+    # torch: clip the float64 average, then AdamW
+    p = torch.nn.Parameter(torch.from_numpy(P.astype(np.float64)))
+    p.grad = torch.from_numpy(g.astype(np.float64))
+    torch.nn.utils.clip_grad_norm_([p], max_norm)
+    opt = torch.optim.AdamW([p], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["weight_decay"], foreach=False, fused=False)
+    st = opt.state[p]
+    st["step"] = torch.tensor(float(t - 1), dtype=torch.float64)
+    st["exp_avg"] = torch.from_numpy(M.astype(np.float64))
+    st["exp_avg_sq"] = torch.from_numpy(V.astype(np.float64))
+    opt.step()
+    gk = (g * np.float32(k)).astype(np.float64)
+    for got, ref, scale in ((out[1], st["exp_avg"].numpy(), np.abs(M) + np.abs(gk)),
+                            (out[2], st["exp_avg_sq"].numpy(), np.abs(V) + gk * gk)):
+        assert np.all(np.abs(got - ref) <= 8 * U * scale + 1e-30), "P15: clipped moments differ from torch"
+    step_ref = p.detach().numpy() - P.astype(np.float64)
+    step_got = out[0].astype(np.float64) - P
+    assert np.all(np.abs(step_got - step_ref) <= 64 * U * np.abs(step_ref) + 2 * ulp32(out[0]) + 2 * ulp32(P)), \
+        "P15: clipped update differs from torch"
+
+
+# ---------------------------------------------------------------------- P16
+def pin_overflow_skips(o):
+    rng = np.random.default_rng(117)
+    G, P, M, V, hp, t = random_case(rng, 2, 1024, True, 5, 0.0)
+    g = o.reduce_unscale(G, 0, 1.0, threads=1)
+    g[7] = np.inf
+    ts = o.sqnorm(g)
+    P1, M1, V1, B1, taken = o.adam_from_gbar(g, P, M, V, hp, t, ts, 1.0)
+    assert not taken and np.array_equal(P1, P) and np.array_equal(M1, M) and np.array_equal(V1, V)
+
+
+# ---------------------------------------------------------------------- P17
+def pin_loss_scaler(o):
+    """The dynamic loss scale of the DeepSpeed fp16 block: start 2^16, window
+    1000, hysteresis 2, minimum 1 (scripted sequence with hand-derived states)."""
+    s = o.scaler(2.0 ** 16, 1.0, 1000, 2)
+    for _ in range(999):
+        assert o.scaler_update(s, False)
+    assert s.scale == 2.0 ** 16
+    assert o.scaler_update(s, False) and s.scale == 2.0 ** 17          # 1000 clean steps: grow
+    assert not o.scaler_update(s, True) and s.scale == 2.0 ** 17       # first overflow: hysteresis holds
+    assert not o.scaler_update(s, True) and s.scale == 2.0 ** 16       # second: halve
+    for _ in range(40):
+        o.scaler_update(s, True)
+    assert s.scale == 1.0                                             # never below the minimum
+    for _ in range(500):
+        o.scaler_update(s, False)
+    assert not o.scaler_update(s, True) and s.scale == 1.0            # the clean run restarts
+    for _ in range(1000):
+        o.scaler_update(s, False)
+    assert s.scale == 2.0
+
+
+TWO_PASS = [pin_f16_casts, pin_two_pass_equals_fused, pin_unscale_and_fp16_grads, pin_sqnorm, pin_clipping,
+            pin_overflow_skips, pin_loss_scaler]
+
 ALL = [pin_identical_replicas, pin_first_step, pin_zero_grad, pin_decoupled_decay, pin_constant_grad_run,
-       pin_memory_accounting, pin_f64_bound, pin_rank_order, pin_bf16_cast, pin_torch_adamw, pin_folded_scalars]
+       pin_memory_accounting, pin_f64_bound, pin_rank_order, pin_bf16_cast, pin_torch_adamw, pin_folded_scalars] + TWO_PASS

@@ -40,6 +40,21 @@ MUTANTS = [
     ("bf16_nan_to_inf", "return 0x7FC0;  // NaN", "return (uint16_t)(u >> 16) & 0xFF80;  // NaN"),
     ("copy_from_wrong_value", "B[i] = to_bf16(p1);", "B[i] = to_bf16(m1);"),
     ("state_bytes_fp32_grad", "return 4 + 2 + 2 + 4 + 4;", "return 4 + 2 + 4 + 4 + 4;"),
+    # two-pass form
+    ("f16_truncates", "const uint32_t r = (a + 0xFFFu + lsb) >> 13;", "const uint32_t r = a >> 13;"),
+    ("f16_subnormal_scale", "const float q = f * 0x1p24f;", "const float q = f * 0x1p23f;"),
+    ("f16_decode_bias", "u = sign | ((uint32_t)(exp - 15 + 127) << 23) | (man << 13);",
+     "u = sign | ((uint32_t)(exp - 16 + 127) << 23) | (man << 13);"),
+    ("unscale_multiplies", "gbar[i] = (s / (float)N) * inv;", "gbar[i] = (s / (float)N) * (float)loss_scale;"),
+    ("norm_not_squared", "acc += (double)gbar[i] * (double)gbar[i];", "acc += std::fabs((double)gbar[i]);"),
+    ("clip_no_min", "return (float)(c < 1.0 ? c : 1.0);", "return (float)c;"),
+    ("clip_no_eps", "const double c = max_norm / (std::sqrt(total_sq) + 1e-6);", "const double c = max_norm / total_sq;"),
+    ("overflow_not_skipped", "if (skip_nonfinite && !std::isfinite(total_sq)) return 2;", ""),
+    ("clip_coef_unused", "const float g = gbar[i] * k;", "const float g = gbar[i];"),
+    ("scaler_no_hysteresis", "if (s->overflows >= s->hysteresis) {", "if (s->overflows >= 1) {"),
+    ("scaler_window_off_by_one", "if (s->clean >= s->window) {", "if (s->clean > s->window) {"),
+    ("scaler_no_floor", "s->scale = s->scale / 2.0 < s->min_scale ? s->min_scale : s->scale / 2.0;",
+     "s->scale = s->scale / 2.0;"),
 ]
 
 
