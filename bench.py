@@ -25,7 +25,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "params/s and achieved HBM GB/s (% of peak) for fused reduce+Adam shard step"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "sharded_mixed_precision_rank_amd", "csrc", "zs_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "sharded_mixed_precision_rank_amd", "csrc", f)
+               for f in ("zs_kernels.hip", "zs_device.h", "zs_internal.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -40,8 +41,12 @@ def workload(name: str):
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the sources the step kernels are built from."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def counter_traffic(w, n_launch_params: int):
@@ -86,6 +91,44 @@ def spot_check(w, d, samples: int, seed: int = 1234) -> dict:
     rep = parity.assert_step(got, dict(P=P, M=M, V=V, B=B), f"{w.name} sampled")
     return dict(samples=int(idx.size), bit_identical=parity.bit_identical(got, dict(P=P, M=M, V=V, B=B)),
                 max_rel=max(rep[k]["max_rel"] for k in "PMV"), max_bf16_ulp=rep["B"]["max_ulp"])
+
+
+def spot_check_two_pass(w, d, samples: int, sq: float, loss_scale: float, gfmt: str, seed: int = 1234) -> dict:
+    """Sampled parity of the two-pass path: the oracle's pass 1 on the host
+    draws at the sampled positions, then its pass 2 with the device's global
+    squared norm (the one input that covers the whole shard)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from synth import workloads as W
+    from tests import parity
+
+    o = oracle.load()
+    L = d["arena_len"]
+    rng = np.random.default_rng(seed)
+    idx = np.unique(np.concatenate([rng.integers(0, L, samples), np.arange(min(L, 4096)),
+                                    np.arange(max(0, L - 4096), L)]))
+    it = torch.from_numpy(idx).to(d["P"].device)
+    got = dict(P=d["P"][it].cpu().numpy(), M=d["M"][it].cpu().numpy(), V=d["V"][it].cpu().numpy(),
+               B=d["B"].view(torch.int16)[it].cpu().numpy().view(np.uint16))
+    h = W.host_inputs_at(w, idx)
+    if gfmt == "fp16":
+        import synth
+
+        k = w.keys()
+        G = np.stack([o.f16(synth.normal_f32_at(k["G"][r], idx, w.g_sigma * loss_scale)) for r in range(w.N)])
+        fmt = 1
+    else:
+        G, fmt = h["G"], 0
+    g = o.reduce_unscale(G, fmt, loss_scale)
+    P, M, V, B, taken = o.adam_from_gbar(g, h["P"], h["M"], h["V"], w.hp(), w.step, sq, 1.0, out_fmt=fmt)
+    ref = dict(P=P, M=M, V=V, B=B)
+    rep = {k: parity.assert_f32(got[k], ref[k], f"{w.name} two-pass {k}") for k in "PMV"}
+    same = all(np.array_equal(got[k].view(np.uint32), ref[k].view(np.uint32)) for k in "PMV") and \
+        np.array_equal(got["B"], B)
+    return dict(samples=int(idx.size), bit_identical=bool(same), max_rel=max(r["max_rel"] for r in rep.values()),
+                step_taken=bool(taken), sqnorm=sq)
 
 
 def copy_ceiling(gbytes: float = 8.0, reps: int = 5) -> float:
@@ -151,6 +194,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 = skip)")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy-kernel ceiling")
     ap.add_argument("--blocks", type=int, default=0, help="workgroups per launch (0 = library default)")
+    ap.add_argument("--path", default="fused", choices=["fused", "clip", "fp16"],
+                    help="fused: the one-pass step; clip: two-pass with global-norm clipping (max_norm 1); "
+                         "fp16: two-pass with fp16 replicas, loss scale 2^16, clipping and an fp16 working copy")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -172,6 +218,28 @@ def main() -> int:
     log(f"inputs drawn in device memory in {time.perf_counter() - t0:.1f} s "
         f"({torch.cuda.memory_allocated() / 1e9:.1f} GB)")
 
+    two_pass = args.path != "fused"
+    if two_pass and w.is_list:
+        print("the two-pass paths run on flat shards", file=sys.stderr)
+        return 2
+    loss_scale = 2.0 ** 16 if args.path == "fp16" else 1.0
+    gfmt = "fp16" if args.path == "fp16" else "bf16"
+    if args.path == "fp16":
+        # fp16 replicas: the same seeded draws times the loss scale, rounded to fp16 (input preparation)
+        import synth
+
+        k = w.keys()
+        tmp = torch.empty(d["arena_len"], dtype=torch.float32, device="cuda")
+        for r in range(w.N):
+            synth.dev_fill_normal_f32(tmp, k["G"][r], 0, w.g_sigma * loss_scale)
+            d["G"][r] = tmp.half()
+        del tmp
+        d["B"] = torch.zeros(d["arena_len"], dtype=torch.float16, device="cuda")
+    ws = sqn = None
+    if two_pass:
+        ws = torch.empty(zs.two_pass_workspace_bytes(d["arena_len"]), dtype=torch.uint8, device="cuda")
+        sqn = torch.empty(1, dtype=torch.float64, device="cuda")
+
     plan = None
     if w.is_list:
         offs, _ = w.layout()
@@ -180,14 +248,20 @@ def main() -> int:
     def step(t):
         if plan is not None:
             plan.step(w.hp(), t)
+        elif two_pass:
+            zs.clipped_step_flat(d["G"], d["P"], d["M"], d["V"], d["B"], w.hp(), t, max_norm=1.0,
+                                 loss_scale=loss_scale, grad_format=gfmt, param_format=gfmt, workspace=ws, sqnorm=sqn)
         else:
             zs.reduce_adam_flat(d["G"], d["P"], d["M"], d["V"], d["B"], w.hp(), t)
 
     step(w.step)
     torch.cuda.synchronize()
     check = None
-    if args.samples > 0:
+    if args.samples > 0 and not two_pass:
         check = spot_check(w, d, args.samples)
+        log(f"sampled parity vs oracle: {check}")
+    elif args.samples > 0:
+        check = spot_check_two_pass(w, d, args.samples, float(sqn.item()), loss_scale, gfmt)
         log(f"sampled parity vs oracle: {check}")
 
     for k in range(args.warmup):
@@ -201,7 +275,8 @@ def main() -> int:
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     n = w.n_params
-    bytes_per_launch = (2 * w.N + 26) * n
+    bpp = 2 * w.N + (34 if two_pass else 26)
+    bytes_per_launch = bpp * n
     achieved = bytes_per_launch / (ms / 1e3) / 1e9
     log(f"{ms:.3f} ms/step, {n / (ms / 1e3) / 1e9:.2f} G params/s, {achieved:.0f} GB/s")
 
@@ -220,12 +295,13 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "n_params": n, "replicas": w.N, "adam_step": w.step,
-                   "weight_decay": w.weight_decay, "storage": "bf16 grads and working copy, fp32 master/m/v"},
+                   "weight_decay": w.weight_decay, "path": args.path,
+                   "storage": ("fp16" if args.path == "fp16" else "bf16") + " grads and working copy, fp32 master/m/v"},
         "hbm_GBps": achieved, "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,
         "copy_ceiling_GBps": ceiling,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "bytes_per_param": 2 * w.N + 26, "kernel": ("list_kernel" if w.is_list else "flat_kernel") + (
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic if not two_pass else None,
+                     "bytes_per_param": bpp, "kernel": ("list_kernel" if w.is_list else "flat_kernel") + (
                          f"<{w.N}>" if w.N in (1, 2, 4, 8, 16, 32, 64) else "<0>")},
         "cpu_baseline": base,
         "parity_sample": check,

@@ -47,6 +47,7 @@
 #ifndef ZSHARD_H
 #define ZSHARD_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -162,6 +163,70 @@ ZS_API void zs_list_plan_destroy(zs_list_plan_t plan);
 
 /* Shape of a plan: total parameters, tensors and chunks (any output may be NULL). */
 ZS_API zs_status zs_list_plan_info(zs_list_plan_t plan, int64_t* n_params, int32_t* n_tensors, int32_t* n_chunks);
+
+/* ---------------------------------------------------------------------------
+ * Two-pass form: global-norm gradient clipping and fp16 loss scaling.
+ *
+ * Both need a quantity over the whole model (the gradient norm, or whether
+ * any gradient overflowed) before any state may change: the gradient_clipping
+ * and dynamic fp16 loss-scale settings of the DeepSpeed config in "Почему
+ * training 70B модели требует optimizer sharding (ZeRO-3)?", §8.  Pass 1
+ * reduces the replicas into an fp32 gradient (in a caller-provided workspace)
+ * and this shard's squared norm; the caller sums the shards' squared norms
+ * over ranks (one scalar; on one GPU it is this shard's own); pass 2 applies
+ * AdamW with the clip coefficient, or skips the step on overflow.  Without
+ * clipping or loss scaling the two passes give exactly the fused step.
+ * ------------------------------------------------------------------------- */
+
+/* Storage format of 16-bit gradients and working copies. */
+#define ZS_FORMAT_BF16 0
+#define ZS_FORMAT_FP16 1
+
+/* Bytes of workspace the two passes need for a shard of n parameters (the
+   fp32 gradient plus one double per 2048-parameter tile, and alignment slack). */
+ZS_API size_t zs_two_pass_workspace_bytes(int64_t n);
+
+/* Pass 1.  g[i] = (s_i / N) * f32(1/loss_scale), s_i the rank-ordered sum of
+   the replicas (bf16 or fp16 bits per grad_format), written into `workspace`;
+   *sqnorm (device double) = sum of g[i]^2 in double, reduced per 2048-parameter
+   tile and then over tiles in a fixed order (independent of the launch size).
+   loss_scale > 0 (1 = no scaling).  Enqueues two kernels on `stream`.
+   Errors: ZS_ERR_NULL, ZS_ERR_RANGE (also: workspace too small),
+   ZS_ERR_ALIGN, ZS_ERR_ALIAS (workspace or sqnorm overlapping a gradient), ZS_ERR_HIP. */
+ZS_API zs_status zs_reduce_grads_flat(const uint16_t* const* grad_chunks, int32_t N, int64_t n, int32_t grad_format,
+                                      double loss_scale, void* workspace, size_t workspace_bytes, double* sqnorm,
+                                      zs_stream stream);
+
+/* Pass 2.  Reads *total_sq (device double, the global squared norm) when the
+   kernel runs: if skip_nonfinite and it is not finite, nothing is written (the
+   step is skipped, e.g. an fp16 overflow).  Otherwise, with
+   k = f32(min(1, max_norm / (sqrt(total_sq) + 1e-6))) (k = 1 when max_norm <= 0),
+   applies the update to g[i]*k from `workspace` (as written by pass 1 for the
+   same n), updating master/m/v in place and writing param_half in
+   param_format.  Errors: ZS_ERR_NULL, ZS_ERR_RANGE, ZS_ERR_ALIGN, ZS_ERR_ALIAS,
+   ZS_ERR_HIP. */
+ZS_API zs_status zs_adam_from_grads_flat(const void* workspace, size_t workspace_bytes, int64_t n, float* master,
+                                         float* m, float* v, uint16_t* param_half, int32_t param_format,
+                                         const zs_adam_hp* hp, int64_t step, const double* total_sq,
+                                         double max_norm, int32_t skip_nonfinite, zs_stream stream);
+
+/* Dynamic loss scale for fp16 training (the DeepSpeed fp16 block's
+   loss_scale 0 = dynamic, initial_scale_power, loss_scale_window, hysteresis,
+   min_loss_scale).  Host-only state. */
+typedef struct zs_loss_scaler {
+  double scale, min_scale;
+  int64_t window, hysteresis, overflows, clean;
+} zs_loss_scaler;
+
+/* scale = initial_scale; window >= 1; hysteresis >= 1; 0 < min_scale <= initial_scale. */
+ZS_API zs_status zs_loss_scaler_init(zs_loss_scaler* s, double initial_scale, double min_scale, int64_t window,
+                                     int64_t hysteresis);
+
+/* Records one step's outcome and returns 1 if the step was taken.  On
+   overflow: the step is skipped and, once `hysteresis` overflows have been
+   seen since the scale last changed, the scale halves (not below min_scale).
+   After `window` consecutive clean steps the scale doubles. */
+ZS_API int32_t zs_loss_scaler_update(zs_loss_scaler* s, int32_t overflow);
 
 /* Workgroups per launch for all later step calls in this process: 0 picks
    automatically from the device's compute-unit count.  Results do not depend

@@ -67,6 +67,27 @@ _lib.zs_list_plan_info.restype = ctypes.c_int
 _lib.zs_list_plan_info.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
 _lib.zs_set_grid_blocks.restype = ctypes.c_int
 _lib.zs_set_grid_blocks.argtypes = [_i32]
+_lib.zs_two_pass_workspace_bytes.restype = ctypes.c_size_t
+_lib.zs_two_pass_workspace_bytes.argtypes = [_i64]
+_lib.zs_reduce_grads_flat.restype = ctypes.c_int
+_lib.zs_reduce_grads_flat.argtypes = [ctypes.POINTER(_vp), _i32, _i64, _i32, ctypes.c_double, _vp, ctypes.c_size_t,
+                                      _vp, _vp]
+_lib.zs_adam_from_grads_flat.restype = ctypes.c_int
+_lib.zs_adam_from_grads_flat.argtypes = [_vp, ctypes.c_size_t, _i64, _vp, _vp, _vp, _vp, _i32,
+                                         ctypes.POINTER(AdamHPStruct), _i64, _vp, ctypes.c_double, _i32, _vp]
+
+
+class LossScalerStruct(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_double), ("min_scale", ctypes.c_double), ("window", ctypes.c_int64),
+                ("hysteresis", ctypes.c_int64), ("overflows", ctypes.c_int64), ("clean", ctypes.c_int64)]
+
+
+_lib.zs_loss_scaler_init.restype = ctypes.c_int
+_lib.zs_loss_scaler_init.argtypes = [ctypes.POINTER(LossScalerStruct), ctypes.c_double, ctypes.c_double, _i64, _i64]
+_lib.zs_loss_scaler_update.restype = _i32
+_lib.zs_loss_scaler_update.argtypes = [ctypes.POINTER(LossScalerStruct), _i32]
+
+FORMATS = {"bf16": 0, "fp16": 1}
 
 
 class ZShardError(RuntimeError):
@@ -145,6 +166,12 @@ def _bf16_types():
     import torch
 
     return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _half_types():
+    import torch
+
+    return (torch.bfloat16, torch.float16, torch.int16, torch.uint16)
 
 
 def _f32_types():
@@ -301,6 +328,99 @@ def reduce_adam_list(tensors: Sequence[ShardTensor], N: int, hp, step: int, stre
     h = _hp(hp)
     _check(_lib.zs_reduce_adam_list(tab, len(tensors), N, ctypes.byref(h), step, _stream_handle(stream)),
            "zs_reduce_adam_list")
+
+
+# ------------------------------------------------------------ two-pass form
+def two_pass_workspace_bytes(n: int) -> int:
+    return int(_lib.zs_two_pass_workspace_bytes(n))
+
+
+def _fmt(name) -> int:
+    if isinstance(name, int):
+        return name
+    return FORMATS[name]
+
+
+def reduce_grads_flat(grads: Sequence, workspace, sqnorm, loss_scale: float = 1.0, grad_format="bf16",
+                      stream=None) -> None:
+    """Pass 1: average (and unscale) the replicas into ``workspace`` and write the
+    shard's squared gradient norm to ``sqnorm`` (a 1-element float64 device tensor)."""
+    import torch
+
+    N = len(grads)
+    n = grads[0].numel() if N else 0
+    for r, g in enumerate(grads):
+        _dev_check(g, _half_types(), f"grads[{r}]")
+        if g.numel() != n:
+            raise ValueError(f"grads[{r}] has {g.numel()} elements, grads[0] has {n}")
+    _dev_check(workspace, (torch.uint8, torch.int8, torch.float32, torch.float64), "workspace")
+    _dev_check(sqnorm, (torch.float64,), "sqnorm")
+    tab = (_vp * max(N, 1))(*[g.data_ptr() for g in grads])
+    _check(_lib.zs_reduce_grads_flat(tab, N, n, _fmt(grad_format), loss_scale, workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), sqnorm.data_ptr(),
+                                     _stream_handle(stream)), "zs_reduce_grads_flat")
+
+
+def adam_from_grads_flat(workspace, n: int, master, m, v, param, hp, step: int, total_sq, max_norm: float = 0.0,
+                         param_format="bf16", skip_nonfinite: bool = True, stream=None) -> None:
+    """Pass 2: AdamW from the reduced gradient in ``workspace``, clipped to
+    ``max_norm`` by the global squared norm ``total_sq`` (device float64), and
+    skipped entirely when that norm is not finite."""
+    import torch
+
+    _dev_check(master, _f32_types(), "master")
+    _dev_check(m, _f32_types(), "m")
+    _dev_check(v, _f32_types(), "v")
+    _dev_check(param, _half_types(), "param")
+    _dev_check(total_sq, (torch.float64,), "total_sq")
+    for name, t in (("master", master), ("m", m), ("v", v), ("param", param)):
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    h = _hp(hp)
+    _check(_lib.zs_adam_from_grads_flat(workspace.data_ptr(), workspace.numel() * workspace.element_size(), n,
+                                        master.data_ptr(), m.data_ptr(), v.data_ptr(), param.data_ptr(),
+                                        _fmt(param_format), ctypes.byref(h), step, total_sq.data_ptr(), max_norm,
+                                        int(skip_nonfinite), _stream_handle(stream)), "zs_adam_from_grads_flat")
+
+
+def clipped_step_flat(grads: Sequence, master, m, v, param, hp, step: int, max_norm: float = 0.0,
+                      loss_scale: float = 1.0, grad_format="bf16", param_format="bf16", workspace=None,
+                      sqnorm=None, stream=None):
+    """Both passes on one shard, the shard's own norm standing for the global
+    one (one GPU).  Returns the device tensor holding the squared norm: a
+    non-finite value means the step was skipped (an fp16 overflow)."""
+    import torch
+
+    n = master.numel()
+    if workspace is None:
+        workspace = torch.empty(two_pass_workspace_bytes(n), dtype=torch.uint8, device=master.device)
+    if sqnorm is None:
+        sqnorm = torch.empty(1, dtype=torch.float64, device=master.device)
+    reduce_grads_flat(grads, workspace, sqnorm, loss_scale, grad_format, stream)
+    adam_from_grads_flat(workspace, n, master, m, v, param, hp, step, sqnorm, max_norm, param_format, True, stream)
+    return sqnorm
+
+
+class LossScaler:
+    """Dynamic loss scale for fp16 training: halves after `hysteresis` overflows
+    (not below `min_scale`), doubles after `window` clean steps."""
+
+    def __init__(self, initial_scale: float = 2.0 ** 16, min_scale: float = 1.0, window: int = 1000,
+                 hysteresis: int = 2):
+        self._s = LossScalerStruct()
+        _check(_lib.zs_loss_scaler_init(ctypes.byref(self._s), initial_scale, min_scale, window, hysteresis),
+               "zs_loss_scaler_init")
+
+    @property
+    def scale(self) -> float:
+        return self._s.scale
+
+    def update(self, overflow: bool) -> bool:
+        """Record a step; returns True if the step was taken."""
+        return bool(_lib.zs_loss_scaler_update(ctypes.byref(self._s), int(overflow)))
+
+    def state(self) -> dict:
+        return {k: getattr(self._s, k) for k, _ in LossScalerStruct._fields_}
 
 
 def library():

@@ -5,7 +5,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libzshard.so")
-SOURCES = [os.path.join(CSRC, "zs_kernels.hip"), os.path.join(CSRC, "zs_api.cpp")]
+SOURCES = [os.path.join(CSRC, "zs_kernels.hip"), os.path.join(CSRC, "zs_twopass.hip"), os.path.join(CSRC, "zs_api.cpp")]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
     # one rounding per operation, correctly rounded divide and sqrt
@@ -17,7 +17,10 @@ FLAGS = [
 
 
 def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
-    cmd = ["hipcc", *FLAGS, *extra, "-x", "hip", SOURCES[0], "-x", "hip", SOURCES[1], "-o", out]
+    cmd = ["hipcc", *FLAGS, *extra]
+    for src in SOURCES:
+        cmd += ["-x", "hip", src]
+    cmd += ["-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

@@ -199,7 +199,42 @@ int64_t common_peel(const float* p, const float* m, const float* v, const uint16
   return -1;
 }
 
+int64_t common_peel_sized(const void* const* ptrs, const int* elem_bytes, int count) {
+  for (int64_t h = 0; h < 8; ++h) {
+    bool ok = true;
+    for (int k = 0; ok && k < count; ++k)
+      ok = aligned(static_cast<const char*>(ptrs[k]) + h * elem_bytes[k], 16);
+    if (ok) return h;
+  }
+  return -1;
+}
+
 }  // namespace zs
+
+namespace {
+
+constexpr int64_t kTileElems = (int64_t)zs::kBlock * 8;
+
+struct WorkspaceLayout {
+  float* gbar;
+  double* partials;
+  size_t need;  // bytes from the workspace start
+};
+
+// fp32 gradient at the first 256-byte boundary, then one double per tile
+// (plus the head slot).
+WorkspaceLayout layout_of(const void* ws, int64_t n) {
+  WorkspaceLayout L;
+  const uintptr_t base = reinterpret_cast<uintptr_t>(ws);
+  const uintptr_t g = (base + 255) & ~(uintptr_t)255;
+  const uintptr_t p = g + (((uintptr_t)n * 4 + 255) & ~(uintptr_t)255);
+  L.gbar = reinterpret_cast<float*>(g);
+  L.partials = reinterpret_cast<double*>(p);
+  L.need = (size_t)(p - base) + 8 * (size_t)(n / kTileElems + 2);
+  return L;
+}
+
+}  // namespace
 
 struct zs_list_plan {
   int device;
@@ -408,6 +443,171 @@ zs_status zs_reduce_adam_list(const zs_tensor* tensors, int32_t T, int32_t N, co
   }
   zs_list_plan_destroy(plan);
   return st;
+}
+
+size_t zs_two_pass_workspace_bytes(int64_t n) {
+  if (n < 0) return 0;
+  return 255 + (((size_t)n * 4 + 255) & ~(size_t)255) + 8 * (size_t)(n / kTileElems + 2);
+}
+
+zs_status zs_reduce_grads_flat(const uint16_t* const* grad_chunks, int32_t N, int64_t n, int32_t grad_format,
+                               double loss_scale, void* workspace, size_t workspace_bytes, double* sqnorm,
+                               zs_stream stream) {
+  try {
+    g_last_error.clear();
+    if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
+    if (n < 0 || n > (int64_t(1) << 56)) return fail(ZS_ERR_RANGE, "n out of range");
+    if (grad_format != ZS_FORMAT_BF16 && grad_format != ZS_FORMAT_FP16)
+      return fail(ZS_ERR_RANGE, "grad_format must be ZS_FORMAT_BF16 or ZS_FORMAT_FP16");
+    if (!(loss_scale > 0) || !std::isfinite(loss_scale)) return fail(ZS_ERR_RANGE, "loss_scale must be finite and > 0");
+    if (!sqnorm) return fail(ZS_ERR_NULL, "sqnorm is NULL");
+    if (!aligned(sqnorm, 8)) return fail(ZS_ERR_ALIGN, "sqnorm must be 8-byte aligned");
+    if (n > 0 && !workspace) return fail(ZS_ERR_NULL, "workspace is NULL");
+    std::vector<Range> rs;
+    if (n > 0) {
+      if (!grad_chunks) return fail(ZS_ERR_NULL, "grad_chunks is NULL");
+      for (int32_t r = 0; r < N; ++r) {
+        if (!grad_chunks[r]) return fail(ZS_ERR_NULL, "grad_chunks[%d] is NULL", r);
+        if (!aligned(grad_chunks[r], 2)) return fail(ZS_ERR_ALIGN, "grad_chunks[%d] not 2-byte aligned", r);
+        rs.push_back({(uintptr_t)grad_chunks[r], (uintptr_t)grad_chunks[r] + 2 * (uintptr_t)n, 1, 0});
+      }
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    zs::TwoPassShape sh{};
+    sh.sqnorm = sqnorm;
+    sh.n = n;
+    sh.n_rep = N;
+    sh.inv_scale = (float)(1.0 / loss_scale);
+    if (n == 0) {  // an empty shard: only the (zero) norm is written
+      sh.partials = nullptr;
+      sh.ntiles = -1;
+      rs.push_back({(uintptr_t)sqnorm, (uintptr_t)sqnorm + 8, 0, 1});
+    } else {
+      const WorkspaceLayout L = layout_of(workspace, n);
+      if (workspace_bytes < L.need)
+        return fail(ZS_ERR_RANGE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, L.need);
+      rs.push_back({(uintptr_t)workspace, (uintptr_t)workspace + L.need, 0, 0});
+      rs.push_back({(uintptr_t)sqnorm, (uintptr_t)sqnorm + 8, 0, 1});
+      zs_status st = check_alias(rs);
+      if (st) return st;
+      sh.gbar = L.gbar;
+      sh.partials = L.partials;
+      std::vector<const void*> ptrs(grad_chunks, grad_chunks + N);
+      std::vector<int> sizes(N, 2);
+      ptrs.push_back(L.gbar);
+      sizes.push_back(4);
+      const int64_t h = zs::common_peel_sized(ptrs.data(), sizes.data(), (int)ptrs.size());
+      if (h < 0) {
+        sh.scalar_only = 1;
+        sh.head = 0;
+      } else {
+        sh.scalar_only = 0;
+        sh.head = h < n ? h : n;
+      }
+      sh.ntiles = (n - sh.head + kTileElems - 1) / kTileElems;
+    }
+    return after_launch(zs::launch_reduce(grad_chunks, sh, grad_format, auto_blocks(), hs), hs,
+                        "zs_reduce_grads_flat launch");
+  } catch (const std::bad_alloc&) {
+    return fail(ZS_ERR_NOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(ZS_ERR_HIP, "unexpected exception");
+  }
+}
+
+zs_status zs_adam_from_grads_flat(const void* workspace, size_t workspace_bytes, int64_t n, float* master, float* m,
+                                  float* v, uint16_t* param_half, int32_t param_format, const zs_adam_hp* hp,
+                                  int64_t step, const double* total_sq, double max_norm, int32_t skip_nonfinite,
+                                  zs_stream stream) {
+  try {
+    g_last_error.clear();
+    zs_status st = check_hp(hp, step);
+    if (st) return st;
+    if (n < 0 || n > (int64_t(1) << 56)) return fail(ZS_ERR_RANGE, "n out of range");
+    if (param_format != ZS_FORMAT_BF16 && param_format != ZS_FORMAT_FP16)
+      return fail(ZS_ERR_RANGE, "param_format must be ZS_FORMAT_BF16 or ZS_FORMAT_FP16");
+    if (!std::isfinite(max_norm)) return fail(ZS_ERR_RANGE, "max_norm must be finite (<= 0: no clipping)");
+    if (n == 0) return ZS_OK;
+    if (!workspace || !total_sq || !master || !m || !v || !param_half)
+      return fail(ZS_ERR_NULL, "workspace, total_sq, master, m, v and param_half must be non-NULL");
+    if (!aligned(total_sq, 8)) return fail(ZS_ERR_ALIGN, "total_sq must be 8-byte aligned");
+    if (!aligned(master, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(param_half, 2))
+      return fail(ZS_ERR_ALIGN, "master/m/v must be 4-byte and param_half 2-byte aligned");
+    const WorkspaceLayout L = layout_of(workspace, n);
+    if (workspace_bytes < L.need)
+      return fail(ZS_ERR_RANGE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, L.need);
+    const uintptr_t n4 = (uintptr_t)n * 4, n2 = (uintptr_t)n * 2;
+    std::vector<Range> rs = {{(uintptr_t)master, (uintptr_t)master + n4, 0, 0},
+                             {(uintptr_t)m, (uintptr_t)m + n4, 0, 0},
+                             {(uintptr_t)v, (uintptr_t)v + n4, 0, 0},
+                             {(uintptr_t)param_half, (uintptr_t)param_half + n2, 0, 0},
+                             {(uintptr_t)workspace, (uintptr_t)workspace + L.need, 1, 0},
+                             {(uintptr_t)total_sq, (uintptr_t)total_sq + 8, 1, 0}};
+    st = check_alias(rs);
+    if (st) return st;
+    zs::FlatShape s;
+    s.p = master;
+    s.m = m;
+    s.v = v;
+    s.b = param_half;
+    s.n = n;
+    const void* ptrs[5] = {L.gbar, master, m, v, param_half};
+    const int sizes[5] = {4, 4, 4, 4, 2};
+    const int64_t h = zs::common_peel_sized(ptrs, sizes, 5);
+    if (h < 0 || n < h + 8) {
+      s.head = 0;
+      s.nvec = 0;
+      s.scalar_only = 1;
+    } else {
+      s.head = h;
+      s.nvec = (n - h) / 8;
+      s.scalar_only = 0;
+    }
+    const zs::Scalars c = make_scalars(*hp, step, 1);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return after_launch(zs::launch_gbar(L.gbar, s, c, total_sq, max_norm, skip_nonfinite, param_format,
+                                        auto_blocks(), hs),
+                        hs, "zs_adam_from_grads_flat launch");
+  } catch (const std::bad_alloc&) {
+    return fail(ZS_ERR_NOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(ZS_ERR_HIP, "unexpected exception");
+  }
+}
+
+zs_status zs_loss_scaler_init(zs_loss_scaler* s, double initial_scale, double min_scale, int64_t window,
+                              int64_t hysteresis) {
+  g_last_error.clear();
+  if (!s) return fail(ZS_ERR_NULL, "scaler is NULL");
+  if (!(min_scale > 0) || !(initial_scale >= min_scale) || !std::isfinite(initial_scale) || window < 1 ||
+      hysteresis < 1)
+    return fail(ZS_ERR_RANGE, "need 0 < min_scale <= initial_scale (finite), window >= 1, hysteresis >= 1");
+  s->scale = initial_scale;
+  s->min_scale = min_scale;
+  s->window = window;
+  s->hysteresis = hysteresis;
+  s->overflows = 0;
+  s->clean = 0;
+  return ZS_OK;
+}
+
+int32_t zs_loss_scaler_update(zs_loss_scaler* s, int32_t overflow) {
+  if (!s) return 0;
+  if (overflow) {
+    s->clean = 0;
+    if (++s->overflows >= s->hysteresis) {
+      const double half = s->scale / 2.0;
+      s->scale = half < s->min_scale ? s->min_scale : half;
+      s->overflows = 0;
+    }
+    return 0;
+  }
+  if (++s->clean >= s->window) {
+    s->scale *= 2.0;
+    s->clean = 0;
+    s->overflows = 0;
+  }
+  return 1;
 }
 
 zs_status zs_list_plan_info(zs_list_plan_t plan, int64_t* n_params, int32_t* n_tensors, int32_t* n_chunks) {

@@ -1,0 +1,236 @@
+// Device helpers shared by the libzshard kernels: vector types, addressing
+// in the SGPR-base + 32-bit-offset form, bf16/fp16 conversions, the lane
+// layout of a tile, and the per-parameter AdamW update.
+#pragma once
+
+#include <type_traits>
+
+#include "zs_internal.h"
+
+namespace zs {
+namespace dev {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBatch = 8;  // replica loads in flight per thread per batch
+
+
+#define GLB __attribute__((address_space(1)))
+
+// A tile's base pointer: wave-uniform, in the global address space, pinned in
+// SGPRs and opaque to the optimizer.  Adding a lane's 32-bit byte offset then
+// stays the SGPR-base + VGPR-offset addressing form (one offset register for
+// every array) instead of being folded into a 64-bit per-lane address.
+template <class T>
+__device__ __forceinline__ GLB T* tile_base(T* p) {
+  GLB T* q = (GLB T*)p;
+  asm volatile("" : "+s"(q));
+  return q;
+}
+// A lane's 32-bit offset re-materialised in the current basic block:
+// instruction selection only recognises base + zero-extended 32-bit offset
+// when the extension is visible in the block of the access, and the loop
+// optimisers would otherwise hoist it out of the tile loop.
+__device__ __forceinline__ uint32_t here(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+template <class T>
+__device__ __forceinline__ GLB T* at(GLB T* base, uint32_t bytes) {
+  return (GLB T*)((GLB char*)base + bytes);
+}
+template <class T>
+__device__ __forceinline__ T ld_g(const GLB T* p) {
+  return __builtin_nontemporal_load(p);
+}
+template <class T>
+__device__ __forceinline__ void st_g(GLB T* p, T x) {
+  __builtin_nontemporal_store(x, p);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf_one(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);  // round to nearest even
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ uint16_t to_bf16(float a) { return __builtin_bit_cast(uint16_t, (__bf16)a); }
+
+// s / N.  For the replica counts the kernels are specialised on (powers of
+// two) this is a multiply by the exact reciprocal, the same correctly rounded
+// result; otherwise a correctly rounded divide.
+template <int NT>
+__device__ __forceinline__ float mean_of(float s, const Scalars& c) {
+  if constexpr (NT > 0 && (NT & (NT - 1)) == 0)
+    return s * (1.0f / (float)NT);
+  else
+    return s / (float)c.n_rep;
+}
+
+// The per-parameter AdamW update; every path calls this one function.
+__device__ __forceinline__ void adam(float g, float& p, float& m, float& v, const Scalars& c) {
+  const float m1 = c.b1 * m + c.c1 * g;
+  const float v1 = c.b2 * v + c.c2 * (g * g);
+  const float d = __builtin_sqrtf(v1) * c.rb + c.e;
+  const float u = m1 / d;
+  p = c.dk * p - c.ss * u;
+  m = m1;
+  v = v1;
+}
+
+// 16-bit storage formats of gradients and of the working copy.
+constexpr int kBF16 = 0;
+constexpr int kFP16 = 1;
+
+__device__ __forceinline__ float fp16_one(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// Exact widening of the low / high 16-bit half of a packed word.
+template <int FMT>
+__device__ __forceinline__ float h_lo(uint32_t w) {
+  if constexpr (FMT == kBF16) return bf_lo(w);
+  else return fp16_one((uint16_t)(w & 0xFFFFu));
+}
+template <int FMT>
+__device__ __forceinline__ float h_hi(uint32_t w) {
+  if constexpr (FMT == kBF16) return bf_hi(w);
+  else return fp16_one((uint16_t)(w >> 16));
+}
+template <int FMT>
+__device__ __forceinline__ float h_one(uint16_t h) {
+  if constexpr (FMT == kBF16) return bf_one(h);
+  else return fp16_one(h);
+}
+
+// Round to nearest even into the 16-bit format; two values packed low, high.
+template <int FMT>
+__device__ __forceinline__ uint32_t pack_half(float a, float b) {
+  if constexpr (FMT == kBF16) {
+    return pack_bf16(a, b);
+  } else {
+    const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)a);
+    const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)b);
+    return lo | (hi << 16);
+  }
+}
+template <int FMT>
+__device__ __forceinline__ uint16_t to_half(float a) {
+  if constexpr (FMT == kBF16) return to_bf16(a);
+  else return __builtin_bit_cast(uint16_t, (_Float16)a);
+}
+
+template <int FMT = kBF16>
+__device__ __forceinline__ void accumulate(float (&acc)[8], const u32x4 w) {
+  acc[0] = acc[0] + h_lo<FMT>(w.x);
+  acc[1] = acc[1] + h_hi<FMT>(w.x);
+  acc[2] = acc[2] + h_lo<FMT>(w.y);
+  acc[3] = acc[3] + h_hi<FMT>(w.y);
+  acc[4] = acc[4] + h_lo<FMT>(w.z);
+  acc[5] = acc[5] + h_hi<FMT>(w.z);
+  acc[6] = acc[6] + h_lo<FMT>(w.w);
+  acc[7] = acc[7] + h_hi<FMT>(w.w);
+}
+
+// Lane layouts of an 8-parameter group inside a tile of kBlock groups.
+//  Split (full tiles): lane l of wave q owns the quads at tile elements
+//    512q + 4l and 512q + 256 + 4l.  Every access instruction of a wave then
+//    covers whole contiguous lines: 1 KiB per fp32 access, 512 B per bf16
+//    access (8 bytes per lane).  Writes in particular go out as full lines.
+//  Contiguous (the one partial tile of a shard): thread t owns the 8
+//    elements 8t..8t+7; used where only a prefix of the tile's groups exists.
+template <bool SPLIT>
+struct Layout {
+  static __device__ __forceinline__ uint32_t first() {
+    return SPLIT ? 512u * (threadIdx.x >> 6) + 4u * (threadIdx.x & 63u) : 8u * threadIdx.x;
+  }
+  static constexpr uint32_t kSecond = SPLIT ? 256u : 4u;  // element distance to the 2nd quad
+};
+
+
+// Replica r's 8 gradient values (bf16 or fp16 bits) of this lane's group.  G(r) is replica r's
+// gradient pointer advanced to the tile (wave-uniform, SGPRs); `e` is the
+// lane's first element in the tile.
+template <bool SPLIT, class GP>
+__device__ __forceinline__ u32x4 ld_grad(GP G, int r, uint32_t e) {
+  if constexpr (SPLIT) {
+    const GLB u32x2* a = (const GLB u32x2*)at(G(r), here(e) * 2u);
+    const u32x2 x = ld_g(a), y = ld_g(a + Layout<true>::kSecond / 4);
+    return (u32x4){x.x, x.y, y.x, y.y};
+  } else {
+    return ld_g((const GLB u32x4*)at(G(r), here(e) * 2u));
+  }
+}
+
+template <bool SPLIT, class GP>
+__device__ __forceinline__ void load_batch(GP G, int r, int N, uint32_t e, u32x4 (&w)[kBatch]) {
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j)
+    if (r + j < N) w[j] = ld_grad<SPLIT>(G, r + j, e);
+}
+
+// Adds a batch, then pins the accumulators: the sums must be formed here, not
+// sunk towards their use after the last batch (which would keep every loaded
+// batch live at once).
+template <int FMT>
+__device__ __forceinline__ void add_batch(float (&acc)[8], const u32x4 (&w)[kBatch], int r, int N) {
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j)
+    if (r + j < N) accumulate<FMT>(acc, w[j]);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(acc[k]));
+}
+
+// acc[k] = sum over replicas r = 0..N-1, in that order, of element k of the
+// lane's group.  Replicas 1..N-1 stream in batches of kBatch loads; the next
+// batch is in flight while the current one is added (two register buffers),
+// and scheduling barriers stop the compiler from hoisting later batches,
+// which would buy nothing but registers.
+template <int NT, bool SPLIT, int FMT = kBF16, class GP>
+__device__ __forceinline__ void reduce_replicas(GP G, int N, uint32_t e, float (&acc)[8]) {
+  {
+    const u32x4 w = ld_grad<SPLIT>(G, 0, e);
+    acc[0] = h_lo<FMT>(w.x);
+    acc[1] = h_hi<FMT>(w.x);
+    acc[2] = h_lo<FMT>(w.y);
+    acc[3] = h_hi<FMT>(w.y);
+    acc[4] = h_lo<FMT>(w.z);
+    acc[5] = h_hi<FMT>(w.z);
+    acc[6] = h_lo<FMT>(w.w);
+    acc[7] = h_hi<FMT>(w.w);
+  }
+  if constexpr (NT > 0) {
+    constexpr int NB = (NT - 1 + kBatch - 1) / kBatch;
+    u32x4 w[2][kBatch];
+    if constexpr (NB > 0) load_batch<SPLIT>(G, 1, NT, e, w[0]);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (k + 1 < NB) load_batch<SPLIT>(G, 1 + (k + 1) * kBatch, NT, e, w[(k + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      add_batch<FMT>(acc, w[k & 1], 1 + k * kBatch, NT);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    u32x4 wa[kBatch], wb[kBatch];
+    if (N > 1) load_batch<SPLIT>(G, 1, N, e, wa);
+#pragma unroll 1
+    for (int r0 = 1; r0 < N; r0 += 2 * kBatch) {
+      const int r1 = r0 + kBatch, r2 = r1 + kBatch;
+      if (r1 < N) load_batch<SPLIT>(G, r1, N, e, wb);
+      __builtin_amdgcn_sched_barrier(0);
+      add_batch<FMT>(acc, wa, r0, N);
+      __builtin_amdgcn_sched_barrier(0);
+      if (r2 < N) load_batch<SPLIT>(G, r2, N, e, wa);
+      __builtin_amdgcn_sched_barrier(0);
+      if (r1 < N) add_batch<FMT>(acc, wb, r1, N);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+}  // namespace dev
+}  // namespace zs

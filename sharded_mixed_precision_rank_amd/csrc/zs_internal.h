@@ -59,16 +59,40 @@ struct ListChunk {
 static_assert(sizeof(ListTensor) == 64, "ListTensor layout");
 static_assert(sizeof(ListChunk) == 32, "ListChunk layout");
 
+// Pass 1 of the two-pass form: tiles of kBlock*8 parameters start at `head`
+// (the common 16-byte peel of the replicas and the fp32 gradient buffer);
+// scalar_only = 1 when no common peel exists.
+struct TwoPassShape {
+  float* gbar;
+  double* partials;  // ntiles + 1 slots
+  double* sqnorm;    // the shard's squared norm (device)
+  int64_t n;
+  int64_t head;
+  int64_t ntiles;
+  int32_t scalar_only;
+  int32_t n_rep;
+  float inv_scale;
+};
+
 // Common alignment peel: the smallest h in [0, 8) such that every pointer
 // advanced by h elements is 16-byte aligned, or -1 if none exists.
 int64_t common_peel(const float* p, const float* m, const float* v, const uint16_t* b,
                     const uint16_t* const* g, int32_t N);
+
+// The smallest h in [0, 8) such that every (pointer, element size) pair,
+// advanced by h elements, is 16-byte aligned; -1 if none exists.
+int64_t common_peel_sized(const void* const* ptrs, const int* elem_bytes, int count);
 
 // Launches (host side, defined with the kernels).
 hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, int blocks,
                        hipStream_t stream);
 hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
                        const uint16_t* const* gptrs, const Scalars& c, int blocks, hipStream_t stream);
+
+hipError_t launch_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int grad_format, int blocks,
+                         hipStream_t stream);
+hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, const double* total_sq,
+                       double max_norm, int skip_nonfinite, int param_format, int blocks, hipStream_t stream);
 
 // Elements per list chunk (vector tensors: groups of 8 per chunk = this / 8).
 constexpr int64_t kChunkElems = 65536;

@@ -30,191 +30,12 @@
 // contraction) and correctly rounded fp32 divide and sqrt; fp32 denormals are
 // kept.  Division by N is a multiply by 1/N only when N is a power of two,
 // where both are the same correctly rounded result.
-#include <type_traits>
-
-#include "zs_internal.h"
+#include "zs_device.h"
 
 namespace zs {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kBatch = 8;  // replica loads in flight per thread per batch
-
-
-#define GLB __attribute__((address_space(1)))
-
-// A tile's base pointer: wave-uniform, in the global address space, pinned in
-// SGPRs and opaque to the optimizer.  Adding a lane's 32-bit byte offset then
-// stays the SGPR-base + VGPR-offset addressing form (one offset register for
-// every array) instead of being folded into a 64-bit per-lane address.
-template <class T>
-__device__ __forceinline__ GLB T* tile_base(T* p) {
-  GLB T* q = (GLB T*)p;
-  asm volatile("" : "+s"(q));
-  return q;
-}
-// A lane's 32-bit offset re-materialised in the current basic block:
-// instruction selection only recognises base + zero-extended 32-bit offset
-// when the extension is visible in the block of the access, and the loop
-// optimisers would otherwise hoist it out of the tile loop.
-__device__ __forceinline__ uint32_t here(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-template <class T>
-__device__ __forceinline__ GLB T* at(GLB T* base, uint32_t bytes) {
-  return (GLB T*)((GLB char*)base + bytes);
-}
-template <class T>
-__device__ __forceinline__ T ld_g(const GLB T* p) {
-  return __builtin_nontemporal_load(p);
-}
-template <class T>
-__device__ __forceinline__ void st_g(GLB T* p, T x) {
-  __builtin_nontemporal_store(x, p);
-}
-
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ __forceinline__ float bf_one(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);  // round to nearest even
-  return __builtin_bit_cast(uint32_t, h);
-}
-__device__ __forceinline__ uint16_t to_bf16(float a) { return __builtin_bit_cast(uint16_t, (__bf16)a); }
-
-// s / N.  For the replica counts the kernels are specialised on (powers of
-// two) this is a multiply by the exact reciprocal, the same correctly rounded
-// result; otherwise a correctly rounded divide.
-template <int NT>
-__device__ __forceinline__ float mean_of(float s, const Scalars& c) {
-  if constexpr (NT > 0 && (NT & (NT - 1)) == 0)
-    return s * (1.0f / (float)NT);
-  else
-    return s / (float)c.n_rep;
-}
-
-// The per-parameter AdamW update; every path calls this one function.
-__device__ __forceinline__ void adam(float g, float& p, float& m, float& v, const Scalars& c) {
-  const float m1 = c.b1 * m + c.c1 * g;
-  const float v1 = c.b2 * v + c.c2 * (g * g);
-  const float d = __builtin_sqrtf(v1) * c.rb + c.e;
-  const float u = m1 / d;
-  p = c.dk * p - c.ss * u;
-  m = m1;
-  v = v1;
-}
-
-__device__ __forceinline__ void accumulate(float (&acc)[8], const u32x4 w) {
-  acc[0] = acc[0] + bf_lo(w.x);
-  acc[1] = acc[1] + bf_hi(w.x);
-  acc[2] = acc[2] + bf_lo(w.y);
-  acc[3] = acc[3] + bf_hi(w.y);
-  acc[4] = acc[4] + bf_lo(w.z);
-  acc[5] = acc[5] + bf_hi(w.z);
-  acc[6] = acc[6] + bf_lo(w.w);
-  acc[7] = acc[7] + bf_hi(w.w);
-}
-
-// Lane layouts of an 8-parameter group inside a tile of kBlock groups.
-//  Split (full tiles): lane l of wave q owns the quads at tile elements
-//    512q + 4l and 512q + 256 + 4l.  Every access instruction of a wave then
-//    covers whole contiguous lines: 1 KiB per fp32 access, 512 B per bf16
-//    access (8 bytes per lane).  Writes in particular go out as full lines.
-//  Contiguous (the one partial tile of a shard): thread t owns the 8
-//    elements 8t..8t+7; used where only a prefix of the tile's groups exists.
-template <bool SPLIT>
-struct Layout {
-  static __device__ __forceinline__ uint32_t first() {
-    return SPLIT ? 512u * (threadIdx.x >> 6) + 4u * (threadIdx.x & 63u) : 8u * threadIdx.x;
-  }
-  static constexpr uint32_t kSecond = SPLIT ? 256u : 4u;  // element distance to the 2nd quad
-};
-
-// Replica r's 8 bf16 values of this lane's group.  G(r) is replica r's
-// gradient pointer advanced to the tile (wave-uniform, SGPRs); `e` is the
-// lane's first element in the tile.
-template <bool SPLIT, class GP>
-__device__ __forceinline__ u32x4 ld_grad(GP G, int r, uint32_t e) {
-  if constexpr (SPLIT) {
-    const GLB u32x2* a = (const GLB u32x2*)at(G(r), here(e) * 2u);
-    const u32x2 x = ld_g(a), y = ld_g(a + Layout<true>::kSecond / 4);
-    return (u32x4){x.x, x.y, y.x, y.y};
-  } else {
-    return ld_g((const GLB u32x4*)at(G(r), here(e) * 2u));
-  }
-}
-
-template <bool SPLIT, class GP>
-__device__ __forceinline__ void load_batch(GP G, int r, int N, uint32_t e, u32x4 (&w)[kBatch]) {
-#pragma unroll
-  for (int j = 0; j < kBatch; ++j)
-    if (r + j < N) w[j] = ld_grad<SPLIT>(G, r + j, e);
-}
-
-// Adds a batch, then pins the accumulators: the sums must be formed here, not
-// sunk towards their use after the last batch (which would keep every loaded
-// batch live at once).
-__device__ __forceinline__ void add_batch(float (&acc)[8], const u32x4 (&w)[kBatch], int r, int N) {
-#pragma unroll
-  for (int j = 0; j < kBatch; ++j)
-    if (r + j < N) accumulate(acc, w[j]);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(acc[k]));
-}
-
-// acc[k] = sum over replicas r = 0..N-1, in that order, of element k of the
-// lane's group.  Replicas 1..N-1 stream in batches of kBatch loads; the next
-// batch is in flight while the current one is added (two register buffers),
-// and scheduling barriers stop the compiler from hoisting later batches,
-// which would buy nothing but registers.
-template <int NT, bool SPLIT, class GP>
-__device__ __forceinline__ void reduce_replicas(GP G, int N, uint32_t e, float (&acc)[8]) {
-  {
-    const u32x4 w = ld_grad<SPLIT>(G, 0, e);
-    acc[0] = bf_lo(w.x);
-    acc[1] = bf_hi(w.x);
-    acc[2] = bf_lo(w.y);
-    acc[3] = bf_hi(w.y);
-    acc[4] = bf_lo(w.z);
-    acc[5] = bf_hi(w.z);
-    acc[6] = bf_lo(w.w);
-    acc[7] = bf_hi(w.w);
-  }
-  if constexpr (NT > 0) {
-    constexpr int NB = (NT - 1 + kBatch - 1) / kBatch;
-    u32x4 w[2][kBatch];
-    if constexpr (NB > 0) load_batch<SPLIT>(G, 1, NT, e, w[0]);
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      if (k + 1 < NB) load_batch<SPLIT>(G, 1 + (k + 1) * kBatch, NT, e, w[(k + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      add_batch(acc, w[k & 1], 1 + k * kBatch, NT);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  } else {
-    u32x4 wa[kBatch], wb[kBatch];
-    if (N > 1) load_batch<SPLIT>(G, 1, N, e, wa);
-#pragma unroll 1
-    for (int r0 = 1; r0 < N; r0 += 2 * kBatch) {
-      const int r1 = r0 + kBatch, r2 = r1 + kBatch;
-      if (r1 < N) load_batch<SPLIT>(G, r1, N, e, wb);
-      __builtin_amdgcn_sched_barrier(0);
-      add_batch(acc, wa, r0, N);
-      __builtin_amdgcn_sched_barrier(0);
-      if (r2 < N) load_batch<SPLIT>(G, r2, N, e, wa);
-      __builtin_amdgcn_sched_barrier(0);
-      if (r1 < N) add_batch(acc, wb, r1, N);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-}
+using namespace dev;
 
 // One 8-parameter group of the tile starting at element e0 (wave-uniform,
 // 16-byte aligned in every array).  G(r) returns replica r's gradient pointer

@@ -1,0 +1,277 @@
+// Two-pass form of the shard step, for the features that need a whole-model
+// quantity before any state may change: global-norm gradient clipping and
+// fp16 dynamic loss scaling (the gradient_clipping and fp16 settings of the
+// DeepSpeed config in "Почему training 70B модели требует optimizer sharding
+// (ZeRO-3)?", §8).
+//
+//  pass 1 (reduce_kernel)   g = (rank-ordered sum / N) * (1 / loss scale), from
+//          bf16 or fp16 replicas; g is written to an fp32 workspace and its
+//          squared norm is summed in double, one partial per 2048-parameter
+//          tile, then the partials in a fixed order (finalize_kernel).  The
+//          result does not depend on the launch size.
+//  pass 2 (gbar_kernel)     reads the global squared norm from device memory:
+//          if it is not finite the step is skipped (nothing is written);
+//          otherwise k = f32(min(1, max_norm / (sqrt(norm^2) + 1e-6))) (k = 1
+//          without clipping) and the AdamW update runs on g * k, writing the
+//          working copy as bf16 or fp16.
+//
+// Bytes per parameter: pass 1 reads 2N and writes 4; pass 2 reads 4 + 12 and
+// writes 12 + 2: (2N + 34) in all, against (2N + 26) for the fused step.
+#include "zs_device.h"
+
+namespace zs {
+namespace {
+
+using namespace dev;
+
+constexpr int kTile = kBlock * 8;  // parameters per tile
+
+// Fixed-order block sum of one double per thread: butterfly within each wave,
+// then the waves' sums in wave order.  Every thread gets the result.
+__device__ __forceinline__ double block_sum(double x, double* lds4) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const double r = (lds4[0] + lds4[1]) + (lds4[2] + lds4[3]);
+  __syncthreads();
+  return r;
+}
+
+template <int NT>
+struct ReduceArgs {
+  const uint16_t* g[NT > 0 ? NT : ZS_MAX_REPLICAS];
+  float* gbar;
+  double* partials;  // ntiles + 1 slots; the last one holds the head elements
+  int64_t n;
+  int64_t head;      // elements before the first tile (alignment peel)
+  int64_t ntiles;    // tiles of kTile parameters starting at `head` (the last may be partial)
+  int32_t scalar_only;
+  int32_t n_rep;
+  float inv_scale;   // f32(1 / loss scale)
+};
+
+// g of element i through the per-element path.
+template <int FMT, class GP>
+__device__ __forceinline__ float elem_mean(GP G, int N, int64_t i, float inv) {
+  float acc = h_one<FMT>(G(0)[i]);
+  for (int r = 1; r < N; ++r) acc = acc + h_one<FMT>(G(r)[i]);
+  return (acc / (float)N) * inv;
+}
+
+template <int NT, int FMT>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs<NT> a) {
+  __shared__ double lds4[4];
+  const int N = NT > 0 ? NT : a.n_rep;
+  Scalars c{};
+  c.n_rep = N;
+  auto G0 = [&](int r) { return a.g[r]; };
+  for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+    const int64_t e0 = a.head + t * kTile;
+    double sq = 0.0;
+    if (!a.scalar_only && e0 + kTile <= a.n) {
+      // full tile, whole-line layout
+      auto G = [&](int r) { return tile_base(G0(r) + e0); };
+      const uint32_t e = Layout<true>::first();
+      float acc[8];
+      reduce_replicas<NT, true, FMT>(G, N, e, acc);
+      float g[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) g[k] = mean_of<NT>(acc[k], c) * a.inv_scale;
+      GLB f32x4* O = (GLB f32x4*)at(tile_base(a.gbar + e0), here(e) * 4u);
+      st_g(O, (f32x4){g[0], g[1], g[2], g[3]});
+      st_g(O + Layout<true>::kSecond / 4, (f32x4){g[4], g[5], g[6], g[7]});
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sq += (double)g[k] * (double)g[k];
+    } else {
+      // partial tile, or a shard without a common alignment: element by element
+      const int64_t lo = e0 + 8 * (int64_t)threadIdx.x;
+      for (int k = 0; k < 8; ++k) {
+        const int64_t i = lo + k;
+        if (i < a.n && i < e0 + kTile) {
+          const float g = elem_mean<FMT>(G0, N, i, a.inv_scale);
+          a.gbar[i] = g;
+          sq += (double)g * (double)g;
+        }
+      }
+    }
+    sq = block_sum(sq, lds4);
+    if (threadIdx.x == 0) a.partials[t] = sq;
+  }
+  if (blockIdx.x == 0) {
+    double sq = 0.0;
+    if (threadIdx.x < a.head) {
+      const float g = elem_mean<FMT>(G0, N, threadIdx.x, a.inv_scale);
+      a.gbar[threadIdx.x] = g;
+      sq = (double)g * (double)g;
+    }
+    sq = block_sum(sq, lds4);
+    if (threadIdx.x == 0) a.partials[a.ntiles] = sq;
+  }
+}
+
+// One workgroup: thread t sums partials t, t+256, ... in order, then the
+// fixed-order block sum.
+__global__ __launch_bounds__(kBlock) void finalize_kernel(const double* __restrict__ partials, int64_t count,
+                                                          double* __restrict__ out) {
+  __shared__ double lds4[4];
+  double x = 0.0;
+  for (int64_t i = threadIdx.x; i < count; i += kBlock) x += partials[i];
+  x = block_sum(x, lds4);
+  if (threadIdx.x == 0) *out = x;
+}
+
+struct GbarArgs {
+  const float* gbar;
+  FlatShape s;  // master / m / v / working copy, with the common peel over all five arrays
+  Scalars c;
+  const double* total_sq;
+  double max_norm;
+  int32_t skip_nonfinite;
+};
+
+__device__ __forceinline__ float clip_factor(double total_sq, double max_norm) {
+  if (!(max_norm > 0)) return 1.0f;
+  const double q = max_norm / (__builtin_sqrt(total_sq) + 1e-6);
+  return (float)(q < 1.0 ? q : 1.0);
+}
+
+template <int OFMT>
+__device__ __forceinline__ void gbar_elem(const GbarArgs& a, int64_t i, float k) {
+  float p = a.s.p[i], m = a.s.m[i], v = a.s.v[i];
+  adam(a.gbar[i] * k, p, m, v, a.c);
+  a.s.p[i] = p;
+  a.s.m[i] = m;
+  a.s.v[i] = v;
+  a.s.b[i] = to_half<OFMT>(p);
+}
+
+template <int OFMT>
+__global__ __launch_bounds__(kBlock) void gbar_kernel(const GbarArgs a) {
+  const double tsq = *a.total_sq;
+  if (a.skip_nonfinite && !__builtin_isfinite(tsq)) return;  // overflow: the step is skipped everywhere
+  const float k = clip_factor(tsq, a.max_norm);
+  const FlatShape& s = a.s;
+  const int64_t ntiles = s.scalar_only ? (s.n + kTile - 1) / kTile : (s.nvec + kBlock - 1) / kBlock;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    if (!s.scalar_only && (t + 1) * kBlock <= s.nvec) {
+      const int64_t e0 = s.head + t * kTile;
+      const uint32_t e = Layout<true>::first();
+      constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+      const uint32_t o = here(e) * 4u;
+      const GLB f32x4* G4 = (const GLB f32x4*)at(tile_base(a.gbar + e0), o);
+      const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(s.p + e0), o);
+      const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(s.m + e0), o);
+      const GLB f32x4* V4 = (const GLB f32x4*)at(tile_base(s.v + e0), o);
+      const f32x4 ga = ld_g(G4), gb = ld_g(G4 + q2);
+      const f32x4 pa = ld_g(P4), pb = ld_g(P4 + q2);
+      const f32x4 ma = ld_g(M4), mb = ld_g(M4 + q2);
+      const f32x4 va = ld_g(V4), vb = ld_g(V4 + q2);
+      float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+      float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+      float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+      float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) adam(g[j] * k, p[j], m[j], v[j], a.c);
+      const uint32_t o2 = here(e) * 4u;
+      GLB f32x4* Po = (GLB f32x4*)at(tile_base(s.p + e0), o2);
+      GLB f32x4* Mo = (GLB f32x4*)at(tile_base(s.m + e0), o2);
+      GLB f32x4* Vo = (GLB f32x4*)at(tile_base(s.v + e0), o2);
+      st_g(Po, (f32x4){p[0], p[1], p[2], p[3]});
+      st_g(Po + q2, (f32x4){p[4], p[5], p[6], p[7]});
+      st_g(Mo, (f32x4){m[0], m[1], m[2], m[3]});
+      st_g(Mo + q2, (f32x4){m[4], m[5], m[6], m[7]});
+      st_g(Vo, (f32x4){v[0], v[1], v[2], v[3]});
+      st_g(Vo + q2, (f32x4){v[4], v[5], v[6], v[7]});
+      GLB u32x2* B2 = (GLB u32x2*)at(tile_base(s.b + e0), here(e) * 2u);
+      st_g(B2, (u32x2){pack_half<OFMT>(p[0], p[1]), pack_half<OFMT>(p[2], p[3])});
+      st_g(B2 + Layout<true>::kSecond / 4, (u32x2){pack_half<OFMT>(p[4], p[5]), pack_half<OFMT>(p[6], p[7])});
+    } else {
+      // partial tile (vector shards) or any tile of a shard without common alignment
+      const int64_t e0 = s.scalar_only ? t * kTile : s.head + t * kTile;
+      const int64_t end = s.scalar_only ? s.n : s.head + 8 * s.nvec;
+      const int64_t lo = e0 + 8 * (int64_t)threadIdx.x;
+      for (int j = 0; j < 8; ++j)
+        if (lo + j < end && lo + j < e0 + kTile) gbar_elem<OFMT>(a, lo + j, k);
+    }
+  }
+  if (blockIdx.x == 0 && !s.scalar_only) {  // head and tail elements
+    const int64_t tail = s.n - s.head - 8 * s.nvec;
+    const int t = threadIdx.x;
+    if (t < s.head)
+      gbar_elem<OFMT>(a, t, k);
+    else if (t < s.head + tail)
+      gbar_elem<OFMT>(a, s.head + 8 * s.nvec + (t - s.head), k);
+  }
+}
+
+template <int NT, int FMT>
+hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int blocks, hipStream_t stream) {
+  (void)hipGetLastError();
+  if (sh.ntiles < 0) {  // empty shard: write a zero norm
+    finalize_kernel<<<dim3(1), dim3(kBlock), 0, stream>>>(nullptr, 0, sh.sqnorm);
+    return hipGetLastError();
+  }
+  ReduceArgs<NT> a;
+  for (int r = 0; r < sh.n_rep; ++r) a.g[r] = grads[r];
+  a.gbar = sh.gbar;
+  a.partials = sh.partials;
+  a.n = sh.n;
+  a.head = sh.head;
+  a.ntiles = sh.ntiles;
+  a.scalar_only = sh.scalar_only;
+  a.n_rep = sh.n_rep;
+  a.inv_scale = sh.inv_scale;
+  int grid = (int)(sh.ntiles < blocks ? sh.ntiles : blocks);
+  if (grid < 1) grid = 1;
+  (void)hipGetLastError();
+  reduce_kernel<NT, FMT><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  finalize_kernel<<<dim3(1), dim3(kBlock), 0, stream>>>(sh.partials, sh.ntiles + 1, sh.sqnorm);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t dispatch_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int blocks, hipStream_t stream) {
+  switch (sh.n_rep) {
+    case 1: return go_reduce<1, FMT>(grads, sh, blocks, stream);
+    case 2: return go_reduce<2, FMT>(grads, sh, blocks, stream);
+    case 4: return go_reduce<4, FMT>(grads, sh, blocks, stream);
+    case 8: return go_reduce<8, FMT>(grads, sh, blocks, stream);
+    case 16: return go_reduce<16, FMT>(grads, sh, blocks, stream);
+    case 32: return go_reduce<32, FMT>(grads, sh, blocks, stream);
+    case 64: return go_reduce<64, FMT>(grads, sh, blocks, stream);
+    default: return go_reduce<0, FMT>(grads, sh, blocks, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int grad_format, int blocks,
+                         hipStream_t stream) {
+  return grad_format == 1 ? dispatch_reduce<kFP16>(grads, sh, blocks, stream)
+                          : dispatch_reduce<kBF16>(grads, sh, blocks, stream);
+}
+
+hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, const double* total_sq,
+                       double max_norm, int skip_nonfinite, int param_format, int blocks, hipStream_t stream) {
+  GbarArgs a;
+  a.gbar = gbar;
+  a.s = s;
+  a.c = c;
+  a.total_sq = total_sq;
+  a.max_norm = max_norm;
+  a.skip_nonfinite = skip_nonfinite;
+  const int64_t ntiles = s.scalar_only ? (s.n + kTile - 1) / kTile : (s.nvec + kBlock - 1) / kBlock;
+  int grid = (int)(ntiles < blocks ? ntiles : blocks);
+  if (grid < 1) grid = 1;
+  (void)hipGetLastError();
+  if (param_format == 1)
+    gbar_kernel<kFP16><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
+  else
+    gbar_kernel<kBF16><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace zs

@@ -145,3 +145,67 @@ def test_python_binding_refuses_host_tensors():
     p = torch.zeros(8)
     with pytest.raises(ValueError):
         zs.reduce_adam_flat([g], p, p.clone(), p.clone(), g.clone(), HP, 1)
+
+
+# ------------------------------------------------------------ two-pass form
+def test_loss_scaler_matches_the_oracle(orc):
+    rng = np.random.default_rng(3)
+    for window, hyst, init, mn in ((1000, 2, 2.0 ** 16, 1.0), (3, 1, 8.0, 2.0), (7, 3, 2.0 ** 10, 1.0)):
+        lib_s = zs.LossScaler(init, mn, window, hyst)
+        o_s = orc.scaler(init, mn, window, hyst)
+        for k in range(5000):
+            ov = bool(rng.random() < (0.3 if k % 500 < 50 else 0.002))
+            assert lib_s.update(ov) == orc.scaler_update(o_s, ov)
+            st = lib_s.state()
+            assert (st["scale"], st["overflows"], st["clean"]) == (o_s.scale, o_s.overflows, o_s.clean)
+
+
+def test_loss_scaler_rejects_bad_settings():
+    with pytest.raises(zs.ZShardError):
+        zs.LossScaler(1.0, 2.0, 10, 1)
+    with pytest.raises(zs.ZShardError):
+        zs.LossScaler(2.0, 1.0, 0, 1)
+
+
+def test_workspace_size_covers_gradient_and_tiles():
+    for n in (0, 1, 2047, 2048, 10 ** 6, 1093750000):
+        need = zs.two_pass_workspace_bytes(n)
+        assert need >= 4 * n + 8 * (n // 2048 + 2) and need < 4 * n + 8 * (n // 2048 + 2) + 600
+
+
+def test_two_pass_rejects_bad_arguments_without_gpu():
+    lib = zs.library()
+    n = 4096
+    g = (ctypes.c_void_p * 2)(A + 0x100000, A + 0x200000)
+    ws_bytes = zs.two_pass_workspace_bytes(n)
+    ws = A + 0x400000
+    sq = A + 0x800000
+    ok = dict(N=2, n=n, fmt=0, scale=1.0, ws=ws, wsb=ws_bytes, sq=sq)
+    def call(**kw):
+        a = dict(ok, **kw)
+        return zs.STATUS[lib.zs_reduce_grads_flat(g, a["N"], a["n"], a["fmt"], a["scale"], a["ws"], a["wsb"],
+                                                  a["sq"], None)]
+    assert call(fmt=2) == "ZS_ERR_RANGE"
+    assert call(scale=0.0) == "ZS_ERR_RANGE"
+    assert call(scale=float("inf")) == "ZS_ERR_RANGE"
+    assert call(wsb=ws_bytes - 300) == "ZS_ERR_RANGE"
+    assert call(sq=0) == "ZS_ERR_NULL"
+    assert call(sq=sq + 4) == "ZS_ERR_ALIGN"
+    assert call(ws=A + 0x100000 + 64) == "ZS_ERR_ALIAS"          # workspace over a gradient
+    assert call(sq=A + 0x200000 + 8) == "ZS_ERR_ALIAS"            # norm slot inside a gradient
+    h = zs.AdamHPStruct(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    def call2(**kw):
+        a = dict(ws=ws, wsb=ws_bytes, n=n, p=A + 0x1000000, m=A + 0x1100000, v=A + 0x1200000, b=A + 0x1300000,
+                 fmt=0, step=1, tsq=sq, max_norm=1.0)
+        a.update(kw)
+        return zs.STATUS[lib.zs_adam_from_grads_flat(a["ws"], a["wsb"], a["n"], a["p"], a["m"], a["v"], a["b"],
+                                                     a["fmt"], ctypes.byref(h), a["step"], a["tsq"], a["max_norm"],
+                                                     1, None)]
+    assert call2(fmt=3) == "ZS_ERR_RANGE"
+    assert call2(max_norm=float("nan")) == "ZS_ERR_RANGE"
+    assert call2(step=0) == "ZS_ERR_RANGE"
+    assert call2(tsq=0) == "ZS_ERR_NULL"
+    assert call2(m=A + 0x1000000 + 16) == "ZS_ERR_ALIAS"           # m over master
+    assert call2(p=ws + 256) == "ZS_ERR_ALIAS"                      # master over the workspace
+    assert call2(tsq=A + 0x1100000 + 8) == "ZS_ERR_ALIAS"           # norm inside m
+    assert call2(wsb=100) == "ZS_ERR_RANGE"

@@ -1,0 +1,170 @@
+"""GPU parity of the two-pass form (clipping, fp16 loss scaling) against the oracle."""
+import numpy as np
+import pytest
+
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1)
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    import sharded_mixed_precision_rank_amd as zs
+
+    zs.set_grid_blocks(0)
+    return dict(torch=torch, zs=zs, dev=torch.device("cuda:0"))
+
+
+def rand_case(rng, N, n, fmt="bf16", scale=1.0, gscale=1e-3, orc=None):
+    x = (rng.standard_normal((N, n)) * gscale * scale).astype(np.float32)
+    if fmt == "bf16":
+        G = (x.view(np.uint32) >> 16).astype(np.uint16)
+    else:
+        G = orc.f16(x)
+    P = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    M = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    V = np.abs(rng.standard_normal(n) * 1e-6).astype(np.float32)
+    return dict(G=G, P=P, M=M, V=V)
+
+
+def run(env, host, hp, t, max_norm=0.0, loss_scale=1.0, gfmt="bf16", pfmt="bf16", offset=0):
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    n = host["P"].size
+    pad = offset
+    G = [torch.from_numpy(np.concatenate([np.zeros(pad, np.uint16), g]).view(np.int16)).to(dev)[pad:]
+         for g in host["G"]]
+    P = torch.from_numpy(np.concatenate([np.zeros(pad, np.float32), host["P"]])).to(dev)[pad:]
+    M = torch.from_numpy(np.concatenate([np.zeros(pad, np.float32), host["M"]])).to(dev)[pad:]
+    V = torch.from_numpy(np.concatenate([np.zeros(pad, np.float32), host["V"]])).to(dev)[pad:]
+    B = torch.zeros(n + pad, dtype=torch.int16, device=dev)[pad:]
+    ws = torch.empty(zs.two_pass_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    sq = torch.empty(1, dtype=torch.float64, device=dev)
+    zs.reduce_grads_flat(G, ws, sq, loss_scale, gfmt)
+    torch.cuda.synchronize()
+    start = (256 - ws.data_ptr() % 256) % 256
+    gbar = ws[start:start + 4 * n].cpu().numpy().view(np.float32).copy()
+    sqv = float(sq.cpu().item())
+    zs.adam_from_grads_flat(ws, n, P, M, V, B, hp, t, sq, max_norm, pfmt)
+    torch.cuda.synchronize()
+    got = dict(P=P.cpu().numpy(), M=M.cpu().numpy(), V=V.cpu().numpy(), B=B.cpu().numpy().view(np.uint16))
+    return gbar, sqv, got
+
+
+@pytest.mark.parametrize("N", [1, 3, 8, 64])
+@pytest.mark.parametrize("n", [1, 2047, 2048, 100_003])
+def test_two_pass_equals_fused_and_oracle(env, orc, N, n):
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    rng = np.random.default_rng(N * 1000 + n)
+    host = rand_case(rng, N, n)
+    gbar, sqv, got = run(env, host, HP, 12)
+    # pass 1 against the oracle: the gradient bit for bit, the norm to double rounding
+    ref_g = orc.reduce_unscale(host["G"], 0, 1.0)
+    assert np.array_equal(gbar.view(np.uint32), ref_g.view(np.uint32))
+    ref_sq = orc.sqnorm(ref_g)
+    assert abs(sqv - ref_sq) <= 1e-12 * ref_sq
+    # pass 2 against the oracle and against the fused step
+    P1, M1, V1, B1, taken = orc.adam_from_gbar(ref_g, host["P"], host["M"], host["V"], HP, 12, sqv, 0.0)
+    assert taken
+    assert parity.bit_identical(got, dict(P=P1, M=M1, V=V1, B=B1))
+    fP, fM, fV, fB = orc.step(host["G"], host["P"], host["M"], host["V"], HP, 12)
+    assert parity.bit_identical(got, dict(P=fP, M=fM, V=fV, B=fB))
+
+
+@pytest.mark.parametrize("shrink", [2.0, 7.0, 1000.0])
+def test_clipping_matches_oracle(env, orc, shrink):
+    rng = np.random.default_rng(int(shrink))
+    host = rand_case(rng, 8, 50_001)
+    ref_g = orc.reduce_unscale(host["G"], 0, 1.0)
+    norm = orc.sqnorm(ref_g) ** 0.5
+    gbar, sqv, got = run(env, host, HP, 300, max_norm=norm / shrink)
+    P1, M1, V1, B1, taken = orc.adam_from_gbar(ref_g, host["P"], host["M"], host["V"], HP, 300, sqv, norm / shrink)
+    ref = dict(P=P1, M=M1, V=V1, B=B1)
+    parity.assert_step(got, ref, f"clip /{shrink}")
+    assert parity.bit_identical(got, ref)
+    # and with the oracle's own norm: the coefficient agrees
+    assert orc.clip_coef(sqv, norm / shrink) == orc.clip_coef(orc.sqnorm(ref_g), norm / shrink)
+
+
+@pytest.mark.parametrize("loss_scale", [1.0, 2.0 ** 8, 2.0 ** 16])
+def test_fp16_loss_scaled_grads_and_fp16_copy(env, orc, loss_scale):
+    rng = np.random.default_rng(int(np.log2(loss_scale)) + 5)
+    host = rand_case(rng, 4, 30_000, fmt="fp16", scale=loss_scale, orc=orc)
+    gbar, sqv, got = run(env, host, HP, 40, max_norm=1.0, loss_scale=loss_scale, gfmt="fp16", pfmt="fp16")
+    ref_g = orc.reduce_unscale(host["G"], 1, loss_scale)
+    assert np.array_equal(gbar.view(np.uint32), ref_g.view(np.uint32))
+    P1, M1, V1, B1, taken = orc.adam_from_gbar(ref_g, host["P"], host["M"], host["V"], HP, 40, sqv, 1.0, out_fmt=1)
+    ref = dict(P=P1, M=M1, V=V1, B=B1)
+    for k in "PMV":
+        parity.assert_f32(got[k], ref[k], k)
+    assert np.array_equal(got["B"], B1), "fp16 working copy"
+    for k in "PMV":
+        assert np.array_equal(got[k].view(np.uint32), ref[k].view(np.uint32)), k
+
+
+def test_fp16_overflow_skips_the_step(env, orc):
+    rng = np.random.default_rng(9)
+    host = rand_case(rng, 4, 10_000, fmt="fp16", scale=2.0 ** 16, orc=orc)
+    host["G"][2, 1234] = 0x7C00  # +Inf in one replica
+    gbar, sqv, got = run(env, host, HP, 7, max_norm=1.0, loss_scale=2.0 ** 16, gfmt="fp16", pfmt="fp16")
+    assert not np.isfinite(sqv)
+    assert np.array_equal(got["P"], host["P"]) and np.array_equal(got["M"], host["M"])
+    assert np.array_equal(got["V"], host["V"]) and np.all(got["B"] == 0)
+
+
+def test_misaligned_two_pass(env, orc):
+    rng = np.random.default_rng(11)
+    host = rand_case(rng, 3, 9_999)
+    for off in (1, 3):
+        gbar, sqv, got = run(env, host, HP, 2, max_norm=0.5, offset=off)
+        ref_g = orc.reduce_unscale(host["G"], 0, 1.0)
+        assert np.array_equal(gbar.view(np.uint32), ref_g.view(np.uint32))
+        P1, M1, V1, B1, _ = orc.adam_from_gbar(ref_g, host["P"], host["M"], host["V"], HP, 2, sqv, 0.5)
+        assert parity.bit_identical(got, dict(P=P1, M=M1, V=V1, B=B1))
+
+
+def test_norm_does_not_depend_on_launch_size(env):
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    rng = np.random.default_rng(13)
+    n, N = 1_000_003, 8
+    G = [torch.from_numpy(((rng.standard_normal(n) * 1e-3).astype(np.float32).view(np.uint32) >> 16)
+                          .astype(np.uint16).view(np.int16)).to(dev) for _ in range(N)]
+    ws = torch.empty(zs.two_pass_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    vals = []
+    try:
+        for blocks in (0, 1, 7, 333):
+            zs.set_grid_blocks(blocks)
+            sq = torch.empty(1, dtype=torch.float64, device=dev)
+            zs.reduce_grads_flat(G, ws, sq)
+            torch.cuda.synchronize()
+            vals.append(sq.item())
+    finally:
+        zs.set_grid_blocks(0)
+    assert len(set(vals)) == 1, vals
+
+
+def test_empty_shard_norm_is_zero(env):
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    sq = torch.full((1,), 5.0, dtype=torch.float64, device=dev)
+    e = torch.empty(0, dtype=torch.bfloat16, device=dev)
+    zs.reduce_grads_flat([e, e], torch.empty(0, dtype=torch.uint8, device=dev), sq)
+    torch.cuda.synchronize()
+    assert sq.item() == 0.0
+
+
+def test_clipped_step_convenience(env, orc):
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    rng = np.random.default_rng(17)
+    host = rand_case(rng, 2, 5000)
+    G = [torch.from_numpy(g.view(np.int16)).to(dev) for g in host["G"]]
+    P, M, V = (torch.from_numpy(host[k]).to(dev) for k in "PMV")
+    B = torch.zeros(5000, dtype=torch.int16, device=dev)
+    sq = zs.clipped_step_flat(G, P, M, V, B, HP, 3, max_norm=0.01)
+    torch.cuda.synchronize()
+    ref_g = orc.reduce_unscale(host["G"], 0, 1.0)
+    P1, M1, V1, B1, _ = orc.adam_from_gbar(ref_g, host["P"], host["M"], host["V"], HP, 3, sq.item(), 0.01)
+    got = dict(P=P.cpu().numpy(), M=M.cpu().numpy(), V=V.cpu().numpy(), B=B.cpu().numpy().view(np.uint16))
+    assert parity.bit_identical(got, dict(P=P1, M=M1, V=V1, B=B1))
