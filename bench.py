@@ -83,9 +83,10 @@ def spot_check(w, d, samples: int, seed: int = 1234) -> dict:
         sizes = np.asarray(w.sizes)
         t = np.searchsorted(offs, idx, side="right") - 1
         idx = idx[(t >= 0) & (idx < offs[np.maximum(t, 0)] + sizes[np.maximum(t, 0)])]
-    it = torch.from_numpy(idx).to(d["P"].device)
-    got = dict(P=d["P"][it].cpu().numpy(), M=d["M"][it].cpu().numpy(), V=d["V"][it].cpu().numpy(),
-               B=d["B"].view(torch.int16)[it].cpu().numpy().view(np.uint16))
+    it = torch.from_numpy(idx)
+    at = lambda t: t[it.to(t.device)].cpu()
+    got = dict(P=at(d["P"]).numpy(), M=at(d["M"]).numpy(), V=at(d["V"]).numpy(),
+               B=at(d["B"].view(torch.int16)).numpy().view(np.uint16))
     h = W.host_inputs_at(w, idx)
     P, M, V, B = oracle.load().step(h["G"], h["P"], h["M"], h["V"], w.hp(), w.step)
     rep = parity.assert_step(got, dict(P=P, M=M, V=V, B=B), f"{w.name} sampled")
@@ -194,9 +195,11 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 = skip)")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy-kernel ceiling")
     ap.add_argument("--blocks", type=int, default=0, help="workgroups per launch (0 = library default)")
-    ap.add_argument("--path", default="fused", choices=["fused", "clip", "fp16"],
+    ap.add_argument("--path", default="fused", choices=["fused", "clip", "fp16", "offload"],
                     help="fused: the one-pass step; clip: two-pass with global-norm clipping (max_norm 1); "
-                         "fp16: two-pass with fp16 replicas, loss scale 2^16, clipping and an fp16 working copy")
+                         "fp16: two-pass with fp16 replicas, loss scale 2^16, clipping and an fp16 working copy; "
+                         "offload: fp32 state in host memory, AdamW on the CPU, reduction on the GPU")
+    ap.add_argument("--offload-chunk", type=int, default=1 << 24, help="parameters per offload pipeline chunk")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -218,7 +221,19 @@ def main() -> int:
     log(f"inputs drawn in device memory in {time.perf_counter() - t0:.1f} s "
         f"({torch.cuda.memory_allocated() / 1e9:.1f} GB)")
 
-    two_pass = args.path != "fused"
+    two_pass = args.path in ("clip", "fp16")
+    offload = None
+    if args.path == "offload":
+        if w.is_list:
+            print("the offload path runs on flat shards", file=sys.stderr)
+            return 2
+        threads = min(16, len(os.sched_getaffinity(0)))
+        for k in "PMV":   # the fp32 state moves to pinned host memory
+            d[k] = d[k].cpu().pin_memory()
+        torch.cuda.empty_cache()
+        offload = zs.Offload(args.offload_chunk, threads)
+        log(f"offload: host state {3 * 4 * d['arena_len'] / 1e9:.1f} GB pinned, {threads} CPU threads, "
+            f"chunk {args.offload_chunk}")
     if two_pass and w.is_list:
         print("the two-pass paths run on flat shards", file=sys.stderr)
         return 2
@@ -248,6 +263,8 @@ def main() -> int:
     def step(t):
         if plan is not None:
             plan.step(w.hp(), t)
+        elif offload is not None:
+            offload.step(d["G"], d["P"], d["M"], d["V"], d["B"], w.hp(), t)
         elif two_pass:
             zs.clipped_step_flat(d["G"], d["P"], d["M"], d["V"], d["B"], w.hp(), t, max_norm=1.0,
                                  loss_scale=loss_scale, grad_format=gfmt, param_format=gfmt, workspace=ws, sqnorm=sqn)
@@ -275,11 +292,13 @@ def main() -> int:
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     n = w.n_params
-    bpp = 2 * w.N + (34 if two_pass else 26)
+    bpp = 2 * w.N + (34 if two_pass else 26)   # offload: the same algorithmic bytes as the fused step
     bytes_per_launch = bpp * n
     achieved = bytes_per_launch / (ms / 1e3) / 1e9
     log(f"{ms:.3f} ms/step, {n / (ms / 1e3) / 1e9:.2f} G params/s, {achieved:.0f} GB/s")
 
+    if offload is not None:
+        offload.close()
     del d, plan
     torch.cuda.empty_cache()
     ceiling = None if args.no_copy else copy_ceiling()

@@ -228,6 +228,44 @@ ZS_API zs_status zs_loss_scaler_init(zs_loss_scaler* s, double initial_scale, do
    After `window` consecutive clean steps the scale doubles. */
 ZS_API int32_t zs_loss_scaler_update(zs_loss_scaler* s, int32_t overflow);
 
+/* ---------------------------------------------------------------------------
+ * Optimizer offload (ZeRO-Offload, "Почему training 70B модели требует
+ * optimizer sharding (ZeRO-3)?", §6-§8): the rank's fp32 master, momentum and
+ * variance stay in host memory and the update runs on the CPU.  The GPU
+ * reduces the replicas chunk by chunk; each fp32 gradient chunk crosses PCIe
+ * (4 B/param), the CPU updates the host state, and the bf16 working copy
+ * returns to the device (2 B/param).  Chunks are pipelined so the GPU reduce,
+ * both copies and the CPU update overlap.  Results equal the fused device
+ * step bit for bit.
+ * ------------------------------------------------------------------------- */
+typedef struct zs_offload* zs_offload_t;
+
+/* A context holding two pipeline slots of chunk_elems parameters (device
+   workspaces, pinned host buffers, a copy stream); buffers are allocated on
+   the current device at the first step.  2048 <= chunk_elems <= 2^32;
+   threads = CPU threads for the update.  Errors: ZS_ERR_NULL, ZS_ERR_RANGE,
+   ZS_ERR_NOMEM. */
+ZS_API zs_status zs_offload_create(int64_t chunk_elems, int32_t threads, zs_offload_t* out);
+
+/* One step with host-resident state.  grad_chunks: host array of N device
+   pointers (bf16); master, m, v: HOST fp32 arrays of n, updated in place
+   before the call returns; param_dev: DEVICE bf16 array of n.  The reduce
+   kernels run on `stream`; work enqueued on `stream` after the call sees the
+   new param_dev.  Blocks until the host state is updated.  Errors:
+   ZS_ERR_NULL, ZS_ERR_RANGE, ZS_ERR_ALIGN, ZS_ERR_ALIAS, ZS_ERR_HIP (the host
+   state may then be partly updated). */
+ZS_API zs_status zs_offload_step_flat(zs_offload_t ctx, const uint16_t* const* grad_chunks, int32_t N, int64_t n,
+                                      float* master, float* m, float* v, uint16_t* param_dev, const zs_adam_hp* hp,
+                                      int64_t step, zs_stream stream);
+
+/* Waits for the context's copies, frees its buffers.  NULL is a no-op. */
+ZS_API void zs_offload_destroy(zs_offload_t ctx);
+
+/* The host AdamW on its own (no GPU): master/m/v updated from gbar, bf16
+   copy into param_bf16; all host arrays of n.  Errors: ZS_ERR_NULL, ZS_ERR_RANGE. */
+ZS_API zs_status zs_cpu_adam(const float* gbar, int64_t n, float* master, float* m, float* v, uint16_t* param_bf16,
+                             const zs_adam_hp* hp, int64_t step, int32_t threads);
+
 /* Workgroups per launch for all later step calls in this process: 0 picks
    automatically from the device's compute-unit count.  Results do not depend
    on it (every element is computed by one thread with the same operations). */

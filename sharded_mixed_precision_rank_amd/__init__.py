@@ -87,6 +87,16 @@ _lib.zs_loss_scaler_init.argtypes = [ctypes.POINTER(LossScalerStruct), ctypes.c_
 _lib.zs_loss_scaler_update.restype = _i32
 _lib.zs_loss_scaler_update.argtypes = [ctypes.POINTER(LossScalerStruct), _i32]
 
+_lib.zs_offload_create.restype = ctypes.c_int
+_lib.zs_offload_create.argtypes = [_i64, _i32, ctypes.POINTER(_vp)]
+_lib.zs_offload_step_flat.restype = ctypes.c_int
+_lib.zs_offload_step_flat.argtypes = [_vp, ctypes.POINTER(_vp), _i32, _i64, _vp, _vp, _vp, _vp,
+                                      ctypes.POINTER(AdamHPStruct), _i64, _vp]
+_lib.zs_offload_destroy.restype = None
+_lib.zs_offload_destroy.argtypes = [_vp]
+_lib.zs_cpu_adam.restype = ctypes.c_int
+_lib.zs_cpu_adam.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, ctypes.POINTER(AdamHPStruct), _i64, _i32]
+
 FORMATS = {"bf16": 0, "fp16": 1}
 
 
@@ -421,6 +431,79 @@ class LossScaler:
 
     def state(self) -> dict:
         return {k: getattr(self._s, k) for k, _ in LossScalerStruct._fields_}
+
+
+# ------------------------------------------------------------ optimizer offload
+def _host_ptr(a, dtype_name: str):
+    """Address of a contiguous host array (numpy array or CPU torch tensor)."""
+    import numpy as np
+
+    if isinstance(a, np.ndarray):
+        if not a.flags.c_contiguous or a.dtype.name != dtype_name:
+            raise TypeError(f"expected a contiguous {dtype_name} numpy array")
+        return a.ctypes.data, a.size
+    import torch
+
+    want = {"float32": torch.float32, "uint16": (torch.int16, torch.uint16, torch.bfloat16)}[dtype_name]
+    ok = a.dtype in want if isinstance(want, tuple) else a.dtype == want
+    if not isinstance(a, torch.Tensor) or a.is_cuda or not a.is_contiguous() or not ok:
+        raise TypeError(f"expected a contiguous host {dtype_name} array")
+    return a.data_ptr(), a.numel()
+
+
+def cpu_adam(gbar, master, m, v, param, hp, step: int, threads: int = 1) -> None:
+    """Host AdamW (no GPU): master/m/v updated from gbar, bf16 copy into param."""
+    g, n = _host_ptr(gbar, "float32")
+    ptrs = [_host_ptr(x, "float32") for x in (master, m, v)]
+    b, nb = _host_ptr(param, "uint16")
+    if any(k != n for _, k in ptrs) or nb != n:
+        raise ValueError("all arrays must have the same length")
+    h = _hp(hp)
+    _check(_lib.zs_cpu_adam(g, n, ptrs[0][0], ptrs[1][0], ptrs[2][0], b, ctypes.byref(h), step, threads),
+           "zs_cpu_adam")
+
+
+class Offload:
+    """Optimizer offload: fp32 master/m/v in host memory, AdamW on the CPU,
+    replica reduction on the GPU, chunks pipelined over PCIe."""
+
+    def __init__(self, chunk_elems: int = 1 << 24, threads: int = 16):
+        h = _vp()
+        _check(_lib.zs_offload_create(chunk_elems, threads, ctypes.byref(h)), "zs_offload_create")
+        self._h = h
+
+    def step(self, grads: Sequence, master, m, v, param, hp, step: int, stream=None) -> None:
+        N = len(grads)
+        n = param.numel()
+        _dev_check(param, _bf16_types(), "param")
+        for r, g in enumerate(grads):
+            _dev_check(g, _bf16_types(), f"grads[{r}]")
+            if g.numel() != n:
+                raise ValueError(f"grads[{r}] has {g.numel()} elements, param has {n}")
+        ptrs = [_host_ptr(x, "float32") for x in (master, m, v)]
+        if any(k != n for _, k in ptrs):
+            raise ValueError("host master/m/v must have the parameter count")
+        tab = (_vp * max(N, 1))(*[g.data_ptr() for g in grads])
+        h = _hp(hp)
+        _check(_lib.zs_offload_step_flat(self._h, tab, N, n, ptrs[0][0], ptrs[1][0], ptrs[2][0], param.data_ptr(),
+                                         ctypes.byref(h), step, _stream_handle(stream)), "zs_offload_step_flat")
+
+    def close(self) -> None:
+        if self._h:
+            _lib.zs_offload_destroy(self._h)
+            self._h = _vp()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def library():

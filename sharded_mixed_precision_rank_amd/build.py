@@ -5,7 +5,14 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libzshard.so")
-SOURCES = [os.path.join(CSRC, "zs_kernels.hip"), os.path.join(CSRC, "zs_twopass.hip"), os.path.join(CSRC, "zs_api.cpp")]
+# Device code and HIP-runtime host code compile as HIP in one hipcc command.
+SOURCES = [os.path.join(CSRC, f) for f in ("zs_kernels.hip", "zs_twopass.hip", "zs_api.cpp", "zs_offload.cpp")]
+# The host AdamW is plain C++ built by the host compiler into an object that
+# the hipcc link takes as is (its AVX2 path is chosen at run time).  Compiling
+# it as a C++ input inside the hipcc command produced a library that crashed
+# when loaded, so it stays a separate object.
+HOST_SOURCES = [os.path.join(CSRC, "zs_cpu_adam.cpp")]
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off", "-fno-fast-math", "-Wall"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
     # one rounding per operation, correctly rounded divide and sqrt
@@ -17,10 +24,18 @@ FLAGS = [
 
 
 def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(HERE, os.path.splitext(os.path.basename(src))[0] + ".o")
+        hcmd = ["g++", *HOST_FLAGS, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(hcmd), flush=True)
+        subprocess.run(hcmd, check=True)
+        objs.append(obj)
     cmd = ["hipcc", *FLAGS, *extra]
     for src in SOURCES:
         cmd += ["-x", "hip", src]
-    cmd += ["-o", out]
+    cmd += ["-x", "none", *objs, "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

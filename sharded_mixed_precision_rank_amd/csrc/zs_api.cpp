@@ -11,6 +11,7 @@
 #include <string>
 #include <vector>
 
+#include "zs_cpu_adam.h"
 #include "zs_internal.h"
 
 namespace {
@@ -234,7 +235,58 @@ WorkspaceLayout layout_of(const void* ws, int64_t n) {
   return L;
 }
 
+// Pass-1 shape for n parameters of replicas `g` and workspace `ws` (the
+// workspace must already be known to be large enough).
+void reduce_shape(const uint16_t* const* g, int32_t N, int64_t n, void* ws, double* sq, float inv_scale,
+                  zs::TwoPassShape* sh) {
+  *sh = zs::TwoPassShape{};
+  sh->sqnorm = sq;
+  sh->n = n;
+  sh->n_rep = N;
+  sh->inv_scale = inv_scale;
+  const WorkspaceLayout L = layout_of(ws, n);
+  sh->gbar = L.gbar;
+  sh->partials = L.partials;
+  std::vector<const void*> ptrs(g, g + N);
+  std::vector<int> sizes(N, 2);
+  ptrs.push_back(L.gbar);
+  sizes.push_back(4);
+  const int64_t h = zs::common_peel_sized(ptrs.data(), sizes.data(), (int)ptrs.size());
+  if (h < 0) {
+    sh->scalar_only = 1;
+    sh->head = 0;
+  } else {
+    sh->scalar_only = 0;
+    sh->head = h < n ? h : n;
+  }
+  sh->ntiles = (n - sh->head + kTileElems - 1) / kTileElems;
+}
+
 }  // namespace
+
+namespace zs {
+
+zs_status offload_fail(zs_status st, const char* msg) { return fail(st, "%s", msg); }
+
+bool offload_fold(const zs_adam_hp* hp, int64_t step, HostScalars* out) {
+  g_last_error.clear();
+  if (check_hp(hp, step) != ZS_OK) return false;
+  zs_folded f;
+  fold_scalars(*hp, step, &f);
+  *out = HostScalars{f.b1, f.c1, f.b2, f.c2, f.eps, f.ss, f.rb, f.dk, 1.0f};
+  return true;
+}
+
+bool offload_reduce_shape(const uint16_t* const* grads, int32_t N, int64_t n, void* ws, double* sq,
+                          TwoPassShape* sh) {
+  if (n <= 0) return false;
+  reduce_shape(grads, N, n, ws, sq, 1.0f, sh);
+  return true;
+}
+
+int offload_blocks() { return auto_blocks(); }
+
+}  // namespace zs
 
 struct zs_list_plan {
   int device;
@@ -490,21 +542,7 @@ zs_status zs_reduce_grads_flat(const uint16_t* const* grad_chunks, int32_t N, in
       rs.push_back({(uintptr_t)sqnorm, (uintptr_t)sqnorm + 8, 0, 1});
       zs_status st = check_alias(rs);
       if (st) return st;
-      sh.gbar = L.gbar;
-      sh.partials = L.partials;
-      std::vector<const void*> ptrs(grad_chunks, grad_chunks + N);
-      std::vector<int> sizes(N, 2);
-      ptrs.push_back(L.gbar);
-      sizes.push_back(4);
-      const int64_t h = zs::common_peel_sized(ptrs.data(), sizes.data(), (int)ptrs.size());
-      if (h < 0) {
-        sh.scalar_only = 1;
-        sh.head = 0;
-      } else {
-        sh.scalar_only = 0;
-        sh.head = h < n ? h : n;
-      }
-      sh.ntiles = (n - sh.head + kTileElems - 1) / kTileElems;
+      reduce_shape(grad_chunks, N, n, workspace, sqnorm, (float)(1.0 / loss_scale), &sh);
     }
     return after_launch(zs::launch_reduce(grad_chunks, sh, grad_format, auto_blocks(), hs), hs,
                         "zs_reduce_grads_flat launch");

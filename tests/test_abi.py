@@ -209,3 +209,44 @@ def test_two_pass_rejects_bad_arguments_without_gpu():
     assert call2(p=ws + 256) == "ZS_ERR_ALIAS"                      # master over the workspace
     assert call2(tsq=A + 0x1100000 + 8) == "ZS_ERR_ALIAS"           # norm inside m
     assert call2(wsb=100) == "ZS_ERR_RANGE"
+
+
+# ------------------------------------------------------------ optimizer offload (host AdamW)
+@pytest.mark.parametrize("n,threads", [(1, 1), (7, 1), (8, 1), (1000, 3), (300_001, 8)])
+def test_cpu_adam_matches_oracle(orc, n, threads):
+    rng = np.random.default_rng(n)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    P = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    M = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    V = np.abs(rng.standard_normal(n) * 1e-6).astype(np.float32)
+    if n >= 16:
+        g[:6] = [0.0, -0.0, np.inf, -np.inf, np.nan, 1e-40]
+        P[6:9] = [1e-40, -0.0, 3e38]
+    hp = dict(pins.HP, weight_decay=0.1)
+    rP, rM, rV, rB, _ = orc.adam_from_gbar(g, P, M, V, hp, 42, 1.0, 0.0)
+    Pc, Mc, Vc, Bc = P.copy(), M.copy(), V.copy(), np.zeros(n, dtype=np.uint16)
+    zs.cpu_adam(g, Pc, Mc, Vc, Bc, hp, 42, threads)
+    for got, ref in ((Pc, rP), (Mc, rM), (Vc, rV)):
+        both_nan = np.isnan(got) & np.isnan(ref)
+        assert np.array_equal(got.view(np.uint32)[~both_nan], ref.view(np.uint32)[~both_nan])
+    nan = lambda b: ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+    assert np.array_equal(nan(Bc), nan(rB)) and np.array_equal(Bc[~nan(Bc)], rB[~nan(rB)])
+
+
+def test_offload_rejects_bad_arguments_without_gpu():
+    lib = zs.library()
+    h = ctypes.c_void_p()
+    assert zs.STATUS[lib.zs_offload_create(100, 4, ctypes.byref(h))] == "ZS_ERR_RANGE"
+    assert zs.STATUS[lib.zs_offload_create(1 << 20, 0, ctypes.byref(h))] == "ZS_ERR_RANGE"
+    assert zs.STATUS[lib.zs_offload_create(1 << 20, 4, ctypes.byref(h))] == "ZS_OK" and h
+    g = (ctypes.c_void_p * 2)(A + 0x100000, A + 0x200000)
+    hp = zs.AdamHPStruct(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    P = np.zeros(1024, np.float32)
+    # host arrays overlapping, before any device work
+    st = lib.zs_offload_step_flat(h, g, 2, 1024, P.ctypes.data, P.ctypes.data + 64, A, A + 0x300000,
+                                  ctypes.byref(hp), 1, None)
+    assert zs.STATUS[st] == "ZS_ERR_ALIAS"
+    st = lib.zs_offload_step_flat(h, g, 0, 1024, P.ctypes.data, P.ctypes.data, P.ctypes.data, A, ctypes.byref(hp), 1,
+                                  None)
+    assert zs.STATUS[st] == "ZS_ERR_RANGE"
+    lib.zs_offload_destroy(h)   # never allocated device buffers: nothing to wait for
