@@ -185,6 +185,39 @@ def cpu_baseline(w, target_s: float) -> dict:
                        f"{threads} threads of {cores} cores")
 
 
+def offload_breakdown(zs, torch, d, w, n, chunk) -> dict:
+    """Rates of the offload step's parts, each timed alone: the host AdamW over the whole shard (it reads
+    the fp32 mean gradient, master, m, v and writes master, m, v and the bf16 copy: 30 B/param of host
+    memory traffic) and one chunk's fp32 gradient copy to pinned memory and bf16 copy back."""
+    threads = min(16, len(os.sched_getaffinity(0)))
+    n = d["P"].numel()
+    g = torch.full((n,), 1e-3, dtype=torch.float32)
+    b = torch.empty(n, dtype=torch.int16)
+    t0 = time.perf_counter()
+    zs.cpu_adam(g, d["P"], d["M"], d["V"], b, w.hp(), w.step + 10_000, threads)
+    host_s = time.perf_counter() - t0
+    del g, b
+    k = min(chunk, n)
+    dg = torch.empty(k, dtype=torch.float32, device="cuda")
+    db = torch.empty(k, dtype=torch.int16, device="cuda")
+    hg = torch.empty(k, dtype=torch.float32).pin_memory()
+    hb = torch.empty(k, dtype=torch.int16).pin_memory()
+    rates = {}
+    for name, dst, src in (("d2h", hg, dg), ("h2d", db, hb)):
+        dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        rates[name] = 10 * src.numel() * src.element_size() / (e0.elapsed_time(e1) / 1e3) / 1e9
+    return {"host_adam_params_per_s": n / host_s, "host_adam_GBps": 30 * n / host_s / 1e9, "host_threads": threads,
+            "d2h_GBps": rates["d2h"], "h2d_GBps": rates["h2d"],
+            "pcie_bytes_per_param": 6, "chunk_elems": k}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,7 +232,7 @@ def main() -> int:
                     help="fused: the one-pass step; clip: two-pass with global-norm clipping (max_norm 1); "
                          "fp16: two-pass with fp16 replicas, loss scale 2^16, clipping and an fp16 working copy; "
                          "offload: fp32 state in host memory, AdamW on the CPU, reduction on the GPU")
-    ap.add_argument("--offload-chunk", type=int, default=1 << 24, help="parameters per offload pipeline chunk")
+    ap.add_argument("--offload-chunk", type=int, default=1 << 26, help="parameters per offload pipeline chunk")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -297,8 +330,11 @@ def main() -> int:
     achieved = bytes_per_launch / (ms / 1e3) / 1e9
     log(f"{ms:.3f} ms/step, {n / (ms / 1e3) / 1e9:.2f} G params/s, {achieved:.0f} GB/s")
 
+    offload_parts = None
     if offload is not None:
         offload.close()
+        offload_parts = offload_breakdown(zs, torch, d, w, n, args.offload_chunk)
+        log(f"offload parts: {offload_parts}")
     del d, plan
     torch.cuda.empty_cache()
     ceiling = None if args.no_copy else copy_ceiling()
@@ -325,6 +361,8 @@ def main() -> int:
         "cpu_baseline": base,
         "parity_sample": check,
     }
+    if offload_parts:
+        rec["offload"] = offload_parts
     print(json.dumps(rec), flush=True)
     return 0
 

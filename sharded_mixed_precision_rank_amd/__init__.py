@@ -467,7 +467,7 @@ class Offload:
     """Optimizer offload: fp32 master/m/v in host memory, AdamW on the CPU,
     replica reduction on the GPU, chunks pipelined over PCIe."""
 
-    def __init__(self, chunk_elems: int = 1 << 24, threads: int = 16):
+    def __init__(self, chunk_elems: int = 1 << 26, threads: int = 16):
         h = _vp()
         _check(_lib.zs_offload_create(chunk_elems, threads, ctypes.byref(h)), "zs_offload_create")
         self._h = h
