@@ -115,8 +115,10 @@ ZS_API zs_status zs_fold(const zs_adam_hp* hp, int64_t step, zs_folded* out);
                   update (the library keeps no state and never increments it)
      stream       the stream the kernel is enqueued on
    Layout: any natural alignment works; when every array can be brought to
-   16-byte alignment by the same element offset, the kernel uses 16-byte
-   vector accesses for all but at most 14 elements.
+   16-byte alignment by the same element offset, the kernel uses vector
+   accesses for all but at most 70 elements.  It prefers an offset that puts
+   every array on a 128-byte line boundary (arrays whose addresses agree
+   modulo 128 bytes, in elements, run fastest).
    Errors: ZS_ERR_NULL, ZS_ERR_RANGE, ZS_ERR_ALIGN, ZS_ERR_ALIAS (outputs must
    be pairwise disjoint and disjoint from every gradient range), ZS_ERR_HIP. */
 ZS_API zs_status zs_reduce_adam_flat(const uint16_t* const* grad_chunks, int32_t N, int64_t n, float* master,

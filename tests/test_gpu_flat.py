@@ -87,13 +87,19 @@ def test_lengths(env, orc, n):
     run_and_compare(env, orc, host, HP, 100, f"n={n}")
 
 
-@pytest.mark.parametrize("shift", [1, 2, 3, 5, 7])
-def test_common_misalignment_peels_a_head(env, orc, shift):
+@pytest.mark.parametrize("shift,n", [(1, 10_000), (2, 10_000), (3, 10_000), (5, 10_000), (7, 10_000),
+                                     (8, 10_000), (24, 10_000), (32, 10_000), (40, 10_000), (56, 10_000),
+                                     (63, 10_000), (72, 10_000), (8, 9), (8, 63), (8, 64), (8, 70), (8, 71),
+                                     (40, 33), (1, 70)])
+def test_common_misalignment_peels_a_head(env, orc, shift, n):
     """Every array starts `shift` elements past a 256-byte boundary: the kernel
-    peels a head of 8 - shift elements and runs the vector path on the rest."""
+    peels a head up to the next common line boundary (up to 63 elements; a
+    16-byte one when no line boundary is common) and runs the vector path on
+    the rest; shards too short for one group after the head run element by
+    element."""
     torch, zs, dev = env["torch"], env["zs"], env["dev"]
-    rng = np.random.default_rng(3000 + shift)
-    n, N = 10_000, 4
+    rng = np.random.default_rng(3000 + shift + n)
+    N = 4
     host = rand_host(rng, N, n)
     d = upload(torch, dev, host)
     B = torch.zeros(n, dtype=torch.int16, device=dev)
@@ -105,7 +111,7 @@ def test_common_misalignment_peels_a_head(env, orc, shift):
     got = download(dict(d, B=B))
     ref = dict(P=rP, M=rM, V=rV, B=rB)
     got_s = {k: v[shift:] for k, v in got.items()}
-    parity.assert_step(got_s, ref, f"shift={shift}")
+    parity.assert_step(got_s, ref, f"shift={shift} n={n}")
     assert parity.bit_identical(got_s, ref)
     # the elements before the view are untouched
     assert np.array_equal(got["P"][:shift], host["P"][:shift]) and np.all(got["B"][:shift] == 0)

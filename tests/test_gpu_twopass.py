@@ -118,7 +118,7 @@ def test_fp16_overflow_skips_the_step(env, orc):
 def test_misaligned_two_pass(env, orc):
     rng = np.random.default_rng(11)
     host = rand_case(rng, 3, 9_999)
-    for off in (1, 3):
+    for off in (1, 3, 8, 40, 63):
         gbar, sqv, got = run(env, host, HP, 2, max_norm=0.5, offset=off)
         ref_g = orc.reduce_unscale(host["G"], 0, 1.0)
         assert np.array_equal(gbar.view(np.uint32), ref_g.view(np.uint32))
