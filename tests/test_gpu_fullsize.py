@@ -1,0 +1,176 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (the library's default grid), on sampled outputs.
+
+Inputs are drawn in device memory by the seeded counter-based generator; the
+oracle recomputes each sampled position from the host's draws of the same
+counters, so no expected value comes from the device.  The tiny workload is
+compared at every position.  Ragged lists also check every gap position
+between tensors (the step must leave it untouched).  The two-pass global
+norm, which no sample covers, is checked against the float64 sum of squares
+of the fp32 mean-gradient buffer, whose values are themselves checked at the
+sampled positions.
+"""
+import numpy as np
+import pytest
+
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+SAMPLES = 200_000
+SENTINEL = 0x7FBF
+
+
+def workload(name):
+    from synth import workloads as W
+
+    return {"c1": lambda: W.C1, "c2": lambda: W.C2, "c3": W.C3, "c4": lambda: W.C4,
+            "c5": lambda: W.C5(1), "c5w": lambda: W.C5(10_000)}[name]()
+
+
+def positions(w, L, seed=1234):
+    """Sampled arena positions inside tensors (plus both ends), and every gap position."""
+    if L <= 1 << 21:
+        idx = np.arange(L, dtype=np.int64)
+    else:
+        rng = np.random.default_rng(seed)
+        idx = np.unique(np.concatenate([rng.integers(0, L, SAMPLES), np.arange(4096), np.arange(L - 4096, L)]))
+    gaps = np.zeros(0, dtype=np.int64)
+    if w.is_list:
+        offs, _ = w.layout()
+        sizes = np.asarray(w.sizes, dtype=np.int64)
+        inside = np.zeros(L, dtype=bool)
+        for o, n in zip(offs.tolist(), sizes.tolist()):
+            inside[o:o + n] = True
+        idx = idx[inside[idx]]
+        gaps = np.flatnonzero(~inside)
+    return idx, gaps
+
+
+def gather(torch, d, idx):
+    it = torch.from_numpy(idx).to(d["P"].device)
+    return dict(P=d["P"][it].cpu().numpy(), M=d["M"][it].cpu().numpy(), V=d["V"][it].cpu().numpy(),
+                B=d["B"].view(torch.int16)[it].cpu().numpy().view(np.uint16))
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "c5w"])
+def test_fused_step_full_size(orc, name):
+    import torch
+
+    import sharded_mixed_precision_rank_amd as zs
+    from synth import workloads as W
+
+    w = workload(name)
+    zs.set_grid_blocks(0)
+    d = W.device_inputs(w, b_fill=SENTINEL)
+    L = d["arena_len"]
+    plan = None
+    if w.is_list:
+        offs, _ = w.layout()
+        plan = zs.ListPlan.from_arenas(w.sizes, offs, d["G"], d["P"], d["M"], d["V"], d["B"])
+        plan.step(w.hp(), w.step)
+    else:
+        zs.reduce_adam_flat(d["G"], d["P"], d["M"], d["V"], d["B"], w.hp(), w.step)
+    torch.cuda.synchronize()
+    idx, gaps = positions(w, L)
+    got = gather(torch, d, idx)
+    h = W.host_inputs_at(w, idx)
+    P, M, V, B = orc.step(h["G"], h["P"], h["M"], h["V"], w.hp(), w.step)
+    ref = dict(P=P, M=M, V=V, B=B)
+    parity.assert_step(got, ref, f"{w.name} ({idx.size} positions)")
+    assert parity.bit_identical(got, ref), w.name
+    if gaps.size:
+        g = gather(torch, d, gaps)
+        hg = W.host_inputs_at(w, gaps)
+        for k in "PMV":
+            assert np.array_equal(g[k].view(np.uint32), hg[k].view(np.uint32)), f"{w.name}: gap {k} was written"
+        assert np.all(g["B"] == SENTINEL), f"{w.name}: gap of the working copy was written"
+    if plan is not None:
+        plan.close()
+    del d, plan
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("path", ["clip", "fp16"])
+def test_two_pass_full_size(orc, path):
+    """The 70B/64 shard through both passes: global-norm clipping at 1.0, with
+    bf16 replicas, or fp16 replicas at loss scale 2^16 with an fp16 working copy."""
+    import torch
+
+    import sharded_mixed_precision_rank_amd as zs
+    import synth
+    from synth import workloads as W
+
+    w = W.C4
+    zs.set_grid_blocks(0)
+    d = W.device_inputs(w)
+    n = d["arena_len"]
+    loss_scale = 2.0 ** 16 if path == "fp16" else 1.0
+    fmt = "fp16" if path == "fp16" else "bf16"
+    k = w.keys()
+    if path == "fp16":
+        tmp = torch.empty(n, dtype=torch.float32, device="cuda")
+        for r in range(w.N):
+            synth.dev_fill_normal_f32(tmp, k["G"][r], 0, w.g_sigma * loss_scale)
+            d["G"][r] = tmp.half()
+        del tmp
+        d["B"] = torch.zeros(n, dtype=torch.float16, device="cuda")
+    ws = torch.empty(zs.two_pass_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    sq = torch.empty(1, dtype=torch.float64, device="cuda")
+    zs.reduce_grads_flat(d["G"], ws, sq, loss_scale, fmt)
+    torch.cuda.synchronize()
+    start = (256 - ws.data_ptr() % 256) % 256
+    gbar = ws[start:start + 4 * n].view(torch.float32)
+    sqv = float(sq.item())
+    # the norm: a property at any size, against the buffer the sampled checks pin below
+    ref_sq = float((gbar.double() ** 2).sum().item())
+    assert abs(sqv - ref_sq) <= 1e-12 * ref_sq, (sqv, ref_sq)
+    idx, _ = positions(w, n)
+    it = torch.from_numpy(idx).to("cuda")
+    gbar_s = gbar[it].cpu().numpy()
+    zs.adam_from_grads_flat(ws, n, d["P"], d["M"], d["V"], d["B"], w.hp(), w.step, sq, 1.0, fmt)
+    torch.cuda.synchronize()
+    got = gather(torch, d, idx)
+    h = W.host_inputs_at(w, idx)
+    if path == "fp16":
+        G = np.stack([orc.f16(synth.normal_f32_at(k["G"][r], idx, w.g_sigma * loss_scale)) for r in range(w.N)])
+        gfmt = 1
+    else:
+        G, gfmt = h["G"], 0
+    g = orc.reduce_unscale(G, gfmt, loss_scale)
+    assert np.array_equal(gbar_s.view(np.uint32), g.view(np.uint32)), "pass 1 mean gradient"
+    P, M, V, B, taken = orc.adam_from_gbar(g, h["P"], h["M"], h["V"], w.hp(), w.step, sqv, 1.0, out_fmt=gfmt)
+    assert taken
+    ref = dict(P=P, M=M, V=V, B=B)
+    for key in "PMV":
+        parity.assert_f32(got[key], ref[key], f"{path} {key}")
+    assert parity.bit_identical(got, ref), path
+    del d, ws, sq, gbar
+    torch.cuda.empty_cache()
+
+
+def test_offload_full_size(orc):
+    """The 124M-parameter shard (N=8) with its fp32 state in pinned host memory."""
+    import torch
+
+    import sharded_mixed_precision_rank_amd as zs
+    from synth import workloads as W
+
+    w = W.C2
+    d = W.device_inputs(w)
+    for key in "PMV":
+        d[key] = d[key].cpu().pin_memory()
+    torch.cuda.empty_cache()
+    with zs.Offload() as off:
+        off.step(d["G"], d["P"], d["M"], d["V"], d["B"], w.hp(), w.step)
+    torch.cuda.synchronize()
+    idx, _ = positions(w, d["arena_len"])
+    got = dict(P=d["P"].numpy()[idx], M=d["M"].numpy()[idx], V=d["V"].numpy()[idx],
+               B=d["B"].view(torch.int16)[torch.from_numpy(idx).cuda()].cpu().numpy().view(np.uint16))
+    h = W.host_inputs_at(w, idx)
+    P, M, V, B = orc.step(h["G"], h["P"], h["M"], h["V"], w.hp(), w.step)
+    ref = dict(P=P, M=M, V=V, B=B)
+    parity.assert_step(got, ref, "offload 124M")
+    assert parity.bit_identical(got, ref)
+    del d
+    torch.cuda.empty_cache()
