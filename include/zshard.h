@@ -252,10 +252,14 @@ ZS_API zs_status zs_offload_create(int64_t chunk_elems, int32_t threads, zs_offl
 /* One step with host-resident state.  grad_chunks: host array of N device
    pointers (bf16); master, m, v: HOST fp32 arrays of n, updated in place
    before the call returns; param_dev: DEVICE bf16 array of n.  The reduce
-   kernels run on `stream`; work enqueued on `stream` after the call sees the
-   new param_dev.  Blocks until the host state is updated.  Errors:
-   ZS_ERR_NULL, ZS_ERR_RANGE, ZS_ERR_ALIGN, ZS_ERR_ALIAS, ZS_ERR_HIP (the host
-   state may then be partly updated). */
+   kernels run on `stream`; the copies into param_dev run on the context's
+   stream after all work already enqueued on `stream`, and work enqueued on
+   `stream` after the call sees the new param_dev.  Blocks until the host
+   state is updated.  A context is bound to the device current at its first
+   step; calling it with another device current fails with ZS_ERR_RANGE.
+   Errors: ZS_ERR_NULL, ZS_ERR_RANGE, ZS_ERR_ALIGN, ZS_ERR_ALIAS, ZS_ERR_NOMEM,
+   ZS_ERR_HIP (after ZS_ERR_HIP or ZS_ERR_NOMEM the host state may be partly
+   updated). */
 ZS_API zs_status zs_offload_step_flat(zs_offload_t ctx, const uint16_t* const* grad_chunks, int32_t N, int64_t n,
                                       float* master, float* m, float* v, uint16_t* param_dev, const zs_adam_hp* hp,
                                       int64_t step, zs_stream stream);

@@ -103,11 +103,17 @@ void cpu_adam(const float* g, int64_t n, float* P, float* M, float* V, uint16_t*
     return;
   }
   std::vector<std::thread> pool;
-  pool.reserve(threads);
+  pool.reserve(threads);  // may throw before any element is touched
   for (int t = 0; t < threads; ++t) {
     // 8-aligned split points keep the vector path on whole groups
     const int64_t lo = (n * t / threads) & ~int64_t(7), hi = t + 1 == threads ? n : (n * (t + 1) / threads) & ~int64_t(7);
-    pool.emplace_back(body, lo, hi);
+    bool started = false;
+    try {
+      pool.emplace_back(body, lo, hi);
+      started = true;
+    } catch (...) {
+    }
+    if (!started) body(lo, hi);  // no thread to spare: this range runs here
   }
   for (auto& th : pool) th.join();
 }

@@ -37,12 +37,13 @@ struct zs_offload {
   uint16_t* hb[2] = {nullptr, nullptr};    // pinned: bf16 chunks
   hipStream_t up = nullptr;                // host-to-device copies
   hipEvent_t ev_down[2] = {nullptr, nullptr}, ev_up[2] = {nullptr, nullptr}, ev_done = nullptr;
+  hipEvent_t ev_start = nullptr;           // orders the copy stream after the caller's stream
 };
 
 namespace {
 
-void release(zs_offload* c) {
-  if (!c) return;
+// Frees every buffer, stream and event the context holds (on its device).
+void free_resources(zs_offload* c) {
   if (c->device >= 0) {
     int cur = 0;
     (void)hipGetDevice(&cur);
@@ -57,9 +58,20 @@ void release(zs_offload* c) {
     }
     if (c->sq) (void)hipFree(c->sq);
     if (c->ev_done) (void)hipEventDestroy(c->ev_done);
+    if (c->ev_start) (void)hipEventDestroy(c->ev_start);
     if (c->up) (void)hipStreamDestroy(c->up);
     (void)hipSetDevice(cur);
   }
+  const int64_t chunk = c->chunk;
+  const int threads = c->threads;
+  *c = zs_offload{};
+  c->chunk = chunk;
+  c->threads = threads;
+}
+
+void release(zs_offload* c) {
+  if (!c) return;
+  free_resources(c);
   delete c;
 }
 
@@ -78,9 +90,14 @@ hipError_t ensure(zs_offload* c) {
   }
   if (e == hipSuccess) e = hipMalloc((void**)&c->sq, 8);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_done, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_start, hipEventDisableTiming);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->up, hipStreamNonBlocking);
+  if (e != hipSuccess) free_resources(c);  // the next step starts from scratch
   return e;
 }
+
+zs_status run_step(zs_offload* ctx, const uint16_t* const* grad_chunks, int32_t N, int64_t n, float* master,
+                   float* m, float* v, uint16_t* param_dev, const zs::HostScalars& c, hipStream_t hs);
 
 }  // namespace
 
@@ -110,7 +127,11 @@ zs_status zs_cpu_adam(const float* gbar, int64_t n, float* master, float* m, flo
   if (n == 0) return ZS_OK;
   if (!gbar || !master || !m || !v || !param_bf16) return zs::offload_fail(ZS_ERR_NULL, "NULL array");
   if (threads < 1) threads = 1;
-  zs::cpu_adam(gbar, n, master, m, v, param_bf16, c, threads);
+  try {
+    zs::cpu_adam(gbar, n, master, m, v, param_bf16, c, threads);
+  } catch (...) {
+    return zs::offload_fail(ZS_ERR_HIP, "host error (thread creation)");
+  }
   return ZS_OK;
 }
 
@@ -141,9 +162,32 @@ zs_status zs_offload_step_flat(zs_offload_t ctx, const uint16_t* const* grad_chu
         return zs::offload_fail(ZS_ERR_ALIAS, "param overlaps a gradient chunk");
     }
   }
-  hipError_t e = ensure(ctx);
+  try {
+    return run_step(ctx, grad_chunks, N, n, master, m, v, param_dev, c, static_cast<hipStream_t>(stream));
+  } catch (const std::bad_alloc&) {
+    return zs::offload_fail(ZS_ERR_NOMEM, "host allocation failed");
+  } catch (...) {
+    return zs::offload_fail(ZS_ERR_HIP, "host error (thread creation)");
+  }
+}
+
+}  // extern "C"
+
+namespace {
+
+zs_status run_step(zs_offload* ctx, const uint16_t* const* grad_chunks, int32_t N, int64_t n, float* master,
+                   float* m, float* v, uint16_t* param_dev, const zs::HostScalars& c, hipStream_t hs) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return zs::offload_fail(ZS_ERR_HIP, hipGetErrorString(e));
-  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (ctx->device >= 0 && cur != ctx->device)
+    return zs::offload_fail(ZS_ERR_RANGE, "the context belongs to another device than the current one");
+  e = ensure(ctx);
+  if (e != hipSuccess) return zs::offload_fail(ZS_ERR_HIP, hipGetErrorString(e));
+  // the uploads run on the context's stream: order them after everything already on the caller's stream
+  e = hipEventRecord(ctx->ev_start, hs);
+  if (e == hipSuccess) e = hipStreamWaitEvent(ctx->up, ctx->ev_start, 0);
+  if (e != hipSuccess) return zs::offload_fail(ZS_ERR_HIP, hipGetErrorString(e));
   const int64_t C = ctx->chunk;
   const int64_t K = (n + C - 1) / C;
   std::vector<const uint16_t*> g(N);
@@ -162,16 +206,24 @@ zs_status zs_offload_step_flat(zs_offload_t ctx, const uint16_t* const* grad_chu
 
   e = enqueue_down(0);
   if (e == hipSuccess && K > 1) e = enqueue_down(1);
-  for (int64_t k = 0; k < K && e == hipSuccess; ++k) {
-    const int s = (int)(k & 1);
-    const int64_t lo = k * C, len = n - lo < C ? n - lo : C;
-    e = hipEventSynchronize(ctx->ev_down[s]);
-    if (e == hipSuccess && k >= 2) e = hipEventSynchronize(ctx->ev_up[s]);  // its bf16 buffer is free
-    if (e != hipSuccess) break;
-    zs::cpu_adam(ctx->hg[s], len, master + lo, m + lo, v + lo, ctx->hb[s], c, ctx->threads);
-    e = hipMemcpyAsync(param_dev + lo, ctx->hb[s], 2 * (size_t)len, hipMemcpyHostToDevice, ctx->up);
-    if (e == hipSuccess) e = hipEventRecord(ctx->ev_up[s], ctx->up);
-    if (e == hipSuccess && k + 2 < K) e = enqueue_down(k + 2);
+  // A host exception (thread creation) inside the loop must not leave copies in flight
+  // into buffers the caller may free: drain both streams before passing it on.
+  try {
+    for (int64_t k = 0; k < K && e == hipSuccess; ++k) {
+      const int s = (int)(k & 1);
+      const int64_t lo = k * C, len = n - lo < C ? n - lo : C;
+      e = hipEventSynchronize(ctx->ev_down[s]);
+      if (e == hipSuccess && k >= 2) e = hipEventSynchronize(ctx->ev_up[s]);  // its bf16 buffer is free
+      if (e != hipSuccess) break;
+      zs::cpu_adam(ctx->hg[s], len, master + lo, m + lo, v + lo, ctx->hb[s], c, ctx->threads);
+      e = hipMemcpyAsync(param_dev + lo, ctx->hb[s], 2 * (size_t)len, hipMemcpyHostToDevice, ctx->up);
+      if (e == hipSuccess) e = hipEventRecord(ctx->ev_up[s], ctx->up);
+      if (e == hipSuccess && k + 2 < K) e = enqueue_down(k + 2);
+    }
+  } catch (...) {
+    (void)hipStreamSynchronize(hs);
+    (void)hipStreamSynchronize(ctx->up);
+    throw;
   }
   if (e == hipSuccess) e = hipEventRecord(ctx->ev_done, ctx->up);
   if (e == hipSuccess) e = hipStreamWaitEvent(hs, ctx->ev_done, 0);  // later work on `stream` sees the copy
@@ -184,4 +236,4 @@ zs_status zs_offload_step_flat(zs_offload_t ctx, const uint16_t* const* grad_chu
   return ZS_OK;
 }
 
-}  // extern "C"
+}  // namespace

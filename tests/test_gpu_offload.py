@@ -89,3 +89,31 @@ def test_offload_against_oracle(orc, n, N, t, chunk):
     ref = dict(P=Pr, M=Mr, V=Vr, B=Br)
     parity.assert_step(got, ref, f"offload n={n} N={N}")
     assert parity.bit_identical(got, ref)
+
+
+def test_offload_copies_follow_earlier_work_on_the_stream(orc):
+    """Work already on the caller's stream that writes the working copy (here a
+    bounded spin, then a fill) lands before the step's bf16 copies, not after."""
+    import torch
+
+    import sharded_mixed_precision_rank_amd as zs
+
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(77)
+    n, N, t = 50_000, 2, 4
+    G = np.stack([((rng.standard_normal(n) * 1e-3).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+                  for _ in range(N)])
+    P = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    Z = np.zeros(n, np.float32)
+    Gd = [torch.from_numpy(np.ascontiguousarray(g).view(np.int16)).to(dev) for g in G]
+    Ph, Mh, Vh = (torch.from_numpy(x.copy()).pin_memory() for x in (P, Z, Z))
+    Bo = torch.zeros(n, dtype=torch.int16, device=dev)
+    torch.cuda.synchronize()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(20_000_000)  # a few milliseconds of spinning on the current stream
+    Bo.fill_(0x1234)
+    with zs.Offload(8192, 2) as off:
+        off.step(Gd, Ph, Mh, Vh, Bo, HP, t)
+    torch.cuda.synchronize()
+    _, _, _, Br = orc.step(G, P, Z, Z, HP, t)
+    assert np.array_equal(Bo.cpu().numpy().view(np.uint16), Br)
