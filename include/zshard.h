@@ -151,7 +151,9 @@ typedef struct zs_list_plan* zs_list_plan_t;
 ZS_API zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_t N, zs_stream stream,
                                      zs_list_plan_t* out);
 
-/* The step on every tensor of the plan: one kernel launch on `stream`. */
+/* The step on every tensor of the plan: one kernel launch on `stream`.  The
+   plan's table lives on the device that was current at creation; calling with
+   another device current fails with ZS_ERR_RANGE. */
 ZS_API zs_status zs_reduce_adam_list_plan(zs_list_plan_t plan, const zs_adam_hp* hp, int64_t step,
                                           zs_stream stream);
 

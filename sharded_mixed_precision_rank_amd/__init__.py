@@ -149,14 +149,29 @@ def set_grid_blocks(blocks: int) -> None:
     _check(_lib.zs_set_grid_blocks(blocks), "zs_set_grid_blocks")
 
 
-def _stream_handle(stream):
+def _stream_handle(stream, device=None):
+    """The raw stream handle: torch's current stream of ``device`` by default."""
     if stream is None:
         import torch
 
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, int):
         return stream
+    if device is not None and getattr(stream, "device", device) != device:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {device}")
     return stream.cuda_stream
+
+
+def _one_device(*tensors):
+    """The device every tensor lives on (the current device if there are none).
+    The library launches on the current device, so each call runs with this
+    device made current; tensors spread over devices are rejected."""
+    import torch
+
+    devs = {t.device for t in tensors}
+    if len(devs) > 1:
+        raise ValueError(f"tensors live on several devices: {sorted(str(d) for d in devs)}")
+    return devs.pop() if devs else torch.device("cuda", torch.cuda.current_device())
 
 
 def _dev_check(t, dtypes, name):
@@ -210,17 +225,22 @@ def reduce_adam_flat(grads: Sequence, master, m, v, param, hp, step: int, stream
     """One shard step: average ``grads`` (N bf16 device tensors, rank order) and
     apply AdamW to ``master``/``m``/``v`` in place, writing the bf16 copy to
     ``param``.  Enqueued on ``stream`` (default: torch's current stream)."""
+    import torch
+
     N = len(grads)
     n = _tensor_args(grads, master, m, v, param)
+    dev = _one_device(master, m, v, param, *grads)
     tab = (_vp * max(N, 1))(*[g.data_ptr() for g in grads])
     h = _hp(hp)
-    _check(_lib.zs_reduce_adam_flat(tab, N, n, master.data_ptr(), m.data_ptr(), v.data_ptr(), param.data_ptr(),
-                                    ctypes.byref(h), step, _stream_handle(stream)), "zs_reduce_adam_flat")
+    with torch.cuda.device(dev):
+        _check(_lib.zs_reduce_adam_flat(tab, N, n, master.data_ptr(), m.data_ptr(), v.data_ptr(), param.data_ptr(),
+                                        ctypes.byref(h), step, _stream_handle(stream, dev)), "zs_reduce_adam_flat")
 
 
 def reduce_adam_flat_ptrs(grad_ptrs: Sequence[int], n: int, master: int, m: int, v: int, param: int, hp,
                           step: int, stream) -> None:
-    """Raw-pointer form of :func:`reduce_adam_flat` (device addresses as ints)."""
+    """Raw-pointer form of :func:`reduce_adam_flat` (device addresses as ints,
+    all on the current device)."""
     N = len(grad_ptrs)
     tab = (_vp * max(N, 1))(*grad_ptrs)
     h = _hp(hp)
@@ -239,6 +259,7 @@ class ShardTensor:
 
 
 def _tensor_table(tensors: Sequence[ShardTensor], N: int):
+    _one_device(*[x for t in tensors for x in (t.master, t.m, t.v, t.param, *t.grads)])
     keep = []
     tab = (TensorStruct * max(len(tensors), 1))()
     for i, t in enumerate(tensors):
@@ -257,11 +278,16 @@ class ListPlan:
     :meth:`step` is one kernel launch covering every tensor."""
 
     def __init__(self, tensors: Sequence[ShardTensor], N: int, stream=None):
+        import torch
+
         tab, keep = _tensor_table(tensors, N)
+        dev = _one_device(*[t.master for t in tensors])
         h = _vp()
-        _check(_lib.zs_list_plan_create(tab, len(tensors), N, _stream_handle(stream), ctypes.byref(h)),
-               "zs_list_plan_create")
+        with torch.cuda.device(dev):
+            _check(_lib.zs_list_plan_create(tab, len(tensors), N, _stream_handle(stream, dev), ctypes.byref(h)),
+                   "zs_list_plan_create")
         self._h = h
+        self._dev = dev
         self.N = N
         self._tensors = list(tensors)   # the plan holds their addresses: keep them alive
 
@@ -272,9 +298,12 @@ class ListPlan:
         and of every replica's gradient arena in ``grads``."""
         import numpy as np
 
+        import torch
+
         N = len(grads)
         L = master.numel()
         _tensor_args(grads, master, m, v, param)
+        dev = _one_device(master, m, v, param, *grads)
         sizes = np.asarray(sizes, dtype=np.int64)
         offsets = np.asarray(offsets, dtype=np.int64)
         if sizes.shape != offsets.shape or (sizes.size and (offsets.min() < 0 or (offsets + sizes).max() > L)):
@@ -293,9 +322,11 @@ class ListPlan:
         assert ctypes.sizeof(TensorStruct) == 48
         self = cls.__new__(cls)
         h = _vp()
-        _check(_lib.zs_list_plan_create(ctypes.cast(rec.ctypes.data, ctypes.POINTER(TensorStruct)), T, N,
-                                        _stream_handle(stream), ctypes.byref(h)), "zs_list_plan_create")
+        with torch.cuda.device(dev):
+            _check(_lib.zs_list_plan_create(ctypes.cast(rec.ctypes.data, ctypes.POINTER(TensorStruct)), T, N,
+                                            _stream_handle(stream, dev), ctypes.byref(h)), "zs_list_plan_create")
         self._h = h
+        self._dev = dev
         self.N = N
         self._tensors = [grads, master, m, v, param]
         return self
@@ -303,9 +334,12 @@ class ListPlan:
     def step(self, hp, step: int, stream=None) -> None:
         if not self._h:
             raise ValueError("plan is closed")
+        import torch
+
         h = _hp(hp)
-        _check(_lib.zs_reduce_adam_list_plan(self._h, ctypes.byref(h), step, _stream_handle(stream)),
-               "zs_reduce_adam_list_plan")
+        with torch.cuda.device(self._dev):
+            _check(_lib.zs_reduce_adam_list_plan(self._h, ctypes.byref(h), step, _stream_handle(stream, self._dev)),
+                   "zs_reduce_adam_list_plan")
 
     def info(self) -> dict:
         n, t, c = _i64(), _i32(), _i32()
@@ -334,10 +368,14 @@ class ListPlan:
 
 def reduce_adam_list(tensors: Sequence[ShardTensor], N: int, hp, step: int, stream=None) -> None:
     """One-shot list step (builds a plan, runs it, waits, frees it)."""
+    import torch
+
     tab, keep = _tensor_table(tensors, N)
+    dev = _one_device(*[t.master for t in tensors])
     h = _hp(hp)
-    _check(_lib.zs_reduce_adam_list(tab, len(tensors), N, ctypes.byref(h), step, _stream_handle(stream)),
-           "zs_reduce_adam_list")
+    with torch.cuda.device(dev):
+        _check(_lib.zs_reduce_adam_list(tab, len(tensors), N, ctypes.byref(h), step, _stream_handle(stream, dev)),
+               "zs_reduce_adam_list")
 
 
 # ------------------------------------------------------------ two-pass form
@@ -365,10 +403,12 @@ def reduce_grads_flat(grads: Sequence, workspace, sqnorm, loss_scale: float = 1.
             raise ValueError(f"grads[{r}] has {g.numel()} elements, grads[0] has {n}")
     _dev_check(workspace, (torch.uint8, torch.int8, torch.float32, torch.float64), "workspace")
     _dev_check(sqnorm, (torch.float64,), "sqnorm")
+    dev = _one_device(workspace, sqnorm, *grads)
     tab = (_vp * max(N, 1))(*[g.data_ptr() for g in grads])
-    _check(_lib.zs_reduce_grads_flat(tab, N, n, _fmt(grad_format), loss_scale, workspace.data_ptr(),
-                                     workspace.numel() * workspace.element_size(), sqnorm.data_ptr(),
-                                     _stream_handle(stream)), "zs_reduce_grads_flat")
+    with torch.cuda.device(dev):
+        _check(_lib.zs_reduce_grads_flat(tab, N, n, _fmt(grad_format), loss_scale, workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(), sqnorm.data_ptr(),
+                                         _stream_handle(stream, dev)), "zs_reduce_grads_flat")
 
 
 def adam_from_grads_flat(workspace, n: int, master, m, v, param, hp, step: int, total_sq, max_norm: float = 0.0,
@@ -383,14 +423,18 @@ def adam_from_grads_flat(workspace, n: int, master, m, v, param, hp, step: int, 
     _dev_check(v, _f32_types(), "v")
     _dev_check(param, _half_types(), "param")
     _dev_check(total_sq, (torch.float64,), "total_sq")
+    _dev_check(workspace, (torch.uint8, torch.int8, torch.float32, torch.float64), "workspace")
     for name, t in (("master", master), ("m", m), ("v", v), ("param", param)):
         if t.numel() != n:
             raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    dev = _one_device(workspace, master, m, v, param, total_sq)
     h = _hp(hp)
-    _check(_lib.zs_adam_from_grads_flat(workspace.data_ptr(), workspace.numel() * workspace.element_size(), n,
-                                        master.data_ptr(), m.data_ptr(), v.data_ptr(), param.data_ptr(),
-                                        _fmt(param_format), ctypes.byref(h), step, total_sq.data_ptr(), max_norm,
-                                        int(skip_nonfinite), _stream_handle(stream)), "zs_adam_from_grads_flat")
+    with torch.cuda.device(dev):
+        _check(_lib.zs_adam_from_grads_flat(workspace.data_ptr(), workspace.numel() * workspace.element_size(), n,
+                                            master.data_ptr(), m.data_ptr(), v.data_ptr(), param.data_ptr(),
+                                            _fmt(param_format), ctypes.byref(h), step, total_sq.data_ptr(), max_norm,
+                                            int(skip_nonfinite), _stream_handle(stream, dev)),
+               "zs_adam_from_grads_flat")
 
 
 def clipped_step_flat(grads: Sequence, master, m, v, param, hp, step: int, max_norm: float = 0.0,
@@ -483,10 +527,17 @@ class Offload:
         ptrs = [_host_ptr(x, "float32") for x in (master, m, v)]
         if any(k != n for _, k in ptrs):
             raise ValueError("host master/m/v must have the parameter count")
+        import torch
+
+        if not self._h:
+            raise ValueError("offload context is closed")
+        dev = _one_device(param, *grads)
         tab = (_vp * max(N, 1))(*[g.data_ptr() for g in grads])
         h = _hp(hp)
-        _check(_lib.zs_offload_step_flat(self._h, tab, N, n, ptrs[0][0], ptrs[1][0], ptrs[2][0], param.data_ptr(),
-                                         ctypes.byref(h), step, _stream_handle(stream)), "zs_offload_step_flat")
+        with torch.cuda.device(dev):
+            _check(_lib.zs_offload_step_flat(self._h, tab, N, n, ptrs[0][0], ptrs[1][0], ptrs[2][0],
+                                             param.data_ptr(), ctypes.byref(h), step, _stream_handle(stream, dev)),
+                   "zs_offload_step_flat")
 
     def close(self) -> None:
         if self._h:

@@ -470,24 +470,41 @@ zs_status zs_reduce_adam_list_plan(zs_list_plan_t plan, const zs_adam_hp* hp, in
   zs_status st = check_hp(hp, step);
   if (st) return st;
   if (plan->n_chunks == 0) return ZS_OK;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (cur != plan->device)  // the table lives in the other device's memory
+    return fail(ZS_ERR_RANGE, "the plan was built on device %d, device %d is current", plan->device, cur);
   const zs::Scalars c = make_scalars(*hp, step, plan->N);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   return after_launch(zs::launch_list(plan->chunks, plan->n_chunks, plan->tensors, plan->gptrs, c, auto_blocks(), hs),
                       hs, "zs_reduce_adam_list launch");
 }
 
-void zs_list_plan_destroy(zs_list_plan_t plan) {
+}  // extern "C"
+
+namespace {
+
+// Frees a plan; with wait_device, first waits for every stream of its device
+// (the plan may have been launched on any of them).
+void free_plan(zs_list_plan_t plan, bool wait_device) {
   if (!plan) return;
   if (plan->table) {
     int cur = 0;
     (void)hipGetDevice(&cur);
     (void)hipSetDevice(plan->device);
-    (void)hipDeviceSynchronize();
+    if (wait_device) (void)hipDeviceSynchronize();
     (void)hipFree(plan->table);
     (void)hipSetDevice(cur);
   }
   delete plan;
 }
+
+}  // namespace
+
+extern "C" {
+
+void zs_list_plan_destroy(zs_list_plan_t plan) { free_plan(plan, true); }
 
 zs_status zs_reduce_adam_list(const zs_tensor* tensors, int32_t T, int32_t N, const zs_adam_hp* hp, int64_t step,
                               zs_stream stream) {
@@ -497,11 +514,10 @@ zs_status zs_reduce_adam_list(const zs_tensor* tensors, int32_t T, int32_t N, co
   st = zs_list_plan_create(tensors, T, N, stream, &plan);
   if (st) return st;
   st = zs_reduce_adam_list_plan(plan, hp, step, stream);
-  if (st == ZS_OK) {
-    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) st = hip_fail(e, "zs_reduce_adam_list");
-  }
-  zs_list_plan_destroy(plan);
+  // the plan's only launch is on `stream`: once the stream is idle the table is free
+  const hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (st == ZS_OK && e != hipSuccess) st = hip_fail(e, "zs_reduce_adam_list");
+  free_plan(plan, e != hipSuccess);
   return st;
 }
 

@@ -250,3 +250,18 @@ def test_offload_rejects_bad_arguments_without_gpu():
                                   None)
     assert zs.STATUS[st] == "ZS_ERR_RANGE"
     lib.zs_offload_destroy(h)   # never allocated device buffers: nothing to wait for
+
+
+def test_binding_rejects_tensors_on_several_devices():
+    """The library launches on the current device, so the binding makes the
+    tensors' device current and refuses a call whose tensors are spread over
+    several devices (checked here with host and meta tensors, no GPU)."""
+    import torch
+
+    import sharded_mixed_precision_rank_amd as zs
+
+    a = torch.zeros(4)
+    b = torch.zeros(4, device="meta")
+    assert zs._one_device(a, torch.ones(2)) == torch.device("cpu")
+    with pytest.raises(ValueError, match="several devices"):
+        zs._one_device(a, b)
