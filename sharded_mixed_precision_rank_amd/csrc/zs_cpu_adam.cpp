@@ -54,6 +54,8 @@ __attribute__((target("avx2"))) void range_avx2(const float* g, int64_t lo, int6
   const __m256i abs_mask = _mm256_set1_epi32(0x7FFFFFFF), inf = _mm256_set1_epi32(0x7F800000),
                 round = _mm256_set1_epi32(0x7FFF), one = _mm256_set1_epi32(1),
                 quiet = _mm256_set1_epi32(0x0040);
+  // The bf16 output is write-only: stream it past the cache when it is 16-byte aligned.
+  const bool stream_b = ((reinterpret_cast<uintptr_t>(B + lo) & 15) == 0);
   int64_t i = lo;
   for (; i + 8 <= hi; i += 8) {
     const __m256 gi = _mm256_mul_ps(_mm256_loadu_ps(g + i), kk);
@@ -72,10 +74,15 @@ __attribute__((target("avx2"))) void range_avx2(const float* g, int64_t lo, int6
     __m256i r = _mm256_srli_epi32(_mm256_add_epi32(_mm256_add_epi32(w, round), lsb), 16);
     const __m256i is_nan = _mm256_cmpgt_epi32(_mm256_and_si256(w, abs_mask), inf);
     r = _mm256_blendv_epi8(r, _mm256_or_si256(_mm256_srli_epi32(w, 16), quiet), is_nan);
-    alignas(32) uint32_t tmp[8];
-    _mm256_store_si256(reinterpret_cast<__m256i*>(tmp), r);
-    for (int j = 0; j < 8; ++j) B[i + j] = (uint16_t)tmp[j];
+    // eight 16-bit values (each < 2^16, so the unsigned-saturating pack is exact) into 16 bytes
+    const __m256i packed = _mm256_permute4x64_epi64(_mm256_packus_epi32(r, r), 0x08);
+    const __m128i b8 = _mm256_castsi256_si128(packed);
+    if (stream_b)
+      _mm_stream_si128(reinterpret_cast<__m128i*>(B + i), b8);
+    else
+      _mm_storeu_si128(reinterpret_cast<__m128i*>(B + i), b8);
   }
+  if (stream_b) _mm_sfence();  // streamed stores are visible before the caller reads or copies B
   range_scalar(g, i, hi, P, M, V, B, c);
 }
 

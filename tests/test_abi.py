@@ -224,8 +224,15 @@ def test_cpu_adam_matches_oracle(orc, n, threads):
         P[6:9] = [1e-40, -0.0, 3e38]
     hp = dict(pins.HP, weight_decay=0.1)
     rP, rM, rV, rB, _ = orc.adam_from_gbar(g, P, M, V, hp, 42, 1.0, 0.0)
-    Pc, Mc, Vc, Bc = P.copy(), M.copy(), V.copy(), np.zeros(n, dtype=np.uint16)
-    zs.cpu_adam(g, Pc, Mc, Vc, Bc, hp, 42, threads)
+    Pc, Mc, Vc = P.copy(), M.copy(), V.copy()
+    for shift in (0, 1):  # the bf16 output 16-byte aligned (streamed stores) and not
+        Pc, Mc, Vc = P.copy(), M.copy(), V.copy()
+        Bc = np.zeros(n + 8, dtype=np.uint16)[8 - shift:8 - shift + n]
+        zs.cpu_adam(g, Pc, Mc, Vc, Bc, hp, 42, threads)
+        if shift == 0:
+            B0 = Bc.copy()
+        else:
+            assert np.array_equal(Bc, B0)
     for got, ref in ((Pc, rP), (Mc, rM), (Vc, rV)):
         both_nan = np.isnan(got) & np.isnan(ref)
         assert np.array_equal(got.view(np.uint32)[~both_nan], ref.view(np.uint32)[~both_nan])
