@@ -35,10 +35,21 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# bench.py --workload NAME
+WORKLOADS = {
+    "flat-1m": lambda W: W.FLAT_1M_N2,                             # 2^20 params, N=2, cold, step 1
+    "flat-124m": lambda W: W.FLAT_124M_N8,                         # 124M params, N=8, warm, step 100
+    "list-llama7b": lambda W: W.list_llama7b_dp8_n8(),             # 288 tensors, 809.5M params, N=8
+    "flat-70b": lambda W: W.FLAT_70B_DP64_N64,                     # 70B/64 shard, N=64, step 5000, wd 0.1
+    "list-ragged": lambda W: W.list_ragged_20000_n16(1),           # 20,000 ragged tensors, N=16, cold
+    "list-ragged-warm": lambda W: W.list_ragged_20000_n16(10000),  # the same, warm, step 10000
+}
+
+
 def workload(name: str):
     from synth import workloads as W
 
-    return {"c1": W.C1, "c2": W.C2, "c3": W.C3(), "c4": W.C4, "c5": W.C5(1), "c5w": W.C5(10000)}[name]
+    return WORKLOADS[name](W)
 
 
 def kernel_hash() -> str:
@@ -177,7 +188,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "c5w"])
+    ap.add_argument("--workload", default="flat-70b", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 = skip)")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy-kernel ceiling")
     ap.add_argument("--blocks", type=int, default=0, help="workgroups per launch (0 = library default)")
@@ -189,7 +200,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build runs one rank's shard step on a single MI355X and has no "
+        print("bench.py measures one GPU: the library runs one rank's shard step on a single MI355X and has no "
               "multi-GPU path; run with --gpus 1", file=sys.stderr)
         return 2
 

@@ -103,17 +103,17 @@ def log_uniform_sizes(count: int, lo: int, hi: int, seed: int = 0):
 
 
 # The five workloads.
-C1 = Workload("flat-1M-N2", N=2, step=1, weight_decay=0.0, warm=False, n_flat=1_048_576)
-C2 = Workload("flat-124M-N8", N=8, step=100, weight_decay=0.0, warm=True, n_flat=124_000_000)
-C4 = Workload("flat-70B/64-N64", N=64, step=5000, weight_decay=0.1, warm=True, n_flat=1_093_750_000)
+FLAT_1M_N2 = Workload("flat-1M-N2", N=2, step=1, weight_decay=0.0, warm=False, n_flat=1_048_576)
+FLAT_124M_N8 = Workload("flat-124M-N8", N=8, step=100, weight_decay=0.0, warm=True, n_flat=124_000_000)
+FLAT_70B_DP64_N64 = Workload("flat-70B/64-N64", N=64, step=5000, weight_decay=0.1, warm=True, n_flat=1_093_750_000)
 
 
-def C3() -> Workload:
+def list_llama7b_dp8_n8() -> Workload:
     return Workload("list-llama7b/8-N8", N=8, step=1000, weight_decay=0.0, warm=True,
                     sizes=llama7b_rank_shard_sizes())
 
 
-def C5(step: int = 1) -> Workload:
+def list_ragged_20000_n16(step: int = 1) -> Workload:
     return Workload(f"list-20000-ragged-N16-t{step}", N=16, step=step, weight_decay=0.0, warm=step > 1,
                     sizes=log_uniform_sizes(20_000, 64, 1 << 20), zero_frac=0.001)
 

@@ -60,9 +60,9 @@ def test_c1_flat_1M_N2_first_step(env, orc):
     """Flat shard of 2^20 params, 2 replicas, cold state, step 1 (the small workload)."""
     from synth import workloads as W
 
-    w = W.C1
+    w = W.FLAT_1M_N2
     host = W.host_inputs(w, 0, w.n_flat)
-    run_and_compare(env, orc, host, w.hp(), w.step, "C1")
+    run_and_compare(env, orc, host, w.hp(), w.step, "flat-1M-N2")
 
 
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 9, 16, 17, 31, 32, 33, 63, 64, 65, 100, 256])

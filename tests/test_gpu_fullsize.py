@@ -24,8 +24,10 @@ SENTINEL = 0x7FBF
 def workload(name):
     from synth import workloads as W
 
-    return {"c1": lambda: W.C1, "c2": lambda: W.C2, "c3": W.C3, "c4": lambda: W.C4,
-            "c5": lambda: W.C5(1), "c5w": lambda: W.C5(10_000)}[name]()
+    return {"flat-1m": lambda: W.FLAT_1M_N2, "flat-124m": lambda: W.FLAT_124M_N8,
+            "list-llama7b": W.list_llama7b_dp8_n8, "flat-70b": lambda: W.FLAT_70B_DP64_N64,
+            "list-ragged": lambda: W.list_ragged_20000_n16(1),
+            "list-ragged-warm": lambda: W.list_ragged_20000_n16(10_000)}[name]()
 
 
 def positions(w, L, seed=1234):
@@ -53,7 +55,8 @@ def gather(torch, d, idx):
                 B=d["B"].view(torch.int16)[it].cpu().numpy().view(np.uint16))
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "c5w"])
+@pytest.mark.parametrize("name", ["flat-1m", "flat-124m", "list-llama7b", "flat-70b", "list-ragged",
+                                  "list-ragged-warm"])
 def test_fused_step_full_size(orc, name):
     import torch
 
@@ -101,7 +104,7 @@ def test_two_pass_full_size(orc, path):
     import synth
     from synth import workloads as W
 
-    w = W.C4
+    w = W.FLAT_70B_DP64_N64
     zs.set_grid_blocks(0)
     d = W.device_inputs(w)
     n = d["arena_len"]
@@ -156,7 +159,7 @@ def test_offload_full_size(orc):
     import sharded_mixed_precision_rank_amd as zs
     from synth import workloads as W
 
-    w = W.C2
+    w = W.FLAT_124M_N8
     d = W.device_inputs(w)
     for key in "PMV":
         d[key] = d[key].cpu().pin_memory()

@@ -41,18 +41,18 @@ def test_moments():
 
 
 def test_workload_sizes():
-    c3 = W.C3()
-    assert len(c3.sizes) == 288 and c3.n_params == 809_533_440
-    c5 = W.C5()
-    assert len(c5.sizes) == 20_000 and min(c5.sizes) >= 64 and max(c5.sizes) <= 1 << 20
-    assert 2.0e9 < c5.n_params < 2.3e9       # log-uniform 64..2^20 has mean ~108k
-    offs, L = c5.layout()
-    assert np.all(offs % 8 == 0) and L >= c5.n_params
-    assert W.C4.n_params == 70_000_000_000 // 64
+    llama = W.list_llama7b_dp8_n8()
+    assert len(llama.sizes) == 288 and llama.n_params == 809_533_440
+    ragged = W.list_ragged_20000_n16()
+    assert len(ragged.sizes) == 20_000 and min(ragged.sizes) >= 64 and max(ragged.sizes) <= 1 << 20
+    assert 2.0e9 < ragged.n_params < 2.3e9       # log-uniform 64..2^20 has mean ~108k
+    offs, L = ragged.layout()
+    assert np.all(offs % 8 == 0) and L >= ragged.n_params
+    assert W.FLAT_70B_DP64_N64.n_params == 70_000_000_000 // 64
 
 
 def test_host_inputs_at_matches_slices():
-    w = W.C1.with_(warm=True, zero_frac=0.01)
+    w = W.FLAT_1M_N2.with_(warm=True, zero_frac=0.01)
     a = W.host_inputs(w, 100, 300)
     b = W.host_inputs_at(w, np.arange(100, 300))
     for k in "GPMV":
