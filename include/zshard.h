@@ -187,7 +187,8 @@ ZS_API zs_status zs_list_plan_info(zs_list_plan_t plan, int64_t* n_params, int32
 #define ZS_FORMAT_FP16 1
 
 /* Bytes of workspace the two passes need for a shard of n parameters (the
-   fp32 gradient plus one double per 2048-parameter tile, and alignment slack). */
+   fp32 gradient, one double per 2048-parameter tile and one per 4096 tiles
+   for the norm, and alignment slack). */
 ZS_API size_t zs_two_pass_workspace_bytes(int64_t n);
 
 /* Pass 1.  g[i] = (s_i / N) * f32(1/loss_scale), s_i the rank-ordered sum of

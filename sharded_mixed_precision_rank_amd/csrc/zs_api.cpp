@@ -227,19 +227,27 @@ constexpr int64_t kTileElems = (int64_t)zs::kBlock * 8;
 struct WorkspaceLayout {
   float* gbar;
   double* partials;
+  double* partials2;
   size_t need;  // bytes from the workspace start
 };
 
-// fp32 gradient at the first 256-byte boundary, then one double per tile
-// (plus the head slot).
+// Norm slots for n parameters: one per tile plus the head slot (at most
+// n / kTileElems + 2), and one first-stage sum per kFinalSeg of those.
+size_t partial_slots(int64_t n) { return (size_t)(n / kTileElems + 2); }
+size_t partial2_slots(int64_t n) { return partial_slots(n) / (size_t)zs::kFinalSeg + 1; }
+
+// fp32 gradient at the first 256-byte boundary, then the per-tile norm
+// partials, then their first-stage sums.
 WorkspaceLayout layout_of(const void* ws, int64_t n) {
   WorkspaceLayout L;
   const uintptr_t base = reinterpret_cast<uintptr_t>(ws);
   const uintptr_t g = (base + 255) & ~(uintptr_t)255;
   const uintptr_t p = g + (((uintptr_t)n * 4 + 255) & ~(uintptr_t)255);
+  const uintptr_t p2 = p + 8 * partial_slots(n);
   L.gbar = reinterpret_cast<float*>(g);
   L.partials = reinterpret_cast<double*>(p);
-  L.need = (size_t)(p - base) + 8 * (size_t)(n / kTileElems + 2);
+  L.partials2 = reinterpret_cast<double*>(p2);
+  L.need = (size_t)(p2 - base) + 8 * partial2_slots(n);
   return L;
 }
 
@@ -255,6 +263,7 @@ void reduce_shape(const uint16_t* const* g, int32_t N, int64_t n, void* ws, doub
   const WorkspaceLayout L = layout_of(ws, n);
   sh->gbar = L.gbar;
   sh->partials = L.partials;
+  sh->partials2 = L.partials2;
   std::vector<const void*> ptrs(g, g + N);
   std::vector<int> sizes(N, 2);
   ptrs.push_back(L.gbar);
@@ -523,7 +532,7 @@ zs_status zs_reduce_adam_list(const zs_tensor* tensors, int32_t T, int32_t N, co
 
 size_t zs_two_pass_workspace_bytes(int64_t n) {
   if (n < 0) return 0;
-  return 255 + (((size_t)n * 4 + 255) & ~(size_t)255) + 8 * (size_t)(n / kTileElems + 2);
+  return 255 + (((size_t)n * 4 + 255) & ~(size_t)255) + 8 * (partial_slots(n) + partial2_slots(n));
 }
 
 zs_status zs_reduce_grads_flat(const uint16_t* const* grad_chunks, int32_t N, int64_t n, int32_t grad_format,

@@ -66,6 +66,7 @@ static_assert(sizeof(ListChunk) == 32, "ListChunk layout");
 struct TwoPassShape {
   float* gbar;
   double* partials;  // ntiles + 1 slots
+  double* partials2; // first-stage sums of the partials, one per kFinalSeg of them
   double* sqnorm;    // the shard's squared norm (device)
   int64_t n;
   int64_t head;
@@ -98,5 +99,7 @@ hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, 
 // Elements per list chunk (vector tensors: groups of 8 per chunk = this / 8).
 constexpr int64_t kChunkElems = 65536;
 constexpr int kBlock = 256;
+// Per-tile norm partials summed by one first-stage workgroup.
+constexpr int64_t kFinalSeg = 4096;
 
 }  // namespace zs

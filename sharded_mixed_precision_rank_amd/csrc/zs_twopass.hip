@@ -7,8 +7,9 @@
 //  pass 1 (reduce_kernel)   g = (rank-ordered sum / N) * (1 / loss scale), from
 //          bf16 or fp16 replicas; g is written to an fp32 workspace and its
 //          squared norm is summed in double, one partial per 2048-parameter
-//          tile, then the partials in a fixed order (finalize_kernel).  The
-//          result does not depend on the launch size.
+//          tile, then the partials in a fixed two-stage order
+//          (finalize_partial_kernel, finalize_kernel).  The result does not
+//          depend on the launch size.
 //  pass 2 (gbar_kernel)     reads the global squared norm from device memory:
 //          if it is not finite the step is skipped (nothing is written);
 //          otherwise k = f32(min(1, max_norm / (sqrt(norm^2) + 1e-6))) (k = 1
@@ -110,7 +111,30 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs<NT> a) 
   }
 }
 
-// One workgroup: thread t sums partials t, t+256, ... in order, then the
+// First stage of the norm: workgroup b takes partials [b*kFinalSeg,
+// (b+1)*kFinalSeg); thread t sums its 16 of them (t, t+256, ...) in order,
+// then the fixed-order block sum.  The loads are issued together, so the
+// stage costs one memory latency instead of one per partial.
+__global__ __launch_bounds__(kBlock) void finalize_partial_kernel(const double* __restrict__ partials, int64_t count,
+                                                                  double* __restrict__ out) {
+  static_assert(kFinalSeg % kBlock == 0, "segment = whole rows of the workgroup");
+  constexpr int kPer = (int)(kFinalSeg / kBlock);
+  __shared__ double lds4[4];
+  const int64_t lo = (int64_t)blockIdx.x * kFinalSeg + threadIdx.x;
+  double v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int64_t i = lo + (int64_t)k * kBlock;
+    v[k] = i < count ? partials[i] : 0.0;
+  }
+  double x = 0.0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) x += v[k];
+  x = block_sum(x, lds4);
+  if (threadIdx.x == 0) out[blockIdx.x] = x;
+}
+
+// One workgroup: thread t sums values t, t+256, ... in order, then the
 // fixed-order block sum.
 __global__ __launch_bounds__(kBlock) void finalize_kernel(const double* __restrict__ partials, int64_t count,
                                                           double* __restrict__ out) {
@@ -228,7 +252,13 @@ hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int b
   reduce_kernel<NT, FMT><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  finalize_kernel<<<dim3(1), dim3(kBlock), 0, stream>>>(sh.partials, sh.ntiles + 1, sh.sqnorm);
+  // the norm: tile partials -> one sum per kFinalSeg of them -> the total, in a fixed order
+  const int64_t count = sh.ntiles + 1;
+  const int64_t nb1 = (count + kFinalSeg - 1) / kFinalSeg;
+  finalize_partial_kernel<<<dim3((unsigned)nb1), dim3(kBlock), 0, stream>>>(sh.partials, count, sh.partials2);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  finalize_kernel<<<dim3(1), dim3(kBlock), 0, stream>>>(sh.partials2, nb1, sh.sqnorm);
   return hipGetLastError();
 }
 

@@ -168,9 +168,13 @@ def test_loss_scaler_rejects_bad_settings():
 
 
 def test_workspace_size_covers_gradient_and_tiles():
+    """fp32 gradient + one norm slot per 2048-parameter tile (plus the head
+    slot) + one first-stage sum per 4096 of those, plus alignment slack."""
     for n in (0, 1, 2047, 2048, 10 ** 6, 1093750000):
         need = zs.two_pass_workspace_bytes(n)
-        assert need >= 4 * n + 8 * (n // 2048 + 2) and need < 4 * n + 8 * (n // 2048 + 2) + 600
+        slots = n // 2048 + 2
+        core = 4 * n + 8 * (slots + slots // 4096 + 1)
+        assert core <= need < core + 600
 
 
 def test_two_pass_rejects_bad_arguments_without_gpu():
