@@ -116,17 +116,22 @@ def cpu_baseline(w, target_s: float) -> dict:
     o = oracle.load()
     P, M, V = h["P"].copy(), h["M"].copy(), h["V"].copy()
     B = np.empty(n, dtype=np.uint16)
-    reps, spent = 0, 0.0
-    while spent < target_s or reps == 0:
-        t0 = time.perf_counter()
-        o.step_inplace(h["G"], P, M, V, B, w.hp(), w.step + reps, threads=threads)
-        spent += time.perf_counter() - t0
-        reps += 1
+    def timed(nthreads: int, budget: float):
+        reps, spent = 0, 0.0
+        while spent < budget or reps == 0:
+            t0 = time.perf_counter()
+            o.step_inplace(h["G"], P, M, V, B, w.hp(), w.step + reps, threads=nthreads)
+            spent += time.perf_counter() - t0
+            reps += 1
+        return reps, spent
+
+    reps, spent = timed(threads, target_s)
+    reps1, spent1 = timed(1, min(3.0, target_s / 3))  # the same oracle on one core
     pps = n * reps / spent
     return dict(value=pps, unit="params/s", cores=threads, kind="oracle",
-                gbps=pps * (2 * w.N + 26) / 1e9,
+                gbps=pps * (2 * w.N + 26) / 1e9, single_thread_value=n * reps1 / spent1,
                 sample=f"first {n} params of {w.name} (N={w.N}), {reps} oracle steps in {spent:.1f} s on "
-                       f"{threads} threads of {cores} cores")
+                       f"{threads} threads of {cores} cores; {reps1} steps in {spent1:.1f} s on one thread")
 
 
 def offload_breakdown(zs, torch, d, w, n, chunk) -> dict:
