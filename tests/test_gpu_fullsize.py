@@ -177,3 +177,43 @@ def test_offload_full_size(orc):
     assert parity.bit_identical(got, ref)
     del d
     torch.cuda.empty_cache()
+
+
+def test_flat_shard_beyond_2_31_elements(orc):
+    """A flat shard of 2^31 + 12,345 parameters (N=2): element indices pass the
+    32-bit range, so positions around 2^31 and at the tail are checked, through
+    the fused step and the two-pass form."""
+    import torch
+
+    import sharded_mixed_precision_rank_amd as zs
+    from synth import workloads as W
+
+    n = (1 << 31) + 12_345
+    w = W.FLAT_124M_N8.with_(name="flat-2^31+12345-N2", n_flat=n, N=2, step=3)
+    zs.set_grid_blocks(0)
+    d = W.device_inputs(w)
+    rng = np.random.default_rng(31)
+    edge = np.arange((1 << 31) - 4096, (1 << 31) + 4096, dtype=np.int64)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 50_000), edge, np.arange(n - 4096, n), np.arange(4096)]))
+    h = W.host_inputs_at(w, idx)
+    P, M, V, B = orc.step(h["G"], h["P"], h["M"], h["V"], w.hp(), w.step)
+    ref = dict(P=P, M=M, V=V, B=B)
+    # two-pass first (unclipped: the same result as the fused step), on copies of the state
+    P0, M0, V0 = d["P"].clone(), d["M"].clone(), d["V"].clone()
+    ws = torch.empty(zs.two_pass_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    sq = torch.empty(1, dtype=torch.float64, device="cuda")
+    zs.reduce_grads_flat(d["G"], ws, sq)
+    zs.adam_from_grads_flat(ws, n, P0, M0, V0, d["B"], w.hp(), w.step, sq)
+    torch.cuda.synchronize()
+    got = gather(torch, dict(P=P0, M=M0, V=V0, B=d["B"]), idx)
+    assert parity.bit_identical(got, ref), "two-pass beyond 2^31"
+    del P0, M0, V0, ws, sq
+    torch.cuda.empty_cache()
+    d["B"].zero_()
+    zs.reduce_adam_flat(d["G"], d["P"], d["M"], d["V"], d["B"], w.hp(), w.step)
+    torch.cuda.synchronize()
+    got = gather(torch, d, idx)
+    parity.assert_step(got, ref, w.name)
+    assert parity.bit_identical(got, ref), "fused beyond 2^31"
+    del d
+    torch.cuda.empty_cache()
