@@ -1,0 +1,211 @@
+/* A plain C client of libzshard: device memory from the HIP runtime's C API,
+ * the step through include/zshard.h, and the CPU oracle (liboracle, its C
+ * entry points) as the reference.  No Python and no PyTorch are involved.
+ *
+ * Cases (each compared bit for bit with the oracle):
+ *   1. flat shard, n = 100,003, N = 3, step 7, weight decay 0.1, arrays
+ *      starting 5 elements past an allocation (a peeled head);
+ *   2. a list plan over three tensors (1, 5,000 and 70,001 parameters, each
+ *      in its own allocations), run at steps 1 and 2;
+ *   3. the one-shot list call on the same tensors at step 3;
+ *   4. argument errors (N = 0, a NULL array) return their statuses before
+ *      anything is enqueued.
+ * Prints "zs_c_client ok" and exits 0 on success, 1 on any mismatch or error.
+ * Test code: the inputs come from a small generator of its own. */
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "zshard.h"
+
+/* the oracle's C entry points (oracle/oracle.cpp) */
+typedef struct oracle_hp {
+  double lr, beta1, beta2, eps, weight_decay;
+} oracle_hp;
+int oracle_reduce_adam(const uint16_t* const* G, int32_t N, int64_t n, float* P, float* M, float* V, uint16_t* B,
+                       const oracle_hp* hp, int64_t t, int32_t threads);
+
+#define CHECK_HIP(x)                                                              \
+  do {                                                                            \
+    hipError_t e_ = (x);                                                          \
+    if (e_ != hipSuccess) {                                                       \
+      fprintf(stderr, "%s:%d: %s: %s\n", __FILE__, __LINE__, #x, hipGetErrorString(e_)); \
+      exit(1);                                                                    \
+    }                                                                             \
+  } while (0)
+
+#define CHECK_ZS(x)                                                                               \
+  do {                                                                                            \
+    zs_status s_ = (x);                                                                           \
+    if (s_ != ZS_OK) {                                                                            \
+      fprintf(stderr, "%s:%d: %s: %s (%s)\n", __FILE__, __LINE__, #x, zs_status_string(s_), zs_last_error()); \
+      exit(1);                                                                                    \
+    }                                                                                             \
+  } while (0)
+
+/* input generator: SplitMix64 -> uniform in [-1, 1) */
+static uint64_t g_state = 0x5EEDull;
+static double uniform(void) {
+  uint64_t z = (g_state += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return (double)(z >> 11) * (2.0 / 9007199254740992.0) - 1.0;
+}
+static uint16_t bf16_bits(float x) { /* input preparation: the upper half of the fp32 bits */
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  return (uint16_t)(u >> 16);
+}
+
+/* One shard's host inputs and its device copies. */
+typedef struct {
+  int64_t n;
+  int32_t N;
+  uint16_t** hg;   /* N host gradient arrays */
+  float *hp, *hm, *hv;
+  uint16_t** dg;   /* N device gradient pointers (into allocations with `pad` leading elements) */
+  float *dp, *dm, *dv;
+  uint16_t* db;
+  void* allocs[32];
+  int nalloc;
+} shard;
+
+static void* dalloc(shard* s, size_t bytes) {
+  void* p = NULL;
+  CHECK_HIP(hipMalloc(&p, bytes));
+  s->allocs[s->nalloc++] = p;
+  return p;
+}
+
+static void shard_init(shard* s, int64_t n, int32_t N, int64_t pad) {
+  memset(s, 0, sizeof *s);
+  s->n = n;
+  s->N = N;
+  s->hg = (uint16_t**)calloc((size_t)N, sizeof(uint16_t*));
+  s->dg = (uint16_t**)calloc((size_t)N, sizeof(uint16_t*));
+  s->hp = (float*)malloc((size_t)n * 4);
+  s->hm = (float*)malloc((size_t)n * 4);
+  s->hv = (float*)malloc((size_t)n * 4);
+  for (int32_t r = 0; r < N; ++r) {
+    s->hg[r] = (uint16_t*)malloc((size_t)n * 2);
+    for (int64_t i = 0; i < n; ++i) s->hg[r][i] = bf16_bits((float)(uniform() * 2e-3));
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    s->hp[i] = (float)(uniform() * 0.04);
+    s->hm[i] = (float)(uniform() * 1e-4);
+    s->hv[i] = (float)((uniform() + 1.0) * 1e-6);
+  }
+  for (int32_t r = 0; r < N; ++r) {
+    s->dg[r] = (uint16_t*)dalloc(s, (size_t)(n + pad) * 2) + pad;
+    CHECK_HIP(hipMemcpy(s->dg[r], s->hg[r], (size_t)n * 2, hipMemcpyHostToDevice));
+  }
+  s->dp = (float*)dalloc(s, (size_t)(n + pad) * 4) + pad;
+  s->dm = (float*)dalloc(s, (size_t)(n + pad) * 4) + pad;
+  s->dv = (float*)dalloc(s, (size_t)(n + pad) * 4) + pad;
+  s->db = (uint16_t*)dalloc(s, (size_t)(n + pad) * 2) + pad;
+  CHECK_HIP(hipMemcpy(s->dp, s->hp, (size_t)n * 4, hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(s->dm, s->hm, (size_t)n * 4, hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(s->dv, s->hv, (size_t)n * 4, hipMemcpyHostToDevice));
+}
+
+static void shard_free(shard* s) {
+  for (int k = 0; k < s->nalloc; ++k) CHECK_HIP(hipFree(s->allocs[k]));
+  for (int32_t r = 0; r < s->N; ++r) free(s->hg[r]);
+  free(s->hg);
+  free(s->dg);
+  free(s->hp);
+  free(s->hm);
+  free(s->hv);
+}
+
+/* Advances the host copy with the oracle at step t and compares the device state with it, bit for bit. */
+static int oracle_compare(shard* s, const zs_adam_hp* hp, int64_t t, const char* what) {
+  const int64_t n = s->n;
+  uint16_t* hb = (uint16_t*)malloc((size_t)n * 2);
+  oracle_hp oh = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+  if (oracle_reduce_adam((const uint16_t* const*)s->hg, s->N, n, s->hp, s->hm, s->hv, hb, &oh, t, 4) != 0) {
+    fprintf(stderr, "%s: oracle rejected its arguments\n", what);
+    return 1;
+  }
+  float* gp = (float*)malloc((size_t)n * 4);
+  float* gm = (float*)malloc((size_t)n * 4);
+  float* gv = (float*)malloc((size_t)n * 4);
+  uint16_t* gb = (uint16_t*)malloc((size_t)n * 2);
+  CHECK_HIP(hipMemcpy(gp, s->dp, (size_t)n * 4, hipMemcpyDeviceToHost));
+  CHECK_HIP(hipMemcpy(gm, s->dm, (size_t)n * 4, hipMemcpyDeviceToHost));
+  CHECK_HIP(hipMemcpy(gv, s->dv, (size_t)n * 4, hipMemcpyDeviceToHost));
+  CHECK_HIP(hipMemcpy(gb, s->db, (size_t)n * 2, hipMemcpyDeviceToHost));
+  int bad = memcmp(gp, s->hp, (size_t)n * 4) || memcmp(gm, s->hm, (size_t)n * 4) ||
+            memcmp(gv, s->hv, (size_t)n * 4) || memcmp(gb, hb, (size_t)n * 2);
+  if (bad) fprintf(stderr, "%s: device state differs from the oracle\n", what);
+  free(gp);
+  free(gm);
+  free(gv);
+  free(gb);
+  free(hb);
+  return bad;
+}
+
+int main(void) {
+  int bad = 0;
+  if (zs_abi_version() != ZS_ABI_VERSION) {
+    fprintf(stderr, "ABI version %d, header %d\n", zs_abi_version(), ZS_ABI_VERSION);
+    return 1;
+  }
+  hipStream_t stream;
+  CHECK_HIP(hipStreamCreate(&stream));
+  zs_adam_hp hp = {1e-3, 0.9, 0.999, 1e-8, 0.1};
+
+  /* 1. flat shard with a peeled head */
+  shard f;
+  shard_init(&f, 100003, 3, 5);
+  CHECK_ZS(zs_reduce_adam_flat((const uint16_t* const*)f.dg, f.N, f.n, f.dp, f.dm, f.dv, f.db, &hp, 7, stream));
+  CHECK_HIP(hipStreamSynchronize(stream));
+  bad |= oracle_compare(&f, &hp, 7, "flat");
+
+  /* 4. argument errors, before anything is enqueued */
+  if (zs_reduce_adam_flat((const uint16_t* const*)f.dg, 0, f.n, f.dp, f.dm, f.dv, f.db, &hp, 8, stream) !=
+      ZS_ERR_RANGE) {
+    fprintf(stderr, "N = 0 was not rejected\n");
+    bad = 1;
+  }
+  if (zs_reduce_adam_flat((const uint16_t* const*)f.dg, f.N, f.n, NULL, f.dm, f.dv, f.db, &hp, 8, stream) !=
+      ZS_ERR_NULL) {
+    fprintf(stderr, "a NULL master was not rejected\n");
+    bad = 1;
+  }
+  shard_free(&f);
+
+  /* 2. and 3. a ragged list */
+  const int64_t sizes[3] = {1, 5000, 70001};
+  shard ts[3];
+  zs_tensor tab[3];
+  for (int k = 0; k < 3; ++k) {
+    shard_init(&ts[k], sizes[k], 3, 0);
+    tab[k].n = ts[k].n;
+    tab[k].master = ts[k].dp;
+    tab[k].m = ts[k].dm;
+    tab[k].v = ts[k].dv;
+    tab[k].param_bf16 = ts[k].db;
+    tab[k].grad_chunks = (const uint16_t* const*)ts[k].dg;
+  }
+  zs_list_plan_t plan = NULL;
+  CHECK_ZS(zs_list_plan_create(tab, 3, 3, stream, &plan));
+  for (int64_t t = 1; t <= 2; ++t) {
+    CHECK_ZS(zs_reduce_adam_list_plan(plan, &hp, t, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    for (int k = 0; k < 3; ++k) bad |= oracle_compare(&ts[k], &hp, t, "list plan");
+  }
+  zs_list_plan_destroy(plan);
+  CHECK_ZS(zs_reduce_adam_list(tab, 3, 3, &hp, 3, stream));
+  for (int k = 0; k < 3; ++k) bad |= oracle_compare(&ts[k], &hp, 3, "one-shot list");
+  for (int k = 0; k < 3; ++k) shard_free(&ts[k]);
+
+  CHECK_HIP(hipStreamDestroy(stream));
+  if (bad) return 1;
+  printf("zs_c_client ok\n");
+  return 0;
+}
