@@ -96,8 +96,11 @@ hipError_t launch_reduce(const uint16_t* const* grads, const TwoPassShape& sh, i
 hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, const double* total_sq,
                        double max_norm, int skip_nonfinite, int param_format, int blocks, hipStream_t stream);
 
-// Elements per list chunk (vector tensors: groups of 8 per chunk = this / 8).
-constexpr int64_t kChunkElems = 65536;
+// Elements per list chunk (vector tensors: groups of 8 per chunk = this / 8):
+// two tiles, so each workgroup streams for about as long as a flat-kernel
+// workgroup; longer chunks (more tiles per workgroup) measured 3-6% slower,
+// because a workgroup's next loads wait behind its previous stores.
+constexpr int64_t kChunkElems = 4096;
 constexpr int kBlock = 256;
 // Per-tile norm partials summed by one first-stage workgroup.
 constexpr int64_t kFinalSeg = 4096;
