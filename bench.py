@@ -76,6 +76,44 @@ def counter_traffic(w, n_launch_params: int):
     return float(m_bytes.group(1))
 
 
+def pattern_ceiling(w, d, reps: int = 5):
+    """What the memory system delivers for the step's own access pattern on this machine: the measurement
+    probe (libzshard_probe.so) replays the fused kernel's loads and stores, tile layout and
+    non-temporal hints included, with the AdamW arithmetic taken out, on the same buffers.  Reported as
+    GB/s of the pattern's own bytes for the read streams alone ((2N+12) B/param) and for the full
+    read+write mix ((2N+26) B/param).  It overwrites the state: run it after the timed steps."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "sharded_mixed_precision_rank_amd", "libzshard_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.zs_probe_pattern.restype = ctypes.c_int
+    lib.zs_probe_pattern.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int32, ctypes.c_void_p]
+    N, n = w.N, d["arena_len"]
+    full = n // 2048 * 2048
+    tab = (ctypes.c_void_p * N)(*[g.data_ptr() for g in d["G"]])
+    stream = torch.cuda.current_stream()
+    out = {}
+    for write, bpp, name in ((0, 2 * N + 12, "read"), (1, 2 * N + 26, "read_write")):
+        def call():
+            return lib.zs_probe_pattern(tab, N, n, d["P"].data_ptr(), d["M"].data_ptr(), d["V"].data_ptr(),
+                                        d["B"].data_ptr(), write, stream.cuda_stream)
+        if call() != 0:
+            return None  # a replica count or alignment the probe does not cover
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[f"{name}_GBps"] = bpp * full * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    return out
+
+
 def copy_ceiling(gbytes: float = 8.0, reps: int = 5) -> float:
     """Read+write GB/s of a plain 16-byte-per-lane copy kernel over `gbytes`."""
     import torch
@@ -195,7 +233,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="flat-70b", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 = skip)")
-    ap.add_argument("--no-copy", action="store_true", help="skip the copy-kernel ceiling")
+    ap.add_argument("--no-copy", action="store_true", help="skip the copy-kernel and access-pattern ceilings")
     ap.add_argument("--blocks", type=int, default=0, help="workgroups per launch (0 = library default)")
     ap.add_argument("--path", default="fused", choices=["fused", "clip", "fp16", "offload"],
                     help="fused: the one-pass step; clip: two-pass with global-norm clipping (max_norm 1); "
@@ -289,6 +327,14 @@ def main() -> int:
     achieved = bytes_per_launch / (ms / 1e3) / 1e9
     log(f"{ms:.3f} ms/step, {n / (ms / 1e3) / 1e9:.2f} G params/s, {achieved:.0f} GB/s")
 
+    pattern = None
+    if args.path == "fused" and not w.is_list and not args.no_copy:
+        pattern = pattern_ceiling(w, d)
+        if pattern:
+            pattern["kernel_frac_of_read_write"] = achieved / pattern["read_write_GBps"]
+            log(f"access-pattern ceiling without arithmetic: reads alone {pattern['read_GBps']:.0f} GB/s, "
+                f"reads+writes {pattern['read_write_GBps']:.0f} GB/s; the step reaches "
+                f"{100 * pattern['kernel_frac_of_read_write']:.1f}% of the latter")
     offload_parts = None
     if offload is not None:
         offload.close()
@@ -313,6 +359,7 @@ def main() -> int:
                    "storage": ("fp16" if args.path == "fp16" else "bf16") + " grads and working copy, fp32 master/m/v"},
         "hbm_GBps": achieved, "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,
         "copy_ceiling_GBps": ceiling,
+        "pattern_ceiling": pattern,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic if args.path == "fused" else None,
                      "bytes_per_param": bpp, "kernel": ("list_kernel" if w.is_list else "flat_kernel") + (

@@ -1,10 +1,14 @@
-"""Builds libzshard.so (gfx950) in place with hipcc."""
+"""Builds libzshard.so (gfx950) in place with hipcc, and the measurement probe
+libzshard_probe.so (the step's access pattern without its arithmetic; used by
+the benchmark, not part of the library's ABI)."""
 import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libzshard.so")
+PROBE_LIB = os.path.join(HERE, "libzshard_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "zs_probe.hip")]
 # Device code and HIP-runtime host code compile as HIP in one hipcc command.
 SOURCES = [os.path.join(CSRC, f) for f in ("zs_kernels.hip", "zs_twopass.hip", "zs_api.cpp", "zs_offload.cpp")]
 # The host AdamW is plain C++ built by the host compiler into an object that
@@ -23,19 +27,13 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
-    objs = []
-    for src in HOST_SOURCES:
-        obj = os.path.join(HERE, os.path.splitext(os.path.basename(src))[0] + ".o")
-        hcmd = ["g++", *HOST_FLAGS, "-c", src, "-o", obj]
-        if verbose:
-            print(" ".join(hcmd), flush=True)
-        subprocess.run(hcmd, check=True)
-        objs.append(obj)
+def _hipcc(sources, objs, out, extra, verbose):
     cmd = ["hipcc", *FLAGS, *extra]
-    for src in SOURCES:
+    for src in sources:
         cmd += ["-x", "hip", src]
-    cmd += ["-x", "none", *objs, "-o", out]
+    if objs:
+        cmd += ["-x", "none", *objs]
+    cmd += ["-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -45,6 +43,20 @@ def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
+
+
+def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(HERE, os.path.splitext(os.path.basename(src))[0] + ".o")
+        hcmd = ["g++", *HOST_FLAGS, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(hcmd), flush=True)
+        subprocess.run(hcmd, check=True)
+        objs.append(obj)
+    _hipcc(SOURCES, objs, out, extra, verbose)
+    if out == LIB:
+        _hipcc(PROBE_SOURCES, [], PROBE_LIB, extra, verbose)
     return out
 
 

@@ -1,0 +1,132 @@
+// Measurement probe (libzshard_probe.so, not part of the library's ABI): the
+// fused step's exact HBM access pattern with the AdamW arithmetic taken out,
+// to measure what the memory system delivers for this mix of streams on the
+// box at hand.
+//
+// Each workgroup takes one full 2048-parameter tile, with the same whole-line
+// lane layout, SGPR-base addressing, non-temporal accesses, state-before-
+// replicas load order and batched rank-ordered replica stream as the fused
+// kernel.  Then:
+//   write = 0: nothing is stored (a runtime flag the host never sets guards
+//              one store, so the loads cannot be optimised away): the read
+//              streams alone, (2N + 12) bytes per parameter;
+//   write = 1: master, m, v and the 16-bit copy are written back with values
+//              that need one add per element: the full (2N + 26) bytes per
+//              parameter of the step.
+// Only full tiles are processed; the caller passes arrays that start on a
+// 128-byte boundary.  The values written are meaningless: run the probe on
+// scratch state or after the state is no longer needed.
+#include "zs_device.h"
+
+namespace zs {
+namespace {
+
+using namespace dev;
+
+template <int NT>
+struct ProbeArgs {
+  const uint16_t* g[NT];
+  float* p;
+  float* m;
+  float* v;
+  uint16_t* b;
+  float* sink;      // receives one value only if `sink_flag` is set (never, in use)
+  int32_t sink_flag;
+};
+
+template <int NT, bool WRITE>
+__global__ __launch_bounds__(kBlock) void pattern_kernel(const ProbeArgs<NT> a) {
+  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  const int64_t e0 = (int64_t)blockIdx.x * (kBlock * 8);
+  const uint32_t e = Layout<true>::first();
+  f32x4 pa, pb, ma, mb, va, vb;
+  {
+    const uint32_t o = here(e) * 4u;
+    const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(a.p + e0), o);
+    const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(a.m + e0), o);
+    const GLB f32x4* V4 = (const GLB f32x4*)at(tile_base(a.v + e0), o);
+    pa = ld_g(P4);
+    pb = ld_g(P4 + q2);
+    ma = ld_g(M4);
+    mb = ld_g(M4 + q2);
+    va = ld_g(V4);
+    vb = ld_g(V4 + q2);
+  }
+  auto G = [&](int r) { return tile_base(a.g[r] + e0); };
+  float acc[8];
+  reduce_replicas<NT, true>(G, NT, e, acc);
+  float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+  float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+  float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+  if constexpr (WRITE) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[k] = p[k] + acc[k];
+    const uint32_t o = here(e) * 4u;
+    GLB f32x4* P4 = (GLB f32x4*)at(tile_base(a.p + e0), o);
+    GLB f32x4* M4 = (GLB f32x4*)at(tile_base(a.m + e0), o);
+    GLB f32x4* V4 = (GLB f32x4*)at(tile_base(a.v + e0), o);
+    st_g(P4, (f32x4){p[0], p[1], p[2], p[3]});
+    st_g(P4 + q2, (f32x4){p[4], p[5], p[6], p[7]});
+    st_g(M4, (f32x4){acc[0], acc[1], acc[2], acc[3]});
+    st_g(M4 + q2, (f32x4){acc[4], acc[5], acc[6], acc[7]});
+    st_g(V4, (f32x4){v[0] + m[0], v[1] + m[1], v[2] + m[2], v[3] + m[3]});
+    st_g(V4 + q2, (f32x4){v[4] + m[4], v[5] + m[5], v[6] + m[6], v[7] + m[7]});
+    GLB u32x2* B2 = (GLB u32x2*)at(tile_base(a.b + e0), here(e) * 2u);
+    st_g(B2, (u32x2){pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])});
+    st_g(B2 + Layout<true>::kSecond / 4, (u32x2){pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])});
+  } else {
+    float x = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x = x + acc[k] + p[k] + m[k] + v[k];
+    if (a.sink_flag) a.sink[blockIdx.x * kBlock + threadIdx.x] = x;
+  }
+}
+
+template <int NT>
+hipError_t go(const uint16_t* const* g, int64_t tiles, float* p, float* m, float* v, uint16_t* b, float* sink,
+              int write, hipStream_t stream) {
+  ProbeArgs<NT> a;
+  for (int r = 0; r < NT; ++r) a.g[r] = g[r];
+  a.p = p;
+  a.m = m;
+  a.v = v;
+  a.b = b;
+  a.sink = sink;
+  a.sink_flag = 0;
+  (void)hipGetLastError();
+  if (write)
+    pattern_kernel<NT, true><<<dim3((unsigned)tiles), dim3(kBlock), 0, stream>>>(a);
+  else
+    pattern_kernel<NT, false><<<dim3((unsigned)tiles), dim3(kBlock), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+bool line_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 127) == 0; }
+
+}  // namespace
+}  // namespace zs
+
+// Runs the probe over the n / 2048 full tiles of the shard on `stream`.
+// Returns 0 on success, 1 for unsupported arguments (N not 2, 8, 16 or 64,
+// fewer than 2048 parameters, an array not on a 128-byte boundary), 2 for a
+// launch error.
+extern "C" __attribute__((visibility("default"))) int zs_probe_pattern(const uint16_t* const* g, int32_t N,
+                                                                       int64_t n, float* p, float* m, float* v,
+                                                                       uint16_t* b, int32_t write, void* stream) {
+  using namespace zs;
+  const int64_t tiles = n / (kBlock * 8);
+  if (tiles < 1 || tiles > 0x7FFFFFFF || !g || !p || !m || !v || !b) return 1;
+  if (!line_aligned(p) || !line_aligned(m) || !line_aligned(v) || !line_aligned(b)) return 1;
+  for (int32_t r = 0; r < N; ++r)
+    if (!g[r] || !line_aligned(g[r])) return 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (N) {
+    case 2: e = go<2>(g, tiles, p, m, v, b, p, write, s); break;
+    case 8: e = go<8>(g, tiles, p, m, v, b, p, write, s); break;
+    case 16: e = go<16>(g, tiles, p, m, v, b, p, write, s); break;
+    case 64: e = go<64>(g, tiles, p, m, v, b, p, write, s); break;
+    default: return 1;
+  }
+  return e == hipSuccess ? 0 : 2;
+}

@@ -276,3 +276,18 @@ def test_binding_rejects_tensors_on_several_devices():
     assert zs._one_device(a, torch.ones(2)) == torch.device("cpu")
     with pytest.raises(ValueError, match="several devices"):
         zs._one_device(a, b)
+
+
+def test_probe_library_rejects_unsupported_arguments_without_gpu():
+    """The measurement probe (libzshard_probe.so) checks its arguments before any launch."""
+    path = os.path.join(os.path.dirname(zs.LIB_PATH), "libzshard_probe.so")
+    lib = ctypes.CDLL(path)
+    f = lib.zs_probe_pattern
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64] + [ctypes.c_void_p] * 4 + \
+        [ctypes.c_int32, ctypes.c_void_p]
+    g = (ctypes.c_void_p * 3)(A + 0x100000, A + 0x200000, A + 0x300000)
+    arr = [A + 0x400000, A + 0x500000, A + 0x600000, A + 0x700000]
+    assert f(g, 3, 1 << 20, *arr, 0, None) == 1            # N = 3 is not covered
+    assert f(g, 2, 1000, *arr, 0, None) == 1               # less than one tile
+    assert f(g, 2, 1 << 20, A + 0x400004, *arr[1:], 0, None) == 1   # not on a 128-byte boundary

@@ -1,0 +1,40 @@
+"""The measurement probe on the GPU: the read-only pattern leaves every array
+as it was, and the read+write pattern touches exactly the full tiles."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+def test_probe_modes():
+    import torch
+
+    import sharded_mixed_precision_rank_amd as zs
+
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(zs.LIB_PATH), "libzshard_probe.so"))
+    f = lib.zs_probe_pattern
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64] + [ctypes.c_void_p] * 4 + \
+        [ctypes.c_int32, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    N, n = 8, 3 * 2048 + 100
+    gen = torch.Generator().manual_seed(5)
+    G = [torch.randint(-2 ** 15, 2 ** 15, (n,), dtype=torch.int16, generator=gen).to(dev) for _ in range(N)]
+    P, M, V = (torch.randn(n, generator=gen).to(dev) for _ in range(3))
+    B = torch.zeros(n, dtype=torch.int16, device=dev)
+    before = [x.clone() for x in (P, M, V, B)]
+    tab = (ctypes.c_void_p * N)(*[g.data_ptr() for g in G])
+    s = torch.cuda.current_stream().cuda_stream
+    assert f(tab, N, n, P.data_ptr(), M.data_ptr(), V.data_ptr(), B.data_ptr(), 0, s) == 0
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip((P, M, V, B), before)), "read-only probe wrote"
+    assert f(tab, N, n, P.data_ptr(), M.data_ptr(), V.data_ptr(), B.data_ptr(), 1, s) == 0
+    torch.cuda.synchronize()
+    full = 3 * 2048
+    for a, b in zip((P, M, V, B), before):
+        assert torch.equal(a[full:], b[full:]), "the probe wrote past the full tiles"
+    assert not torch.equal(M[:full], before[1][:full])
+    assert np.any(B[:full].cpu().numpy() != 0)
