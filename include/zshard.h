@@ -217,7 +217,10 @@ ZS_API zs_status zs_adam_from_grads_flat(const void* workspace, size_t workspace
 
 /* Dynamic loss scale for fp16 training (the DeepSpeed fp16 block's
    loss_scale 0 = dynamic, initial_scale_power, loss_scale_window, hysteresis,
-   min_loss_scale).  Host-only state. */
+   min_loss_scale, in "Почему training 70B модели требует optimizer sharding
+   (ZeRO-3)?", §8).  The state lives in host memory for zs_loss_scaler_update,
+   or in device memory (a copy of an initialised host state) for
+   zs_loss_scaler_update_device and zs_reduce_grads_flat_device_scale. */
 typedef struct zs_loss_scaler {
   double scale, min_scale;
   int64_t window, hysteresis, overflows, clean;
@@ -232,6 +235,27 @@ ZS_API zs_status zs_loss_scaler_init(zs_loss_scaler* s, double initial_scale, do
    seen since the scale last changed, the scale halves (not below min_scale).
    After `window` consecutive clean steps the scale doubles. */
 ZS_API int32_t zs_loss_scaler_update(zs_loss_scaler* s, int32_t overflow);
+
+/* The same update, on the device, enqueued on `stream` after the work that
+   writes the global squared norm: a non-finite *total_sq is an overflow (the
+   test pass 2 uses to skip the step).  state: device zs_loss_scaler, 8-byte
+   aligned, read and written; total_sq: device double, read; taken: optional
+   device int32, set to 1 if the step was taken and 0 if it was skipped.  No
+   host synchronisation.  Errors: ZS_ERR_NULL, ZS_ERR_ALIGN, ZS_ERR_ALIAS
+   (total_sq or taken inside the state), ZS_ERR_HIP. */
+ZS_API zs_status zs_loss_scaler_update_device(zs_loss_scaler* state, const double* total_sq, int32_t* taken,
+                                              zs_stream stream);
+
+/* Pass 1 with the loss scale read on the device from scale_state->scale
+   (device memory; the unscale factor is f32(1/scale), as in
+   zs_reduce_grads_flat).  With zs_loss_scaler_update_device this keeps an fp16
+   step free of host round trips.  Other arguments and errors as
+   zs_reduce_grads_flat; the state must not overlap the workspace or sqnorm
+   (ZS_ERR_ALIAS). */
+ZS_API zs_status zs_reduce_grads_flat_device_scale(const uint16_t* const* grad_chunks, int32_t N, int64_t n,
+                                                   int32_t grad_format, const zs_loss_scaler* scale_state,
+                                                   void* workspace, size_t workspace_bytes, double* sqnorm,
+                                                   zs_stream stream);
 
 /* ---------------------------------------------------------------------------
  * Optimizer offload (ZeRO-Offload, "Почему training 70B модели требует

@@ -86,6 +86,11 @@ _lib.zs_loss_scaler_init.restype = ctypes.c_int
 _lib.zs_loss_scaler_init.argtypes = [ctypes.POINTER(LossScalerStruct), ctypes.c_double, ctypes.c_double, _i64, _i64]
 _lib.zs_loss_scaler_update.restype = _i32
 _lib.zs_loss_scaler_update.argtypes = [ctypes.POINTER(LossScalerStruct), _i32]
+_lib.zs_loss_scaler_update_device.restype = ctypes.c_int
+_lib.zs_loss_scaler_update_device.argtypes = [_vp, _vp, _vp, _vp]
+_lib.zs_reduce_grads_flat_device_scale.restype = ctypes.c_int
+_lib.zs_reduce_grads_flat_device_scale.argtypes = [ctypes.POINTER(_vp), _i32, _i64, _i32, _vp, _vp, ctypes.c_size_t,
+                                                   _vp, _vp]
 
 _lib.zs_offload_create.restype = ctypes.c_int
 _lib.zs_offload_create.argtypes = [_i64, _i32, ctypes.POINTER(_vp)]
@@ -475,6 +480,67 @@ class LossScaler:
 
     def state(self) -> dict:
         return {k: getattr(self._s, k) for k, _ in LossScalerStruct._fields_}
+
+    def to_device(self, device="cuda") -> "DeviceLossScaler":
+        """A copy of this state in device memory, updated there by the device forms."""
+        return DeviceLossScaler(self, device)
+
+
+class DeviceLossScaler:
+    """Loss-scaler state in device memory: pass 1 reads the scale there
+    (:func:`reduce_grads_flat_device_scale`) and :meth:`update` applies the
+    scaler's rule on the device from the global squared norm, so an fp16 step
+    never waits on the host."""
+
+    def __init__(self, host: LossScaler, device="cuda"):
+        import torch
+
+        raw = bytes(memoryview(host._s))
+        self.tensor = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(device)
+        self.device = self.tensor.device
+
+    def update(self, total_sq, taken=None, stream=None) -> None:
+        """Record the step whose global squared norm is ``total_sq`` (device float64); ``taken``
+        (optional device int32) receives 1 if the step was taken, 0 if it was skipped."""
+        import torch
+
+        _dev_check(total_sq, (torch.float64,), "total_sq")
+        tensors = [self.tensor, total_sq] + ([taken] if taken is not None else [])
+        if taken is not None:
+            _dev_check(taken, (torch.int32,), "taken")
+        dev = _one_device(*tensors)
+        with torch.cuda.device(dev):
+            _check(_lib.zs_loss_scaler_update_device(self.tensor.data_ptr(), total_sq.data_ptr(),
+                                                     taken.data_ptr() if taken is not None else None,
+                                                     _stream_handle(stream, dev)), "zs_loss_scaler_update_device")
+
+    def state(self) -> dict:
+        """The state, copied to the host (synchronises)."""
+        s = LossScalerStruct.from_buffer_copy(bytes(self.tensor.cpu().numpy()))
+        return {k: getattr(s, k) for k, _ in LossScalerStruct._fields_}
+
+
+def reduce_grads_flat_device_scale(grads: Sequence, workspace, sqnorm, scaler: DeviceLossScaler,
+                                   grad_format="fp16", stream=None) -> None:
+    """Pass 1 with the loss scale read on the device from ``scaler``."""
+    import torch
+
+    N = len(grads)
+    n = grads[0].numel() if N else 0
+    for r, g in enumerate(grads):
+        _dev_check(g, _half_types(), f"grads[{r}]")
+        if g.numel() != n:
+            raise ValueError(f"grads[{r}] has {g.numel()} elements, grads[0] has {n}")
+    _dev_check(workspace, (torch.uint8, torch.int8, torch.float32, torch.float64), "workspace")
+    _dev_check(sqnorm, (torch.float64,), "sqnorm")
+    dev = _one_device(workspace, sqnorm, scaler.tensor, *grads)
+    tab = (_vp * max(N, 1))(*[g.data_ptr() for g in grads])
+    with torch.cuda.device(dev):
+        _check(_lib.zs_reduce_grads_flat_device_scale(tab, N, n, _fmt(grad_format), scaler.tensor.data_ptr(),
+                                                      workspace.data_ptr(),
+                                                      workspace.numel() * workspace.element_size(),
+                                                      sqnorm.data_ptr(), _stream_handle(stream, dev)),
+               "zs_reduce_grads_flat_device_scale")
 
 
 # ------------------------------------------------------------ optimizer offload

@@ -13,6 +13,7 @@
 
 #include "zs_cpu_adam.h"
 #include "zs_internal.h"
+#include "zs_twopass.h"
 
 namespace {
 
@@ -535,16 +536,24 @@ size_t zs_two_pass_workspace_bytes(int64_t n) {
   return 255 + (((size_t)n * 4 + 255) & ~(size_t)255) + 8 * (partial_slots(n) + partial2_slots(n));
 }
 
-zs_status zs_reduce_grads_flat(const uint16_t* const* grad_chunks, int32_t N, int64_t n, int32_t grad_format,
-                               double loss_scale, void* workspace, size_t workspace_bytes, double* sqnorm,
-                               zs_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// Pass 1 with the loss scale given on the host (scale_state == NULL) or read
+// on the device from scale_state->scale.
+zs_status reduce_grads(const uint16_t* const* grad_chunks, int32_t N, int64_t n, int32_t grad_format,
+                       double loss_scale, const zs_loss_scaler* scale_state, void* workspace,
+                       size_t workspace_bytes, double* sqnorm, zs_stream stream, const char* what) {
   try {
     g_last_error.clear();
     if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
     if (n < 0 || n > (int64_t(1) << 56)) return fail(ZS_ERR_RANGE, "n out of range");
     if (grad_format != ZS_FORMAT_BF16 && grad_format != ZS_FORMAT_FP16)
       return fail(ZS_ERR_RANGE, "grad_format must be ZS_FORMAT_BF16 or ZS_FORMAT_FP16");
-    if (!(loss_scale > 0) || !std::isfinite(loss_scale)) return fail(ZS_ERR_RANGE, "loss_scale must be finite and > 0");
+    if (!scale_state && (!(loss_scale > 0) || !std::isfinite(loss_scale)))
+      return fail(ZS_ERR_RANGE, "loss_scale must be finite and > 0");
+    if (scale_state && !aligned(scale_state, 8)) return fail(ZS_ERR_ALIGN, "the scaler state must be 8-byte aligned");
     if (!sqnorm) return fail(ZS_ERR_NULL, "sqnorm is NULL");
     if (!aligned(sqnorm, 8)) return fail(ZS_ERR_ALIGN, "sqnorm must be 8-byte aligned");
     if (n > 0 && !workspace) return fail(ZS_ERR_NULL, "workspace is NULL");
@@ -557,16 +566,21 @@ zs_status zs_reduce_grads_flat(const uint16_t* const* grad_chunks, int32_t N, in
         rs.push_back({(uintptr_t)grad_chunks[r], (uintptr_t)grad_chunks[r] + 2 * (uintptr_t)n, 1, 0});
       }
     }
+    if (scale_state)  // read by the kernels: it must not overlap what they write
+      rs.push_back({(uintptr_t)scale_state, (uintptr_t)scale_state + sizeof(zs_loss_scaler), 1, 0});
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    const double host_scale = scale_state ? 1.0 : loss_scale;
     zs::TwoPassShape sh{};
     sh.sqnorm = sqnorm;
     sh.n = n;
     sh.n_rep = N;
-    sh.inv_scale = (float)(1.0 / loss_scale);
+    sh.inv_scale = (float)(1.0 / host_scale);
     if (n == 0) {  // an empty shard: only the (zero) norm is written
       sh.partials = nullptr;
       sh.ntiles = -1;
       rs.push_back({(uintptr_t)sqnorm, (uintptr_t)sqnorm + 8, 0, 1});
+      zs_status st = check_alias(rs);
+      if (st) return st;
     } else {
       const WorkspaceLayout L = layout_of(workspace, n);
       if (workspace_bytes < L.need)
@@ -575,15 +589,49 @@ zs_status zs_reduce_grads_flat(const uint16_t* const* grad_chunks, int32_t N, in
       rs.push_back({(uintptr_t)sqnorm, (uintptr_t)sqnorm + 8, 0, 1});
       zs_status st = check_alias(rs);
       if (st) return st;
-      reduce_shape(grad_chunks, N, n, workspace, sqnorm, (float)(1.0 / loss_scale), &sh);
+      reduce_shape(grad_chunks, N, n, workspace, sqnorm, (float)(1.0 / host_scale), &sh);
     }
-    return after_launch(zs::launch_reduce(grad_chunks, sh, grad_format, auto_blocks(), hs), hs,
-                        "zs_reduce_grads_flat launch");
+    sh.scale_dev = scale_state ? &scale_state->scale : nullptr;
+    return after_launch(zs::launch_reduce(grad_chunks, sh, grad_format, auto_blocks(), hs), hs, what);
   } catch (const std::bad_alloc&) {
     return fail(ZS_ERR_NOMEM, "host allocation failed");
   } catch (...) {
     return fail(ZS_ERR_HIP, "unexpected exception");
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+zs_status zs_reduce_grads_flat(const uint16_t* const* grad_chunks, int32_t N, int64_t n, int32_t grad_format,
+                               double loss_scale, void* workspace, size_t workspace_bytes, double* sqnorm,
+                               zs_stream stream) {
+  return reduce_grads(grad_chunks, N, n, grad_format, loss_scale, nullptr, workspace, workspace_bytes, sqnorm,
+                      stream, "zs_reduce_grads_flat launch");
+}
+
+zs_status zs_reduce_grads_flat_device_scale(const uint16_t* const* grad_chunks, int32_t N, int64_t n,
+                                            int32_t grad_format, const zs_loss_scaler* scale_state,
+                                            void* workspace, size_t workspace_bytes, double* sqnorm,
+                                            zs_stream stream) {
+  if (!scale_state) return fail(ZS_ERR_NULL, "scale_state is NULL");
+  return reduce_grads(grad_chunks, N, n, grad_format, 1.0, scale_state, workspace, workspace_bytes, sqnorm,
+                      stream, "zs_reduce_grads_flat_device_scale launch");
+}
+
+zs_status zs_loss_scaler_update_device(zs_loss_scaler* state, const double* total_sq, int32_t* taken,
+                                       zs_stream stream) {
+  g_last_error.clear();
+  if (!state || !total_sq) return fail(ZS_ERR_NULL, "state and total_sq must not be NULL");
+  if (!aligned(state, 8) || !aligned(total_sq, 8) || (taken && !aligned(taken, 4)))
+    return fail(ZS_ERR_ALIGN, "state and total_sq must be 8-byte aligned, taken 4-byte aligned");
+  const uintptr_t s0 = (uintptr_t)state, s1 = s0 + sizeof(zs_loss_scaler);
+  if (((uintptr_t)total_sq < s1 && s0 < (uintptr_t)total_sq + 8) ||
+      (taken && (uintptr_t)taken < s1 && s0 < (uintptr_t)taken + 4))
+    return fail(ZS_ERR_ALIAS, "total_sq or taken overlaps the scaler state");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  return after_launch(zs::launch_scaler_update(state, total_sq, taken, hs), hs, "zs_loss_scaler_update_device");
 }
 
 zs_status zs_adam_from_grads_flat(const void* workspace, size_t workspace_bytes, int64_t n, float* master, float* m,

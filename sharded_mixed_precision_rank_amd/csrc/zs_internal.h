@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI front end (zs_api.cpp) and the device
-// kernels (zs_kernels.hip).  Not installed; not part of the ABI.
+// kernels of the fused step (zs_kernels.hip).  Not installed; not part of the
+// ABI.  The two-pass form's interface is in zs_twopass.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -60,22 +61,6 @@ struct ListChunk {
 static_assert(sizeof(ListTensor) == 64, "ListTensor layout");
 static_assert(sizeof(ListChunk) == 32, "ListChunk layout");
 
-// Pass 1 of the two-pass form: tiles of kBlock*8 parameters start at `head`
-// (the common alignment peel of the replicas and the fp32 gradient buffer);
-// scalar_only = 1 when no common peel exists.
-struct TwoPassShape {
-  float* gbar;
-  double* partials;  // ntiles + 1 slots
-  double* partials2; // first-stage sums of the partials, one per kFinalSeg of them
-  double* sqnorm;    // the shard's squared norm (device)
-  int64_t n;
-  int64_t head;
-  int64_t ntiles;
-  int32_t scalar_only;
-  int32_t n_rep;
-  float inv_scale;
-};
-
 // Common alignment peel: the smallest h such that every pointer advanced by h
 // elements sits on a 128-byte line boundary (h < 64); failing that, a 64-,
 // 32- or 16-byte boundary; -1 if not even a 16-byte one exists.
@@ -91,18 +76,11 @@ hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const S
 hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
                        const uint16_t* const* gptrs, const Scalars& c, int blocks, hipStream_t stream);
 
-hipError_t launch_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int grad_format, int blocks,
-                         hipStream_t stream);
-hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, const double* total_sq,
-                       double max_norm, int skip_nonfinite, int param_format, int blocks, hipStream_t stream);
-
 // Elements per list chunk (vector tensors: groups of 8 per chunk = this / 8):
 // two tiles, so each workgroup streams for about as long as a flat-kernel
 // workgroup; longer chunks (more tiles per workgroup) measured 3-6% slower,
 // because a workgroup's next loads wait behind its previous stores.
 constexpr int64_t kChunkElems = 4096;
 constexpr int kBlock = 256;
-// Per-tile norm partials summed by one first-stage workgroup.
-constexpr int64_t kFinalSeg = 4096;
 
 }  // namespace zs

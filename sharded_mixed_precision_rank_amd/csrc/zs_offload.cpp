@@ -18,6 +18,7 @@
 
 #include "zs_cpu_adam.h"
 #include "zs_internal.h"
+#include "zs_twopass.h"
 
 namespace zs {
 zs_status offload_fail(zs_status st, const char* msg);

@@ -19,6 +19,7 @@
 // Bytes per parameter: pass 1 reads 2N and writes 4; pass 2 reads 4 + 12 and
 // writes 12 + 2: (2N + 34) in all, against (2N + 26) for the fused step.
 #include "zs_device.h"
+#include "zs_twopass.h"
 
 namespace zs {
 namespace {
@@ -50,7 +51,15 @@ struct ReduceArgs {
   int32_t scalar_only;
   int32_t n_rep;
   float inv_scale;   // f32(1 / loss scale)
+  const double* scale_dev;  // if set: the loss scale in device memory (inv_scale is then unused)
 };
+
+// f32(1 / loss scale): from the kernel argument, or from device memory (the
+// same double divide, rounded once, as the host form).
+template <int NT>
+__device__ __forceinline__ float unscale_factor(const ReduceArgs<NT>& a) {
+  return a.scale_dev ? (float)(1.0 / *a.scale_dev) : a.inv_scale;
+}
 
 // g of element i through the per-element path.
 template <int FMT, class GP>
@@ -66,6 +75,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs<NT> a) 
   const int N = NT > 0 ? NT : a.n_rep;
   Scalars c{};
   c.n_rep = N;
+  const float inv = unscale_factor(a);
   auto G0 = [&](int r) { return a.g[r]; };
   for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
     const int64_t e0 = a.head + t * kTile;
@@ -78,7 +88,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs<NT> a) 
       reduce_replicas<NT, true, FMT>(G, N, e, acc);
       float g[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) g[k] = mean_of<NT>(acc[k], c) * a.inv_scale;
+      for (int k = 0; k < 8; ++k) g[k] = mean_of<NT>(acc[k], c) * inv;
       GLB f32x4* O = (GLB f32x4*)at(tile_base(a.gbar + e0), here(e) * 4u);
       st_g(O, (f32x4){g[0], g[1], g[2], g[3]});
       st_g(O + Layout<true>::kSecond / 4, (f32x4){g[4], g[5], g[6], g[7]});
@@ -90,7 +100,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs<NT> a) 
       for (int k = 0; k < 8; ++k) {
         const int64_t i = lo + k;
         if (i < a.n && i < e0 + kTile) {
-          const float g = elem_mean<FMT>(G0, N, i, a.inv_scale);
+          const float g = elem_mean<FMT>(G0, N, i, inv);
           a.gbar[i] = g;
           sq += (double)g * (double)g;
         }
@@ -102,7 +112,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs<NT> a) 
   if (blockIdx.x == 0) {
     double sq = 0.0;
     if (threadIdx.x < a.head) {
-      const float g = elem_mean<FMT>(G0, N, threadIdx.x, a.inv_scale);
+      const float g = elem_mean<FMT>(G0, N, threadIdx.x, inv);
       a.gbar[threadIdx.x] = g;
       sq = (double)g * (double)g;
     }
@@ -246,6 +256,7 @@ hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int b
   a.scalar_only = sh.scalar_only;
   a.n_rep = sh.n_rep;
   a.inv_scale = sh.inv_scale;
+  a.scale_dev = sh.scale_dev;
   int grid = (int)(sh.ntiles < blocks ? sh.ntiles : blocks);
   if (grid < 1) grid = 1;
   (void)hipGetLastError();
@@ -282,6 +293,43 @@ hipError_t launch_reduce(const uint16_t* const* grads, const TwoPassShape& sh, i
                          hipStream_t stream) {
   return grad_format == 1 ? dispatch_reduce<kFP16>(grads, sh, blocks, stream)
                           : dispatch_reduce<kBF16>(grads, sh, blocks, stream);
+}
+
+namespace {
+
+// The loss-scale update of zs_loss_scaler_update, on one device thread, so an
+// fp16 step needs no round trip to the host: the overflow is a non-finite
+// global squared norm (the same test pass 2 uses to skip the step).
+__global__ void scaler_update_kernel(zs_loss_scaler* __restrict__ s, const double* __restrict__ total_sq,
+                                     int32_t* __restrict__ taken) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  const bool overflow = !__builtin_isfinite(*total_sq);
+  int64_t overflows = s->overflows, clean = s->clean;
+  double scale = s->scale;
+  if (overflow) {
+    clean = 0;
+    if (++overflows >= s->hysteresis) {
+      const double half = scale / 2.0;
+      scale = half < s->min_scale ? s->min_scale : half;
+      overflows = 0;
+    }
+  } else if (++clean >= s->window) {
+    scale *= 2.0;
+    clean = 0;
+    overflows = 0;
+  }
+  s->scale = scale;
+  s->overflows = overflows;
+  s->clean = clean;
+  if (taken) *taken = overflow ? 0 : 1;
+}
+
+}  // namespace
+
+hipError_t launch_scaler_update(zs_loss_scaler* state, const double* total_sq, int32_t* taken, hipStream_t stream) {
+  (void)hipGetLastError();
+  scaler_update_kernel<<<dim3(1), dim3(64), 0, stream>>>(state, total_sq, taken);
+  return hipGetLastError();
 }
 
 hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, const double* total_sq,

@@ -291,3 +291,22 @@ def test_probe_library_rejects_unsupported_arguments_without_gpu():
     assert f(g, 3, 1 << 20, *arr, 0, None) == 1            # N = 3 is not covered
     assert f(g, 2, 1000, *arr, 0, None) == 1               # less than one tile
     assert f(g, 2, 1 << 20, A + 0x400004, *arr[1:], 0, None) == 1   # not on a 128-byte boundary
+
+
+def test_device_scaler_entry_points_reject_bad_arguments_without_gpu():
+    lib = zs.library()
+    st, sq, tk = A + 0x100000, A + 0x200000, A + 0x300000
+    assert zs.STATUS[lib.zs_loss_scaler_update_device(None, sq, tk, None)] == "ZS_ERR_NULL"
+    assert zs.STATUS[lib.zs_loss_scaler_update_device(st, None, tk, None)] == "ZS_ERR_NULL"
+    assert zs.STATUS[lib.zs_loss_scaler_update_device(st + 4, sq, tk, None)] == "ZS_ERR_ALIGN"
+    assert zs.STATUS[lib.zs_loss_scaler_update_device(st, sq, tk + 2, None)] == "ZS_ERR_ALIGN"
+    assert zs.STATUS[lib.zs_loss_scaler_update_device(st, st + 8, tk, None)] == "ZS_ERR_ALIAS"
+    assert zs.STATUS[lib.zs_loss_scaler_update_device(st, sq, st + 40, None)] == "ZS_ERR_ALIAS"
+    n = 4096
+    g = (ctypes.c_void_p * 2)(A + 0x1000000, A + 0x2000000)
+    ws, wsb = A + 0x4000000, zs.two_pass_workspace_bytes(n)
+    f = lib.zs_reduce_grads_flat_device_scale
+    assert zs.STATUS[f(g, 2, n, 1, None, ws, wsb, sq, None)] == "ZS_ERR_NULL"
+    assert zs.STATUS[f(g, 2, n, 1, st + 4, ws, wsb, sq, None)] == "ZS_ERR_ALIGN"
+    assert zs.STATUS[f(g, 2, n, 1, ws + 1024, ws, wsb, sq, None)] == "ZS_ERR_ALIAS"   # state inside the workspace
+    assert zs.STATUS[f(g, 2, n, 1, sq, ws, wsb, sq, None)] == "ZS_ERR_ALIAS"          # state over the norm slot

@@ -168,3 +168,92 @@ def test_clipped_step_convenience(env, orc):
     P1, M1, V1, B1, _ = orc.adam_from_gbar(ref_g, host["P"], host["M"], host["V"], HP, 3, sq.item(), 0.01)
     got = dict(P=P.cpu().numpy(), M=M.cpu().numpy(), V=V.cpu().numpy(), B=B.cpu().numpy().view(np.uint16))
     assert parity.bit_identical(got, dict(P=P1, M=M1, V=V1, B=B1))
+
+
+def _scaler_state(st) -> dict:
+    return {k: getattr(st, k) for k in ("scale", "min_scale", "window", "hysteresis", "overflows", "clean")}
+
+
+def test_device_loss_scaler_follows_the_oracle(env, orc):
+    """The device scaler against the oracle's scaler, step by step, on a random
+    overflow sequence (an Inf or NaN global norm is an overflow)."""
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    rng = np.random.default_rng(21)
+    ds = zs.LossScaler(2.0 ** 16, 1.0, 7, 2).to_device(dev)
+    ref = orc.scaler(2.0 ** 16, 1.0, 7, 2)
+    taken = torch.zeros(1, dtype=torch.int32, device=dev)
+    for k in range(200):
+        u = rng.random()
+        value = float("inf") if u < 0.15 else float("nan") if u < 0.2 else float(rng.random() * 10)
+        sq = torch.tensor([value], dtype=torch.float64, device=dev)
+        ds.update(sq, taken)
+        ref_taken = orc.scaler_update(ref, not np.isfinite(value))
+        assert ds.state() == _scaler_state(ref), k
+        assert int(taken.item()) == int(ref_taken), k
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** 8, 2.0 ** 16, 3.0])
+def test_device_scale_pass1_equals_host_scale(env, orc, scale):
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    rng = np.random.default_rng(int(scale) + 40)
+    n = 50_001
+    host = rand_case(rng, 3, n, fmt="fp16", scale=scale, orc=orc)
+    G = [torch.from_numpy(g.view(np.int16)).to(dev) for g in host["G"]]
+    outs = []
+    for device_scale in (False, True):
+        ws = torch.zeros(zs.two_pass_workspace_bytes(n), dtype=torch.uint8, device=dev)
+        sq = torch.zeros(1, dtype=torch.float64, device=dev)
+        if device_scale:
+            zs.reduce_grads_flat_device_scale(G, ws, sq, zs.LossScaler(scale, 1.0, 10, 2).to_device(dev), "fp16")
+        else:
+            zs.reduce_grads_flat(G, ws, sq, scale, "fp16")
+        torch.cuda.synchronize()
+        start = (256 - ws.data_ptr() % 256) % 256
+        outs.append((ws[start:start + 4 * n].cpu().numpy().copy(), float(sq.item())))
+    assert np.array_equal(outs[0][0], outs[1][0]) and outs[0][1] == outs[1][1]
+    ref_g = orc.reduce_unscale(host["G"], 1, scale)
+    assert np.array_equal(outs[1][0].view(np.float32).view(np.uint32), ref_g.view(np.uint32))
+
+
+def test_fp16_steps_without_host_round_trips(env, orc):
+    """Six fp16 steps, each pass 1 with the device scale, pass 2 with clipping
+    and overflow skip, then the device scaler update, with no host
+    synchronisation between them; steps 2 and 4 carry an Inf replica.  The
+    final state and scale equal the oracle's run of the same sequence."""
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    rng = np.random.default_rng(77)
+    n, N = 20_003, 4
+    P = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    M = np.zeros(n, np.float32)
+    V = np.zeros(n, np.float32)
+    scaler = zs.LossScaler(2.0 ** 15, 1.0, 2, 1)
+    ds = scaler.to_device(dev)
+    ref_sc = orc.scaler(2.0 ** 15, 1.0, 2, 1)
+    Pd, Md, Vd = (torch.from_numpy(x.copy()).to(dev) for x in (P, M, V))
+    Bd = torch.zeros(n, dtype=torch.float16, device=dev)
+    ws = torch.empty(zs.two_pass_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    sq = torch.empty(1, dtype=torch.float64, device=dev)
+    Pr, Mr, Vr, Br = P.copy(), M.copy(), V.copy(), np.zeros(n, np.uint16)
+    for t in range(1, 7):
+        x = (rng.standard_normal((N, n)) * 1e-3).astype(np.float32)
+        # the replicas the device sees are scaled by the scale the oracle's scaler holds at this step
+        Gh = orc.f16(x * np.float32(ref_sc.scale))
+        if t in (2, 4):
+            Gh[1, 77] = 0x7C00
+        G = [torch.from_numpy(g.view(np.int16)).to(dev) for g in Gh]
+        zs.reduce_grads_flat_device_scale(G, ws, sq, ds, "fp16")
+        zs.adam_from_grads_flat(ws, n, Pd, Md, Vd, Bd, HP, t, sq, 1.0, "fp16")
+        ds.update(sq)
+        # the oracle, driven from the host
+        g = orc.reduce_unscale(Gh, 1, ref_sc.scale)
+        tsq = orc.sqnorm(g)
+        Pr, Mr, Vr, B1, taken = orc.adam_from_gbar(g, Pr, Mr, Vr, HP, t, tsq, 1.0, out_fmt=1)
+        if taken:
+            Br = B1
+        orc.scaler_update(ref_sc, not np.isfinite(tsq))
+    torch.cuda.synchronize()
+    assert ds.state() == _scaler_state(ref_sc)
+    got = dict(P=Pd.cpu().numpy(), M=Md.cpu().numpy(), V=Vd.cpu().numpy(), B=Bd.view(torch.int16).cpu().numpy().view(np.uint16))
+    for k, r in (("P", Pr), ("M", Mr), ("V", Vr)):
+        assert np.array_equal(got[k].view(np.uint32), r.view(np.uint32)), k
+    assert np.array_equal(got["B"], Br)
