@@ -64,6 +64,8 @@ extern "C" {
 /* Largest replica count N one call accepts (the N chunk pointers travel as
    kernel arguments). */
 #define ZS_MAX_REPLICAS 256
+/* Hyperparameter groups a list plan can carry (zs_list_plan_set_groups). */
+#define ZS_MAX_GROUPS 8
 
 /* A hipStream_t, passed as an opaque pointer; NULL is the null stream. */
 typedef void* zs_stream;
@@ -156,6 +158,25 @@ ZS_API zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_
    another device current fails with ZS_ERR_RANGE. */
 ZS_API zs_status zs_reduce_adam_list_plan(zs_list_plan_t plan, const zs_adam_hp* hp, int64_t step,
                                           zs_stream stream);
+
+/* Hyperparameter groups for a plan's tensors: AdamW setups commonly give norms
+   and biases no weight decay, as separate parameter groups (the pages use a
+   single setting, which a plan without groups keeps).  group: host array of
+   the plan's T group indices, each in [0, n_groups), copied into the plan's
+   table on `stream` before the call returns; 1 <= n_groups <= ZS_MAX_GROUPS.
+   Until groups are set every tensor is in group 0.  Errors: ZS_ERR_NULL,
+   ZS_ERR_RANGE (bad count or index, or another device current), ZS_ERR_HIP. */
+ZS_API zs_status zs_list_plan_set_groups(zs_list_plan_t plan, const int32_t* group, int32_t n_groups,
+                                         zs_stream stream);
+
+/* The step with one hyperparameter set per group: hps is a host array of the
+   n_groups sets (n_groups as set on the plan); tensor t uses hps[group[t]].
+   One kernel launch; the same arithmetic per tensor as the single-set call
+   with that tensor's set.  zs_reduce_adam_list_plan still applies its one hp
+   to every tensor, whatever the groups.  Errors as zs_reduce_adam_list_plan,
+   and ZS_ERR_RANGE if n_groups differs from the plan's. */
+ZS_API zs_status zs_reduce_adam_list_plan_groups(zs_list_plan_t plan, const zs_adam_hp* hps, int32_t n_groups,
+                                                 int64_t step, zs_stream stream);
 
 /* One-shot form: create a plan, run it, wait for the step to finish on
    `stream`, destroy the plan.  Blocks the calling thread. */

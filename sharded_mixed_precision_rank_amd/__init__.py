@@ -63,6 +63,10 @@ _lib.zs_reduce_adam_list.argtypes = [ctypes.POINTER(TensorStruct), _i32, _i32, c
                                      _vp]
 _lib.zs_list_plan_destroy.restype = None
 _lib.zs_list_plan_destroy.argtypes = [_vp]
+_lib.zs_list_plan_set_groups.restype = ctypes.c_int
+_lib.zs_list_plan_set_groups.argtypes = [_vp, ctypes.POINTER(_i32), _i32, _vp]
+_lib.zs_reduce_adam_list_plan_groups.restype = ctypes.c_int
+_lib.zs_reduce_adam_list_plan_groups.argtypes = [_vp, ctypes.POINTER(AdamHPStruct), _i32, _i64, _vp]
 _lib.zs_list_plan_info.restype = ctypes.c_int
 _lib.zs_list_plan_info.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
 _lib.zs_set_grid_blocks.restype = ctypes.c_int
@@ -345,6 +349,29 @@ class ListPlan:
         with torch.cuda.device(self._dev):
             _check(_lib.zs_reduce_adam_list_plan(self._h, ctypes.byref(h), step, _stream_handle(stream, self._dev)),
                    "zs_reduce_adam_list_plan")
+
+    def set_groups(self, groups: Sequence[int], n_groups: int, stream=None) -> None:
+        """Assign tensor t to hyperparameter group groups[t] (0 <= groups[t] < n_groups <= 8)."""
+        import torch
+
+        if not self._h:
+            raise ValueError("plan is closed")
+        arr = (_i32 * max(len(groups), 1))(*groups)
+        with torch.cuda.device(self._dev):
+            _check(_lib.zs_list_plan_set_groups(self._h, arr, n_groups, _stream_handle(stream, self._dev)),
+                   "zs_list_plan_set_groups")
+
+    def step_groups(self, hps: Sequence, step: int, stream=None) -> None:
+        """The step with hps[g] for the tensors of group g."""
+        import torch
+
+        if not self._h:
+            raise ValueError("plan is closed")
+        arr = (AdamHPStruct * max(len(hps), 1))(*[_hp(h) for h in hps])
+        with torch.cuda.device(self._dev):
+            _check(_lib.zs_reduce_adam_list_plan_groups(self._h, arr, len(hps), step,
+                                                        _stream_handle(stream, self._dev)),
+                   "zs_reduce_adam_list_plan_groups")
 
     def info(self) -> dict:
         n, t, c = _i64(), _i32(), _i32()

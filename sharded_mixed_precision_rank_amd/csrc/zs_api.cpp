@@ -2,6 +2,7 @@
 // launches and error reporting.  The arithmetic contract is in include/zshard.h.
 #include <algorithm>
 #include <atomic>
+#include <cstddef>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -312,6 +313,7 @@ struct zs_list_plan {
   int32_t T;
   int32_t n_chunks;
   int64_t n_params;
+  int32_t n_groups;  // hyperparameter groups set by zs_list_plan_set_groups (1 until then)
   void* table;  // device: chunks | tensors | grad pointers
   zs::ListChunk* chunks;
   zs::ListTensor* tensors;
@@ -436,6 +438,7 @@ zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_t N, zs
     plan->T = T;
     plan->n_chunks = (int32_t)hc.size();
     plan->n_params = total;
+    plan->n_groups = 1;
     plan->table = nullptr;
     if (hipGetDevice(&plan->device) != hipSuccess) plan->device = 0;
     const size_t bc = hc.size() * sizeof(zs::ListChunk), bt = ht.size() * sizeof(zs::ListTensor),
@@ -474,21 +477,78 @@ zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_t N, zs
   }
 }
 
-zs_status zs_reduce_adam_list_plan(zs_list_plan_t plan, const zs_adam_hp* hp, int64_t step, zs_stream stream) {
-  g_last_error.clear();
-  if (!plan) return fail(ZS_ERR_NULL, "plan is NULL");
-  zs_status st = check_hp(hp, step);
-  if (st) return st;
-  if (plan->n_chunks == 0) return ZS_OK;
+}  // extern "C"
+
+namespace {
+
+zs_status plan_on_current_device(zs_list_plan_t plan) {
   int cur = -1;
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (cur != plan->device)  // the table lives in the other device's memory
     return fail(ZS_ERR_RANGE, "the plan was built on device %d, device %d is current", plan->device, cur);
-  const zs::Scalars c = make_scalars(*hp, step, plan->N);
+  return ZS_OK;
+}
+
+// The step with `n` hyperparameter sets: one for every tensor (n == 1) or one per group.
+zs_status run_plan(zs_list_plan_t plan, const zs_adam_hp* hps, int32_t n, int64_t step, zs_stream stream) {
+  for (int32_t k = 0; k < n; ++k) {
+    zs_status st = check_hp(hps + k, step);
+    if (st) return st;
+  }
+  if (plan->n_chunks == 0) return ZS_OK;
+  zs_status st = plan_on_current_device(plan);
+  if (st) return st;
+  zs::Scalars cs[zs::kMaxGroups];
+  for (int32_t k = 0; k < n; ++k) cs[k] = make_scalars(hps[k], step, plan->N);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  return after_launch(zs::launch_list(plan->chunks, plan->n_chunks, plan->tensors, plan->gptrs, c, auto_blocks(), hs),
-                      hs, "zs_reduce_adam_list launch");
+  return after_launch(
+      zs::launch_list(plan->chunks, plan->n_chunks, plan->tensors, plan->gptrs, cs, n, auto_blocks(), hs), hs,
+      "zs_reduce_adam_list launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+zs_status zs_reduce_adam_list_plan(zs_list_plan_t plan, const zs_adam_hp* hp, int64_t step, zs_stream stream) {
+  g_last_error.clear();
+  if (!plan) return fail(ZS_ERR_NULL, "plan is NULL");
+  return run_plan(plan, hp, 1, step, stream);
+}
+
+zs_status zs_list_plan_set_groups(zs_list_plan_t plan, const int32_t* group, int32_t n_groups, zs_stream stream) {
+  g_last_error.clear();
+  if (!plan) return fail(ZS_ERR_NULL, "plan is NULL");
+  if (n_groups < 1 || n_groups > ZS_MAX_GROUPS)
+    return fail(ZS_ERR_RANGE, "n_groups must be in [1, %d] (got %d)", ZS_MAX_GROUPS, n_groups);
+  if (plan->T > 0 && !group) return fail(ZS_ERR_NULL, "group is NULL");
+  for (int32_t t = 0; t < plan->T; ++t)
+    if (group[t] < 0 || group[t] >= n_groups)
+      return fail(ZS_ERR_RANGE, "group[%d] = %d is not in [0, %d)", t, group[t], n_groups);
+  if (plan->T > 0) {
+    zs_status st = plan_on_current_device(plan);
+    if (st) return st;
+    // each tensor descriptor's `group` field, one int32 every sizeof(ListTensor) bytes
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpy2DAsync(reinterpret_cast<char*>(plan->tensors) + offsetof(zs::ListTensor, group),
+                                    sizeof(zs::ListTensor), group, sizeof(int32_t), sizeof(int32_t), (size_t)plan->T,
+                                    hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);  // `group` may be freed on return
+    if (e != hipSuccess) return hip_fail(e, "group upload");
+  }
+  plan->n_groups = n_groups;
+  return ZS_OK;
+}
+
+zs_status zs_reduce_adam_list_plan_groups(zs_list_plan_t plan, const zs_adam_hp* hps, int32_t n_groups,
+                                          int64_t step, zs_stream stream) {
+  g_last_error.clear();
+  if (!plan) return fail(ZS_ERR_NULL, "plan is NULL");
+  if (!hps) return fail(ZS_ERR_NULL, "hps is NULL");
+  if (n_groups != plan->n_groups)
+    return fail(ZS_ERR_RANGE, "the plan has %d groups, %d hyperparameter sets were given", plan->n_groups, n_groups);
+  return run_plan(plan, hps, n_groups, step, stream);
 }
 
 }  // extern "C"

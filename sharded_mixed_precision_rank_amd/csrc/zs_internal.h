@@ -44,7 +44,7 @@ struct ListTensor {
   int64_t head;
   int64_t nvec;
   int32_t scalar_only;
-  int32_t pad_;
+  int32_t group;  // hyperparameter group (list plans with groups; else 0)
 };
 
 // One chunk of a list plan (device table): for a vector tensor, groups
@@ -73,8 +73,10 @@ int64_t common_peel_sized(const void* const* ptrs, const int* elem_bytes, int co
 // Launches (host side, defined with the kernels).
 hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, int blocks,
                        hipStream_t stream);
+// cs: n_sets folded scalar sets, one per hyperparameter group (1 <= n_sets <= kMaxGroups).
 hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
-                       const uint16_t* const* gptrs, const Scalars& c, int blocks, hipStream_t stream);
+                       const uint16_t* const* gptrs, const Scalars* cs, int n_sets, int blocks,
+                       hipStream_t stream);
 
 // Elements per list chunk (vector tensors: groups of 8 per chunk = this / 8):
 // two tiles, so each workgroup streams for about as long as a flat-kernel
@@ -82,5 +84,7 @@ hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTens
 // because a workgroup's next loads wait behind its previous stores.
 constexpr int64_t kChunkElems = 4096;
 constexpr int kBlock = 256;
+// Hyperparameter groups a list plan can carry (their scalars travel as kernel arguments).
+constexpr int kMaxGroups = ZS_MAX_GROUPS;
 
 }  // namespace zs

@@ -179,14 +179,22 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
 // Ragged list: each workgroup takes chunks; per chunk it stages the owning
 // tensor's descriptor and its N replica pointers into LDS, then runs the same
 // group/element code as the flat kernel over the chunk.
-template <int NT>
+// NG sets of folded scalars: one for every tensor (NG = 1), or one per
+// hyperparameter group, the group of a tensor being its descriptor's `group`.
+template <int NG>
+struct ListScalars {
+  Scalars c[NG];
+};
+
+template <int NT, int NG>
 __global__ __launch_bounds__(kBlock) void list_kernel(const ListChunk* __restrict__ chunks, int32_t n_chunks,
                                                       const ListTensor* __restrict__ tensors,
-                                                      const uint16_t* const* __restrict__ gptrs, const Scalars c) {
+                                                      const uint16_t* const* __restrict__ gptrs,
+                                                      const ListScalars<NG> sc) {
   constexpr int kMaxN = NT > 0 ? NT : ZS_MAX_REPLICAS;
   __shared__ int64_t s_tensor[8];
   __shared__ const uint16_t* s_g[kMaxN];
-  const int N = NT > 0 ? NT : c.n_rep;
+  const int N = NT > 0 ? NT : sc.c[0].n_rep;
   for (int32_t ci = blockIdx.x; ci < n_chunks; ci += gridDim.x) {
     const ListChunk ch = chunks[ci];
     const int32_t t = ch.tensor;
@@ -202,6 +210,9 @@ __global__ __launch_bounds__(kBlock) void list_kernel(const ListChunk* __restric
     s.head = uniform_i64(s_tensor[5]);
     s.nvec = uniform_i64(s_tensor[6]);
     s.scalar_only = (int32_t)uniform_i64(s_tensor[7] & 0xFFFFFFFF);
+    int32_t grp = 0;
+    if constexpr (NG > 1) grp = (int32_t)uniform_i64(s_tensor[7] >> 32);  // the tensor's group, < NG
+    const Scalars& c = sc.c[grp];
     auto G = [&](int r) { return uniform_ptr(s_g[r]); };
     if (!s.scalar_only) {
       tiles<NT>(G, N, ch.begin, ch.end, 0, 1, s, c);
@@ -234,10 +245,18 @@ hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scala
 
 template <int NT>
 hipError_t go_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
-                   const uint16_t* const* gptrs, const Scalars& c, int blocks, hipStream_t stream) {
+                   const uint16_t* const* gptrs, const Scalars* cs, int n_sets, int blocks, hipStream_t stream) {
   const int grid = blocks < n_chunks ? blocks : n_chunks;
   (void)hipGetLastError();
-  list_kernel<NT><<<dim3(grid), dim3(kBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, c);
+  if (n_sets <= 1) {
+    ListScalars<1> sc;
+    sc.c[0] = cs[0];
+    list_kernel<NT, 1><<<dim3(grid), dim3(kBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc);
+  } else {
+    ListScalars<kMaxGroups> sc;
+    for (int k = 0; k < kMaxGroups; ++k) sc.c[k] = cs[k < n_sets ? k : 0];
+    list_kernel<NT, kMaxGroups><<<dim3(grid), dim3(kBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc);
+  }
   return hipGetLastError();
 }
 
@@ -258,16 +277,17 @@ hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const S
 }
 
 hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
-                       const uint16_t* const* gptrs, const Scalars& c, int blocks, hipStream_t stream) {
-  switch (c.n_rep) {
-    case 1: return go_list<1>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
-    case 2: return go_list<2>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
-    case 4: return go_list<4>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
-    case 8: return go_list<8>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
-    case 16: return go_list<16>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
-    case 32: return go_list<32>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
-    case 64: return go_list<64>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
-    default: return go_list<0>(chunks, n_chunks, tensors, gptrs, c, blocks, stream);
+                       const uint16_t* const* gptrs, const Scalars* cs, int n_sets, int blocks,
+                       hipStream_t stream) {
+  switch (cs[0].n_rep) {
+    case 1: return go_list<1>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
+    case 2: return go_list<2>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
+    case 4: return go_list<4>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
+    case 8: return go_list<8>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
+    case 16: return go_list<16>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
+    case 32: return go_list<32>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
+    case 64: return go_list<64>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
+    default: return go_list<0>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
   }
 }
 

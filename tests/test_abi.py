@@ -310,3 +310,24 @@ def test_device_scaler_entry_points_reject_bad_arguments_without_gpu():
     assert zs.STATUS[f(g, 2, n, 1, st + 4, ws, wsb, sq, None)] == "ZS_ERR_ALIGN"
     assert zs.STATUS[f(g, 2, n, 1, ws + 1024, ws, wsb, sq, None)] == "ZS_ERR_ALIAS"   # state inside the workspace
     assert zs.STATUS[f(g, 2, n, 1, sq, ws, wsb, sq, None)] == "ZS_ERR_ALIAS"          # state over the norm slot
+
+
+def test_list_plan_groups_reject_bad_arguments_without_gpu():
+    """An empty plan needs no device table, so the group calls' checks run without a GPU."""
+    lib = zs.library()
+    h = ctypes.c_void_p()
+    assert zs.STATUS[lib.zs_list_plan_create(None, 0, 2, None, ctypes.byref(h))] == "ZS_OK"
+    try:
+        g = (ctypes.c_int32 * 1)(0)
+        assert zs.STATUS[lib.zs_list_plan_set_groups(None, g, 2, None)] == "ZS_ERR_NULL"
+        assert zs.STATUS[lib.zs_list_plan_set_groups(h, g, 0, None)] == "ZS_ERR_RANGE"
+        assert zs.STATUS[lib.zs_list_plan_set_groups(h, g, 9, None)] == "ZS_ERR_RANGE"
+        assert zs.STATUS[lib.zs_list_plan_set_groups(h, None, 3, None)] == "ZS_OK"     # no tensors to assign
+        hps = (zs.AdamHPStruct * 3)(*[zs.AdamHPStruct(1e-3, 0.9, 0.999, 1e-8, wd) for wd in (0.1, 0.0, 0.01)])
+        assert zs.STATUS[lib.zs_reduce_adam_list_plan_groups(h, hps, 2, 1, None)] == "ZS_ERR_RANGE"  # plan has 3
+        assert zs.STATUS[lib.zs_reduce_adam_list_plan_groups(h, None, 3, 1, None)] == "ZS_ERR_NULL"
+        bad = (zs.AdamHPStruct * 3)(*[zs.AdamHPStruct(1e-3, 0.9, 1.5, 1e-8, 0.0)] * 3)
+        assert zs.STATUS[lib.zs_reduce_adam_list_plan_groups(h, bad, 3, 1, None)] == "ZS_ERR_RANGE"
+        assert zs.STATUS[lib.zs_reduce_adam_list_plan_groups(h, hps, 3, 1, None)] == "ZS_OK"         # nothing to do
+    finally:
+        lib.zs_list_plan_destroy(h)

@@ -140,3 +140,45 @@ def test_list_rejects_overlap_on_gpu(env):
     with pytest.raises(zs.ZShardError) as ei:
         zs.ListPlan([t0, t1], 1)
     assert ei.value.name == "ZS_ERR_ALIAS"
+
+
+def oracle_list_groups(orc, w, host, offsets, t, hps, groups):
+    """The oracle tensor by tensor, tensor k with hps[groups[k]]; gaps keep their inputs."""
+    L = host["P"].size
+    P, M, V = host["P"].copy(), host["M"].copy(), host["V"].copy()
+    B = np.full(L, 0x7FBF, dtype=np.uint16)
+    for k, (o, n) in enumerate(zip(offsets, w.sizes)):
+        sl = slice(int(o), int(o) + int(n))
+        p, m, v, b = P[sl].copy(), M[sl].copy(), V[sl].copy(), B[sl].copy()
+        orc.step_inplace([g[sl] for g in host["G"]], p, m, v, b, hps[groups[k]], t)
+        P[sl], M[sl], V[sl], B[sl] = p, m, v, b
+    return dict(P=P, M=M, V=V, B=B)
+
+
+@pytest.mark.parametrize("N,n_groups", [(3, 3), (16, 8), (8, 1)])
+def test_list_plan_hyperparameter_groups(env, orc, N, n_groups):
+    """Tensors in hyperparameter groups (different lr and weight decay per
+    group, e.g. no decay on norms and biases), one launch, against the oracle
+    per tensor with its group's set; then the single-set call again applies
+    its one set to every tensor."""
+    torch, zs = env["torch"], env["zs"]
+    w = small_ragged(N, 120, seed=300 + N, zero_frac=0.01)
+    host, d, offsets, L = arena_case(env, w)
+    groups = [(k * 7 + 3) % n_groups for k in range(len(w.sizes))]
+    hps = [dict(lr=1e-3 * (1 + g), beta1=0.9, beta2=0.999 - 0.0001 * g, eps=1e-8, weight_decay=0.1 * (g % 2))
+           for g in range(n_groups)]
+    with zs.ListPlan.from_arenas(w.sizes, offsets, d["G"], d["P"], d["M"], d["V"], d["B"]) as plan:
+        plan.set_groups(groups, n_groups)
+        plan.step_groups(hps, 4)
+        torch.cuda.synchronize()
+        got = dict(P=d["P"].cpu().numpy(), M=d["M"].cpu().numpy(), V=d["V"].cpu().numpy(),
+                   B=d["B"].cpu().numpy().view(np.uint16))
+        ref = oracle_list_groups(orc, w, host, offsets, 4, hps, groups)
+        parity.assert_step(got, ref, f"groups N={N}")
+        assert parity.bit_identical(got, ref)
+        plan.step(HP, 5)   # one set for every tensor, whatever the groups
+        torch.cuda.synchronize()
+    got2 = dict(P=d["P"].cpu().numpy(), M=d["M"].cpu().numpy(), V=d["V"].cpu().numpy(),
+                B=d["B"].cpu().numpy().view(np.uint16))
+    ref2 = oracle_list(orc, w, dict(G=host["G"], P=ref["P"], M=ref["M"], V=ref["V"]), offsets, 5, HP)
+    assert parity.bit_identical(got2, ref2)
