@@ -19,7 +19,7 @@ def build(verbose: bool = False) -> str:
     orc = os.path.join(ROOT, "oracle")
     cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROCM, "include"), SRC, "-o", OUT,
-           "-L", pkg, "-lzshard", "-L", orc, "-loracle", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+           "-L", pkg, "-lzshard", "-L", orc, "-loracle", "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-lm",
            "-Wl,-rpath,$ORIGIN/../../sharded_mixed_precision_rank_amd:$ORIGIN/../../oracle:" + os.path.join(ROCM, "lib")]
     if verbose:
         print(" ".join(cmd), flush=True)

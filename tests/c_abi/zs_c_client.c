@@ -9,7 +9,12 @@
  *      in its own allocations), run at steps 1 and 2;
  *   3. the one-shot list call on the same tensors at step 3;
  *   4. argument errors (N = 0, a NULL array) return their statuses before
- *      anything is enqueued.
+ *      anything is enqueued;
+ *   5. the two-pass form with global-norm clipping active (70,001 parameters,
+ *      a peeled head): the mean gradient, the norm (to 1e-12 relative, as
+ *      the order of the double sum is the kernel's) and the clipped step;
+ *   6. the device loss scaler over a sequence of finite, Inf and NaN norms;
+ *   7. the optimizer-offload step (fp32 state in host memory, 13 chunks).
  * Prints "zs_c_client ok" and exits 0 on success, 1 on any mismatch or error.
  * Test code: the inputs come from a small generator of its own. */
 #include <hip/hip_runtime_api.h>
@@ -26,6 +31,17 @@ typedef struct oracle_hp {
 } oracle_hp;
 int oracle_reduce_adam(const uint16_t* const* G, int32_t N, int64_t n, float* P, float* M, float* V, uint16_t* B,
                        const oracle_hp* hp, int64_t t, int32_t threads);
+int oracle_reduce_unscale(const uint16_t* const* G, int32_t N, int64_t n, int32_t fmt, double loss_scale, float* gbar,
+                          int32_t threads);
+double oracle_sqnorm(const float* gbar, int64_t n);
+int oracle_adam_from_gbar(const float* gbar, int64_t n, float* P, float* M, float* V, uint16_t* B, int32_t out_fmt,
+                          const oracle_hp* hp, int64_t t, double total_sq, double max_norm, int32_t skip_nonfinite,
+                          int32_t threads);
+typedef struct oracle_scaler {
+  double scale, min_scale;
+  int64_t window, hysteresis, overflows, clean;
+} oracle_scaler;
+int oracle_scaler_update(oracle_scaler* s, int32_t overflow);
 
 #define CHECK_HIP(x)                                                              \
   do {                                                                            \
@@ -203,6 +219,114 @@ int main(void) {
   CHECK_ZS(zs_reduce_adam_list(tab, 3, 3, &hp, 3, stream));
   for (int k = 0; k < 3; ++k) bad |= oracle_compare(&ts[k], &hp, 3, "one-shot list");
   for (int k = 0; k < 3; ++k) shard_free(&ts[k]);
+
+  /* 5. two-pass form with clipping */
+  {
+    shard s;
+    shard_init(&s, 70001, 3, 3);
+    const int64_t n = s.n;
+    const size_t wsb = zs_two_pass_workspace_bytes(n);
+    void* ws = dalloc(&s, wsb);
+    double* dsq = (double*)dalloc(&s, 8);
+    CHECK_ZS(zs_reduce_grads_flat((const uint16_t* const*)s.dg, s.N, n, ZS_FORMAT_BF16, 1.0, ws, wsb, dsq, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    double sq = 0;
+    CHECK_HIP(hipMemcpy(&sq, dsq, 8, hipMemcpyDeviceToHost));
+    float* gref = (float*)malloc((size_t)n * 4);
+    float* gdev = (float*)malloc((size_t)n * 4);
+    oracle_reduce_unscale((const uint16_t* const*)s.hg, s.N, n, 0, 1.0, gref, 4);
+    const uintptr_t g0 = ((uintptr_t)ws + 255) & ~(uintptr_t)255;  /* the mean gradient's place in the workspace */
+    CHECK_HIP(hipMemcpy(gdev, (void*)g0, (size_t)n * 4, hipMemcpyDeviceToHost));
+    if (memcmp(gdev, gref, (size_t)n * 4)) { fprintf(stderr, "two-pass: mean gradient differs\n"); bad = 1; }
+    const double sref = oracle_sqnorm(gref, n);
+    if (!(sq == sq) || (sq > sref ? sq - sref : sref - sq) > 1e-12 * sref) {
+      fprintf(stderr, "two-pass: norm %.17g against %.17g\n", sq, sref);
+      bad = 1;
+    }
+    const double max_norm = 0.5 * __builtin_sqrt(sref);  /* clipping active: coefficient about 1/2 */
+    CHECK_ZS(zs_adam_from_grads_flat(ws, wsb, n, s.dp, s.dm, s.dv, s.db, ZS_FORMAT_BF16, &hp, 11, dsq, max_norm, 1,
+                                     stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    uint16_t* hb = (uint16_t*)malloc((size_t)n * 2);
+    oracle_hp oh = {hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay};
+    if (oracle_adam_from_gbar(gref, n, s.hp, s.hm, s.hv, hb, 0, &oh, 11, sq, max_norm, 1, 4) != 0) {
+      fprintf(stderr, "two-pass: the oracle skipped or rejected the step\n");
+      bad = 1;
+    }
+    float* gp = (float*)malloc((size_t)n * 4);
+    uint16_t* gb = (uint16_t*)malloc((size_t)n * 2);
+    CHECK_HIP(hipMemcpy(gp, s.dp, (size_t)n * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(gb, s.db, (size_t)n * 2, hipMemcpyDeviceToHost));
+    if (memcmp(gp, s.hp, (size_t)n * 4) || memcmp(gb, hb, (size_t)n * 2)) {
+      fprintf(stderr, "two-pass: clipped step differs from the oracle\n");
+      bad = 1;
+    }
+    free(gref); free(gdev); free(hb); free(gp); free(gb);
+    shard_free(&s);
+  }
+
+  /* 6. device loss scaler */
+  {
+    zs_loss_scaler host;
+    CHECK_ZS(zs_loss_scaler_init(&host, 65536.0, 1.0, 3, 2));
+    oracle_scaler ref = {65536.0, 1.0, 3, 2, 0, 0};
+    zs_loss_scaler* dstate = NULL;
+    double* dsq = NULL;
+    int32_t* dtaken = NULL;
+    CHECK_HIP(hipMalloc((void**)&dstate, sizeof host));
+    CHECK_HIP(hipMalloc((void**)&dsq, 8));
+    CHECK_HIP(hipMalloc((void**)&dtaken, 4));
+    CHECK_HIP(hipMemcpy(dstate, &host, sizeof host, hipMemcpyHostToDevice));
+    const double inf = __builtin_inf(), nan = __builtin_nan("");
+    const double norms[12] = {1.0, inf, 2.0, nan, inf, 0.5, 0.25, 3.0, 4.0, inf, inf, 1.0};
+    for (int k = 0; k < 12; ++k) {
+      CHECK_HIP(hipMemcpy(dsq, &norms[k], 8, hipMemcpyHostToDevice));
+      CHECK_ZS(zs_loss_scaler_update_device(dstate, dsq, dtaken, stream));
+      CHECK_HIP(hipStreamSynchronize(stream));
+      const int32_t want = oracle_scaler_update(&ref, !(norms[k] - norms[k] == 0.0));
+      zs_loss_scaler got;
+      int32_t taken = -1;
+      CHECK_HIP(hipMemcpy(&got, dstate, sizeof got, hipMemcpyDeviceToHost));
+      CHECK_HIP(hipMemcpy(&taken, dtaken, 4, hipMemcpyDeviceToHost));
+      if (memcmp(&got, &ref, sizeof got) || taken != want) {
+        fprintf(stderr, "device scaler differs from the oracle at step %d\n", k);
+        bad = 1;
+      }
+    }
+    CHECK_HIP(hipFree(dstate));
+    CHECK_HIP(hipFree(dsq));
+    CHECK_HIP(hipFree(dtaken));
+  }
+
+  /* 7. optimizer offload */
+  {
+    shard s;
+    shard_init(&s, 50000, 4, 0);
+    const int64_t n = s.n;
+    float* P = (float*)malloc((size_t)n * 4);
+    float* M = (float*)malloc((size_t)n * 4);
+    float* V = (float*)malloc((size_t)n * 4);
+    memcpy(P, s.hp, (size_t)n * 4);
+    memcpy(M, s.hm, (size_t)n * 4);
+    memcpy(V, s.hv, (size_t)n * 4);
+    zs_offload_t off = NULL;
+    CHECK_ZS(zs_offload_create(4096, 3, &off));
+    CHECK_ZS(zs_offload_step_flat(off, (const uint16_t* const*)s.dg, s.N, n, P, M, V, s.db, &hp, 13, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    zs_offload_destroy(off);
+    uint16_t* hb = (uint16_t*)malloc((size_t)n * 2);
+    uint16_t* gb = (uint16_t*)malloc((size_t)n * 2);
+    oracle_hp oh = {hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay};
+    oracle_reduce_adam((const uint16_t* const*)s.hg, s.N, n, s.hp, s.hm, s.hv, hb, &oh, 13, 4);
+    CHECK_HIP(hipMemcpy(gb, s.db, (size_t)n * 2, hipMemcpyDeviceToHost));
+    if (memcmp(P, s.hp, (size_t)n * 4) || memcmp(M, s.hm, (size_t)n * 4) || memcmp(V, s.hv, (size_t)n * 4) ||
+        memcmp(gb, hb, (size_t)n * 2)) {
+      fprintf(stderr, "offload step differs from the oracle\n");
+      bad = 1;
+    }
+    free(P); free(M); free(V); free(hb); free(gb);
+    shard_free(&s);
+  }
 
   CHECK_HIP(hipStreamDestroy(stream));
   if (bad) return 1;

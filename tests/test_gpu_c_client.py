@@ -1,6 +1,7 @@
 """The C ABI from a plain C program (tests/c_abi/zs_c_client.c): HIP-runtime
-memory, the flat step, a list plan and the one-shot list call, each checked
-bit for bit against the oracle's C entry points, plus argument errors."""
+memory; the flat step, a list plan, the one-shot list call, the clipped
+two-pass step, the device loss scaler and the offload step, each checked bit
+for bit against the oracle's C entry points; plus argument errors."""
 import os
 import subprocess
 import sys
