@@ -183,6 +183,40 @@ ZS_API zs_status zs_reduce_adam_list_plan_groups(zs_list_plan_t plan, const zs_a
 ZS_API zs_status zs_reduce_adam_list(const zs_tensor* tensors, int32_t T, int32_t N, const zs_adam_hp* hp,
                                      int64_t step, zs_stream stream);
 
+/* ---------------------------------------------------------------------------
+ * Device-resident step index, for training steps captured once in a HIP graph
+ * and replayed: the step index (and with it the bias corrections) must then
+ * change on every replay without host work.  The folded scalars of a range of
+ * steps are computed on the host once (zs_fold_table, the same values zs_fold
+ * gives) and kept in device memory; the kernels read the row of the current
+ * step, *step, and zs_step_advance increments it on the device.
+ * ------------------------------------------------------------------------- */
+typedef struct zs_step_source {
+  const zs_folded* table; /* device: the folded scalars of steps t0 .. t0 + count - 1, in order */
+  int64_t t0;             /* the step of table[0], >= 1 */
+  int64_t count;          /* rows in the table, >= 1 */
+  const int64_t* step;    /* device: the step index the kernels use, read when they run */
+  int32_t* status;        /* device, optional: set to 1 by a kernel that found *step outside the table */
+} zs_step_source;
+
+/* The folded scalars of steps t0 .. t0 + count - 1 into the host array out
+   (count rows).  Errors: ZS_ERR_NULL, ZS_ERR_RANGE (as zs_fold, or count < 1). */
+ZS_API zs_status zs_fold_table(const zs_adam_hp* hp, int64_t t0, int64_t count, zs_folded* out);
+
+/* zs_reduce_adam_flat with the step taken from src on the device.  A step
+   outside the table updates nothing (the whole launch skips) and sets
+   *src->status to 1 if status is given.  src itself is read during the call
+   (its pointers are device addresses, 8-byte aligned; status 4-byte).  Other
+   arguments and errors as zs_reduce_adam_flat; ZS_ERR_ALIAS if the table,
+   step or status overlap an output or each other. */
+ZS_API zs_status zs_reduce_adam_flat_devstep(const uint16_t* const* grad_chunks, int32_t N, int64_t n,
+                                             float* master, float* m, float* v, uint16_t* param_bf16,
+                                             const zs_step_source* src, zs_stream stream);
+
+/* *step += 1 on the device (one thread), enqueued on `stream`.  Errors:
+   ZS_ERR_NULL, ZS_ERR_ALIGN, ZS_ERR_HIP. */
+ZS_API zs_status zs_step_advance(int64_t* step, zs_stream stream);
+
 /* Waits for the device to go idle, then frees the plan's table.  NULL is a no-op. */
 ZS_API void zs_list_plan_destroy(zs_list_plan_t plan);
 
@@ -235,6 +269,15 @@ ZS_API zs_status zs_adam_from_grads_flat(const void* workspace, size_t workspace
                                          float* m, float* v, uint16_t* param_half, int32_t param_format,
                                          const zs_adam_hp* hp, int64_t step, const double* total_sq,
                                          double max_norm, int32_t skip_nonfinite, zs_stream stream);
+
+/* zs_adam_from_grads_flat with the step taken from src on the device (see
+   zs_step_source); a step outside the table updates nothing and sets
+   *src->status.  Other arguments and errors as zs_adam_from_grads_flat. */
+ZS_API zs_status zs_adam_from_grads_flat_devstep(const void* workspace, size_t workspace_bytes, int64_t n,
+                                                 float* master, float* m, float* v, uint16_t* param_half,
+                                                 int32_t param_format, const zs_step_source* src,
+                                                 const double* total_sq, double max_norm, int32_t skip_nonfinite,
+                                                 zs_stream stream);
 
 /* Dynamic loss scale for fp16 training (the DeepSpeed fp16 block's
    loss_scale 0 = dynamic, initial_scale_power, loss_scale_window, hysteresis,

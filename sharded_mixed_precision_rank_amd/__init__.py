@@ -45,6 +45,11 @@ class TensorStruct(ctypes.Structure):
 
 
 _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+
+
+class StepSourceStruct(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_void_p), ("t0", ctypes.c_int64), ("count", ctypes.c_int64),
+                ("step", ctypes.c_void_p), ("status", ctypes.c_void_p)]
 _lib.zs_abi_version.restype = ctypes.c_int
 _lib.zs_status_string.restype = ctypes.c_char_p
 _lib.zs_status_string.argtypes = [ctypes.c_int]
@@ -69,6 +74,13 @@ _lib.zs_reduce_adam_list_plan_groups.restype = ctypes.c_int
 _lib.zs_reduce_adam_list_plan_groups.argtypes = [_vp, ctypes.POINTER(AdamHPStruct), _i32, _i64, _vp]
 _lib.zs_list_plan_info.restype = ctypes.c_int
 _lib.zs_list_plan_info.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+_lib.zs_fold_table.restype = ctypes.c_int
+_lib.zs_fold_table.argtypes = [ctypes.POINTER(AdamHPStruct), _i64, _i64, _vp]
+_lib.zs_reduce_adam_flat_devstep.restype = ctypes.c_int
+_lib.zs_reduce_adam_flat_devstep.argtypes = [ctypes.POINTER(_vp), _i32, _i64, _vp, _vp, _vp, _vp,
+                                             ctypes.POINTER(StepSourceStruct), _vp]
+_lib.zs_step_advance.restype = ctypes.c_int
+_lib.zs_step_advance.argtypes = [_vp, _vp]
 _lib.zs_set_grid_blocks.restype = ctypes.c_int
 _lib.zs_set_grid_blocks.argtypes = [_i32]
 _lib.zs_two_pass_workspace_bytes.restype = ctypes.c_size_t
@@ -76,6 +88,9 @@ _lib.zs_two_pass_workspace_bytes.argtypes = [_i64]
 _lib.zs_reduce_grads_flat.restype = ctypes.c_int
 _lib.zs_reduce_grads_flat.argtypes = [ctypes.POINTER(_vp), _i32, _i64, _i32, ctypes.c_double, _vp, ctypes.c_size_t,
                                       _vp, _vp]
+_lib.zs_adam_from_grads_flat_devstep.restype = ctypes.c_int
+_lib.zs_adam_from_grads_flat_devstep.argtypes = [_vp, ctypes.c_size_t, _i64, _vp, _vp, _vp, _vp, _i32,
+                                                 ctypes.POINTER(StepSourceStruct), _vp, ctypes.c_double, _i32, _vp]
 _lib.zs_adam_from_grads_flat.restype = ctypes.c_int
 _lib.zs_adam_from_grads_flat.argtypes = [_vp, ctypes.c_size_t, _i64, _vp, _vp, _vp, _vp, _i32,
                                          ctypes.POINTER(AdamHPStruct), _i64, _vp, ctypes.c_double, _i32, _vp]
@@ -152,6 +167,62 @@ def fold(hp, step: int) -> dict:
     h = _hp(hp)
     _check(_lib.zs_fold(ctypes.byref(h), step, ctypes.byref(out)), "zs_fold")
     return {k: getattr(out, k) for k, _ in FoldedStruct._fields_}
+
+
+def fold_table(hp, t0: int, count: int):
+    """The folded scalars of steps t0 .. t0+count-1: a (count, 8) float32 array, rows as :func:`fold`."""
+    import numpy as np
+
+    out = np.empty((count, 8), dtype=np.float32)
+    h = _hp(hp)
+    _check(_lib.zs_fold_table(ctypes.byref(h), t0, count, out.ctypes.data), "zs_fold_table")
+    return out
+
+
+class StepSource:
+    """A device-resident step index with the folded scalars of steps
+    t0 .. t0+count-1, for steps captured in a HIP graph: the *_devstep calls
+    read the current step on the device and :meth:`advance` increments it
+    there, so each replay takes the next step."""
+
+    def __init__(self, hp, t0: int, count: int, device="cuda", start: int = None):
+        import torch
+
+        self.table = torch.from_numpy(fold_table(hp, t0, count)).to(device)
+        self.step_t = torch.tensor([t0 if start is None else start], dtype=torch.int64, device=device)
+        self.status_t = torch.zeros(1, dtype=torch.int32, device=device)
+        self.device = self.table.device
+        self._s = StepSourceStruct(self.table.data_ptr(), t0, count, self.step_t.data_ptr(),
+                                   self.status_t.data_ptr())
+
+    def advance(self, stream=None) -> None:
+        import torch
+
+        with torch.cuda.device(self.device):
+            _check(_lib.zs_step_advance(self.step_t.data_ptr(), _stream_handle(stream, self.device)),
+                   "zs_step_advance")
+
+    @property
+    def step(self) -> int:
+        return int(self.step_t.item())
+
+    @property
+    def status(self) -> int:
+        return int(self.status_t.item())
+
+
+def reduce_adam_flat_devstep(grads: Sequence, master, m, v, param, src: StepSource, stream=None) -> None:
+    """:func:`reduce_adam_flat` with the step (and its folded scalars) read from ``src`` on the device."""
+    import torch
+
+    N = len(grads)
+    n = _tensor_args(grads, master, m, v, param)
+    dev = _one_device(master, m, v, param, src.table, *grads)
+    tab = (_vp * max(N, 1))(*[g.data_ptr() for g in grads])
+    with torch.cuda.device(dev):
+        _check(_lib.zs_reduce_adam_flat_devstep(tab, N, n, master.data_ptr(), m.data_ptr(), v.data_ptr(),
+                                                param.data_ptr(), ctypes.byref(src._s), _stream_handle(stream, dev)),
+               "zs_reduce_adam_flat_devstep")
 
 
 def set_grid_blocks(blocks: int) -> None:
@@ -467,6 +538,31 @@ def adam_from_grads_flat(workspace, n: int, master, m, v, param, hp, step: int, 
                                             _fmt(param_format), ctypes.byref(h), step, total_sq.data_ptr(), max_norm,
                                             int(skip_nonfinite), _stream_handle(stream, dev)),
                "zs_adam_from_grads_flat")
+
+
+def adam_from_grads_flat_devstep(workspace, n: int, master, m, v, param, src: StepSource, total_sq,
+                                 max_norm: float = 0.0, param_format="bf16", skip_nonfinite: bool = True,
+                                 stream=None) -> None:
+    """:func:`adam_from_grads_flat` with the step read from ``src`` on the device."""
+    import torch
+
+    _dev_check(master, _f32_types(), "master")
+    _dev_check(m, _f32_types(), "m")
+    _dev_check(v, _f32_types(), "v")
+    _dev_check(param, _half_types(), "param")
+    _dev_check(total_sq, (torch.float64,), "total_sq")
+    _dev_check(workspace, (torch.uint8, torch.int8, torch.float32, torch.float64), "workspace")
+    for name, t in (("master", master), ("m", m), ("v", v), ("param", param)):
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    dev = _one_device(workspace, master, m, v, param, total_sq, src.table)
+    with torch.cuda.device(dev):
+        _check(_lib.zs_adam_from_grads_flat_devstep(workspace.data_ptr(),
+                                                    workspace.numel() * workspace.element_size(), n,
+                                                    master.data_ptr(), m.data_ptr(), v.data_ptr(), param.data_ptr(),
+                                                    _fmt(param_format), ctypes.byref(src._s), total_sq.data_ptr(),
+                                                    max_norm, int(skip_nonfinite), _stream_handle(stream, dev)),
+               "zs_adam_from_grads_flat_devstep")
 
 
 def clipped_step_flat(grads: Sequence, master, m, v, param, hp, step: int, max_norm: float = 0.0,

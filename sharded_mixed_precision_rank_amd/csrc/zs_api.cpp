@@ -188,6 +188,30 @@ zs_status after_launch(hipError_t e, hipStream_t stream, const char* what) {
   return ZS_OK;
 }
 
+// A device step source: checked, its ranges appended to `rs` (the table and
+// the step are read, the status word is written), and turned into the
+// kernels' StepRef.
+zs_status step_ref_of(const zs_step_source* src, std::vector<Range>& rs, zs::StepRef* ref) {
+  if (!src) return fail(ZS_ERR_NULL, "src is NULL");
+  if (!src->table || !src->step) return fail(ZS_ERR_NULL, "src->table and src->step must not be NULL");
+  if (src->t0 < 1 || src->count < 1 || src->count > (int64_t(1) << 40))
+    return fail(ZS_ERR_RANGE, "src->t0 must be >= 1 and src->count in [1, 2^40]");
+  if (!aligned(src->table, 4) || !aligned(src->step, 8) || (src->status && !aligned(src->status, 4)))
+    return fail(ZS_ERR_ALIGN, "the table must be 4-byte, the step 8-byte and the status 4-byte aligned");
+  const uintptr_t tb = (uintptr_t)src->table, te = tb + sizeof(zs_folded) * (uintptr_t)src->count;
+  const uintptr_t sp = (uintptr_t)src->step;
+  if (src->status) {  // the one output among these: it must not lie inside the table or the step
+    const uintptr_t st = (uintptr_t)src->status;
+    if ((st < te && tb < st + 4) || (st < sp + 8 && sp < st + 4))
+      return fail(ZS_ERR_ALIAS, "src->status overlaps the table or the step");
+    rs.push_back({st, st + 4, 0, -1});
+  }
+  rs.push_back({tb, te, 1, -1});
+  rs.push_back({sp, sp + 8, 1, -1});
+  *ref = zs::StepRef{src->table, src->step, src->status, src->t0, src->count};
+  return ZS_OK;
+}
+
 }  // namespace
 
 namespace zs {
@@ -320,6 +344,45 @@ struct zs_list_plan {
   const uint16_t** gptrs;
 };
 
+namespace {
+
+// zs_reduce_adam_flat with the step from the host (src == NULL) or the device.
+zs_status flat_step(const uint16_t* const* grad_chunks, int32_t N, int64_t n, float* master, float* m, float* v,
+                    uint16_t* param_bf16, const zs_adam_hp* hp, int64_t step, const zs_step_source* src,
+                    zs_stream stream, const char* what) {
+  try {
+    g_last_error.clear();
+    if (!src) {
+      zs_status st = check_hp(hp, step);
+      if (st) return st;
+    }
+    if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
+    std::vector<Range> rs;
+    zs_status st = check_tensor(grad_chunks, N, n, master, m, v, param_bf16, 0, rs);
+    if (st) return st;
+    zs::StepRef ref{};
+    if (src) {
+      st = step_ref_of(src, rs, &ref);
+      if (st) return st;
+    }
+    if (n == 0) return ZS_OK;
+    st = check_alias(rs);
+    if (st) return st;
+    const zs::FlatShape s = shape_of(grad_chunks, N, n, master, m, v, param_bf16);
+    // with a device step the table supplies the folded scalars; only N's fields are used from these
+    const zs_adam_hp placeholder = {0.0, 0.0, 0.0, 1.0, 0.0};
+    const zs::Scalars c = make_scalars(src ? placeholder : *hp, src ? 1 : step, N);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return after_launch(zs::launch_flat(grad_chunks, s, c, ref, auto_blocks(), hs), hs, what);
+  } catch (const std::bad_alloc&) {
+    return fail(ZS_ERR_NOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(ZS_ERR_HIP, "unexpected exception");
+  }
+}
+
+}  // namespace
+
 extern "C" {
 
 int zs_abi_version(void) { return ZS_ABI_VERSION; }
@@ -357,26 +420,34 @@ zs_status zs_set_grid_blocks(int32_t blocks) {
 zs_status zs_reduce_adam_flat(const uint16_t* const* grad_chunks, int32_t N, int64_t n, float* master, float* m,
                               float* v, uint16_t* param_bf16, const zs_adam_hp* hp, int64_t step,
                               zs_stream stream) {
-  try {
-    g_last_error.clear();
-    zs_status st = check_hp(hp, step);
-    if (st) return st;
-    if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
-    std::vector<Range> rs;
-    st = check_tensor(grad_chunks, N, n, master, m, v, param_bf16, 0, rs);
-    if (st) return st;
-    if (n == 0) return ZS_OK;
-    st = check_alias(rs);
-    if (st) return st;
-    const zs::FlatShape s = shape_of(grad_chunks, N, n, master, m, v, param_bf16);
-    const zs::Scalars c = make_scalars(*hp, step, N);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    return after_launch(zs::launch_flat(grad_chunks, s, c, auto_blocks(), hs), hs, "zs_reduce_adam_flat launch");
-  } catch (const std::bad_alloc&) {
-    return fail(ZS_ERR_NOMEM, "host allocation failed");
-  } catch (...) {
-    return fail(ZS_ERR_HIP, "unexpected exception");
-  }
+  return flat_step(grad_chunks, N, n, master, m, v, param_bf16, hp, step, nullptr, stream,
+                   "zs_reduce_adam_flat launch");
+}
+
+zs_status zs_reduce_adam_flat_devstep(const uint16_t* const* grad_chunks, int32_t N, int64_t n, float* master,
+                                      float* m, float* v, uint16_t* param_bf16, const zs_step_source* src,
+                                      zs_stream stream) {
+  if (!src) return fail(ZS_ERR_NULL, "src is NULL");
+  return flat_step(grad_chunks, N, n, master, m, v, param_bf16, nullptr, 0, src, stream,
+                   "zs_reduce_adam_flat_devstep launch");
+}
+
+zs_status zs_fold_table(const zs_adam_hp* hp, int64_t t0, int64_t count, zs_folded* out) {
+  g_last_error.clear();
+  if (!out) return fail(ZS_ERR_NULL, "out is NULL");
+  if (count < 1 || count > (int64_t(1) << 40)) return fail(ZS_ERR_RANGE, "count must be in [1, 2^40]");
+  zs_status st = check_hp(hp, t0);
+  if (st) return st;
+  for (int64_t k = 0; k < count; ++k) fold_scalars(*hp, t0 + k, out + k);
+  return ZS_OK;
+}
+
+zs_status zs_step_advance(int64_t* step, zs_stream stream) {
+  g_last_error.clear();
+  if (!step) return fail(ZS_ERR_NULL, "step is NULL");
+  if (!aligned(step, 8)) return fail(ZS_ERR_ALIGN, "step must be 8-byte aligned");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  return after_launch(zs::launch_step_advance(step, hs), hs, "zs_step_advance");
 }
 
 zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_t N, zs_stream stream,
@@ -694,14 +765,22 @@ zs_status zs_loss_scaler_update_device(zs_loss_scaler* state, const double* tota
   return after_launch(zs::launch_scaler_update(state, total_sq, taken, hs), hs, "zs_loss_scaler_update_device");
 }
 
-zs_status zs_adam_from_grads_flat(const void* workspace, size_t workspace_bytes, int64_t n, float* master, float* m,
-                                  float* v, uint16_t* param_half, int32_t param_format, const zs_adam_hp* hp,
-                                  int64_t step, const double* total_sq, double max_norm, int32_t skip_nonfinite,
-                                  zs_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// Pass 2 with the step from the host (src == NULL) or the device.
+zs_status gbar_step(const void* workspace, size_t workspace_bytes, int64_t n, float* master, float* m, float* v,
+                    uint16_t* param_half, int32_t param_format, const zs_adam_hp* hp, int64_t step,
+                    const zs_step_source* src, const double* total_sq, double max_norm, int32_t skip_nonfinite,
+                    zs_stream stream, const char* what) {
   try {
     g_last_error.clear();
-    zs_status st = check_hp(hp, step);
-    if (st) return st;
+    zs_status st = ZS_OK;
+    if (!src) {
+      st = check_hp(hp, step);
+      if (st) return st;
+    }
     if (n < 0 || n > (int64_t(1) << 56)) return fail(ZS_ERR_RANGE, "n out of range");
     if (param_format != ZS_FORMAT_BF16 && param_format != ZS_FORMAT_FP16)
       return fail(ZS_ERR_RANGE, "param_format must be ZS_FORMAT_BF16 or ZS_FORMAT_FP16");
@@ -722,6 +801,11 @@ zs_status zs_adam_from_grads_flat(const void* workspace, size_t workspace_bytes,
                              {(uintptr_t)param_half, (uintptr_t)param_half + n2, 0, 0},
                              {(uintptr_t)workspace, (uintptr_t)workspace + L.need, 1, 0},
                              {(uintptr_t)total_sq, (uintptr_t)total_sq + 8, 1, 0}};
+    zs::StepRef ref{};
+    if (src) {
+      st = step_ref_of(src, rs, &ref);
+      if (st) return st;
+    }
     st = check_alias(rs);
     if (st) return st;
     zs::FlatShape s;
@@ -742,16 +826,38 @@ zs_status zs_adam_from_grads_flat(const void* workspace, size_t workspace_bytes,
       s.nvec = (n - h) / 8;
       s.scalar_only = 0;
     }
-    const zs::Scalars c = make_scalars(*hp, step, 1);
+    const zs_adam_hp placeholder = {0.0, 0.0, 0.0, 1.0, 0.0};  // a device step: the table supplies the scalars
+    const zs::Scalars c = make_scalars(src ? placeholder : *hp, src ? 1 : step, 1);
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    return after_launch(zs::launch_gbar(L.gbar, s, c, total_sq, max_norm, skip_nonfinite, param_format,
+    return after_launch(zs::launch_gbar(L.gbar, s, c, ref, total_sq, max_norm, skip_nonfinite, param_format,
                                         auto_blocks(), hs),
-                        hs, "zs_adam_from_grads_flat launch");
+                        hs, what);
   } catch (const std::bad_alloc&) {
     return fail(ZS_ERR_NOMEM, "host allocation failed");
   } catch (...) {
     return fail(ZS_ERR_HIP, "unexpected exception");
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+zs_status zs_adam_from_grads_flat(const void* workspace, size_t workspace_bytes, int64_t n, float* master, float* m,
+                                  float* v, uint16_t* param_half, int32_t param_format, const zs_adam_hp* hp,
+                                  int64_t step, const double* total_sq, double max_norm, int32_t skip_nonfinite,
+                                  zs_stream stream) {
+  return gbar_step(workspace, workspace_bytes, n, master, m, v, param_half, param_format, hp, step, nullptr,
+                   total_sq, max_norm, skip_nonfinite, stream, "zs_adam_from_grads_flat launch");
+}
+
+zs_status zs_adam_from_grads_flat_devstep(const void* workspace, size_t workspace_bytes, int64_t n, float* master,
+                                          float* m, float* v, uint16_t* param_half, int32_t param_format,
+                                          const zs_step_source* src, const double* total_sq, double max_norm,
+                                          int32_t skip_nonfinite, zs_stream stream) {
+  if (!src) return fail(ZS_ERR_NULL, "src is NULL");
+  return gbar_step(workspace, workspace_bytes, n, master, m, v, param_half, param_format, nullptr, 0, src,
+                   total_sq, max_norm, skip_nonfinite, stream, "zs_adam_from_grads_flat_devstep launch");
 }
 
 zs_status zs_loss_scaler_init(zs_loss_scaler* s, double initial_scale, double min_scale, int64_t window,

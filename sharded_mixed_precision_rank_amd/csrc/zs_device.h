@@ -84,6 +84,29 @@ __device__ __forceinline__ void adam(float g, float& p, float& m, float& v, cons
   v = v1;
 }
 
+// The launch's scalars: the host-folded ones, or the device table's row for
+// the device step.  False when that step is outside the table: the launch
+// then updates nothing (every workgroup reads the same step), and one thread
+// records it in *status.
+__device__ __forceinline__ bool step_scalars(const StepRef& r, Scalars& c) {
+  if (!r.table) return true;
+  const int64_t t = *r.step;
+  if (t < r.t0 || t - r.t0 >= r.count) {
+    if (r.status && blockIdx.x == 0 && threadIdx.x == 0) *r.status = 1;
+    return false;
+  }
+  const zs_folded f = r.table[t - r.t0];
+  c.b1 = f.b1;
+  c.c1 = f.c1;
+  c.b2 = f.b2;
+  c.c2 = f.c2;
+  c.e = f.eps;
+  c.ss = f.ss;
+  c.rb = f.rb;
+  c.dk = f.dk;
+  return true;
+}
+
 // 16-bit storage formats of gradients and of the working copy.
 constexpr int kBF16 = 0;
 constexpr int kFP16 = 1;

@@ -18,6 +18,18 @@ struct Scalars {
   int32_t pow2;     // N is a power of two: s * inv_n is bit-identical to s / N
 };
 
+// Where a launch takes its step's folded scalars from: the host-folded
+// Scalars (table == NULL), or row *step - t0 of a device table (the step
+// index in device memory; a step outside the table skips the launch and sets
+// *status when status is not NULL).
+struct StepRef {
+  const zs_folded* table;
+  const int64_t* step;
+  int32_t* status;
+  int64_t t0;
+  int64_t count;
+};
+
 // Flat shard, as the kernel sees it.  Elements [0, head) and
 // [head + 8*nvec, n) go through the per-element path; the 8-element groups in
 // between through vector accesses (16-byte aligned at least, 128-byte when the
@@ -71,8 +83,10 @@ int64_t common_peel(const float* p, const float* m, const float* v, const uint16
 int64_t common_peel_sized(const void* const* ptrs, const int* elem_bytes, int count);
 
 // Launches (host side, defined with the kernels).
-hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, int blocks,
-                       hipStream_t stream);
+hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, const StepRef& ref,
+                       int blocks, hipStream_t stream);
+// One device thread: *step += 1.
+hipError_t launch_step_advance(int64_t* step, hipStream_t stream);
 // cs: n_sets folded scalar sets, one per hyperparameter group (1 <= n_sets <= kMaxGroups).
 hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
                        const uint16_t* const* gptrs, const Scalars* cs, int n_sets, int blocks,

@@ -138,21 +138,28 @@ struct FlatArgs {
   const uint16_t* g[NT > 0 ? NT : ZS_MAX_REPLICAS];
   FlatShape s;
   Scalars c;
+  StepRef r;  // table == NULL: the step of `c`
 };
 
 template <int NT>
 __global__ __launch_bounds__(kBlock) void flat_kernel(const FlatArgs<NT> a) {
-  const int N = NT > 0 ? NT : a.c.n_rep;
+  Scalars c = a.c;
+  if (!step_scalars(a.r, c)) return;
+  const int N = NT > 0 ? NT : c.n_rep;
   if (!a.s.scalar_only) {
     auto G0 = [&](int r) { return a.g[r]; };
-    tiles<NT>(G0, N, 0, a.s.nvec, blockIdx.x, gridDim.x, a.s, a.c);
+    tiles<NT>(G0, N, 0, a.s.nvec, blockIdx.x, gridDim.x, a.s, c);
     auto G = [&](int r) { return a.g[r]; };
-    if (blockIdx.x == gridDim.x - 1) edge_step(G, N, threadIdx.x, a.s, a.c);
+    if (blockIdx.x == gridDim.x - 1) edge_step(G, N, threadIdx.x, a.s, c);
   } else {
     auto G = [&](int r) { return a.g[r]; };
     const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < a.s.n; i += stride) elem_step(G, N, i, a.s, a.c);
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < a.s.n; i += stride) elem_step(G, N, i, a.s, c);
   }
+}
+
+__global__ void step_advance_kernel(int64_t* step) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *step = *step + 1;
 }
 
 __device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
@@ -231,12 +238,13 @@ int clamp_grid(int blocks, int64_t work) {
 }
 
 template <int NT>
-hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, int blocks,
-                   hipStream_t stream) {
+hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, const StepRef& ref,
+                   int blocks, hipStream_t stream) {
   FlatArgs<NT> a;
   for (int r = 0; r < c.n_rep; ++r) a.g[r] = grads[r];
   a.s = s;
   a.c = c;
+  a.r = ref;
   const int grid = clamp_grid(blocks, s.scalar_only ? s.n : s.nvec);
   (void)hipGetLastError();
   flat_kernel<NT><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
@@ -262,18 +270,24 @@ hipError_t go_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* 
 
 }  // namespace
 
-hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, int blocks,
-                       hipStream_t stream) {
+hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, const StepRef& ref,
+                       int blocks, hipStream_t stream) {
   switch (c.n_rep) {
-    case 1: return go_flat<1>(grads, s, c, blocks, stream);
-    case 2: return go_flat<2>(grads, s, c, blocks, stream);
-    case 4: return go_flat<4>(grads, s, c, blocks, stream);
-    case 8: return go_flat<8>(grads, s, c, blocks, stream);
-    case 16: return go_flat<16>(grads, s, c, blocks, stream);
-    case 32: return go_flat<32>(grads, s, c, blocks, stream);
-    case 64: return go_flat<64>(grads, s, c, blocks, stream);
-    default: return go_flat<0>(grads, s, c, blocks, stream);
+    case 1: return go_flat<1>(grads, s, c, ref, blocks, stream);
+    case 2: return go_flat<2>(grads, s, c, ref, blocks, stream);
+    case 4: return go_flat<4>(grads, s, c, ref, blocks, stream);
+    case 8: return go_flat<8>(grads, s, c, ref, blocks, stream);
+    case 16: return go_flat<16>(grads, s, c, ref, blocks, stream);
+    case 32: return go_flat<32>(grads, s, c, ref, blocks, stream);
+    case 64: return go_flat<64>(grads, s, c, ref, blocks, stream);
+    default: return go_flat<0>(grads, s, c, ref, blocks, stream);
   }
+}
+
+hipError_t launch_step_advance(int64_t* step, hipStream_t stream) {
+  (void)hipGetLastError();
+  step_advance_kernel<<<dim3(1), dim3(64), 0, stream>>>(step);
+  return hipGetLastError();
 }
 
 hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,

@@ -34,7 +34,8 @@ hipError_t launch_reduce(const uint16_t* const* grads, const TwoPassShape& sh, i
 // *taken when taken is not NULL.
 hipError_t launch_scaler_update(zs_loss_scaler* state, const double* total_sq, int32_t* taken, hipStream_t stream);
 
-hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, const double* total_sq,
-                       double max_norm, int skip_nonfinite, int param_format, int blocks, hipStream_t stream);
+hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, const StepRef& ref,
+                       const double* total_sq, double max_norm, int skip_nonfinite, int param_format, int blocks,
+                       hipStream_t stream);
 
 }  // namespace zs

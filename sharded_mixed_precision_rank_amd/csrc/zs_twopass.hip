@@ -162,6 +162,7 @@ struct GbarArgs {
   const double* total_sq;
   double max_norm;
   int32_t skip_nonfinite;
+  StepRef r;  // table == NULL: the step of `c`
 };
 
 __device__ __forceinline__ float clip_factor(double total_sq, double max_norm) {
@@ -171,9 +172,9 @@ __device__ __forceinline__ float clip_factor(double total_sq, double max_norm) {
 }
 
 template <int OFMT>
-__device__ __forceinline__ void gbar_elem(const GbarArgs& a, int64_t i, float k) {
+__device__ __forceinline__ void gbar_elem(const GbarArgs& a, const Scalars& c, int64_t i, float k) {
   float p = a.s.p[i], m = a.s.m[i], v = a.s.v[i];
-  adam(a.gbar[i] * k, p, m, v, a.c);
+  adam(a.gbar[i] * k, p, m, v, c);
   a.s.p[i] = p;
   a.s.m[i] = m;
   a.s.v[i] = v;
@@ -182,6 +183,8 @@ __device__ __forceinline__ void gbar_elem(const GbarArgs& a, int64_t i, float k)
 
 template <int OFMT>
 __global__ __launch_bounds__(kBlock) void gbar_kernel(const GbarArgs a) {
+  Scalars c = a.c;
+  if (!step_scalars(a.r, c)) return;
   const double tsq = *a.total_sq;
   if (a.skip_nonfinite && !__builtin_isfinite(tsq)) return;  // overflow: the step is skipped everywhere
   const float k = clip_factor(tsq, a.max_norm);
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(kBlock) void gbar_kernel(const GbarArgs a) {
       float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
       float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) adam(g[j] * k, p[j], m[j], v[j], a.c);
+      for (int j = 0; j < 8; ++j) adam(g[j] * k, p[j], m[j], v[j], c);
       const uint32_t o2 = here(e) * 4u;
       GLB f32x4* Po = (GLB f32x4*)at(tile_base(s.p + e0), o2);
       GLB f32x4* Mo = (GLB f32x4*)at(tile_base(s.m + e0), o2);
@@ -226,16 +229,16 @@ __global__ __launch_bounds__(kBlock) void gbar_kernel(const GbarArgs a) {
       const int64_t end = s.scalar_only ? s.n : s.head + 8 * s.nvec;
       const int64_t lo = e0 + 8 * (int64_t)threadIdx.x;
       for (int j = 0; j < 8; ++j)
-        if (lo + j < end && lo + j < e0 + kTile) gbar_elem<OFMT>(a, lo + j, k);
+        if (lo + j < end && lo + j < e0 + kTile) gbar_elem<OFMT>(a, c, lo + j, k);
     }
   }
   if (blockIdx.x == 0 && !s.scalar_only) {  // head and tail elements
     const int64_t tail = s.n - s.head - 8 * s.nvec;
     const int t = threadIdx.x;
     if (t < s.head)
-      gbar_elem<OFMT>(a, t, k);
+      gbar_elem<OFMT>(a, c, t, k);
     else if (t < s.head + tail)
-      gbar_elem<OFMT>(a, s.head + 8 * s.nvec + (t - s.head), k);
+      gbar_elem<OFMT>(a, c, s.head + 8 * s.nvec + (t - s.head), k);
   }
 }
 
@@ -332,12 +335,14 @@ hipError_t launch_scaler_update(zs_loss_scaler* state, const double* total_sq, i
   return hipGetLastError();
 }
 
-hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, const double* total_sq,
-                       double max_norm, int skip_nonfinite, int param_format, int blocks, hipStream_t stream) {
+hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, const StepRef& ref,
+                       const double* total_sq, double max_norm, int skip_nonfinite, int param_format, int blocks,
+                       hipStream_t stream) {
   GbarArgs a;
   a.gbar = gbar;
   a.s = s;
   a.c = c;
+  a.r = ref;
   a.total_sq = total_sq;
   a.max_norm = max_norm;
   a.skip_nonfinite = skip_nonfinite;

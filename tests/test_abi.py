@@ -331,3 +331,43 @@ def test_list_plan_groups_reject_bad_arguments_without_gpu():
         assert zs.STATUS[lib.zs_reduce_adam_list_plan_groups(h, hps, 3, 1, None)] == "ZS_OK"         # nothing to do
     finally:
         lib.zs_list_plan_destroy(h)
+
+
+@pytest.mark.parametrize("t0,count", [(1, 40), (4990, 25)])
+def test_fold_table_rows_are_the_oracle_fold(orc, t0, count):
+    hp = dict(pins.HP, weight_decay=0.1)
+    table = zs.fold_table(hp, t0, count)
+    for k in range(count):
+        ref = np.array(orc.fold(hp, t0 + k), dtype=np.float32)
+        assert np.array_equal(table[k].view(np.uint32), ref.view(np.uint32)), t0 + k
+
+
+def test_devstep_entry_points_reject_bad_arguments_without_gpu():
+    lib = zs.library()
+    hp = zs.AdamHPStruct(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    out = (ctypes.c_float * 8)()
+    assert zs.STATUS[lib.zs_fold_table(ctypes.byref(hp), 1, 0, out)] == "ZS_ERR_RANGE"
+    assert zs.STATUS[lib.zs_fold_table(ctypes.byref(hp), 0, 1, out)] == "ZS_ERR_RANGE"
+    assert zs.STATUS[lib.zs_fold_table(ctypes.byref(hp), 1, 1, None)] == "ZS_ERR_NULL"
+    assert zs.STATUS[lib.zs_step_advance(None, None)] == "ZS_ERR_NULL"
+    assert zs.STATUS[lib.zs_step_advance(A + 4, None)] == "ZS_ERR_ALIGN"
+    n = 4096
+    g = (ctypes.c_void_p * 2)(A + 0x1000000, A + 0x2000000)
+    P, M, V, B = A + 0x3000000, A + 0x4000000, A + 0x5000000, A + 0x6000000
+    tab, step, status = A + 0x7000000, A + 0x7100000, A + 0x7200000
+    def src(**kw):
+        d = dict(table=tab, t0=1, count=100, step=step, status=status)
+        d.update(kw)
+        return zs.StepSourceStruct(d["table"], d["t0"], d["count"], d["step"], d["status"])
+    f = lambda s: zs.STATUS[lib.zs_reduce_adam_flat_devstep(g, 2, n, P, M, V, B, ctypes.byref(s) if s else None,
+                                                             None)]
+    assert f(None) == "ZS_ERR_NULL"
+    assert f(src(table=None)) == "ZS_ERR_NULL"
+    assert f(src(step=None)) == "ZS_ERR_NULL"
+    assert f(src(t0=0)) == "ZS_ERR_RANGE"
+    assert f(src(count=0)) == "ZS_ERR_RANGE"
+    assert f(src(step=step + 4)) == "ZS_ERR_ALIGN"
+    assert f(src(status=status + 2)) == "ZS_ERR_ALIGN"
+    assert f(src(status=tab + 64)) == "ZS_ERR_ALIAS"        # status inside the table
+    assert f(src(table=P + 1024)) == "ZS_ERR_ALIAS"         # table inside the master array (written)
+    assert f(src(status=A + 0x1000000 + 8)) == "ZS_ERR_ALIAS"  # status inside a gradient chunk
