@@ -217,6 +217,14 @@ ZS_API zs_status zs_reduce_adam_flat_devstep(const uint16_t* const* grad_chunks,
    ZS_ERR_NULL, ZS_ERR_ALIGN, ZS_ERR_HIP. */
 ZS_API zs_status zs_step_advance(int64_t* step, zs_stream stream);
 
+/* The plan's step with the step index taken from src on the device (see
+   zs_step_source; one hyperparameter set for every tensor, the table's).  The
+   plan keeps no copy of its tensors' address ranges, so this call checks src
+   within itself only: src's buffers must not overlap the plan's tensors.
+   Errors: ZS_ERR_NULL, ZS_ERR_RANGE, ZS_ERR_ALIGN, ZS_ERR_ALIAS (within src),
+   ZS_ERR_HIP. */
+ZS_API zs_status zs_reduce_adam_list_plan_devstep(zs_list_plan_t plan, const zs_step_source* src, zs_stream stream);
+
 /* Waits for the device to go idle, then frees the plan's table.  NULL is a no-op. */
 ZS_API void zs_list_plan_destroy(zs_list_plan_t plan);
 

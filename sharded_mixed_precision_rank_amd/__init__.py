@@ -79,6 +79,8 @@ _lib.zs_fold_table.argtypes = [ctypes.POINTER(AdamHPStruct), _i64, _i64, _vp]
 _lib.zs_reduce_adam_flat_devstep.restype = ctypes.c_int
 _lib.zs_reduce_adam_flat_devstep.argtypes = [ctypes.POINTER(_vp), _i32, _i64, _vp, _vp, _vp, _vp,
                                              ctypes.POINTER(StepSourceStruct), _vp]
+_lib.zs_reduce_adam_list_plan_devstep.restype = ctypes.c_int
+_lib.zs_reduce_adam_list_plan_devstep.argtypes = [_vp, ctypes.POINTER(StepSourceStruct), _vp]
 _lib.zs_step_advance.restype = ctypes.c_int
 _lib.zs_step_advance.argtypes = [_vp, _vp]
 _lib.zs_set_grid_blocks.restype = ctypes.c_int
@@ -431,6 +433,19 @@ class ListPlan:
         with torch.cuda.device(self._dev):
             _check(_lib.zs_list_plan_set_groups(self._h, arr, n_groups, _stream_handle(stream, self._dev)),
                    "zs_list_plan_set_groups")
+
+    def step_devstep(self, src: "StepSource", stream=None) -> None:
+        """The step with the step index read from ``src`` on the device."""
+        import torch
+
+        if not self._h:
+            raise ValueError("plan is closed")
+        if src.device != self._dev:
+            raise ValueError(f"the step source is on {src.device}, the plan on {self._dev}")
+        with torch.cuda.device(self._dev):
+            _check(_lib.zs_reduce_adam_list_plan_devstep(self._h, ctypes.byref(src._s),
+                                                         _stream_handle(stream, self._dev)),
+                   "zs_reduce_adam_list_plan_devstep")
 
     def step_groups(self, hps: Sequence, step: int, stream=None) -> None:
         """The step with hps[g] for the tensors of group g."""

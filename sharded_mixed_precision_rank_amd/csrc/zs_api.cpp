@@ -561,20 +561,31 @@ zs_status plan_on_current_device(zs_list_plan_t plan) {
   return ZS_OK;
 }
 
-// The step with `n` hyperparameter sets: one for every tensor (n == 1) or one per group.
-zs_status run_plan(zs_list_plan_t plan, const zs_adam_hp* hps, int32_t n, int64_t step, zs_stream stream) {
-  for (int32_t k = 0; k < n; ++k) {
-    zs_status st = check_hp(hps + k, step);
+// The step with `n` hyperparameter sets (one for every tensor, n == 1, or one
+// per group), or with the device step of `src` (hps == NULL, n == 1).
+zs_status run_plan(zs_list_plan_t plan, const zs_adam_hp* hps, int32_t n, int64_t step, const zs_step_source* src,
+                   zs_stream stream) {
+  zs::StepRef ref{};
+  zs::Scalars cs[zs::kMaxGroups];
+  if (src) {
+    std::vector<Range> rs;
+    zs_status st = step_ref_of(src, rs, &ref);
     if (st) return st;
+    const zs_adam_hp placeholder = {0.0, 0.0, 0.0, 1.0, 0.0};  // the table supplies the folded scalars
+    cs[0] = make_scalars(placeholder, 1, plan->N);
+  } else {
+    for (int32_t k = 0; k < n; ++k) {
+      zs_status st = check_hp(hps + k, step);
+      if (st) return st;
+    }
+    for (int32_t k = 0; k < n; ++k) cs[k] = make_scalars(hps[k], step, plan->N);
   }
   if (plan->n_chunks == 0) return ZS_OK;
   zs_status st = plan_on_current_device(plan);
   if (st) return st;
-  zs::Scalars cs[zs::kMaxGroups];
-  for (int32_t k = 0; k < n; ++k) cs[k] = make_scalars(hps[k], step, plan->N);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   return after_launch(
-      zs::launch_list(plan->chunks, plan->n_chunks, plan->tensors, plan->gptrs, cs, n, auto_blocks(), hs), hs,
+      zs::launch_list(plan->chunks, plan->n_chunks, plan->tensors, plan->gptrs, cs, n, ref, auto_blocks(), hs), hs,
       "zs_reduce_adam_list launch");
 }
 
@@ -585,7 +596,14 @@ extern "C" {
 zs_status zs_reduce_adam_list_plan(zs_list_plan_t plan, const zs_adam_hp* hp, int64_t step, zs_stream stream) {
   g_last_error.clear();
   if (!plan) return fail(ZS_ERR_NULL, "plan is NULL");
-  return run_plan(plan, hp, 1, step, stream);
+  return run_plan(plan, hp, 1, step, nullptr, stream);
+}
+
+zs_status zs_reduce_adam_list_plan_devstep(zs_list_plan_t plan, const zs_step_source* src, zs_stream stream) {
+  g_last_error.clear();
+  if (!plan) return fail(ZS_ERR_NULL, "plan is NULL");
+  if (!src) return fail(ZS_ERR_NULL, "src is NULL");
+  return run_plan(plan, nullptr, 1, 0, src, stream);
 }
 
 zs_status zs_list_plan_set_groups(zs_list_plan_t plan, const int32_t* group, int32_t n_groups, zs_stream stream) {
@@ -619,7 +637,7 @@ zs_status zs_reduce_adam_list_plan_groups(zs_list_plan_t plan, const zs_adam_hp*
   if (!hps) return fail(ZS_ERR_NULL, "hps is NULL");
   if (n_groups != plan->n_groups)
     return fail(ZS_ERR_RANGE, "the plan has %d groups, %d hyperparameter sets were given", plan->n_groups, n_groups);
-  return run_plan(plan, hps, n_groups, step, stream);
+  return run_plan(plan, hps, n_groups, step, nullptr, stream);
 }
 
 }  // extern "C"

@@ -87,9 +87,11 @@ hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const S
                        int blocks, hipStream_t stream);
 // One device thread: *step += 1.
 hipError_t launch_step_advance(int64_t* step, hipStream_t stream);
-// cs: n_sets folded scalar sets, one per hyperparameter group (1 <= n_sets <= kMaxGroups).
+// cs: n_sets folded scalar sets, one per hyperparameter group (1 <= n_sets <=
+// kMaxGroups); with a device step (ref.table set) n_sets is 1 and the table
+// supplies the folded scalars.
 hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
-                       const uint16_t* const* gptrs, const Scalars* cs, int n_sets, int blocks,
+                       const uint16_t* const* gptrs, const Scalars* cs, int n_sets, const StepRef& ref, int blocks,
                        hipStream_t stream);
 
 // Elements per list chunk (vector tensors: groups of 8 per chunk = this / 8):

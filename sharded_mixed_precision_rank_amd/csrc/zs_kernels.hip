@@ -197,11 +197,17 @@ template <int NT, int NG>
 __global__ __launch_bounds__(kBlock) void list_kernel(const ListChunk* __restrict__ chunks, int32_t n_chunks,
                                                       const ListTensor* __restrict__ tensors,
                                                       const uint16_t* const* __restrict__ gptrs,
-                                                      const ListScalars<NG> sc) {
+                                                      const ListScalars<NG> sc, const StepRef ref) {
   constexpr int kMaxN = NT > 0 ? NT : ZS_MAX_REPLICAS;
   __shared__ int64_t s_tensor[8];
   __shared__ const uint16_t* s_g[kMaxN];
   const int N = NT > 0 ? NT : sc.c[0].n_rep;
+  // single-set launches: the host-folded scalars, or the device step's row
+  // (a device step is not combined with groups, so NG > 1 launches skip this)
+  Scalars one = sc.c[0];
+  if constexpr (NG == 1) {
+    if (!step_scalars(ref, one)) return;
+  }
   for (int32_t ci = blockIdx.x; ci < n_chunks; ci += gridDim.x) {
     const ListChunk ch = chunks[ci];
     const int32_t t = ch.tensor;
@@ -219,7 +225,7 @@ __global__ __launch_bounds__(kBlock) void list_kernel(const ListChunk* __restric
     s.scalar_only = (int32_t)uniform_i64(s_tensor[7] & 0xFFFFFFFF);
     int32_t grp = 0;
     if constexpr (NG > 1) grp = (int32_t)uniform_i64(s_tensor[7] >> 32);  // the tensor's group, < NG
-    const Scalars& c = sc.c[grp];
+    const Scalars& c = NG == 1 ? one : sc.c[grp];
     auto G = [&](int r) { return uniform_ptr(s_g[r]); };
     if (!s.scalar_only) {
       tiles<NT>(G, N, ch.begin, ch.end, 0, 1, s, c);
@@ -253,17 +259,18 @@ hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scala
 
 template <int NT>
 hipError_t go_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
-                   const uint16_t* const* gptrs, const Scalars* cs, int n_sets, int blocks, hipStream_t stream) {
+                   const uint16_t* const* gptrs, const Scalars* cs, int n_sets, const StepRef& ref, int blocks,
+                   hipStream_t stream) {
   const int grid = blocks < n_chunks ? blocks : n_chunks;
   (void)hipGetLastError();
   if (n_sets <= 1) {
     ListScalars<1> sc;
     sc.c[0] = cs[0];
-    list_kernel<NT, 1><<<dim3(grid), dim3(kBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc);
+    list_kernel<NT, 1><<<dim3(grid), dim3(kBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc, ref);
   } else {
     ListScalars<kMaxGroups> sc;
     for (int k = 0; k < kMaxGroups; ++k) sc.c[k] = cs[k < n_sets ? k : 0];
-    list_kernel<NT, kMaxGroups><<<dim3(grid), dim3(kBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc);
+    list_kernel<NT, kMaxGroups><<<dim3(grid), dim3(kBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc, ref);
   }
   return hipGetLastError();
 }
@@ -291,17 +298,17 @@ hipError_t launch_step_advance(int64_t* step, hipStream_t stream) {
 }
 
 hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
-                       const uint16_t* const* gptrs, const Scalars* cs, int n_sets, int blocks,
+                       const uint16_t* const* gptrs, const Scalars* cs, int n_sets, const StepRef& ref, int blocks,
                        hipStream_t stream) {
   switch (cs[0].n_rep) {
-    case 1: return go_list<1>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
-    case 2: return go_list<2>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
-    case 4: return go_list<4>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
-    case 8: return go_list<8>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
-    case 16: return go_list<16>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
-    case 32: return go_list<32>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
-    case 64: return go_list<64>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
-    default: return go_list<0>(chunks, n_chunks, tensors, gptrs, cs, n_sets, blocks, stream);
+    case 1: return go_list<1>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
+    case 2: return go_list<2>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
+    case 4: return go_list<4>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
+    case 8: return go_list<8>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
+    case 16: return go_list<16>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
+    case 32: return go_list<32>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
+    case 64: return go_list<64>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
+    default: return go_list<0>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
   }
 }
 

@@ -231,3 +231,42 @@ def test_fp16_graph_replays_with_device_step_and_scaler(orc):
             assert np.array_equal(got[k].view(np.uint32), r.view(np.uint32)), (t, k)
         assert np.array_equal(B.view(torch.int16).cpu().numpy().view(np.uint16), Br), t
     assert src.step == 7
+
+
+def test_list_plan_graph_replays_advance_the_step(orc):
+    """A ragged list plan's step with the device step, [step, advance] captured
+    once and replayed four times, against the oracle per tensor at t = 1..4."""
+    import torch
+
+    import sharded_mixed_precision_rank_amd as zs
+    from tests.test_gpu_list import arena_case, oracle_list, small_ragged
+
+    dev = torch.device("cuda:0")
+    env = dict(torch=torch, zs=zs, dev=dev)
+    w = small_ragged(8, 80, seed=55)
+    host, d, offsets, L = arena_case(env, w)
+    src = zs.StepSource(HP, 1, 10, dev)
+    with zs.ListPlan.from_arenas(w.sizes, offsets, d["G"], d["P"], d["M"], d["V"], d["B"]) as plan:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm-up outside capture: an out-of-range step updates nothing
+            w_src = zs.StepSource(HP, 1, 10, dev, start=11)
+            plan.step_devstep(w_src)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert w_src.status == 1
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            plan.step_devstep(src)
+            src.advance()
+        state = dict(G=host["G"], P=host["P"], M=host["M"], V=host["V"])
+        for t in range(1, 5):
+            graph.replay()
+            torch.cuda.synchronize()
+            ref = oracle_list(orc, w, state, offsets, t, HP)
+            state = dict(G=host["G"], P=ref["P"], M=ref["M"], V=ref["V"])
+            got = dict(P=d["P"].cpu().numpy(), M=d["M"].cpu().numpy(), V=d["V"].cpu().numpy(),
+                       B=d["B"].cpu().numpy().view(np.uint16))
+            for k in "PMV":
+                assert np.array_equal(got[k].view(np.uint32), ref[k].view(np.uint32)), (t, k)
+            assert np.array_equal(got["B"], ref["B"]), t
