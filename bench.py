@@ -314,21 +314,44 @@ def main() -> int:
     for k in range(args.warmup):
         step(w.step + k)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    # one event between consecutive steps: the K-step total gives the mean, the gaps the median and minimum
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record()
     for k in range(args.steps):
         step(w.step + args.warmup + k)
-    e1.record()
+        ev[k + 1].record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps))
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else \
+        0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
+    ms_min = per_step[0]
+    cold_ms = None
+    footprint = sum(t.numel() * t.element_size() for t in (*d["G"], d["P"], d["M"], d["V"], d["B"]) if t.is_cuda)
+    if offload is None and footprint < (1 << 30):
+        # the workload fits in the 256 MB Infinity Cache: also time each step after a 1 GB scratch write
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cold = []
+        for k in range(10):
+            scratch.fill_(k)
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            step(w.step + args.warmup + args.steps + k)
+            c1.record()
+            torch.cuda.synchronize()
+            cold.append(c0.elapsed_time(c1))
+        del scratch
+        cold_ms = sorted(cold)[len(cold) // 2]
+        log(f"cold (after a 1 GB scratch write): {cold_ms:.4f} ms/step, median of 10")
     n = w.n_params
     bpp = 2 * w.N + (34 if two_pass else 26)   # offload: the same algorithmic bytes as the fused step
     bytes_per_launch = bpp * n
     achieved = bytes_per_launch / (ms / 1e3) / 1e9
-    log(f"{ms:.3f} ms/step, {n / (ms / 1e3) / 1e9:.2f} G params/s, {achieved:.0f} GB/s")
+    log(f"{ms:.3f} ms/step, {n / (ms / 1e3) / 1e9:.2f} G params/s, {achieved:.0f} GB/s "
+        f"(per step: median {ms_median:.3f} ms, min {ms_min:.3f} ms)")
 
     pattern = None
-    if args.path == "fused" and not w.is_list and not args.no_copy:
+    if args.path == "fused" and not w.is_list and not args.no_copy and footprint >= (1 << 30):
         pattern = pattern_ceiling(w, d)
         if pattern:
             pattern["kernel_frac_of_read_write"] = achieved / pattern["read_write_GBps"]
@@ -352,7 +375,8 @@ def main() -> int:
 
     rec = {
         "metric": METRIC, "value": n / (ms / 1e3), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_median": ms_median, "ms_per_step_min": ms_min,
+        "cold_ms_per_step": cold_ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "n_params": n, "replicas": w.N, "adam_step": w.step,
                    "weight_decay": w.weight_decay, "path": args.path,
