@@ -171,62 +171,6 @@ def fold(hp, step: int) -> dict:
     return {k: getattr(out, k) for k, _ in FoldedStruct._fields_}
 
 
-def fold_table(hp, t0: int, count: int):
-    """The folded scalars of steps t0 .. t0+count-1: a (count, 8) float32 array, rows as :func:`fold`."""
-    import numpy as np
-
-    out = np.empty((count, 8), dtype=np.float32)
-    h = _hp(hp)
-    _check(_lib.zs_fold_table(ctypes.byref(h), t0, count, out.ctypes.data), "zs_fold_table")
-    return out
-
-
-class StepSource:
-    """A device-resident step index with the folded scalars of steps
-    t0 .. t0+count-1, for steps captured in a HIP graph: the *_devstep calls
-    read the current step on the device and :meth:`advance` increments it
-    there, so each replay takes the next step."""
-
-    def __init__(self, hp, t0: int, count: int, device="cuda", start: int = None):
-        import torch
-
-        self.table = torch.from_numpy(fold_table(hp, t0, count)).to(device)
-        self.step_t = torch.tensor([t0 if start is None else start], dtype=torch.int64, device=device)
-        self.status_t = torch.zeros(1, dtype=torch.int32, device=device)
-        self.device = self.table.device
-        self._s = StepSourceStruct(self.table.data_ptr(), t0, count, self.step_t.data_ptr(),
-                                   self.status_t.data_ptr())
-
-    def advance(self, stream=None) -> None:
-        import torch
-
-        with torch.cuda.device(self.device):
-            _check(_lib.zs_step_advance(self.step_t.data_ptr(), _stream_handle(stream, self.device)),
-                   "zs_step_advance")
-
-    @property
-    def step(self) -> int:
-        return int(self.step_t.item())
-
-    @property
-    def status(self) -> int:
-        return int(self.status_t.item())
-
-
-def reduce_adam_flat_devstep(grads: Sequence, master, m, v, param, src: StepSource, stream=None) -> None:
-    """:func:`reduce_adam_flat` with the step (and its folded scalars) read from ``src`` on the device."""
-    import torch
-
-    N = len(grads)
-    n = _tensor_args(grads, master, m, v, param)
-    dev = _one_device(master, m, v, param, src.table, *grads)
-    tab = (_vp * max(N, 1))(*[g.data_ptr() for g in grads])
-    with torch.cuda.device(dev):
-        _check(_lib.zs_reduce_adam_flat_devstep(tab, N, n, master.data_ptr(), m.data_ptr(), v.data_ptr(),
-                                                param.data_ptr(), ctypes.byref(src._s), _stream_handle(stream, dev)),
-               "zs_reduce_adam_flat_devstep")
-
-
 def set_grid_blocks(blocks: int) -> None:
     _check(_lib.zs_set_grid_blocks(blocks), "zs_set_grid_blocks")
 
@@ -328,6 +272,63 @@ def reduce_adam_flat_ptrs(grad_ptrs: Sequence[int], n: int, master: int, m: int,
     h = _hp(hp)
     _check(_lib.zs_reduce_adam_flat(tab, N, n, master, m, v, param, ctypes.byref(h), step, _stream_handle(stream)),
            "zs_reduce_adam_flat")
+
+
+# ------------------------------------------------------------ device-resident step index
+def fold_table(hp, t0: int, count: int):
+    """The folded scalars of steps t0 .. t0+count-1: a (count, 8) float32 array, rows as :func:`fold`."""
+    import numpy as np
+
+    out = np.empty((count, 8), dtype=np.float32)
+    h = _hp(hp)
+    _check(_lib.zs_fold_table(ctypes.byref(h), t0, count, out.ctypes.data), "zs_fold_table")
+    return out
+
+
+class StepSource:
+    """A device-resident step index with the folded scalars of steps
+    t0 .. t0+count-1, for steps captured in a HIP graph: the *_devstep calls
+    read the current step on the device and :meth:`advance` increments it
+    there, so each replay takes the next step."""
+
+    def __init__(self, hp, t0: int, count: int, device="cuda", start: int = None):
+        import torch
+
+        self.table = torch.from_numpy(fold_table(hp, t0, count)).to(device)
+        self.step_t = torch.tensor([t0 if start is None else start], dtype=torch.int64, device=device)
+        self.status_t = torch.zeros(1, dtype=torch.int32, device=device)
+        self.device = self.table.device
+        self._s = StepSourceStruct(self.table.data_ptr(), t0, count, self.step_t.data_ptr(),
+                                   self.status_t.data_ptr())
+
+    def advance(self, stream=None) -> None:
+        import torch
+
+        with torch.cuda.device(self.device):
+            _check(_lib.zs_step_advance(self.step_t.data_ptr(), _stream_handle(stream, self.device)),
+                   "zs_step_advance")
+
+    @property
+    def step(self) -> int:
+        return int(self.step_t.item())
+
+    @property
+    def status(self) -> int:
+        return int(self.status_t.item())
+
+
+def reduce_adam_flat_devstep(grads: Sequence, master, m, v, param, src: StepSource, stream=None) -> None:
+    """:func:`reduce_adam_flat` with the step (and its folded scalars) read from ``src`` on the device."""
+    import torch
+
+    N = len(grads)
+    n = _tensor_args(grads, master, m, v, param)
+    dev = _one_device(master, m, v, param, src.table, *grads)
+    tab = (_vp * max(N, 1))(*[g.data_ptr() for g in grads])
+    with torch.cuda.device(dev):
+        _check(_lib.zs_reduce_adam_flat_devstep(tab, N, n, master.data_ptr(), m.data_ptr(), v.data_ptr(),
+                                                param.data_ptr(), ctypes.byref(src._s), _stream_handle(stream, dev)),
+               "zs_reduce_adam_flat_devstep")
 
 
 @dataclass
