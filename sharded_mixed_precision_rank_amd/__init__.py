@@ -9,7 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
-from typing import Sequence
+from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzshard.so")
@@ -21,7 +21,8 @@ if not os.path.exists(LIB_PATH):
 # PyTorch-ROCm ships its own HIP runtime (same soname).  Load it first so the
 # library binds to the runtime that owns torch's devices, streams and memory;
 # loading the library first would bring in a second runtime.
-import torch  # noqa: E402,F401
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -50,6 +51,8 @@ _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 class StepSourceStruct(ctypes.Structure):
     _fields_ = [("table", ctypes.c_void_p), ("t0", ctypes.c_int64), ("count", ctypes.c_int64),
                 ("step", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+
+
 _lib.zs_abi_version.restype = ctypes.c_int
 _lib.zs_status_string.restype = ctypes.c_char_p
 _lib.zs_status_string.argtypes = [ctypes.c_int]
@@ -178,8 +181,6 @@ def set_grid_blocks(blocks: int) -> None:
 def _stream_handle(stream, device=None):
     """The raw stream handle: torch's current stream of ``device`` by default."""
     if stream is None:
-        import torch
-
         return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, int):
         return stream
@@ -192,8 +193,6 @@ def _one_device(*tensors):
     """The device every tensor lives on (the current device if there are none).
     The library launches on the current device, so each call runs with this
     device made current; tensors spread over devices are rejected."""
-    import torch
-
     devs = {t.device for t in tensors}
     if len(devs) > 1:
         raise ValueError(f"tensors live on several devices: {sorted(str(d) for d in devs)}")
@@ -201,8 +200,6 @@ def _one_device(*tensors):
 
 
 def _dev_check(t, dtypes, name):
-    import torch
-
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype not in dtypes:
@@ -213,35 +210,23 @@ def _dev_check(t, dtypes, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _bf16_types():
-    import torch
-
-    return (torch.bfloat16, torch.int16, torch.uint16)
-
-
-def _half_types():
-    import torch
-
-    return (torch.bfloat16, torch.float16, torch.int16, torch.uint16)
-
-
-def _f32_types():
-    import torch
-
-    return (torch.float32,)
+# Accepted dtypes: 16-bit arrays are passed as raw bits, so integer views of them are accepted too.
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_HALF = (torch.bfloat16, torch.float16, torch.int16, torch.uint16)
+_F32 = (torch.float32,)
 
 
 def _tensor_args(grads, master, m, v, param):
     n = master.numel()
-    _dev_check(master, _f32_types(), "master")
-    _dev_check(m, _f32_types(), "m")
-    _dev_check(v, _f32_types(), "v")
-    _dev_check(param, _bf16_types(), "param")
+    _dev_check(master, _F32, "master")
+    _dev_check(m, _F32, "m")
+    _dev_check(v, _F32, "v")
+    _dev_check(param, _BF16, "param")
     for name, t in (("m", m), ("v", v), ("param", param)):
         if t.numel() != n:
             raise ValueError(f"{name} has {t.numel()} elements, master has {n}")
     for r, g in enumerate(grads):
-        _dev_check(g, _bf16_types(), f"grads[{r}]")
+        _dev_check(g, _BF16, f"grads[{r}]")
         if g.numel() != n:
             raise ValueError(f"grads[{r}] has {g.numel()} elements, master has {n}")
     return n
@@ -251,8 +236,6 @@ def reduce_adam_flat(grads: Sequence, master, m, v, param, hp, step: int, stream
     """One shard step: average ``grads`` (N bf16 device tensors, rank order) and
     apply AdamW to ``master``/``m``/``v`` in place, writing the bf16 copy to
     ``param``.  Enqueued on ``stream`` (default: torch's current stream)."""
-    import torch
-
     N = len(grads)
     n = _tensor_args(grads, master, m, v, param)
     dev = _one_device(master, m, v, param, *grads)
@@ -277,8 +260,6 @@ def reduce_adam_flat_ptrs(grad_ptrs: Sequence[int], n: int, master: int, m: int,
 # ------------------------------------------------------------ device-resident step index
 def fold_table(hp, t0: int, count: int):
     """The folded scalars of steps t0 .. t0+count-1: a (count, 8) float32 array, rows as :func:`fold`."""
-    import numpy as np
-
     out = np.empty((count, 8), dtype=np.float32)
     h = _hp(hp)
     _check(_lib.zs_fold_table(ctypes.byref(h), t0, count, out.ctypes.data), "zs_fold_table")
@@ -291,9 +272,7 @@ class StepSource:
     read the current step on the device and :meth:`advance` increments it
     there, so each replay takes the next step."""
 
-    def __init__(self, hp, t0: int, count: int, device="cuda", start: int = None):
-        import torch
-
+    def __init__(self, hp, t0: int, count: int, device="cuda", start: Optional[int] = None):
         self.table = torch.from_numpy(fold_table(hp, t0, count)).to(device)
         self.step_t = torch.tensor([t0 if start is None else start], dtype=torch.int64, device=device)
         self.status_t = torch.zeros(1, dtype=torch.int32, device=device)
@@ -302,8 +281,6 @@ class StepSource:
                                    self.status_t.data_ptr())
 
     def advance(self, stream=None) -> None:
-        import torch
-
         with torch.cuda.device(self.device):
             _check(_lib.zs_step_advance(self.step_t.data_ptr(), _stream_handle(stream, self.device)),
                    "zs_step_advance")
@@ -319,8 +296,6 @@ class StepSource:
 
 def reduce_adam_flat_devstep(grads: Sequence, master, m, v, param, src: StepSource, stream=None) -> None:
     """:func:`reduce_adam_flat` with the step (and its folded scalars) read from ``src`` on the device."""
-    import torch
-
     N = len(grads)
     n = _tensor_args(grads, master, m, v, param)
     dev = _one_device(master, m, v, param, src.table, *grads)
@@ -361,8 +336,6 @@ class ListPlan:
     :meth:`step` is one kernel launch covering every tensor."""
 
     def __init__(self, tensors: Sequence[ShardTensor], N: int, stream=None):
-        import torch
-
         tab, keep = _tensor_table(tensors, N)
         dev = _one_device(*[t.master for t in tensors])
         h = _vp()
@@ -379,10 +352,6 @@ class ListPlan:
         """Plan over tensors laid out in per-array arenas: tensor t is elements
         [offsets[t], offsets[t] + sizes[t]) of ``master``, ``m``, ``v``, ``param``
         and of every replica's gradient arena in ``grads``."""
-        import numpy as np
-
-        import torch
-
         N = len(grads)
         L = master.numel()
         _tensor_args(grads, master, m, v, param)
@@ -417,8 +386,6 @@ class ListPlan:
     def step(self, hp, step: int, stream=None) -> None:
         if not self._h:
             raise ValueError("plan is closed")
-        import torch
-
         h = _hp(hp)
         with torch.cuda.device(self._dev):
             _check(_lib.zs_reduce_adam_list_plan(self._h, ctypes.byref(h), step, _stream_handle(stream, self._dev)),
@@ -426,8 +393,6 @@ class ListPlan:
 
     def set_groups(self, groups: Sequence[int], n_groups: int, stream=None) -> None:
         """Assign tensor t to hyperparameter group groups[t] (0 <= groups[t] < n_groups <= 8)."""
-        import torch
-
         if not self._h:
             raise ValueError("plan is closed")
         arr = (_i32 * max(len(groups), 1))(*groups)
@@ -437,8 +402,6 @@ class ListPlan:
 
     def step_devstep(self, src: "StepSource", stream=None) -> None:
         """The step with the step index read from ``src`` on the device."""
-        import torch
-
         if not self._h:
             raise ValueError("plan is closed")
         if src.device != self._dev:
@@ -450,8 +413,6 @@ class ListPlan:
 
     def step_groups(self, hps: Sequence, step: int, stream=None) -> None:
         """The step with hps[g] for the tensors of group g."""
-        import torch
-
         if not self._h:
             raise ValueError("plan is closed")
         arr = (AdamHPStruct * max(len(hps), 1))(*[_hp(h) for h in hps])
@@ -487,8 +448,6 @@ class ListPlan:
 
 def reduce_adam_list(tensors: Sequence[ShardTensor], N: int, hp, step: int, stream=None) -> None:
     """One-shot list step (builds a plan, runs it, waits, frees it)."""
-    import torch
-
     tab, keep = _tensor_table(tensors, N)
     dev = _one_device(*[t.master for t in tensors])
     h = _hp(hp)
@@ -508,20 +467,38 @@ def _fmt(name) -> int:
     return FORMATS[name]
 
 
+_WORKSPACE_TYPES = (torch.uint8, torch.int8, torch.float32, torch.float64)
+
+
+def _pass1_args(grads, workspace, sqnorm) -> int:
+    n = grads[0].numel() if grads else 0
+    for r, g in enumerate(grads):
+        _dev_check(g, _HALF, f"grads[{r}]")
+        if g.numel() != n:
+            raise ValueError(f"grads[{r}] has {g.numel()} elements, grads[0] has {n}")
+    _dev_check(workspace, _WORKSPACE_TYPES, "workspace")
+    _dev_check(sqnorm, (torch.float64,), "sqnorm")
+    return n
+
+
+def _pass2_args(workspace, n, master, m, v, param, total_sq) -> None:
+    _dev_check(master, _F32, "master")
+    _dev_check(m, _F32, "m")
+    _dev_check(v, _F32, "v")
+    _dev_check(param, _HALF, "param")
+    _dev_check(total_sq, (torch.float64,), "total_sq")
+    _dev_check(workspace, _WORKSPACE_TYPES, "workspace")
+    for name, t in (("master", master), ("m", m), ("v", v), ("param", param)):
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+
+
 def reduce_grads_flat(grads: Sequence, workspace, sqnorm, loss_scale: float = 1.0, grad_format="bf16",
                       stream=None) -> None:
     """Pass 1: average (and unscale) the replicas into ``workspace`` and write the
     shard's squared gradient norm to ``sqnorm`` (a 1-element float64 device tensor)."""
-    import torch
-
     N = len(grads)
-    n = grads[0].numel() if N else 0
-    for r, g in enumerate(grads):
-        _dev_check(g, _half_types(), f"grads[{r}]")
-        if g.numel() != n:
-            raise ValueError(f"grads[{r}] has {g.numel()} elements, grads[0] has {n}")
-    _dev_check(workspace, (torch.uint8, torch.int8, torch.float32, torch.float64), "workspace")
-    _dev_check(sqnorm, (torch.float64,), "sqnorm")
+    n = _pass1_args(grads, workspace, sqnorm)
     dev = _one_device(workspace, sqnorm, *grads)
     tab = (_vp * max(N, 1))(*[g.data_ptr() for g in grads])
     with torch.cuda.device(dev):
@@ -535,17 +512,7 @@ def adam_from_grads_flat(workspace, n: int, master, m, v, param, hp, step: int, 
     """Pass 2: AdamW from the reduced gradient in ``workspace``, clipped to
     ``max_norm`` by the global squared norm ``total_sq`` (device float64), and
     skipped entirely when that norm is not finite."""
-    import torch
-
-    _dev_check(master, _f32_types(), "master")
-    _dev_check(m, _f32_types(), "m")
-    _dev_check(v, _f32_types(), "v")
-    _dev_check(param, _half_types(), "param")
-    _dev_check(total_sq, (torch.float64,), "total_sq")
-    _dev_check(workspace, (torch.uint8, torch.int8, torch.float32, torch.float64), "workspace")
-    for name, t in (("master", master), ("m", m), ("v", v), ("param", param)):
-        if t.numel() != n:
-            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    _pass2_args(workspace, n, master, m, v, param, total_sq)
     dev = _one_device(workspace, master, m, v, param, total_sq)
     h = _hp(hp)
     with torch.cuda.device(dev):
@@ -560,17 +527,7 @@ def adam_from_grads_flat_devstep(workspace, n: int, master, m, v, param, src: St
                                  max_norm: float = 0.0, param_format="bf16", skip_nonfinite: bool = True,
                                  stream=None) -> None:
     """:func:`adam_from_grads_flat` with the step read from ``src`` on the device."""
-    import torch
-
-    _dev_check(master, _f32_types(), "master")
-    _dev_check(m, _f32_types(), "m")
-    _dev_check(v, _f32_types(), "v")
-    _dev_check(param, _half_types(), "param")
-    _dev_check(total_sq, (torch.float64,), "total_sq")
-    _dev_check(workspace, (torch.uint8, torch.int8, torch.float32, torch.float64), "workspace")
-    for name, t in (("master", master), ("m", m), ("v", v), ("param", param)):
-        if t.numel() != n:
-            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    _pass2_args(workspace, n, master, m, v, param, total_sq)
     dev = _one_device(workspace, master, m, v, param, total_sq, src.table)
     with torch.cuda.device(dev):
         _check(_lib.zs_adam_from_grads_flat_devstep(workspace.data_ptr(),
@@ -587,8 +544,6 @@ def clipped_step_flat(grads: Sequence, master, m, v, param, hp, step: int, max_n
     """Both passes on one shard, the shard's own norm standing for the global
     one (one GPU).  Returns the device tensor holding the squared norm: a
     non-finite value means the step was skipped (an fp16 overflow)."""
-    import torch
-
     n = master.numel()
     if workspace is None:
         workspace = torch.empty(two_pass_workspace_bytes(n), dtype=torch.uint8, device=master.device)
@@ -632,8 +587,6 @@ class DeviceLossScaler:
     never waits on the host."""
 
     def __init__(self, host: LossScaler, device="cuda"):
-        import torch
-
         raw = bytes(memoryview(host._s))
         self.tensor = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(device)
         self.device = self.tensor.device
@@ -641,8 +594,6 @@ class DeviceLossScaler:
     def update(self, total_sq, taken=None, stream=None) -> None:
         """Record the step whose global squared norm is ``total_sq`` (device float64); ``taken``
         (optional device int32) receives 1 if the step was taken, 0 if it was skipped."""
-        import torch
-
         _dev_check(total_sq, (torch.float64,), "total_sq")
         tensors = [self.tensor, total_sq] + ([taken] if taken is not None else [])
         if taken is not None:
@@ -662,16 +613,8 @@ class DeviceLossScaler:
 def reduce_grads_flat_device_scale(grads: Sequence, workspace, sqnorm, scaler: DeviceLossScaler,
                                    grad_format="fp16", stream=None) -> None:
     """Pass 1 with the loss scale read on the device from ``scaler``."""
-    import torch
-
     N = len(grads)
-    n = grads[0].numel() if N else 0
-    for r, g in enumerate(grads):
-        _dev_check(g, _half_types(), f"grads[{r}]")
-        if g.numel() != n:
-            raise ValueError(f"grads[{r}] has {g.numel()} elements, grads[0] has {n}")
-    _dev_check(workspace, (torch.uint8, torch.int8, torch.float32, torch.float64), "workspace")
-    _dev_check(sqnorm, (torch.float64,), "sqnorm")
+    n = _pass1_args(grads, workspace, sqnorm)
     dev = _one_device(workspace, sqnorm, scaler.tensor, *grads)
     tab = (_vp * max(N, 1))(*[g.data_ptr() for g in grads])
     with torch.cuda.device(dev):
@@ -685,17 +628,12 @@ def reduce_grads_flat_device_scale(grads: Sequence, workspace, sqnorm, scaler: D
 # ------------------------------------------------------------ optimizer offload
 def _host_ptr(a, dtype_name: str):
     """Address of a contiguous host array (numpy array or CPU torch tensor)."""
-    import numpy as np
-
     if isinstance(a, np.ndarray):
         if not a.flags.c_contiguous or a.dtype.name != dtype_name:
             raise TypeError(f"expected a contiguous {dtype_name} numpy array")
         return a.ctypes.data, a.size
-    import torch
-
-    want = {"float32": torch.float32, "uint16": (torch.int16, torch.uint16, torch.bfloat16)}[dtype_name]
-    ok = a.dtype in want if isinstance(want, tuple) else a.dtype == want
-    if not isinstance(a, torch.Tensor) or a.is_cuda or not a.is_contiguous() or not ok:
+    want = {"float32": (torch.float32,), "uint16": (torch.int16, torch.uint16, torch.bfloat16)}[dtype_name]
+    if not isinstance(a, torch.Tensor) or a.is_cuda or not a.is_contiguous() or a.dtype not in want:
         raise TypeError(f"expected a contiguous host {dtype_name} array")
     return a.data_ptr(), a.numel()
 
@@ -722,20 +660,18 @@ class Offload:
         self._h = h
 
     def step(self, grads: Sequence, master, m, v, param, hp, step: int, stream=None) -> None:
+        if not self._h:
+            raise ValueError("offload context is closed")
         N = len(grads)
         n = param.numel()
-        _dev_check(param, _bf16_types(), "param")
+        _dev_check(param, _BF16, "param")
         for r, g in enumerate(grads):
-            _dev_check(g, _bf16_types(), f"grads[{r}]")
+            _dev_check(g, _BF16, f"grads[{r}]")
             if g.numel() != n:
                 raise ValueError(f"grads[{r}] has {g.numel()} elements, param has {n}")
         ptrs = [_host_ptr(x, "float32") for x in (master, m, v)]
         if any(k != n for _, k in ptrs):
             raise ValueError("host master/m/v must have the parameter count")
-        import torch
-
-        if not self._h:
-            raise ValueError("offload context is closed")
         dev = _one_device(param, *grads)
         tab = (_vp * max(N, 1))(*[g.data_ptr() for g in grads])
         h = _hp(hp)
