@@ -93,7 +93,7 @@ def pattern_ceiling(w, d, reps: int = 5):
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_int32, ctypes.c_void_p]
     N, n = w.N, d["arena_len"]
-    full = n // 2048 * 2048
+    full = n // 512 * 512   # the probe covers whole 512-parameter tiles
     tab = (ctypes.c_void_p * N)(*[g.data_ptr() for g in d["G"]])
     stream = torch.cuda.current_stream()
     out = {}

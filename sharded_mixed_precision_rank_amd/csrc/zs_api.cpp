@@ -164,19 +164,12 @@ zs::FlatShape shape_of(const uint16_t* const* g, int32_t N, int64_t n, float* p,
   return s;
 }
 
+// Workgroups per launch: one per tile (measured best; each launch clamps this
+// to its tile count, and the tile loops cover shards of more than 2^30 tiles),
+// unless zs_set_grid_blocks fixed a count.
 int auto_blocks() {
   const int32_t forced = g_grid_blocks.load(std::memory_order_relaxed);
-  if (forced > 0) return forced;
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!cached[dev]) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    cached[dev] = 1 << 30;  // one tile per workgroup: measured best; the loop covers any remainder
-  }
-  return cached[dev];
+  return forced > 0 ? forced : 1 << 30;
 }
 
 zs_status after_launch(hipError_t e, hipStream_t stream, const char* what) {

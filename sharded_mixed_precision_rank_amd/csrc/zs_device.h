@@ -159,7 +159,7 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], const u32x4 w) {
   acc[7] = acc[7] + h_hi<FMT>(w.w);
 }
 
-// Lane layouts of an 8-parameter group inside a tile of kBlock groups.
+// Lane layouts of an 8-parameter group inside a tile (one group per thread).
 //  Split (full tiles): lane l of wave q owns the quads at tile elements
 //    512q + 4l and 512q + 256 + 4l.  Every access instruction of a wave then
 //    covers whole contiguous lines: 1 KiB per fp32 access, 512 B per bf16

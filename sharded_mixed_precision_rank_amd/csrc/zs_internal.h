@@ -94,11 +94,21 @@ hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTens
                        const uint16_t* const* gptrs, const Scalars* cs, int n_sets, const StepRef& ref, int blocks,
                        hipStream_t stream);
 
+// Threads per workgroup of the fused step's kernels; each thread owns one
+// 8-parameter group, so a tile is 8x this many parameters.
+//  Flat shards: one wave, a 512-parameter tile dispatched and retired on its
+//  own.  Measured on the same buffers against 256-thread workgroups: 1-4%
+//  faster (70B/64 shard +1.2%, 124M-parameter N=8 shard +4.4%).
+//  List plans: four waves.  A list workgroup first loads its chunk's
+//  descriptor and replica pointers (dependent loads); one-wave workgroups
+//  measured 1-3% slower there at every chunk size from 1024 to 4096.
+constexpr int kFlatBlock = 64;
+constexpr int kListBlock = 256;
 // Elements per list chunk (vector tensors: groups of 8 per chunk = this / 8):
-// two tiles, so each workgroup streams for about as long as a flat-kernel
-// workgroup; longer chunks (more tiles per workgroup) measured 3-6% slower,
-// because a workgroup's next loads wait behind its previous stores.
+// two list tiles.
 constexpr int64_t kChunkElems = 4096;
+// Threads per workgroup of the two-pass kernels (four waves; their norm
+// partials are reduced across the waves through LDS).
 constexpr int kBlock = 256;
 // Hyperparameter groups a list plan can carry (their scalars travel as kernel arguments).
 constexpr int kMaxGroups = ZS_MAX_GROUPS;

@@ -21,6 +21,10 @@
 //    stream so their latency overlaps it.
 //  * Every access is marked non-temporal: nothing is re-read, so nothing
 //    should displace useful lines in L2 or the Infinity Cache.
+//  * A flat shard runs one wave per workgroup, one 512-parameter tile each;
+//    a list plan runs four waves per workgroup over 4096-parameter chunks
+//    (two 2048-parameter tiles).  The measurements behind both choices are
+//    noted at kFlatBlock and kListBlock.
 //  * Tiles start where every array sits on a 128-byte line boundary when the
 //    arrays allow it (else 64, 32 or 16 bytes), so each wave access covers
 //    whole lines and no line is written in two halves by two tiles.
@@ -92,18 +96,18 @@ __device__ __forceinline__ void group_step(GP G, int N, int64_t e0, const FlatSh
 }
 
 // Groups [g_begin, g_end) of a vector-path shard, one workgroup-wide tile of
-// kBlock groups at a time starting at tile index `tile0` and stepping by
+// BLOCK groups at a time starting at tile index `tile0` and stepping by
 // `tstep` tiles.  G0(r) returns replica r's unadvanced base pointer.  Whole
 // tiles use the split layout; the last, partial tile the contiguous one.
-template <int NT, class GP0>
+template <int NT, int BLOCK, class GP0>
 __device__ __forceinline__ void tiles(GP0 G0, int N, int64_t g_begin, int64_t g_end, int64_t tile0, int64_t tstep,
                                       const FlatShape& s, const Scalars& c) {
   for (int64_t t = tile0;; t += tstep) {
-    const int64_t gt = g_begin + t * kBlock;  // first group of the tile
+    const int64_t gt = g_begin + t * BLOCK;  // first group of the tile
     if (gt >= g_end) break;
     const int64_t e0 = s.head + 8 * gt;
     auto G = [&](int r) { return tile_base(G0(r) + e0); };
-    if (gt + kBlock <= g_end)
+    if (gt + BLOCK <= g_end)
       group_step<NT, true>(G, N, e0, s, c);
     else if (gt + threadIdx.x < g_end)
       group_step<NT, false>(G, N, e0, s, c);
@@ -123,14 +127,13 @@ __device__ __forceinline__ void elem_step(GP G, int N, int64_t i, const FlatShap
   s.b[i] = to_bf16(p);
 }
 
-// Head and tail elements of a vector-path shard: thread t < head + tail.
-template <class GP>
-__device__ __forceinline__ void edge_step(GP G, int N, int t, const FlatShape& s, const Scalars& c) {
+// Head and tail elements of a vector-path shard (at most 63 + 7), spread
+// over the workgroup's BLOCK threads.
+template <int BLOCK, class GP>
+__device__ __forceinline__ void edge_step(GP G, int N, const FlatShape& s, const Scalars& c) {
   const int64_t tail = s.n - s.head - 8 * s.nvec;
-  if (t < s.head)
-    elem_step(G, N, t, s, c);
-  else if (t < s.head + tail)
-    elem_step(G, N, s.head + 8 * s.nvec + (t - s.head), s, c);
+  for (int64_t t = threadIdx.x; t < s.head + tail; t += BLOCK)
+    elem_step(G, N, t < s.head ? t : s.head + 8 * s.nvec + (t - s.head), s, c);
 }
 
 template <int NT>
@@ -142,19 +145,20 @@ struct FlatArgs {
 };
 
 template <int NT>
-__global__ __launch_bounds__(kBlock) void flat_kernel(const FlatArgs<NT> a) {
+__global__ __launch_bounds__(kFlatBlock) void flat_kernel(const FlatArgs<NT> a) {
   Scalars c = a.c;
   if (!step_scalars(a.r, c)) return;
   const int N = NT > 0 ? NT : c.n_rep;
   if (!a.s.scalar_only) {
     auto G0 = [&](int r) { return a.g[r]; };
-    tiles<NT>(G0, N, 0, a.s.nvec, blockIdx.x, gridDim.x, a.s, c);
+    tiles<NT, kFlatBlock>(G0, N, 0, a.s.nvec, blockIdx.x, gridDim.x, a.s, c);
     auto G = [&](int r) { return a.g[r]; };
-    if (blockIdx.x == gridDim.x - 1) edge_step(G, N, threadIdx.x, a.s, c);
+    if (blockIdx.x == gridDim.x - 1) edge_step<kFlatBlock>(G, N, a.s, c);
   } else {
     auto G = [&](int r) { return a.g[r]; };
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < a.s.n; i += stride) elem_step(G, N, i, a.s, c);
+    const int64_t stride = (int64_t)gridDim.x * kFlatBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kFlatBlock + threadIdx.x; i < a.s.n; i += stride)
+      elem_step(G, N, i, a.s, c);
   }
 }
 
@@ -194,7 +198,7 @@ struct ListScalars {
 };
 
 template <int NT, int NG>
-__global__ __launch_bounds__(kBlock) void list_kernel(const ListChunk* __restrict__ chunks, int32_t n_chunks,
+__global__ __launch_bounds__(kListBlock) void list_kernel(const ListChunk* __restrict__ chunks, int32_t n_chunks,
                                                       const ListTensor* __restrict__ tensors,
                                                       const uint16_t* const* __restrict__ gptrs,
                                                       const ListScalars<NG> sc, const StepRef ref) {
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(kBlock) void list_kernel(const ListChunk* __restric
     const ListChunk ch = chunks[ci];
     const int32_t t = ch.tensor;
     if (threadIdx.x < 8) s_tensor[threadIdx.x] = reinterpret_cast<const int64_t*>(tensors + t)[threadIdx.x];
-    for (int r = threadIdx.x; r < N; r += kBlock) s_g[r] = gptrs[(int64_t)t * N + r];
+    for (int r = threadIdx.x; r < N; r += kListBlock) s_g[r] = gptrs[(int64_t)t * N + r];
     __syncthreads();
     FlatShape s;
     s.p = uniform_fptr(reinterpret_cast<float*>(s_tensor[0]));
@@ -228,17 +232,18 @@ __global__ __launch_bounds__(kBlock) void list_kernel(const ListChunk* __restric
     const Scalars& c = NG == 1 ? one : sc.c[grp];
     auto G = [&](int r) { return uniform_ptr(s_g[r]); };
     if (!s.scalar_only) {
-      tiles<NT>(G, N, ch.begin, ch.end, 0, 1, s, c);
-      if (ch.first) edge_step(G, N, threadIdx.x, s, c);
+      tiles<NT, kListBlock>(G, N, ch.begin, ch.end, 0, 1, s, c);
+      if (ch.first) edge_step<kListBlock>(G, N, s, c);
     } else {
-      for (int64_t i = ch.begin + threadIdx.x; i < ch.end; i += kBlock) elem_step(G, N, i, s, c);
+      for (int64_t i = ch.begin + threadIdx.x; i < ch.end; i += kListBlock) elem_step(G, N, i, s, c);
     }
     __syncthreads();  // the next chunk overwrites the staged descriptor
   }
 }
 
+// Flat-kernel grid: `blocks`, but no more workgroups than tiles.
 int clamp_grid(int blocks, int64_t work) {
-  int64_t need = (work + kBlock - 1) / kBlock;
+  int64_t need = (work + kFlatBlock - 1) / kFlatBlock;
   if (need < 1) need = 1;
   return (int)(blocks < need ? blocks : need);
 }
@@ -253,7 +258,7 @@ hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scala
   a.r = ref;
   const int grid = clamp_grid(blocks, s.scalar_only ? s.n : s.nvec);
   (void)hipGetLastError();
-  flat_kernel<NT><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
+  flat_kernel<NT><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -266,11 +271,11 @@ hipError_t go_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* 
   if (n_sets <= 1) {
     ListScalars<1> sc;
     sc.c[0] = cs[0];
-    list_kernel<NT, 1><<<dim3(grid), dim3(kBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc, ref);
+    list_kernel<NT, 1><<<dim3(grid), dim3(kListBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc, ref);
   } else {
     ListScalars<kMaxGroups> sc;
     for (int k = 0; k < kMaxGroups; ++k) sc.c[k] = cs[k < n_sets ? k : 0];
-    list_kernel<NT, kMaxGroups><<<dim3(grid), dim3(kBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc, ref);
+    list_kernel<NT, kMaxGroups><<<dim3(grid), dim3(kListBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc, ref);
   }
   return hipGetLastError();
 }

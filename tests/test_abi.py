@@ -289,7 +289,7 @@ def test_probe_library_rejects_unsupported_arguments_without_gpu():
     g = (ctypes.c_void_p * 3)(A + 0x100000, A + 0x200000, A + 0x300000)
     arr = [A + 0x400000, A + 0x500000, A + 0x600000, A + 0x700000]
     assert f(g, 3, 1 << 20, *arr, 0, None) == 1            # N = 3 is not covered
-    assert f(g, 2, 1000, *arr, 0, None) == 1               # less than one tile
+    assert f(g, 2, 500, *arr, 0, None) == 1                # less than one 512-parameter tile
     assert f(g, 2, 1 << 20, A + 0x400004, *arr[1:], 0, None) == 1   # not on a 128-byte boundary
 
 

@@ -73,7 +73,7 @@ def test_replica_counts(env, orc, N):
     run_and_compare(env, orc, host, dict(HP, weight_decay=0.1), 37, f"N={N}")
 
 
-@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 15, 16, 17, 255, 2047, 2048, 2049, 4095, 100_003])
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 15, 16, 17, 255, 511, 512, 513, 2047, 2048, 2049, 4095, 100_003])
 def test_lengths(env, orc, n):
     rng = np.random.default_rng(2000 + n)
     host = rand_host(rng, 8, n)
@@ -90,13 +90,14 @@ def test_lengths(env, orc, n):
 @pytest.mark.parametrize("shift,n", [(1, 10_000), (2, 10_000), (3, 10_000), (5, 10_000), (7, 10_000),
                                      (8, 10_000), (24, 10_000), (32, 10_000), (40, 10_000), (56, 10_000),
                                      (63, 10_000), (72, 10_000), (8, 9), (8, 63), (8, 64), (8, 70), (8, 71),
-                                     (40, 33), (1, 70)])
+                                     (40, 33), (1, 70), (1, 10_007), (1, 1_000_007)])
 def test_common_misalignment_peels_a_head(env, orc, shift, n):
     """Every array starts `shift` elements past a 256-byte boundary: the kernel
     peels a head up to the next common line boundary (up to 63 elements; a
     16-byte one when no line boundary is common) and runs the vector path on
     the rest; shards too short for one group after the head run element by
-    element."""
+    element.  shift=1 with n=10,007 leaves 63 head and 7 tail elements, more
+    than one per thread of the last workgroup."""
     torch, zs, dev = env["torch"], env["zs"], env["dev"]
     rng = np.random.default_rng(3000 + shift + n)
     N = 4

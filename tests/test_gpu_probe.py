@@ -20,7 +20,7 @@ def test_probe_modes():
     f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64] + [ctypes.c_void_p] * 4 + \
         [ctypes.c_int32, ctypes.c_void_p]
     dev = torch.device("cuda:0")
-    N, n = 8, 3 * 2048 + 100
+    N, n = 8, 12 * 512 + 100   # twelve full 512-parameter tiles and a partial one
     gen = torch.Generator().manual_seed(5)
     G = [torch.randint(-2 ** 15, 2 ** 15, (n,), dtype=torch.int16, generator=gen).to(dev) for _ in range(N)]
     P, M, V = (torch.randn(n, generator=gen).to(dev) for _ in range(3))
@@ -33,7 +33,7 @@ def test_probe_modes():
     assert all(torch.equal(a, b) for a, b in zip((P, M, V, B), before)), "read-only probe wrote"
     assert f(tab, N, n, P.data_ptr(), M.data_ptr(), V.data_ptr(), B.data_ptr(), 1, s) == 0
     torch.cuda.synchronize()
-    full = 3 * 2048
+    full = 12 * 512
     for a, b in zip((P, M, V, B), before):
         assert torch.equal(a[full:], b[full:]), "the probe wrote past the full tiles"
     assert not torch.equal(M[:full], before[1][:full])
