@@ -76,12 +76,14 @@ def counter_traffic(w, n_launch_params: int):
     return float(m_bytes.group(1))
 
 
-def pattern_ceiling(w, d, reps: int = 5):
+def pattern_ceiling(w, d, window=(0, 0), reps: int = 5):
     """What the memory system delivers for the step's own access pattern on this machine: the measurement
     probe (libzshard_probe.so) replays the fused kernel's loads and stores, tile layout and
     non-temporal hints included, with the AdamW arithmetic taken out, on the same buffers.  Reported as
-    GB/s of the pattern's own bytes for the read streams alone ((2N+12) B/param) and for the full
-    read+write mix ((2N+26) B/param).  It overwrites the state: run it after the timed steps."""
+    GB/s of the pattern's own bytes for the read streams alone ((2N+12) B/param), for the full
+    read+write mix ((2N+26) B/param) with each tile's writes issued as soon as it is done, and, when the
+    step groups its writes in device-clock windows (`window` = (period, open) ticks), for the same mix
+    with the same windows.  It overwrites the state: run it after the timed steps."""
     import ctypes
 
     import torch
@@ -92,15 +94,24 @@ def pattern_ceiling(w, d, reps: int = 5):
     lib.zs_probe_pattern.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_int32, ctypes.c_void_p]
+    lib.zs_probe_pattern_windowed.restype = ctypes.c_int
+    lib.zs_probe_pattern_windowed.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     N, n = w.N, d["arena_len"]
     full = n // 512 * 512   # the probe covers whole 512-parameter tiles
     tab = (ctypes.c_void_p * N)(*[g.data_ptr() for g in d["G"]])
     stream = torch.cuda.current_stream()
     out = {}
-    for write, bpp, name in ((0, 2 * N + 12, "read"), (1, 2 * N + 26, "read_write")):
+    modes = [(0, 2 * N + 12, "read"), (1, 2 * N + 26, "read_write")]
+    if window[0]:
+        modes.append((2, 2 * N + 26, "read_write_windowed"))
+    for write, bpp, name in modes:
         def call():
-            return lib.zs_probe_pattern(tab, N, n, d["P"].data_ptr(), d["M"].data_ptr(), d["V"].data_ptr(),
-                                        d["B"].data_ptr(), write, stream.cuda_stream)
+            ptrs = (tab, N, n, d["P"].data_ptr(), d["M"].data_ptr(), d["V"].data_ptr(), d["B"].data_ptr())
+            if write == 2:
+                return lib.zs_probe_pattern_windowed(*ptrs, window[0], window[1], stream.cuda_stream)
+            return lib.zs_probe_pattern(*ptrs, write, stream.cuda_stream)
         if call() != 0:
             return None  # a replica count or alignment the probe does not cover
         torch.cuda.synchronize()
@@ -350,14 +361,21 @@ def main() -> int:
     log(f"{ms:.3f} ms/step, {n / (ms / 1e3) / 1e9:.2f} G params/s, {achieved:.0f} GB/s "
         f"(per step: median {ms_median:.3f} ms, min {ms_min:.3f} ms)")
 
+    # the write window the flat step took (0, 0: none) and so the kernel that ran
+    window = (0, 0) if w.is_list or args.path != "fused" else zs.flat_write_window(w.N, n)
+    kernel = ("list_kernel" if w.is_list else "flat_window_kernel" if window[0] else "flat_kernel") + (
+        f"<{w.N}>" if w.N in (1, 2, 4, 8, 16, 32, 64) else "<0>")
     pattern = None
     if args.path == "fused" and not w.is_list and not args.no_copy and footprint >= (1 << 30):
-        pattern = pattern_ceiling(w, d)
+        pattern = pattern_ceiling(w, d, window)
         if pattern:
-            pattern["kernel_frac_of_read_write"] = achieved / pattern["read_write_GBps"]
+            same = pattern.get("read_write_windowed_GBps", pattern["read_write_GBps"])
+            pattern["kernel_frac_of_read_write"] = achieved / same
             log(f"access-pattern ceiling without arithmetic: reads alone {pattern['read_GBps']:.0f} GB/s, "
-                f"reads+writes {pattern['read_write_GBps']:.0f} GB/s; the step reaches "
-                f"{100 * pattern['kernel_frac_of_read_write']:.1f}% of the latter")
+                f"reads+writes {pattern['read_write_GBps']:.0f} GB/s"
+                + (f", with the step's write windows {same:.0f} GB/s" if window[0] else "")
+                + f"; the step reaches {100 * pattern['kernel_frac_of_read_write']:.1f}% of the pattern with "
+                  f"its own write schedule")
     offload_parts = None
     if offload is not None:
         offload.close()
@@ -380,14 +398,14 @@ def main() -> int:
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "n_params": n, "replicas": w.N, "adam_step": w.step,
                    "weight_decay": w.weight_decay, "path": args.path,
+                   "write_window_ticks": list(window) if window[0] else None,
                    "storage": ("fp16" if args.path == "fp16" else "bf16") + " grads and working copy, fp32 master/m/v"},
         "hbm_GBps": achieved, "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,
         "copy_ceiling_GBps": ceiling,
         "pattern_ceiling": pattern,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic if args.path == "fused" else None,
-                     "bytes_per_param": bpp, "kernel": ("list_kernel" if w.is_list else "flat_kernel") + (
-                         f"<{w.N}>" if w.N in (1, 2, 4, 8, 16, 32, 64) else "<0>")},
+                     "bytes_per_param": bpp, "kernel": kernel},
         "cpu_baseline": base,
     }
     if offload_parts:

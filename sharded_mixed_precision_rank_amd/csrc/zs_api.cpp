@@ -20,6 +20,9 @@ namespace {
 
 thread_local std::string g_last_error;
 std::atomic<int32_t> g_grid_blocks{0};
+// zs_set_write_window: period 0 = automatic, 1 = no windows
+std::atomic<int32_t> g_window_period{0};
+std::atomic<int32_t> g_window_open{0};
 
 zs_status fail(zs_status st, const char* fmt, ...) {
   char buf[512];
@@ -170,6 +173,19 @@ zs::FlatShape shape_of(const uint16_t* const* g, int32_t N, int64_t n, float* p,
 int auto_blocks() {
   const int32_t forced = g_grid_blocks.load(std::memory_order_relaxed);
   return forced > 0 ? forced : 1 << 30;
+}
+
+// The flat step's write window for N replicas: the one set by
+// zs_set_write_window, else the measured default.  Defaults, in ticks of the
+// 100 MHz device clock (period / open): N = 64: 4096 / 512, about 41 us with
+// 5 us of writes.
+zs::WriteWindow write_window(int32_t N) {
+  const int32_t period = g_window_period.load(std::memory_order_relaxed);
+  const int32_t open = g_window_open.load(std::memory_order_relaxed);
+  if (period == 1) return zs::WriteWindow{0, 0};
+  if (period > 1) return zs::WriteWindow{(uint64_t)period - 1, (uint64_t)open};
+  if (N == 64) return zs::WriteWindow{4096 - 1, 512};
+  return zs::WriteWindow{0, 0};
 }
 
 zs_status after_launch(hipError_t e, hipStream_t stream, const char* what) {
@@ -366,7 +382,7 @@ zs_status flat_step(const uint16_t* const* grad_chunks, int32_t N, int64_t n, fl
     const zs_adam_hp placeholder = {0.0, 0.0, 0.0, 1.0, 0.0};
     const zs::Scalars c = make_scalars(src ? placeholder : *hp, src ? 1 : step, N);
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    return after_launch(zs::launch_flat(grad_chunks, s, c, ref, auto_blocks(), hs), hs, what);
+    return after_launch(zs::launch_flat(grad_chunks, s, c, ref, auto_blocks(), write_window(N), hs), hs, what);
   } catch (const std::bad_alloc&) {
     return fail(ZS_ERR_NOMEM, "host allocation failed");
   } catch (...) {
@@ -407,6 +423,38 @@ zs_status zs_fold(const zs_adam_hp* hp, int64_t step, zs_folded* out) {
 zs_status zs_set_grid_blocks(int32_t blocks) {
   if (blocks < 0 || blocks > (1 << 24)) return fail(ZS_ERR_RANGE, "blocks must be in [0, 2^24]");
   g_grid_blocks.store(blocks, std::memory_order_relaxed);
+  return ZS_OK;
+}
+
+zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks) {
+  g_last_error.clear();
+  if (period_ticks == 0 || period_ticks == 1) {
+    g_window_period.store(period_ticks, std::memory_order_relaxed);
+    g_window_open.store(0, std::memory_order_relaxed);
+    return ZS_OK;
+  }
+  if (period_ticks < zs::kWindowMinPeriod || period_ticks > zs::kWindowMaxPeriod ||
+      (period_ticks & (period_ticks - 1)) != 0)
+    return fail(ZS_ERR_RANGE, "period_ticks must be 0, 1 or a power of two in [%d, %d] (got %d)",
+                zs::kWindowMinPeriod, zs::kWindowMaxPeriod, period_ticks);
+  if (open_ticks < 1 || open_ticks >= period_ticks || open_ticks > zs::kWindowMaxOpen)
+    return fail(ZS_ERR_RANGE, "open_ticks must be in [1, min(period_ticks - 1, %d)] (got %d)", zs::kWindowMaxOpen,
+                open_ticks);
+  g_window_open.store(open_ticks, std::memory_order_relaxed);
+  g_window_period.store(period_ticks, std::memory_order_relaxed);
+  return ZS_OK;
+}
+
+zs_status zs_flat_write_window(int32_t N, int64_t n, int32_t* period_ticks, int32_t* open_ticks) {
+  g_last_error.clear();
+  if (!period_ticks || !open_ticks) return fail(ZS_ERR_NULL, "period_ticks or open_ticks is NULL");
+  if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
+  if (n < 0) return fail(ZS_ERR_RANGE, "n must be >= 0");
+  const zs::WriteWindow w = write_window(N);
+  const bool templated = N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64;
+  const bool used = w.period_mask != 0 && templated && n / 8 / zs::kFlatBlock >= zs::kWindowMinTiles;
+  *period_ticks = used ? (int32_t)(w.period_mask + 1) : 0;
+  *open_ticks = used ? (int32_t)w.open_ticks : 0;
   return ZS_OK;
 }
 

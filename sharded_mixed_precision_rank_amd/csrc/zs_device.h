@@ -255,5 +255,139 @@ __device__ __forceinline__ void reduce_replicas(GP G, int N, uint32_t e, float (
   }
 }
 
+// ---------------------------------------------------------------- write windows
+// The finished outputs of one full tile in the split lane layout, and the
+// two-slot hold of the windowed flat step (see flat_window_kernel).
+struct TileOut {
+  f32x4 p0, p1, m0, m1, v0, v1;
+  u32x2 b0, b1;
+};
+
+__device__ __forceinline__ TileOut tile_outputs(const float (&p)[8], const float (&m)[8], const float (&v)[8]) {
+  TileOut h;
+  h.p0 = (f32x4){p[0], p[1], p[2], p[3]};
+  h.p1 = (f32x4){p[4], p[5], p[6], p[7]};
+  h.m0 = (f32x4){m[0], m[1], m[2], m[3]};
+  h.m1 = (f32x4){m[4], m[5], m[6], m[7]};
+  h.v0 = (f32x4){v[0], v[1], v[2], v[3]};
+  h.v1 = (f32x4){v[4], v[5], v[6], v[7]};
+  h.b0 = (u32x2){pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+  h.b1 = (u32x2){pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
+  return h;
+}
+
+// Stores a full tile's outputs at tile element e0 (split layout).
+__device__ __forceinline__ void store_tile(const FlatShape& s, int64_t e0, const TileOut& h) {
+  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  const uint32_t e = Layout<true>::first();
+  const uint32_t o = here(e) * 4u;
+  GLB f32x4* P4 = (GLB f32x4*)at(tile_base(s.p + e0), o);
+  GLB f32x4* M4 = (GLB f32x4*)at(tile_base(s.m + e0), o);
+  GLB f32x4* V4 = (GLB f32x4*)at(tile_base(s.v + e0), o);
+  st_g(P4, h.p0);
+  st_g(P4 + q2, h.p1);
+  st_g(M4, h.m0);
+  st_g(M4 + q2, h.m1);
+  st_g(V4, h.v0);
+  st_g(V4 + q2, h.v1);
+  GLB u32x2* B2 = (GLB u32x2*)at(tile_base(s.b + e0), here(e) * 2u);
+  st_g(B2, h.b0);
+  st_g(B2 + Layout<true>::kSecond / 4, h.b1);
+}
+
+// The device's 100 MHz real-time counter, one clock for the whole chip.
+__device__ __forceinline__ uint64_t device_clock() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Up to two finished tiles held in registers (`a` is the older when both are
+// used).  push() stores the older tile at once when both slots are full;
+// check() stores everything held when the window is open and then sleeps
+// until the window's end.  That end is an absolute clock value, so the wait
+// ends once the clock passes it whatever the clock's resolution, and it is
+// capped at kWindowMaxSleeps sleeps (more than the longest window) in any case.
+struct HeldTiles {
+  int n = 0;
+  int64_t ea = 0, eb = 0;
+  TileOut a, b;
+
+  __device__ __forceinline__ void flush(const FlatShape& s) {
+    if (n >= 1) store_tile(s, ea, a);
+    if (n == 2) store_tile(s, eb, b);
+    n = 0;
+  }
+  __device__ __forceinline__ void push(const FlatShape& s, int64_t e0, const TileOut& h) {
+    if (n == 2) {
+      store_tile(s, ea, a);
+      a = b;
+      ea = eb;
+      b = h;
+      eb = e0;
+    } else if (n == 1) {
+      b = h;
+      eb = e0;
+      n = 2;
+    } else {
+      a = h;
+      ea = e0;
+      n = 1;
+    }
+  }
+  __device__ __forceinline__ void check(const FlatShape& s, const WriteWindow& w) {
+    const uint64_t now = device_clock();
+    const uint64_t phase = now & w.period_mask;
+    if (phase < w.open_ticks) {
+      flush(s);
+      const uint64_t end = now - phase + w.open_ticks;
+      for (int k = 0; k < kWindowMaxSleeps && device_clock() < end; ++k) __builtin_amdgcn_s_sleep(2);
+    }
+  }
+};
+
+// reduce_replicas for a templated replica count on a full tile (split layout),
+// calling hook() after every kBatch / CHK replica loads of the stream, at
+// wave-uniform points between loads.  The windowed flat kernel checks the
+// device clock there.  Same loads, same rank-ordered adds as reduce_replicas.
+template <int NT, int CHK, class GP, class HOOK>
+__device__ __forceinline__ void reduce_replicas_hooked(GP G, uint32_t e, float (&acc)[8], HOOK&& hook) {
+  static_assert(NT > 0 && kBatch % CHK == 0, "templated replica count, CHK divides the batch");
+  {
+    const u32x4 w = ld_grad<true>(G, 0, e);
+    acc[0] = bf_lo(w.x);
+    acc[1] = bf_hi(w.x);
+    acc[2] = bf_lo(w.y);
+    acc[3] = bf_hi(w.y);
+    acc[4] = bf_lo(w.z);
+    acc[5] = bf_hi(w.z);
+    acc[6] = bf_lo(w.w);
+    acc[7] = bf_hi(w.w);
+  }
+  constexpr int NB = (NT - 1 + kBatch - 1) / kBatch;
+  if constexpr (NB == 0) {
+    hook();
+  } else {
+    u32x4 w[2][kBatch];
+    load_batch<true>(G, 1, NT, e, w[0]);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (k + 1 < NB) {
+        const int r0 = 1 + (k + 1) * kBatch;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if (r0 + j < NT) w[(k + 1) & 1][j] = ld_grad<true>(G, r0 + j, e);
+          if (CHK > 1 && (j + 1) % (kBatch / CHK) == 0 && j + 1 < kBatch) {
+            __builtin_amdgcn_sched_barrier(0);
+            hook();
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      hook();
+      __builtin_amdgcn_sched_barrier(0);
+      add_batch<kBF16>(acc, w[k & 1], 1 + k * kBatch, NT);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 }  // namespace dev
 }  // namespace zs

@@ -82,9 +82,17 @@ int64_t common_peel(const float* p, const float* m, const float* v, const uint16
 // The same peel over (pointer, element size) pairs.
 int64_t common_peel_sized(const void* const* ptrs, const int* elem_bytes, int count);
 
+// Write windows of the flat step (see flat_window_kernel): stores go out while
+// (device real-time counter & period_mask) < open_ticks.  period_mask == 0:
+// no windows (one tile per workgroup, stores as soon as a tile is done).
+struct WriteWindow {
+  uint64_t period_mask;  // period - 1, the period a power of two of 100 MHz ticks
+  uint64_t open_ticks;   // window length, 1 .. period - 1
+};
+
 // Launches (host side, defined with the kernels).
 hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, const StepRef& ref,
-                       int blocks, hipStream_t stream);
+                       int blocks, const WriteWindow& win, hipStream_t stream);
 // One device thread: *step += 1.
 hipError_t launch_step_advance(int64_t* step, hipStream_t stream);
 // cs: n_sets folded scalar sets, one per hyperparameter group (1 <= n_sets <=
@@ -112,5 +120,19 @@ constexpr int64_t kChunkElems = 4096;
 constexpr int kBlock = 256;
 // Hyperparameter groups a list plan can carry (their scalars travel as kernel arguments).
 constexpr int kMaxGroups = ZS_MAX_GROUPS;
+// Windowed flat step: clock checks per batch of replica loads, the fewest
+// whole tiles for which a shard takes the windowed kernel, and the most
+// devices whose resident-grid figure is cached.
+constexpr int kWindowChecks = 4;
+constexpr int64_t kWindowMinTiles = 65536;
+constexpr int kMaxDevices = 64;
+// Write-window bounds, in ticks of the 100 MHz device clock: the period a
+// power of two in [kWindowMinPeriod, kWindowMaxPeriod], the open part at most
+// kWindowMaxOpen; a wave's wait in a window is capped at kWindowMaxSleeps
+// sleeps of 128 cycles (about 0.2 ms at 2.4 GHz, past any allowed window).
+constexpr int32_t kWindowMinPeriod = 64;
+constexpr int32_t kWindowMaxPeriod = 1 << 20;
+constexpr int32_t kWindowMaxOpen = 1 << 14;
+constexpr int kWindowMaxSleeps = 4096;
 
 }  // namespace zs

@@ -37,6 +37,8 @@
 // contraction) and correctly rounded fp32 divide and sqrt; fp32 denormals are
 // kept.  Division by N is a multiply by 1/N only when N is a power of two,
 // where both are the same correctly rounded result.
+#include <atomic>
+
 #include "zs_device.h"
 
 namespace zs {
@@ -162,6 +164,71 @@ __global__ __launch_bounds__(kFlatBlock) void flat_kernel(const FlatArgs<NT> a) 
   }
 }
 
+// ---------------------------------------------------------------- write windows
+// The step's 14 bytes per parameter of write-back cost far more when they
+// trickle out beside the replica read streams than when the same bytes are
+// written on their own.  The windowed kernel therefore groups them in time:
+// persistent one-wave workgroups keep the finished outputs of up to two tiles
+// in registers and store them only while the device's 100 MHz real-time
+// counter (s_memrealtime, one clock for the whole chip) is inside a short
+// window that opens once per period.  While the window is open every wave
+// issues no loads: it stores what it holds and sleeps until the window closes,
+// so the memory system sees alternating read-only and write-only phases.  A
+// wave whose two slots are full stores the older tile at once.  Which tile is
+// stored when changes nothing in the results: each tile's outputs are formed
+// exactly as in flat_kernel and written to its own addresses.
+
+template <int NT>
+__global__ __launch_bounds__(kFlatBlock) void flat_window_kernel(const FlatArgs<NT> a, const WriteWindow w) {
+  static_assert(NT > 0, "templated replica counts only");
+  Scalars c = a.c;
+  if (!step_scalars(a.r, c)) return;
+  const FlatShape& s = a.s;
+  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  const uint32_t e = Layout<true>::first();
+  const int64_t full = s.nvec / kFlatBlock;  // whole tiles
+  HeldTiles held;
+  auto check = [&]() { held.check(s, w); };
+  for (int64_t t = blockIdx.x; t < full; t += gridDim.x) {
+    const int64_t e0 = s.head + 8 * kFlatBlock * t;
+    f32x4 pa, pb, ma, mb, va, vb;
+    {
+      const uint32_t o = here(e) * 4u;
+      const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(s.p + e0), o);
+      const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(s.m + e0), o);
+      const GLB f32x4* V4 = (const GLB f32x4*)at(tile_base(s.v + e0), o);
+      pa = ld_g(P4);
+      pb = ld_g(P4 + q2);
+      ma = ld_g(M4);
+      mb = ld_g(M4 + q2);
+      va = ld_g(V4);
+      vb = ld_g(V4 + q2);
+    }
+    auto G = [&](int r) { return tile_base(a.g[r] + e0); };
+    float acc[8];
+    reduce_replicas_hooked<NT, kWindowChecks>(G, e, acc, check);
+    float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+    float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+    float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) adam(mean_of<NT>(acc[k], c), p[k], m[k], v[k], c);
+    held.push(s, e0, tile_outputs(p, m, v));
+  }
+  held.flush(s);
+  // the one partial tile and the head and tail elements, unwindowed
+  if (blockIdx.x == gridDim.x - 1) {
+    const int64_t gt = full * kFlatBlock;
+    const int64_t e0 = s.head + 8 * gt;
+    const int N = NT;
+    if (gt + threadIdx.x < s.nvec) {
+      auto G = [&](int r) { return tile_base(a.g[r] + e0); };
+      group_step<NT, false>(G, N, e0, s, c);
+    }
+    auto G1 = [&](int r) { return a.g[r]; };
+    edge_step<kFlatBlock>(G1, N, s, c);
+  }
+}
+
 __global__ void step_advance_kernel(int64_t* step) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *step = *step + 1;
 }
@@ -248,14 +315,45 @@ int clamp_grid(int blocks, int64_t work) {
   return (int)(blocks < need ? blocks : need);
 }
 
+// Workgroups of flat_window_kernel<NT> that fit on the current device at
+// once (compute units x resident workgroups per unit), cached per device.
+template <int NT>
+int resident_grid() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int g = cache[dev].load(std::memory_order_relaxed);
+  if (g > 0) return g;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, flat_window_kernel<NT>, kFlatBlock, 0) != hipSuccess)
+    return 0;
+  g = cus * per_cu;
+  if (g > 0) cache[dev].store(g, std::memory_order_relaxed);
+  return g;
+}
+
 template <int NT>
 hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, const StepRef& ref,
-                   int blocks, hipStream_t stream) {
+                   int blocks, const WriteWindow& win, hipStream_t stream) {
   FlatArgs<NT> a;
   for (int r = 0; r < c.n_rep; ++r) a.g[r] = grads[r];
   a.s = s;
   a.c = c;
   a.r = ref;
+  if constexpr (NT > 0) {
+    // windowed: shards of many whole tiles, when a window is set
+    if (win.period_mask != 0 && !s.scalar_only && s.nvec / kFlatBlock >= kWindowMinTiles) {
+      int grid = resident_grid<NT>();
+      if (grid > 0) {
+        if (blocks < grid) grid = blocks;
+        (void)hipGetLastError();
+        flat_window_kernel<NT><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(a, win);
+        return hipGetLastError();
+      }
+      (void)hipGetLastError();  // no occupancy figure: take the one-tile kernel
+    }
+  }
   const int grid = clamp_grid(blocks, s.scalar_only ? s.n : s.nvec);
   (void)hipGetLastError();
   flat_kernel<NT><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(a);
@@ -283,16 +381,16 @@ hipError_t go_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* 
 }  // namespace
 
 hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, const StepRef& ref,
-                       int blocks, hipStream_t stream) {
+                       int blocks, const WriteWindow& win, hipStream_t stream) {
   switch (c.n_rep) {
-    case 1: return go_flat<1>(grads, s, c, ref, blocks, stream);
-    case 2: return go_flat<2>(grads, s, c, ref, blocks, stream);
-    case 4: return go_flat<4>(grads, s, c, ref, blocks, stream);
-    case 8: return go_flat<8>(grads, s, c, ref, blocks, stream);
-    case 16: return go_flat<16>(grads, s, c, ref, blocks, stream);
-    case 32: return go_flat<32>(grads, s, c, ref, blocks, stream);
-    case 64: return go_flat<64>(grads, s, c, ref, blocks, stream);
-    default: return go_flat<0>(grads, s, c, ref, blocks, stream);
+    case 1: return go_flat<1>(grads, s, c, ref, blocks, win, stream);
+    case 2: return go_flat<2>(grads, s, c, ref, blocks, win, stream);
+    case 4: return go_flat<4>(grads, s, c, ref, blocks, win, stream);
+    case 8: return go_flat<8>(grads, s, c, ref, blocks, win, stream);
+    case 16: return go_flat<16>(grads, s, c, ref, blocks, win, stream);
+    case 32: return go_flat<32>(grads, s, c, ref, blocks, win, stream);
+    case 64: return go_flat<64>(grads, s, c, ref, blocks, win, stream);
+    default: return go_flat<0>(grads, s, c, ref, blocks, win, stream);
   }
 }
 

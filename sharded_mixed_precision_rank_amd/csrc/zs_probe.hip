@@ -13,7 +13,9 @@
 //              moved behind a branch;
 //   write = 1: master, m, v and the 16-bit copy are written back with values
 //              that need one add per element: the full (2N + 26) bytes per
-//              parameter of the step.
+//              parameter of the step;
+//   windowed:  (zs_probe_pattern_windowed) the writes of write = 1 grouped in
+//              device-clock windows, as the windowed flat step writes.
 // Only full tiles are processed; the caller passes arrays that start on a
 // 128-byte boundary.  The values written are meaningless: run the probe on
 // scratch state or after the state is no longer needed.
@@ -81,6 +83,75 @@ __global__ __launch_bounds__(kFlatBlock) void pattern_kernel(const ProbeArgs<NT>
   }
 }
 
+// write = 2: the writes of write = 1, grouped in device-clock windows as the
+// windowed flat step groups them (persistent one-wave workgroups, up to two
+// finished tiles held, the same clock checks in the replica stream and the
+// same pauses of all loads while a window is open).
+template <int NT>
+__global__ __launch_bounds__(kFlatBlock) void pattern_window_kernel(const ProbeArgs<NT> a, int64_t tiles,
+                                                                    const WriteWindow w) {
+  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  const uint32_t e = Layout<true>::first();
+  FlatShape s{};
+  s.p = a.p;
+  s.m = a.m;
+  s.v = a.v;
+  s.b = a.b;
+  HeldTiles held;
+  auto check = [&]() { held.check(s, w); };
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int64_t e0 = t * (kFlatBlock * 8);
+    f32x4 pa, pb, ma, mb, va, vb;
+    {
+      const uint32_t o = here(e) * 4u;
+      const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(a.p + e0), o);
+      const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(a.m + e0), o);
+      const GLB f32x4* V4 = (const GLB f32x4*)at(tile_base(a.v + e0), o);
+      pa = ld_g(P4);
+      pb = ld_g(P4 + q2);
+      ma = ld_g(M4);
+      mb = ld_g(M4 + q2);
+      va = ld_g(V4);
+      vb = ld_g(V4 + q2);
+    }
+    auto G = [&](int r) { return tile_base(a.g[r] + e0); };
+    float acc[8];
+    reduce_replicas_hooked<NT, kWindowChecks>(G, e, acc, check);
+    float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+    float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+    float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      p[k] = p[k] + acc[k];
+      v[k] = v[k] + m[k];
+      m[k] = acc[k];
+    }
+    held.push(s, e0, tile_outputs(p, m, v));
+  }
+  held.flush(s);
+}
+
+template <int NT>
+hipError_t go_window(const uint16_t* const* g, int64_t tiles, float* p, float* m, float* v, uint16_t* b,
+                     const WriteWindow& w, hipStream_t stream) {
+  ProbeArgs<NT> a;
+  for (int r = 0; r < NT; ++r) a.g[r] = g[r];
+  a.p = p;
+  a.m = m;
+  a.v = v;
+  a.b = b;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pattern_window_kernel<NT>, kFlatBlock, 0) != hipSuccess ||
+      cus * per_cu < 1)
+    return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)cus * per_cu < tiles ? (int64_t)cus * per_cu : tiles;
+  (void)hipGetLastError();
+  pattern_window_kernel<NT><<<dim3((unsigned)grid), dim3(kFlatBlock), 0, stream>>>(a, tiles, w);
+  return hipGetLastError();
+}
+
 template <int NT>
 hipError_t go(const uint16_t* const* g, int64_t tiles, float* p, float* m, float* v, uint16_t* b, int write,
               hipStream_t stream) {
@@ -102,6 +173,35 @@ bool line_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 127)
 
 }  // namespace
 }  // namespace zs
+
+// Runs the windowed write pattern (write = 2 above) over the n / 512 full
+// tiles, with the write window period_ticks / open_ticks (ticks of the 100 MHz
+// device clock; the period a power of two in [64, 2^20], 1 <= open_ticks <
+// period, open_ticks <= 2^14).  Returns as zs_probe_pattern.
+extern "C" __attribute__((visibility("default"))) int zs_probe_pattern_windowed(
+    const uint16_t* const* g, int32_t N, int64_t n, float* p, float* m, float* v, uint16_t* b, int32_t period_ticks,
+    int32_t open_ticks, void* stream) {
+  using namespace zs;
+  const int64_t tiles = n / (kFlatBlock * 8);
+  if (tiles < 1 || !g || !p || !m || !v || !b) return 1;
+  if (period_ticks < kWindowMinPeriod || period_ticks > kWindowMaxPeriod || (period_ticks & (period_ticks - 1)) ||
+      open_ticks < 1 || open_ticks >= period_ticks || open_ticks > kWindowMaxOpen)
+    return 1;
+  if (!line_aligned(p) || !line_aligned(m) || !line_aligned(v) || !line_aligned(b)) return 1;
+  for (int32_t r = 0; r < N; ++r)
+    if (!g[r] || !line_aligned(g[r])) return 1;
+  const WriteWindow w{(uint64_t)period_ticks - 1, (uint64_t)open_ticks};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (N) {
+    case 2: e = go_window<2>(g, tiles, p, m, v, b, w, s); break;
+    case 8: e = go_window<8>(g, tiles, p, m, v, b, w, s); break;
+    case 16: e = go_window<16>(g, tiles, p, m, v, b, w, s); break;
+    case 64: e = go_window<64>(g, tiles, p, m, v, b, w, s); break;
+    default: return 1;
+  }
+  return e == hipSuccess ? 0 : 2;
+}
 
 // Runs the probe over the n / 512 full tiles of the shard on `stream`.
 // Returns 0 on success, 1 for unsupported arguments (N not 2, 8, 16 or 64,

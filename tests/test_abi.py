@@ -291,6 +291,34 @@ def test_probe_library_rejects_unsupported_arguments_without_gpu():
     assert f(g, 3, 1 << 20, *arr, 0, None) == 1            # N = 3 is not covered
     assert f(g, 2, 500, *arr, 0, None) == 1                # less than one 512-parameter tile
     assert f(g, 2, 1 << 20, A + 0x400004, *arr[1:], 0, None) == 1   # not on a 128-byte boundary
+    fw = lib.zs_probe_pattern_windowed
+    fw.restype = ctypes.c_int
+    fw.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64] + [ctypes.c_void_p] * 4 + \
+        [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert fw(g, 3, 1 << 20, *arr, 4096, 512, None) == 1   # N = 3 is not covered
+    assert fw(g, 2, 500, *arr, 4096, 512, None) == 1       # less than one tile
+    assert fw(g, 2, 1 << 20, *arr, 4000, 512, None) == 1   # period not a power of two
+    assert fw(g, 2, 1 << 20, *arr, 32, 8, None) == 1       # period below 64 ticks
+    assert fw(g, 2, 1 << 20, *arr, 4096, 4096, None) == 1  # window not shorter than the period
+    assert fw(g, 2, 1 << 20, A + 0x400004, *arr[1:], 4096, 512, None) == 1
+
+
+def test_flat_write_window_query():
+    """The query reports the window the flat step takes: the N = 64 default on shards of at least
+    65,536 whole tiles, none below that, for other replica counts, or when windows are switched off."""
+    assert zs.flat_write_window(64, 1_093_750_000) == (4096, 512)
+    assert zs.flat_write_window(64, 65536 * 512) == (4096, 512)
+    assert zs.flat_write_window(64, 65536 * 512 - 1) == (0, 0)
+    assert zs.flat_write_window(8, 124_000_000) == (0, 0)
+    assert zs.flat_write_window(3, 1 << 30) == (0, 0)
+    zs.set_write_window(1)
+    assert zs.flat_write_window(64, 1 << 30) == (0, 0)
+    zs.set_write_window(1024, 128)
+    assert zs.flat_write_window(16, 1 << 30) == (1024, 128)
+    assert zs.flat_write_window(5, 1 << 30) == (0, 0)   # runtime replica counts take the one-tile kernel
+    zs.set_write_window(0)
+    with pytest.raises(zs.ZShardError):
+        zs.flat_write_window(0, 1 << 20)
 
 
 def test_device_scaler_entry_points_reject_bad_arguments_without_gpu():
@@ -371,3 +399,20 @@ def test_devstep_entry_points_reject_bad_arguments_without_gpu():
     assert f(src(status=tab + 64)) == "ZS_ERR_ALIAS"        # status inside the table
     assert f(src(table=P + 1024)) == "ZS_ERR_ALIAS"         # table inside the master array (written)
     assert f(src(status=A + 0x1000000 + 8)) == "ZS_ERR_ALIAS"  # status inside a gradient chunk
+
+
+def test_tuning_knobs_check_their_ranges():
+    lib = ctypes.CDLL(zs.LIB_PATH)
+    lib.zs_set_write_window.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.zs_set_grid_blocks.argtypes = [ctypes.c_int32]
+    ok, rng = 0, 2
+    for period, open_ticks, want in [(0, 0, ok), (1, 0, ok), (0, 999, ok), (64, 1, ok), (64, 63, ok),
+                                     (4096, 512, ok), (1 << 20, 1 << 14, ok), (2, 1, rng), (32, 1, rng),
+                                     (96, 1, rng), (4096, 0, rng), (4096, 4096, rng), (1 << 20, (1 << 14) + 1, rng),
+                                     (1 << 21, 1, rng), (-4, 1, rng), (256, -1, rng)]:
+        assert lib.zs_set_write_window(period, open_ticks) == want, (period, open_ticks)
+    assert lib.zs_set_write_window(0, 0) == ok
+    assert lib.zs_set_grid_blocks(-1) == rng and lib.zs_set_grid_blocks(0) == ok
+    with pytest.raises(zs.ZShardError):
+        zs.set_write_window(100, 10)
+    zs.set_write_window(0)

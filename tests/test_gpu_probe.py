@@ -1,5 +1,7 @@
 """The measurement probe on the GPU: the read-only pattern leaves every array
-as it was, and the read+write pattern touches exactly the full tiles."""
+as it was, and the read+write patterns (stores as each tile is done, and stores
+grouped in device-clock windows) touch exactly the full tiles and write the
+same values."""
 import ctypes
 import os
 
@@ -38,3 +40,17 @@ def test_probe_modes():
         assert torch.equal(a[full:], b[full:]), "the probe wrote past the full tiles"
     assert not torch.equal(M[:full], before[1][:full])
     assert np.any(B[:full].cpu().numpy() != 0)
+    after = [x.clone() for x in (P, M, V, B)]
+    # the windowed pattern from the same starting state writes the same values
+    for x, b0 in zip((P, M, V, B), before):
+        x.copy_(b0)
+    fw = lib.zs_probe_pattern_windowed
+    fw.restype = ctypes.c_int
+    fw.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64] + [ctypes.c_void_p] * 4 + \
+        [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert fw(tab, N, n, P.data_ptr(), M.data_ptr(), V.data_ptr(), B.data_ptr(), 256, 32, s) == 0
+    torch.cuda.synchronize()
+    # bit patterns: the random 16-bit replicas include NaN encodings, and NaN != NaN
+    bits = lambda x: x.view(torch.int32) if x.dtype == torch.float32 else x
+    for a, b in zip((P, M, V, B), after):
+        assert torch.equal(bits(a), bits(b)), "the windowed pattern wrote other values than the plain one"

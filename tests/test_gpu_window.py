@@ -1,0 +1,101 @@
+"""GPU parity of the windowed flat step (persistent workgroups that hold
+finished tiles and store them in device-clock windows) against the CPU oracle.
+
+The shards are just above the size at which the library takes the windowed
+kernel (65,536 whole 512-parameter tiles), start off a line boundary (a head
+of peeled elements) and end in a partial tile and a tail.  Each window
+setting, including the extremes (a window open 63 ticks of a 64-tick period;
+one open 1 tick of 2^20, which makes every wave store its older tile as soon
+as both slots are full), and a forced small grid (many tiles per wave) must
+give every output bit-identical to the oracle: the schedule of the stores
+cannot change what is stored.
+"""
+import numpy as np
+import pytest
+
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+# 2^25 + 7 tiles + 123 parameters: 65,543 whole tiles after the head (plus a
+# partial tile and a tail), past the 65,536-tile threshold
+N_PARAMS = (1 << 25) + 7 * 512 + 123
+OFFSET = 8  # elements: every array starts 32 or 16 bytes past a line boundary
+
+WINDOWS = [(0, 0), (1, 0), (256, 32), (64, 63), (1 << 20, 1), (4096, 512)]
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    import sharded_mixed_precision_rank_amd as zs
+
+    yield dict(torch=torch, zs=zs, dev=torch.device("cuda:0"))
+    zs.set_write_window(0)
+    zs.set_grid_blocks(0)
+
+
+def _inputs(N, step, wd):
+    from synth import workloads as W
+
+    w = W.FLAT_1M_N2.with_(n_flat=N_PARAMS, N=N, step=step, warm=True, weight_decay=wd)
+    return w, W.host_inputs(w, 0, w.n_flat)
+
+
+def _upload(torch, dev, host):
+    def put(a, dtype):
+        t = torch.empty(a.size + OFFSET, dtype=dtype, device=dev)
+        view = t[OFFSET:]
+        view.copy_(torch.from_numpy(a))
+        return view
+
+    G = [put(g.view(np.int16), torch.int16) for g in host["G"]]
+    return dict(G=G, P=put(host["P"], torch.float32), M=put(host["M"], torch.float32),
+                V=put(host["V"], torch.float32),
+                B=put(np.full(host["P"].size, 0x7FBF, dtype=np.uint16).view(np.int16), torch.int16))
+
+
+@pytest.mark.parametrize("N", [2, 64])
+def test_windowed_step_matches_oracle(env, orc, N):
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    w, host = _inputs(N, 5000 if N == 64 else 100, 0.1 if N == 64 else 0.0)
+    P, M, V, B = orc.step(host["G"], host["P"], host["M"], host["V"], w.hp(), w.step)
+    ref = dict(P=P, M=M, V=V, B=B)
+    for blocks in (0, 37):
+        zs.set_grid_blocks(blocks)
+        for period, open_ticks in WINDOWS:
+            zs.set_write_window(period, open_ticks)
+            print(f"windowed step: N={N} n={N_PARAMS} blocks={blocks} window={period}/{open_ticks}", flush=True)
+            d = _upload(torch, dev, host)
+            zs.reduce_adam_flat(d["G"], d["P"], d["M"], d["V"], d["B"], w.hp(), w.step)
+            torch.cuda.synchronize()
+            got = dict(P=d["P"].cpu().numpy(), M=d["M"].cpu().numpy(), V=d["V"].cpu().numpy(),
+                       B=d["B"].cpu().numpy().view(np.uint16))
+            what = f"N={N} blocks={blocks} window={period}/{open_ticks}"
+            rep = parity.assert_step(got, ref, what)
+            assert parity.bit_identical(got, ref), f"{what}: not bit-identical: {rep}"
+            del d
+    zs.set_grid_blocks(0)
+    zs.set_write_window(0)
+
+
+def test_windowed_device_step(env, orc):
+    """The device-step form takes the same windowed kernel: equal to the host step."""
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    w, host = _inputs(8, 3, 0.0)
+    zs.set_write_window(256, 64)
+    a, b = _upload(torch, dev, host), _upload(torch, dev, host)
+    src = zs.StepSource(w.hp(), 1, 10, dev, start=3)
+    zs.reduce_adam_flat_devstep(a["G"], a["P"], a["M"], a["V"], a["B"], src)
+    zs.set_write_window(1)
+    zs.reduce_adam_flat(b["G"], b["P"], b["M"], b["V"], b["B"], w.hp(), 3)
+    torch.cuda.synchronize()
+    zs.set_write_window(0)
+    for k in ("P", "M", "V", "B"):
+        assert torch.equal(a[k], b[k]), k
+    assert src.status == 0
+    P, M, V, B = orc.step(host["G"], host["P"], host["M"], host["V"], w.hp(), 3)
+    got = dict(P=a["P"].cpu().numpy(), M=a["M"].cpu().numpy(), V=a["V"].cpu().numpy(),
+               B=a["B"].cpu().numpy().view(np.uint16))
+    assert parity.bit_identical(got, dict(P=P, M=M, V=V, B=B))
