@@ -362,9 +362,14 @@ def main() -> int:
         f"(per step: median {ms_median:.3f} ms, min {ms_min:.3f} ms)")
 
     # the write window the flat step took (0, 0: none) and so the kernel that ran
-    window = (0, 0) if w.is_list or args.path != "fused" else zs.flat_write_window(w.N, n)
-    kernel = ("list_kernel" if w.is_list else "flat_window_kernel" if window[0] else "flat_kernel") + (
-        f"<{w.N}>" if w.N in (1, 2, 4, 8, 16, 32, 64) else "<0>")
+    window = (0, 0) if w.is_list or offload is not None else zs.write_window("reduce" if two_pass else "flat", w.N, n)
+    tn = f"<{w.N}>" if w.N in (1, 2, 4, 8, 16, 32, 64) else "<0>"
+    if w.is_list:
+        kernel = "list_kernel" + tn
+    elif two_pass:
+        kernel = ("reduce_window_kernel" if window[0] else "reduce_kernel") + tn + " + gbar_kernel"
+    else:
+        kernel = ("flat_window_kernel" if window[0] else "flat_kernel") + tn
     pattern = None
     if args.path == "fused" and not w.is_list and not args.no_copy and footprint >= (1 << 30):
         pattern = pattern_ceiling(w, d, window)

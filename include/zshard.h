@@ -376,20 +376,22 @@ ZS_API zs_status zs_cpu_adam(const float* gbar, int64_t n, float* master, float*
    on it (every element is computed by one thread with the same operations). */
 ZS_API zs_status zs_set_grid_blocks(int32_t blocks);
 
-/* Write windows of the flat step, for all later flat step calls in this
-   process (zs_reduce_adam_flat and its device-step form).  The step writes
-   14 bytes per parameter back beside 2N + 12 read; on this memory system the
-   writes cost far less when grouped in time than when they trickle out beside
-   the read streams.  On shards of at least 2^25 parameters (65,536 whole
-   512-parameter tiles) and a replica count of 1, 2, 4, 8, 16, 32 or 64, the
-   step then runs as persistent workgroups that hold finished tiles in
+/* Write windows of the flat step (zs_reduce_adam_flat and its device-step
+   form) and of pass 1 of the two-pass form (zs_reduce_grads_flat and its
+   device-scale form), for all later calls in this process.  The flat step
+   writes 14 bytes per parameter back beside 2N + 12 read, pass 1 writes 4
+   beside 2N; on this memory system the writes cost far less when grouped in
+   time than when they trickle out beside the read streams.  On shards of at
+   least 2^25 parameters and a replica count of 1, 2, 4, 8, 16, 32 or 64, the
+   kernel then runs as persistent workgroups that hold finished tiles in
    registers and store them while the device's 100 MHz real-time counter,
    taken modulo period_ticks, is below open_ticks; no loads are issued in that
    window.  Results do not depend on the setting: each tile's outputs are
-   computed identically and written to their own addresses.
-     period_ticks = 0: the library's measured default for each replica count
-                       (the default; open_ticks is ignored);
-     period_ticks = 1: no windows (one tile per workgroup, stored at once);
+   computed identically and written to their own addresses (pass 1's norm
+   partials too).
+     period_ticks = 0: the library's measured default for each kernel and
+                       replica count (the default; open_ticks is ignored);
+     period_ticks = 1: no windows (tiles stored as they finish);
      otherwise a power of two in [64, 2^20], with 1 <= open_ticks < period_ticks
      and open_ticks <= 2^14.
    A wave waits at most the window's length, and never more than about 0.2 ms
@@ -397,11 +399,17 @@ ZS_API zs_status zs_set_grid_blocks(int32_t blocks);
    Errors: ZS_ERR_RANGE. */
 ZS_API zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks);
 
-/* The write window the flat step takes, under the current setting, for N
-   replicas on a shard of n parameters whose arrays share a 128-byte line
-   phase: *period_ticks = *open_ticks = 0 when it takes no windows.  No GPU
-   call.  Errors: ZS_ERR_NULL, ZS_ERR_RANGE. */
-ZS_API zs_status zs_flat_write_window(int32_t N, int64_t n, int32_t* period_ticks, int32_t* open_ticks);
+/* The write window a kernel takes, under the current setting, for N replicas
+   on a shard of n parameters whose arrays share a 128-byte line phase:
+     kernel = ZS_WINDOW_FLAT_STEP:   the flat step (zs_reduce_adam_flat);
+     kernel = ZS_WINDOW_REDUCE_PASS: pass 1 of the two-pass form
+                                     (zs_reduce_grads_flat), on shards of at
+                                     least 2^25 parameters.
+   *period_ticks = *open_ticks = 0 when it takes no windows.  No GPU call.
+   Errors: ZS_ERR_NULL, ZS_ERR_RANGE. */
+#define ZS_WINDOW_FLAT_STEP 0
+#define ZS_WINDOW_REDUCE_PASS 1
+ZS_API zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* period_ticks, int32_t* open_ticks);
 
 #ifdef __cplusplus
 }

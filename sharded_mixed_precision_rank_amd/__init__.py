@@ -90,8 +90,9 @@ _lib.zs_set_grid_blocks.restype = ctypes.c_int
 _lib.zs_set_grid_blocks.argtypes = [_i32]
 _lib.zs_set_write_window.restype = ctypes.c_int
 _lib.zs_set_write_window.argtypes = [_i32, _i32]
-_lib.zs_flat_write_window.restype = ctypes.c_int
-_lib.zs_flat_write_window.argtypes = [_i32, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+_lib.zs_write_window.restype = ctypes.c_int
+_lib.zs_write_window.argtypes = [_i32, _i32, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+WINDOW_KERNELS = {"flat": 0, "reduce": 1}
 _lib.zs_two_pass_workspace_bytes.restype = ctypes.c_size_t
 _lib.zs_two_pass_workspace_bytes.argtypes = [_i64]
 _lib.zs_reduce_grads_flat.restype = ctypes.c_int
@@ -187,10 +188,11 @@ def set_write_window(period_ticks: int, open_ticks: int = 0) -> None:
     _check(_lib.zs_set_write_window(period_ticks, open_ticks), "zs_set_write_window")
 
 
-def flat_write_window(N: int, n: int):
-    """(period_ticks, open_ticks) the flat step takes for N replicas on n parameters; (0, 0) = no windows."""
+def write_window(kernel: str, N: int, n: int):
+    """(period_ticks, open_ticks) that the flat step (kernel="flat") or pass 1 of the two-pass form
+    (kernel="reduce") takes for N replicas on n parameters; (0, 0) = no windows."""
     p, o = _i32(), _i32()
-    _check(_lib.zs_flat_write_window(N, n, ctypes.byref(p), ctypes.byref(o)), "zs_flat_write_window")
+    _check(_lib.zs_write_window(WINDOW_KERNELS[kernel], N, n, ctypes.byref(p), ctypes.byref(o)), "zs_write_window")
     return p.value, o.value
 
 

@@ -188,6 +188,17 @@ zs::WriteWindow write_window(int32_t N) {
   return zs::WriteWindow{0, 0};
 }
 
+// The same for pass 1 of the two-pass form (which writes 4 bytes per
+// parameter beside 2N read).  Default: N = 64: 4096 / 256.
+zs::WriteWindow reduce_write_window(int32_t N) {
+  const int32_t period = g_window_period.load(std::memory_order_relaxed);
+  const int32_t open = g_window_open.load(std::memory_order_relaxed);
+  if (period == 1) return zs::WriteWindow{0, 0};
+  if (period > 1) return zs::WriteWindow{(uint64_t)period - 1, (uint64_t)open};
+  if (N == 64) return zs::WriteWindow{4096 - 1, 256};
+  return zs::WriteWindow{0, 0};
+}
+
 zs_status after_launch(hipError_t e, hipStream_t stream, const char* what) {
   if (e != hipSuccess) return hip_fail(e, what);
   if (sync_mode()) {
@@ -445,14 +456,19 @@ zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks) {
   return ZS_OK;
 }
 
-zs_status zs_flat_write_window(int32_t N, int64_t n, int32_t* period_ticks, int32_t* open_ticks) {
+zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* period_ticks, int32_t* open_ticks) {
   g_last_error.clear();
   if (!period_ticks || !open_ticks) return fail(ZS_ERR_NULL, "period_ticks or open_ticks is NULL");
+  if (kernel != ZS_WINDOW_FLAT_STEP && kernel != ZS_WINDOW_REDUCE_PASS)
+    return fail(ZS_ERR_RANGE, "kernel must be ZS_WINDOW_FLAT_STEP or ZS_WINDOW_REDUCE_PASS (got %d)", kernel);
   if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
   if (n < 0) return fail(ZS_ERR_RANGE, "n must be >= 0");
-  const zs::WriteWindow w = write_window(N);
+  const bool flat = kernel == ZS_WINDOW_FLAT_STEP;
+  const zs::WriteWindow w = flat ? write_window(N) : reduce_write_window(N);
   const bool templated = N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64;
-  const bool used = w.period_mask != 0 && templated && n / 8 / zs::kFlatBlock >= zs::kWindowMinTiles;
+  const bool big = flat ? n / 8 / zs::kFlatBlock >= zs::kWindowMinTiles
+                        : n / kTileElems >= zs::kReduceWindowMinTiles;
+  const bool used = w.period_mask != 0 && templated && big;
   *period_ticks = used ? (int32_t)(w.period_mask + 1) : 0;
   *open_ticks = used ? (int32_t)w.open_ticks : 0;
   return ZS_OK;
@@ -782,6 +798,7 @@ zs_status reduce_grads(const uint16_t* const* grad_chunks, int32_t N, int64_t n,
       reduce_shape(grad_chunks, N, n, workspace, sqnorm, (float)(1.0 / host_scale), &sh);
     }
     sh.scale_dev = scale_state ? &scale_state->scale : nullptr;
+    sh.window = reduce_write_window(N);
     return after_launch(zs::launch_reduce(grad_chunks, sh, grad_format, auto_blocks(), hs), hs, what);
   } catch (const std::bad_alloc&) {
     return fail(ZS_ERR_NOMEM, "host allocation failed");

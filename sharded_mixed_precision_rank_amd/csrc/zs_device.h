@@ -298,12 +298,25 @@ __device__ __forceinline__ void store_tile(const FlatShape& s, int64_t e0, const
 // The device's 100 MHz real-time counter, one clock for the whole chip.
 __device__ __forceinline__ uint64_t device_clock() { return __builtin_amdgcn_s_memrealtime(); }
 
+// If the write window is open: flush(), then sleep until the window's end.
+// That end is an absolute clock value, so the wait ends once the clock passes
+// it whatever the clock's resolution, and it is capped at kWindowMaxSleeps
+// sleeps (more than the longest window) in any case.
+template <class FLUSH>
+__device__ __forceinline__ void window_wait(const WriteWindow& w, FLUSH&& flush) {
+  const uint64_t now = device_clock();
+  const uint64_t phase = now & w.period_mask;
+  if (phase < w.open_ticks) {
+    flush();
+    const uint64_t end = now - phase + w.open_ticks;
+    for (int k = 0; k < kWindowMaxSleeps && device_clock() < end; ++k) __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 // Up to two finished tiles held in registers (`a` is the older when both are
 // used).  push() stores the older tile at once when both slots are full;
 // check() stores everything held when the window is open and then sleeps
-// until the window's end.  That end is an absolute clock value, so the wait
-// ends once the clock passes it whatever the clock's resolution, and it is
-// capped at kWindowMaxSleeps sleeps (more than the longest window) in any case.
+// until the window's end (window_wait).
 struct HeldTiles {
   int n = 0;
   int64_t ea = 0, eb = 0;
@@ -332,13 +345,53 @@ struct HeldTiles {
     }
   }
   __device__ __forceinline__ void check(const FlatShape& s, const WriteWindow& w) {
-    const uint64_t now = device_clock();
-    const uint64_t phase = now & w.period_mask;
-    if (phase < w.open_ticks) {
-      flush(s);
-      const uint64_t end = now - phase + w.open_ticks;
-      for (int k = 0; k < kWindowMaxSleeps && device_clock() < end; ++k) __builtin_amdgcn_s_sleep(2);
+    window_wait(w, [&]() { flush(s); });
+  }
+};
+
+// Pass 1 of the two-pass form: the fp32 mean gradients of up to K finished
+// full tiles (8 per lane, split layout) held in registers; push() stores the
+// oldest at once when all K slots are used.
+template <int K>
+struct HeldMeans {
+  int n = 0;
+  int64_t e[K];
+  f32x4 g0[K], g1[K];
+
+  __device__ __forceinline__ static void store(float* gbar, int64_t e0, f32x4 a, f32x4 b) {
+    const uint32_t o = here(Layout<true>::first()) * 4u;
+    GLB f32x4* O = (GLB f32x4*)at(tile_base(gbar + e0), o);
+    st_g(O, a);
+    st_g(O + Layout<true>::kSecond / 4, b);
+  }
+  __device__ __forceinline__ void flush(float* gbar) {
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      if (i < n) store(gbar, e[i], g0[i], g1[i]);
+    n = 0;
+  }
+  __device__ __forceinline__ void push(float* gbar, int64_t e0, f32x4 a, f32x4 b) {
+    if (n == K) {
+      store(gbar, e[0], g0[0], g1[0]);
+#pragma unroll
+      for (int i = 0; i + 1 < K; ++i) {
+        e[i] = e[i + 1];
+        g0[i] = g0[i + 1];
+        g1[i] = g1[i + 1];
+      }
+      n = K - 1;
     }
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      if (i == n) {
+        e[i] = e0;
+        g0[i] = a;
+        g1[i] = b;
+      }
+    n = n + 1;
+  }
+  __device__ __forceinline__ void check(float* gbar, const WriteWindow& w) {
+    window_wait(w, [&]() { flush(gbar); });
   }
 };
 
@@ -346,19 +399,19 @@ struct HeldTiles {
 // calling hook() after every kBatch / CHK replica loads of the stream, at
 // wave-uniform points between loads.  The windowed flat kernel checks the
 // device clock there.  Same loads, same rank-ordered adds as reduce_replicas.
-template <int NT, int CHK, class GP, class HOOK>
+template <int NT, int CHK, int FMT = kBF16, class GP, class HOOK>
 __device__ __forceinline__ void reduce_replicas_hooked(GP G, uint32_t e, float (&acc)[8], HOOK&& hook) {
   static_assert(NT > 0 && kBatch % CHK == 0, "templated replica count, CHK divides the batch");
   {
     const u32x4 w = ld_grad<true>(G, 0, e);
-    acc[0] = bf_lo(w.x);
-    acc[1] = bf_hi(w.x);
-    acc[2] = bf_lo(w.y);
-    acc[3] = bf_hi(w.y);
-    acc[4] = bf_lo(w.z);
-    acc[5] = bf_hi(w.z);
-    acc[6] = bf_lo(w.w);
-    acc[7] = bf_hi(w.w);
+    acc[0] = h_lo<FMT>(w.x);
+    acc[1] = h_hi<FMT>(w.x);
+    acc[2] = h_lo<FMT>(w.y);
+    acc[3] = h_hi<FMT>(w.y);
+    acc[4] = h_lo<FMT>(w.z);
+    acc[5] = h_hi<FMT>(w.z);
+    acc[6] = h_lo<FMT>(w.w);
+    acc[7] = h_hi<FMT>(w.w);
   }
   constexpr int NB = (NT - 1 + kBatch - 1) / kBatch;
   if constexpr (NB == 0) {
@@ -383,7 +436,7 @@ __device__ __forceinline__ void reduce_replicas_hooked(GP G, uint32_t e, float (
       __builtin_amdgcn_sched_barrier(0);
       hook();
       __builtin_amdgcn_sched_barrier(0);
-      add_batch<kBF16>(acc, w[k & 1], 1 + k * kBatch, NT);
+      add_batch<FMT>(acc, w[k & 1], 1 + k * kBatch, NT);
       __builtin_amdgcn_sched_barrier(0);
     }
   }

@@ -22,10 +22,15 @@ struct TwoPassShape {
   int32_t n_rep;
   float inv_scale;
   const double* scale_dev;  // if set, the loss scale is read here on the device and inv_scale is unused
+  WriteWindow window;       // write windows of pass 1 (period_mask == 0: none)
 };
 
 // Per-tile norm partials summed by one first-stage workgroup.
 constexpr int64_t kFinalSeg = 4096;
+// Windowed pass 1: finished tiles' means held per wave, and the fewest whole
+// 2048-parameter tiles for which a shard takes it (2^25 parameters).
+constexpr int kHeldMeans = 4;
+constexpr int64_t kReduceWindowMinTiles = 16384;
 
 hipError_t launch_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int grad_format, int blocks,
                          hipStream_t stream);

@@ -18,6 +18,8 @@
 //
 // Bytes per parameter: pass 1 reads 2N and writes 4; pass 2 reads 4 + 12 and
 // writes 12 + 2: (2N + 34) in all, against (2N + 26) for the fused step.
+#include <atomic>
+
 #include "zs_device.h"
 #include "zs_twopass.h"
 
@@ -69,6 +71,37 @@ __device__ __forceinline__ float elem_mean(GP G, int N, int64_t i, float inv) {
   return (acc / (float)N) * inv;
 }
 
+// The tile at e0 element by element (a partial tile, or a shard without a
+// common alignment): thread t takes elements e0 + 8t .. e0 + 8t + 7; returns
+// the thread's sum of squares.
+template <int FMT, class GP>
+__device__ __forceinline__ double elem_tile(GP G0, int N, int64_t e0, int64_t n, float inv, float* gbar) {
+  double sq = 0.0;
+  const int64_t lo = e0 + 8 * (int64_t)threadIdx.x;
+  for (int k = 0; k < 8; ++k) {
+    const int64_t i = lo + k;
+    if (i < n && i < e0 + kTile) {
+      const float g = elem_mean<FMT>(G0, N, i, inv);
+      gbar[i] = g;
+      sq += (double)g * (double)g;
+    }
+  }
+  return sq;
+}
+
+// The head elements (before the first tile) and their partial, slot ntiles.
+template <int NT, int FMT, class GP>
+__device__ __forceinline__ void head_partial(const ReduceArgs<NT>& a, GP G0, int N, float inv, double* lds4) {
+  double sq = 0.0;
+  if (threadIdx.x < a.head) {
+    const float g = elem_mean<FMT>(G0, N, threadIdx.x, inv);
+    a.gbar[threadIdx.x] = g;
+    sq = (double)g * (double)g;
+  }
+  sq = block_sum(sq, lds4);
+  if (threadIdx.x == 0) a.partials[a.ntiles] = sq;
+}
+
 template <int NT, int FMT>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs<NT> a) {
   __shared__ double lds4[4];
@@ -96,29 +129,58 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs<NT> a) 
       for (int k = 0; k < 8; ++k) sq += (double)g[k] * (double)g[k];
     } else {
       // partial tile, or a shard without a common alignment: element by element
-      const int64_t lo = e0 + 8 * (int64_t)threadIdx.x;
-      for (int k = 0; k < 8; ++k) {
-        const int64_t i = lo + k;
-        if (i < a.n && i < e0 + kTile) {
-          const float g = elem_mean<FMT>(G0, N, i, inv);
-          a.gbar[i] = g;
-          sq += (double)g * (double)g;
-        }
-      }
+      sq = elem_tile<FMT>(G0, N, e0, a.n, inv, a.gbar);
     }
     sq = block_sum(sq, lds4);
     if (threadIdx.x == 0) a.partials[t] = sq;
   }
-  if (blockIdx.x == 0) {
+  if (blockIdx.x == 0) head_partial<NT, FMT>(a, G0, N, inv, lds4);
+}
+
+// Pass 1 with its mean-gradient writes grouped in device-clock windows, as
+// the windowed flat step groups its write-back (see flat_window_kernel):
+// persistent workgroups hold the means of up to kHeldMeans finished tiles
+// per wave and store them while the window is open, issuing no loads then.
+// The norm partials are the same per-tile fixed-order sums as reduce_kernel's
+// (written as each tile finishes: 8 bytes per 2048 parameters), so the
+// norm, like the means, is the same bits.  Full tiles only in the loop; the
+// partial tile and the head follow, unwindowed.
+template <int NT, int FMT>
+__global__ __launch_bounds__(kBlock) void reduce_window_kernel(const ReduceArgs<NT> a, const WriteWindow w) {
+  static_assert(NT > 0, "templated replica counts only");
+  __shared__ double lds4[4];
+  Scalars c{};
+  c.n_rep = NT;
+  const float inv = unscale_factor(a);
+  auto G0 = [&](int r) { return a.g[r]; };
+  const int64_t full = (a.n - a.head) / kTile;  // whole tiles (the shard has a common alignment)
+  const uint32_t e = Layout<true>::first();
+  HeldMeans<kHeldMeans> held;
+  auto check = [&]() { held.check(a.gbar, w); };
+  for (int64_t t = blockIdx.x; t < full; t += gridDim.x) {
+    const int64_t e0 = a.head + t * kTile;
+    auto G = [&](int r) { return tile_base(G0(r) + e0); };
+    float acc[8];
+    reduce_replicas_hooked<NT, kWindowChecks, FMT>(G, e, acc, check);
+    float g[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) g[k] = mean_of<NT>(acc[k], c) * inv;
     double sq = 0.0;
-    if (threadIdx.x < a.head) {
-      const float g = elem_mean<FMT>(G0, N, threadIdx.x, inv);
-      a.gbar[threadIdx.x] = g;
-      sq = (double)g * (double)g;
-    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sq += (double)g[k] * (double)g[k];
+    held.push(a.gbar, e0, (f32x4){g[0], g[1], g[2], g[3]}, (f32x4){g[4], g[5], g[6], g[7]});
     sq = block_sum(sq, lds4);
-    if (threadIdx.x == 0) a.partials[a.ntiles] = sq;
+    if (threadIdx.x == 0) a.partials[t] = sq;
   }
+  held.flush(a.gbar);
+  if (blockIdx.x == gridDim.x - 1) {
+    for (int64_t t = full; t < a.ntiles; ++t) {
+      double sq = elem_tile<FMT>(G0, NT, a.head + t * kTile, a.n, inv, a.gbar);
+      sq = block_sum(sq, lds4);
+      if (threadIdx.x == 0) a.partials[t] = sq;
+    }
+  }
+  if (blockIdx.x == 0) head_partial<NT, FMT>(a, G0, NT, inv, lds4);
 }
 
 // First stage of the norm: workgroup b takes partials [b*kFinalSeg,
@@ -242,6 +304,24 @@ __global__ __launch_bounds__(kBlock) void gbar_kernel(const GbarArgs a) {
   }
 }
 
+// Workgroups of reduce_window_kernel<NT, FMT> that fit on the current device
+// at once (compute units x resident workgroups per unit), cached per device.
+template <int NT, int FMT>
+int reduce_resident_grid() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int g = cache[dev].load(std::memory_order_relaxed);
+  if (g > 0) return g;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reduce_window_kernel<NT, FMT>, kBlock, 0) != hipSuccess)
+    return 0;
+  g = cus * per_cu;
+  if (g > 0) cache[dev].store(g, std::memory_order_relaxed);
+  return g;
+}
+
 template <int NT, int FMT>
 hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int blocks, hipStream_t stream) {
   (void)hipGetLastError();
@@ -260,10 +340,25 @@ hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int b
   a.n_rep = sh.n_rep;
   a.inv_scale = sh.inv_scale;
   a.scale_dev = sh.scale_dev;
-  int grid = (int)(sh.ntiles < blocks ? sh.ntiles : blocks);
-  if (grid < 1) grid = 1;
-  (void)hipGetLastError();
-  reduce_kernel<NT, FMT><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
+  bool windowed = false;
+  if constexpr (NT > 0) {
+    // windowed: shards of many whole tiles, when a window is set
+    if (sh.window.period_mask != 0 && !sh.scalar_only && (sh.n - sh.head) / kTile >= kReduceWindowMinTiles) {
+      int grid = reduce_resident_grid<NT, FMT>();
+      if (grid > 0) {
+        if (blocks < grid) grid = blocks;
+        (void)hipGetLastError();
+        reduce_window_kernel<NT, FMT><<<dim3(grid), dim3(kBlock), 0, stream>>>(a, sh.window);
+        windowed = true;
+      }
+    }
+  }
+  if (!windowed) {
+    int grid = (int)(sh.ntiles < blocks ? sh.ntiles : blocks);
+    if (grid < 1) grid = 1;
+    (void)hipGetLastError();
+    reduce_kernel<NT, FMT><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the norm: tile partials -> one sum per kFinalSeg of them -> the total, in a fixed order

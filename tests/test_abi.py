@@ -303,22 +303,29 @@ def test_probe_library_rejects_unsupported_arguments_without_gpu():
     assert fw(g, 2, 1 << 20, A + 0x400004, *arr[1:], 4096, 512, None) == 1
 
 
-def test_flat_write_window_query():
-    """The query reports the window the flat step takes: the N = 64 default on shards of at least
-    65,536 whole tiles, none below that, for other replica counts, or when windows are switched off."""
-    assert zs.flat_write_window(64, 1_093_750_000) == (4096, 512)
-    assert zs.flat_write_window(64, 65536 * 512) == (4096, 512)
-    assert zs.flat_write_window(64, 65536 * 512 - 1) == (0, 0)
-    assert zs.flat_write_window(8, 124_000_000) == (0, 0)
-    assert zs.flat_write_window(3, 1 << 30) == (0, 0)
-    zs.set_write_window(1)
-    assert zs.flat_write_window(64, 1 << 30) == (0, 0)
-    zs.set_write_window(1024, 128)
-    assert zs.flat_write_window(16, 1 << 30) == (1024, 128)
-    assert zs.flat_write_window(5, 1 << 30) == (0, 0)   # runtime replica counts take the one-tile kernel
-    zs.set_write_window(0)
+def test_write_window_query():
+    """The query reports the window each kernel takes: the N = 64 defaults on shards of at least
+    2^25 parameters, none below that, for other replica counts, or when windows are switched off."""
+    for kernel, default in (("flat", (4096, 512)), ("reduce", (4096, 256))):
+        assert zs.write_window(kernel, 64, 1_093_750_000) == default
+        assert zs.write_window(kernel, 64, 1 << 25) == default
+        assert zs.write_window(kernel, 64, (1 << 25) - 1) == (0, 0)
+        assert zs.write_window(kernel, 8, 124_000_000) == (0, 0)
+        assert zs.write_window(kernel, 3, 1 << 30) == (0, 0)
+        zs.set_write_window(1)
+        assert zs.write_window(kernel, 64, 1 << 30) == (0, 0)
+        zs.set_write_window(1024, 128)
+        assert zs.write_window(kernel, 16, 1 << 30) == (1024, 128)
+        assert zs.write_window(kernel, 5, 1 << 30) == (0, 0)   # runtime replica counts: no windows
+        zs.set_write_window(0)
     with pytest.raises(zs.ZShardError):
-        zs.flat_write_window(0, 1 << 20)
+        zs.write_window("flat", 0, 1 << 20)
+    lib = ctypes.CDLL(zs.LIB_PATH)
+    lib.zs_write_window.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    p, o = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.zs_write_window(2, 64, 1 << 30, ctypes.byref(p), ctypes.byref(o)) == 2   # unknown kernel
+    assert lib.zs_write_window(0, 64, 1 << 30, None, ctypes.byref(o)) == 1
 
 
 def test_device_scaler_entry_points_reject_bad_arguments_without_gpu():

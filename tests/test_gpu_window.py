@@ -10,6 +10,8 @@ as both slots are full), and a forced small grid (many tiles per wave) must
 give every output bit-identical to the oracle: the schedule of the stores
 cannot change what is stored.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -99,3 +101,49 @@ def test_windowed_device_step(env, orc):
     got = dict(P=a["P"].cpu().numpy(), M=a["M"].cpu().numpy(), V=a["V"].cpu().numpy(),
                B=a["B"].cpu().numpy().view(np.uint16))
     assert parity.bit_identical(got, dict(P=P, M=M, V=V, B=B))
+
+
+@pytest.mark.parametrize("N,fmt,scale", [(64, "bf16", 1.0), (8, "fp16", 256.0)])
+def test_windowed_pass1_matches_unwindowed_and_oracle(env, orc, N, fmt, scale):
+    """Pass 1 of the two-pass form under write windows: the mean gradients bit-identical to the
+    oracle's and the squared norm bit-identical to the unwindowed pass (the same fixed-order tile
+    partials), for every window setting and grid; then pass 2 from it against the oracle.  The shard
+    has 16,385 whole 2048-parameter tiles after the head, past the 16,384-tile threshold."""
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    w, host = _inputs(N, 40, 0.0)
+    n = N_PARAMS
+    d = _upload(torch, dev, host)
+    ws = torch.empty(zs.two_pass_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    start = (256 - ws.data_ptr() % 256) % 256
+    fmt_id = 1 if fmt == "fp16" else 0
+    ref_g = orc.reduce_unscale(host["G"], fmt_id, scale)
+    # the norm's definition, summed exactly: over 2^25 terms a plain sequential double sum (the
+    # oracle's) drifts by up to n*u, more than the GPU's fixed-order tree (a chain of about 50 adds
+    # of exact squares, so within 50u); 1e-13 is far below what one dropped or doubled tile moves
+    ref_sq = math.fsum((ref_g.astype(np.float64) ** 2).tolist())
+    results = []
+    for blocks in (0, 37):
+        zs.set_grid_blocks(blocks)
+        for period, open_ticks in [(1, 0), (0, 0), (256, 32), (64, 63), (1 << 20, 1), (4096, 256)]:
+            zs.set_write_window(period, open_ticks)
+            print(f"windowed pass 1: N={N} {fmt} n={n} blocks={blocks} window={period}/{open_ticks} "
+                  f"(takes {zs.write_window('reduce', N, n)})", flush=True)
+            ws.fill_(0xFF)   # NaN everywhere the pass does not write
+            sq = torch.full((1,), float("nan"), dtype=torch.float64, device=dev)
+            zs.reduce_grads_flat(d["G"], ws, sq, scale, fmt)
+            torch.cuda.synchronize()
+            g = ws[start:start + 4 * n].cpu().numpy().view(np.float32)
+            assert np.array_equal(g.view(np.uint32), ref_g.view(np.uint32)), f"{period}/{open_ticks}: means"
+            results.append(sq.item())
+    zs.set_grid_blocks(0)
+    zs.set_write_window(0)
+    assert len(set(results)) == 1, results
+    assert abs(results[0] - ref_sq) <= 1e-13 * ref_sq, (results[0], ref_sq)
+    zs.adam_from_grads_flat(ws, n, d["P"], d["M"], d["V"], d["B"], w.hp(), w.step, sq, 1.0, "bf16")
+    torch.cuda.synchronize()
+    P1, M1, V1, B1, taken = orc.adam_from_gbar(ref_g, host["P"], host["M"], host["V"], w.hp(), w.step,
+                                               results[0], 1.0)
+    assert taken
+    got = dict(P=d["P"].cpu().numpy(), M=d["M"].cpu().numpy(), V=d["V"].cpu().numpy(),
+               B=d["B"].cpu().numpy().view(np.uint16))
+    assert parity.bit_identical(got, dict(P=P1, M=M1, V=V1, B=B1))
