@@ -147,3 +147,48 @@ def test_windowed_pass1_matches_unwindowed_and_oracle(env, orc, N, fmt, scale):
     got = dict(P=d["P"].cpu().numpy(), M=d["M"].cpu().numpy(), V=d["V"].cpu().numpy(),
                B=d["B"].cpu().numpy().view(np.uint16))
     assert parity.bit_identical(got, dict(P=P1, M=M1, V=V1, B=B1))
+
+
+def test_windowed_kernels_in_a_graph(env, orc):
+    """The windowed flat step and the windowed pass 1, captured in HIP graphs and replayed: every
+    replay equals the same call run eagerly (with eager work and synchronisation between replays)."""
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    w, host = _inputs(2, 9, 0.0)
+    zs.set_write_window(256, 32)
+    try:
+        a, b = _upload(torch, dev, host), _upload(torch, dev, host)
+        ws_a = torch.empty(zs.two_pass_workspace_bytes(N_PARAMS), dtype=torch.uint8, device=dev)
+        ws_b = torch.empty_like(ws_a)
+        sq_a = torch.empty(1, dtype=torch.float64, device=dev)
+        sq_b = torch.empty_like(sq_a)
+        assert zs.write_window("flat", 2, N_PARAMS) == (256, 32)
+        assert zs.write_window("reduce", 2, N_PARAMS) == (256, 32)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # first calls outside capture settle the one-time occupancy queries
+            zs.reduce_adam_flat(a["G"], a["P"], a["M"], a["V"], a["B"], w.hp(), w.step)
+            zs.reduce_grads_flat(a["G"], ws_a, sq_a)
+        torch.cuda.current_stream().wait_stream(side)
+        zs.reduce_adam_flat(b["G"], b["P"], b["M"], b["V"], b["B"], w.hp(), w.step)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            zs.reduce_adam_flat(a["G"], a["P"], a["M"], a["V"], a["B"], w.hp(), w.step)
+            zs.reduce_grads_flat(a["G"], ws_a, sq_a)
+        for replay in range(3):
+            print(f"windowed kernels in a graph: replay {replay}", flush=True)
+            ws_a.fill_(0)
+            ws_b.fill_(0xFF)
+            sq_a.fill_(-1.0)
+            graph.replay()
+            zs.reduce_adam_flat(b["G"], b["P"], b["M"], b["V"], b["B"], w.hp(), w.step)
+            zs.reduce_grads_flat(b["G"], ws_b, sq_b)
+            torch.cuda.synchronize()
+            for k in ("P", "M", "V", "B"):
+                assert torch.equal(a[k], b[k]), f"replay {replay}: {k}"
+            sa = (256 - ws_a.data_ptr() % 256) % 256
+            sb = (256 - ws_b.data_ptr() % 256) % 256
+            assert torch.equal(ws_a[sa:sa + 4 * N_PARAMS], ws_b[sb:sb + 4 * N_PARAMS]), f"replay {replay}: means"
+            assert sq_a.item() == sq_b.item(), f"replay {replay}: norm"
+    finally:
+        zs.set_write_window(0)
