@@ -53,11 +53,15 @@ def workload(name: str):
 
 
 def kernel_hash() -> str:
-    """Hash of the sources the step kernels are built from."""
+    """Hash of the sources the step kernels are built from, comments and blank space left out (an
+    edit to a comment does not make a counter summary stale)."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -32,6 +32,11 @@
 //    shards whose arrays share no common alignment go through a per-element
 //    path with the identical operation sequence (same inline function), so
 //    results do not depend on alignment, grid size or path.
+//  * Large flat shards at N = 64 run flat_window_kernel instead: the same
+//    tiles and arithmetic, with the write-back held in registers and stored
+//    in short device-clock windows, so the memory system sees read-only and
+//    write-only phases instead of the two interleaved (see "write windows"
+//    below).
 //
 // Arithmetic: see include/zshard.h.  Built with -ffp-contract=off (no FMA
 // contraction) and correctly rounded fp32 divide and sqrt; fp32 denormals are
