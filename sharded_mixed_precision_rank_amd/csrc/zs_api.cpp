@@ -20,9 +20,10 @@ namespace {
 
 thread_local std::string g_last_error;
 std::atomic<int32_t> g_grid_blocks{0};
-// zs_set_write_window: period 0 = automatic, 1 = no windows
-std::atomic<int32_t> g_window_period{0};
-std::atomic<int32_t> g_window_open{0};
+// zs_set_write_window: (period << 32) | open, one word so a reader never pairs
+// one call's period with another's open length; period 0 = automatic, 1 = no
+// windows
+std::atomic<uint64_t> g_window{0};
 
 zs_status fail(zs_status st, const char* fmt, ...) {
   char buf[512];
@@ -180,8 +181,8 @@ int auto_blocks() {
 // 100 MHz device clock (period / open): N = 64: 4096 / 512, about 41 us with
 // 5 us of writes.
 zs::WriteWindow write_window(int32_t N) {
-  const int32_t period = g_window_period.load(std::memory_order_relaxed);
-  const int32_t open = g_window_open.load(std::memory_order_relaxed);
+  const uint64_t word = g_window.load(std::memory_order_relaxed);
+  const int32_t period = (int32_t)(word >> 32), open = (int32_t)(word & 0xFFFFFFFFu);
   if (period == 1) return zs::WriteWindow{0, 0};
   if (period > 1) return zs::WriteWindow{(uint64_t)period - 1, (uint64_t)open};
   if (N == 64) return zs::WriteWindow{4096 - 1, 512};
@@ -191,8 +192,8 @@ zs::WriteWindow write_window(int32_t N) {
 // The same for pass 1 of the two-pass form (which writes 4 bytes per
 // parameter beside 2N read).  Default: N = 64: 4096 / 256.
 zs::WriteWindow reduce_write_window(int32_t N) {
-  const int32_t period = g_window_period.load(std::memory_order_relaxed);
-  const int32_t open = g_window_open.load(std::memory_order_relaxed);
+  const uint64_t word = g_window.load(std::memory_order_relaxed);
+  const int32_t period = (int32_t)(word >> 32), open = (int32_t)(word & 0xFFFFFFFFu);
   if (period == 1) return zs::WriteWindow{0, 0};
   if (period > 1) return zs::WriteWindow{(uint64_t)period - 1, (uint64_t)open};
   if (N == 64) return zs::WriteWindow{4096 - 1, 256};
@@ -440,8 +441,7 @@ zs_status zs_set_grid_blocks(int32_t blocks) {
 zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks) {
   g_last_error.clear();
   if (period_ticks == 0 || period_ticks == 1) {
-    g_window_period.store(period_ticks, std::memory_order_relaxed);
-    g_window_open.store(0, std::memory_order_relaxed);
+    g_window.store((uint64_t)period_ticks << 32, std::memory_order_relaxed);
     return ZS_OK;
   }
   if (period_ticks < zs::kWindowMinPeriod || period_ticks > zs::kWindowMaxPeriod ||
@@ -451,8 +451,7 @@ zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks) {
   if (open_ticks < 1 || open_ticks >= period_ticks || open_ticks > zs::kWindowMaxOpen)
     return fail(ZS_ERR_RANGE, "open_ticks must be in [1, min(period_ticks - 1, %d)] (got %d)", zs::kWindowMaxOpen,
                 open_ticks);
-  g_window_open.store(open_ticks, std::memory_order_relaxed);
-  g_window_period.store(period_ticks, std::memory_order_relaxed);
+  g_window.store(((uint64_t)period_ticks << 32) | (uint32_t)open_ticks, std::memory_order_relaxed);
   return ZS_OK;
 }
 
