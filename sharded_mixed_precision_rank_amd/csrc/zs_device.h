@@ -397,8 +397,8 @@ struct HeldMeans {
 
 // reduce_replicas for a templated replica count on a full tile (split layout),
 // calling hook() after every kBatch / CHK replica loads of the stream, at
-// wave-uniform points between loads.  The windowed flat kernel checks the
-// device clock there.  Same loads, same rank-ordered adds as reduce_replicas.
+// wave-uniform points between loads.  The windowed kernels (the flat step and
+// pass 1 of the two-pass form) check the device clock there.  Same loads, same rank-ordered adds as reduce_replicas.
 template <int NT, int CHK, int FMT = kBF16, class GP, class HOOK>
 __device__ __forceinline__ void reduce_replicas_hooked(GP G, uint32_t e, float (&acc)[8], HOOK&& hook) {
   static_assert(NT > 0 && kBatch % CHK == 0, "templated replica count, CHK divides the batch");
