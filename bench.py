@@ -367,6 +367,21 @@ def main() -> int:
 
     # the write window the flat step took (0, 0: none) and so the kernel that ran
     window = (0, 0) if w.is_list or offload is not None else zs.write_window("reduce" if two_pass else "flat", w.N, n)
+    unwindowed = None
+    if window[0]:
+        # the same steps with the windows switched off, in this process: the windows' own effect
+        zs.set_write_window(1)
+        step(w.step)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        e[0].record()
+        for k in range(5):
+            step(w.step + 1 + k)
+            e[k + 1].record()
+        torch.cuda.synchronize()
+        zs.set_write_window(0)
+        gaps = sorted(e[k].elapsed_time(e[k + 1]) for k in range(5))
+        unwindowed = {"ms_per_step_median": gaps[2], "steps": 5}
+        log(f"without write windows: {gaps[2]:.3f} ms/step (median of 5)")
     tn = f"<{w.N}>" if w.N in (1, 2, 4, 8, 16, 32, 64) else "<0>"
     if w.is_list:
         kernel = "list_kernel" + tn
@@ -412,6 +427,7 @@ def main() -> int:
         "hbm_GBps": achieved, "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,
         "copy_ceiling_GBps": ceiling,
         "pattern_ceiling": pattern,
+        "without_write_windows": unwindowed,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic if args.path == "fused" else None,
                      "bytes_per_param": bpp, "kernel": kernel},
