@@ -395,7 +395,9 @@ ZS_API zs_status zs_set_grid_blocks(int32_t blocks);
      otherwise a power of two in [64, 2^20], with 1 <= open_ticks < period_ticks
      and open_ticks <= 2^14.
    A wave waits at most the window's length, and never more than about 0.2 ms
-   (a fixed number of sleeps), whatever the clock does.
+   (a fixed number of sleeps), whatever the clock does.  Other work running on
+   the device at the same time is not paused: the windows then group only this
+   kernel's writes.
    Errors: ZS_ERR_RANGE. */
 ZS_API zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks);
 
