@@ -382,15 +382,18 @@ ZS_API zs_status zs_set_grid_blocks(int32_t blocks);
    writes 14 bytes per parameter back beside 2N + 12 read, pass 1 writes 4
    beside 2N; on this memory system the writes cost far less when grouped in
    time than when they trickle out beside the read streams.  On shards of at
-   least 2^25 parameters and a replica count of 1, 2, 4, 8, 16, 32 or 64, the
-   kernel then runs as persistent workgroups that hold finished tiles in
-   registers and store them while the device's 100 MHz real-time counter,
-   taken modulo period_ticks, is below open_ticks; no loads are issued in that
-   window.  Results do not depend on the setting: each tile's outputs are
+   least 2^25 parameters, the kernel then runs as persistent workgroups that
+   hold finished tiles in registers and store them while the device's 100 MHz
+   real-time counter, taken modulo period_ticks, is below open_ticks; no loads
+   are issued in that window.  Results do not depend on the setting: each tile's outputs are
    computed identically and written to their own addresses (pass 1's norm
    partials too).
-     period_ticks = 0: the library's measured default for each kernel and
-                       replica count (the default; open_ticks is ignored);
+     period_ticks = 0: the library's measured default (the default;
+                       open_ticks is ignored): for N >= 48 replicas a
+                       4096-tick period with 640 (N < 64), 512 (N <= 128) or
+                       384 ticks open for the flat step and 256 for pass 1;
+                       no windows below 48 replicas, where the writes are too
+                       large a share of the bytes for them to pay;
      period_ticks = 1: no windows (tiles stored as they finish);
      otherwise a power of two in [64, 2^20], with 1 <= open_ticks < period_ticks
      and open_ticks <= 2^14.

@@ -178,26 +178,28 @@ int auto_blocks() {
 
 // The flat step's write window for N replicas: the one set by
 // zs_set_write_window, else the measured default.  Defaults, in ticks of the
-// 100 MHz device clock (period / open): N = 64: 4096 / 512, about 41 us with
-// 5 us of writes.
+// 100 MHz device clock (period / open), for a 4096-tick (41 us) period: open
+// 640 for 48 <= N < 64, 512 for 64 <= N <= 128, 384 above (the writes' share
+// of the bytes shrinks as N grows).  Below 48 replicas the writes are too
+// large a share for windows to pay, and the step stores as it goes.
 zs::WriteWindow write_window(int32_t N) {
   const uint64_t word = g_window.load(std::memory_order_relaxed);
   const int32_t period = (int32_t)(word >> 32), open = (int32_t)(word & 0xFFFFFFFFu);
   if (period == 1) return zs::WriteWindow{0, 0};
   if (period > 1) return zs::WriteWindow{(uint64_t)period - 1, (uint64_t)open};
-  if (N == 64) return zs::WriteWindow{4096 - 1, 512};
-  return zs::WriteWindow{0, 0};
+  if (N < 48) return zs::WriteWindow{0, 0};
+  return zs::WriteWindow{4096 - 1, N < 64 ? 640u : N <= 128 ? 512u : 384u};
 }
 
 // The same for pass 1 of the two-pass form (which writes 4 bytes per
-// parameter beside 2N read).  Default: N = 64: 4096 / 256.
+// parameter beside 2N read).  Default for N >= 48: 4096 / 256.
 zs::WriteWindow reduce_write_window(int32_t N) {
   const uint64_t word = g_window.load(std::memory_order_relaxed);
   const int32_t period = (int32_t)(word >> 32), open = (int32_t)(word & 0xFFFFFFFFu);
   if (period == 1) return zs::WriteWindow{0, 0};
   if (period > 1) return zs::WriteWindow{(uint64_t)period - 1, (uint64_t)open};
-  if (N == 64) return zs::WriteWindow{4096 - 1, 256};
-  return zs::WriteWindow{0, 0};
+  if (N < 48) return zs::WriteWindow{0, 0};
+  return zs::WriteWindow{4096 - 1, 256};
 }
 
 zs_status after_launch(hipError_t e, hipStream_t stream, const char* what) {
@@ -464,10 +466,9 @@ zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* period_
   if (n < 0) return fail(ZS_ERR_RANGE, "n must be >= 0");
   const bool flat = kernel == ZS_WINDOW_FLAT_STEP;
   const zs::WriteWindow w = flat ? write_window(N) : reduce_write_window(N);
-  const bool templated = N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64;
   const bool big = flat ? n / 8 / zs::kFlatBlock >= zs::kWindowMinTiles
                         : n / kTileElems >= zs::kReduceWindowMinTiles;
-  const bool used = w.period_mask != 0 && templated && big;
+  const bool used = w.period_mask != 0 && big;
   *period_ticks = used ? (int32_t)(w.period_mask + 1) : 0;
   *open_ticks = used ? (int32_t)w.open_ticks : 0;
   return ZS_OK;

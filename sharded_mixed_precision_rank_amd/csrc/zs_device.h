@@ -442,5 +442,42 @@ __device__ __forceinline__ void reduce_replicas_hooked(GP G, uint32_t e, float (
   }
 }
 
+// The same for a replica count known only at run time (1 <= N): replicas
+// 1..N-1 stream in double-buffered batches of kBatch as in reduce_replicas,
+// with hook() after each batch's loads are issued.
+template <int FMT = kBF16, class GP, class HOOK>
+__device__ __forceinline__ void reduce_replicas_hooked_rt(GP G, int N, uint32_t e, float (&acc)[8], HOOK&& hook) {
+  {
+    const u32x4 w = ld_grad<true>(G, 0, e);
+    acc[0] = h_lo<FMT>(w.x);
+    acc[1] = h_hi<FMT>(w.x);
+    acc[2] = h_lo<FMT>(w.y);
+    acc[3] = h_hi<FMT>(w.y);
+    acc[4] = h_lo<FMT>(w.z);
+    acc[5] = h_hi<FMT>(w.z);
+    acc[6] = h_lo<FMT>(w.w);
+    acc[7] = h_hi<FMT>(w.w);
+  }
+  u32x4 wa[kBatch], wb[kBatch];
+  if (N > 1) load_batch<true>(G, 1, N, e, wa);
+  hook();
+#pragma unroll 1
+  for (int r0 = 1; r0 < N; r0 += 2 * kBatch) {
+    const int r1 = r0 + kBatch, r2 = r1 + kBatch;
+    if (r1 < N) load_batch<true>(G, r1, N, e, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    hook();
+    __builtin_amdgcn_sched_barrier(0);
+    add_batch<FMT>(acc, wa, r0, N);
+    __builtin_amdgcn_sched_barrier(0);
+    if (r2 < N) load_batch<true>(G, r2, N, e, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    hook();
+    __builtin_amdgcn_sched_barrier(0);
+    if (r1 < N) add_batch<FMT>(acc, wb, r1, N);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 }  // namespace dev
 }  // namespace zs

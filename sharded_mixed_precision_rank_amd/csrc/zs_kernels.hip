@@ -185,9 +185,9 @@ __global__ __launch_bounds__(kFlatBlock) void flat_kernel(const FlatArgs<NT> a) 
 
 template <int NT>
 __global__ __launch_bounds__(kFlatBlock) void flat_window_kernel(const FlatArgs<NT> a, const WriteWindow w) {
-  static_assert(NT > 0, "templated replica counts only");
   Scalars c = a.c;
   if (!step_scalars(a.r, c)) return;
+  const int N = NT > 0 ? NT : c.n_rep;
   const FlatShape& s = a.s;
   constexpr uint32_t q2 = Layout<true>::kSecond / 4;
   const uint32_t e = Layout<true>::first();
@@ -211,7 +211,10 @@ __global__ __launch_bounds__(kFlatBlock) void flat_window_kernel(const FlatArgs<
     }
     auto G = [&](int r) { return tile_base(a.g[r] + e0); };
     float acc[8];
-    reduce_replicas_hooked<NT, kWindowChecks>(G, e, acc, check);
+    if constexpr (NT > 0)
+      reduce_replicas_hooked<NT, kWindowChecks>(G, e, acc, check);
+    else
+      reduce_replicas_hooked_rt(G, N, e, acc, check);
     float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
     float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
     float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
@@ -224,7 +227,6 @@ __global__ __launch_bounds__(kFlatBlock) void flat_window_kernel(const FlatArgs<
   if (blockIdx.x == gridDim.x - 1) {
     const int64_t gt = full * kFlatBlock;
     const int64_t e0 = s.head + 8 * gt;
-    const int N = NT;
     if (gt + threadIdx.x < s.nvec) {
       auto G = [&](int r) { return tile_base(a.g[r] + e0); };
       group_step<NT, false>(G, N, e0, s, c);
@@ -346,18 +348,16 @@ hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scala
   a.s = s;
   a.c = c;
   a.r = ref;
-  if constexpr (NT > 0) {
-    // windowed: shards of many whole tiles, when a window is set
-    if (win.period_mask != 0 && !s.scalar_only && s.nvec / kFlatBlock >= kWindowMinTiles) {
-      int grid = resident_grid<NT>();
-      if (grid > 0) {
-        if (blocks < grid) grid = blocks;
-        (void)hipGetLastError();
-        flat_window_kernel<NT><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(a, win);
-        return hipGetLastError();
-      }
-      (void)hipGetLastError();  // no occupancy figure: take the one-tile kernel
+  // windowed: shards of many whole tiles, when a window is set
+  if (win.period_mask != 0 && !s.scalar_only && s.nvec / kFlatBlock >= kWindowMinTiles) {
+    int grid = resident_grid<NT>();
+    if (grid > 0) {
+      if (blocks < grid) grid = blocks;
+      (void)hipGetLastError();
+      flat_window_kernel<NT><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(a, win);
+      return hipGetLastError();
     }
+    (void)hipGetLastError();  // no occupancy figure: take the one-tile kernel
   }
   const int grid = clamp_grid(blocks, s.scalar_only ? s.n : s.nvec);
   (void)hipGetLastError();

@@ -147,10 +147,10 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs<NT> a) 
 // partial tile and the head follow, unwindowed.
 template <int NT, int FMT>
 __global__ __launch_bounds__(kBlock) void reduce_window_kernel(const ReduceArgs<NT> a, const WriteWindow w) {
-  static_assert(NT > 0, "templated replica counts only");
   __shared__ double lds4[4];
+  const int N = NT > 0 ? NT : a.n_rep;
   Scalars c{};
-  c.n_rep = NT;
+  c.n_rep = N;
   const float inv = unscale_factor(a);
   auto G0 = [&](int r) { return a.g[r]; };
   const int64_t full = (a.n - a.head) / kTile;  // whole tiles (the shard has a common alignment)
@@ -161,7 +161,10 @@ __global__ __launch_bounds__(kBlock) void reduce_window_kernel(const ReduceArgs<
     const int64_t e0 = a.head + t * kTile;
     auto G = [&](int r) { return tile_base(G0(r) + e0); };
     float acc[8];
-    reduce_replicas_hooked<NT, kWindowChecks, FMT>(G, e, acc, check);
+    if constexpr (NT > 0)
+      reduce_replicas_hooked<NT, kWindowChecks, FMT>(G, e, acc, check);
+    else
+      reduce_replicas_hooked_rt<FMT>(G, N, e, acc, check);
     float g[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) g[k] = mean_of<NT>(acc[k], c) * inv;
@@ -175,12 +178,12 @@ __global__ __launch_bounds__(kBlock) void reduce_window_kernel(const ReduceArgs<
   held.flush(a.gbar);
   if (blockIdx.x == gridDim.x - 1) {
     for (int64_t t = full; t < a.ntiles; ++t) {
-      double sq = elem_tile<FMT>(G0, NT, a.head + t * kTile, a.n, inv, a.gbar);
+      double sq = elem_tile<FMT>(G0, N, a.head + t * kTile, a.n, inv, a.gbar);
       sq = block_sum(sq, lds4);
       if (threadIdx.x == 0) a.partials[t] = sq;
     }
   }
-  if (blockIdx.x == 0) head_partial<NT, FMT>(a, G0, NT, inv, lds4);
+  if (blockIdx.x == 0) head_partial<NT, FMT>(a, G0, N, inv, lds4);
 }
 
 // First stage of the norm: workgroup b takes partials [b*kFinalSeg,
@@ -341,16 +344,14 @@ hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int b
   a.inv_scale = sh.inv_scale;
   a.scale_dev = sh.scale_dev;
   bool windowed = false;
-  if constexpr (NT > 0) {
-    // windowed: shards of many whole tiles, when a window is set
-    if (sh.window.period_mask != 0 && !sh.scalar_only && (sh.n - sh.head) / kTile >= kReduceWindowMinTiles) {
-      int grid = reduce_resident_grid<NT, FMT>();
-      if (grid > 0) {
-        if (blocks < grid) grid = blocks;
-        (void)hipGetLastError();
-        reduce_window_kernel<NT, FMT><<<dim3(grid), dim3(kBlock), 0, stream>>>(a, sh.window);
-        windowed = true;
-      }
+  // windowed: shards of many whole tiles, when a window is set
+  if (sh.window.period_mask != 0 && !sh.scalar_only && (sh.n - sh.head) / kTile >= kReduceWindowMinTiles) {
+    int grid = reduce_resident_grid<NT, FMT>();
+    if (grid > 0) {
+      if (blocks < grid) grid = blocks;
+      (void)hipGetLastError();
+      reduce_window_kernel<NT, FMT><<<dim3(grid), dim3(kBlock), 0, stream>>>(a, sh.window);
+      windowed = true;
     }
   }
   if (!windowed) {

@@ -310,14 +310,20 @@ def test_write_window_query():
         assert zs.write_window(kernel, 64, 1_093_750_000) == default
         assert zs.write_window(kernel, 64, 1 << 25) == default
         assert zs.write_window(kernel, 64, (1 << 25) - 1) == (0, 0)
-        assert zs.write_window(kernel, 8, 124_000_000) == (0, 0)
-        assert zs.write_window(kernel, 3, 1 << 30) == (0, 0)
+        assert zs.write_window(kernel, 8, 124_000_000) == (0, 0)   # below 48 replicas: none by default
+        assert zs.write_window(kernel, 47, 1 << 30) == (0, 0)
+        assert zs.write_window(kernel, 100, 1 << 30) == default     # runtime replica counts too
         zs.set_write_window(1)
         assert zs.write_window(kernel, 64, 1 << 30) == (0, 0)
         zs.set_write_window(1024, 128)
         assert zs.write_window(kernel, 16, 1 << 30) == (1024, 128)
-        assert zs.write_window(kernel, 5, 1 << 30) == (0, 0)   # runtime replica counts: no windows
+        assert zs.write_window(kernel, 5, 1 << 30) == (1024, 128)
         zs.set_write_window(0)
+    # the flat step's open length follows the writes' share of the bytes
+    assert zs.write_window("flat", 48, 1 << 30) == (4096, 640)
+    assert zs.write_window("flat", 128, 1 << 30) == (4096, 512)
+    assert zs.write_window("flat", 129, 1 << 30) == (4096, 384)
+    assert zs.write_window("flat", 256, 1 << 30) == (4096, 384)
     with pytest.raises(zs.ZShardError):
         zs.write_window("flat", 0, 1 << 20)
     lib = ctypes.CDLL(zs.LIB_PATH)

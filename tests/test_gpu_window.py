@@ -3,7 +3,8 @@ finished tiles and store them in device-clock windows) against the CPU oracle.
 
 The shards are just above the size at which the library takes the windowed
 kernel (65,536 whole 512-parameter tiles), start off a line boundary (a head
-of peeled elements) and end in a partial tile and a tail.  Each window
+of peeled elements) and end in a partial tile and a tail.  Replica counts
+cover templated (2, 64) and run-time (5, 100) kernel instances.  Each window
 setting, including the extremes (a window open 63 ticks of a 64-tick period;
 one open 1 tick of 2^20, which makes every wave store its older tile as soon
 as both slots are full), and a forced small grid (many tiles per wave) must
@@ -58,7 +59,7 @@ def _upload(torch, dev, host):
                 B=put(np.full(host["P"].size, 0x7FBF, dtype=np.uint16).view(np.int16), torch.int16))
 
 
-@pytest.mark.parametrize("N", [2, 64])
+@pytest.mark.parametrize("N", [2, 5, 64, 100])
 def test_windowed_step_matches_oracle(env, orc, N):
     torch, zs, dev = env["torch"], env["zs"], env["dev"]
     w, host = _inputs(N, 5000 if N == 64 else 100, 0.1 if N == 64 else 0.0)
@@ -103,7 +104,7 @@ def test_windowed_device_step(env, orc):
     assert parity.bit_identical(got, dict(P=P, M=M, V=V, B=B))
 
 
-@pytest.mark.parametrize("N,fmt,scale", [(64, "bf16", 1.0), (8, "fp16", 256.0)])
+@pytest.mark.parametrize("N,fmt,scale", [(64, "bf16", 1.0), (8, "fp16", 256.0), (100, "bf16", 1.0)])
 def test_windowed_pass1_matches_unwindowed_and_oracle(env, orc, N, fmt, scale):
     """Pass 1 of the two-pass form under write windows: the mean gradients bit-identical to the
     oracle's and the squared norm bit-identical to the unwindowed pass (the same fixed-order tile
