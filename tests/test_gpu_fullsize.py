@@ -182,7 +182,8 @@ def test_offload_full_size(orc):
 def test_flat_shard_beyond_2_31_elements(orc):
     """A flat shard of 2^31 + 12,345 parameters (N=2): element indices pass the
     32-bit range, so positions around 2^31 and at the tail are checked, through
-    the fused step and the two-pass form."""
+    the fused step and the two-pass form, each with the write windows off and
+    forced on (the windowed kernels' tile indices pass 2^31 too)."""
     import torch
 
     import sharded_mixed_precision_rank_amd as zs
@@ -198,22 +199,28 @@ def test_flat_shard_beyond_2_31_elements(orc):
     h = W.host_inputs_at(w, idx)
     P, M, V, B = orc.step(h["G"], h["P"], h["M"], h["V"], w.hp(), w.step)
     ref = dict(P=P, M=M, V=V, B=B)
-    # two-pass first (unclipped: the same result as the fused step), on copies of the state
-    P0, M0, V0 = d["P"].clone(), d["M"].clone(), d["V"].clone()
+    pristine = {k: d[k].clone() for k in ("P", "M", "V")}
     ws = torch.empty(zs.two_pass_workspace_bytes(n), dtype=torch.uint8, device="cuda")
     sq = torch.empty(1, dtype=torch.float64, device="cuda")
-    zs.reduce_grads_flat(d["G"], ws, sq)
-    zs.adam_from_grads_flat(ws, n, P0, M0, V0, d["B"], w.hp(), w.step, sq)
-    torch.cuda.synchronize()
-    got = gather(torch, dict(P=P0, M=M0, V=V0, B=d["B"]), idx)
-    assert parity.bit_identical(got, ref), "two-pass beyond 2^31"
-    del P0, M0, V0, ws, sq
-    torch.cuda.empty_cache()
-    d["B"].zero_()
-    zs.reduce_adam_flat(d["G"], d["P"], d["M"], d["V"], d["B"], w.hp(), w.step)
-    torch.cuda.synchronize()
-    got = gather(torch, d, idx)
-    parity.assert_step(got, ref, w.name)
-    assert parity.bit_identical(got, ref), "fused beyond 2^31"
-    del d
+    try:
+        for window in ((1, 0), (256, 32)):
+            zs.set_write_window(*window)
+            assert (zs.write_window("flat", 2, n)[0] != 0) == (window[0] > 1)
+            for path in ("two-pass", "fused"):
+                print(f"beyond 2^31: {path}, window {window}", flush=True)
+                for k in ("P", "M", "V"):
+                    d[k].copy_(pristine[k])
+                d["B"].zero_()
+                if path == "two-pass":  # unclipped: the same result as the fused step
+                    zs.reduce_grads_flat(d["G"], ws, sq)
+                    zs.adam_from_grads_flat(ws, n, d["P"], d["M"], d["V"], d["B"], w.hp(), w.step, sq)
+                else:
+                    zs.reduce_adam_flat(d["G"], d["P"], d["M"], d["V"], d["B"], w.hp(), w.step)
+                torch.cuda.synchronize()
+                got = gather(torch, d, idx)
+                parity.assert_step(got, ref, f"{w.name} {path} {window}")
+                assert parity.bit_identical(got, ref), f"{path} beyond 2^31, window {window}"
+    finally:
+        zs.set_write_window(0)
+    del d, pristine, ws, sq
     torch.cuda.empty_cache()
