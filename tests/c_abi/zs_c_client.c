@@ -9,7 +9,7 @@
  *      in its own allocations), run at steps 1 and 2;
  *   3. the one-shot list call on the same tensors at step 3;
  *   4. argument errors (N = 0, a NULL array) return their statuses before
- *      anything is enqueued;
+ *      anything is enqueued; the write-window setting and its query;
  *   5. the two-pass form with global-norm clipping active (70,001 parameters,
  *      a peeled head): the mean gradient, the norm (to 1e-12 relative, as
  *      the order of the double sum is the kernel's) and the clipped step;
@@ -194,6 +194,27 @@ int main(void) {
     bad = 1;
   }
   shard_free(&f);
+
+  /* 4b. the write-window setting and its query, from C (no GPU work) */
+  {
+    int32_t per = -1, open = -1;
+    CHECK_ZS(zs_write_window(ZS_WINDOW_FLAT_STEP, 64, (int64_t)1 << 30, &per, &open));
+    if (per != 4096 || open != 512) {
+      fprintf(stderr, "default flat window for N = 64: %d / %d\n", per, open);
+      bad = 1;
+    }
+    CHECK_ZS(zs_set_write_window(1, 0));
+    CHECK_ZS(zs_write_window(ZS_WINDOW_REDUCE_PASS, 64, (int64_t)1 << 30, &per, &open));
+    if (per != 0 || open != 0) {
+      fprintf(stderr, "windows switched off, but the query gives %d / %d\n", per, open);
+      bad = 1;
+    }
+    if (zs_set_write_window(100, 10) != ZS_ERR_RANGE) {
+      fprintf(stderr, "a period that is not a power of two was not rejected\n");
+      bad = 1;
+    }
+    CHECK_ZS(zs_set_write_window(0, 0));
+  }
 
   /* 2. and 3. a ragged list */
   const int64_t sizes[3] = {1, 5000, 70001};
