@@ -41,6 +41,7 @@ WORKLOADS = {
     "flat-124m": lambda W: W.FLAT_124M_N8,                         # 124M params, N=8, warm, step 100
     "list-llama7b": lambda W: W.list_llama7b_dp8_n8(),             # 288 tensors, 809.5M params, N=8
     "flat-70b": lambda W: W.FLAT_70B_DP64_N64,                     # 70B/64 shard, N=64, step 5000, wd 0.1
+    "list-llama70b": lambda W: W.list_llama70b_dp64_n64(),         # the 70B/64 shard as 720 per-layer tensors
     "list-ragged": lambda W: W.list_ragged_20000_n16(1),           # 20,000 ragged tensors, N=16, cold
     "list-ragged-warm": lambda W: W.list_ragged_20000_n16(10000),  # the same, warm, step 10000
 }
@@ -365,8 +366,9 @@ def main() -> int:
     log(f"{ms:.3f} ms/step, {n / (ms / 1e3) / 1e9:.2f} G params/s, {achieved:.0f} GB/s "
         f"(per step: median {ms_median:.3f} ms, min {ms_min:.3f} ms)")
 
-    # the write window the flat step took (0, 0: none) and so the kernel that ran
-    window = (0, 0) if w.is_list or offload is not None else zs.write_window("reduce" if two_pass else "flat", w.N, n)
+    # the write window the step took (0, 0: none) and so the kernel that ran; a list plan takes the flat
+    # step's windows, by its total parameter count
+    window = (0, 0) if offload is not None else zs.write_window("reduce" if two_pass else "flat", w.N, n)
     unwindowed = None
     if window[0]:
         # the same steps with the windows switched off, in this process: the windows' own effect
@@ -384,7 +386,7 @@ def main() -> int:
         log(f"without write windows: {gaps[2]:.3f} ms/step (median of 5)")
     tn = f"<{w.N}>" if w.N in (1, 2, 4, 8, 16, 32, 64) else "<0>"
     if w.is_list:
-        kernel = "list_kernel" + tn
+        kernel = ("list_window_kernel" if window[0] else "list_kernel") + tn
     elif two_pass:
         kernel = ("reduce_window_kernel" if window[0] else "reduce_kernel") + tn + " + gbar_kernel"
     else:

@@ -377,7 +377,8 @@ ZS_API zs_status zs_cpu_adam(const float* gbar, int64_t n, float* master, float*
 ZS_API zs_status zs_set_grid_blocks(int32_t blocks);
 
 /* Write windows of the flat step (zs_reduce_adam_flat and its device-step
-   form) and of pass 1 of the two-pass form (zs_reduce_grads_flat and its
+   form), of list plans (every list step call; a plan counts its total
+   parameters) and of pass 1 of the two-pass form (zs_reduce_grads_flat and its
    device-scale form), for all later calls in this process.  The flat step
    writes 14 bytes per parameter back beside 2N + 12 read, pass 1 writes 4
    beside 2N; on this memory system the writes cost far less when grouped in
@@ -406,7 +407,8 @@ ZS_API zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks);
 
 /* The write window a kernel takes, under the current setting, for N replicas
    on a shard of n parameters whose arrays share a 128-byte line phase:
-     kernel = ZS_WINDOW_FLAT_STEP:   the flat step (zs_reduce_adam_flat);
+     kernel = ZS_WINDOW_FLAT_STEP:   the flat step (zs_reduce_adam_flat), and
+                                     list plans of n parameters in all;
      kernel = ZS_WINDOW_REDUCE_PASS: pass 1 of the two-pass form
                                      (zs_reduce_grads_flat), on shards of at
                                      least 2^25 parameters.

@@ -641,9 +641,12 @@ zs_status run_plan(zs_list_plan_t plan, const zs_adam_hp* hps, int32_t n, int64_
   zs_status st = plan_on_current_device(plan);
   if (st) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  // write windows for plans of at least 2^25 parameters, as for flat shards
+  const zs::WriteWindow win = plan->n_params >= ((int64_t)zs::kWindowMinTiles << 9) ? write_window(plan->N)
+                                                                                    : zs::WriteWindow{0, 0};
   return after_launch(
-      zs::launch_list(plan->chunks, plan->n_chunks, plan->tensors, plan->gptrs, cs, n, ref, auto_blocks(), hs), hs,
-      "zs_reduce_adam_list launch");
+      zs::launch_list(plan->chunks, plan->n_chunks, plan->tensors, plan->gptrs, cs, n, ref, auto_blocks(), win, hs),
+      hs, "zs_reduce_adam_list launch");
 }
 
 }  // namespace

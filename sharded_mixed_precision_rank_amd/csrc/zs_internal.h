@@ -98,9 +98,10 @@ hipError_t launch_step_advance(int64_t* step, hipStream_t stream);
 // cs: n_sets folded scalar sets, one per hyperparameter group (1 <= n_sets <=
 // kMaxGroups); with a device step (ref.table set) n_sets is 1 and the table
 // supplies the folded scalars.
+// win: write windows (list_window_kernel) when period_mask != 0.
 hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
                        const uint16_t* const* gptrs, const Scalars* cs, int n_sets, const StepRef& ref, int blocks,
-                       hipStream_t stream);
+                       const WriteWindow& win, hipStream_t stream);
 
 // Threads per workgroup of the fused step's kernels; each thread owns one
 // 8-parameter group, so a tile is 8x this many parameters.

@@ -315,6 +315,143 @@ __global__ __launch_bounds__(kListBlock) void list_kernel(const ListChunk* __res
   }
 }
 
+// The list step with its write-back in device-clock windows, as
+// flat_window_kernel does for a flat shard.  Persistent one-wave workgroups
+// take work items: item w is 512-parameter sub-tile w % 8 of chunk w / 8 (a
+// vector chunk holds kChunkElems parameters from a multiple of that within
+// its tensor, so its sub-tiles are whole wave tiles, except a tensor's last,
+// partial one).  The chunk's tensor descriptor and replica pointers come by
+// scalar loads from the plan's table.  A full sub-tile is held (with its
+// tensor's arrays) and stored in a window; a partial sub-tile, a tensor's head
+// and tail elements and scalar-only tensors are stored at once.  Every element
+// goes through the same operations as in list_kernel.
+struct HeldListTiles {
+  int n = 0;
+  FlatShape sa, sb;  // the held tiles' tensors (arrays only)
+  int64_t ea = 0, eb = 0;
+  TileOut a, b;
+
+  __device__ __forceinline__ static FlatShape arrays(const FlatShape& s) {
+    FlatShape u{};
+    u.p = uniform_fptr(s.p);
+    u.m = uniform_fptr(s.m);
+    u.v = uniform_fptr(s.v);
+    u.b = uniform_fptr(s.b);
+    return u;
+  }
+  __device__ __forceinline__ void flush() {
+    if (n >= 1) store_tile(arrays(sa), uniform_i64(ea), a);
+    if (n == 2) store_tile(arrays(sb), uniform_i64(eb), b);
+    n = 0;
+  }
+  __device__ __forceinline__ void push(const FlatShape& s, int64_t e0, const TileOut& h) {
+    if (n == 2) {
+      store_tile(arrays(sa), uniform_i64(ea), a);
+      sa = sb;
+      ea = eb;
+      a = b;
+      sb = s;
+      eb = e0;
+      b = h;
+    } else if (n == 1) {
+      sb = s;
+      eb = e0;
+      b = h;
+      n = 2;
+    } else {
+      sa = s;
+      ea = e0;
+      a = h;
+      n = 1;
+    }
+  }
+  __device__ __forceinline__ void check(const WriteWindow& w) {
+    window_wait(w, [&]() { flush(); });
+  }
+};
+
+template <int NT, int NG>
+__global__ __launch_bounds__(kFlatBlock) void list_window_kernel(const ListChunk* __restrict__ chunks,
+                                                             int32_t n_chunks, const ListTensor* __restrict__ tensors,
+                                                             const uint16_t* const* __restrict__ gptrs,
+                                                             const ListScalars<NG> sc, const StepRef ref,
+                                                             const WriteWindow w) {
+  constexpr int64_t kSub = kChunkElems / 8 / kFlatBlock;  // wave tiles per chunk
+  static_assert(kSub * 8 * kFlatBlock == kChunkElems, "a chunk is a whole number of wave tiles");
+  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  const int N = NT > 0 ? NT : sc.c[0].n_rep;
+  Scalars one = sc.c[0];
+  if constexpr (NG == 1) {
+    if (!step_scalars(ref, one)) return;
+  }
+  const uint32_t e = Layout<true>::first();
+  const int64_t items = (int64_t)n_chunks * kSub;
+  HeldListTiles held;
+  auto check = [&]() { held.check(w); };
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int32_t ci = (int32_t)(it / kSub);
+    const int64_t j = it - (int64_t)ci * kSub;
+    const ListChunk ch = chunks[ci];
+    const ListTensor& T = tensors[ch.tensor];
+    FlatShape s;
+    s.p = uniform_fptr(T.p);
+    s.m = uniform_fptr(T.m);
+    s.v = uniform_fptr(T.v);
+    s.b = uniform_fptr(T.b);
+    s.n = uniform_i64(T.n);
+    s.head = uniform_i64(T.head);
+    s.nvec = uniform_i64(T.nvec);
+    s.scalar_only = T.scalar_only;
+    int32_t grp = 0;
+    if constexpr (NG > 1) grp = T.group;
+    const Scalars& c = NG == 1 ? one : sc.c[grp];
+    const uint16_t* const* gp = gptrs + (int64_t)ch.tensor * N;
+    auto G0 = [&](int r) { return uniform_ptr(gp[r]); };
+    if (s.scalar_only) {
+      if (j == 0)
+        for (int64_t i = ch.begin + threadIdx.x; i < ch.end; i += kFlatBlock) elem_step(G0, N, i, s, c);
+      continue;
+    }
+    const int64_t gt = ch.begin + kFlatBlock * j;  // first group of the sub-tile
+    const int64_t e0 = s.head + 8 * gt;
+    if (gt + kFlatBlock <= ch.end) {
+      f32x4 pa, pb, ma, mb, va, vb;
+      {
+        const uint32_t o = here(e) * 4u;
+        const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(s.p + e0), o);
+        const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(s.m + e0), o);
+        const GLB f32x4* V4 = (const GLB f32x4*)at(tile_base(s.v + e0), o);
+        pa = ld_g(P4);
+        pb = ld_g(P4 + q2);
+        ma = ld_g(M4);
+        mb = ld_g(M4 + q2);
+        va = ld_g(V4);
+        vb = ld_g(V4 + q2);
+      }
+      auto G = [&](int r) { return tile_base(G0(r) + e0); };
+      float acc[8];
+      if constexpr (NT > 0)
+        reduce_replicas_hooked<NT, kWindowChecks>(G, e, acc, check);
+      else
+        reduce_replicas_hooked_rt(G, N, e, acc, check);
+      float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+      float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+      float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) adam(mean_of<NT>(acc[k], c), p[k], m[k], v[k], c);
+      held.push(s, e0, tile_outputs(p, m, v));
+    } else if (gt < ch.end) {
+      // a tensor's last, partial wave tile: contiguous layout, stored at once
+      if (gt + threadIdx.x < ch.end) {
+        auto G = [&](int r) { return tile_base(G0(r) + e0); };
+        group_step<NT, false>(G, N, e0, s, c);
+      }
+    }
+    if (j == 0 && ch.first) edge_step<kFlatBlock>(G0, N, s, c);
+  }
+  held.flush();
+}
+
 // Flat-kernel grid: `blocks`, but no more workgroups than tiles.
 int clamp_grid(int blocks, int64_t work) {
   int64_t need = (work + kFlatBlock - 1) / kFlatBlock;
@@ -365,10 +502,59 @@ hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scala
   return hipGetLastError();
 }
 
+// Workgroups of `kernel` (one wave each) that fit on the current device at
+// once, cached per device in `cache`.
+template <class K>
+int resident_grid_of(K kernel, std::atomic<int>* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int g = cache[dev].load(std::memory_order_relaxed);
+  if (g > 0) return g;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kFlatBlock, 0) != hipSuccess) return 0;
+  g = cus * per_cu;
+  if (g > 0) cache[dev].store(g, std::memory_order_relaxed);
+  return g;
+}
+
+template <int NT, int NG>
+hipError_t go_list_window(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
+                          const uint16_t* const* gptrs, const ListScalars<NG>& sc, const StepRef& ref, int blocks,
+                          const WriteWindow& win, hipStream_t stream, bool* launched) {
+  static std::atomic<int> cache[kMaxDevices];
+  *launched = false;
+  int grid = resident_grid_of(list_window_kernel<NT, NG>, cache);
+  if (grid <= 0) {
+    (void)hipGetLastError();  // no occupancy figure: take the chunk kernel
+    return hipSuccess;
+  }
+  if (blocks < grid) grid = blocks;
+  (void)hipGetLastError();
+  list_window_kernel<NT, NG><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc, ref,
+                                                                           win);
+  *launched = true;
+  return hipGetLastError();
+}
+
 template <int NT>
 hipError_t go_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
                    const uint16_t* const* gptrs, const Scalars* cs, int n_sets, const StepRef& ref, int blocks,
-                   hipStream_t stream) {
+                   const WriteWindow& win, hipStream_t stream) {
+  if (win.period_mask != 0) {
+    bool launched = false;
+    hipError_t e;
+    if (n_sets <= 1) {
+      ListScalars<1> sc;
+      sc.c[0] = cs[0];
+      e = go_list_window<NT, 1>(chunks, n_chunks, tensors, gptrs, sc, ref, blocks, win, stream, &launched);
+    } else {
+      ListScalars<kMaxGroups> sc;
+      for (int k = 0; k < kMaxGroups; ++k) sc.c[k] = cs[k < n_sets ? k : 0];
+      e = go_list_window<NT, kMaxGroups>(chunks, n_chunks, tensors, gptrs, sc, ref, blocks, win, stream, &launched);
+    }
+    if (launched || e != hipSuccess) return e;
+  }
   const int grid = blocks < n_chunks ? blocks : n_chunks;
   (void)hipGetLastError();
   if (n_sets <= 1) {
@@ -407,16 +593,16 @@ hipError_t launch_step_advance(int64_t* step, hipStream_t stream) {
 
 hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
                        const uint16_t* const* gptrs, const Scalars* cs, int n_sets, const StepRef& ref, int blocks,
-                       hipStream_t stream) {
+                       const WriteWindow& win, hipStream_t stream) {
   switch (cs[0].n_rep) {
-    case 1: return go_list<1>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
-    case 2: return go_list<2>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
-    case 4: return go_list<4>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
-    case 8: return go_list<8>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
-    case 16: return go_list<16>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
-    case 32: return go_list<32>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
-    case 64: return go_list<64>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
-    default: return go_list<0>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, stream);
+    case 1: return go_list<1>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 2: return go_list<2>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 4: return go_list<4>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 8: return go_list<8>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 16: return go_list<16>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 32: return go_list<32>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 64: return go_list<64>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    default: return go_list<0>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
   }
 }
 

@@ -95,6 +95,15 @@ def llama7b_rank_shard_sizes(layers: int = 32, hidden: int = 4096, ffn: int = 11
     return tuple(per_layer * layers)
 
 
+def llama70b_rank_shard_sizes(layers: int = 80, hidden: int = 8192, kv: int = 1024, ffn: int = 28672,
+                              dp: int = 64):
+    """Per-layer tensors of a Llama-style 70B model with grouped-query attention, each sharded 1/dp:
+    q and o hidden x hidden, k and v hidden x kv, 3 MLP matrices hidden x ffn, 2 norm vectors."""
+    per_layer = [hidden * hidden // dp, hidden * kv // dp, hidden * kv // dp, hidden * hidden // dp] + \
+        [hidden * ffn // dp] * 3 + [hidden // dp] * 2
+    return tuple(per_layer * layers)
+
+
 def log_uniform_sizes(count: int, lo: int, hi: int, seed: int = 0):
     """count sizes, floor(exp(U(ln lo, ln hi))) clamped to [lo, hi]; U from a synth stream."""
     u = synth.uniform_f64(synth.key(seed, synth.KIND_SIZES), 0, count)
@@ -111,6 +120,12 @@ FLAT_70B_DP64_N64 = Workload("flat-70B/64-N64", N=64, step=5000, weight_decay=0.
 def list_llama7b_dp8_n8() -> Workload:
     return Workload("list-llama7b/8-N8", N=8, step=1000, weight_decay=0.0, warm=True,
                     sizes=llama7b_rank_shard_sizes())
+
+
+def list_llama70b_dp64_n64() -> Workload:
+    """The 70B/64 shard as per-layer tensors (720 tensors, 1.08B parameters), N=64, warm, step 5000, wd 0.1."""
+    return Workload("list-llama70b/64-N64", N=64, step=5000, weight_decay=0.1, warm=True,
+                    sizes=llama70b_rank_shard_sizes())
 
 
 def list_ragged_20000_n16(step: int = 1) -> Workload:

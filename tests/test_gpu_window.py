@@ -193,3 +193,54 @@ def test_windowed_kernels_in_a_graph(env, orc):
             assert sq_a.item() == sq_b.item(), f"replay {replay}: norm"
     finally:
         zs.set_write_window(0)
+
+
+# a ragged list of about 2^25 parameters: empty, 1- and 9-element (scalar-only) tensors, tensors that end in
+# partial wave tiles, and tensors of several chunks
+LIST_SIZES = (1, 9, 0, 5_000, 4_097, 70_001, (1 << 20) + 3, 3_000_001, 10_000_003, 20_000_017)
+
+
+@pytest.mark.parametrize("N,window", [(64, (0, 0)), (50, (0, 0)), (8, (256, 32))])
+def test_windowed_list_plan_matches_oracle(env, orc, N, window):
+    """List plans under write windows (the library default at N = 64 and at the run-time count 50, a forced
+    window at N = 8): one set for every tensor, then hyperparameter groups, then the device step, each
+    bit-identical to the oracle applied tensor by tensor (the gaps between tensors untouched)."""
+    from synth import workloads as W
+    from tests.test_gpu_list import arena_case, oracle_list, oracle_list_groups
+
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    w = W.Workload(f"window-list-N{N}", N=N, step=7, weight_decay=0.1, warm=True, sizes=LIST_SIZES, seed=N)
+    assert w.n_params >= 1 << 25
+    host, d, offsets, L = arena_case(env, w)
+
+    def got():
+        return dict(P=d["P"].cpu().numpy(), M=d["M"].cpu().numpy(), V=d["V"].cpu().numpy(),
+                    B=d["B"].cpu().numpy().view(np.uint16))
+
+    zs.set_write_window(*window)
+    try:
+        with zs.ListPlan.from_arenas(w.sizes, offsets, d["G"], d["P"], d["M"], d["V"], d["B"]) as plan:
+            print(f"windowed list: N={N} window={window} (flat step takes {zs.write_window('flat', N, w.n_params)})",
+                  flush=True)
+            plan.step(w.hp(), w.step)
+            torch.cuda.synchronize()
+            ref = oracle_list(orc, w, host, offsets, w.step, w.hp())
+            assert parity.bit_identical(got(), ref), "one set"
+            groups = [k % 3 for k in range(len(w.sizes))]
+            hps = [dict(lr=1e-3 * (1 + g), beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1 * (g % 2))
+                   for g in range(3)]
+            plan.set_groups(groups, 3)
+            plan.step_groups(hps, 8)
+            torch.cuda.synchronize()
+            state = dict(G=host["G"], P=ref["P"], M=ref["M"], V=ref["V"])
+            ref = oracle_list_groups(orc, w, state, offsets, 8, hps, groups)
+            assert parity.bit_identical(got(), ref), "groups"
+            src = zs.StepSource(w.hp(), 1, 20, dev, start=9)
+            plan.step_devstep(src)
+            torch.cuda.synchronize()
+            state = dict(G=host["G"], P=ref["P"], M=ref["M"], V=ref["V"])
+            ref = oracle_list(orc, w, state, offsets, 9, w.hp())
+            assert parity.bit_identical(got(), ref), "device step"
+            assert src.status == 0
+    finally:
+        zs.set_write_window(0)
