@@ -26,6 +26,7 @@ def workload(name):
 
     return {"flat-1m": lambda: W.FLAT_1M_N2, "flat-124m": lambda: W.FLAT_124M_N8,
             "list-llama7b": W.list_llama7b_dp8_n8, "flat-70b": lambda: W.FLAT_70B_DP64_N64,
+            "list-llama70b": W.list_llama70b_dp64_n64,
             "list-ragged": lambda: W.list_ragged_20000_n16(1),
             "list-ragged-warm": lambda: W.list_ragged_20000_n16(10_000)}[name]()
 
@@ -55,8 +56,8 @@ def gather(torch, d, idx):
                 B=d["B"].view(torch.int16)[it].cpu().numpy().view(np.uint16))
 
 
-@pytest.mark.parametrize("name", ["flat-1m", "flat-124m", "list-llama7b", "flat-70b", "list-ragged",
-                                  "list-ragged-warm"])
+@pytest.mark.parametrize("name", ["flat-1m", "flat-124m", "list-llama7b", "flat-70b", "list-llama70b",
+                                  "list-ragged", "list-ragged-warm"])
 def test_fused_step_full_size(orc, name):
     import torch
 
