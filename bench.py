@@ -66,19 +66,34 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(w, n_launch_params: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary for
-    this workload, if it was taken on the current kernel source; else None."""
+def counter_traffic(w, kernel: str):
+    """HBM bytes per launch of `kernel` (its name without template arguments) from the committed
+    rocprofv3 counter summary for this workload, if it was taken on the current kernel source; else
+    None.  The per-kernel summary (zs_kernel_<workload>_counters.txt) gives the read+write total; the
+    per-workload one (zs_kernels_<workload>.txt) gives read and write bytes under each kernel's line."""
     tag = w.name.replace("/", "-")
     path = os.path.join(PROFILES, f"zs_kernel_{tag}_counters.txt")
-    if not os.path.exists(path):
+    multi = os.path.join(PROFILES, f"zs_kernels_{tag}.txt")
+    if os.path.exists(path):
+        txt = open(path, encoding="utf-8").read()
+        m_name = re.search(r"^# rocprofv3 counter summary: (\w+),", txt, flags=re.M)
+        m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+        if not m_name or m_name.group(1) != kernel or not m_bytes:
+            return None
+        total = float(m_bytes.group(1))
+    elif os.path.exists(multi):
+        txt = open(multi, encoding="utf-8").read()
+        m = re.search(rf"^{re.escape(kernel)}: average .*\n\s+hbm read\s+([0-9.eE+]+) B/launch.*\n"
+                      rf"\s+hbm write\s+([0-9.eE+]+) B/launch", txt, flags=re.M)
+        if not m:
+            return None
+        total = float(m.group(1)) + float(m.group(2))
+    else:
         return None
-    txt = open(path, encoding="utf-8").read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+    if not m_hash or m_hash.group(1) != kernel_hash():
         return None
-    return float(m_bytes.group(1))
+    return total
 
 
 def pattern_ceiling(w, d, window=(0, 0), reps: int = 5):
@@ -412,7 +427,7 @@ def main() -> int:
     ceiling = None if args.no_copy else copy_ceiling()
     if ceiling:
         log(f"copy-kernel ceiling {ceiling:.0f} GB/s")
-    traffic = counter_traffic(w, n)
+    traffic = counter_traffic(w, kernel.split("<")[0]) if args.path == "fused" else None
     base = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
     if base:
         log(f"cpu baseline {base['value'] / 1e6:.1f} M params/s ({base['sample']})")
