@@ -49,6 +49,10 @@ def test_workload_sizes():
     offs, L = ragged.layout()
     assert np.all(offs % 8 == 0) and L >= ragged.n_params
     assert W.FLAT_70B_DP64_N64.n_params == 70_000_000_000 // 64
+    l70 = W.list_llama70b_dp64_n64()
+    # 80 layers of (2 h^2 + 2 h kv + 3 h ffn + 2 h) / 64 with h = 8192, kv = 1024, ffn = 28672
+    assert len(l70.sizes) == 720 and l70.N == 64
+    assert l70.n_params == 80 * (2 * 8192 ** 2 + 2 * 8192 * 1024 + 3 * 8192 * 28672 + 2 * 8192) // 64 == 1_069_568_000
 
 
 def test_host_inputs_at_matches_slices():
