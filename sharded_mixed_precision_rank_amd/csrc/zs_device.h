@@ -3,11 +3,32 @@
 // layout of a tile, and the per-parameter AdamW update.
 #pragma once
 
+#include <atomic>
 #include <type_traits>
 
 #include "zs_internal.h"
 
 namespace zs {
+
+// Workgroups of `kernel` (launched with `block` threads) that fit on the
+// current device at once: compute units x resident workgroups per unit, the
+// grid of a persistent kernel.  Cached per device in `cache` (kMaxDevices
+// slots, one array per kernel instance).  0 when the runtime gives no figure;
+// the callers then launch their one-tile-per-workgroup kernel instead.
+template <class K>
+int resident_grid(K kernel, int block, std::atomic<int>* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int g = cache[dev].load(std::memory_order_relaxed);
+  if (g > 0) return g;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return 0;
+  g = cus * per_cu;
+  if (g > 0) cache[dev].store(g, std::memory_order_relaxed);
+  return g;
+}
+
 namespace dev {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

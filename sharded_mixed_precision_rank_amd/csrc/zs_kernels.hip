@@ -459,24 +459,6 @@ int clamp_grid(int blocks, int64_t work) {
   return (int)(blocks < need ? blocks : need);
 }
 
-// Workgroups of flat_window_kernel<NT> that fit on the current device at
-// once (compute units x resident workgroups per unit), cached per device.
-template <int NT>
-int resident_grid() {
-  static std::atomic<int> cache[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  int g = cache[dev].load(std::memory_order_relaxed);
-  if (g > 0) return g;
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, flat_window_kernel<NT>, kFlatBlock, 0) != hipSuccess)
-    return 0;
-  g = cus * per_cu;
-  if (g > 0) cache[dev].store(g, std::memory_order_relaxed);
-  return g;
-}
-
 template <int NT>
 hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, const StepRef& ref,
                    int blocks, const WriteWindow& win, hipStream_t stream) {
@@ -487,7 +469,8 @@ hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scala
   a.r = ref;
   // windowed: shards of many whole tiles, when a window is set
   if (win.period_mask != 0 && !s.scalar_only && s.nvec / kFlatBlock >= kWindowMinTiles) {
-    int grid = resident_grid<NT>();
+    static std::atomic<int> cache[kMaxDevices];
+    int grid = resident_grid(flat_window_kernel<NT>, kFlatBlock, cache);
     if (grid > 0) {
       if (blocks < grid) grid = blocks;
       (void)hipGetLastError();
@@ -502,29 +485,13 @@ hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scala
   return hipGetLastError();
 }
 
-// Workgroups of `kernel` (one wave each) that fit on the current device at
-// once, cached per device in `cache`.
-template <class K>
-int resident_grid_of(K kernel, std::atomic<int>* cache) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  int g = cache[dev].load(std::memory_order_relaxed);
-  if (g > 0) return g;
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kFlatBlock, 0) != hipSuccess) return 0;
-  g = cus * per_cu;
-  if (g > 0) cache[dev].store(g, std::memory_order_relaxed);
-  return g;
-}
-
 template <int NT, int NG>
 hipError_t go_list_window(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
                           const uint16_t* const* gptrs, const ListScalars<NG>& sc, const StepRef& ref, int blocks,
                           const WriteWindow& win, hipStream_t stream, bool* launched) {
   static std::atomic<int> cache[kMaxDevices];
   *launched = false;
-  int grid = resident_grid_of(list_window_kernel<NT, NG>, cache);
+  int grid = resident_grid(list_window_kernel<NT, NG>, kFlatBlock, cache);
   if (grid <= 0) {
     (void)hipGetLastError();  // no occupancy figure: take the chunk kernel
     return hipSuccess;

@@ -307,24 +307,6 @@ __global__ __launch_bounds__(kBlock) void gbar_kernel(const GbarArgs a) {
   }
 }
 
-// Workgroups of reduce_window_kernel<NT, FMT> that fit on the current device
-// at once (compute units x resident workgroups per unit), cached per device.
-template <int NT, int FMT>
-int reduce_resident_grid() {
-  static std::atomic<int> cache[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  int g = cache[dev].load(std::memory_order_relaxed);
-  if (g > 0) return g;
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reduce_window_kernel<NT, FMT>, kBlock, 0) != hipSuccess)
-    return 0;
-  g = cus * per_cu;
-  if (g > 0) cache[dev].store(g, std::memory_order_relaxed);
-  return g;
-}
-
 template <int NT, int FMT>
 hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int blocks, hipStream_t stream) {
   (void)hipGetLastError();
@@ -346,7 +328,8 @@ hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int b
   bool windowed = false;
   // windowed: shards of many whole tiles, when a window is set
   if (sh.window.period_mask != 0 && !sh.scalar_only && (sh.n - sh.head) / kTile >= kReduceWindowMinTiles) {
-    int grid = reduce_resident_grid<NT, FMT>();
+    static std::atomic<int> cache[kMaxDevices];
+    int grid = resident_grid(reduce_window_kernel<NT, FMT>, kBlock, cache);
     if (grid > 0) {
       if (blocks < grid) grid = blocks;
       (void)hipGetLastError();
