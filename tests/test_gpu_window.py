@@ -26,6 +26,7 @@ N_PARAMS = (1 << 25) + 7 * 512 + 123
 OFFSET = 8  # elements: every array starts 32 or 16 bytes past a line boundary
 
 WINDOWS = [(0, 0), (1, 0), (256, 32), (64, 63), (1 << 20, 1), (4096, 512)]
+HP_WD = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1)
 
 
 @pytest.fixture(scope="module")
@@ -242,5 +243,55 @@ def test_windowed_list_plan_matches_oracle(env, orc, N, window):
             ref = oracle_list(orc, w, state, offsets, 9, w.hp())
             assert parity.bit_identical(got(), ref), "device step"
             assert src.status == 0
+    finally:
+        zs.set_write_window(0)
+
+
+@pytest.mark.parametrize("N,window", [(64, (0, 0)), (8, (256, 32))])
+def test_windowed_list_plan_with_peels_and_scalar_tensors(env, orc, N, window):
+    """List plans under write windows on tensors in buffers of their own: 2^25 + 1,003 parameters whose
+    arrays all start 3 elements past a 16-byte boundary (a 5-element head peel, whole tiles, a partial
+    tile and tail elements), 100 parameters with that phase, and 10,000 parameters whose arrays share no
+    16-byte phase (stepped element by element).  Bit-identical to the oracle per tensor, over two steps."""
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    rng = np.random.default_rng(N + 11)
+    n_of = [(1 << 25) + 1003, 100, 10_000]
+    # element offsets of each tensor's arrays in their buffers: G_0..G_{N-1}, P, M, V, B
+    shifts = [[3] * (N + 4), [3] * (N + 4), [(1 + r) % 4 for r in range(N)] + [3, 0, 1, 2]]
+    host, tensors, views = [], [], []
+    for n, sh in zip(n_of, shifts):
+        base = ((rng.standard_normal(n) * 1e-3).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        G = [np.roll(base, 977 * r) for r in range(N)]  # distinct replicas, cheaply
+        P = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        M = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+        V = np.abs(rng.standard_normal(n) * 1e-4).astype(np.float32)
+        host.append(dict(G=G, P=P, M=M, V=V))
+
+        def place(a, k, dtype):
+            buf = torch.zeros(n + 8, dtype=dtype, device=dev)
+            view = buf[k:k + n]
+            view.copy_(torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a))
+            return view
+
+        g = [place(G[r], sh[r], torch.int16) for r in range(N)]
+        p, m, v = (place(a, sh[N + j], torch.float32) for j, a in enumerate((P, M, V)))
+        b = place(np.zeros(n, np.uint16), sh[N + 3], torch.int16)
+        views.append((p, m, v, b))
+        tensors.append(zs.ShardTensor(g, p, m, v, b))
+    assert sum(n_of) >= 1 << 25
+    zs.set_write_window(*window)
+    try:
+        assert zs.write_window("flat", N, sum(n_of))[0] > 0, "the plan takes write windows"
+        with zs.ListPlan(tensors, N) as plan:
+            print(f"windowed list, peels and scalar tensors: N={N} window={window}", flush=True)
+            for t in (3, 4):
+                plan.step(HP_WD, t)
+                torch.cuda.synchronize()
+                for k, (h, (p, m, v, b)) in enumerate(zip(host, views)):
+                    rP, rM, rV, rB = orc.step(h["G"], h["P"], h["M"], h["V"], HP_WD, t)
+                    got = dict(P=p.cpu().numpy(), M=m.cpu().numpy(), V=v.cpu().numpy(),
+                               B=b.cpu().numpy().view(np.uint16))
+                    assert parity.bit_identical(got, dict(P=rP, M=rM, V=rV, B=rB)), f"tensor {k}, step {t}"
+                    h.update(P=rP, M=rM, V=rV)
     finally:
         zs.set_write_window(0)
