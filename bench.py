@@ -67,10 +67,11 @@ def kernel_hash() -> str:
 
 
 def counter_traffic(w, kernel: str):
-    """HBM bytes per launch of `kernel` (its name without template arguments) from the committed
-    rocprofv3 counter summary for this workload, if it was taken on the current kernel source; else
-    None.  The per-kernel summary (zs_kernel_<workload>_counters.txt) gives the read+write total; the
-    per-workload one (zs_kernels_<workload>.txt) gives read and write bytes under each kernel's line."""
+    """HBM bytes per step of `kernel` (its name without template arguments; one launch, or the sum over a
+    step's consecutive launches) from the committed rocprofv3 counter summary for this workload, if it
+    was taken on the current kernel source; else None.  The per-kernel summary
+    (zs_kernel_<workload>_counters.txt) gives the read+write total; the per-workload one
+    (zs_kernels_<workload>.txt) gives read and write bytes under each kernel's line."""
     tag = w.name.replace("/", "-")
     path = os.path.join(PROFILES, f"zs_kernel_{tag}_counters.txt")
     multi = os.path.join(PROFILES, f"zs_kernels_{tag}.txt")
@@ -83,8 +84,8 @@ def counter_traffic(w, kernel: str):
         total = float(m_bytes.group(1))
     elif os.path.exists(multi):
         txt = open(multi, encoding="utf-8").read()
-        m = re.search(rf"^{re.escape(kernel)}: average .*\n\s+hbm read\s+([0-9.eE+]+) B/launch.*\n"
-                      rf"\s+hbm write\s+([0-9.eE+]+) B/launch", txt, flags=re.M)
+        m = re.search(rf"^{re.escape(kernel)}: .* per step.*\n\s+hbm read\s+([0-9.eE+]+) B/step.*\n"
+                      rf"\s+hbm write\s+([0-9.eE+]+) B/step", txt, flags=re.M)
         if not m:
             return None
         total = float(m.group(1)) + float(m.group(2))
@@ -376,8 +377,8 @@ def main() -> int:
         log(f"cold (after a 1 GB scratch write): {cold_ms:.4f} ms/step, median of 10")
     n = w.n_params
     bpp = 2 * w.N + (34 if two_pass else 26)   # offload: the same algorithmic bytes as the fused step
-    bytes_per_launch = bpp * n
-    achieved = bytes_per_launch / (ms / 1e3) / 1e9
+    bytes_per_step = bpp * n
+    achieved = bytes_per_step / (ms / 1e3) / 1e9
     log(f"{ms:.3f} ms/step, {n / (ms / 1e3) / 1e9:.2f} G params/s, {achieved:.0f} GB/s "
         f"(per step: median {ms_median:.3f} ms, min {ms_min:.3f} ms)")
 
@@ -440,6 +441,7 @@ def main() -> int:
         "config": {"workload": w.name, "n_params": n, "replicas": w.N, "adam_step": w.step,
                    "weight_decay": w.weight_decay, "path": args.path,
                    "write_window_ticks": list(window) if window[0] else None,
+                   "max_bytes_per_launch": zs.launch_bytes(),
                    "storage": ("fp16" if args.path == "fp16" else "bf16") + " grads and working copy, fp32 master/m/v"},
         "hbm_GBps": achieved, "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,
         "copy_ceiling_GBps": ceiling,

@@ -34,8 +34,10 @@
  * device memory only for list-plan tables.  Host arrays passed in (grad_chunks,
  * tensors) are read during the call and may be freed when it returns.
  *
- * Asynchrony: the step calls enqueue one kernel on `stream` and return; the
- * caller keeps the buffers alive until the stream reaches the work.  Faults
+ * Asynchrony: the step calls enqueue their kernel on `stream` and return (one
+ * launch, or consecutive launches of a few GB each on long shards: see
+ * zs_set_launch_bytes); the caller keeps the buffers alive until the stream
+ * reaches the work.  Faults
  * during execution surface at the caller's next synchronisation.  Setting the
  * environment variable ZS_SYNC=1 makes every step call synchronise the stream
  * and report kernel errors itself.
@@ -141,7 +143,7 @@ typedef struct zs_tensor {
 } zs_tensor;
 
 /* A device-resident chunk table for a fixed list of tensors: built once,
-   then one launch per step covers every tensor. */
+   then one kernel per step covers every tensor. */
 typedef struct zs_list_plan* zs_list_plan_t;
 
 /* Validates the list (as the flat call, per tensor, plus: outputs of all
@@ -153,7 +155,8 @@ typedef struct zs_list_plan* zs_list_plan_t;
 ZS_API zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_t N, zs_stream stream,
                                      zs_list_plan_t* out);
 
-/* The step on every tensor of the plan: one kernel launch on `stream`.  The
+/* The step on every tensor of the plan: one kernel on `stream` (one launch,
+   or consecutive launches over the chunk table, zs_set_launch_bytes).  The
    plan's table lives on the device that was current at creation; calling with
    another device current fails with ZS_ERR_RANGE. */
 ZS_API zs_status zs_reduce_adam_list_plan(zs_list_plan_t plan, const zs_adam_hp* hp, int64_t step,
@@ -375,6 +378,23 @@ ZS_API zs_status zs_cpu_adam(const float* gbar, int64_t n, float* master, float*
    automatically from the device's compute-unit count.  Results do not depend
    on it (every element is computed by one thread with the same operations). */
 ZS_API zs_status zs_set_grid_blocks(int32_t blocks);
+
+/* The most algorithmic bytes one launch of a one-tile-per-workgroup kernel
+   moves, for all later calls in this process: the flat step and list plans
+   when they take no write windows, and both passes of the two-pass form
+   (pass 1 when it takes none).  Such a call covers its shard in consecutive
+   launches on its stream, each of whole tiles (whole chunks for list plans)
+   and at most this many bytes by the step's byte model, and always at least
+   one tile.  On this memory system one long launch lost up to 13% against
+   the same work cut into launches of 1.3-5 GB.  The windowed kernels are
+   persistent and always one launch.  Results do not depend on the setting.
+     bytes = 0: the default, 3e9;
+     bytes > 0: that limit (a value below one tile's bytes gives one tile per
+                launch; INT64_MAX gives one launch per call).
+   Errors: ZS_ERR_RANGE (bytes < 0). */
+ZS_API zs_status zs_set_launch_bytes(int64_t bytes);
+/* The limit in force (the default when none was set). */
+ZS_API int64_t zs_launch_bytes(void);
 
 /* Write windows of the flat step (zs_reduce_adam_flat and its device-step
    form), of list plans (every list step call; a plan counts its total

@@ -88,6 +88,10 @@ _lib.zs_step_advance.restype = ctypes.c_int
 _lib.zs_step_advance.argtypes = [_vp, _vp]
 _lib.zs_set_grid_blocks.restype = ctypes.c_int
 _lib.zs_set_grid_blocks.argtypes = [_i32]
+_lib.zs_set_launch_bytes.restype = ctypes.c_int
+_lib.zs_set_launch_bytes.argtypes = [ctypes.c_int64]
+_lib.zs_launch_bytes.restype = ctypes.c_int64
+_lib.zs_launch_bytes.argtypes = []
 _lib.zs_set_write_window.restype = ctypes.c_int
 _lib.zs_set_write_window.argtypes = [_i32, _i32]
 _lib.zs_write_window.restype = ctypes.c_int
@@ -181,6 +185,17 @@ def fold(hp, step: int) -> dict:
 
 def set_grid_blocks(blocks: int) -> None:
     _check(_lib.zs_set_grid_blocks(blocks), "zs_set_grid_blocks")
+
+
+def set_launch_bytes(nbytes: int) -> None:
+    """Most algorithmic bytes per launch of the one-tile-per-workgroup kernels (0 = library default);
+    see zs_set_launch_bytes."""
+    _check(_lib.zs_set_launch_bytes(nbytes), "zs_set_launch_bytes")
+
+
+def launch_bytes() -> int:
+    """The per-launch byte limit in force."""
+    return int(_lib.zs_launch_bytes())
 
 
 def set_write_window(period_ticks: int, open_ticks: int = 0) -> None:
@@ -351,7 +366,8 @@ def _tensor_table(tensors: Sequence[ShardTensor], N: int):
 
 class ListPlan:
     """A device-resident chunk table for a fixed ragged list of tensors; each
-    :meth:`step` is one kernel launch covering every tensor."""
+    :meth:`step` is one kernel covering every tensor (in consecutive launches of a few GB each on long
+    lists; see zs_set_launch_bytes)."""
 
     def __init__(self, tensors: Sequence[ShardTensor], N: int, stream=None):
         tab, keep = _tensor_table(tensors, N)

@@ -20,6 +20,7 @@ namespace {
 
 thread_local std::string g_last_error;
 std::atomic<int32_t> g_grid_blocks{0};
+std::atomic<int64_t> g_launch_bytes{0};  // zs_set_launch_bytes; 0 = zs::kLaunchBytes
 // zs_set_write_window: (period << 32) | open, one word so a reader never pairs
 // one call's period with another's open length; period 0 = automatic, 1 = no
 // windows
@@ -239,6 +240,11 @@ zs_status step_ref_of(const zs_step_source* src, std::vector<Range>& rs, zs::Ste
 
 namespace zs {
 
+int64_t launch_bytes() {
+  const int64_t b = g_launch_bytes.load(std::memory_order_relaxed);
+  return b > 0 ? b : kLaunchBytes;
+}
+
 // Tiles that start on a cache-line boundary in every array keep every wave
 // access on whole 128-byte lines; a tile grid that straddles lines turns each
 // line at a tile edge into two partial writes (measured 7-9% slower).  So the
@@ -439,6 +445,15 @@ zs_status zs_set_grid_blocks(int32_t blocks) {
   g_grid_blocks.store(blocks, std::memory_order_relaxed);
   return ZS_OK;
 }
+
+zs_status zs_set_launch_bytes(int64_t bytes) {
+  g_last_error.clear();
+  if (bytes < 0) return fail(ZS_ERR_RANGE, "bytes must be >= 0 (got %lld)", (long long)bytes);
+  g_launch_bytes.store(bytes, std::memory_order_relaxed);
+  return ZS_OK;
+}
+
+int64_t zs_launch_bytes(void) { return zs::launch_bytes(); }
 
 zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks) {
   g_last_error.clear();

@@ -135,5 +135,21 @@ constexpr int32_t kWindowMinPeriod = 64;
 constexpr int32_t kWindowMaxPeriod = 1 << 20;
 constexpr int32_t kWindowMaxOpen = 1 << 14;
 constexpr int kWindowMaxSleeps = 4096;
+// The one-tile-per-workgroup kernels (the flat step without windows, list
+// plans without windows, both passes of the two-pass form without windows)
+// cover a shard in consecutive launches of at most about kLaunchBytes
+// algorithmic bytes each.  Measured on one shard, one long launch ran up to
+// 13% slower than the same work cut into launches of 1.3-5 GB; the persistent
+// windowed kernels run as one launch and showed no such loss.  Results do not
+// depend on the cut: every element is computed the same way in any launch.
+constexpr int64_t kLaunchBytes = 3000000000LL;
+// The current limit (zs_set_launch_bytes; kLaunchBytes unless set).
+int64_t launch_bytes();
+// Units of `bytes_per_unit` algorithmic bytes per launch under that limit: a
+// multiple of `align` units, and at least `align`.
+inline int64_t units_per_launch(int64_t bytes_per_unit, int64_t align) {
+  const int64_t u = launch_bytes() / bytes_per_unit / align * align;
+  return u < align ? align : u;
+}
 
 }  // namespace zs

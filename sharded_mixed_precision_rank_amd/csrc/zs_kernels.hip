@@ -149,6 +149,12 @@ struct FlatArgs {
   FlatShape s;
   Scalars c;
   StepRef r;  // table == NULL: the step of `c`
+  // flat_kernel's share of the shard in this launch: 8-element groups
+  // [lo, hi) on the vector path (lo a multiple of a tile), elements [lo, hi)
+  // on the per-element path; edges = 1 when it also takes the head and tail
+  // elements.  The windowed kernel covers the whole shard and ignores them.
+  int64_t lo, hi;
+  int32_t edges;
 };
 
 template <int NT>
@@ -158,13 +164,13 @@ __global__ __launch_bounds__(kFlatBlock) void flat_kernel(const FlatArgs<NT> a) 
   const int N = NT > 0 ? NT : c.n_rep;
   if (!a.s.scalar_only) {
     auto G0 = [&](int r) { return a.g[r]; };
-    tiles<NT, kFlatBlock>(G0, N, 0, a.s.nvec, blockIdx.x, gridDim.x, a.s, c);
+    tiles<NT, kFlatBlock>(G0, N, a.lo, a.hi, blockIdx.x, gridDim.x, a.s, c);
     auto G = [&](int r) { return a.g[r]; };
-    if (blockIdx.x == gridDim.x - 1) edge_step<kFlatBlock>(G, N, a.s, c);
+    if (a.edges && blockIdx.x == gridDim.x - 1) edge_step<kFlatBlock>(G, N, a.s, c);
   } else {
     auto G = [&](int r) { return a.g[r]; };
     const int64_t stride = (int64_t)gridDim.x * kFlatBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kFlatBlock + threadIdx.x; i < a.s.n; i += stride)
+    for (int64_t i = a.lo + (int64_t)blockIdx.x * kFlatBlock + threadIdx.x; i < a.hi; i += stride)
       elem_step(G, N, i, a.s, c);
   }
 }
@@ -467,6 +473,10 @@ hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scala
   a.s = s;
   a.c = c;
   a.r = ref;
+  const int64_t work = s.scalar_only ? s.n : s.nvec;  // elements, or 8-element groups
+  a.lo = 0;
+  a.hi = work;
+  a.edges = 1;
   // windowed: shards of many whole tiles, when a window is set
   if (win.period_mask != 0 && !s.scalar_only && s.nvec / kFlatBlock >= kWindowMinTiles) {
     static std::atomic<int> cache[kMaxDevices];
@@ -479,10 +489,23 @@ hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scala
     }
     (void)hipGetLastError();  // no occupancy figure: take the one-tile kernel
   }
-  const int grid = clamp_grid(blocks, s.scalar_only ? s.n : s.nvec);
-  (void)hipGetLastError();
-  flat_kernel<NT><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(a);
-  return hipGetLastError();
+  // consecutive launches of at most launch_bytes() each, whole tiles apart
+  // from the last; the last also takes the head and tail elements
+  const int64_t bpp = 2 * (int64_t)c.n_rep + 26;
+  const int64_t per = s.scalar_only ? units_per_launch(bpp, kFlatBlock) : units_per_launch(8 * bpp, kFlatBlock);
+  int64_t lo = 0;
+  do {
+    const int64_t hi = work - lo > per ? lo + per : work;
+    a.lo = lo;
+    a.hi = hi;
+    a.edges = hi == work;
+    (void)hipGetLastError();
+    flat_kernel<NT><<<dim3(clamp_grid(blocks, hi - lo)), dim3(kFlatBlock), 0, stream>>>(a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    lo = hi;
+  } while (lo < work);
+  return hipSuccess;
 }
 
 template <int NT, int NG>
@@ -522,18 +545,27 @@ hipError_t go_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* 
     }
     if (launched || e != hipSuccess) return e;
   }
-  const int grid = blocks < n_chunks ? blocks : n_chunks;
-  (void)hipGetLastError();
-  if (n_sets <= 1) {
-    ListScalars<1> sc;
-    sc.c[0] = cs[0];
-    list_kernel<NT, 1><<<dim3(grid), dim3(kListBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc, ref);
-  } else {
-    ListScalars<kMaxGroups> sc;
-    for (int k = 0; k < kMaxGroups; ++k) sc.c[k] = cs[k < n_sets ? k : 0];
-    list_kernel<NT, kMaxGroups><<<dim3(grid), dim3(kListBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc, ref);
+  // consecutive launches over the chunk table, each at most launch_bytes()
+  // (a chunk holds at most kChunkElems parameters; every chunk is complete in
+  // itself, its tensor's head and tail included)
+  const int64_t per = units_per_launch(kChunkElems * (2 * (int64_t)cs[0].n_rep + 26), 1);
+  ListScalars<1> sc1;
+  ListScalars<kMaxGroups> scg;
+  sc1.c[0] = cs[0];
+  for (int k = 0; k < kMaxGroups; ++k) scg.c[k] = cs[k < n_sets ? k : 0];
+  for (int64_t c0 = 0; c0 < n_chunks; c0 += per) {
+    const int32_t cnt = (int32_t)(n_chunks - c0 > per ? per : n_chunks - c0);
+    const int grid = blocks < cnt ? blocks : cnt;
+    (void)hipGetLastError();
+    if (n_sets <= 1)
+      list_kernel<NT, 1><<<dim3(grid), dim3(kListBlock), 0, stream>>>(chunks + c0, cnt, tensors, gptrs, sc1, ref);
+    else
+      list_kernel<NT, kMaxGroups><<<dim3(grid), dim3(kListBlock), 0, stream>>>(chunks + c0, cnt, tensors, gptrs, scg,
+                                                                                ref);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace

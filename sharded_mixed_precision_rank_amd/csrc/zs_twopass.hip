@@ -54,6 +54,10 @@ struct ReduceArgs {
   int32_t n_rep;
   float inv_scale;   // f32(1 / loss scale)
   const double* scale_dev;  // if set: the loss scale in device memory (inv_scale is then unused)
+  // reduce_kernel's tiles in this launch, [t_lo, t_hi); head = 1 when it also
+  // takes the head elements (the windowed kernel covers every tile)
+  int64_t t_lo, t_hi;
+  int32_t head_here;
 };
 
 // f32(1 / loss scale): from the kernel argument, or from device memory (the
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs<NT> a) 
   c.n_rep = N;
   const float inv = unscale_factor(a);
   auto G0 = [&](int r) { return a.g[r]; };
-  for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+  for (int64_t t = a.t_lo + blockIdx.x; t < a.t_hi; t += gridDim.x) {
     const int64_t e0 = a.head + t * kTile;
     double sq = 0.0;
     if (!a.scalar_only && e0 + kTile <= a.n) {
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs<NT> a) 
     sq = block_sum(sq, lds4);
     if (threadIdx.x == 0) a.partials[t] = sq;
   }
-  if (blockIdx.x == 0) head_partial<NT, FMT>(a, G0, N, inv, lds4);
+  if (a.head_here && blockIdx.x == 0) head_partial<NT, FMT>(a, G0, N, inv, lds4);
 }
 
 // Pass 1 with its mean-gradient writes grouped in device-clock windows, as
@@ -228,6 +232,10 @@ struct GbarArgs {
   double max_norm;
   int32_t skip_nonfinite;
   StepRef r;  // table == NULL: the step of `c`
+  // this launch's tiles, [t_lo, t_hi); edges = 1 when it also takes the head
+  // and tail elements of a vector-path shard
+  int64_t t_lo, t_hi;
+  int32_t edges;
 };
 
 __device__ __forceinline__ float clip_factor(double total_sq, double max_norm) {
@@ -254,8 +262,7 @@ __global__ __launch_bounds__(kBlock) void gbar_kernel(const GbarArgs a) {
   if (a.skip_nonfinite && !__builtin_isfinite(tsq)) return;  // overflow: the step is skipped everywhere
   const float k = clip_factor(tsq, a.max_norm);
   const FlatShape& s = a.s;
-  const int64_t ntiles = s.scalar_only ? (s.n + kTile - 1) / kTile : (s.nvec + kBlock - 1) / kBlock;
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+  for (int64_t t = a.t_lo + blockIdx.x; t < a.t_hi; t += gridDim.x) {
     if (!s.scalar_only && (t + 1) * kBlock <= s.nvec) {
       const int64_t e0 = s.head + t * kTile;
       const uint32_t e = Layout<true>::first();
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(kBlock) void gbar_kernel(const GbarArgs a) {
         if (lo + j < end && lo + j < e0 + kTile) gbar_elem<OFMT>(a, c, lo + j, k);
     }
   }
-  if (blockIdx.x == 0 && !s.scalar_only) {  // head and tail elements
+  if (a.edges && blockIdx.x == 0 && !s.scalar_only) {  // head and tail elements
     const int64_t tail = s.n - s.head - 8 * s.nvec;
     const int t = threadIdx.x;
     if (t < s.head)
@@ -325,6 +332,9 @@ hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int b
   a.n_rep = sh.n_rep;
   a.inv_scale = sh.inv_scale;
   a.scale_dev = sh.scale_dev;
+  a.t_lo = 0;
+  a.t_hi = sh.ntiles;
+  a.head_here = 1;
   bool windowed = false;
   // windowed: shards of many whole tiles, when a window is set
   if (sh.window.period_mask != 0 && !sh.scalar_only && (sh.n - sh.head) / kTile >= kReduceWindowMinTiles) {
@@ -337,14 +347,27 @@ hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int b
       windowed = true;
     }
   }
-  if (!windowed) {
-    int grid = (int)(sh.ntiles < blocks ? sh.ntiles : blocks);
-    if (grid < 1) grid = 1;
-    (void)hipGetLastError();
-    reduce_kernel<NT, FMT><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
-  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (!windowed) {
+    // consecutive launches of at most launch_bytes() each (2N + 4 bytes per
+    // parameter); the first also takes the head elements
+    const int64_t per = units_per_launch((2 * (int64_t)sh.n_rep + 4) * kTile, 1);
+    int64_t lo = 0;
+    do {
+      const int64_t hi = sh.ntiles - lo > per ? lo + per : sh.ntiles;
+      a.t_lo = lo;
+      a.t_hi = hi;
+      a.head_here = lo == 0;
+      int grid = (int)(hi - lo < blocks ? hi - lo : blocks);
+      if (grid < 1) grid = 1;
+      (void)hipGetLastError();
+      reduce_kernel<NT, FMT><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      lo = hi;
+    } while (lo < sh.ntiles);
+  }
   // the norm: tile partials -> one sum per kFinalSeg of them -> the total, in a fixed order
   const int64_t count = sh.ntiles + 1;
   const int64_t nb1 = (count + kFinalSeg - 1) / kFinalSeg;
@@ -426,14 +449,27 @@ hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, 
   a.max_norm = max_norm;
   a.skip_nonfinite = skip_nonfinite;
   const int64_t ntiles = s.scalar_only ? (s.n + kTile - 1) / kTile : (s.nvec + kBlock - 1) / kBlock;
-  int grid = (int)(ntiles < blocks ? ntiles : blocks);
-  if (grid < 1) grid = 1;
-  (void)hipGetLastError();
-  if (param_format == 1)
-    gbar_kernel<kFP16><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
-  else
-    gbar_kernel<kBF16><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
-  return hipGetLastError();
+  // consecutive launches of at most launch_bytes() each (30 bytes per
+  // parameter); the first also takes the head and tail elements
+  const int64_t per = units_per_launch(30 * (int64_t)kTile, 1);
+  int64_t lo = 0;
+  do {
+    const int64_t hi = ntiles - lo > per ? lo + per : ntiles;
+    a.t_lo = lo;
+    a.t_hi = hi;
+    a.edges = lo == 0;
+    int grid = (int)(hi - lo < blocks ? hi - lo : blocks);
+    if (grid < 1) grid = 1;
+    (void)hipGetLastError();
+    if (param_format == 1)
+      gbar_kernel<kFP16><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
+    else
+      gbar_kernel<kBF16><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    lo = hi;
+  } while (lo < ntiles);
+  return hipSuccess;
 }
 
 }  // namespace zs

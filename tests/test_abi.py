@@ -429,3 +429,14 @@ def test_tuning_knobs_check_their_ranges():
     with pytest.raises(zs.ZShardError):
         zs.set_write_window(100, 10)
     zs.set_write_window(0)
+    # the per-launch byte limit: 0 restores the 3e9 default, any positive value is taken as is
+    lib.zs_set_launch_bytes.argtypes = [ctypes.c_int64]
+    assert lib.zs_set_launch_bytes(-1) == rng
+    assert zs.launch_bytes() == 3_000_000_000
+    for b in (1, 4096, 10 ** 12, 2 ** 63 - 1):
+        zs.set_launch_bytes(b)
+        assert zs.launch_bytes() == b
+    zs.set_launch_bytes(0)
+    assert zs.launch_bytes() == 3_000_000_000
+    with pytest.raises(zs.ZShardError):
+        zs.set_launch_bytes(-5)
