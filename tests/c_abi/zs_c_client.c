@@ -182,6 +182,22 @@ int main(void) {
   CHECK_HIP(hipStreamSynchronize(stream));
   bad |= oracle_compare(&f, &hp, 7, "flat");
 
+  /* 1b. a flat shard in consecutive launches of one tile each, then the default limit again */
+  {
+    shard g;
+    shard_init(&g, 20011, 5, 3);
+    CHECK_ZS(zs_set_launch_bytes(1));
+    CHECK_ZS(zs_reduce_adam_flat((const uint16_t* const*)g.dg, g.N, g.n, g.dp, g.dm, g.dv, g.db, &hp, 4, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    bad |= oracle_compare(&g, &hp, 4, "flat, one tile per launch");
+    CHECK_ZS(zs_set_launch_bytes(0));
+    if (zs_launch_bytes() != 3000000000LL || zs_set_launch_bytes(-1) != ZS_ERR_RANGE) {
+      fprintf(stderr, "launch byte limit: default %lld, or a negative limit accepted\n", (long long)zs_launch_bytes());
+      bad = 1;
+    }
+    shard_free(&g);
+  }
+
   /* 4. argument errors, before anything is enqueued */
   if (zs_reduce_adam_flat((const uint16_t* const*)f.dg, 0, f.n, f.dp, f.dm, f.dv, f.db, &hp, 8, stream) !=
       ZS_ERR_RANGE) {
