@@ -104,15 +104,13 @@ hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTens
                        const WriteWindow& win, hipStream_t stream);
 
 // Threads per workgroup of the fused step's kernels; each thread owns one
-// 8-parameter group, so a tile is 8x this many parameters.
-//  Flat shards: one wave, a 512-parameter tile dispatched and retired on its
-//  own.  Measured on the same buffers against 256-thread workgroups: 1-4%
-//  faster (70B/64 shard +1.2%, 124M-parameter N=8 shard +4.4%).
-//  List plans: four waves.  A list workgroup first loads its chunk's
-//  descriptor and replica pointers (dependent loads); one-wave workgroups
-//  measured 1-3% slower there at every chunk size from 1024 to 4096.
+// 8-parameter group, so a tile is 8x this many parameters.  One wave: a
+// 512-parameter tile dispatched and retired on its own.  Measured on the same
+// buffers against 256-thread workgroups: 1-4% faster for flat shards (70B/64
+// shard +1.2%, 124M-parameter N=8 shard +4.4%); for list plans, one wave per
+// tile with scalar descriptor loads ran 0-1.6% faster than a four-wave
+// workgroup per chunk that staged its descriptor through LDS.
 constexpr int kFlatBlock = 64;
-constexpr int kListBlock = 256;
 // Elements per list chunk (vector tensors: groups of 8 per chunk = this / 8):
 // two list tiles.
 constexpr int64_t kChunkElems = 4096;

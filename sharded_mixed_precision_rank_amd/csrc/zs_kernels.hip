@@ -10,10 +10,9 @@
 //    store.  A wave touches 1 KiB contiguous per array per access, so every
 //    cache line is fully used and writes never need the line's old contents.
 //  * Replica pointers are wave-uniform.  For the flat call they sit in the
-//    kernel-argument segment and reach SGPRs through scalar loads; for lists
-//    they are staged through LDS per chunk and moved to SGPRs with
-//    readfirstlane.  Either way each global load is SGPR base + one shared
-//    VGPR offset.
+//    kernel-argument segment; for lists in the plan's device table.  Either
+//    way they reach SGPRs through scalar loads, and each global load is SGPR
+//    base + one shared VGPR offset.
 //  * Replicas are accumulated in fp32 registers strictly in rank order
 //    0..N-1; loads are issued in batches so that several are in flight per
 //    thread without holding all N in registers.
@@ -21,10 +20,9 @@
 //    stream so their latency overlaps it.
 //  * Every access is marked non-temporal: nothing is re-read, so nothing
 //    should displace useful lines in L2 or the Infinity Cache.
-//  * A flat shard runs one wave per workgroup, one 512-parameter tile each;
-//    a list plan runs four waves per workgroup over 4096-parameter chunks
-//    (two 2048-parameter tiles).  The measurements behind both choices are
-//    noted at kFlatBlock and kListBlock.
+//  * One wave per workgroup, one 512-parameter tile each, for flat shards and
+//    list plans alike (a list plan's 4096-parameter chunks are eight such
+//    tiles).  The measurements behind this are noted at kFlatBlock.
 //  * Tiles start where every array sits on a 128-byte line boundary when the
 //    arrays allow it (else 64, 32 or 16 bytes), so each wave access covers
 //    whole lines and no line is written in two halves by two tiles.
@@ -32,11 +30,13 @@
 //    shards whose arrays share no common alignment go through a per-element
 //    path with the identical operation sequence (same inline function), so
 //    results do not depend on alignment, grid size or path.
-//  * Large flat shards at N = 64 run flat_window_kernel instead: the same
-//    tiles and arithmetic, with the write-back held in registers and stored
-//    in short device-clock windows, so the memory system sees read-only and
-//    write-only phases instead of the two interleaved (see "write windows"
-//    below).
+//  * Large flat shards and list plans at N >= 48 run flat_window_kernel and
+//    list_window_kernel instead: the same tiles and arithmetic, with the
+//    write-back held in registers and stored in short device-clock windows,
+//    so the memory system sees read-only and write-only phases instead of the
+//    two interleaved (see "write windows" below).
+//  * Without windows, a long shard runs as consecutive launches of at most
+//    about 3 GB each (kLaunchBytes).
 //
 // Arithmetic: see include/zshard.h.  Built with -ffp-contract=off (no FMA
 // contraction) and correctly rounded fp32 divide and sqrt; fp32 denormals are
@@ -267,9 +267,6 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Ragged list: each workgroup takes chunks; per chunk it stages the owning
-// tensor's descriptor and its N replica pointers into LDS, then runs the same
-// group/element code as the flat kernel over the chunk.
 // NG sets of folded scalars: one for every tensor (NG = 1), or one per
 // hyperparameter group, the group of a tensor being its descriptor's `group`.
 template <int NG>
@@ -277,47 +274,62 @@ struct ListScalars {
   Scalars c[NG];
 };
 
+// The ragged-list step: one-wave workgroups, one 512-parameter wave tile
+// each, as flat_kernel: work item w is sub-tile w % 8 of chunk w / 8 (a vector
+// chunk holds kChunkElems parameters from a multiple of that within its
+// tensor, so its sub-tiles are whole wave tiles, except a tensor's last,
+// partial one).  The chunk's tensor descriptor and replica pointers come by
+// scalar loads from the plan's table, so no LDS staging and no barrier sit
+// between a workgroup's start and its first gradient load.  Scalar-only
+// tensors take 512 elements per work item, element by element; the chunk that
+// holds a tensor's start also takes its head and tail elements.  Every
+// element goes through the same operations as in flat_kernel.
 template <int NT, int NG>
-__global__ __launch_bounds__(kListBlock) void list_kernel(const ListChunk* __restrict__ chunks, int32_t n_chunks,
-                                                      const ListTensor* __restrict__ tensors,
-                                                      const uint16_t* const* __restrict__ gptrs,
-                                                      const ListScalars<NG> sc, const StepRef ref) {
-  constexpr int kMaxN = NT > 0 ? NT : ZS_MAX_REPLICAS;
-  __shared__ int64_t s_tensor[8];
-  __shared__ const uint16_t* s_g[kMaxN];
+__global__ __launch_bounds__(kFlatBlock) void list_kernel(const ListChunk* __restrict__ chunks, int32_t n_chunks,
+                                                           const ListTensor* __restrict__ tensors,
+                                                           const uint16_t* const* __restrict__ gptrs,
+                                                           const ListScalars<NG> sc, const StepRef ref) {
+  constexpr int64_t kSub = kChunkElems / 8 / kFlatBlock;  // wave tiles per chunk
+  static_assert(kSub * 8 * kFlatBlock == kChunkElems, "a chunk is a whole number of wave tiles");
   const int N = NT > 0 ? NT : sc.c[0].n_rep;
-  // single-set launches: the host-folded scalars, or the device step's row
-  // (a device step is not combined with groups, so NG > 1 launches skip this)
   Scalars one = sc.c[0];
   if constexpr (NG == 1) {
     if (!step_scalars(ref, one)) return;
   }
-  for (int32_t ci = blockIdx.x; ci < n_chunks; ci += gridDim.x) {
+  const int64_t items = (int64_t)n_chunks * kSub;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int32_t ci = (int32_t)(it / kSub);
+    const int64_t j = it - (int64_t)ci * kSub;
     const ListChunk ch = chunks[ci];
-    const int32_t t = ch.tensor;
-    if (threadIdx.x < 8) s_tensor[threadIdx.x] = reinterpret_cast<const int64_t*>(tensors + t)[threadIdx.x];
-    for (int r = threadIdx.x; r < N; r += kListBlock) s_g[r] = gptrs[(int64_t)t * N + r];
-    __syncthreads();
+    const ListTensor& T = tensors[ch.tensor];
     FlatShape s;
-    s.p = uniform_fptr(reinterpret_cast<float*>(s_tensor[0]));
-    s.m = uniform_fptr(reinterpret_cast<float*>(s_tensor[1]));
-    s.v = uniform_fptr(reinterpret_cast<float*>(s_tensor[2]));
-    s.b = uniform_fptr(reinterpret_cast<uint16_t*>(s_tensor[3]));
-    s.n = uniform_i64(s_tensor[4]);
-    s.head = uniform_i64(s_tensor[5]);
-    s.nvec = uniform_i64(s_tensor[6]);
-    s.scalar_only = (int32_t)uniform_i64(s_tensor[7] & 0xFFFFFFFF);
+    s.p = uniform_fptr(T.p);
+    s.m = uniform_fptr(T.m);
+    s.v = uniform_fptr(T.v);
+    s.b = uniform_fptr(T.b);
+    s.n = uniform_i64(T.n);
+    s.head = uniform_i64(T.head);
+    s.nvec = uniform_i64(T.nvec);
+    s.scalar_only = T.scalar_only;
     int32_t grp = 0;
-    if constexpr (NG > 1) grp = (int32_t)uniform_i64(s_tensor[7] >> 32);  // the tensor's group, < NG
+    if constexpr (NG > 1) grp = T.group;
     const Scalars& c = NG == 1 ? one : sc.c[grp];
-    auto G = [&](int r) { return uniform_ptr(s_g[r]); };
-    if (!s.scalar_only) {
-      tiles<NT, kListBlock>(G, N, ch.begin, ch.end, 0, 1, s, c);
-      if (ch.first) edge_step<kListBlock>(G, N, s, c);
-    } else {
-      for (int64_t i = ch.begin + threadIdx.x; i < ch.end; i += kListBlock) elem_step(G, N, i, s, c);
+    const uint16_t* const* gp = gptrs + (int64_t)ch.tensor * N;
+    auto G0 = [&](int r) { return uniform_ptr(gp[r]); };
+    if (s.scalar_only) {
+      const int64_t lo = ch.begin + j * kFlatBlock * 8;
+      const int64_t hi = lo + kFlatBlock * 8 < ch.end ? lo + kFlatBlock * 8 : ch.end;
+      for (int64_t i = lo + threadIdx.x; i < hi; i += kFlatBlock) elem_step(G0, N, i, s, c);
+      continue;
     }
-    __syncthreads();  // the next chunk overwrites the staged descriptor
+    const int64_t gt = ch.begin + kFlatBlock * j;  // first group of the sub-tile
+    const int64_t e0 = s.head + 8 * gt;
+    auto G = [&](int r) { return tile_base(G0(r) + e0); };
+    if (gt + kFlatBlock <= ch.end)
+      group_step<NT, true>(G, N, e0, s, c);
+    else if (gt + threadIdx.x < ch.end)
+      group_step<NT, false>(G, N, e0, s, c);
+    if (j == 0 && ch.first) edge_step<kFlatBlock>(G0, N, s, c);
   }
 }
 
@@ -555,13 +567,14 @@ hipError_t go_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* 
   for (int k = 0; k < kMaxGroups; ++k) scg.c[k] = cs[k < n_sets ? k : 0];
   for (int64_t c0 = 0; c0 < n_chunks; c0 += per) {
     const int32_t cnt = (int32_t)(n_chunks - c0 > per ? per : n_chunks - c0);
-    const int grid = blocks < cnt ? blocks : cnt;
+    const int64_t items = (int64_t)cnt * (kChunkElems / 8 / kFlatBlock);  // wave tiles
+    const int grid = (int)(blocks < items ? blocks : items);
     (void)hipGetLastError();
     if (n_sets <= 1)
-      list_kernel<NT, 1><<<dim3(grid), dim3(kListBlock), 0, stream>>>(chunks + c0, cnt, tensors, gptrs, sc1, ref);
+      list_kernel<NT, 1><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(chunks + c0, cnt, tensors, gptrs, sc1, ref);
     else
-      list_kernel<NT, kMaxGroups><<<dim3(grid), dim3(kListBlock), 0, stream>>>(chunks + c0, cnt, tensors, gptrs, scg,
-                                                                                ref);
+      list_kernel<NT, kMaxGroups><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(chunks + c0, cnt, tensors, gptrs, scg,
+                                                                               ref);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
