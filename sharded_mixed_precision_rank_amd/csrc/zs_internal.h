@@ -114,8 +114,9 @@ constexpr int kFlatBlock = 64;
 // Elements per list chunk (vector tensors: groups of 8 per chunk = this / 8):
 // two list tiles.
 constexpr int64_t kChunkElems = 4096;
-// Threads per workgroup of the two-pass kernels (four waves; their norm
-// partials are reduced across the waves through LDS).
+// Threads per workgroup of pass 1 of the two-pass form (four waves; its norm
+// partials are reduced across the waves through LDS).  Pass 2 runs one wave
+// per workgroup, as the fused step.
 constexpr int kBlock = 256;
 // Hyperparameter groups a list plan can carry (their scalars travel as kernel arguments).
 constexpr int kMaxGroups = ZS_MAX_GROUPS;

@@ -254,8 +254,9 @@ __device__ __forceinline__ void gbar_elem(const GbarArgs& a, const Scalars& c, i
   a.s.b[i] = to_half<OFMT>(p);
 }
 
-template <int OFMT>
-__global__ __launch_bounds__(kBlock) void gbar_kernel(const GbarArgs a) {
+template <int OFMT, int BLK>
+__global__ __launch_bounds__(BLK) void gbar_kernel(const GbarArgs a) {
+  constexpr int64_t kT = 8 * BLK;  // parameters per tile
   Scalars c = a.c;
   if (!step_scalars(a.r, c)) return;
   const double tsq = *a.total_sq;
@@ -263,8 +264,8 @@ __global__ __launch_bounds__(kBlock) void gbar_kernel(const GbarArgs a) {
   const float k = clip_factor(tsq, a.max_norm);
   const FlatShape& s = a.s;
   for (int64_t t = a.t_lo + blockIdx.x; t < a.t_hi; t += gridDim.x) {
-    if (!s.scalar_only && (t + 1) * kBlock <= s.nvec) {
-      const int64_t e0 = s.head + t * kTile;
+    if (!s.scalar_only && (t + 1) * BLK <= s.nvec) {
+      const int64_t e0 = s.head + t * kT;
       const uint32_t e = Layout<true>::first();
       constexpr uint32_t q2 = Layout<true>::kSecond / 4;
       const uint32_t o = here(e) * 4u;
@@ -297,20 +298,17 @@ __global__ __launch_bounds__(kBlock) void gbar_kernel(const GbarArgs a) {
       st_g(B2 + Layout<true>::kSecond / 4, (u32x2){pack_half<OFMT>(p[4], p[5]), pack_half<OFMT>(p[6], p[7])});
     } else {
       // partial tile (vector shards) or any tile of a shard without common alignment
-      const int64_t e0 = s.scalar_only ? t * kTile : s.head + t * kTile;
+      const int64_t e0 = s.scalar_only ? t * kT : s.head + t * kT;
       const int64_t end = s.scalar_only ? s.n : s.head + 8 * s.nvec;
       const int64_t lo = e0 + 8 * (int64_t)threadIdx.x;
       for (int j = 0; j < 8; ++j)
-        if (lo + j < end && lo + j < e0 + kTile) gbar_elem<OFMT>(a, c, lo + j, k);
+        if (lo + j < end && lo + j < e0 + kT) gbar_elem<OFMT>(a, c, lo + j, k);
     }
   }
   if (a.edges && blockIdx.x == 0 && !s.scalar_only) {  // head and tail elements
     const int64_t tail = s.n - s.head - 8 * s.nvec;
-    const int t = threadIdx.x;
-    if (t < s.head)
-      gbar_elem<OFMT>(a, c, t, k);
-    else if (t < s.head + tail)
-      gbar_elem<OFMT>(a, c, s.head + 8 * s.nvec + (t - s.head), k);
+    for (int64_t t = threadIdx.x; t < s.head + tail; t += BLK)
+      gbar_elem<OFMT>(a, c, t < s.head ? t : s.head + 8 * s.nvec + (t - s.head), k);
   }
 }
 
@@ -448,10 +446,15 @@ hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, 
   a.total_sq = total_sq;
   a.max_norm = max_norm;
   a.skip_nonfinite = skip_nonfinite;
-  const int64_t ntiles = s.scalar_only ? (s.n + kTile - 1) / kTile : (s.nvec + kBlock - 1) / kBlock;
+  // one wave per workgroup, one 512-parameter tile each, as the fused step
+  // (two runs in separate processes: 5.72 / 5.20 ms against 5.95 / 5.29 ms
+  // for four-wave 2048-parameter tiles on the 70B/64 shard)
+  constexpr int BLK = kFlatBlock;
+  constexpr int64_t kT = 8 * BLK;
+  const int64_t ntiles = s.scalar_only ? (s.n + kT - 1) / kT : (s.nvec + BLK - 1) / BLK;
   // consecutive launches of at most launch_bytes() each (30 bytes per
   // parameter); the first also takes the head and tail elements
-  const int64_t per = units_per_launch(30 * (int64_t)kTile, 1);
+  const int64_t per = units_per_launch(30 * kT, 1);
   int64_t lo = 0;
   do {
     const int64_t hi = ntiles - lo > per ? lo + per : ntiles;
@@ -462,9 +465,9 @@ hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, 
     if (grid < 1) grid = 1;
     (void)hipGetLastError();
     if (param_format == 1)
-      gbar_kernel<kFP16><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
+      gbar_kernel<kFP16, BLK><<<dim3(grid), dim3(BLK), 0, stream>>>(a);
     else
-      gbar_kernel<kBF16><<<dim3(grid), dim3(kBlock), 0, stream>>>(a);
+      gbar_kernel<kBF16, BLK><<<dim3(grid), dim3(BLK), 0, stream>>>(a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     lo = hi;
