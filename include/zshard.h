@@ -306,9 +306,14 @@ ZS_API zs_status zs_loss_scaler_init(zs_loss_scaler* s, double initial_scale, do
                                      int64_t hysteresis);
 
 /* Records one step's outcome and returns 1 if the step was taken.  On
-   overflow: the step is skipped and, once `hysteresis` overflows have been
-   seen since the scale last changed, the scale halves (not below min_scale).
-   After `window` consecutive clean steps the scale doubles. */
+   overflow the step is skipped, and the scale halves (not below min_scale) on
+   every overflow from the `hysteresis`-th one counted since the budget was
+   last restored.  After `window` consecutive clean steps the scale doubles,
+   and only that growth restores the budget: a halving does not, nor does a
+   clean step short of the window (DeepSpeed's default reading of the fp16
+   block's hysteresis, which the page sets without defining it).
+   state.overflows counts overflows since the last restore, up to hysteresis;
+   state.clean counts clean steps since the last overflow or growth. */
 ZS_API int32_t zs_loss_scaler_update(zs_loss_scaler* s, int32_t overflow);
 
 /* The same update, on the device, enqueued on `stream` after the work that

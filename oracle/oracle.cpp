@@ -52,10 +52,15 @@
 //          double and k = f32(min(c, 1)) (k = 1 without clipping), the update
 //          above runs on g_i * k (one fp32 multiply) and writes the working copy
 //          as bf16 or fp16 (round to nearest even).
-//  scaler  dynamic loss scale: on overflow the scale halves (not below the
-//          minimum) once `hysteresis` overflows have been seen since the last
-//          change, and the step is skipped; after `window` consecutive clean
-//          steps the scale doubles and the overflow count restarts.
+//  scaler  dynamic loss scale: an overflow skips the step; the scale halves
+//          (not below the minimum) on every overflow from the `hysteresis`-th
+//          one counted since the budget was last restored.  The budget is
+//          restored only when the scale grows: after `window` consecutive
+//          clean steps the scale doubles and the count restarts.  A halving
+//          does not restore it, nor does a clean step short of the window.
+//          This is how DeepSpeed's dynamic loss scaler, the system whose fp16
+//          block the ZeRO-3 page's §8 prints, spends its hysteresis by
+//          default; the page itself does not define the knob.
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -292,8 +297,9 @@ int oracle_adam_from_gbar(const float* gbar, int64_t n, float* P, float* M, floa
   return 0;
 }
 
-// Dynamic loss scale (fp16 training).  state: {scale, overflows since the last
-// change, clean steps since the last change}.  Returns 1 if the step is taken.
+// Dynamic loss scale (fp16 training).  state: {scale, overflows since the
+// budget was last restored (counted up to `hysteresis`), clean steps since the
+// last overflow or growth}.  Returns 1 if the step is taken.
 typedef struct oracle_scaler {
   double scale, min_scale;
   int64_t window, hysteresis, overflows, clean;
@@ -301,11 +307,10 @@ typedef struct oracle_scaler {
 
 int oracle_scaler_update(oracle_scaler* s, int32_t overflow) {
   if (overflow) {
-    s->overflows += 1;
     s->clean = 0;
+    if (s->overflows < s->hysteresis) s->overflows += 1;
     if (s->overflows >= s->hysteresis) {
       s->scale = s->scale / 2.0 < s->min_scale ? s->min_scale : s->scale / 2.0;
-      s->overflows = 0;
     }
     return 0;
   }
@@ -313,7 +318,7 @@ int oracle_scaler_update(oracle_scaler* s, int32_t overflow) {
   if (s->clean >= s->window) {
     s->scale *= 2.0;
     s->clean = 0;
-    s->overflows = 0;
+    s->overflows = 0;  // growth restores the budget
   }
   return 1;
 }

@@ -579,18 +579,29 @@ def clipped_step_flat(grads: Sequence, master, m, v, param, hp, step: int, max_n
     one (one GPU).  Returns the device tensor holding the squared norm: a
     non-finite value means the step was skipped (an fp16 overflow)."""
     n = master.numel()
+    own = []  # buffers allocated here: torch's allocator must not hand them out before `stream` is done
     if workspace is None:
         workspace = torch.empty(two_pass_workspace_bytes(n), dtype=torch.uint8, device=master.device)
+        own.append(workspace)
     if sqnorm is None:
         sqnorm = torch.empty(1, dtype=torch.float64, device=master.device)
+        own.append(sqnorm)
     reduce_grads_flat(grads, workspace, sqnorm, loss_scale, grad_format, stream)
     adam_from_grads_flat(workspace, n, master, m, v, param, hp, step, sqnorm, max_norm, param_format, True, stream)
+    if stream is not None and own:
+        # the allocations were made on torch's current stream, the work runs on `stream`: tie their reuse
+        # to `stream` so a later allocation cannot take them while either pass is still queued there
+        ts = stream if isinstance(stream, torch.cuda.Stream) else \
+            torch.cuda.ExternalStream(stream, device=master.device)
+        for t in own:
+            t.record_stream(ts)
     return sqnorm
 
 
 class LossScaler:
-    """Dynamic loss scale for fp16 training: halves after `hysteresis` overflows
-    (not below `min_scale`), doubles after `window` clean steps."""
+    """Dynamic loss scale for fp16 training: doubles after `window` clean steps;
+    an overflow halves it (not below `min_scale`) once `hysteresis` overflows
+    have been counted since the last growth (see zs_loss_scaler_update)."""
 
     def __init__(self, initial_scale: float = 2.0 ** 16, min_scale: float = 1.0, window: int = 1000,
                  hysteresis: int = 2):

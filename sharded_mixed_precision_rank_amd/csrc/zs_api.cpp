@@ -974,10 +974,11 @@ int32_t zs_loss_scaler_update(zs_loss_scaler* s, int32_t overflow) {
   if (!s) return 0;
   if (overflow) {
     s->clean = 0;
-    if (++s->overflows >= s->hysteresis) {
+    // the budget is spent by overflows and restored only by growth
+    if (s->overflows < s->hysteresis) ++s->overflows;
+    if (s->overflows >= s->hysteresis) {
       const double half = s->scale / 2.0;
       s->scale = half < s->min_scale ? s->min_scale : half;
-      s->overflows = 0;
     }
     return 0;
   }

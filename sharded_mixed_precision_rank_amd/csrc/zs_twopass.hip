@@ -411,10 +411,10 @@ __global__ void scaler_update_kernel(zs_loss_scaler* __restrict__ s, const doubl
   double scale = s->scale;
   if (overflow) {
     clean = 0;
-    if (++overflows >= s->hysteresis) {
+    if (overflows < s->hysteresis) ++overflows;
+    if (overflows >= s->hysteresis) {
       const double half = scale / 2.0;
       scale = half < s->min_scale ? s->min_scale : half;
-      overflows = 0;
     }
   } else if (++clean >= s->window) {
     scale *= 2.0;

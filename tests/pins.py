@@ -440,23 +440,48 @@ def pin_overflow_skips(o):
 # ---------------------------------------------------------------------- P17
 def pin_loss_scaler(o):
     """The dynamic loss scale of the DeepSpeed fp16 block: start 2^16, window
-    1000, hysteresis 2, minimum 1 (scripted sequence with hand-derived states)."""
+    1000, hysteresis 2, minimum 1.  Scripted sequence with hand-derived
+    states.  hysteresis is a DeepSpeed knob the page sets but does not define;
+    the reading taken is DeepSpeed's default one: the overflow budget is spent
+    by overflows and restored only when the scale grows, so once it is spent
+    every further overflow halves.  The steps marked (*) separate that reading
+    from two others: a budget restored at every halving, and a budget restored
+    by any clean step."""
     s = o.scaler(2.0 ** 16, 1.0, 1000, 2)
     for _ in range(999):
         assert o.scaler_update(s, False)
     assert s.scale == 2.0 ** 16
     assert o.scaler_update(s, False) and s.scale == 2.0 ** 17          # 1000 clean steps: grow
-    assert not o.scaler_update(s, True) and s.scale == 2.0 ** 17       # first overflow: hysteresis holds
-    assert not o.scaler_update(s, True) and s.scale == 2.0 ** 16       # second: halve
+    assert not o.scaler_update(s, True) and s.scale == 2.0 ** 17       # first overflow: the budget holds
+    assert o.scaler_update(s, False) and s.scale == 2.0 ** 17          # one clean step ...
+    assert not o.scaler_update(s, True) and s.scale == 2.0 ** 16       # (*) ... does not restore it: halve
+    assert not o.scaler_update(s, True) and s.scale == 2.0 ** 15       # (*) a halving does not restore it
+    assert not o.scaler_update(s, True) and s.scale == 2.0 ** 14       # every overflow now halves
     for _ in range(40):
         o.scaler_update(s, True)
     assert s.scale == 1.0                                             # never below the minimum
     for _ in range(500):
         o.scaler_update(s, False)
     assert not o.scaler_update(s, True) and s.scale == 1.0            # the clean run restarts
-    for _ in range(1000):
-        o.scaler_update(s, False)
-    assert s.scale == 2.0
+    for _ in range(999):
+        assert o.scaler_update(s, False) and s.scale == 1.0
+    assert o.scaler_update(s, False) and s.scale == 2.0               # growth ...
+    assert not o.scaler_update(s, True) and s.scale == 2.0            # (*) ... restores the budget
+    assert not o.scaler_update(s, True) and s.scale == 1.0
+    # hysteresis 1: every overflow halves; hysteresis 3: the third halves
+    s1 = o.scaler(8.0, 1.0, 1000, 1)
+    assert not o.scaler_update(s1, True) and s1.scale == 4.0
+    assert not o.scaler_update(s1, True) and s1.scale == 2.0
+    s3 = o.scaler(8.0, 1.0, 4, 3)
+    assert not o.scaler_update(s3, True) and s3.scale == 8.0
+    assert not o.scaler_update(s3, True) and s3.scale == 8.0
+    assert not o.scaler_update(s3, True) and s3.scale == 4.0
+    for _ in range(3):
+        assert o.scaler_update(s3, False) and s3.scale == 4.0
+    assert o.scaler_update(s3, False) and s3.scale == 8.0            # window 4: grow, budget restored
+    assert not o.scaler_update(s3, True) and s3.scale == 8.0
+    assert not o.scaler_update(s3, True) and s3.scale == 8.0
+    assert not o.scaler_update(s3, True) and s3.scale == 4.0
 
 
 TWO_PASS = [pin_f16_casts, pin_two_pass_equals_fused, pin_unscale_and_fp16_grads, pin_sqnorm, pin_clipping,

@@ -6,10 +6,12 @@ oracle recomputes each sampled position from the host's draws of the same
 counters, so no expected value comes from the device.  The tiny workload is
 compared at every position.  Ragged lists also check every gap position
 between tensors (the step must leave it untouched).  The two-pass global
-norm, which no sample covers, is checked against the float64 sum of squares
-of the fp32 mean-gradient buffer, whose values are themselves checked at the
-sampled positions.
+norm, which no sample covers, is the oracle's own: its mean gradient over the
+whole shard (from the generator's replica values) and its sum of squares over
+that, in index order; the GPU's norm is only compared with it.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -48,6 +50,41 @@ def positions(w, L, seed=1234):
         idx = idx[inside[idx]]
         gaps = np.flatnonzero(~inside)
     return idx, gaps
+
+
+def host_threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_full_mean_and_norm(orc, torch, G, fmt, loss_scale, slice_elems=1 << 23):
+    """The oracle's pass 1 over the whole shard and its squared norm of the
+    result (one sum over every position, in index order, as the oracle defines
+    it).  The replica values are the generator's draws: they are copied from
+    the device buffers the library only reads, slice by slice, through pinned
+    memory."""
+    import torch as _t
+
+    N, n = len(G), G[0].numel()
+    gbar = np.empty(n, dtype=np.float32)
+    buf = _t.empty((N, min(n, slice_elems)), dtype=_t.int16).pin_memory()
+    for lo in range(0, n, slice_elems):
+        hi = min(n, lo + slice_elems)
+        for r in range(N):
+            buf[r, :hi - lo].copy_(G[r][lo:hi].view(_t.int16), non_blocking=True)
+        torch.cuda.synchronize()
+        rows = [buf[r, :hi - lo].numpy().view(np.uint16) for r in range(N)]
+        gbar[lo:hi] = orc.reduce_unscale(rows, fmt, loss_scale, threads=host_threads())
+    del buf
+    return gbar, orc.sqnorm(gbar)
+
+
+def assert_norm(orc, sqv, ref_sq, n, max_norm):
+    """The GPU's squared norm against the oracle's: both sum the same n
+    non-negative doubles, in different orders, so they differ by at most
+    2(n-1)u of the sum (u = 2^-53); and the fp32 clip coefficient, which is
+    what the update uses, must be the same."""
+    assert abs(sqv - ref_sq) <= 2 * max(n - 1, 1) * 2.0 ** -53 * ref_sq, (sqv, ref_sq)
+    assert orc.clip_coef(sqv, max_norm) == orc.clip_coef(ref_sq, max_norm), (sqv, ref_sq)
 
 
 def gather(torch, d, idx):
@@ -126,9 +163,12 @@ def test_two_pass_full_size(orc, path):
     start = (256 - ws.data_ptr() % 256) % 256
     gbar = ws[start:start + 4 * n].view(torch.float32)
     sqv = float(sq.item())
-    # the norm: a property at any size, against the buffer the sampled checks pin below
-    ref_sq = float((gbar.double() ** 2).sum().item())
-    assert abs(sqv - ref_sq) <= 1e-12 * ref_sq, (sqv, ref_sq)
+    gfmt = 1 if path == "fp16" else 0
+    # the oracle's own norm over the whole shard; the GPU's is only compared with it
+    print(f"two-pass {path}: oracle pass 1 over {n} positions x {w.N} replicas", flush=True)
+    ref_gbar, ref_sq = oracle_full_mean_and_norm(orc, torch, d["G"], gfmt, loss_scale)
+    assert_norm(orc, sqv, ref_sq, n, 1.0)
+    assert orc.clip_coef(ref_sq, 1.0) < 1.0  # clipping is active
     idx, _ = positions(w, n)
     it = torch.from_numpy(idx).to("cuda")
     gbar_s = gbar[it].cpu().numpy()
@@ -138,18 +178,58 @@ def test_two_pass_full_size(orc, path):
     h = W.host_inputs_at(w, idx)
     if path == "fp16":
         G = np.stack([orc.f16(synth.normal_f32_at(k["G"][r], idx, w.g_sigma * loss_scale)) for r in range(w.N)])
-        gfmt = 1
     else:
-        G, gfmt = h["G"], 0
+        G = h["G"]
     g = orc.reduce_unscale(G, gfmt, loss_scale)
+    # the replica values the whole-shard pass read are the host generator's at the sampled positions
+    assert np.array_equal(ref_gbar[idx].view(np.uint32), g.view(np.uint32)), "replica values"
     assert np.array_equal(gbar_s.view(np.uint32), g.view(np.uint32)), "pass 1 mean gradient"
-    P, M, V, B, taken = orc.adam_from_gbar(g, h["P"], h["M"], h["V"], w.hp(), w.step, sqv, 1.0, out_fmt=gfmt)
+    del ref_gbar
+    P, M, V, B, taken = orc.adam_from_gbar(g, h["P"], h["M"], h["V"], w.hp(), w.step, ref_sq, 1.0, out_fmt=gfmt)
     assert taken
     ref = dict(P=P, M=M, V=V, B=B)
     for key in "PMV":
         parity.assert_f32(got[key], ref[key], f"{path} {key}")
     assert parity.bit_identical(got, ref), path
     del d, ws, sq, gbar
+    torch.cuda.empty_cache()
+
+
+def test_clipped_step_every_position_124m(orc):
+    """The 124M-parameter shard (N=8) through both passes with global-norm
+    clipping at 1.0, compared at every position: the oracle's mean gradient
+    over the whole shard, its norm, and its update from the pristine state."""
+    import torch
+
+    import sharded_mixed_precision_rank_amd as zs
+    from synth import workloads as W
+
+    w = W.FLAT_124M_N8
+    zs.set_grid_blocks(0)
+    d = W.device_inputs(w)
+    n = d["arena_len"]
+    host = {k: d[k].cpu().numpy().copy() for k in "PMV"}  # the generator's draws, before the step
+    ref_gbar, ref_sq = oracle_full_mean_and_norm(orc, torch, d["G"], 0, 1.0)
+    assert orc.clip_coef(ref_sq, 1.0) < 1.0  # clipping is active
+    ws = torch.empty(zs.two_pass_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    sq = torch.empty(1, dtype=torch.float64, device="cuda")
+    zs.reduce_grads_flat(d["G"], ws, sq)
+    torch.cuda.synchronize()
+    start = (256 - ws.data_ptr() % 256) % 256
+    gbar = ws[start:start + 4 * n].view(torch.float32).cpu().numpy()
+    assert np.array_equal(gbar.view(np.uint32), ref_gbar.view(np.uint32)), "pass 1 mean gradient"
+    assert_norm(orc, float(sq.item()), ref_sq, n, 1.0)
+    zs.adam_from_grads_flat(ws, n, d["P"], d["M"], d["V"], d["B"], w.hp(), w.step, sq, 1.0)
+    torch.cuda.synchronize()
+    got = dict(P=d["P"].cpu().numpy(), M=d["M"].cpu().numpy(), V=d["V"].cpu().numpy(),
+               B=d["B"].view(torch.int16).cpu().numpy().view(np.uint16))
+    P, M, V, B, taken = orc.adam_from_gbar(ref_gbar, host["P"], host["M"], host["V"], w.hp(), w.step, ref_sq, 1.0,
+                                           threads=host_threads())
+    assert taken
+    ref = dict(P=P, M=M, V=V, B=B)
+    parity.assert_step(got, ref, "clipped 124M, every position")
+    assert parity.bit_identical(got, ref)
+    del d, ws, sq
     torch.cuda.empty_cache()
 
 

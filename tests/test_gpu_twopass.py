@@ -54,6 +54,17 @@ def run(env, host, hp, t, max_norm=0.0, loss_scale=1.0, gfmt="bf16", pfmt="bf16"
     return gbar, sqv, got
 
 
+def oracle_pass2(orc, host, ref_g, sqv, hp, t, max_norm, out_fmt=0):
+    """Pass 2 of the oracle on its own mean gradient and its own squared norm.
+    The GPU's norm (sqv) is only compared: within 1e-12 relative (the two sum
+    the same doubles in different orders) and giving the same fp32 clip
+    coefficient."""
+    ref_sq = orc.sqnorm(ref_g)
+    assert abs(sqv - ref_sq) <= 1e-12 * ref_sq, (sqv, ref_sq)
+    assert orc.clip_coef(sqv, max_norm) == orc.clip_coef(ref_sq, max_norm)
+    return orc.adam_from_gbar(ref_g, host["P"], host["M"], host["V"], hp, t, ref_sq, max_norm, out_fmt=out_fmt)
+
+
 @pytest.mark.parametrize("N", [1, 3, 8, 64])
 @pytest.mark.parametrize("n", [1, 2047, 2048, 100_003])
 def test_two_pass_equals_fused_and_oracle(env, orc, N, n):
@@ -67,7 +78,7 @@ def test_two_pass_equals_fused_and_oracle(env, orc, N, n):
     ref_sq = orc.sqnorm(ref_g)
     assert abs(sqv - ref_sq) <= 1e-12 * ref_sq
     # pass 2 against the oracle and against the fused step
-    P1, M1, V1, B1, taken = orc.adam_from_gbar(ref_g, host["P"], host["M"], host["V"], HP, 12, sqv, 0.0)
+    P1, M1, V1, B1, taken = oracle_pass2(orc, host, ref_g, sqv, HP, 12, 0.0)
     assert taken
     assert parity.bit_identical(got, dict(P=P1, M=M1, V=V1, B=B1))
     fP, fM, fV, fB = orc.step(host["G"], host["P"], host["M"], host["V"], HP, 12)
@@ -81,12 +92,12 @@ def test_clipping_matches_oracle(env, orc, shrink):
     ref_g = orc.reduce_unscale(host["G"], 0, 1.0)
     norm = orc.sqnorm(ref_g) ** 0.5
     gbar, sqv, got = run(env, host, HP, 300, max_norm=norm / shrink)
-    P1, M1, V1, B1, taken = orc.adam_from_gbar(ref_g, host["P"], host["M"], host["V"], HP, 300, sqv, norm / shrink)
+    assert np.array_equal(gbar.view(np.uint32), ref_g.view(np.uint32))
+    assert orc.clip_coef(orc.sqnorm(ref_g), norm / shrink) < 1.0  # clipping is active
+    P1, M1, V1, B1, taken = oracle_pass2(orc, host, ref_g, sqv, HP, 300, norm / shrink)
     ref = dict(P=P1, M=M1, V=V1, B=B1)
     parity.assert_step(got, ref, f"clip /{shrink}")
     assert parity.bit_identical(got, ref)
-    # and with the oracle's own norm: the coefficient agrees
-    assert orc.clip_coef(sqv, norm / shrink) == orc.clip_coef(orc.sqnorm(ref_g), norm / shrink)
 
 
 @pytest.mark.parametrize("loss_scale", [1.0, 2.0 ** 8, 2.0 ** 16])
@@ -96,7 +107,7 @@ def test_fp16_loss_scaled_grads_and_fp16_copy(env, orc, loss_scale):
     gbar, sqv, got = run(env, host, HP, 40, max_norm=1.0, loss_scale=loss_scale, gfmt="fp16", pfmt="fp16")
     ref_g = orc.reduce_unscale(host["G"], 1, loss_scale)
     assert np.array_equal(gbar.view(np.uint32), ref_g.view(np.uint32))
-    P1, M1, V1, B1, taken = orc.adam_from_gbar(ref_g, host["P"], host["M"], host["V"], HP, 40, sqv, 1.0, out_fmt=1)
+    P1, M1, V1, B1, taken = oracle_pass2(orc, host, ref_g, sqv, HP, 40, 1.0, out_fmt=1)
     ref = dict(P=P1, M=M1, V=V1, B=B1)
     for k in "PMV":
         parity.assert_f32(got[k], ref[k], k)
@@ -116,14 +127,18 @@ def test_fp16_overflow_skips_the_step(env, orc):
 
 
 def test_misaligned_two_pass(env, orc):
+    """Offsets 1..63 put up to 63 elements in the head partial of the norm;
+    clipping is active, so a wrong head partial would change every update."""
     rng = np.random.default_rng(11)
     host = rand_case(rng, 3, 9_999)
+    ref_g = orc.reduce_unscale(host["G"], 0, 1.0)
+    max_norm = orc.sqnorm(ref_g) ** 0.5 / 3
+    assert orc.clip_coef(orc.sqnorm(ref_g), max_norm) < 0.5
     for off in (1, 3, 8, 40, 63):
-        gbar, sqv, got = run(env, host, HP, 2, max_norm=0.5, offset=off)
-        ref_g = orc.reduce_unscale(host["G"], 0, 1.0)
+        gbar, sqv, got = run(env, host, HP, 2, max_norm=max_norm, offset=off)
         assert np.array_equal(gbar.view(np.uint32), ref_g.view(np.uint32))
-        P1, M1, V1, B1, _ = orc.adam_from_gbar(ref_g, host["P"], host["M"], host["V"], HP, 2, sqv, 0.5)
-        assert parity.bit_identical(got, dict(P=P1, M=M1, V=V1, B=B1))
+        P1, M1, V1, B1, _ = oracle_pass2(orc, host, ref_g, sqv, HP, 2, max_norm)
+        assert parity.bit_identical(got, dict(P=P1, M=M1, V=V1, B=B1)), off
 
 
 def test_norm_does_not_depend_on_launch_size(env):
@@ -165,7 +180,36 @@ def test_clipped_step_convenience(env, orc):
     sq = zs.clipped_step_flat(G, P, M, V, B, HP, 3, max_norm=0.01)
     torch.cuda.synchronize()
     ref_g = orc.reduce_unscale(host["G"], 0, 1.0)
-    P1, M1, V1, B1, _ = orc.adam_from_gbar(ref_g, host["P"], host["M"], host["V"], HP, 3, sq.item(), 0.01)
+    P1, M1, V1, B1, _ = oracle_pass2(orc, host, ref_g, sq.item(), HP, 3, 0.01)
+    got = dict(P=P.cpu().numpy(), M=M.cpu().numpy(), V=V.cpu().numpy(), B=B.cpu().numpy().view(np.uint16))
+    assert parity.bit_identical(got, dict(P=P1, M=M1, V=V1, B=B1))
+
+
+def test_clipped_step_on_a_side_stream(env, orc):
+    """clipped_step_flat on a non-default stream, with its workspace allocated
+    by the call: allocations made on the current stream right after it must not
+    take that workspace while the side stream still has the passes queued."""
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    rng = np.random.default_rng(19)
+    n = 3_000_017
+    host = rand_case(rng, 8, n)
+    G = [torch.from_numpy(g.view(np.int16)).to(dev) for g in host["G"]]
+    P, M, V = (torch.from_numpy(host[k]).to(dev) for k in "PMV")
+    B = torch.zeros(n, dtype=torch.int16, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    # keep the side stream busy first, so both passes are still queued when the call returns
+    big = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    with torch.cuda.stream(side):
+        for _ in range(8):
+            big.mul_(1.0)
+    sq = zs.clipped_step_flat(G, P, M, V, B, HP, 4, max_norm=0.05, stream=side)
+    # allocations of the workspace's size on the current stream, filled at once
+    junk = [torch.full((zs.two_pass_workspace_bytes(n) // 4,), float("nan"), device=dev) for _ in range(3)]
+    torch.cuda.synchronize()
+    del junk, big
+    ref_g = orc.reduce_unscale(host["G"], 0, 1.0)
+    P1, M1, V1, B1, _ = oracle_pass2(orc, host, ref_g, sq.item(), HP, 4, 0.05)
     got = dict(P=P.cpu().numpy(), M=M.cpu().numpy(), V=V.cpu().numpy(), B=B.cpu().numpy().view(np.uint16))
     assert parity.bit_identical(got, dict(P=P1, M=M1, V=V1, B=B1))
 

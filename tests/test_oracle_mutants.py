@@ -55,6 +55,14 @@ MUTANTS = [
     ("scaler_window_off_by_one", "if (s->clean >= s->window) {", "if (s->clean > s->window) {"),
     ("scaler_no_floor", "s->scale = s->scale / 2.0 < s->min_scale ? s->min_scale : s->scale / 2.0;",
      "s->scale = s->scale / 2.0;"),
+    # the other readings of hysteresis: the budget restored at every halving, by any clean step, or never
+    ("scaler_budget_restored_on_halving",
+     "s->scale = s->scale / 2.0 < s->min_scale ? s->min_scale : s->scale / 2.0;",
+     "s->scale = s->scale / 2.0 < s->min_scale ? s->min_scale : s->scale / 2.0; s->overflows = 0;"),
+    ("scaler_budget_restored_on_clean", "  s->clean += 1;\n", "  s->clean += 1;\n  s->overflows = 0;\n"),
+    ("scaler_budget_never_restored", "    s->overflows = 0;  // growth restores the budget", ""),
+    ("scaler_overflow_keeps_clean_run", "    s->clean = 0;\n    if (s->overflows < s->hysteresis)",
+     "    if (s->overflows < s->hysteresis)"),
 ]
 
 
