@@ -99,7 +99,7 @@ def counter_traffic(w, kernel: str):
 
 def pattern_ceiling(w, d, window=(0, 0), reps: int = 5):
     """What the memory system delivers for the step's own access pattern on this machine: the measurement
-    probe (libzshard_probe.so) replays the fused kernel's loads and stores, tile layout and
+    probe (bench_probe/libzshard_probe.so) replays the fused kernel's loads and stores, tile layout and
     non-temporal hints included, with the AdamW arithmetic taken out, on the same buffers.  Reported as
     GB/s of the pattern's own bytes for the read streams alone ((2N+12) B/param), for the full
     read+write mix ((2N+26) B/param) with each tile's writes issued as soon as it is done, and, when the
@@ -109,16 +109,9 @@ def pattern_ceiling(w, d, window=(0, 0), reps: int = 5):
 
     import torch
 
-    path = os.path.join(ROOT, "sharded_mixed_precision_rank_amd", "libzshard_probe.so")
-    lib = ctypes.CDLL(path)
-    lib.zs_probe_pattern.restype = ctypes.c_int
-    lib.zs_probe_pattern.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64,
-                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                     ctypes.c_int32, ctypes.c_void_p]
-    lib.zs_probe_pattern_windowed.restype = ctypes.c_int
-    lib.zs_probe_pattern_windowed.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64,
-                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    import bench_probe
+
+    lib = bench_probe.load()
     N, n = w.N, d["arena_len"]
     full = n // 512 * 512   # the probe covers whole 512-parameter tiles
     tab = (ctypes.c_void_p * N)(*[g.data_ptr() for g in d["G"]])
@@ -147,27 +140,34 @@ def pattern_ceiling(w, d, window=(0, 0), reps: int = 5):
 
 
 def copy_ceiling(gbytes: float = 8.0, reps: int = 5) -> float:
-    """Read+write GB/s of a plain 16-byte-per-lane copy kernel over `gbytes`."""
+    """Read+write GB/s of the probe's copy kernel (built as the step's kernels are: one-wave
+    512-element tiles, whole-line lane layout, non-temporal loads and stores, launches of at most
+    3 GB) over `gbytes` in all, half read and half written: the box's rate for an even mix."""
     import torch
 
-    import synth
+    import bench_probe
 
-    n = int(gbytes * 1e9) // 16 * 4
-    src = torch.empty(n, dtype=torch.int32, device="cuda")
+    lib = bench_probe.load()
+    n = int(gbytes * 1e9) // 8
+    src = torch.empty(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    src.fill_(1)
-    synth.dev_copy16(src, dst, blocks=256 * 8)
+    src.fill_(1.0)
+    stream = torch.cuda.current_stream()
+    def call():
+        if lib.zs_probe_copy(src.data_ptr(), dst.data_ptr(), n, stream.cuda_stream) != 0:
+            raise RuntimeError("zs_probe_copy failed")
+    call()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    e0.record(stream)
     for _ in range(reps):
-        synth.dev_copy16(src, dst, blocks=256 * 8)
-    e1.record()
+        call()
+    e1.record(stream)
     torch.cuda.synchronize()
     t = e0.elapsed_time(e1) / 1e3 / reps
     del src, dst
     torch.cuda.empty_cache()
-    return 2 * n * 4 / t / 1e9
+    return 8 * n / t / 1e9
 
 
 def cpu_baseline(w, target_s: float) -> dict:

@@ -1,24 +1,31 @@
-// Measurement probe (libzshard_probe.so, not part of the library's ABI): the
-// fused step's exact HBM access pattern with the AdamW arithmetic taken out,
-// to measure what the memory system delivers for this mix of streams on the
-// box at hand.
+// Measurement probe for the benchmark (libzshard_probe.so; not part of the
+// library or its ABI).  Two instruments:
 //
-// Each workgroup takes one full 512-parameter tile (one wave), as the flat
-// kernel's workgroups do, with the same whole-line lane layout, SGPR-base
-// addressing, non-temporal accesses, state-before-replicas load order and
-// batched rank-ordered replica stream.  Then:
-//   write = 0: nothing is stored: the read streams alone, (2N + 12) bytes
-//              per parameter.  Every loaded value feeds one sum that an
-//              empty asm statement consumes, so no load can be dropped or
-//              moved behind a branch;
-//   write = 1: master, m, v and the 16-bit copy are written back with values
-//              that need one add per element: the full (2N + 26) bytes per
-//              parameter of the step;
-//   windowed:  (zs_probe_pattern_windowed) the writes of write = 1 grouped in
-//              device-clock windows, as the windowed flat step writes.
-// Only full tiles are processed; the caller passes arrays that start on a
-// 128-byte boundary.  The values written are meaningless: run the probe on
-// scratch state or after the state is no longer needed.
+// 1. The fused step's exact HBM access pattern with the AdamW arithmetic taken
+//    out, to measure what the memory system delivers for this mix of streams
+//    on the box at hand.  Each workgroup takes one full 512-parameter tile (one
+//    wave), as the flat kernel's workgroups do, with the same whole-line lane
+//    layout, SGPR-base addressing, non-temporal accesses,
+//    state-before-replicas load order and batched rank-ordered replica stream.
+//    Then:
+//      write = 0: nothing is stored: the read streams alone, (2N + 12) bytes
+//                 per parameter.  Every loaded value feeds one sum that an
+//                 empty asm statement consumes, so no load can be dropped or
+//                 moved behind a branch;
+//      write = 1: master, m, v and the 16-bit copy are written back with
+//                 values that need one add per element: the full (2N + 26)
+//                 bytes per parameter of the step;
+//      windowed:  (zs_probe_pattern_windowed) the writes of write = 1 grouped
+//                 in device-clock windows, as the windowed flat step writes.
+//    Only full tiles are processed; the caller passes arrays that start on a
+//    128-byte boundary.  The values written are meaningless: run the probe on
+//    scratch state or after the state is no longer needed.
+//
+// 2. A copy (zs_probe_copy): the box's rate for an even read/write stream,
+//    built the way the step's kernels are: one wave per 512-element fp32 tile,
+//    the whole-line lane layout (every access instruction covers whole 128-byte
+//    lines), SGPR-base addressing, non-temporal loads and stores, and
+//    consecutive launches of at most 3e9 bytes each.
 #include "zs_device.h"
 
 namespace zs {
@@ -169,6 +176,25 @@ hipError_t go(const uint16_t* const* g, int64_t tiles, float* p, float* m, float
   return hipGetLastError();
 }
 
+// One 512-element fp32 tile per one-wave workgroup, tiles [t0, t0 + gridDim.x);
+// the workgroup holding the last tile also copies the tail elements.
+__global__ __launch_bounds__(kFlatBlock) void copy_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                          int64_t t0, int64_t n) {
+  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  const int64_t t = t0 + blockIdx.x;
+  const int64_t e0 = t * (kFlatBlock * 8);
+  if (e0 + kFlatBlock * 8 <= n) {
+    const uint32_t o = here(Layout<true>::first()) * 4u;
+    const GLB f32x4* S = (const GLB f32x4*)at(tile_base(src + e0), o);
+    GLB f32x4* D = (GLB f32x4*)at(tile_base(dst + e0), o);
+    const f32x4 x = ld_g(S), y = ld_g(S + q2);
+    st_g(D, x);
+    st_g(D + q2, y);
+  } else {
+    for (int64_t i = e0 + threadIdx.x; i < n; i += kFlatBlock) dst[i] = src[i];
+  }
+}
+
 bool line_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 127) == 0; }
 
 }  // namespace
@@ -226,4 +252,27 @@ extern "C" __attribute__((visibility("default"))) int zs_probe_pattern(const uin
     default: return 1;
   }
   return e == hipSuccess ? 0 : 2;
+}
+
+// Copies n fp32 values src -> dst on `stream` (the arrays must not overlap and
+// must be 16-byte aligned).  Returns 0 on success, 1 for bad arguments, 2 for
+// a launch error.
+extern "C" __attribute__((visibility("default"))) int zs_probe_copy(const float* src, float* dst, int64_t n,
+                                                                    void* stream) {
+  using namespace zs;
+  if (n < 0 || (n > 0 && (!src || !dst))) return 1;
+  if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) != 0) return 1;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (n > 0 && s0 < d0 + 4 * (uintptr_t)n && d0 < s0 + 4 * (uintptr_t)n) return 1;
+  constexpr int64_t kTile = kFlatBlock * 8;
+  const int64_t tiles = (n + kTile - 1) / kTile;
+  const int64_t per = kLaunchBytes / (8 * kTile);  // tiles per launch: 8 bytes per element
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t t0 = 0; t0 < tiles; t0 += per) {
+    const int64_t cnt = tiles - t0 < per ? tiles - t0 : per;
+    (void)hipGetLastError();
+    copy_kernel<<<dim3((unsigned)cnt), dim3(kFlatBlock), 0, s>>>(src, dst, t0, n);
+    if (hipGetLastError() != hipSuccess) return 2;
+  }
+  return 0;
 }

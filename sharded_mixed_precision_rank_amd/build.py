@@ -1,14 +1,10 @@
-"""Builds libzshard.so (gfx950) in place with hipcc, and the measurement probe
-libzshard_probe.so (the step's access pattern without its arithmetic; used by
-the benchmark, not part of the library's ABI)."""
+"""Builds libzshard.so (gfx950) in place with hipcc."""
 import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libzshard.so")
-PROBE_LIB = os.path.join(HERE, "libzshard_probe.so")
-PROBE_SOURCES = [os.path.join(CSRC, "zs_probe.hip")]
 # Device code and HIP-runtime host code compile as HIP in one hipcc command.
 SOURCES = [os.path.join(CSRC, f) for f in ("zs_kernels.hip", "zs_twopass.hip", "zs_api.cpp", "zs_offload.cpp")]
 # The host AdamW is plain C++ built by the host compiler into an object that
@@ -55,8 +51,6 @@ def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
         subprocess.run(hcmd, check=True)
         objs.append(obj)
     _hipcc(SOURCES, objs, out, extra, verbose)
-    if out == LIB:
-        _hipcc(PROBE_SOURCES, [], PROBE_LIB, extra, verbose)
     return out
 
 

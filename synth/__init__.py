@@ -65,8 +65,6 @@ def _dev_lib():
         lib.synth_dev_fill_normal_f32.argtypes = [_u64, _u64, _i64, _dbl, _int, _vp, _vp]
         lib.synth_dev_fill_normal_bf16.restype = _int
         lib.synth_dev_fill_normal_bf16.argtypes = [_u64, _u64, _i64, _dbl, _u64, _u64, _vp, _vp]
-        lib.synth_dev_copy16.restype = _int
-        lib.synth_dev_copy16.argtypes = [_vp, _vp, _i64, _int, _vp]
         _dev = lib
     return _dev
 
@@ -151,11 +149,3 @@ def dev_fill_normal_bf16(t, k: int, offset: int, sigma: float, mask_key: int = 0
                                                _stream_ptr(stream))
     if rc:
         raise RuntimeError(f"synth_dev_fill_normal_bf16 failed: hip error {rc}")
-
-
-def dev_copy16(src, dst, blocks: int = 0, stream=None) -> None:
-    nbytes = src.numel() * src.element_size()
-    assert dst.numel() * dst.element_size() == nbytes and nbytes % 16 == 0
-    rc = _dev_lib().synth_dev_copy16(src.data_ptr(), dst.data_ptr(), nbytes // 16, blocks, _stream_ptr(stream))
-    if rc:
-        raise RuntimeError(f"synth_dev_copy16 failed: {rc}")

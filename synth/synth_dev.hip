@@ -1,12 +1,9 @@
-// Seeded synthetic inputs, device side, plus a plain streaming copy.
+// Seeded synthetic inputs, device side.
 //
 // Shared test/bench plumbing: fills device buffers with the same numbers the
 // host generator (synth_host.c) draws, so that inputs of 100+ GB never cross
 // PCIe.  Same definition, written again for the device; a GPU test checks the
 // two produce identical bits.  No optimizer arithmetic lives here.
-//
-// The copy kernel is the reference point for HBM measurements: a read and a
-// write of a known number of bytes, 16 bytes per lane, grid-stride.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,11 +46,6 @@ __global__ void fill_normal_bf16(uint64_t key, uint64_t offset, int64_t n, doubl
   }
 }
 
-__global__ void copy16(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n16; t += stride) dst[t] = src[t];
-}
-
 int grid_for(int64_t n) {
   int64_t b = (n + 255) / 256;
   if (b > 65536) b = 65536;
@@ -78,15 +70,6 @@ int synth_dev_fill_normal_bf16(uint64_t key, uint64_t offset, int64_t n, double 
   if (n <= 0) return 0;
   hipLaunchKernelGGL(fill_normal_bf16, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, key, offset, n, sigma,
                      mask_key, mask_thresh, out);
-  return (int)hipGetLastError();
-}
-
-// Copies n16 16-byte units; both pointers must be 16-byte aligned (checked).
-int synth_dev_copy16(const void* src, void* dst, int64_t n16, int blocks, void* stream) {
-  if (n16 <= 0) return 0;
-  if (((uintptr_t)src | (uintptr_t)dst) & 15u) return -1;
-  if (blocks <= 0) blocks = grid_for(n16);
-  hipLaunchKernelGGL(copy16, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, (uint4*)dst, n16);
   return (int)hipGetLastError();
 }
 

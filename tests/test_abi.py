@@ -279,25 +279,27 @@ def test_binding_rejects_tensors_on_several_devices():
 
 
 def test_probe_library_rejects_unsupported_arguments_without_gpu():
-    """The measurement probe (libzshard_probe.so) checks its arguments before any launch."""
-    path = os.path.join(os.path.dirname(zs.LIB_PATH), "libzshard_probe.so")
-    lib = ctypes.CDLL(path)
+    """The benchmark's measurement probe (bench_probe/libzshard_probe.so) checks its arguments before any
+    launch."""
+    import bench_probe
+
+    lib = bench_probe.load()
     f = lib.zs_probe_pattern
-    f.restype = ctypes.c_int
-    f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64] + [ctypes.c_void_p] * 4 + \
-        [ctypes.c_int32, ctypes.c_void_p]
     g = (ctypes.c_void_p * 3)(A + 0x100000, A + 0x200000, A + 0x300000)
     arr = [A + 0x400000, A + 0x500000, A + 0x600000, A + 0x700000]
     assert f(g, 3, 1 << 20, *arr, 0, None) == 1            # N = 3 is not covered
     assert f(g, 2, 500, *arr, 0, None) == 1                # less than one 512-parameter tile
     assert f(g, 2, 1 << 20, A + 0x400004, *arr[1:], 0, None) == 1   # not on a 128-byte boundary
     fw = lib.zs_probe_pattern_windowed
-    fw.restype = ctypes.c_int
-    fw.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64] + [ctypes.c_void_p] * 4 + \
-        [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     assert fw(g, 3, 1 << 20, *arr, 4096, 512, None) == 1   # N = 3 is not covered
     assert fw(g, 2, 500, *arr, 4096, 512, None) == 1       # less than one tile
     assert fw(g, 2, 1 << 20, *arr, 4000, 512, None) == 1   # period not a power of two
+    fc = lib.zs_probe_copy
+    assert fc(A + 0x100000, A + 0x200004, 1024, None) == 1  # not 16-byte aligned
+    assert fc(A + 0x100000, A + 0x100800, 1024, None) == 1  # overlapping arrays
+    assert fc(0, A + 0x200000, 1024, None) == 1             # NULL
+    assert fc(A + 0x100000, A + 0x200000, -1, None) == 1    # negative length
+    assert fc(0, 0, 0, None) == 0                           # nothing to copy
     assert fw(g, 2, 1 << 20, *arr, 32, 8, None) == 1       # period below 64 ticks
     assert fw(g, 2, 1 << 20, *arr, 4096, 4096, None) == 1  # window not shorter than the period
     assert fw(g, 2, 1 << 20, A + 0x400004, *arr[1:], 4096, 512, None) == 1

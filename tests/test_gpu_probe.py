@@ -3,7 +3,6 @@ as it was, and the read+write patterns (stores as each tile is done, and stores
 grouped in device-clock windows) touch exactly the full tiles and write the
 same values."""
 import ctypes
-import os
 
 import numpy as np
 import pytest
@@ -14,13 +13,10 @@ pytestmark = pytest.mark.gpu
 def test_probe_modes():
     import torch
 
-    import sharded_mixed_precision_rank_amd as zs
+    import bench_probe
 
-    lib = ctypes.CDLL(os.path.join(os.path.dirname(zs.LIB_PATH), "libzshard_probe.so"))
+    lib = bench_probe.load()
     f = lib.zs_probe_pattern
-    f.restype = ctypes.c_int
-    f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64] + [ctypes.c_void_p] * 4 + \
-        [ctypes.c_int32, ctypes.c_void_p]
     dev = torch.device("cuda:0")
     N, n = 8, 12 * 512 + 100   # twelve full 512-parameter tiles and a partial one
     gen = torch.Generator().manual_seed(5)
@@ -45,12 +41,43 @@ def test_probe_modes():
     for x, b0 in zip((P, M, V, B), before):
         x.copy_(b0)
     fw = lib.zs_probe_pattern_windowed
-    fw.restype = ctypes.c_int
-    fw.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64] + [ctypes.c_void_p] * 4 + \
-        [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     assert fw(tab, N, n, P.data_ptr(), M.data_ptr(), V.data_ptr(), B.data_ptr(), 256, 32, s) == 0
     torch.cuda.synchronize()
     # bit patterns: the random 16-bit replicas include NaN encodings, and NaN != NaN
     bits = lambda x: x.view(torch.int32) if x.dtype == torch.float32 else x
     for a, b in zip((P, M, V, B), after):
         assert torch.equal(bits(a), bits(b)), "the windowed pattern wrote other values than the plain one"
+
+
+@pytest.mark.parametrize("n", [0, 1, 511, 512, 513, 12 * 512 + 100, 3_000_001])
+def test_probe_copy(n):
+    """The copy kernel copies every element, full tiles and the tail, and nothing past them."""
+    import torch
+
+    import bench_probe
+
+    lib = bench_probe.load()
+    dev = torch.device("cuda:0")
+    src = torch.randn(n + 64, generator=torch.Generator().manual_seed(n)).to(dev)
+    dst = torch.full((n + 64,), -7.0, device=dev)
+    assert lib.zs_probe_copy(src.data_ptr(), dst.data_ptr(), n, torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n], src[:n])
+    assert torch.all(dst[n:] == -7.0)
+
+
+def test_probe_copy_in_several_launches():
+    """Past 3e9 bytes the copy runs as consecutive launches; the boundary between them is exact."""
+    import torch
+
+    import bench_probe
+
+    lib = bench_probe.load()
+    n = 400_000_123   # 3.2 GB of traffic: two launches, the second starting at tile 732,421
+    src = torch.arange(n, dtype=torch.int32, device="cuda").view(torch.float32)
+    dst = torch.zeros(n, dtype=torch.float32, device="cuda")
+    assert lib.zs_probe_copy(src.data_ptr(), dst.data_ptr(), n, torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dst.view(torch.int32), src.view(torch.int32))
+    del src, dst
+    torch.cuda.empty_cache()

@@ -137,7 +137,7 @@ def test_two_pass_in_consecutive_launches(env, orc, fmt, offset):
     scale = 256.0 if fmt == "fp16" else 1.0
     host = rand_case(np.random.default_rng(17 + offset), N, n, fmt=fmt, scale=scale, orc=orc)
     base = run(env, host, HP_WD, 4, max_norm=0.05, loss_scale=scale, gfmt=fmt, offset=offset)
-    zs.set_launch_bytes(2 * 2048 * 30)  # two tiles of either pass per launch
+    zs.set_launch_bytes(2 * 2048 * 30)  # N = 8: three pass-1 tiles (2048 params) or eight pass-2 tiles (512) per launch
     try:
         gbar, sqv, got = run(env, host, HP_WD, 4, max_norm=0.05, loss_scale=scale, gfmt=fmt, offset=offset)
     finally:

@@ -28,14 +28,3 @@ def test_device_fill_matches_host(offset):
                           synth.normal_f32(synth.key(0, synth.KIND_V), offset, n, 1e-6, True).view(np.uint32))
     assert np.array_equal(g.view(torch.int16).cpu().numpy().view(np.uint16),
                           synth.normal_bf16(synth.key(0, synth.KIND_GRAD, 5), offset, n, 1e-3, km, th))
-
-
-def test_copy_kernel_copies():
-    import torch
-
-    dev = torch.device("cuda:0")
-    src = torch.arange(1 << 20, dtype=torch.int32, device=dev)
-    dst = torch.zeros_like(src)
-    synth.dev_copy16(src, dst)
-    torch.cuda.synchronize()
-    assert torch.equal(src, dst)
