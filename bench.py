@@ -382,29 +382,48 @@ def main() -> int:
     log(f"{ms:.3f} ms/step, {n / (ms / 1e3) / 1e9:.2f} G params/s, {achieved:.0f} GB/s "
         f"(per step: median {ms_median:.3f} ms, min {ms_min:.3f} ms)")
 
-    # the write window the step took (0, 0: none) and so the kernel that ran; a list plan takes the flat
-    # step's windows, by its total parameter count
+    # the flat step's schedule and the write window the step took (0, 0: none), and so the kernel that ran;
+    # a list plan takes the flat step's windows, by its total parameter count
+    flat_fused = offload is None and not two_pass and not w.is_list
+    sched = zs.flat_schedule(w.N, n) if flat_fused else None
     window = (0, 0) if offload is not None else zs.write_window("reduce" if two_pass else "flat", w.N, n)
+
+    def median_ms(k: int = 5) -> float:
+        step(w.step)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+        e[0].record()
+        for j in range(k):
+            step(w.step + 1 + j)
+            e[j + 1].record()
+        torch.cuda.synchronize()
+        return sorted(e[j].elapsed_time(e[j + 1]) for j in range(k))[k // 2]
+
     unwindowed = None
-    if window[0]:
+    other_schedules = None
+    if flat_fused:
+        # the same steps on the flat step's other schedules, in this process: what the schedule is worth
+        other_schedules = {}
+        for other in ("phased", "windowed", "stream"):
+            if other == sched:
+                continue
+            zs.set_flat_schedule(other)
+            if zs.flat_schedule(w.N, n) == other:
+                other_schedules[other] = {"ms_per_step_median": median_ms(), "steps": 5}
+                log(f"{other} schedule: {other_schedules[other]['ms_per_step_median']:.3f} ms/step (median of 5)")
+        zs.set_flat_schedule("auto")
+    elif window[0]:
         # the same steps with the windows switched off, in this process: the windows' own effect
         zs.set_write_window(1)
-        step(w.step)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        e[0].record()
-        for k in range(5):
-            step(w.step + 1 + k)
-            e[k + 1].record()
-        torch.cuda.synchronize()
+        unwindowed = {"ms_per_step_median": median_ms(), "steps": 5}
         zs.set_write_window(0)
-        gaps = sorted(e[k].elapsed_time(e[k + 1]) for k in range(5))
-        unwindowed = {"ms_per_step_median": gaps[2], "steps": 5}
-        log(f"without write windows: {gaps[2]:.3f} ms/step (median of 5)")
+        log(f"without write windows: {unwindowed['ms_per_step_median']:.3f} ms/step (median of 5)")
     tn = f"<{w.N}>" if w.N in (1, 2, 4, 8, 16, 32, 64) else "<0>"
     if w.is_list:
         kernel = ("list_window_kernel" if window[0] else "list_kernel") + tn
     elif two_pass:
         kernel = ("reduce_window_kernel" if window[0] else "reduce_kernel") + tn + " + gbar_kernel"
+    elif sched == "phased":
+        kernel = "flat_phased_kernel" + (tn if w.N == 64 else "<0>")
     else:
         kernel = ("flat_window_kernel" if window[0] else "flat_kernel") + tn
     pattern = None
@@ -440,13 +459,14 @@ def main() -> int:
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "n_params": n, "replicas": w.N, "adam_step": w.step,
                    "weight_decay": w.weight_decay, "path": args.path,
-                   "write_window_ticks": list(window) if window[0] else None,
+                   "schedule": sched, "write_window_ticks": list(window) if window[0] else None,
                    "max_bytes_per_launch": zs.launch_bytes(),
                    "storage": ("fp16" if args.path == "fp16" else "bf16") + " grads and working copy, fp32 master/m/v"},
         "hbm_GBps": achieved, "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,
         "copy_ceiling_GBps": ceiling,
         "pattern_ceiling": pattern,
         "without_write_windows": unwindowed,
+        "other_schedules": other_schedules,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic if args.path == "fused" else None,
                      "bytes_per_param": bpp, "kernel": kernel},

@@ -186,6 +186,7 @@ ZS_API zs_status zs_reduce_adam_list_plan_groups(zs_list_plan_t plan, const zs_a
 ZS_API zs_status zs_reduce_adam_list(const zs_tensor* tensors, int32_t T, int32_t N, const zs_adam_hp* hp,
                                      int64_t step, zs_stream stream);
 
+
 /* ---------------------------------------------------------------------------
  * Device-resident step index, for training steps captured once in a HIP graph
  * and replayed: the step index (and with it the bias corrections) must then
@@ -430,18 +431,79 @@ ZS_API int64_t zs_launch_bytes(void);
    Errors: ZS_ERR_RANGE. */
 ZS_API zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks);
 
-/* The write window a kernel takes, under the current setting, for N replicas
-   on a shard of n parameters whose arrays share a 128-byte line phase:
-     kernel = ZS_WINDOW_FLAT_STEP:   the flat step (zs_reduce_adam_flat), and
-                                     list plans of n parameters in all;
+/* The write window a kernel takes, under the current settings, for N
+   replicas on a shard of n parameters whose arrays share a 128-byte line
+   phase:
+     kernel = ZS_WINDOW_FLAT_STEP:   the flat step (zs_reduce_adam_flat): only
+                                     on the windowed schedule
+                                     (zs_set_flat_schedule), on shards of at
+                                     least 2^25 parameters;
      kernel = ZS_WINDOW_REDUCE_PASS: pass 1 of the two-pass form
                                      (zs_reduce_grads_flat), on shards of at
-                                     least 2^25 parameters.
+                                     least 2^25 parameters;
+     kernel = ZS_WINDOW_LIST_PLAN:   a list plan of n parameters in all (the
+                                     flat step's default windows for N, from
+                                     2^25 parameters on).
    *period_ticks = *open_ticks = 0 when it takes no windows.  No GPU call.
    Errors: ZS_ERR_NULL, ZS_ERR_RANGE. */
 #define ZS_WINDOW_FLAT_STEP 0
 #define ZS_WINDOW_REDUCE_PASS 1
+#define ZS_WINDOW_LIST_PLAN 2
 ZS_API zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* period_ticks, int32_t* open_ticks);
+
+/* The schedule of the flat step (zs_reduce_adam_flat and its device-step
+   form), for all later calls in this process.  Every schedule computes every
+   parameter by the same operations in the same order, so results do not
+   depend on it; only when the bytes move does.
+     ZS_SCHEDULE_AUTO:     the default.  An explicit zs_set_write_window
+                           decides when one was made (no windows:
+                           ZS_SCHEDULE_STREAM; a window: ZS_SCHEDULE_WINDOWED);
+                           otherwise ZS_SCHEDULE_PHASED for N >= 48 replicas on
+                           shards of at least 2^25 parameters, and
+                           ZS_SCHEDULE_STREAM below.
+     ZS_SCHEDULE_STREAM:   one 512-parameter tile per workgroup, its outputs
+                           stored as soon as it is done; consecutive launches
+                           of at most zs_launch_bytes() each.
+     ZS_SCHEDULE_WINDOWED: persistent waves that hold up to two finished tiles
+                           and store them in device-clock write windows
+                           (zs_set_write_window; the default window when none
+                           was set), on shards of at least 2^25 parameters
+                           (ZS_SCHEDULE_STREAM below).
+     ZS_SCHEDULE_PHASED:   one persistent workgroup of 12 waves per compute
+                           unit; the shard goes in super-chunks of 8 tiles per
+                           wave.  First every wave reads all N replicas of its
+                           tiles into register accumulators, the workgroup's
+                           waves kept on the same replicas, so the device
+                           reads one or two replica streams at a time over one
+                           contiguous region each; then, after a grid barrier,
+                           it reads master, m and v and writes the four
+                           outputs of the super-chunk.  Any shard of at least
+                           one whole tile.  The barrier counter lives in the
+                           library's device memory (16 slots, one per launch in
+                           turn): phased calls that run at the same time on one
+                           device may meet at each other's barriers, which
+                           changes their timing only.  A workgroup waits at a
+                           barrier at most zs_set_phased_max_polls() polls.
+   When the device cannot hold the persistent grid of the windowed or phased
+   kernel, the call takes ZS_SCHEDULE_STREAM.  Errors: ZS_ERR_RANGE. */
+#define ZS_SCHEDULE_AUTO 0
+#define ZS_SCHEDULE_STREAM 1
+#define ZS_SCHEDULE_WINDOWED 2
+#define ZS_SCHEDULE_PHASED 3
+ZS_API zs_status zs_set_flat_schedule(int32_t schedule);
+
+/* The schedule a flat step for N replicas on a shard of n parameters (arrays
+   on a common 128-byte line phase) takes under the current settings
+   (ZS_SCHEDULE_STREAM, _WINDOWED or _PHASED).  No GPU call.
+   Errors: ZS_ERR_NULL, ZS_ERR_RANGE. */
+ZS_API zs_status zs_flat_schedule(int32_t N, int64_t n, int32_t* schedule);
+
+/* The longest a workgroup of the phased schedule waits at a grid barrier, in
+   polls of about 50 ns (0: the default, 2^16, about 3 ms).  Past it the
+   workgroup goes on; results do not change, only the timing.  A test knob for
+   the bounded wait, and a guard for devices shared with other work.
+   Errors: ZS_ERR_RANGE (polls < 0). */
+ZS_API zs_status zs_set_phased_max_polls(int32_t polls);
 
 #ifdef __cplusplus
 }

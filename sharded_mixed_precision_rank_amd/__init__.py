@@ -96,7 +96,14 @@ _lib.zs_set_write_window.restype = ctypes.c_int
 _lib.zs_set_write_window.argtypes = [_i32, _i32]
 _lib.zs_write_window.restype = ctypes.c_int
 _lib.zs_write_window.argtypes = [_i32, _i32, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
-WINDOW_KERNELS = {"flat": 0, "reduce": 1}
+WINDOW_KERNELS = {"flat": 0, "reduce": 1, "list": 2}
+_lib.zs_set_flat_schedule.restype = ctypes.c_int
+_lib.zs_set_flat_schedule.argtypes = [_i32]
+_lib.zs_flat_schedule.restype = ctypes.c_int
+_lib.zs_flat_schedule.argtypes = [_i32, _i64, ctypes.POINTER(_i32)]
+_lib.zs_set_phased_max_polls.restype = ctypes.c_int
+_lib.zs_set_phased_max_polls.argtypes = [_i32]
+SCHEDULES = {"auto": 0, "stream": 1, "windowed": 2, "phased": 3}
 _lib.zs_two_pass_workspace_bytes.restype = ctypes.c_size_t
 _lib.zs_two_pass_workspace_bytes.argtypes = [_i64]
 _lib.zs_reduce_grads_flat.restype = ctypes.c_int
@@ -204,11 +211,31 @@ def set_write_window(period_ticks: int, open_ticks: int = 0) -> None:
 
 
 def write_window(kernel: str, N: int, n: int):
-    """(period_ticks, open_ticks) that the flat step (kernel="flat") or pass 1 of the two-pass form
-    (kernel="reduce") takes for N replicas on n parameters; (0, 0) = no windows."""
+    """(period_ticks, open_ticks) that the flat step (kernel="flat"), pass 1 of the two-pass form
+    (kernel="reduce") or a list plan (kernel="list", n parameters in all) takes for N replicas on n
+    parameters; (0, 0) = no windows."""
     p, o = _i32(), _i32()
     _check(_lib.zs_write_window(WINDOW_KERNELS[kernel], N, n, ctypes.byref(p), ctypes.byref(o)), "zs_write_window")
     return p.value, o.value
+
+
+def set_flat_schedule(schedule) -> None:
+    """How the flat step schedules its reads and writes: "auto" (the default), "stream", "windowed" or
+    "phased" (or the ZS_SCHEDULE_* value); see zs_set_flat_schedule.  Results do not depend on it."""
+    _check(_lib.zs_set_flat_schedule(SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)),
+           "zs_set_flat_schedule")
+
+
+def flat_schedule(N: int, n: int) -> str:
+    """The schedule ("stream", "windowed" or "phased") a flat step for N replicas on n parameters takes."""
+    out = _i32()
+    _check(_lib.zs_flat_schedule(N, n, ctypes.byref(out)), "zs_flat_schedule")
+    return {v: k for k, v in SCHEDULES.items()}[out.value]
+
+
+def set_phased_max_polls(polls: int) -> None:
+    """The longest wait at a grid barrier of the phased schedule, in polls of about 50 ns (0 = default)."""
+    _check(_lib.zs_set_phased_max_polls(polls), "zs_set_phased_max_polls")
 
 
 def _stream_handle(stream, device=None):

@@ -25,6 +25,11 @@ std::atomic<int64_t> g_launch_bytes{0};  // zs_set_launch_bytes; 0 = zs::kLaunch
 // one call's period with another's open length; period 0 = automatic, 1 = no
 // windows
 std::atomic<uint64_t> g_window{0};
+// zs_set_flat_schedule (0 = automatic) and zs_set_phased_max_polls (0 = default)
+std::atomic<int32_t> g_flat_schedule{0};
+std::atomic<int32_t> g_phased_max_polls{0};
+// the phased kernel's barrier-counter slot of the next launch (round robin)
+std::atomic<uint32_t> g_phased_slot{0};
 
 zs_status fail(zs_status st, const char* fmt, ...) {
   char buf[512];
@@ -190,6 +195,45 @@ zs::WriteWindow write_window(int32_t N) {
   if (period > 1) return zs::WriteWindow{(uint64_t)period - 1, (uint64_t)open};
   if (N < 48) return zs::WriteWindow{0, 0};
   return zs::WriteWindow{4096 - 1, N < 64 ? 640u : N <= 128 ? 512u : 384u};
+}
+
+// The flat step's schedule for N replicas on a shard of n parameters, and
+// the write window it takes (period_mask 0 unless windowed).  An explicit
+// zs_set_flat_schedule wins; otherwise an explicit zs_set_write_window decides
+// (no windows: per-tile stores; a window: the windowed kernel); otherwise the
+// phased kernel for N >= kPhasedMinReplicas on shards of at least
+// kPhasedMinParams, and per-tile stores below.
+zs::FlatSchedule flat_schedule(int32_t N, int64_t n, zs::WriteWindow* win) {
+  const int32_t forced = g_flat_schedule.load(std::memory_order_relaxed);
+  const uint64_t word = g_window.load(std::memory_order_relaxed);
+  const int32_t period = (int32_t)(word >> 32);
+  zs::FlatSchedule sched;
+  if (forced != 0)
+    sched = (zs::FlatSchedule)forced;
+  else if (period == 1)
+    sched = zs::FlatSchedule::kStream;
+  else if (period > 1)
+    sched = zs::FlatSchedule::kWindowed;
+  else
+    sched = N >= zs::kPhasedMinReplicas && n >= zs::kPhasedMinParams ? zs::FlatSchedule::kPhased
+                                                                      : zs::FlatSchedule::kStream;
+  zs::WriteWindow w{0, 0};
+  if (sched == zs::FlatSchedule::kWindowed) {
+    // an explicit window, none when windows were switched off, else the default for N (any N)
+    const int32_t open = (int32_t)(word & 0xFFFFFFFFu);
+    if (period > 1)
+      w = zs::WriteWindow{(uint64_t)period - 1, (uint64_t)open};
+    else if (period == 0)
+      w = zs::WriteWindow{4096 - 1, N < 64 ? 640u : N <= 128 ? 512u : 384u};
+  }
+  if (win) *win = w;
+  return sched;
+}
+
+zs::PhasedCtl phased_ctl() {
+  const int32_t polls = g_phased_max_polls.load(std::memory_order_relaxed);
+  return zs::PhasedCtl{(int32_t)(g_phased_slot.fetch_add(1, std::memory_order_relaxed) % zs::kPhasedSlots),
+                       polls > 0 ? polls : zs::kPhasedMaxPolls};
 }
 
 // The same for pass 1 of the two-pass form (which writes 4 bytes per
@@ -360,6 +404,84 @@ int offload_blocks() { return auto_blocks(); }
 
 }  // namespace zs
 
+namespace {
+
+// A list plan's device table, laid out on the host: chunks | tensors | grad
+// pointers, in one byte image ready to upload.
+struct ListTable {
+  std::vector<unsigned char> bytes;
+  size_t off_tensors = 0, off_gptrs = 0;
+  int32_t n_chunks = 0;
+  int64_t n_params = 0;
+};
+
+// Checks the tensors (as zs_list_plan_create documents) and lays out their
+// table: every vector tensor cut into chunks of kChunkElems parameters from
+// its common alignment peel, every scalar-only tensor into chunks of
+// kChunkElems elements.
+zs_status build_list_table(const zs_tensor* tensors, int32_t T, int32_t N, ListTable& out) {
+  if (T < 0) return fail(ZS_ERR_RANGE, "T must be >= 0 (got %d)", T);
+  if (T > 0 && !tensors) return fail(ZS_ERR_NULL, "tensors is NULL");
+  if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
+  std::vector<Range> rs;
+  int64_t total = 0;
+  for (int32_t t = 0; t < T; ++t) {
+    const zs_tensor& x = tensors[t];
+    zs_status st = check_tensor(x.grad_chunks, N, x.n, x.master, x.m, x.v, x.param_bf16, t, rs);
+    if (st) return st;
+    total += x.n;
+  }
+  zs_status st = check_alias(rs);
+  if (st) return st;
+
+  std::vector<zs::ListTensor> ht;
+  std::vector<zs::ListChunk> hc;
+  std::vector<const uint16_t*> hg;
+  ht.reserve(T);
+  hg.reserve((size_t)T * N);
+  for (int32_t t = 0; t < T; ++t) {
+    const zs_tensor& x = tensors[t];
+    zs::ListTensor d{};
+    if (x.n == 0) {
+      d.scalar_only = 1;
+    } else {
+      const zs::FlatShape s = shape_of(x.grad_chunks, N, x.n, x.master, x.m, x.v, x.param_bf16);
+      d.p = s.p;
+      d.m = s.m;
+      d.v = s.v;
+      d.b = s.b;
+      d.n = s.n;
+      d.head = s.head;
+      d.nvec = s.nvec;
+      d.scalar_only = s.scalar_only;
+      if (!s.scalar_only) {
+        const int64_t per = zs::kChunkElems / 8;
+        for (int64_t g0 = 0; g0 < s.nvec; g0 += per)
+          hc.push_back({t, g0 == 0 ? 1 : 0, g0, std::min(s.nvec, g0 + per), 0});
+      } else {
+        for (int64_t e0 = 0; e0 < s.n; e0 += zs::kChunkElems)
+          hc.push_back({t, 0, e0, std::min(s.n, e0 + zs::kChunkElems), 0});
+      }
+    }
+    ht.push_back(d);
+    for (int32_t r = 0; r < N; ++r) hg.push_back(x.n ? x.grad_chunks[r] : nullptr);
+  }
+  if (hc.size() > (size_t)INT32_MAX) return fail(ZS_ERR_RANGE, "too many chunks");
+  const size_t bc = hc.size() * sizeof(zs::ListChunk), bt = ht.size() * sizeof(zs::ListTensor),
+               bg = hg.size() * sizeof(void*);
+  out.bytes.resize(bc + bt + bg);
+  if (bc) std::memcpy(out.bytes.data(), hc.data(), bc);
+  if (bt) std::memcpy(out.bytes.data() + bc, ht.data(), bt);
+  if (bg) std::memcpy(out.bytes.data() + bc + bt, hg.data(), bg);
+  out.off_tensors = bc;
+  out.off_gptrs = bc + bt;
+  out.n_chunks = (int32_t)hc.size();
+  out.n_params = total;
+  return ZS_OK;
+}
+
+}  // namespace
+
 struct zs_list_plan {
   int device;
   int32_t N;
@@ -402,7 +524,10 @@ zs_status flat_step(const uint16_t* const* grad_chunks, int32_t N, int64_t n, fl
     const zs_adam_hp placeholder = {0.0, 0.0, 0.0, 1.0, 0.0};
     const zs::Scalars c = make_scalars(src ? placeholder : *hp, src ? 1 : step, N);
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    return after_launch(zs::launch_flat(grad_chunks, s, c, ref, auto_blocks(), write_window(N), hs), hs, what);
+    zs::WriteWindow win{};
+    const zs::FlatSchedule sched = flat_schedule(N, n, &win);
+    return after_launch(zs::launch_flat(grad_chunks, s, c, ref, auto_blocks(), sched, win, phased_ctl(), hs), hs,
+                        what);
   } catch (const std::bad_alloc&) {
     return fail(ZS_ERR_NOMEM, "host allocation failed");
   } catch (...) {
@@ -475,17 +600,54 @@ zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks) {
 zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* period_ticks, int32_t* open_ticks) {
   g_last_error.clear();
   if (!period_ticks || !open_ticks) return fail(ZS_ERR_NULL, "period_ticks or open_ticks is NULL");
-  if (kernel != ZS_WINDOW_FLAT_STEP && kernel != ZS_WINDOW_REDUCE_PASS)
-    return fail(ZS_ERR_RANGE, "kernel must be ZS_WINDOW_FLAT_STEP or ZS_WINDOW_REDUCE_PASS (got %d)", kernel);
+  if (kernel != ZS_WINDOW_FLAT_STEP && kernel != ZS_WINDOW_REDUCE_PASS && kernel != ZS_WINDOW_LIST_PLAN)
+    return fail(ZS_ERR_RANGE, "kernel must be ZS_WINDOW_FLAT_STEP, _REDUCE_PASS or _LIST_PLAN (got %d)", kernel);
   if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
   if (n < 0) return fail(ZS_ERR_RANGE, "n must be >= 0");
-  const bool flat = kernel == ZS_WINDOW_FLAT_STEP;
-  const zs::WriteWindow w = flat ? write_window(N) : reduce_write_window(N);
+  const bool flat = kernel != ZS_WINDOW_REDUCE_PASS;  // the flat step and list plans: 512-parameter tiles
+  zs::WriteWindow w{};
+  if (kernel == ZS_WINDOW_FLAT_STEP)
+    (void)flat_schedule(N, n, &w);
+  else if (kernel == ZS_WINDOW_LIST_PLAN)
+    w = write_window(N);
+  else
+    w = reduce_write_window(N);
   const bool big = flat ? n / 8 / zs::kFlatBlock >= zs::kWindowMinTiles
                         : n / kTileElems >= zs::kReduceWindowMinTiles;
   const bool used = w.period_mask != 0 && big;
   *period_ticks = used ? (int32_t)(w.period_mask + 1) : 0;
   *open_ticks = used ? (int32_t)w.open_ticks : 0;
+  return ZS_OK;
+}
+
+zs_status zs_set_flat_schedule(int32_t schedule) {
+  g_last_error.clear();
+  if (schedule < 0 || schedule > ZS_SCHEDULE_PHASED)
+    return fail(ZS_ERR_RANGE, "schedule must be ZS_SCHEDULE_AUTO, _STREAM, _WINDOWED or _PHASED (got %d)", schedule);
+  g_flat_schedule.store(schedule, std::memory_order_relaxed);
+  return ZS_OK;
+}
+
+zs_status zs_flat_schedule(int32_t N, int64_t n, int32_t* schedule) {
+  g_last_error.clear();
+  if (!schedule) return fail(ZS_ERR_NULL, "schedule is NULL");
+  if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
+  if (n < 0) return fail(ZS_ERR_RANGE, "n must be >= 0");
+  zs::WriteWindow w{};
+  zs::FlatSchedule sched = flat_schedule(N, n, &w);
+  const int64_t tiles = n / 8 / zs::kFlatBlock;
+  // the kernels' own size conditions (a shard on a common 128-byte line phase)
+  if (sched == zs::FlatSchedule::kWindowed && (w.period_mask == 0 || tiles < zs::kWindowMinTiles))
+    sched = zs::FlatSchedule::kStream;
+  if (sched == zs::FlatSchedule::kPhased && tiles < 1) sched = zs::FlatSchedule::kStream;
+  *schedule = (int32_t)sched;
+  return ZS_OK;
+}
+
+zs_status zs_set_phased_max_polls(int32_t polls) {
+  g_last_error.clear();
+  if (polls < 0) return fail(ZS_ERR_RANGE, "polls must be >= 0 (got %d)", polls);
+  g_phased_max_polls.store(polls, std::memory_order_relaxed);
   return ZS_OK;
 }
 
@@ -528,65 +690,18 @@ zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_t N, zs
     g_last_error.clear();
     if (!out) return fail(ZS_ERR_NULL, "out is NULL");
     *out = nullptr;
-    if (T < 0) return fail(ZS_ERR_RANGE, "T must be >= 0 (got %d)", T);
-    if (T > 0 && !tensors) return fail(ZS_ERR_NULL, "tensors is NULL");
-    if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
-    std::vector<Range> rs;
-    int64_t total = 0;
-    for (int32_t t = 0; t < T; ++t) {
-      const zs_tensor& x = tensors[t];
-      zs_status st = check_tensor(x.grad_chunks, N, x.n, x.master, x.m, x.v, x.param_bf16, t, rs);
-      if (st) return st;
-      total += x.n;
-    }
-    zs_status st = check_alias(rs);
+    ListTable tab;
+    zs_status st = build_list_table(tensors, T, N, tab);
     if (st) return st;
-
-    std::vector<zs::ListTensor> ht;
-    std::vector<zs::ListChunk> hc;
-    std::vector<const uint16_t*> hg;
-    ht.reserve(T);
-    hg.reserve((size_t)T * N);
-    for (int32_t t = 0; t < T; ++t) {
-      const zs_tensor& x = tensors[t];
-      zs::ListTensor d{};
-      if (x.n == 0) {
-        d.scalar_only = 1;
-      } else {
-        const zs::FlatShape s = shape_of(x.grad_chunks, N, x.n, x.master, x.m, x.v, x.param_bf16);
-        d.p = s.p;
-        d.m = s.m;
-        d.v = s.v;
-        d.b = s.b;
-        d.n = s.n;
-        d.head = s.head;
-        d.nvec = s.nvec;
-        d.scalar_only = s.scalar_only;
-        if (!s.scalar_only) {
-          const int64_t per = zs::kChunkElems / 8;
-          for (int64_t g0 = 0; g0 < s.nvec; g0 += per)
-            hc.push_back({t, g0 == 0 ? 1 : 0, g0, std::min(s.nvec, g0 + per), 0});
-        } else {
-          for (int64_t e0 = 0; e0 < s.n; e0 += zs::kChunkElems)
-            hc.push_back({t, 0, e0, std::min(s.n, e0 + zs::kChunkElems), 0});
-        }
-      }
-      ht.push_back(d);
-      for (int32_t r = 0; r < N; ++r) hg.push_back(x.n ? x.grad_chunks[r] : nullptr);
-    }
-    if (hc.size() > (size_t)INT32_MAX) return fail(ZS_ERR_RANGE, "too many chunks");
-
     zs_list_plan* plan = new zs_list_plan();
     plan->N = N;
     plan->T = T;
-    plan->n_chunks = (int32_t)hc.size();
-    plan->n_params = total;
+    plan->n_chunks = tab.n_chunks;
+    plan->n_params = tab.n_params;
     plan->n_groups = 1;
     plan->table = nullptr;
     if (hipGetDevice(&plan->device) != hipSuccess) plan->device = 0;
-    const size_t bc = hc.size() * sizeof(zs::ListChunk), bt = ht.size() * sizeof(zs::ListTensor),
-                 bg = hg.size() * sizeof(void*);
-    const size_t bytes = bc + bt + bg;
+    const size_t bytes = tab.bytes.size();
     if (bytes > 0) {
       hipError_t e = hipMalloc(&plan->table, bytes);
       if (e != hipSuccess) {
@@ -594,12 +709,8 @@ zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_t N, zs
         (void)hipGetLastError();
         return fail(ZS_ERR_NOMEM, "plan table of %zu bytes: %s", bytes, hipGetErrorString(e));
       }
-      std::vector<unsigned char> host(bytes);
-      std::memcpy(host.data(), hc.data(), bc);
-      std::memcpy(host.data() + bc, ht.data(), bt);
-      std::memcpy(host.data() + bc + bt, hg.data(), bg);
       hipStream_t hs = static_cast<hipStream_t>(stream);
-      e = hipMemcpyAsync(plan->table, host.data(), bytes, hipMemcpyHostToDevice, hs);
+      e = hipMemcpyAsync(plan->table, tab.bytes.data(), bytes, hipMemcpyHostToDevice, hs);
       if (e == hipSuccess) e = hipStreamSynchronize(hs);
       if (e != hipSuccess) {
         (void)hipFree(plan->table);
@@ -609,8 +720,8 @@ zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_t N, zs
     }
     unsigned char* base = static_cast<unsigned char*>(plan->table);
     plan->chunks = reinterpret_cast<zs::ListChunk*>(base);
-    plan->tensors = reinterpret_cast<zs::ListTensor*>(base + bc);
-    plan->gptrs = reinterpret_cast<const uint16_t**>(base + bc + bt);
+    plan->tensors = reinterpret_cast<zs::ListTensor*>(base + tab.off_tensors);
+    plan->gptrs = reinterpret_cast<const uint16_t**>(base + tab.off_gptrs);
     *out = plan;
     return ZS_OK;
   } catch (const std::bad_alloc&) {
@@ -631,6 +742,18 @@ zs_status plan_on_current_device(zs_list_plan_t plan) {
   if (cur != plan->device)  // the table lives in the other device's memory
     return fail(ZS_ERR_RANGE, "the plan was built on device %d, device %d is current", plan->device, cur);
   return ZS_OK;
+}
+
+// The list step over a device table.
+zs_status launch_list_table(const zs::ListChunk* chunks, int32_t n_chunks, const zs::ListTensor* tensors,
+                            const uint16_t* const* gptrs, int32_t N, int64_t n_params, const zs::Scalars* cs,
+                            int32_t n_sets, const zs::StepRef& ref, zs_stream stream) {
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // write windows for plans of at least 2^25 parameters, as for flat shards
+  const zs::WriteWindow win =
+      n_params >= ((int64_t)zs::kWindowMinTiles << 9) ? write_window(N) : zs::WriteWindow{0, 0};
+  return after_launch(zs::launch_list(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, auto_blocks(), win, hs), hs,
+                      "zs_reduce_adam_list launch");
 }
 
 // The step with `n` hyperparameter sets (one for every tensor, n == 1, or one
@@ -655,13 +778,8 @@ zs_status run_plan(zs_list_plan_t plan, const zs_adam_hp* hps, int32_t n, int64_
   if (plan->n_chunks == 0) return ZS_OK;
   zs_status st = plan_on_current_device(plan);
   if (st) return st;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  // write windows for plans of at least 2^25 parameters, as for flat shards
-  const zs::WriteWindow win = plan->n_params >= ((int64_t)zs::kWindowMinTiles << 9) ? write_window(plan->N)
-                                                                                    : zs::WriteWindow{0, 0};
-  return after_launch(
-      zs::launch_list(plan->chunks, plan->n_chunks, plan->tensors, plan->gptrs, cs, n, ref, auto_blocks(), win, hs),
-      hs, "zs_reduce_adam_list launch");
+  return launch_list_table(plan->chunks, plan->n_chunks, plan->tensors, plan->gptrs, plan->N, plan->n_params, cs, n,
+                           ref, stream);
 }
 
 }  // namespace

@@ -90,9 +90,28 @@ struct WriteWindow {
   uint64_t open_ticks;   // window length, 1 .. period - 1
 };
 
+// How the flat step schedules its reads and writes (zs_set_flat_schedule):
+//  kStream:   one tile per workgroup, each tile's stores issued as it finishes;
+//  kWindowed: persistent waves holding finished tiles in registers, storing
+//             them in device-clock write windows (flat_window_kernel);
+//  kPhased:   persistent workgroups that read every replica of a super-chunk
+//             into register accumulators (all waves on about the same replica
+//             at once), meet at a grid barrier, then read the state and write
+//             the outputs of that super-chunk (flat_phased_kernel).
+enum class FlatSchedule : int32_t { kStream = 1, kWindowed = 2, kPhased = 3 };
+
+// The phased kernel's control: its barrier counter (one of kPhasedSlots in
+// device memory, picked per launch) and the longest a workgroup waits at a
+// barrier, in polls of about 50 ns.
+struct PhasedCtl {
+  int32_t slot;
+  int32_t max_polls;
+};
+
 // Launches (host side, defined with the kernels).
 hipError_t launch_flat(const uint16_t* const* grads, const FlatShape& s, const Scalars& c, const StepRef& ref,
-                       int blocks, const WriteWindow& win, hipStream_t stream);
+                       int blocks, FlatSchedule sched, const WriteWindow& win, const PhasedCtl& ctl,
+                       hipStream_t stream);
 // One device thread: *step += 1.
 hipError_t launch_step_advance(int64_t* step, hipStream_t stream);
 // cs: n_sets folded scalar sets, one per hyperparameter group (1 <= n_sets <=
@@ -126,6 +145,17 @@ constexpr int kMaxGroups = ZS_MAX_GROUPS;
 constexpr int kWindowChecks = 4;
 constexpr int64_t kWindowMinTiles = 65536;
 constexpr int kMaxDevices = 64;
+// Phased flat step: 512-parameter tiles per wave in one super-chunk (their
+// fp32 accumulators take 64 VGPRs), waves per workgroup (one workgroup per
+// compute unit at 3 waves per SIMD), barrier counter slots, the default
+// longest wait at one barrier (polls of about 50 ns: about 3 ms), and the
+// fewest parameters and replicas for which the automatic schedule takes it.
+constexpr int kPhasedTiles = 8;
+constexpr int kPhasedWaves = 12;
+constexpr int kPhasedSlots = 16;
+constexpr int32_t kPhasedMaxPolls = 1 << 16;
+constexpr int64_t kPhasedMinParams = (int64_t)1 << 25;
+constexpr int32_t kPhasedMinReplicas = 48;
 // Write-window bounds, in ticks of the 100 MHz device clock: the period a
 // power of two in [kWindowMinPeriod, kWindowMaxPeriod], the open part at most
 // kWindowMaxOpen; a wave's wait in a window is capped at kWindowMaxSleeps

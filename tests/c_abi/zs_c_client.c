@@ -211,12 +211,28 @@ int main(void) {
   }
   shard_free(&f);
 
-  /* 4b. the write-window setting and its query, from C (no GPU work) */
+  /* 4b. the write-window and schedule settings and their queries, from C (no GPU work) */
   {
-    int32_t per = -1, open = -1;
+    int32_t per = -1, open = -1, sched = -1;
+    CHECK_ZS(zs_write_window(ZS_WINDOW_LIST_PLAN, 64, (int64_t)1 << 30, &per, &open));
+    if (per != 4096 || open != 512) {
+      fprintf(stderr, "default list-plan window for N = 64: %d / %d\n", per, open);
+      bad = 1;
+    }
+    CHECK_ZS(zs_flat_schedule(64, (int64_t)1 << 30, &sched));
+    if (sched != ZS_SCHEDULE_PHASED) {
+      fprintf(stderr, "default flat schedule for N = 64 on 2^30 parameters: %d\n", sched);
+      bad = 1;
+    }
+    CHECK_ZS(zs_set_flat_schedule(ZS_SCHEDULE_WINDOWED));
     CHECK_ZS(zs_write_window(ZS_WINDOW_FLAT_STEP, 64, (int64_t)1 << 30, &per, &open));
     if (per != 4096 || open != 512) {
-      fprintf(stderr, "default flat window for N = 64: %d / %d\n", per, open);
+      fprintf(stderr, "flat window on the windowed schedule for N = 64: %d / %d\n", per, open);
+      bad = 1;
+    }
+    CHECK_ZS(zs_set_flat_schedule(ZS_SCHEDULE_AUTO));
+    if (zs_set_flat_schedule(7) != ZS_ERR_RANGE) {
+      fprintf(stderr, "an unknown schedule was not rejected\n");
       bad = 1;
     }
     CHECK_ZS(zs_set_write_window(1, 0));

@@ -306,33 +306,55 @@ def test_probe_library_rejects_unsupported_arguments_without_gpu():
 
 
 def test_write_window_query():
-    """The query reports the window each kernel takes: the N = 64 defaults on shards of at least
-    2^25 parameters, none below that, for other replica counts, or when windows are switched off."""
-    for kernel, default in (("flat", (4096, 512)), ("reduce", (4096, 256))):
-        assert zs.write_window(kernel, 64, 1_093_750_000) == default
-        assert zs.write_window(kernel, 64, 1 << 25) == default
-        assert zs.write_window(kernel, 64, (1 << 25) - 1) == (0, 0)
-        assert zs.write_window(kernel, 8, 124_000_000) == (0, 0)   # below 48 replicas: none by default
-        assert zs.write_window(kernel, 47, 1 << 30) == (0, 0)
-        assert zs.write_window(kernel, 100, 1 << 30) == default     # runtime replica counts too
-        zs.set_write_window(1)
-        assert zs.write_window(kernel, 64, 1 << 30) == (0, 0)
-        zs.set_write_window(1024, 128)
-        assert zs.write_window(kernel, 16, 1 << 30) == (1024, 128)
-        assert zs.write_window(kernel, 5, 1 << 30) == (1024, 128)
+    """The query reports the window each kernel takes.  Pass 1: the N = 64 default on shards of at least
+    2^25 parameters, none below that, for other replica counts, or when windows are switched off.  The
+    flat step takes windows only on the windowed schedule (explicit, or an explicit window setting under
+    the automatic one): its automatic default is the phased schedule."""
+    assert zs.write_window("flat", 64, 1_093_750_000) == (0, 0)
+    assert zs.write_window("reduce", 64, 1_093_750_000) == (4096, 256)
+    assert zs.write_window("list", 64, 1_093_750_000) == (4096, 512)   # list plans keep the windows
+    assert zs.write_window("list", 64, (1 << 25) - 1) == (0, 0)
+    assert zs.write_window("list", 8, 1 << 30) == (0, 0)
+    try:
+        for kernel, default, setup in (("reduce", (4096, 256), lambda: None),
+                                       ("flat", (4096, 512), lambda: zs.set_flat_schedule("windowed"))):
+            setup()
+            assert zs.write_window(kernel, 64, 1_093_750_000) == default
+            assert zs.write_window(kernel, 64, 1 << 25) == default
+            assert zs.write_window(kernel, 64, (1 << 25) - 1) == (0, 0)
+            assert zs.write_window(kernel, 100, 1 << 30) == default     # runtime replica counts too
+            if kernel == "reduce":
+                assert zs.write_window(kernel, 8, 124_000_000) == (0, 0)   # below 48 replicas: none by default
+                assert zs.write_window(kernel, 47, 1 << 30) == (0, 0)
+            zs.set_write_window(1)
+            assert zs.write_window(kernel, 64, 1 << 30) == (0, 0)
+            zs.set_write_window(1024, 128)
+            assert zs.write_window(kernel, 16, 1 << 30) == (1024, 128)
+            assert zs.write_window(kernel, 5, 1 << 30) == (1024, 128)
+            zs.set_write_window(0)
+        # the flat step's open length follows the writes' share of the bytes
+        assert zs.write_window("flat", 48, 1 << 30) == (4096, 640)
+        assert zs.write_window("flat", 128, 1 << 30) == (4096, 512)
+        assert zs.write_window("flat", 129, 1 << 30) == (4096, 384)
+        assert zs.write_window("flat", 256, 1 << 30) == (4096, 384)
+        assert zs.write_window("flat", 8, 1 << 30) == (4096, 640)      # windowed on request, any N
+    finally:
+        zs.set_flat_schedule("auto")
         zs.set_write_window(0)
-    # the flat step's open length follows the writes' share of the bytes
-    assert zs.write_window("flat", 48, 1 << 30) == (4096, 640)
-    assert zs.write_window("flat", 128, 1 << 30) == (4096, 512)
-    assert zs.write_window("flat", 129, 1 << 30) == (4096, 384)
-    assert zs.write_window("flat", 256, 1 << 30) == (4096, 384)
+    # an explicit window under the automatic schedule still takes the windowed kernel
+    zs.set_write_window(2048, 256)
+    try:
+        assert zs.write_window("flat", 64, 1 << 30) == (2048, 256)
+        assert zs.flat_schedule(64, 1 << 30) == "windowed"
+    finally:
+        zs.set_write_window(0)
     with pytest.raises(zs.ZShardError):
         zs.write_window("flat", 0, 1 << 20)
     lib = ctypes.CDLL(zs.LIB_PATH)
     lib.zs_write_window.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                     ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     p, o = ctypes.c_int32(), ctypes.c_int32()
-    assert lib.zs_write_window(2, 64, 1 << 30, ctypes.byref(p), ctypes.byref(o)) == 2   # unknown kernel
+    assert lib.zs_write_window(3, 64, 1 << 30, ctypes.byref(p), ctypes.byref(o)) == 2   # unknown kernel
     assert lib.zs_write_window(0, 64, 1 << 30, None, ctypes.byref(o)) == 1
 
 
@@ -442,3 +464,40 @@ def test_tuning_knobs_check_their_ranges():
     assert zs.launch_bytes() == 3_000_000_000
     with pytest.raises(zs.ZShardError):
         zs.set_launch_bytes(-5)
+
+
+def test_flat_schedule_query_and_setting():
+    """The automatic schedule: phased for N >= 48 on shards of at least 2^25 parameters, per-tile stores
+    otherwise; an explicit schedule wins (each kernel's own size conditions aside)."""
+    assert zs.flat_schedule(64, 1_093_750_000) == "phased"
+    assert zs.flat_schedule(48, 1 << 25) == "phased"
+    assert zs.flat_schedule(256, 1 << 30) == "phased"
+    assert zs.flat_schedule(47, 1 << 30) == "stream"
+    assert zs.flat_schedule(8, 124_000_000) == "stream"
+    assert zs.flat_schedule(64, (1 << 25) - 1) == "stream"
+    zs.set_write_window(1)   # an explicit "no windows" keeps per-tile stores
+    try:
+        assert zs.flat_schedule(64, 1 << 30) == "stream"
+    finally:
+        zs.set_write_window(0)
+    try:
+        zs.set_flat_schedule("phased")
+        assert zs.flat_schedule(8, 512) == "phased"       # one whole tile is enough
+        assert zs.flat_schedule(8, 511) == "stream"       # no whole tile
+        zs.set_flat_schedule("windowed")
+        assert zs.flat_schedule(64, 1 << 30) == "windowed"
+        assert zs.flat_schedule(64, 1 << 20) == "stream"  # below the windowed kernel's size
+        zs.set_flat_schedule("stream")
+        assert zs.flat_schedule(64, 1 << 30) == "stream"
+        with pytest.raises(zs.ZShardError):
+            zs.set_flat_schedule(4)
+        with pytest.raises(zs.ZShardError):
+            zs.set_flat_schedule(-1)
+        with pytest.raises(zs.ZShardError):
+            zs.flat_schedule(0, 1 << 20)
+        with pytest.raises(zs.ZShardError):
+            zs.set_phased_max_polls(-1)
+        zs.set_phased_max_polls(1)
+        zs.set_phased_max_polls(0)
+    finally:
+        zs.set_flat_schedule("auto")

@@ -281,7 +281,7 @@ def test_windowed_list_plan_with_peels_and_scalar_tensors(env, orc, N, window):
     assert sum(n_of) >= 1 << 25
     zs.set_write_window(*window)
     try:
-        assert zs.write_window("flat", N, sum(n_of))[0] > 0, "the plan takes write windows"
+        assert zs.write_window("list", N, sum(n_of))[0] > 0, "the plan takes write windows"
         with zs.ListPlan(tensors, N) as plan:
             print(f"windowed list, peels and scalar tensors: N={N} window={window}", flush=True)
             for t in (3, 4):
