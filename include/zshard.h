@@ -186,6 +186,25 @@ ZS_API zs_status zs_reduce_adam_list_plan_groups(zs_list_plan_t plan, const zs_a
 ZS_API zs_status zs_reduce_adam_list(const zs_tensor* tensors, int32_t T, int32_t N, const zs_adam_hp* hp,
                                      int64_t step, zs_stream stream);
 
+/* For callers that cannot allocate device memory (code that must not call
+   hipMalloc, such as tight serving loops or harnesses that forbid it): the
+   one-shot list step of zs_reduce_adam_list, with the same arguments,
+   checks, kernels and results, whose chunk table goes into a fixed array of
+   ZS_STATIC_TABLE_BYTES (32 MiB) of device memory that the library holds on
+   each device it runs on until the process ends, instead of a plan allocated
+   and freed per call.  The call uploads the table on `stream`, runs the step
+   there and waits for it (it blocks the calling thread), and calls no
+   hipMalloc or hipFree.  The table takes 32 bytes per chunk (a chunk is
+   4,096 parameters of a tensor, or fewer at its end), 64 per tensor and 8 per
+   tensor per replica: a list whose table needs more returns ZS_ERR_RANGE
+   (about 4 billion parameters in all for 1,000 tensors and N = 64).  Every call on
+   a device shares that device's array and rewrites it: calls that overlap on
+   one device (from other threads, or on other streams) race and must be
+   serialised by the caller.  Errors as zs_reduce_adam_list, and ZS_ERR_RANGE
+   for a table beyond the array. */
+#define ZS_STATIC_TABLE_BYTES (32u << 20)
+ZS_API zs_status zs_reduce_adam_list_static(const zs_tensor* tensors, int32_t T, int32_t N, const zs_adam_hp* hp,
+                                            int64_t step, zs_stream stream);
 
 /* ---------------------------------------------------------------------------
  * Device-resident step index, for training steps captured once in a HIP graph

@@ -69,6 +69,9 @@ _lib.zs_reduce_adam_list_plan.argtypes = [_vp, ctypes.POINTER(AdamHPStruct), _i6
 _lib.zs_reduce_adam_list.restype = ctypes.c_int
 _lib.zs_reduce_adam_list.argtypes = [ctypes.POINTER(TensorStruct), _i32, _i32, ctypes.POINTER(AdamHPStruct), _i64,
                                      _vp]
+_lib.zs_reduce_adam_list_static.restype = ctypes.c_int
+_lib.zs_reduce_adam_list_static.argtypes = [ctypes.POINTER(TensorStruct), _i32, _i32, ctypes.POINTER(AdamHPStruct),
+                                            _i64, _vp]
 _lib.zs_list_plan_destroy.restype = None
 _lib.zs_list_plan_destroy.argtypes = [_vp]
 _lib.zs_list_plan_set_groups.restype = ctypes.c_int
@@ -515,6 +518,17 @@ def reduce_adam_list(tensors: Sequence[ShardTensor], N: int, hp, step: int, stre
     with torch.cuda.device(dev):
         _check(_lib.zs_reduce_adam_list(tab, len(tensors), N, ctypes.byref(h), step, _stream_handle(stream, dev)),
                "zs_reduce_adam_list")
+
+
+def reduce_adam_list_static(tensors: Sequence[ShardTensor], N: int, hp, step: int, stream=None) -> None:
+    """:func:`reduce_adam_list` with its table in the library's fixed device array (no device
+    allocation; see zs_reduce_adam_list_static for the size limit and the sharing rule)."""
+    tab, keep = _tensor_table(tensors, N)
+    dev = _one_device(*[t.master for t in tensors])
+    h = _hp(hp)
+    with torch.cuda.device(dev):
+        _check(_lib.zs_reduce_adam_list_static(tab, len(tensors), N, ctypes.byref(h), step,
+                                               _stream_handle(stream, dev)), "zs_reduce_adam_list_static")
 
 
 # ------------------------------------------------------------ two-pass form

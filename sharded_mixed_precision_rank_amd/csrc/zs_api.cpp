@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -744,7 +745,7 @@ zs_status plan_on_current_device(zs_list_plan_t plan) {
   return ZS_OK;
 }
 
-// The list step over a device table.
+// The list step over a device table (a plan's, or the fixed array of zs_reduce_adam_list_static).
 zs_status launch_list_table(const zs::ListChunk* chunks, int32_t n_chunks, const zs::ListTensor* tensors,
                             const uint16_t* const* gptrs, int32_t N, int64_t n_params, const zs::Scalars* cs,
                             int32_t n_sets, const zs::StepRef& ref, zs_stream stream) {
@@ -871,6 +872,83 @@ zs_status zs_reduce_adam_list(const zs_tensor* tensors, int32_t T, int32_t N, co
   if (st == ZS_OK && e != hipSuccess) st = hip_fail(e, "zs_reduce_adam_list");
   free_plan(plan, e != hipSuccess);
   return st;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no allocation
+// The table of zs_reduce_adam_list_static lives here: device memory held by
+// the library on each device it runs on, for the life of the process.  Host
+// code never names this array as an address: it takes the device's address
+// from hipGetSymbolAddress (scratch_address) and uses that.
+constexpr size_t kStaticTableBytes = (size_t)ZS_STATIC_TABLE_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticTableBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[zs::kMaxDevices];  // per device: scratch's device address there
+
+// scratch's address on the current device, looked up once per device with
+// that device current.
+zs_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= zs::kMaxDevices) return fail(ZS_ERR_RANGE, "device %d is beyond the library's %d", dev,
+                                                     zs::kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ZS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+zs_status zs_reduce_adam_list_static(const zs_tensor* tensors, int32_t T, int32_t N, const zs_adam_hp* hp,
+                                     int64_t step, zs_stream stream) {
+  try {
+    g_last_error.clear();
+    zs_status st = check_hp(hp, step);
+    if (st) return st;
+    // the host image of the table, kept per thread so that repeated calls reuse its memory
+    thread_local ListTable tab;
+    st = build_list_table(tensors, T, N, tab);
+    if (st) return st;
+    if (tab.bytes.size() > kStaticTableBytes)
+      return fail(ZS_ERR_RANGE,
+                  "the list's table needs %zu bytes (%d chunks of %lld parameters, %d tensors, %d replicas); "
+                  "zs_reduce_adam_list_static holds at most %zu: use zs_reduce_adam_list or a plan",
+                  tab.bytes.size(), tab.n_chunks, (long long)zs::kChunkElems, T, N, kStaticTableBytes);
+    if (tab.n_chunks == 0) return ZS_OK;
+    void* base = nullptr;
+    st = scratch_address(&base);
+    if (st) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(base, tab.bytes.data(), tab.bytes.size(), hipMemcpyHostToDevice, hs);
+    if (e != hipSuccess) return hip_fail(e, "table upload");
+    unsigned char* b = static_cast<unsigned char*>(base);
+    const zs::Scalars c = make_scalars(*hp, step, N);
+    st = launch_list_table(reinterpret_cast<const zs::ListChunk*>(b), tab.n_chunks,
+                           reinterpret_cast<const zs::ListTensor*>(b + tab.off_tensors),
+                           reinterpret_cast<const uint16_t* const*>(b + tab.off_gptrs), N, tab.n_params, &c, 1,
+                           zs::StepRef{}, stream);
+    // the next call on this device rewrites the table, and the host image is reused: wait for this step
+    e = hipStreamSynchronize(hs);
+    if (st == ZS_OK && e != hipSuccess) st = hip_fail(e, "zs_reduce_adam_list_static");
+    return st;
+  } catch (const std::bad_alloc&) {
+    return fail(ZS_ERR_NOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(ZS_ERR_HIP, "unexpected exception");
+  }
 }
 
 size_t zs_two_pass_workspace_bytes(int64_t n) {

@@ -501,3 +501,21 @@ def test_flat_schedule_query_and_setting():
         zs.set_phased_max_polls(0)
     finally:
         zs.set_flat_schedule("auto")
+
+
+def test_static_list_step_refuses_a_table_beyond_its_array_without_gpu():
+    """zs_reduce_adam_list_static checks the table's size against its fixed array before any GPU work:
+    one tensor of 5e9 parameters needs about 1.22M chunks, 39 MB of table, beyond 32 MiB."""
+    lib = zs.library()
+    n = 5_000_000_000
+    span = 1 << 40
+    g = (ctypes.c_void_p * 1)(A + 1 * span)
+    t = (zs.TensorStruct * 1)()
+    t[0] = zs.TensorStruct(n, A + 2 * span, A + 3 * span, A + 4 * span, A + 5 * span,
+                           ctypes.cast(g, ctypes.POINTER(ctypes.c_void_p)))
+    h = zs.AdamHPStruct(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    assert zs.STATUS[lib.zs_reduce_adam_list_static(t, 1, 1, ctypes.byref(h), 1, None)] == "ZS_ERR_RANGE"
+    assert b"zs_reduce_adam_list_static holds at most" in lib.zs_last_error()
+    assert zs.STATUS[lib.zs_reduce_adam_list_static(t, 1, 1, None, 1, None)] == "ZS_ERR_NULL"
+    assert zs.STATUS[lib.zs_reduce_adam_list_static(t, 1, 0, ctypes.byref(h), 1, None)] == "ZS_ERR_RANGE"
+    assert zs.STATUS[lib.zs_reduce_adam_list_static(t, 0, 1, ctypes.byref(h), 1, None)] == "ZS_OK"  # no tensors
