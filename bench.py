@@ -97,14 +97,16 @@ def counter_traffic(w, kernel: str):
     return total
 
 
-def pattern_ceiling(w, d, window=(0, 0), reps: int = 5):
+def pattern_ceiling(w, d, window=(0, 0), reps: int = 5, phased: bool = False):
     """What the memory system delivers for the step's own access pattern on this machine: the measurement
     probe (bench_probe/libzshard_probe.so) replays the fused kernel's loads and stores, tile layout and
     non-temporal hints included, with the AdamW arithmetic taken out, on the same buffers.  Reported as
     GB/s of the pattern's own bytes for the read streams alone ((2N+12) B/param), for the full
-    read+write mix ((2N+26) B/param) with each tile's writes issued as soon as it is done, and, when the
-    step groups its writes in device-clock windows (`window` = (period, open) ticks), for the same mix
-    with the same windows.  It overwrites the state: run it after the timed steps."""
+    read+write mix ((2N+26) B/param) with each tile's writes issued as soon as it is done, when the
+    step groups its writes in device-clock windows (`window` = (period, open) ticks) for the same mix
+    with the same windows, and when the step runs the phased schedule, for its super-chunk loop (the
+    library's own code, zs_phased.h) over the shard's whole super-chunks.  It overwrites the state: run
+    it after the timed steps."""
     import ctypes
 
     import torch
@@ -120,13 +122,20 @@ def pattern_ceiling(w, d, window=(0, 0), reps: int = 5):
     modes = [(0, 2 * N + 12, "read"), (1, 2 * N + 26, "read_write")]
     if window[0]:
         modes.append((2, 2 * N + 26, "read_write_windowed"))
+    if phased:
+        modes.append((3, 2 * N + 26, "read_write_phased"))
+    covered = torch.zeros(1, dtype=torch.int64, device="cuda")
     for write, bpp, name in modes:
         def call():
             ptrs = (tab, N, n, d["P"].data_ptr(), d["M"].data_ptr(), d["V"].data_ptr(), d["B"].data_ptr())
+            if write == 3:
+                return lib.zs_probe_pattern_phased(*ptrs, covered.data_ptr(), stream.cuda_stream)
             if write == 2:
                 return lib.zs_probe_pattern_windowed(*ptrs, window[0], window[1], stream.cuda_stream)
             return lib.zs_probe_pattern(*ptrs, write, stream.cuda_stream)
         if call() != 0:
+            if write == 3:
+                continue  # the phased probe covers N = 64 only
             return None  # a replica count or alignment the probe does not cover
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -135,7 +144,8 @@ def pattern_ceiling(w, d, window=(0, 0), reps: int = 5):
             call()
         e1.record(stream)
         torch.cuda.synchronize()
-        out[f"{name}_GBps"] = bpp * full * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+        params = int(covered.item()) if write == 3 else full
+        out[f"{name}_GBps"] = bpp * params * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
     return out
 
 
@@ -428,15 +438,19 @@ def main() -> int:
         kernel = ("flat_window_kernel" if window[0] else "flat_kernel") + tn
     pattern = None
     if args.path == "fused" and not w.is_list and not args.no_copy and footprint >= (1 << 30):
-        pattern = pattern_ceiling(w, d, window)
+        pattern = pattern_ceiling(w, d, window, phased=sched == "phased")
         if pattern:
-            same = pattern.get("read_write_windowed_GBps", pattern["read_write_GBps"])
+            own = ("read_write_phased_GBps" if sched == "phased" and "read_write_phased_GBps" in pattern else
+                   "read_write_windowed_GBps" if window[0] else "read_write_GBps")
+            same = pattern[own]
             pattern["kernel_frac_of_read_write"] = achieved / same
+            pattern["kernel_pattern"] = own[:-5]
             log(f"access-pattern ceiling without arithmetic: reads alone {pattern['read_GBps']:.0f} GB/s, "
-                f"reads+writes {pattern['read_write_GBps']:.0f} GB/s"
+                f"reads+writes stored per tile {pattern['read_write_GBps']:.0f} GB/s"
                 + (f", with the step's write windows {same:.0f} GB/s" if window[0] else "")
+                + (f", on the step's phased schedule {same:.0f} GB/s" if own == "read_write_phased_GBps" else "")
                 + f"; the step reaches {100 * pattern['kernel_frac_of_read_write']:.1f}% of the pattern with "
-                  f"its own write schedule")
+                  f"its own schedule")
     offload_parts = None
     if offload is not None:
         offload.close()

@@ -23,6 +23,8 @@ def load():
         lib.zs_probe_pattern.argtypes = [ctypes.POINTER(vp), i32, i64, vp, vp, vp, vp, i32, vp]
         lib.zs_probe_pattern_windowed.restype = ctypes.c_int
         lib.zs_probe_pattern_windowed.argtypes = [ctypes.POINTER(vp), i32, i64, vp, vp, vp, vp, i32, i32, vp]
+        lib.zs_probe_pattern_phased.restype = ctypes.c_int
+        lib.zs_probe_pattern_phased.argtypes = [ctypes.POINTER(vp), i32, i64, vp, vp, vp, vp, vp, vp]
         lib.zs_probe_copy.restype = ctypes.c_int
         lib.zs_probe_copy.argtypes = [vp, vp, i64, vp]
         _lib = lib

@@ -27,6 +27,7 @@
 //    lines), SGPR-base addressing, non-temporal loads and stores, and
 //    consecutive launches of at most 3e9 bytes each.
 #include "zs_device.h"
+#include "zs_phased.h"
 
 namespace zs {
 namespace {
@@ -195,6 +196,32 @@ __global__ __launch_bounds__(kFlatBlock) void copy_kernel(const float* __restric
   }
 }
 
+// The phased schedule's pattern (zs_probe_pattern_phased): the library's own
+// super-chunk loop (zs_phased.h), its AdamW replaced by the write = 1 values.
+template <int NT>
+__global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void pattern_phased_kernel(const ProbeArgs<NT> a, int64_t n,
+                                                                                   int32_t slot, int64_t* covered) {
+  FlatShape s{};
+  s.p = a.p;
+  s.m = a.m;
+  s.v = a.v;
+  s.b = a.b;
+  s.n = n;
+  s.head = 0;
+  s.nvec = n / 8;
+  auto G = [&](int r) { return a.g[r]; };
+  const int64_t t = phased_super_chunks<NT>(G, NT, s, slot, kPhasedMaxPolls,
+                                            [](const float(&acc)[8], float(&p)[8], float(&m)[8], float(&v)[8]) {
+#pragma unroll
+                                              for (int k = 0; k < 8; ++k) {
+                                                p[k] = p[k] + acc[k];
+                                                v[k] = v[k] + m[k];
+                                                m[k] = acc[k];
+                                              }
+                                            });
+  if (blockIdx.x == 0 && threadIdx.x == 0) *covered = t * (kFlatBlock * 8);
+}
+
 bool line_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 127) == 0; }
 
 }  // namespace
@@ -275,4 +302,36 @@ extern "C" __attribute__((visibility("default"))) int zs_probe_copy(const float*
     if (hipGetLastError() != hipSuccess) return 2;
   }
   return 0;
+}
+
+// The phased pattern over the whole super-chunks of the n-parameter arrays (N =
+// 64 only), one workgroup of 12 waves per compute unit; *covered (device
+// int64) receives the number of parameters it covered.  Returns as
+// zs_probe_pattern.
+extern "C" __attribute__((visibility("default"))) int zs_probe_pattern_phased(
+    const uint16_t* const* g, int32_t N, int64_t n, float* p, float* m, float* v, uint16_t* b, int64_t* covered,
+    void* stream) {
+  using namespace zs;
+  if (N != 64 || n < kFlatBlock * 8 || !g || !p || !m || !v || !b || !covered) return 1;
+  if (!line_aligned(p) || !line_aligned(m) || !line_aligned(v) || !line_aligned(b)) return 1;
+  for (int32_t r = 0; r < N; ++r)
+    if (!g[r] || !line_aligned(g[r])) return 1;
+  ProbeArgs<64> a;
+  for (int r = 0; r < 64; ++r) a.g[r] = g[r];
+  a.p = p;
+  a.m = m;
+  a.v = v;
+  a.b = b;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pattern_phased_kernel<64>, kFlatBlock * kPhasedWaves,
+                                                   0) != hipSuccess ||
+      cus * per_cu < 1)
+    return 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  phased_clear_kernel<<<dim3(1), dim3(64), 0, s>>>(0);
+  pattern_phased_kernel<64><<<dim3(cus * per_cu), dim3(kFlatBlock * kPhasedWaves), 0, s>>>(a, n, 0, covered);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
 }

@@ -477,9 +477,10 @@ ZS_API zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* 
      ZS_SCHEDULE_AUTO:     the default.  An explicit zs_set_write_window
                            decides when one was made (no windows:
                            ZS_SCHEDULE_STREAM; a window: ZS_SCHEDULE_WINDOWED);
-                           otherwise ZS_SCHEDULE_PHASED for N >= 48 replicas on
+                           otherwise ZS_SCHEDULE_PHASED for N >= 32 replicas on
                            shards of at least 2^25 parameters, and
-                           ZS_SCHEDULE_STREAM below.
+                           ZS_SCHEDULE_STREAM below (at N = 8 and 16 per-tile
+                           stores measured faster).
      ZS_SCHEDULE_STREAM:   one 512-parameter tile per workgroup, its outputs
                            stored as soon as it is done; consecutive launches
                            of at most zs_launch_bytes() each.
@@ -494,9 +495,10 @@ ZS_API zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* 
                            tiles into register accumulators, the workgroup's
                            waves kept on the same replicas, so the device
                            reads one or two replica streams at a time over one
-                           contiguous region each; then, after a grid barrier,
-                           it reads master, m and v and writes the four
-                           outputs of the super-chunk.  Any shard of at least
+                           contiguous region each; then, after a grid barrier
+                           (released once 95% of the workgroups have
+                           arrived), it reads master, m and v and writes the
+                           four outputs of the super-chunk.  Any shard of at least
                            one whole tile.  The barrier counter lives in the
                            library's device memory (16 slots, one per launch in
                            turn): phased calls that run at the same time on one

@@ -202,7 +202,7 @@ zs::WriteWindow write_window(int32_t N) {
 // the write window it takes (period_mask 0 unless windowed).  An explicit
 // zs_set_flat_schedule wins; otherwise an explicit zs_set_write_window decides
 // (no windows: per-tile stores; a window: the windowed kernel); otherwise the
-// phased kernel for N >= kPhasedMinReplicas on shards of at least
+// phased kernel for N >= kPhasedMinReplicas (32) on shards of at least
 // kPhasedMinParams, and per-tile stores below.
 zs::FlatSchedule flat_schedule(int32_t N, int64_t n, zs::WriteWindow* win) {
   const int32_t forced = g_flat_schedule.load(std::memory_order_relaxed);

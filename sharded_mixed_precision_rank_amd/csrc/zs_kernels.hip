@@ -45,6 +45,7 @@
 #include <atomic>
 
 #include "zs_device.h"
+#include "zs_phased.h"
 
 namespace zs {
 namespace {
@@ -257,7 +258,8 @@ __global__ __launch_bounds__(kFlatBlock) void flat_window_kernel(const FlatArgs<
 // workgroups start the phase together, so at any moment the chip reads one or
 // two replica streams, each over one contiguous region, instead of all N
 // interleaved (on this memory system reading 2 streams at once runs about 9%
-// faster than reading 64).  The workgroups then meet at a grid barrier.
+// faster than reading 64).  The workgroups then meet at a grid barrier, which
+// lets them go once kPhasedQuorumPct percent of them have arrived.
 // Phase B: each wave reads its tiles' master, m and v, applies AdamW and
 // writes master, m, v and the bf16 copy, so the super-chunk's 14 bytes per
 // parameter of writes go out together instead of trickling out beside the
@@ -272,154 +274,26 @@ __global__ __launch_bounds__(kFlatBlock) void flat_window_kernel(const FlatArgs<
 // most ctl.max_polls polls at the grid barrier and then goes on, so the kernel
 // ends even when not every workgroup is resident (other work on the device).
 
-// Grid-barrier counters, one per slot, each in its own 128-byte line; a
-// launch clears its slot on its stream before the kernel starts.
-__device__ __align__(128) uint32_t g_phased_counters[kPhasedSlots * 32];
-
-__global__ void phased_clear_kernel(int32_t slot) {
-  if (blockIdx.x == 0 && threadIdx.x == 0)
-    __hip_atomic_store(&g_phased_counters[32 * slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Every workgroup adds one to the counter and waits (bounded) until all
-// gridDim.x of them have added their `round`-th one.
-__device__ __forceinline__ void phased_grid_barrier(uint32_t* counter, uint32_t target, int32_t max_polls) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int32_t k = 0; k < max_polls; ++k) {
-      if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-  }
-  __syncthreads();
-}
-
 template <int NT>
 __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void flat_phased_kernel(const FlatArgs<NT> a,
                                                                                 const PhasedCtl ctl) {
-  constexpr int K = kPhasedTiles;
-  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
   Scalars c = a.c;
   if (!step_scalars(a.r, c)) return;  // the same decision in every workgroup
   const int N = NT > 0 ? NT : c.n_rep;
   const FlatShape& s = a.s;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t e = 4u * (threadIdx.x & 63u);  // the split lane layout inside a tile
+  const uint32_t e = 4u * (threadIdx.x & 63u);
   const int64_t nw = (int64_t)gridDim.x * kPhasedWaves;
   const int64_t gw = (int64_t)blockIdx.x * kPhasedWaves + wave;
   const int64_t full = s.nvec / kFlatBlock;  // whole tiles
-  const int64_t per = nw * K;                // tiles per super-chunk
-  const int64_t nsup = full / per;           // whole super-chunks; the rest of the tiles after them
-  uint32_t* counter = &g_phased_counters[32 * ctl.slot];
-  for (int64_t sc = 0; sc < nsup; ++sc) {
-    // slot k of this wave: tile sc*per + k*nw + gw, from element es[k] (wave-uniform)
-    int64_t es[K];
+  auto G0 = [&](int r) { return a.g[r]; };
+  const int64_t covered = phased_super_chunks<NT>(
+      G0, N, s, ctl.slot, ctl.max_polls, [&](const float(&acc)[8], float(&p)[8], float(&m)[8], float(&v)[8]) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) es[k] = s.head + 8 * kFlatBlock * (sc * per + k * nw + gw);
-    // ---- phase A: the replicas, in rank order, into the accumulators
-    float acc[K][8];
-    {
-      u32x2 w0[K][2], w1[K][2];
-      auto load = [&](int r, u32x2(&w)[K][2]) {
-        const uint16_t* g = a.g[r];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const GLB u32x2* q = (const GLB u32x2*)at(tile_base(g + es[k]), here(e) * 2u);
-          w[k][0] = ld_g(q);
-          w[k][1] = ld_g(q + q2);  // the second quad: 256 elements on (64 u32x2)
-        }
-      };
-      auto add = [&](const u32x2(&w)[K][2], bool first) {
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const float x[8] = {bf_lo(w[k][0].x), bf_hi(w[k][0].x), bf_lo(w[k][0].y), bf_hi(w[k][0].y),
-                              bf_lo(w[k][1].x), bf_hi(w[k][1].x), bf_lo(w[k][1].y), bf_hi(w[k][1].y)};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[k][j] = first ? x[j] : acc[k][j] + x[j];
-        }
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(acc[k][j]));
-      };
-      load(0, w0);
-      if constexpr (NT > 0) {
-#pragma unroll
-        for (int r = 0; r < NT; r += 2) {
-          if (r + 1 < NT) load(r + 1, w1);
-          __builtin_amdgcn_sched_barrier(0);
-          add(w0, r == 0);
-          __builtin_amdgcn_sched_barrier(0);
-          if (r + 2 < NT) load(r + 2, w0);
-          __builtin_amdgcn_sched_barrier(0);
-          if (r + 1 < NT) add(w1, false);
-          __builtin_amdgcn_sched_barrier(0);
-          __syncthreads();  // keep the workgroup's waves on the same replicas
-        }
-      } else {
-#pragma unroll 1
-        for (int r = 0; r < N; r += 2) {
-          if (r + 1 < N) load(r + 1, w1);
-          __builtin_amdgcn_sched_barrier(0);
-          add(w0, r == 0);
-          __builtin_amdgcn_sched_barrier(0);
-          if (r + 2 < N) load(r + 2, w0);
-          __builtin_amdgcn_sched_barrier(0);
-          if (r + 1 < N) add(w1, false);
-          __builtin_amdgcn_sched_barrier(0);
-          __syncthreads();
-        }
-      }
-    }
-    phased_grid_barrier(counter, (uint32_t)(sc + 1) * gridDim.x, ctl.max_polls);
-    // ---- phase B: state, AdamW, outputs, tile by tile (the next tile's state in flight)
-    {
-      f32x4 st[2][6];
-      auto sload = [&](int k, f32x4(&q)[6]) {
-        const uint32_t o = here(e) * 4u;
-        const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(s.p + es[k]), o);
-        const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(s.m + es[k]), o);
-        const GLB f32x4* V4 = (const GLB f32x4*)at(tile_base(s.v + es[k]), o);
-        q[0] = ld_g(P4);
-        q[1] = ld_g(P4 + q2);
-        q[2] = ld_g(M4);
-        q[3] = ld_g(M4 + q2);
-        q[4] = ld_g(V4);
-        q[5] = ld_g(V4 + q2);
-      };
-      sload(0, st[0]);
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        {
-          if (k + 1 < K) sload(k + 1, st[(k + 1) & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-          const f32x4* q = st[k & 1];
-          float p[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
-          float m[8] = {q[2].x, q[2].y, q[2].z, q[2].w, q[3].x, q[3].y, q[3].z, q[3].w};
-          float v[8] = {q[4].x, q[4].y, q[4].z, q[4].w, q[5].x, q[5].y, q[5].z, q[5].w};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) adam(mean_of<NT>(acc[k][j], c), p[j], m[j], v[j], c);
-          const TileOut h = tile_outputs(p, m, v);
-          const uint32_t o = here(e) * 4u;
-          GLB f32x4* P4 = (GLB f32x4*)at(tile_base(s.p + es[k]), o);
-          GLB f32x4* M4 = (GLB f32x4*)at(tile_base(s.m + es[k]), o);
-          GLB f32x4* V4 = (GLB f32x4*)at(tile_base(s.v + es[k]), o);
-          st_g(P4, h.p0);
-          st_g(P4 + q2, h.p1);
-          st_g(M4, h.m0);
-          st_g(M4 + q2, h.m1);
-          st_g(V4, h.v0);
-          st_g(V4 + q2, h.v1);
-          GLB u32x2* B2 = (GLB u32x2*)at(tile_base(s.b + es[k]), here(e) * 2u);
-          st_g(B2, h.b0);
-          st_g(B2 + q2, h.b1);
-        }
-      }
-    }
-  }
+        for (int j = 0; j < 8; ++j) adam(mean_of<NT>(acc[j], c), p[j], m[j], v[j], c);
+      });
   // the whole tiles after the last super-chunk, one at a time per wave, stored as each is done
-  for (int64_t t = nsup * per + gw; t < full; t += nw) {
+  for (int64_t t = covered + gw; t < full; t += nw) {
     const int64_t e0 = s.head + 8 * kFlatBlock * t;
     auto G = [&](int r) { return tile_base(a.g[r] + e0); };
     group_step_at<NT, true>(G, N, e0, e, s, c);

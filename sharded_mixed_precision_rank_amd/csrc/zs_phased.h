@@ -1,0 +1,174 @@
+// The phased schedule's super-chunk loop (see flat_phased_kernel in
+// zs_kernels.hip), shared by the library's kernel and the benchmark's
+// access-pattern probe, which replays it with its arithmetic taken out: one
+// copy of the code, so the probe's pattern is the kernel's.
+#pragma once
+
+#include "zs_device.h"
+
+namespace zs {
+namespace dev {
+namespace {  // each including source file (the library's, the probe's) gets its own counters
+
+// Grid-barrier counters, one per slot, each in its own 128-byte line; a
+// launch clears its slot on its stream before the kernel starts.
+__device__ __align__(128) uint32_t g_phased_counters[kPhasedSlots * 32];
+
+__global__ void phased_clear_kernel(int32_t slot) {
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_store(&g_phased_counters[32 * slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every workgroup adds one to the counter and waits (bounded) until it reads
+// at least `target`.
+__device__ __forceinline__ void phased_grid_barrier(uint32_t* counter, uint32_t target, int32_t max_polls) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int32_t k = 0; k < max_polls; ++k) {
+      if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
+// Workgroups whose arrival releases a grid barrier: kPhasedQuorum of the grid (all of a grid of up to 19).
+__device__ __forceinline__ uint32_t phased_quorum(uint32_t grid) {
+  return (grid * kPhasedQuorumPct + 99u) / 100u;
+}
+
+// The whole super-chunks of a flat shard (tiles of 512 parameters from element
+// s.head; s.nvec 8-element groups on the vector path): phase A, the grid
+// barrier, phase B, for each.  gp(r) is replica r's gradient pointer (the
+// shard's element 0); upd(acc, p, m, v) turns the 8 rank-ordered replica sums
+// of a lane and its 8 master, m and v values into the new master, m and v.
+// Returns the number of whole tiles covered; the caller takes the rest.
+// Launched as one workgroup of kPhasedWaves waves per compute unit.
+template <int NT, class GP, class UPD>
+__device__ __forceinline__ int64_t phased_super_chunks(GP gp, int N, const FlatShape& s, int32_t slot,
+                                                      int32_t max_polls, UPD&& upd) {
+  constexpr int K = kPhasedTiles;
+  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t e = 4u * (threadIdx.x & 63u);  // the split lane layout inside a tile
+  const int64_t nw = (int64_t)gridDim.x * kPhasedWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kPhasedWaves + wave;
+  const int64_t full = s.nvec / kFlatBlock;  // whole tiles
+  const int64_t per = nw * K;                // tiles per super-chunk
+  const int64_t nsup = full / per;           // whole super-chunks; the rest of the tiles after them
+  uint32_t* counter = &g_phased_counters[32 * slot];
+  for (int64_t sc = 0; sc < nsup; ++sc) {
+    // slot k of this wave: tile sc*per + k*nw + gw, from element es[k] (wave-uniform)
+    int64_t es[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) es[k] = s.head + 8 * kFlatBlock * (sc * per + k * nw + gw);
+    // ---- phase A: the replicas, in rank order, into the accumulators
+    float acc[K][8];
+    {
+      u32x2 w0[K][2], w1[K][2];
+      auto load = [&](int r, u32x2(&w)[K][2]) {
+        const uint16_t* g = gp(r);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const GLB u32x2* q = (const GLB u32x2*)at(tile_base(g + es[k]), here(e) * 2u);
+          w[k][0] = ld_g(q);
+          w[k][1] = ld_g(q + q2);  // the second quad: 256 elements on (64 u32x2)
+        }
+      };
+      auto add = [&](const u32x2(&w)[K][2], bool first) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const float x[8] = {bf_lo(w[k][0].x), bf_hi(w[k][0].x), bf_lo(w[k][0].y), bf_hi(w[k][0].y),
+                              bf_lo(w[k][1].x), bf_hi(w[k][1].x), bf_lo(w[k][1].y), bf_hi(w[k][1].y)};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[k][j] = first ? x[j] : acc[k][j] + x[j];
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(acc[k][j]));
+      };
+      load(0, w0);
+      if constexpr (NT > 0) {
+#pragma unroll
+        for (int r = 0; r < NT; r += 2) {
+          if (r + 1 < NT) load(r + 1, w1);
+          __builtin_amdgcn_sched_barrier(0);
+          add(w0, r == 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (r + 2 < NT) load(r + 2, w0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (r + 1 < NT) add(w1, false);
+          __builtin_amdgcn_sched_barrier(0);
+          __syncthreads();  // keep the workgroup's waves on the same replicas
+        }
+      } else {
+#pragma unroll 1
+        for (int r = 0; r < N; r += 2) {
+          if (r + 1 < N) load(r + 1, w1);
+          __builtin_amdgcn_sched_barrier(0);
+          add(w0, r == 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (r + 2 < N) load(r + 2, w0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (r + 1 < N) add(w1, false);
+          __builtin_amdgcn_sched_barrier(0);
+          __syncthreads();
+        }
+      }
+    }
+    // ---- phase B: state, AdamW, outputs, tile by tile (the next tile's state in flight).  The first
+    // tile's state is requested before the barrier: reads, like the stragglers' replica reads.
+    f32x4 st[2][6];
+    auto sload = [&](int k, f32x4(&q)[6]) {
+        const uint32_t o = here(e) * 4u;
+        const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(s.p + es[k]), o);
+        const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(s.m + es[k]), o);
+        const GLB f32x4* V4 = (const GLB f32x4*)at(tile_base(s.v + es[k]), o);
+        q[0] = ld_g(P4);
+        q[1] = ld_g(P4 + q2);
+        q[2] = ld_g(M4);
+        q[3] = ld_g(M4 + q2);
+        q[4] = ld_g(V4);
+        q[5] = ld_g(V4 + q2);
+      };
+    sload(0, st[0]);
+    // the grid barrier lets the workgroups go once kPhasedQuorum of them have arrived: waiting for the
+    // last few costs more than their reads overlapping the others' writes
+    phased_grid_barrier(counter, (uint32_t)sc * gridDim.x + phased_quorum(gridDim.x), max_polls);
+    {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        {
+          if (k + 1 < K) sload(k + 1, st[(k + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          const f32x4* q = st[k & 1];
+          float p[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
+          float m[8] = {q[2].x, q[2].y, q[2].z, q[2].w, q[3].x, q[3].y, q[3].z, q[3].w};
+          float v[8] = {q[4].x, q[4].y, q[4].z, q[4].w, q[5].x, q[5].y, q[5].z, q[5].w};
+          upd(acc[k], p, m, v);
+          const TileOut h = tile_outputs(p, m, v);
+          const uint32_t o = here(e) * 4u;
+          GLB f32x4* P4 = (GLB f32x4*)at(tile_base(s.p + es[k]), o);
+          GLB f32x4* M4 = (GLB f32x4*)at(tile_base(s.m + es[k]), o);
+          GLB f32x4* V4 = (GLB f32x4*)at(tile_base(s.v + es[k]), o);
+          st_g(P4, h.p0);
+          st_g(P4 + q2, h.p1);
+          st_g(M4, h.m0);
+          st_g(M4 + q2, h.m1);
+          st_g(V4, h.v0);
+          st_g(V4 + q2, h.v1);
+          GLB u32x2* B2 = (GLB u32x2*)at(tile_base(s.b + es[k]), here(e) * 2u);
+          st_g(B2, h.b0);
+          st_g(B2 + q2, h.b1);
+        }
+      }
+    }
+  }
+  return nsup * per;
+}
+
+}  // namespace
+}  // namespace dev
+}  // namespace zs

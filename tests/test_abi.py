@@ -467,12 +467,13 @@ def test_tuning_knobs_check_their_ranges():
 
 
 def test_flat_schedule_query_and_setting():
-    """The automatic schedule: phased for N >= 48 on shards of at least 2^25 parameters, per-tile stores
+    """The automatic schedule: phased for N >= 32 on shards of at least 2^25 parameters, per-tile stores
     otherwise; an explicit schedule wins (each kernel's own size conditions aside)."""
     assert zs.flat_schedule(64, 1_093_750_000) == "phased"
-    assert zs.flat_schedule(48, 1 << 25) == "phased"
+    assert zs.flat_schedule(32, 1 << 25) == "phased"
     assert zs.flat_schedule(256, 1 << 30) == "phased"
-    assert zs.flat_schedule(47, 1 << 30) == "stream"
+    assert zs.flat_schedule(31, 1 << 30) == "stream"
+    assert zs.flat_schedule(16, 1 << 30) == "stream"
     assert zs.flat_schedule(8, 124_000_000) == "stream"
     assert zs.flat_schedule(64, (1 << 25) - 1) == "stream"
     zs.set_write_window(1)   # an explicit "no windows" keeps per-tile stores

@@ -81,3 +81,44 @@ def test_probe_copy_in_several_launches():
     assert torch.equal(dst.view(torch.int32), src.view(torch.int32))
     del src, dst
     torch.cuda.empty_cache()
+
+
+def test_probe_phased_pattern():
+    """The phased pattern (the library's super-chunk loop with its AdamW replaced by the write = 1
+    values) covers the whole super-chunks, writes there what the per-tile pattern writes, and nothing
+    past them."""
+    import torch
+
+    import bench_probe
+
+    lib = bench_probe.load()
+    dev = torch.device("cuda:0")
+    N = 64
+    n = 256 * 12 * 8 * 512 + 5_000   # one super-chunk on a 256-workgroup grid, and a rest
+    gen = torch.Generator().manual_seed(9)
+    G = [torch.randint(-2 ** 14, 2 ** 14, (n,), dtype=torch.int16, generator=gen).to(dev) for _ in range(N)]
+    P, M, V = (torch.randn(n, generator=gen).to(dev) for _ in range(3))
+    B = torch.zeros(n, dtype=torch.int16, device=dev)
+    before = [x.clone() for x in (P, M, V, B)]
+    tab = (ctypes.c_void_p * N)(*[g.data_ptr() for g in G])
+    s = torch.cuda.current_stream().cuda_stream
+    covered = torch.zeros(1, dtype=torch.int64, device=dev)
+    assert lib.zs_probe_pattern_phased(tab, N, n, P.data_ptr(), M.data_ptr(), V.data_ptr(), B.data_ptr(),
+                                       covered.data_ptr(), s) == 0
+    torch.cuda.synchronize()
+    c = int(covered.item())
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    assert c == (n // 512) // (cus * 12 * 8) * (cus * 12 * 8) * 512 and c > 0
+    for a, b in zip((P, M, V, B), before):
+        assert torch.equal(a[c:], b[c:]), "the phased pattern wrote past its super-chunks"
+    got = [x[:c].clone() for x in (P, M, V, B)]
+    for x, b0 in zip((P, M, V, B), before):
+        x.copy_(b0)
+    f = lib.zs_probe_pattern
+    assert f(tab, N, n, P.data_ptr(), M.data_ptr(), V.data_ptr(), B.data_ptr(), 1, s) == 0
+    torch.cuda.synchronize()
+    bits = lambda x: x.view(torch.int32) if x.dtype == torch.float32 else x  # noqa: E731
+    for a, b in zip(got, (P, M, V, B)):
+        assert torch.equal(bits(a), bits(b[:c])), "the phased pattern wrote other values than the per-tile one"
+    del G, P, M, V, B
+    torch.cuda.empty_cache()
