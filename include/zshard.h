@@ -142,13 +142,14 @@ typedef struct zs_tensor {
   const uint16_t* const* grad_chunks; /* host array of N device pointers */
 } zs_tensor;
 
-/* A device-resident chunk table for a fixed list of tensors: built once,
-   then one kernel per step covers every tensor. */
+/* A device-resident work table for a fixed list of tensors (one entry per
+   512-parameter wave tile, naming its tensor): built once, then one kernel
+   per step covers every tensor. */
 typedef struct zs_list_plan* zs_list_plan_t;
 
 /* Validates the list (as the flat call, per tensor, plus: outputs of all
    tensors pairwise disjoint and disjoint from every gradient range), splits
-   every tensor into chunks, and uploads the table on `stream`; returns after
+   every tensor into wave tiles, and uploads the table on `stream`; returns after
    the upload has completed.  T >= 0 tensors, 1 <= N <= ZS_MAX_REPLICAS.
    Errors: ZS_ERR_NULL, ZS_ERR_RANGE, ZS_ERR_ALIGN, ZS_ERR_ALIAS, ZS_ERR_NOMEM,
    ZS_ERR_HIP. */
@@ -156,7 +157,7 @@ ZS_API zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_
                                      zs_list_plan_t* out);
 
 /* The step on every tensor of the plan: one kernel on `stream` (one launch,
-   or consecutive launches over the chunk table, zs_set_launch_bytes).  The
+   or consecutive launches over the work table, zs_set_launch_bytes).  The
    plan's table lives on the device that was current at creation; calling with
    another device current fails with ZS_ERR_RANGE. */
 ZS_API zs_status zs_reduce_adam_list_plan(zs_list_plan_t plan, const zs_adam_hp* hp, int64_t step,
@@ -189,13 +190,13 @@ ZS_API zs_status zs_reduce_adam_list(const zs_tensor* tensors, int32_t T, int32_
 /* For callers that cannot allocate device memory (code that must not call
    hipMalloc, such as tight serving loops or harnesses that forbid it): the
    one-shot list step of zs_reduce_adam_list, with the same arguments,
-   checks, kernels and results, whose chunk table goes into a fixed array of
+   checks, kernels and results, whose work table goes into a fixed array of
    ZS_STATIC_TABLE_BYTES (32 MiB) of device memory that the library holds on
    each device it runs on until the process ends, instead of a plan allocated
    and freed per call.  The call uploads the table on `stream`, runs the step
    there and waits for it (it blocks the calling thread), and calls no
-   hipMalloc or hipFree.  The table takes 32 bytes per chunk (a chunk is
-   4,096 parameters of a tensor, or fewer at its end), 64 per tensor and 8 per
+   hipMalloc or hipFree.  The table takes 4 bytes per work item (a wave tile:
+   512 parameters of a tensor, or fewer at either end), 64 per tensor and 8 per
    tensor per replica: a list whose table needs more returns ZS_ERR_RANGE
    (about 4 billion parameters in all for 1,000 tensors and N = 64).  Every call on
    a device shares that device's array and rewrites it: calls that overlap on
@@ -251,8 +252,9 @@ ZS_API zs_status zs_reduce_adam_list_plan_devstep(zs_list_plan_t plan, const zs_
 /* Waits for the device to go idle, then frees the plan's table.  NULL is a no-op. */
 ZS_API void zs_list_plan_destroy(zs_list_plan_t plan);
 
-/* Shape of a plan: total parameters, tensors and chunks (any output may be NULL). */
-ZS_API zs_status zs_list_plan_info(zs_list_plan_t plan, int64_t* n_params, int32_t* n_tensors, int32_t* n_chunks);
+/* Shape of a plan: total parameters, tensors and work items (wave tiles, one
+   workgroup each; any output may be NULL). */
+ZS_API zs_status zs_list_plan_info(zs_list_plan_t plan, int64_t* n_params, int32_t* n_tensors, int32_t* n_items);
 
 /* ---------------------------------------------------------------------------
  * Two-pass form: global-norm gradient clipping and fp16 loss scaling.
@@ -408,7 +410,7 @@ ZS_API zs_status zs_set_grid_blocks(int32_t blocks);
    moves, for all later calls in this process: the flat step and list plans
    when they take no write windows, and both passes of the two-pass form
    (pass 1 when it takes none).  Such a call covers its shard in consecutive
-   launches on its stream, each of whole tiles (whole chunks for list plans)
+   launches on its stream, each of whole tiles (whole work items for list plans)
    and at most this many bytes by the step's byte model, and always at least
    one tile.  On this memory system one long launch lost up to 13% against
    the same work cut into launches of 1.3-5 GB.  The windowed kernels are

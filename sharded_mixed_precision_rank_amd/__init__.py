@@ -489,7 +489,7 @@ class ListPlan:
         n, t, c = _i64(), _i32(), _i32()
         _check(_lib.zs_list_plan_info(self._h, ctypes.byref(n), ctypes.byref(t), ctypes.byref(c)),
                "zs_list_plan_info")
-        return dict(n_params=n.value, n_tensors=t.value, n_chunks=c.value)
+        return dict(n_params=n.value, n_tensors=t.value, n_items=c.value)
 
     def close(self) -> None:
         if self._h:

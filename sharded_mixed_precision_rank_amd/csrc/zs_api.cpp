@@ -307,6 +307,33 @@ int64_t common_peel_sized(const void* const* ptrs, const int* elem_bytes, int co
   return -1;
 }
 
+// Tiles that also start on a boundary of 512 of their own elements run
+// faster again: the same flat shard with every array starting 64 to 448
+// elements past such a boundary took 2.6-4.1% longer than from the boundary
+// (a ragged list, whose tensors start at every phase, lost about as much).
+int64_t tile_anchor_sized(const void* const* ptrs, const int* elem_bytes, int count) {
+  int64_t phase = -1;
+  for (int k = 0; k < count; ++k) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(ptrs[k]);
+    if (a % (uintptr_t)elem_bytes[k] != 0) return -1;
+    const int64_t ph = (int64_t)((a / (uintptr_t)elem_bytes[k]) % (uintptr_t)kTileElemsWave);
+    if (phase >= 0 && ph != phase) return -1;
+    phase = ph;
+  }
+  return phase <= 0 ? 0 : kTileElemsWave - phase;
+}
+
+int64_t tile_anchor(const float* p, const float* m, const float* v, const uint16_t* b, const uint16_t* const* g,
+                    int32_t N) {
+  std::vector<const void*> ptrs{p, m, v, b};
+  std::vector<int> sizes{4, 4, 4, 2};
+  for (int32_t r = 0; r < N; ++r) {
+    ptrs.push_back(g[r]);
+    sizes.push_back(2);
+  }
+  return tile_anchor_sized(ptrs.data(), sizes.data(), (int)ptrs.size());
+}
+
 int64_t common_peel(const float* p, const float* m, const float* v, const uint16_t* b, const uint16_t* const* g,
                     int32_t N) {
   std::vector<const void*> ptrs{p, m, v, b};
@@ -407,19 +434,21 @@ int offload_blocks() { return auto_blocks(); }
 
 namespace {
 
-// A list plan's device table, laid out on the host: chunks | tensors | grad
+// A list plan's device table, laid out on the host: items | tensors | grad
 // pointers, in one byte image ready to upload.
 struct ListTable {
   std::vector<unsigned char> bytes;
   size_t off_tensors = 0, off_gptrs = 0;
-  int32_t n_chunks = 0;
+  int32_t n_items = 0;
   int64_t n_params = 0;
 };
 
 // Checks the tensors (as zs_list_plan_create documents) and lays out their
-// table: every vector tensor cut into chunks of kChunkElems parameters from
-// its common alignment peel, every scalar-only tensor into chunks of
-// kChunkElems elements.
+// table: one work item per wave tile, tensor by tensor.  A vector tensor's
+// tiles start at its tile grid's anchor (the groups before it, if any, a
+// partial tile of their own); a scalar-only tensor's items take 512 elements
+// each.  Every item is a whole or partial tile of one tensor, so no workgroup
+// is launched for nothing.
 zs_status build_list_table(const zs_tensor* tensors, int32_t T, int32_t N, ListTable& out) {
   if (T < 0) return fail(ZS_ERR_RANGE, "T must be >= 0 (got %d)", T);
   if (T > 0 && !tensors) return fail(ZS_ERR_NULL, "tensors is NULL");
@@ -435,14 +464,18 @@ zs_status build_list_table(const zs_tensor* tensors, int32_t T, int32_t N, ListT
   zs_status st = check_alias(rs);
   if (st) return st;
 
+  constexpr int64_t kGroupsPerTile = zs::kTileElemsWave / 8;
   std::vector<zs::ListTensor> ht;
-  std::vector<zs::ListChunk> hc;
+  std::vector<int32_t> hi;
   std::vector<const uint16_t*> hg;
   ht.reserve(T);
   hg.reserve((size_t)T * N);
   for (int32_t t = 0; t < T; ++t) {
     const zs_tensor& x = tensors[t];
+    if ((int64_t)hi.size() > (int64_t)INT32_MAX) return fail(ZS_ERR_RANGE, "too many work items");
     zs::ListTensor d{};
+    d.item0 = (int32_t)hi.size();
+    int64_t items = 0;
     if (x.n == 0) {
       d.scalar_only = 1;
     } else {
@@ -452,31 +485,36 @@ zs_status build_list_table(const zs_tensor* tensors, int32_t T, int32_t N, ListT
       d.v = s.v;
       d.b = s.b;
       d.n = s.n;
-      d.head = s.head;
+      d.head_lead = (int32_t)s.head;
       d.nvec = s.nvec;
       d.scalar_only = s.scalar_only;
       if (!s.scalar_only) {
-        const int64_t per = zs::kChunkElems / 8;
-        for (int64_t g0 = 0; g0 < s.nvec; g0 += per)
-          hc.push_back({t, g0 == 0 ? 1 : 0, g0, std::min(s.nvec, g0 + per), 0});
+        // the groups before the tile grid's anchor form a partial tile of their own, so that every
+        // later tile starts on a 512-element boundary of every array
+        const int64_t a = zs::tile_anchor(x.master, x.m, x.v, x.param_bf16, x.grad_chunks, N);
+        const int64_t lead = a > s.head ? std::min(s.nvec, (a - s.head) / 8) : 0;
+        d.head_lead |= (int32_t)lead << 8;
+        const int64_t gofs = lead > 0 ? lead - kGroupsPerTile : 0;
+        items = (s.nvec - gofs + kGroupsPerTile - 1) / kGroupsPerTile;
       } else {
-        for (int64_t e0 = 0; e0 < s.n; e0 += zs::kChunkElems)
-          hc.push_back({t, 0, e0, std::min(s.n, e0 + zs::kChunkElems), 0});
+        items = (s.n + zs::kTileElemsWave - 1) / zs::kTileElemsWave;
       }
     }
+    if ((int64_t)hi.size() + items > (int64_t)INT32_MAX) return fail(ZS_ERR_RANGE, "too many work items");
+    hi.insert(hi.end(), (size_t)items, t);
     ht.push_back(d);
     for (int32_t r = 0; r < N; ++r) hg.push_back(x.n ? x.grad_chunks[r] : nullptr);
   }
-  if (hc.size() > (size_t)INT32_MAX) return fail(ZS_ERR_RANGE, "too many chunks");
-  const size_t bc = hc.size() * sizeof(zs::ListChunk), bt = ht.size() * sizeof(zs::ListTensor),
+  // the tensor descriptors start on a 64-byte boundary after the item indices
+  const size_t bi = (hi.size() * sizeof(int32_t) + 63) / 64 * 64, bt = ht.size() * sizeof(zs::ListTensor),
                bg = hg.size() * sizeof(void*);
-  out.bytes.resize(bc + bt + bg);
-  if (bc) std::memcpy(out.bytes.data(), hc.data(), bc);
-  if (bt) std::memcpy(out.bytes.data() + bc, ht.data(), bt);
-  if (bg) std::memcpy(out.bytes.data() + bc + bt, hg.data(), bg);
-  out.off_tensors = bc;
-  out.off_gptrs = bc + bt;
-  out.n_chunks = (int32_t)hc.size();
+  out.bytes.assign(bi + bt + bg, 0);
+  if (!hi.empty()) std::memcpy(out.bytes.data(), hi.data(), hi.size() * sizeof(int32_t));
+  if (bt) std::memcpy(out.bytes.data() + bi, ht.data(), bt);
+  if (bg) std::memcpy(out.bytes.data() + bi + bt, hg.data(), bg);
+  out.off_tensors = bi;
+  out.off_gptrs = bi + bt;
+  out.n_items = (int32_t)hi.size();
   out.n_params = total;
   return ZS_OK;
 }
@@ -487,11 +525,11 @@ struct zs_list_plan {
   int device;
   int32_t N;
   int32_t T;
-  int32_t n_chunks;
+  int32_t n_items;
   int64_t n_params;
   int32_t n_groups;  // hyperparameter groups set by zs_list_plan_set_groups (1 until then)
-  void* table;  // device: chunks | tensors | grad pointers
-  zs::ListChunk* chunks;
+  void* table;  // device: items | tensors | grad pointers
+  int32_t* items;
   zs::ListTensor* tensors;
   const uint16_t** gptrs;
 };
@@ -526,6 +564,21 @@ zs_status flat_step(const uint16_t* const* grad_chunks, int32_t N, int64_t n, fl
     const zs::Scalars c = make_scalars(src ? placeholder : *hp, src ? 1 : step, N);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     zs::WriteWindow win{};
+    const int64_t a = s.scalar_only ? 0 : zs::tile_anchor(master, m, v, param_bf16, grad_chunks, N);
+    if (a > 0 && a < n) {
+      // the elements before the tile grid's anchor as a shard of their own (one-tile kernel), then the
+      // rest from the anchor, whose tiles start on a 512-element boundary of every array
+      const zs::FlatShape f = shape_of(grad_chunks, N, a, master, m, v, param_bf16);
+      const hipError_t e = zs::launch_flat(grad_chunks, f, c, ref, auto_blocks(), zs::FlatSchedule::kStream,
+                                           zs::WriteWindow{}, phased_ctl(), hs);
+      if (e != hipSuccess) return after_launch(e, hs, what);
+      std::vector<const uint16_t*> ga(grad_chunks, grad_chunks + N);
+      for (auto& q : ga) q += a;
+      const zs::FlatShape r = shape_of(ga.data(), N, n - a, master + a, m + a, v + a, param_bf16 + a);
+      const zs::FlatSchedule sched = flat_schedule(N, n - a, &win);
+      return after_launch(zs::launch_flat(ga.data(), r, c, ref, auto_blocks(), sched, win, phased_ctl(), hs), hs,
+                          what);
+    }
     const zs::FlatSchedule sched = flat_schedule(N, n, &win);
     return after_launch(zs::launch_flat(grad_chunks, s, c, ref, auto_blocks(), sched, win, phased_ctl(), hs), hs,
                         what);
@@ -697,7 +750,7 @@ zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_t N, zs
     zs_list_plan* plan = new zs_list_plan();
     plan->N = N;
     plan->T = T;
-    plan->n_chunks = tab.n_chunks;
+    plan->n_items = tab.n_items;
     plan->n_params = tab.n_params;
     plan->n_groups = 1;
     plan->table = nullptr;
@@ -720,7 +773,7 @@ zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_t N, zs
       }
     }
     unsigned char* base = static_cast<unsigned char*>(plan->table);
-    plan->chunks = reinterpret_cast<zs::ListChunk*>(base);
+    plan->items = reinterpret_cast<int32_t*>(base);
     plan->tensors = reinterpret_cast<zs::ListTensor*>(base + tab.off_tensors);
     plan->gptrs = reinterpret_cast<const uint16_t**>(base + tab.off_gptrs);
     *out = plan;
@@ -746,14 +799,14 @@ zs_status plan_on_current_device(zs_list_plan_t plan) {
 }
 
 // The list step over a device table (a plan's, or the fixed array of zs_reduce_adam_list_static).
-zs_status launch_list_table(const zs::ListChunk* chunks, int32_t n_chunks, const zs::ListTensor* tensors,
+zs_status launch_list_table(const int32_t* items, int32_t n_items, const zs::ListTensor* tensors,
                             const uint16_t* const* gptrs, int32_t N, int64_t n_params, const zs::Scalars* cs,
                             int32_t n_sets, const zs::StepRef& ref, zs_stream stream) {
   hipStream_t hs = static_cast<hipStream_t>(stream);
   // write windows for plans of at least 2^25 parameters, as for flat shards
   const zs::WriteWindow win =
       n_params >= ((int64_t)zs::kWindowMinTiles << 9) ? write_window(N) : zs::WriteWindow{0, 0};
-  return after_launch(zs::launch_list(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, auto_blocks(), win, hs), hs,
+  return after_launch(zs::launch_list(items, n_items, tensors, gptrs, cs, n_sets, ref, auto_blocks(), win, hs), hs,
                       "zs_reduce_adam_list launch");
 }
 
@@ -776,10 +829,10 @@ zs_status run_plan(zs_list_plan_t plan, const zs_adam_hp* hps, int32_t n, int64_
     }
     for (int32_t k = 0; k < n; ++k) cs[k] = make_scalars(hps[k], step, plan->N);
   }
-  if (plan->n_chunks == 0) return ZS_OK;
+  if (plan->n_items == 0) return ZS_OK;
   zs_status st = plan_on_current_device(plan);
   if (st) return st;
-  return launch_list_table(plan->chunks, plan->n_chunks, plan->tensors, plan->gptrs, plan->N, plan->n_params, cs, n,
+  return launch_list_table(plan->items, plan->n_items, plan->tensors, plan->gptrs, plan->N, plan->n_params, cs, n,
                            ref, stream);
 }
 
@@ -924,10 +977,10 @@ zs_status zs_reduce_adam_list_static(const zs_tensor* tensors, int32_t T, int32_
     if (st) return st;
     if (tab.bytes.size() > kStaticTableBytes)
       return fail(ZS_ERR_RANGE,
-                  "the list's table needs %zu bytes (%d chunks of %lld parameters, %d tensors, %d replicas); "
-                  "zs_reduce_adam_list_static holds at most %zu: use zs_reduce_adam_list or a plan",
-                  tab.bytes.size(), tab.n_chunks, (long long)zs::kChunkElems, T, N, kStaticTableBytes);
-    if (tab.n_chunks == 0) return ZS_OK;
+                  "the list's table needs %zu bytes (%d work items of up to %lld parameters, %d tensors, %d "
+                  "replicas); zs_reduce_adam_list_static holds at most %zu: use zs_reduce_adam_list or a plan",
+                  tab.bytes.size(), tab.n_items, (long long)zs::kTileElemsWave, T, N, kStaticTableBytes);
+    if (tab.n_items == 0) return ZS_OK;
     void* base = nullptr;
     st = scratch_address(&base);
     if (st) return st;
@@ -936,7 +989,7 @@ zs_status zs_reduce_adam_list_static(const zs_tensor* tensors, int32_t T, int32_
     if (e != hipSuccess) return hip_fail(e, "table upload");
     unsigned char* b = static_cast<unsigned char*>(base);
     const zs::Scalars c = make_scalars(*hp, step, N);
-    st = launch_list_table(reinterpret_cast<const zs::ListChunk*>(b), tab.n_chunks,
+    st = launch_list_table(reinterpret_cast<const int32_t*>(b), tab.n_items,
                            reinterpret_cast<const zs::ListTensor*>(b + tab.off_tensors),
                            reinterpret_cast<const uint16_t* const*>(b + tab.off_gptrs), N, tab.n_params, &c, 1,
                            zs::StepRef{}, stream);
@@ -1186,11 +1239,11 @@ int32_t zs_loss_scaler_update(zs_loss_scaler* s, int32_t overflow) {
   return 1;
 }
 
-zs_status zs_list_plan_info(zs_list_plan_t plan, int64_t* n_params, int32_t* n_tensors, int32_t* n_chunks) {
+zs_status zs_list_plan_info(zs_list_plan_t plan, int64_t* n_params, int32_t* n_tensors, int32_t* n_items) {
   if (!plan) return fail(ZS_ERR_NULL, "plan is NULL");
   if (n_params) *n_params = plan->n_params;
   if (n_tensors) *n_tensors = plan->T;
-  if (n_chunks) *n_chunks = plan->n_chunks;
+  if (n_items) *n_items = plan->n_items;
   return ZS_OK;
 }
 

@@ -180,6 +180,19 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], const u32x4 w) {
   acc[7] = acc[7] + h_hi<FMT>(w.w);
 }
 
+// acc = the 8 values of replica 0's group (the first term of the rank-ordered sum).
+template <int FMT>
+__device__ __forceinline__ void widen_first(float (&acc)[8], const u32x4 w) {
+  acc[0] = h_lo<FMT>(w.x);
+  acc[1] = h_hi<FMT>(w.x);
+  acc[2] = h_lo<FMT>(w.y);
+  acc[3] = h_hi<FMT>(w.y);
+  acc[4] = h_lo<FMT>(w.z);
+  acc[5] = h_hi<FMT>(w.z);
+  acc[6] = h_lo<FMT>(w.w);
+  acc[7] = h_hi<FMT>(w.w);
+}
+
 // Lane layouts of an 8-parameter group inside a tile (one group per thread).
 //  Split (full tiles): lane l of wave q owns the quads at tile elements
 //    512q + 4l and 512q + 256 + 4l.  Every access instruction of a wave then
@@ -236,17 +249,7 @@ __device__ __forceinline__ void add_batch(float (&acc)[8], const u32x4 (&w)[kBat
 // which would buy nothing but registers.
 template <int NT, bool SPLIT, int FMT = kBF16, class GP>
 __device__ __forceinline__ void reduce_replicas(GP G, int N, uint32_t e, float (&acc)[8]) {
-  {
-    const u32x4 w = ld_grad<SPLIT>(G, 0, e);
-    acc[0] = h_lo<FMT>(w.x);
-    acc[1] = h_hi<FMT>(w.x);
-    acc[2] = h_lo<FMT>(w.y);
-    acc[3] = h_hi<FMT>(w.y);
-    acc[4] = h_lo<FMT>(w.z);
-    acc[5] = h_hi<FMT>(w.z);
-    acc[6] = h_lo<FMT>(w.w);
-    acc[7] = h_hi<FMT>(w.w);
-  }
+  widen_first<FMT>(acc, ld_grad<SPLIT>(G, 0, e));
   if constexpr (NT > 0) {
     constexpr int NB = (NT - 1 + kBatch - 1) / kBatch;
     u32x4 w[2][kBatch];
@@ -423,17 +426,7 @@ struct HeldMeans {
 template <int NT, int CHK, int FMT = kBF16, class GP, class HOOK>
 __device__ __forceinline__ void reduce_replicas_hooked(GP G, uint32_t e, float (&acc)[8], HOOK&& hook) {
   static_assert(NT > 0 && kBatch % CHK == 0, "templated replica count, CHK divides the batch");
-  {
-    const u32x4 w = ld_grad<true>(G, 0, e);
-    acc[0] = h_lo<FMT>(w.x);
-    acc[1] = h_hi<FMT>(w.x);
-    acc[2] = h_lo<FMT>(w.y);
-    acc[3] = h_hi<FMT>(w.y);
-    acc[4] = h_lo<FMT>(w.z);
-    acc[5] = h_hi<FMT>(w.z);
-    acc[6] = h_lo<FMT>(w.w);
-    acc[7] = h_hi<FMT>(w.w);
-  }
+  widen_first<FMT>(acc, ld_grad<true>(G, 0, e));
   constexpr int NB = (NT - 1 + kBatch - 1) / kBatch;
   if constexpr (NB == 0) {
     hook();
@@ -468,17 +461,7 @@ __device__ __forceinline__ void reduce_replicas_hooked(GP G, uint32_t e, float (
 // with hook() after each batch's loads are issued.
 template <int FMT = kBF16, class GP, class HOOK>
 __device__ __forceinline__ void reduce_replicas_hooked_rt(GP G, int N, uint32_t e, float (&acc)[8], HOOK&& hook) {
-  {
-    const u32x4 w = ld_grad<true>(G, 0, e);
-    acc[0] = h_lo<FMT>(w.x);
-    acc[1] = h_hi<FMT>(w.x);
-    acc[2] = h_lo<FMT>(w.y);
-    acc[3] = h_hi<FMT>(w.y);
-    acc[4] = h_lo<FMT>(w.z);
-    acc[5] = h_hi<FMT>(w.z);
-    acc[6] = h_lo<FMT>(w.w);
-    acc[7] = h_hi<FMT>(w.w);
-  }
+  widen_first<FMT>(acc, ld_grad<true>(G, 0, e));
   u32x4 wa[kBatch], wb[kBatch];
   if (N > 1) load_batch<true>(G, 1, N, e, wa);
   hook();

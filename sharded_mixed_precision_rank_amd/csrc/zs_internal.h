@@ -46,32 +46,29 @@ struct FlatShape {
   int32_t scalar_only;
 };
 
-// One tensor of a list plan (64 bytes, device table).
+// One tensor of a list plan (64 bytes, device table).  Its work items are
+// items [item0, item0 + count) of the plan, one wave tile each: for a vector
+// tensor, item item0 + k takes 8-groups [max(0, gofs + 64k), gofs + 64k + 64)
+// (clipped to nvec), with gofs = lead - 64 when lead > 0 (the groups before the
+// tensor's tile grid anchor, a partial tile of their own) and 0 otherwise, and
+// its first item also the head and tail elements; for a scalar-only tensor,
+// item item0 + k takes elements [512k, 512k + 512), element by element.
 struct ListTensor {
   float* p;
   float* m;
   float* v;
   uint16_t* b;
   int64_t n;
-  int64_t head;
   int64_t nvec;
-  int32_t scalar_only;
+  int32_t item0;
   int32_t group;  // hyperparameter group (list plans with groups; else 0)
-};
-
-// One chunk of a list plan (device table): for a vector tensor, groups
-// [begin, end); for a scalar-only tensor, elements [begin, end).  The chunk
-// with first != 0 also handles its tensor's head and tail elements.
-struct ListChunk {
-  int32_t tensor;
-  int32_t first;
-  int64_t begin;
-  int64_t end;
-  int64_t pad_;
+  // head | lead << 8: the elements before the first 8-group (< 64) and the
+  // 8-groups before the tile grid anchor (< 64), in one word for one scalar load
+  int32_t head_lead;
+  int32_t scalar_only;
 };
 
 static_assert(sizeof(ListTensor) == 64, "ListTensor layout");
-static_assert(sizeof(ListChunk) == 32, "ListChunk layout");
 
 // Common alignment peel: the smallest h such that every pointer advanced by h
 // elements sits on a 128-byte line boundary (h < 64); failing that, a 64-,
@@ -81,6 +78,15 @@ int64_t common_peel(const float* p, const float* m, const float* v, const uint16
 
 // The same peel over (pointer, element size) pairs.
 int64_t common_peel_sized(const void* const* ptrs, const int* elem_bytes, int count);
+
+// Elements in a wave tile, and the anchor of the tile grid: the smallest a in
+// [0, kTileElemsWave) such that every pointer advanced by a elements sits on a
+// boundary of kTileElemsWave of its own elements (2 KiB of fp32, 1 KiB of
+// bf16), or -1 if the arrays reach such boundaries at different elements.
+constexpr int64_t kTileElemsWave = 512;
+int64_t tile_anchor_sized(const void* const* ptrs, const int* elem_bytes, int count);
+int64_t tile_anchor(const float* p, const float* m, const float* v, const uint16_t* b, const uint16_t* const* g,
+                    int32_t N);
 
 // Write windows of the flat step (see flat_window_kernel): stores go out while
 // (device real-time counter & period_mask) < open_ticks.  period_mask == 0:
@@ -118,7 +124,9 @@ hipError_t launch_step_advance(int64_t* step, hipStream_t stream);
 // kMaxGroups); with a device step (ref.table set) n_sets is 1 and the table
 // supplies the folded scalars.
 // win: write windows (list_window_kernel) when period_mask != 0.
-hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
+// items: n_items tensor indices, one per work item (a wave tile), tensor by
+// tensor in order.
+hipError_t launch_list(const int32_t* items, int32_t n_items, const ListTensor* tensors,
                        const uint16_t* const* gptrs, const Scalars* cs, int n_sets, const StepRef& ref, int blocks,
                        const WriteWindow& win, hipStream_t stream);
 
@@ -128,11 +136,9 @@ hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTens
 // buffers against 256-thread workgroups: 1-4% faster for flat shards (70B/64
 // shard +1.2%, 124M-parameter N=8 shard +4.4%); for list plans, one wave per
 // tile with scalar descriptor loads ran 0-1.6% faster than a four-wave
-// workgroup per chunk that staged its descriptor through LDS.
+// workgroup per 4096-parameter chunk that staged its descriptor through LDS.
 constexpr int kFlatBlock = 64;
-// Elements per list chunk (vector tensors: groups of 8 per chunk = this / 8):
-// two list tiles.
-constexpr int64_t kChunkElems = 4096;
+static_assert(kTileElemsWave == 8 * kFlatBlock, "a wave tile: one 8-group per thread");
 // Threads per workgroup of pass 1 of the two-pass form (four waves; its norm
 // partials are reduced across the waves through LDS).  Pass 2 runs one wave
 // per workgroup, as the fused step.

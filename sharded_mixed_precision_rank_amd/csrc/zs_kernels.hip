@@ -21,11 +21,15 @@
 //  * Every access is marked non-temporal: nothing is re-read, so nothing
 //    should displace useful lines in L2 or the Infinity Cache.
 //  * One wave per workgroup, one 512-parameter tile each, for flat shards and
-//    list plans alike (a list plan's 4096-parameter chunks are eight such
-//    tiles).  The measurements behind this are noted at kFlatBlock.
+//    list plans alike (a list plan's table names one tensor per wave tile).
+//    The measurements behind this are noted at kFlatBlock.
 //  * Tiles start where every array sits on a 128-byte line boundary when the
 //    arrays allow it (else 64, 32 or 16 bytes), so each wave access covers
-//    whole lines and no line is written in two halves by two tiles.
+//    whole lines and no line is written in two halves by two tiles; and,
+//    where the arrays allow, on a boundary of 512 of their own elements (a
+//    flat shard whose arrays start elsewhere runs its first elements as a
+//    shard of their own; a list tensor's groups before that point form a
+//    partial tile of their own).
 //  * Elements outside the aligned middle (at most 63 before it, 7 after) and
 //    shards whose arrays share no common alignment go through a per-element
 //    path with the identical operation sequence (same inline function), so
@@ -110,10 +114,88 @@ __device__ __forceinline__ void group_step(GP G, int N, int64_t e0, const FlatSh
   group_step_at<NT, SPLIT>(G, N, e0, Layout<SPLIT>::first(), s, c);
 }
 
+// A partial wave tile: `groups` (1..63) 8-groups from element e0, in the split
+// lane layout of a whole tile (lane t holds the quads at tile elements 4t and
+// 256 + 4t).  A quad past the tile's end is neither loaded nor stored (its
+// lane computes on zeros there).  The loads, the rank-ordered sums and the
+// update are those of group_step, so every element gets the same bits as on
+// a whole tile; and each store instruction writes whole 128-byte lines except
+// at the tile's end.  The contiguous layout, where two store instructions
+// write alternate 16-byte pieces of every line, made each partial tile cost
+// several whole ones: lists whose tensors each ended in a partial tile ran
+// 1.6-2.0% behind a flat call over the same arena.
+template <int NT, class GP>
+__device__ __forceinline__ void partial_step(GP G, int N, int64_t e0, int64_t groups, const FlatShape& s,
+                                             const Scalars& c) {
+  constexpr uint32_t q2 = Layout<true>::kSecond / 4;  // second quad, in f32x4 units
+  const uint32_t t = threadIdx.x & 63u;
+  const uint32_t e = 4u * t;
+  const bool qa = (int64_t)t < 2 * groups, qb = (int64_t)t + 64 < 2 * groups;
+  auto ldq = [&](int r) {
+    const GLB u32x2* a = (const GLB u32x2*)at(G(r), here(e) * 2u);
+    u32x2 x = {0u, 0u}, y = {0u, 0u};
+    if (qa) x = ld_g(a);
+    if (qb) y = ld_g(a + q2);
+    return (u32x4){x.x, x.y, y.x, y.y};
+  };
+  const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 pa = z, pb = z, ma = z, mb = z, va = z, vb = z;
+  {
+    const uint32_t o = here(e) * 4u;
+    const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(s.p + e0), o);
+    const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(s.m + e0), o);
+    const GLB f32x4* V4 = (const GLB f32x4*)at(tile_base(s.v + e0), o);
+    if (qa) {
+      pa = ld_g(P4);
+      ma = ld_g(M4);
+      va = ld_g(V4);
+    }
+    if (qb) {
+      pb = ld_g(P4 + q2);
+      mb = ld_g(M4 + q2);
+      vb = ld_g(V4 + q2);
+    }
+  }
+  float acc[8];
+  widen_first<kBF16>(acc, ldq(0));
+  for (int r = 1; r < N; r += kBatch) {
+    u32x4 w[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (r + j < N) w[j] = ldq(r + j);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (r + j < N) accumulate<kBF16>(acc, w[j]);
+  }
+  float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+  float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+  float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) adam(mean_of<NT>(acc[k], c), p[k], m[k], v[k], c);
+  const TileOut h = tile_outputs(p, m, v);
+  const uint32_t o = here(e) * 4u;
+  GLB f32x4* P4 = (GLB f32x4*)at(tile_base(s.p + e0), o);
+  GLB f32x4* M4 = (GLB f32x4*)at(tile_base(s.m + e0), o);
+  GLB f32x4* V4 = (GLB f32x4*)at(tile_base(s.v + e0), o);
+  GLB u32x2* B2 = (GLB u32x2*)at(tile_base(s.b + e0), here(e) * 2u);
+  if (qa) {
+    st_g(P4, h.p0);
+    st_g(M4, h.m0);
+    st_g(V4, h.v0);
+    st_g(B2, h.b0);
+  }
+  if (qb) {
+    st_g(P4 + q2, h.p1);
+    st_g(M4 + q2, h.m1);
+    st_g(V4 + q2, h.v1);
+    st_g(B2 + q2, h.b1);
+  }
+}
+
 // Groups [g_begin, g_end) of a vector-path shard, one workgroup-wide tile of
 // BLOCK groups at a time starting at tile index `tile0` and stepping by
-// `tstep` tiles.  G0(r) returns replica r's unadvanced base pointer.  Whole
-// tiles use the split layout; the last, partial tile the contiguous one.
+// `tstep` tiles.  G0(r) returns replica r's unadvanced base pointer.  Every
+// tile uses the split layout (the last, partial one through partial_step).
 template <int NT, int BLOCK, class GP0>
 __device__ __forceinline__ void tiles(GP0 G0, int N, int64_t g_begin, int64_t g_end, int64_t tile0, int64_t tstep,
                                       const FlatShape& s, const Scalars& c) {
@@ -124,8 +206,8 @@ __device__ __forceinline__ void tiles(GP0 G0, int N, int64_t g_begin, int64_t g_
     auto G = [&](int r) { return tile_base(G0(r) + e0); };
     if (gt + BLOCK <= g_end)
       group_step<NT, true>(G, N, e0, s, c);
-    else if (gt + threadIdx.x < g_end)
-      group_step<NT, false>(G, N, e0, s, c);
+    else
+      partial_step<NT>(G, N, e0, g_end - gt, s, c);
   }
 }
 
@@ -241,9 +323,9 @@ __global__ __launch_bounds__(kFlatBlock) void flat_window_kernel(const FlatArgs<
   if (blockIdx.x == gridDim.x - 1) {
     const int64_t gt = full * kFlatBlock;
     const int64_t e0 = s.head + 8 * gt;
-    if (gt + threadIdx.x < s.nvec) {
+    if (gt < s.nvec) {
       auto G = [&](int r) { return tile_base(a.g[r] + e0); };
-      group_step<NT, false>(G, N, e0, s, c);
+      partial_step<NT>(G, N, e0, s.nvec - gt, s, c);
     }
     auto G1 = [&](int r) { return a.g[r]; };
     edge_step<kFlatBlock>(G1, N, s, c);
@@ -302,9 +384,9 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void flat_phased_kernel(c
   if (blockIdx.x == gridDim.x - 1 && wave == 0) {
     const int64_t gt = full * kFlatBlock;
     const int64_t e1 = s.head + 8 * gt;
-    if (gt + threadIdx.x < s.nvec) {
+    if (gt < s.nvec) {
       auto G = [&](int r) { return tile_base(a.g[r] + e1); };
-      group_step<NT, false>(G, N, e1, s, c);
+      partial_step<NT>(G, N, e1, s.nvec - gt, s, c);
     }
     auto G1 = [&](int r) { return a.g[r]; };
     edge_step<kFlatBlock>(G1, N, s, c);
@@ -343,74 +425,95 @@ struct ListScalars {
   Scalars c[NG];
 };
 
-// The ragged-list step: one-wave workgroups, one 512-parameter wave tile
-// each, as flat_kernel: work item w is sub-tile w % 8 of chunk w / 8 (a vector
-// chunk holds kChunkElems parameters from a multiple of that within its
-// tensor, so its sub-tiles are whole wave tiles, except a tensor's last,
-// partial one).  The chunk's tensor descriptor and replica pointers come by
-// scalar loads from the plan's table, so no LDS staging and no barrier sit
-// between a workgroup's start and its first gradient load.  Scalar-only
-// tensors take 512 elements per work item, element by element; the chunk that
-// holds a tensor's start also takes its head and tail elements.  Every
-// element goes through the same operations as in flat_kernel.
+// A list plan's work item: one wave tile (or part of one) of one tensor.
+struct ListWork {
+  FlatShape s;                // the tensor (wave-uniform)
+  const uint16_t* const* gp;  // its N replica pointers in the plan's table
+  int64_t lo, hi;             // vector tensor: 8-groups [lo, hi); scalar-only: elements [lo, hi)
+  int32_t grp;                // hyperparameter group
+  bool first;                 // the tensor's first item, which also takes its head and tail elements
+};
+
+// Item i0 + it of the plan, whose tensor index is items[it]: the tensor's
+// descriptor and its share of it (see ListTensor), by scalar loads.
+__device__ __forceinline__ ListWork list_work(const int32_t* __restrict__ items, int64_t it, int64_t i0,
+                                              const ListTensor* __restrict__ tensors,
+                                              const uint16_t* const* __restrict__ gptrs, int N) {
+  constexpr int64_t kGroups = kTileElemsWave / 8;
+  const int32_t t = items[it];
+  const ListTensor& T = tensors[t];
+  ListWork w;
+  w.s.p = uniform_fptr(T.p);
+  w.s.m = uniform_fptr(T.m);
+  w.s.v = uniform_fptr(T.v);
+  w.s.b = uniform_fptr(T.b);
+  w.s.n = uniform_i64(T.n);
+  const int32_t hl = T.head_lead;
+  w.s.head = hl & 0xFF;
+  w.s.nvec = uniform_i64(T.nvec);
+  w.s.scalar_only = T.scalar_only;
+  w.grp = T.group;
+  w.gp = gptrs + (int64_t)t * N;
+  const int64_t k = i0 + it - T.item0;  // the item's place in its tensor
+  w.first = k == 0;
+  if (w.s.scalar_only) {
+    w.lo = k * kTileElemsWave;
+    w.hi = w.lo + kTileElemsWave < w.s.n ? w.lo + kTileElemsWave : w.s.n;
+  } else {
+    const int32_t lead = hl >> 8;
+    const int64_t g = (lead > 0 ? lead - kGroups : 0) + k * kGroups;
+    w.lo = g > 0 ? g : 0;
+    w.hi = g + kGroups < w.s.nvec ? g + kGroups : w.s.nvec;
+  }
+  return w;
+}
+
+// The ragged-list step: one-wave workgroups, one work item each, as
+// flat_kernel takes one tile: the plan's table holds one entry per wave tile
+// of every tensor (its tensor's index), tensor by tensor, so every workgroup
+// has work.  A vector tensor's tiles start at its tile grid's anchor, the
+// groups before it forming a partial tile of their own.  The tensor's
+// descriptor and replica pointers come by scalar loads from the table, so no
+// LDS staging and no barrier sit between a workgroup's start and its first
+// gradient load.  A scalar-only tensor's items take 512 elements each, element
+// by element; a vector tensor's first item also takes its head and tail
+// elements.  Every element goes through the same operations as in flat_kernel.
 template <int NT, int NG>
-__global__ __launch_bounds__(kFlatBlock) void list_kernel(const ListChunk* __restrict__ chunks, int32_t n_chunks,
-                                                           const ListTensor* __restrict__ tensors,
+__global__ __launch_bounds__(kFlatBlock) void list_kernel(const int32_t* __restrict__ items, int32_t n_items,
+                                                           int64_t i0, const ListTensor* __restrict__ tensors,
                                                            const uint16_t* const* __restrict__ gptrs,
                                                            const ListScalars<NG> sc, const StepRef ref) {
-  constexpr int64_t kSub = kChunkElems / 8 / kFlatBlock;  // wave tiles per chunk
-  static_assert(kSub * 8 * kFlatBlock == kChunkElems, "a chunk is a whole number of wave tiles");
   const int N = NT > 0 ? NT : sc.c[0].n_rep;
   Scalars one = sc.c[0];
   if constexpr (NG == 1) {
     if (!step_scalars(ref, one)) return;
   }
-  const int64_t items = (int64_t)n_chunks * kSub;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int32_t ci = (int32_t)(it / kSub);
-    const int64_t j = it - (int64_t)ci * kSub;
-    const ListChunk ch = chunks[ci];
-    const ListTensor& T = tensors[ch.tensor];
-    FlatShape s;
-    s.p = uniform_fptr(T.p);
-    s.m = uniform_fptr(T.m);
-    s.v = uniform_fptr(T.v);
-    s.b = uniform_fptr(T.b);
-    s.n = uniform_i64(T.n);
-    s.head = uniform_i64(T.head);
-    s.nvec = uniform_i64(T.nvec);
-    s.scalar_only = T.scalar_only;
-    int32_t grp = 0;
-    if constexpr (NG > 1) grp = T.group;
-    const Scalars& c = NG == 1 ? one : sc.c[grp];
-    const uint16_t* const* gp = gptrs + (int64_t)ch.tensor * N;
-    auto G0 = [&](int r) { return uniform_ptr(gp[r]); };
+  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const ListWork w = list_work(items, it, i0, tensors, gptrs, N);
+    const FlatShape& s = w.s;
+    const Scalars& c = NG == 1 ? one : sc.c[w.grp];
+    auto G0 = [&](int r) { return uniform_ptr(w.gp[r]); };
     if (s.scalar_only) {
-      const int64_t lo = ch.begin + j * kFlatBlock * 8;
-      const int64_t hi = lo + kFlatBlock * 8 < ch.end ? lo + kFlatBlock * 8 : ch.end;
-      for (int64_t i = lo + threadIdx.x; i < hi; i += kFlatBlock) elem_step(G0, N, i, s, c);
+      for (int64_t i = w.lo + threadIdx.x; i < w.hi; i += kFlatBlock) elem_step(G0, N, i, s, c);
       continue;
     }
-    const int64_t gt = ch.begin + kFlatBlock * j;  // first group of the sub-tile
-    const int64_t e0 = s.head + 8 * gt;
+    const int64_t e0 = s.head + 8 * w.lo;
     auto G = [&](int r) { return tile_base(G0(r) + e0); };
-    if (gt + kFlatBlock <= ch.end)
+    if (w.hi - w.lo == kFlatBlock)
       group_step<NT, true>(G, N, e0, s, c);
-    else if (gt + threadIdx.x < ch.end)
-      group_step<NT, false>(G, N, e0, s, c);
-    if (j == 0 && ch.first) edge_step<kFlatBlock>(G0, N, s, c);
+    else
+      partial_step<NT>(G, N, e0, w.hi - w.lo, s, c);
+    if (w.first) edge_step<kFlatBlock>(G0, N, s, c);
   }
 }
 
 // The list step with its write-back in device-clock windows, as
 // flat_window_kernel does for a flat shard.  Persistent one-wave workgroups
-// take work items: item w is 512-parameter sub-tile w % 8 of chunk w / 8 (a
-// vector chunk holds kChunkElems parameters from a multiple of that within
-// its tensor, so its sub-tiles are whole wave tiles, except a tensor's last,
-// partial one).  The chunk's tensor descriptor and replica pointers come by
-// scalar loads from the plan's table.  A full sub-tile is held (with its
-// tensor's arrays) and stored in a window; a partial sub-tile, a tensor's head
-// and tail elements and scalar-only tensors are stored at once.  Every element
+// take the plan's work items (one wave tile of one tensor each; see
+// list_kernel) in turn; each item's tensor descriptor and replica pointers
+// come by scalar loads from the plan's table.  A full tile is held (with its
+// tensor's arrays) and stored in a window; a partial tile, a tensor's head and
+// tail elements and scalar-only tensors are stored at once.  Every element
 // goes through the same operations as in list_kernel.
 struct HeldListTiles {
   int n = 0;
@@ -458,13 +561,11 @@ struct HeldListTiles {
 };
 
 template <int NT, int NG>
-__global__ __launch_bounds__(kFlatBlock) void list_window_kernel(const ListChunk* __restrict__ chunks,
-                                                             int32_t n_chunks, const ListTensor* __restrict__ tensors,
+__global__ __launch_bounds__(kFlatBlock) void list_window_kernel(const int32_t* __restrict__ items, int32_t n_items,
+                                                             const ListTensor* __restrict__ tensors,
                                                              const uint16_t* const* __restrict__ gptrs,
                                                              const ListScalars<NG> sc, const StepRef ref,
                                                              const WriteWindow w) {
-  constexpr int64_t kSub = kChunkElems / 8 / kFlatBlock;  // wave tiles per chunk
-  static_assert(kSub * 8 * kFlatBlock == kChunkElems, "a chunk is a whole number of wave tiles");
   constexpr uint32_t q2 = Layout<true>::kSecond / 4;
   const int N = NT > 0 ? NT : sc.c[0].n_rep;
   Scalars one = sc.c[0];
@@ -472,36 +573,19 @@ __global__ __launch_bounds__(kFlatBlock) void list_window_kernel(const ListChunk
     if (!step_scalars(ref, one)) return;
   }
   const uint32_t e = Layout<true>::first();
-  const int64_t items = (int64_t)n_chunks * kSub;
   HeldListTiles held;
   auto check = [&]() { held.check(w); };
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int32_t ci = (int32_t)(it / kSub);
-    const int64_t j = it - (int64_t)ci * kSub;
-    const ListChunk ch = chunks[ci];
-    const ListTensor& T = tensors[ch.tensor];
-    FlatShape s;
-    s.p = uniform_fptr(T.p);
-    s.m = uniform_fptr(T.m);
-    s.v = uniform_fptr(T.v);
-    s.b = uniform_fptr(T.b);
-    s.n = uniform_i64(T.n);
-    s.head = uniform_i64(T.head);
-    s.nvec = uniform_i64(T.nvec);
-    s.scalar_only = T.scalar_only;
-    int32_t grp = 0;
-    if constexpr (NG > 1) grp = T.group;
-    const Scalars& c = NG == 1 ? one : sc.c[grp];
-    const uint16_t* const* gp = gptrs + (int64_t)ch.tensor * N;
-    auto G0 = [&](int r) { return uniform_ptr(gp[r]); };
+  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const ListWork wk = list_work(items, it, 0, tensors, gptrs, N);
+    const FlatShape& s = wk.s;
+    const Scalars& c = NG == 1 ? one : sc.c[wk.grp];
+    auto G0 = [&](int r) { return uniform_ptr(wk.gp[r]); };
     if (s.scalar_only) {
-      if (j == 0)
-        for (int64_t i = ch.begin + threadIdx.x; i < ch.end; i += kFlatBlock) elem_step(G0, N, i, s, c);
+      for (int64_t i = wk.lo + threadIdx.x; i < wk.hi; i += kFlatBlock) elem_step(G0, N, i, s, c);
       continue;
     }
-    const int64_t gt = ch.begin + kFlatBlock * j;  // first group of the sub-tile
-    const int64_t e0 = s.head + 8 * gt;
-    if (gt + kFlatBlock <= ch.end) {
+    const int64_t e0 = s.head + 8 * wk.lo;
+    if (wk.hi - wk.lo == kFlatBlock) {
       f32x4 pa, pb, ma, mb, va, vb;
       {
         const uint32_t o = here(e) * 4u;
@@ -527,14 +611,12 @@ __global__ __launch_bounds__(kFlatBlock) void list_window_kernel(const ListChunk
 #pragma unroll
       for (int k = 0; k < 8; ++k) adam(mean_of<NT>(acc[k], c), p[k], m[k], v[k], c);
       held.push(s, e0, tile_outputs(p, m, v));
-    } else if (gt < ch.end) {
-      // a tensor's last, partial wave tile: contiguous layout, stored at once
-      if (gt + threadIdx.x < ch.end) {
-        auto G = [&](int r) { return tile_base(G0(r) + e0); };
-        group_step<NT, false>(G, N, e0, s, c);
-      }
+    } else {
+      // a partial wave tile (a tensor's last, or the groups before its tile grid's anchor), stored at once
+      auto G = [&](int r) { return tile_base(G0(r) + e0); };
+      partial_step<NT>(G, N, e0, wk.hi - wk.lo, s, c);
     }
-    if (j == 0 && ch.first) edge_step<kFlatBlock>(G0, N, s, c);
+    if (wk.first) edge_step<kFlatBlock>(G0, N, s, c);
   }
   held.flush();
 }
@@ -626,26 +708,26 @@ hipError_t go_flat(const uint16_t* const* grads, const FlatShape& s, const Scala
 }
 
 template <int NT, int NG>
-hipError_t go_list_window(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
+hipError_t go_list_window(const int32_t* items, int32_t n_items, const ListTensor* tensors,
                           const uint16_t* const* gptrs, const ListScalars<NG>& sc, const StepRef& ref, int blocks,
                           const WriteWindow& win, hipStream_t stream, bool* launched) {
   static std::atomic<int> cache[kMaxDevices];
   *launched = false;
   int grid = resident_grid(list_window_kernel<NT, NG>, kFlatBlock, cache);
   if (grid <= 0) {
-    (void)hipGetLastError();  // no occupancy figure: take the chunk kernel
+    (void)hipGetLastError();  // no occupancy figure: take the one-tile kernel
     return hipSuccess;
   }
   if (blocks < grid) grid = blocks;
   (void)hipGetLastError();
-  list_window_kernel<NT, NG><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(chunks, n_chunks, tensors, gptrs, sc, ref,
+  list_window_kernel<NT, NG><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(items, n_items, tensors, gptrs, sc, ref,
                                                                            win);
   *launched = true;
   return hipGetLastError();
 }
 
 template <int NT>
-hipError_t go_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
+hipError_t go_list(const int32_t* items, int32_t n_items, const ListTensor* tensors,
                    const uint16_t* const* gptrs, const Scalars* cs, int n_sets, const StepRef& ref, int blocks,
                    const WriteWindow& win, hipStream_t stream) {
   if (win.period_mask != 0) {
@@ -654,32 +736,31 @@ hipError_t go_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* 
     if (n_sets <= 1) {
       ListScalars<1> sc;
       sc.c[0] = cs[0];
-      e = go_list_window<NT, 1>(chunks, n_chunks, tensors, gptrs, sc, ref, blocks, win, stream, &launched);
+      e = go_list_window<NT, 1>(items, n_items, tensors, gptrs, sc, ref, blocks, win, stream, &launched);
     } else {
       ListScalars<kMaxGroups> sc;
       for (int k = 0; k < kMaxGroups; ++k) sc.c[k] = cs[k < n_sets ? k : 0];
-      e = go_list_window<NT, kMaxGroups>(chunks, n_chunks, tensors, gptrs, sc, ref, blocks, win, stream, &launched);
+      e = go_list_window<NT, kMaxGroups>(items, n_items, tensors, gptrs, sc, ref, blocks, win, stream, &launched);
     }
     if (launched || e != hipSuccess) return e;
   }
-  // consecutive launches over the chunk table, each at most launch_bytes()
-  // (a chunk holds at most kChunkElems parameters; every chunk is complete in
-  // itself, its tensor's head and tail included)
-  const int64_t per = units_per_launch(kChunkElems * (2 * (int64_t)cs[0].n_rep + 26), 1);
+  // consecutive launches over the item table, each at most launch_bytes()
+  // (an item is at most one wave tile; every item is complete in itself, its
+  // tensor's head and tail included)
+  const int64_t per = units_per_launch(kTileElemsWave * (2 * (int64_t)cs[0].n_rep + 26), 1);
   ListScalars<1> sc1;
   ListScalars<kMaxGroups> scg;
   sc1.c[0] = cs[0];
   for (int k = 0; k < kMaxGroups; ++k) scg.c[k] = cs[k < n_sets ? k : 0];
-  for (int64_t c0 = 0; c0 < n_chunks; c0 += per) {
-    const int32_t cnt = (int32_t)(n_chunks - c0 > per ? per : n_chunks - c0);
-    const int64_t items = (int64_t)cnt * (kChunkElems / 8 / kFlatBlock);  // wave tiles
-    const int grid = (int)(blocks < items ? blocks : items);
+  for (int64_t i0 = 0; i0 < n_items; i0 += per) {
+    const int32_t cnt = (int32_t)(n_items - i0 > per ? per : n_items - i0);
+    const int grid = blocks < cnt ? blocks : cnt;
     (void)hipGetLastError();
     if (n_sets <= 1)
-      list_kernel<NT, 1><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(chunks + c0, cnt, tensors, gptrs, sc1, ref);
+      list_kernel<NT, 1><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(items + i0, cnt, i0, tensors, gptrs, sc1, ref);
     else
-      list_kernel<NT, kMaxGroups><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(chunks + c0, cnt, tensors, gptrs, scg,
-                                                                               ref);
+      list_kernel<NT, kMaxGroups><<<dim3(grid), dim3(kFlatBlock), 0, stream>>>(items + i0, cnt, i0, tensors, gptrs,
+                                                                               scg, ref);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -709,18 +790,18 @@ hipError_t launch_step_advance(int64_t* step, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_list(const ListChunk* chunks, int32_t n_chunks, const ListTensor* tensors,
+hipError_t launch_list(const int32_t* items, int32_t n_items, const ListTensor* tensors,
                        const uint16_t* const* gptrs, const Scalars* cs, int n_sets, const StepRef& ref, int blocks,
                        const WriteWindow& win, hipStream_t stream) {
   switch (cs[0].n_rep) {
-    case 1: return go_list<1>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    case 2: return go_list<2>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    case 4: return go_list<4>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    case 8: return go_list<8>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    case 16: return go_list<16>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    case 32: return go_list<32>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    case 64: return go_list<64>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    default: return go_list<0>(chunks, n_chunks, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 1: return go_list<1>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 2: return go_list<2>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 4: return go_list<4>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 8: return go_list<8>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 16: return go_list<16>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 32: return go_list<32>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 64: return go_list<64>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    default: return go_list<0>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
   }
 }
 

@@ -506,7 +506,7 @@ def test_flat_schedule_query_and_setting():
 
 def test_static_list_step_refuses_a_table_beyond_its_array_without_gpu():
     """zs_reduce_adam_list_static checks the table's size against its fixed array before any GPU work:
-    one tensor of 5e9 parameters needs about 1.22M chunks, 39 MB of table, beyond 32 MiB."""
+    one tensor of 5e9 parameters needs about 9.8M work items of 4 bytes, 39 MB of table, beyond 32 MiB."""
     lib = zs.library()
     n = 5_000_000_000
     span = 1 << 40

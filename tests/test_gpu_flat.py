@@ -118,6 +118,31 @@ def test_common_misalignment_peels_a_head(env, orc, shift, n):
     assert np.array_equal(got["P"][:shift], host["P"][:shift]) and np.all(got["B"][:shift] == 0)
 
 
+@pytest.mark.parametrize("shift", [64, 128, 200, 256, 448, 504, 511])
+def test_tile_anchor_splits_the_shard(env, orc, shift):
+    """Every array starts `shift` elements past a boundary of 512 of its own
+    elements: the elements up to the next such boundary run as a shard of
+    their own, the rest as a shard whose tiles start on those boundaries.
+    The split changes no result."""
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    rng = np.random.default_rng(3500 + shift)
+    N, n = 8, 512 * 12 + 37
+    host = rand_host(rng, N, n + shift)
+    d = upload(torch, dev, host)
+    B = torch.zeros(n + shift, dtype=torch.int16, device=dev)
+    zs.reduce_adam_flat([g[shift:] for g in d["G"]], d["P"][shift:], d["M"][shift:], d["V"][shift:], B[shift:],
+                        HP, 9)
+    torch.cuda.synchronize()
+    rP, rM, rV, rB = orc.step([g[shift:] for g in host["G"]], host["P"][shift:], host["M"][shift:],
+                              host["V"][shift:], HP, 9)
+    got = download(dict(d, B=B))
+    ref = dict(P=rP, M=rM, V=rV, B=rB)
+    got_s = {k: v[shift:] for k, v in got.items()}
+    parity.assert_step(got_s, ref, f"anchor shift={shift}")
+    assert parity.bit_identical(got_s, ref)
+    assert np.array_equal(got["P"][:shift], host["P"][:shift]) and np.all(got["B"][:shift] == 0)
+
+
 def test_mixed_alignment_takes_the_element_path(env, orc):
     """Arrays whose 16-byte phases differ cannot share a head peel: every
     element goes through the per-element path, with the same results."""

@@ -1,4 +1,4 @@
-"""GPU parity of the ragged-list step (chunk-table plan) against the oracle."""
+"""GPU parity of the ragged-list step (work-table plan) against the oracle."""
 import numpy as np
 import pytest
 
@@ -182,3 +182,32 @@ def test_list_plan_hyperparameter_groups(env, orc, N, n_groups):
                 B=d["B"].cpu().numpy().view(np.uint16))
     ref2 = oracle_list(orc, w, dict(G=host["G"], P=ref["P"], M=ref["M"], V=ref["V"]), offsets, 5, HP)
     assert parity.bit_identical(got2, ref2)
+
+
+@pytest.mark.parametrize("N", [8, 64])
+def test_tensors_at_every_tile_phase(env, orc, N):
+    """Tensors that start at different phases of the 512-element tile grid: each
+    tensor's groups before its next 512-element boundary form a partial tile of
+    their own (the whole tensor when it ends before that boundary), and every
+    later tile starts on the boundary.  Phase 3 also needs a 61-element head peel."""
+    from synth import workloads as W
+
+    torch, zs, dev = env["torch"], env["zs"], env["dev"]
+    cases = [(8, 100), (8, 504), (8, 505), (64, 448 + 512 * 9 + 3), (448, 64 + 512 * 20 + 100), (0, 5000),
+             (3, 3000), (504, 8), (256, 512 * 9)]
+    offsets = np.array([16384 * k + ph for k, (ph, _) in enumerate(cases)], dtype=np.int64)
+    sizes = tuple(n for _, n in cases)
+    L = int(offsets[-1] + sizes[-1] + 64)
+    w = W.Workload(f"phases-N{N}", N=N, step=11, weight_decay=0.1, warm=True, sizes=sizes, seed=77 + N)
+    host = W.host_inputs(w, 0, L)
+    d = dict(G=[torch.from_numpy(g.view(np.int16)).to(dev) for g in host["G"]],
+             P=torch.from_numpy(host["P"]).to(dev), M=torch.from_numpy(host["M"]).to(dev),
+             V=torch.from_numpy(host["V"]).to(dev), B=torch.full((L,), 0x7FBF, dtype=torch.int16, device=dev))
+    with zs.ListPlan.from_arenas(sizes, offsets, d["G"], d["P"], d["M"], d["V"], d["B"]) as plan:
+        plan.step(w.hp(), w.step)
+        torch.cuda.synchronize()
+    got = dict(P=d["P"].cpu().numpy(), M=d["M"].cpu().numpy(), V=d["V"].cpu().numpy(),
+               B=d["B"].cpu().numpy().view(np.uint16))
+    ref = oracle_list(orc, w, host, offsets, w.step, w.hp())
+    parity.assert_step(got, ref, f"tile phases N={N}")
+    assert parity.bit_identical(got, ref)

@@ -104,10 +104,10 @@ def test_list_plan_in_consecutive_launches(env, orc, N):
     torch, zs = env["torch"], env["zs"]
     w = small_ragged(N, 60, seed=N + 40)
     host, d, offsets, L = arena_case(env, w)
-    zs.set_launch_bytes(3 * 4096 * (2 * N + 26))  # three chunks per launch
+    zs.set_launch_bytes(3 * 512 * (2 * N + 26))  # three work items per launch
     try:
         with zs.ListPlan.from_arenas(w.sizes, offsets, d["G"], d["P"], d["M"], d["V"], d["B"]) as plan:
-            assert plan.info()["n_chunks"] > 30
+            assert plan.info()["n_items"] > 240
             plan.step(w.hp(), w.step)
             torch.cuda.synchronize()
             got = dict(P=d["P"].cpu().numpy(), M=d["M"].cpu().numpy(), V=d["V"].cpu().numpy(),

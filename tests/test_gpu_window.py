@@ -197,7 +197,7 @@ def test_windowed_kernels_in_a_graph(env, orc):
 
 
 # a ragged list of about 2^25 parameters: empty, 1- and 9-element (scalar-only) tensors, tensors that end in
-# partial wave tiles, and tensors of several chunks
+# partial wave tiles, and tensors of many wave tiles
 LIST_SIZES = (1, 9, 0, 5_000, 4_097, 70_001, (1 << 20) + 3, 3_000_001, 10_000_003, 20_000_017)
 
 
