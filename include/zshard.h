@@ -460,8 +460,9 @@ ZS_API zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks);
                                      (zs_set_flat_schedule), on shards of at
                                      least 2^25 parameters;
      kernel = ZS_WINDOW_REDUCE_PASS: pass 1 of the two-pass form
-                                     (zs_reduce_grads_flat), on shards of at
-                                     least 2^25 parameters;
+                                     (zs_reduce_grads_flat): only on the
+                                     windowed schedule (zs_reduce_schedule),
+                                     on shards of at least 2^25 parameters;
      kernel = ZS_WINDOW_LIST_PLAN:   a list plan of n parameters in all (the
                                      flat step's default windows for N, from
                                      2^25 parameters on).
@@ -473,9 +474,13 @@ ZS_API zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks);
 ZS_API zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* period_ticks, int32_t* open_ticks);
 
 /* The schedule of the flat step (zs_reduce_adam_flat and its device-step
-   form), for all later calls in this process.  Every schedule computes every
-   parameter by the same operations in the same order, so results do not
-   depend on it; only when the bytes move does.
+   form) and of pass 1 of the two-pass form (zs_reduce_grads_flat and its
+   device-scale form), for all later calls in this process.  Every schedule
+   computes every parameter by the same operations in the same order, and
+   pass 1's norm partials in the same order, so results do not depend on it;
+   only when the bytes move does.  For pass 1 the phased schedule writes the
+   mean gradient and the norm partials after the grid barrier, and its
+   windowed default is 4096 / 256 ticks.
      ZS_SCHEDULE_AUTO:     the default.  An explicit zs_set_write_window
                            decides when one was made (no windows:
                            ZS_SCHEDULE_STREAM; a window: ZS_SCHEDULE_WINDOWED);
@@ -520,6 +525,11 @@ ZS_API zs_status zs_set_flat_schedule(int32_t schedule);
    (ZS_SCHEDULE_STREAM, _WINDOWED or _PHASED).  No GPU call.
    Errors: ZS_ERR_NULL, ZS_ERR_RANGE. */
 ZS_API zs_status zs_flat_schedule(int32_t N, int64_t n, int32_t* schedule);
+
+/* The same for pass 1 of the two-pass form (zs_reduce_grads_flat) on a shard
+   of n parameters whose replicas and fp32 workspace share a 128-byte line
+   phase.  No GPU call.  Errors: ZS_ERR_NULL, ZS_ERR_RANGE. */
+ZS_API zs_status zs_reduce_schedule(int32_t N, int64_t n, int32_t* schedule);
 
 /* The longest a workgroup of the phased schedule waits at a grid barrier, in
    polls of about 50 ns (0: the default, 2^16, about 3 ms).  Past it the

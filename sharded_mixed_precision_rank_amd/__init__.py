@@ -104,6 +104,8 @@ _lib.zs_set_flat_schedule.restype = ctypes.c_int
 _lib.zs_set_flat_schedule.argtypes = [_i32]
 _lib.zs_flat_schedule.restype = ctypes.c_int
 _lib.zs_flat_schedule.argtypes = [_i32, _i64, ctypes.POINTER(_i32)]
+_lib.zs_reduce_schedule.restype = ctypes.c_int
+_lib.zs_reduce_schedule.argtypes = [_i32, _i64, ctypes.POINTER(_i32)]
 _lib.zs_set_phased_max_polls.restype = ctypes.c_int
 _lib.zs_set_phased_max_polls.argtypes = [_i32]
 SCHEDULES = {"auto": 0, "stream": 1, "windowed": 2, "phased": 3}
@@ -233,6 +235,14 @@ def flat_schedule(N: int, n: int) -> str:
     """The schedule ("stream", "windowed" or "phased") a flat step for N replicas on n parameters takes."""
     out = _i32()
     _check(_lib.zs_flat_schedule(N, n, ctypes.byref(out)), "zs_flat_schedule")
+    return {v: k for k, v in SCHEDULES.items()}[out.value]
+
+
+def reduce_schedule(N: int, n: int) -> str:
+    """The schedule ("stream", "windowed" or "phased") pass 1 of the two-pass form takes for N replicas
+    on n parameters."""
+    out = _i32()
+    _check(_lib.zs_reduce_schedule(N, n, ctypes.byref(out)), "zs_reduce_schedule")
     return {v: k for k, v in SCHEDULES.items()}[out.value]
 
 

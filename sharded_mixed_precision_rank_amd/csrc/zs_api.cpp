@@ -237,15 +237,34 @@ zs::PhasedCtl phased_ctl() {
                        polls > 0 ? polls : zs::kPhasedMaxPolls};
 }
 
-// The same for pass 1 of the two-pass form (which writes 4 bytes per
-// parameter beside 2N read).  Default for N >= 48: 4096 / 256.
-zs::WriteWindow reduce_write_window(int32_t N) {
+// Pass 1 of the two-pass form (2N bytes read and 4 written per parameter)
+// follows the same setting: an explicit schedule, else an explicit window
+// (1: none, > 1: windowed), else phased for N >= kPhasedMinReplicas on shards
+// of at least kPhasedMinParams, else one tile per workgroup.  Its windowed
+// default is 4096 / 256.
+zs::FlatSchedule reduce_schedule(int32_t N, int64_t n, zs::WriteWindow* win) {
+  const int32_t forced = g_flat_schedule.load(std::memory_order_relaxed);
   const uint64_t word = g_window.load(std::memory_order_relaxed);
   const int32_t period = (int32_t)(word >> 32), open = (int32_t)(word & 0xFFFFFFFFu);
-  if (period == 1) return zs::WriteWindow{0, 0};
-  if (period > 1) return zs::WriteWindow{(uint64_t)period - 1, (uint64_t)open};
-  if (N < 48) return zs::WriteWindow{0, 0};
-  return zs::WriteWindow{4096 - 1, 256};
+  zs::FlatSchedule sched;
+  if (forced != 0)
+    sched = (zs::FlatSchedule)forced;
+  else if (period == 1)
+    sched = zs::FlatSchedule::kStream;
+  else if (period > 1)
+    sched = zs::FlatSchedule::kWindowed;
+  else
+    sched = N >= zs::kPhasedMinReplicas && n >= zs::kPhasedMinParams ? zs::FlatSchedule::kPhased
+                                                                      : zs::FlatSchedule::kStream;
+  zs::WriteWindow w{0, 0};
+  if (sched == zs::FlatSchedule::kWindowed) {
+    if (period > 1)
+      w = zs::WriteWindow{(uint64_t)period - 1, (uint64_t)open};
+    else if (period == 0)
+      w = zs::WriteWindow{4096 - 1, 256};
+  }
+  if (win) *win = w;
+  return sched;
 }
 
 zs_status after_launch(hipError_t e, hipStream_t stream, const char* what) {
@@ -665,7 +684,7 @@ zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* period_
   else if (kernel == ZS_WINDOW_LIST_PLAN)
     w = write_window(N);
   else
-    w = reduce_write_window(N);
+    (void)reduce_schedule(N, n, &w);
   const bool big = flat ? n / 8 / zs::kFlatBlock >= zs::kWindowMinTiles
                         : n / kTileElems >= zs::kReduceWindowMinTiles;
   const bool used = w.period_mask != 0 && big;
@@ -679,6 +698,21 @@ zs_status zs_set_flat_schedule(int32_t schedule) {
   if (schedule < 0 || schedule > ZS_SCHEDULE_PHASED)
     return fail(ZS_ERR_RANGE, "schedule must be ZS_SCHEDULE_AUTO, _STREAM, _WINDOWED or _PHASED (got %d)", schedule);
   g_flat_schedule.store(schedule, std::memory_order_relaxed);
+  return ZS_OK;
+}
+
+zs_status zs_reduce_schedule(int32_t N, int64_t n, int32_t* schedule) {
+  g_last_error.clear();
+  if (!schedule) return fail(ZS_ERR_NULL, "schedule is NULL");
+  if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
+  if (n < 0) return fail(ZS_ERR_RANGE, "n must be >= 0");
+  zs::WriteWindow w{};
+  zs::FlatSchedule sched = reduce_schedule(N, n, &w);
+  // the kernels' own size conditions (a shard on a common 128-byte line phase)
+  if (sched == zs::FlatSchedule::kWindowed && (w.period_mask == 0 || n / kTileElems < zs::kReduceWindowMinTiles))
+    sched = zs::FlatSchedule::kStream;
+  if (sched == zs::FlatSchedule::kPhased && n / (8 * zs::kFlatBlock) < 1) sched = zs::FlatSchedule::kStream;
+  *schedule = (int32_t)sched;
   return ZS_OK;
 }
 
@@ -1065,7 +1099,11 @@ zs_status reduce_grads(const uint16_t* const* grad_chunks, int32_t N, int64_t n,
       reduce_shape(grad_chunks, N, n, workspace, sqnorm, (float)(1.0 / host_scale), &sh);
     }
     sh.scale_dev = scale_state ? &scale_state->scale : nullptr;
-    sh.window = reduce_write_window(N);
+    zs::WriteWindow w{};
+    const zs::FlatSchedule sched = reduce_schedule(N, n, &w);
+    sh.window = w;
+    sh.phased = sched == zs::FlatSchedule::kPhased ? 1 : 0;
+    sh.ctl = phased_ctl();
     return after_launch(zs::launch_reduce(grad_chunks, sh, grad_format, auto_blocks(), hs), hs, what);
   } catch (const std::bad_alloc&) {
     return fail(ZS_ERR_NOMEM, "host allocation failed");

@@ -38,6 +38,69 @@ __device__ __forceinline__ uint32_t phased_quorum(uint32_t grid) {
   return (grid * kPhasedQuorumPct + 99u) / 100u;
 }
 
+// Phase A of a super-chunk: replicas 0..N-1 (rank order) of a wave's K tiles
+// (tile k from element es[k], wave-uniform; the split lane layout, lane
+// offset e) into fp32 register accumulators, two replicas in flight, the
+// workgroup's waves meeting at a workgroup barrier every two replicas so that
+// they read the same replicas at about the same time.  gp(r) is replica r's
+// gradient pointer (bf16 or fp16 bits per FMT).
+template <int NT, int FMT, int K, class GP>
+__device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&es)[K], uint32_t e,
+                                                  float (&acc)[K][8]) {
+  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  u32x2 w0[K][2], w1[K][2];
+  auto load = [&](int r, u32x2(&w)[K][2]) {
+    const uint16_t* g = gp(r);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const GLB u32x2* q = (const GLB u32x2*)at(tile_base(g + es[k]), here(e) * 2u);
+      w[k][0] = ld_g(q);
+      w[k][1] = ld_g(q + q2);  // the second quad: 256 elements on (64 u32x2)
+    }
+  };
+  auto add = [&](const u32x2(&w)[K][2], bool first) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const float x[8] = {h_lo<FMT>(w[k][0].x), h_hi<FMT>(w[k][0].x), h_lo<FMT>(w[k][0].y), h_hi<FMT>(w[k][0].y),
+                          h_lo<FMT>(w[k][1].x), h_hi<FMT>(w[k][1].x), h_lo<FMT>(w[k][1].y), h_hi<FMT>(w[k][1].y)};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[k][j] = first ? x[j] : acc[k][j] + x[j];
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(acc[k][j]));
+  };
+  load(0, w0);
+  if constexpr (NT > 0) {
+#pragma unroll
+    for (int r = 0; r < NT; r += 2) {
+      if (r + 1 < NT) load(r + 1, w1);
+      __builtin_amdgcn_sched_barrier(0);
+      add(w0, r == 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (r + 2 < NT) load(r + 2, w0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (r + 1 < NT) add(w1, false);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();  // keep the workgroup's waves on the same replicas
+    }
+  } else {
+#pragma unroll 1
+    for (int r = 0; r < N; r += 2) {
+      if (r + 1 < N) load(r + 1, w1);
+      __builtin_amdgcn_sched_barrier(0);
+      add(w0, r == 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (r + 2 < N) load(r + 2, w0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (r + 1 < N) add(w1, false);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    }
+  }
+}
+
 // The whole super-chunks of a flat shard (tiles of 512 parameters from element
 // s.head; s.nvec 8-element groups on the vector path): phase A, the grid
 // barrier, phase B, for each.  gp(r) is replica r's gradient pointer (the
@@ -65,59 +128,7 @@ __device__ __forceinline__ int64_t phased_super_chunks(GP gp, int N, const FlatS
     for (int k = 0; k < K; ++k) es[k] = s.head + 8 * kFlatBlock * (sc * per + k * nw + gw);
     // ---- phase A: the replicas, in rank order, into the accumulators
     float acc[K][8];
-    {
-      u32x2 w0[K][2], w1[K][2];
-      auto load = [&](int r, u32x2(&w)[K][2]) {
-        const uint16_t* g = gp(r);
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const GLB u32x2* q = (const GLB u32x2*)at(tile_base(g + es[k]), here(e) * 2u);
-          w[k][0] = ld_g(q);
-          w[k][1] = ld_g(q + q2);  // the second quad: 256 elements on (64 u32x2)
-        }
-      };
-      auto add = [&](const u32x2(&w)[K][2], bool first) {
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const float x[8] = {bf_lo(w[k][0].x), bf_hi(w[k][0].x), bf_lo(w[k][0].y), bf_hi(w[k][0].y),
-                              bf_lo(w[k][1].x), bf_hi(w[k][1].x), bf_lo(w[k][1].y), bf_hi(w[k][1].y)};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[k][j] = first ? x[j] : acc[k][j] + x[j];
-        }
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(acc[k][j]));
-      };
-      load(0, w0);
-      if constexpr (NT > 0) {
-#pragma unroll
-        for (int r = 0; r < NT; r += 2) {
-          if (r + 1 < NT) load(r + 1, w1);
-          __builtin_amdgcn_sched_barrier(0);
-          add(w0, r == 0);
-          __builtin_amdgcn_sched_barrier(0);
-          if (r + 2 < NT) load(r + 2, w0);
-          __builtin_amdgcn_sched_barrier(0);
-          if (r + 1 < NT) add(w1, false);
-          __builtin_amdgcn_sched_barrier(0);
-          __syncthreads();  // keep the workgroup's waves on the same replicas
-        }
-      } else {
-#pragma unroll 1
-        for (int r = 0; r < N; r += 2) {
-          if (r + 1 < N) load(r + 1, w1);
-          __builtin_amdgcn_sched_barrier(0);
-          add(w0, r == 0);
-          __builtin_amdgcn_sched_barrier(0);
-          if (r + 2 < N) load(r + 2, w0);
-          __builtin_amdgcn_sched_barrier(0);
-          if (r + 1 < N) add(w1, false);
-          __builtin_amdgcn_sched_barrier(0);
-          __syncthreads();
-        }
-      }
-    }
+    phased_accumulate<NT, kBF16, K>(gp, N, es, e, acc);
     // ---- phase B: state, AdamW, outputs, tile by tile (the next tile's state in flight).  The first
     // tile's state is requested before the barrier: reads, like the stragglers' replica reads.
     f32x4 st[2][6];

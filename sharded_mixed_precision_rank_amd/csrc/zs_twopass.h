@@ -23,6 +23,8 @@ struct TwoPassShape {
   float inv_scale;
   const double* scale_dev;  // if set, the loss scale is read here on the device and inv_scale is unused
   WriteWindow window;       // write windows of pass 1 (period_mask == 0: none)
+  int32_t phased;           // pass 1 on the phased schedule (reduce_phased_kernel) where the shard allows
+  PhasedCtl ctl;            // its barrier slot and wait bound
 };
 
 // Per-tile norm partials summed by one first-stage workgroup.

@@ -21,6 +21,7 @@
 #include <atomic>
 
 #include "zs_device.h"
+#include "zs_phased.h"
 #include "zs_twopass.h"
 
 namespace zs {
@@ -190,6 +191,71 @@ __global__ __launch_bounds__(kBlock) void reduce_window_kernel(const ReduceArgs<
   if (blockIdx.x == 0) head_partial<NT, FMT>(a, G0, N, inv, lds4);
 }
 
+// Pass 1 on the phased schedule of the flat step (flat_phased_kernel): one
+// workgroup of kPhasedWaves waves per compute unit; for each of `nsup` whole
+// super-chunks of wave tiles (512 parameters from `head`, kPhasedTiles per
+// wave, slot k of wave w at tile sc*per + k*waves + w), phase A streams the
+// replicas in rank order into register accumulators (phased_accumulate, the
+// flat step's own code), the grid barrier follows, and phase B writes the
+// means and the norm partials.  A 2048-parameter norm tile is four
+// consecutive wave tiles, held by four consecutive waves of one workgroup in
+// the same slot: each wave forms its sum of squares as reduce_kernel's wave
+// does for that quarter (per thread in element order, then the same
+// butterfly), and the four are added in reduce_kernel's order, so the
+// partials, and the norm, are the same bits.  reduce_kernel takes the norm
+// tiles after the super-chunks and the head elements.
+template <int NT, int FMT>
+__global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void reduce_phased_kernel(const ReduceArgs<NT> a,
+                                                                                 const PhasedCtl ctl, int64_t nsup) {
+  constexpr int K = kPhasedTiles;
+  constexpr int kQuarters = kTile / (8 * kFlatBlock);  // wave tiles per norm tile
+  static_assert(kQuarters == 4 && kPhasedWaves % kQuarters == 0, "norm tiles of whole waves of one workgroup");
+  constexpr int kNormTiles = kPhasedWaves / kQuarters;  // per slot per workgroup
+  __shared__ double wsum[K][kPhasedWaves];
+  const int N = NT > 0 ? NT : a.n_rep;
+  Scalars c{};
+  c.n_rep = N;
+  const float inv = unscale_factor(a);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t e = 4u * (threadIdx.x & 63u);
+  const int64_t nw = (int64_t)gridDim.x * kPhasedWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kPhasedWaves + wave;
+  const int64_t per = nw * K;
+  uint32_t* counter = &g_phased_counters[32 * ctl.slot];
+  auto gp = [&](int r) { return a.g[r]; };
+  for (int64_t sc = 0; sc < nsup; ++sc) {
+    int64_t es[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) es[k] = a.head + 8 * kFlatBlock * (sc * per + k * nw + gw);
+    float acc[K][8];
+    phased_accumulate<NT, FMT, K>(gp, N, es, e, acc);
+    phased_grid_barrier(counter, (uint32_t)sc * gridDim.x + phased_quorum(gridDim.x), ctl.max_polls);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      float g[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) g[j] = mean_of<NT>(acc[k][j], c) * inv;
+      GLB f32x4* O = (GLB f32x4*)at(tile_base(a.gbar + es[k]), here(e) * 4u);
+      st_g(O, (f32x4){g[0], g[1], g[2], g[3]});
+      st_g(O + Layout<true>::kSecond / 4, (f32x4){g[4], g[5], g[6], g[7]});
+      double sq = 0.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sq += (double)g[j] * (double)g[j];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, 64);
+      if ((threadIdx.x & 63) == 0) wsum[k][wave] = sq;
+    }
+    __syncthreads();
+    if (threadIdx.x < K * kNormTiles) {
+      const int k = threadIdx.x / kNormTiles, i = threadIdx.x % kNormTiles;
+      const double* q = &wsum[k][kQuarters * i];
+      const int64_t w0 = sc * per + k * nw + (int64_t)blockIdx.x * kPhasedWaves + kQuarters * i;
+      a.partials[w0 / kQuarters] = (q[0] + q[1]) + (q[2] + q[3]);
+    }
+    __syncthreads();
+  }
+}
+
 // First stage of the norm: workgroup b takes partials [b*kFinalSeg,
 // (b+1)*kFinalSeg); thread t sums its 16 of them (t, t+256, ...) in order,
 // then the fixed-order block sum.  The loads are issued together, so the
@@ -334,8 +400,51 @@ hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int b
   a.t_hi = sh.ntiles;
   a.head_here = 1;
   bool windowed = false;
+  int64_t t_first = 0;  // the first norm tile left to the one-tile kernel
+  // phased: the whole super-chunks of wave tiles, when the grid fits the device (templated for 64
+  // replicas; other counts take the run-time instance)
+  if (sh.phased && !sh.scalar_only) {
+    static std::atomic<int> cache[kMaxDevices];
+    const bool t64 = NT == 64;
+    int grid = t64 ? resident_grid(reduce_phased_kernel<64, FMT>, kFlatBlock * kPhasedWaves, cache)
+                   : resident_grid(reduce_phased_kernel<0, FMT>, kFlatBlock * kPhasedWaves, cache);
+    if (grid > 0) {
+      if (blocks < grid) grid = blocks;
+      const int64_t per = (int64_t)grid * kPhasedWaves * kPhasedTiles;  // wave tiles per super-chunk
+      const int64_t nsup = (sh.n - sh.head) / (8 * kFlatBlock) / per;
+      if (nsup > 0) {
+        (void)hipGetLastError();
+        phased_clear_kernel<<<dim3(1), dim3(64), 0, stream>>>(sh.ctl.slot);
+        if constexpr (NT == 64) {
+          reduce_phased_kernel<64, FMT><<<dim3(grid), dim3(kFlatBlock * kPhasedWaves), 0, stream>>>(a, sh.ctl, nsup);
+        } else {
+          ReduceArgs<0> b;
+          for (int r = 0; r < sh.n_rep; ++r) b.g[r] = grads[r];
+          b.gbar = a.gbar;
+          b.partials = a.partials;
+          b.n = a.n;
+          b.head = a.head;
+          b.ntiles = a.ntiles;
+          b.scalar_only = a.scalar_only;
+          b.n_rep = a.n_rep;
+          b.inv_scale = a.inv_scale;
+          b.scale_dev = a.scale_dev;
+          b.t_lo = a.t_lo;
+          b.t_hi = a.t_hi;
+          b.head_here = a.head_here;
+          reduce_phased_kernel<0, FMT><<<dim3(grid), dim3(kFlatBlock * kPhasedWaves), 0, stream>>>(b, sh.ctl, nsup);
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        t_first = nsup * per / 4;  // four wave tiles per norm tile
+      }
+    } else {
+      (void)hipGetLastError();  // no occupancy figure: the one-tile kernel takes the shard
+    }
+  }
   // windowed: shards of many whole tiles, when a window is set
-  if (sh.window.period_mask != 0 && !sh.scalar_only && (sh.n - sh.head) / kTile >= kReduceWindowMinTiles) {
+  if (!sh.phased && sh.window.period_mask != 0 && !sh.scalar_only &&
+      (sh.n - sh.head) / kTile >= kReduceWindowMinTiles) {
     static std::atomic<int> cache[kMaxDevices];
     int grid = resident_grid(reduce_window_kernel<NT, FMT>, kBlock, cache);
     if (grid > 0) {
@@ -351,12 +460,12 @@ hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int b
     // consecutive launches of at most launch_bytes() each (2N + 4 bytes per
     // parameter); the first also takes the head elements
     const int64_t per = units_per_launch((2 * (int64_t)sh.n_rep + 4) * kTile, 1);
-    int64_t lo = 0;
+    int64_t lo = t_first;
     do {
       const int64_t hi = sh.ntiles - lo > per ? lo + per : sh.ntiles;
       a.t_lo = lo;
       a.t_hi = hi;
-      a.head_here = lo == 0;
+      a.head_here = lo == t_first;
       int grid = (int)(hi - lo < blocks ? hi - lo : blocks);
       if (grid < 1) grid = 1;
       (void)hipGetLastError();

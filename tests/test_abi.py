@@ -306,26 +306,25 @@ def test_probe_library_rejects_unsupported_arguments_without_gpu():
 
 
 def test_write_window_query():
-    """The query reports the window each kernel takes.  Pass 1: the N = 64 default on shards of at least
-    2^25 parameters, none below that, for other replica counts, or when windows are switched off.  The
-    flat step takes windows only on the windowed schedule (explicit, or an explicit window setting under
-    the automatic one): its automatic default is the phased schedule."""
+    """The query reports the window each kernel takes.  The flat step and pass 1 take windows only on
+    the windowed schedule (explicit, or an explicit window setting under the automatic one): their
+    automatic default is the phased schedule, and the windowed one's default window is 4096 / 512
+    (flat, N = 64) and 4096 / 256 (pass 1), on shards of at least 2^25 parameters."""
     assert zs.write_window("flat", 64, 1_093_750_000) == (0, 0)
-    assert zs.write_window("reduce", 64, 1_093_750_000) == (4096, 256)
+    assert zs.write_window("reduce", 64, 1_093_750_000) == (0, 0)
     assert zs.write_window("list", 64, 1_093_750_000) == (4096, 512)   # list plans keep the windows
     assert zs.write_window("list", 64, (1 << 25) - 1) == (0, 0)
     assert zs.write_window("list", 8, 1 << 30) == (0, 0)
     try:
-        for kernel, default, setup in (("reduce", (4096, 256), lambda: None),
-                                       ("flat", (4096, 512), lambda: zs.set_flat_schedule("windowed"))):
-            setup()
+        zs.set_flat_schedule("windowed")
+        for kernel, default in (("reduce", (4096, 256)), ("flat", (4096, 512))):
             assert zs.write_window(kernel, 64, 1_093_750_000) == default
             assert zs.write_window(kernel, 64, 1 << 25) == default
             assert zs.write_window(kernel, 64, (1 << 25) - 1) == (0, 0)
             assert zs.write_window(kernel, 100, 1 << 30) == default     # runtime replica counts too
             if kernel == "reduce":
-                assert zs.write_window(kernel, 8, 124_000_000) == (0, 0)   # below 48 replicas: none by default
-                assert zs.write_window(kernel, 47, 1 << 30) == (0, 0)
+                assert zs.write_window(kernel, 8, 124_000_000) == default   # windowed on request, any N
+                assert zs.write_window(kernel, 47, 1 << 30) == default
             zs.set_write_window(1)
             assert zs.write_window(kernel, 64, 1 << 30) == (0, 0)
             zs.set_write_window(1024, 128)
@@ -464,6 +463,35 @@ def test_tuning_knobs_check_their_ranges():
     assert zs.launch_bytes() == 3_000_000_000
     with pytest.raises(zs.ZShardError):
         zs.set_launch_bytes(-5)
+
+
+def test_reduce_schedule_query():
+    """Pass 1 of the two-pass form follows the same setting: phased for N >= 32 on shards of at least
+    2^25 parameters, one tile per workgroup otherwise; windowed only on request."""
+    assert zs.reduce_schedule(64, 1_093_750_000) == "phased"
+    assert zs.reduce_schedule(32, 1 << 25) == "phased"
+    assert zs.reduce_schedule(31, 1 << 30) == "stream"
+    assert zs.reduce_schedule(8, 124_000_000) == "stream"
+    assert zs.reduce_schedule(64, (1 << 25) - 1) == "stream"
+    try:
+        zs.set_write_window(1)
+        assert zs.reduce_schedule(64, 1 << 30) == "stream"
+        zs.set_write_window(2048, 256)
+        assert zs.reduce_schedule(8, 1 << 30) == "windowed"
+        assert zs.reduce_schedule(8, 1 << 20) == "stream"   # below the windowed kernel's size
+        zs.set_write_window(0)
+        zs.set_flat_schedule("phased")
+        assert zs.reduce_schedule(8, 512) == "phased"       # one whole wave tile is enough
+        assert zs.reduce_schedule(8, 511) == "stream"
+        zs.set_flat_schedule("stream")
+        assert zs.reduce_schedule(64, 1 << 30) == "stream"
+        with pytest.raises(zs.ZShardError):
+            zs.reduce_schedule(0, 1 << 20)
+        with pytest.raises(zs.ZShardError):
+            zs.reduce_schedule(8, -1)
+    finally:
+        zs.set_flat_schedule("auto")
+        zs.set_write_window(0)
 
 
 def test_flat_schedule_query_and_setting():
