@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 METRIC = "params/s and achieved HBM GB/s (% of peak) for fused reduce+Adam shard step"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SRCS = [os.path.join(ROOT, "sharded_mixed_precision_rank_amd", "csrc", f)
-               for f in ("zs_kernels.hip", "zs_device.h", "zs_internal.h")]
+               for f in ("zs_kernels.hip", "zs_twopass.hip", "zs_device.h", "zs_phased.h", "zs_internal.h",
+                         "zs_twopass.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -276,6 +277,9 @@ def main() -> int:
     ap.add_argument("--workload", default="flat-70b", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle baseline budget (0 = skip)")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy-kernel and access-pattern ceilings")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the step itself: no other schedules, per-pass times, flat reference or "
+                         "window-less rerun (for profiler runs that count launches per step)")
     ap.add_argument("--blocks", type=int, default=0, help="workgroups per launch (0 = library default)")
     ap.add_argument("--path", default="fused", choices=["fused", "clip", "fp16", "offload"],
                     help="fused: the one-pass step; clip: two-pass with global-norm clipping (max_norm 1); "
@@ -398,19 +402,55 @@ def main() -> int:
     sched = zs.flat_schedule(w.N, n) if flat_fused else None
     window = (0, 0) if offload is not None else zs.write_window("reduce" if two_pass else "flat", w.N, n)
 
-    def median_ms(k: int = 5) -> float:
-        step(w.step)
+    def median_ms_of(fn, t0: int, k: int = 5) -> float:
+        fn(t0)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
         e[0].record()
         for j in range(k):
-            step(w.step + 1 + j)
+            fn(t0 + 1 + j)
             e[j + 1].record()
         torch.cuda.synchronize()
         return sorted(e[j].elapsed_time(e[j + 1]) for j in range(k))[k // 2]
 
+    def median_ms(k: int = 5) -> float:
+        return median_ms_of(step, w.step, k)
+
     unwindowed = None
     other_schedules = None
-    if flat_fused:
+    passes = None
+    flat_reference = None
+    if two_pass and offload is None and not args.no_extras:
+        # each pass on its own, in this process: pass 1 (2N read, 4 written per parameter, and the norm) and
+        # pass 2 (16 read, 14 written), against the algorithmic bytes of each
+        gfmt_ = "fp16" if args.path == "fp16" else "bf16"
+
+        def pass_ms(fn, k: int = 5) -> float:
+            fn()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+            e[0].record()
+            for j in range(k):
+                fn()
+                e[j + 1].record()
+            torch.cuda.synchronize()
+            return sorted(e[j].elapsed_time(e[j + 1]) for j in range(k))[k // 2]
+
+        p1 = pass_ms(lambda: zs.reduce_grads_flat(d["G"], ws, sqn, loss_scale, gfmt_))
+        p2 = pass_ms(lambda: zs.adam_from_grads_flat(ws, n, d["P"], d["M"], d["V"], d["B"], w.hp(), w.step, sqn,
+                                                     1.0, gfmt_))
+        passes = {"pass1_ms": p1, "pass1_GBps": (2 * w.N + 4) * n / (p1 / 1e3) / 1e9,
+                  "pass2_ms": p2, "pass2_GBps": 30 * n / (p2 / 1e3) / 1e9,
+                  "pass1_schedule": zs.reduce_schedule(w.N, n)}
+        log(f"pass 1 ({passes['pass1_schedule']}): {p1:.3f} ms, {passes['pass1_GBps']:.0f} GB/s; "
+            f"pass 2: {p2:.3f} ms, {passes['pass2_GBps']:.0f} GB/s (medians of 5)")
+    if w.is_list and plan is not None and not args.no_extras:
+        # one flat call over the list's whole arena (its gaps included), in this process: what the list's
+        # per-tensor structure costs
+        L = d["P"].numel()
+        fm = median_ms_of(lambda t: zs.reduce_adam_flat(d["G"], d["P"], d["M"], d["V"], d["B"], w.hp(), t), w.step)
+        flat_reference = {"ms_per_step_median": fm, "arena_params": L, "list_over_flat": ms_median / (fm * n / L)}
+        log(f"one flat call over the arena: {fm:.3f} ms ({fm * n / L:.3f} ms for the list's parameters); "
+            f"the list takes {100 * (flat_reference['list_over_flat'] - 1):+.2f}%")
+    if flat_fused and not args.no_extras:
         # the same steps on the flat step's other schedules, in this process: what the schedule is worth
         other_schedules = {}
         for other in ("phased", "windowed", "stream"):
@@ -421,7 +461,7 @@ def main() -> int:
                 other_schedules[other] = {"ms_per_step_median": median_ms(), "steps": 5}
                 log(f"{other} schedule: {other_schedules[other]['ms_per_step_median']:.3f} ms/step (median of 5)")
         zs.set_flat_schedule("auto")
-    elif window[0]:
+    elif window[0] and not args.no_extras:
         # the same steps with the windows switched off, in this process: the windows' own effect
         zs.set_write_window(1)
         unwindowed = {"ms_per_step_median": median_ms(), "steps": 5}
@@ -431,7 +471,9 @@ def main() -> int:
     if w.is_list:
         kernel = ("list_window_kernel" if window[0] else "list_kernel") + tn
     elif two_pass:
-        kernel = ("reduce_window_kernel" if window[0] else "reduce_kernel") + tn + " + gbar_kernel"
+        p1s = zs.reduce_schedule(w.N, n)
+        kernel = ("reduce_phased_kernel" + (tn if w.N == 64 else "<0>") if p1s == "phased" else
+                  ("reduce_window_kernel" if window[0] else "reduce_kernel") + tn) + " + gbar_kernel"
     elif sched == "phased":
         kernel = "flat_phased_kernel" + (tn if w.N == 64 else "<0>")
     else:
@@ -481,6 +523,8 @@ def main() -> int:
         "pattern_ceiling": pattern,
         "without_write_windows": unwindowed,
         "other_schedules": other_schedules,
+        "passes": passes,
+        "flat_reference": flat_reference,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic if args.path == "fused" else None,
                      "bytes_per_param": bpp, "kernel": kernel},
