@@ -437,11 +437,14 @@ ZS_API int64_t zs_launch_bytes(void);
    computed identically and written to their own addresses (pass 1's norm
    partials too).
      period_ticks = 0: the library's measured default (the default;
-                       open_ticks is ignored): for N >= 48 replicas a
-                       4096-tick period with 640 (N < 64), 512 (N <= 128) or
-                       384 ticks open for the flat step and 256 for pass 1;
-                       no windows below 48 replicas, where the writes are too
-                       large a share of the bytes for them to pay;
+                       open_ticks is ignored): list plans of N >= 48
+                       replicas take a 4096-tick period with 640 (N < 64),
+                       512 (N <= 128) or 384 ticks open, and none below 48
+                       replicas, where the writes are too large a share of
+                       the bytes for them to pay; the flat step and pass 1
+                       take windows only on the windowed schedule
+                       (zs_set_flat_schedule), with those windows for the
+                       flat step (any N) and 4096 / 256 for pass 1;
      period_ticks = 1: no windows (tiles stored as they finish);
      otherwise a power of two in [64, 2^20], with 1 <= open_ticks < period_ticks
      and open_ticks <= 2^14.
