@@ -400,7 +400,8 @@ def main() -> int:
     # a list plan takes the flat step's windows, by its total parameter count
     flat_fused = offload is None and not two_pass and not w.is_list
     sched = zs.flat_schedule(w.N, n) if flat_fused else None
-    window = (0, 0) if offload is not None else zs.write_window("reduce" if two_pass else "flat", w.N, n)
+    window = (0, 0) if offload is not None else zs.write_window(
+        "reduce" if two_pass else "list" if w.is_list else "flat", w.N, n)
 
     def median_ms_of(fn, t0: int, k: int = 5) -> float:
         fn(t0)
@@ -469,7 +470,9 @@ def main() -> int:
         log(f"without write windows: {unwindowed['ms_per_step_median']:.3f} ms/step (median of 5)")
     tn = f"<{w.N}>" if w.N in (1, 2, 4, 8, 16, 32, 64) else "<0>"
     if w.is_list:
-        kernel = ("list_window_kernel" if window[0] else "list_kernel") + tn
+        lsched = zs.flat_schedule(w.N, n)   # a list plan takes the schedule of a flat shard of its size
+        kernel = ("list_phased_kernel" + (tn if w.N == 64 else "<0>") if lsched == "phased" else
+                  ("list_window_kernel" if window[0] else "list_kernel") + tn)
     elif two_pass:
         p1s = zs.reduce_schedule(w.N, n)
         kernel = ("reduce_phased_kernel" + (tn if w.N == 64 else "<0>") if p1s == "phased" else
@@ -515,7 +518,8 @@ def main() -> int:
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "n_params": n, "replicas": w.N, "adam_step": w.step,
                    "weight_decay": w.weight_decay, "path": args.path,
-                   "schedule": sched, "write_window_ticks": list(window) if window[0] else None,
+                   "schedule": sched if not w.is_list else zs.flat_schedule(w.N, n),
+                   "write_window_ticks": list(window) if window[0] else None,
                    "max_bytes_per_launch": zs.launch_bytes(),
                    "storage": ("fp16" if args.path == "fp16" else "bf16") + " grads and working copy, fp32 master/m/v"},
         "hbm_GBps": achieved, "hbm_frac_of_peak": achieved / HBM_PEAK_GBPS,

@@ -437,14 +437,11 @@ ZS_API int64_t zs_launch_bytes(void);
    computed identically and written to their own addresses (pass 1's norm
    partials too).
      period_ticks = 0: the library's measured default (the default;
-                       open_ticks is ignored): list plans of N >= 48
-                       replicas take a 4096-tick period with 640 (N < 64),
-                       512 (N <= 128) or 384 ticks open, and none below 48
-                       replicas, where the writes are too large a share of
-                       the bytes for them to pay; the flat step and pass 1
-                       take windows only on the windowed schedule
-                       (zs_set_flat_schedule), with those windows for the
-                       flat step (any N) and 4096 / 256 for pass 1;
+                       open_ticks is ignored): windows only on the windowed
+                       schedule (zs_set_flat_schedule): a 4096-tick period
+                       with 640 (N < 64), 512 (N <= 128) or 384 ticks open
+                       for the flat step and list plans, 4096 / 256 for
+                       pass 1;
      period_ticks = 1: no windows (tiles stored as they finish);
      otherwise a power of two in [64, 2^20], with 1 <= open_ticks < period_ticks
      and open_ticks <= 2^14.
@@ -466,9 +463,8 @@ ZS_API zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks);
                                      (zs_reduce_grads_flat): only on the
                                      windowed schedule (zs_reduce_schedule),
                                      on shards of at least 2^25 parameters;
-     kernel = ZS_WINDOW_LIST_PLAN:   a list plan of n parameters in all (the
-                                     flat step's default windows for N, from
-                                     2^25 parameters on).
+     kernel = ZS_WINDOW_LIST_PLAN:   a list plan of n parameters in all: as the
+                                     flat step on a shard of that size.
    *period_ticks = *open_ticks = 0 when it takes no windows.  No GPU call.
    Errors: ZS_ERR_NULL, ZS_ERR_RANGE. */
 #define ZS_WINDOW_FLAT_STEP 0
@@ -477,13 +473,18 @@ ZS_API zs_status zs_set_write_window(int32_t period_ticks, int32_t open_ticks);
 ZS_API zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* period_ticks, int32_t* open_ticks);
 
 /* The schedule of the flat step (zs_reduce_adam_flat and its device-step
-   form) and of pass 1 of the two-pass form (zs_reduce_grads_flat and its
-   device-scale form), for all later calls in this process.  Every schedule
+   form), of list plans (every zs_reduce_adam_list* call, taking the schedule
+   of a flat shard of the plan's total size) and of pass 1 of the two-pass
+   form (zs_reduce_grads_flat and its device-scale form), for all later calls
+   in this process.  Every schedule
    computes every parameter by the same operations in the same order, and
    pass 1's norm partials in the same order, so results do not depend on it;
    only when the bytes move does.  For pass 1 the phased schedule writes the
    mean gradient and the norm partials after the grid barrier, and its
-   windowed default is 4096 / 256 ticks.
+   windowed default is 4096 / 256 ticks.  A list plan on the phased schedule
+   gives each wave 8 consecutive wave tiles per super-chunk; when they are not
+   whole tiles of one tensor (near a tensor's ends) the wave takes them one at
+   a time after the barrier.
      ZS_SCHEDULE_AUTO:     the default.  An explicit zs_set_write_window
                            decides when one was made (no windows:
                            ZS_SCHEDULE_STREAM; a window: ZS_SCHEDULE_WINDOWED);

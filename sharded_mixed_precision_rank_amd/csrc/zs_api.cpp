@@ -183,27 +183,15 @@ int auto_blocks() {
   return forced > 0 ? forced : 1 << 30;
 }
 
-// The flat step's write window for N replicas: the one set by
-// zs_set_write_window, else the measured default.  Defaults, in ticks of the
-// 100 MHz device clock (period / open), for a 4096-tick (41 us) period: open
-// 640 for 48 <= N < 64, 512 for 64 <= N <= 128, 384 above (the writes' share
-// of the bytes shrinks as N grows).  Below 48 replicas the writes are too
-// large a share for windows to pay, and the step stores as it goes.
-zs::WriteWindow write_window(int32_t N) {
-  const uint64_t word = g_window.load(std::memory_order_relaxed);
-  const int32_t period = (int32_t)(word >> 32), open = (int32_t)(word & 0xFFFFFFFFu);
-  if (period == 1) return zs::WriteWindow{0, 0};
-  if (period > 1) return zs::WriteWindow{(uint64_t)period - 1, (uint64_t)open};
-  if (N < 48) return zs::WriteWindow{0, 0};
-  return zs::WriteWindow{4096 - 1, N < 64 ? 640u : N <= 128 ? 512u : 384u};
-}
-
-// The flat step's schedule for N replicas on a shard of n parameters, and
-// the write window it takes (period_mask 0 unless windowed).  An explicit
-// zs_set_flat_schedule wins; otherwise an explicit zs_set_write_window decides
-// (no windows: per-tile stores; a window: the windowed kernel); otherwise the
-// phased kernel for N >= kPhasedMinReplicas (32) on shards of at least
-// kPhasedMinParams, and per-tile stores below.
+// The flat step's schedule for N replicas on a shard of n parameters (and a
+// list plan's, for n parameters in all), and the write window it takes
+// (period_mask 0 unless windowed).  An explicit zs_set_flat_schedule wins;
+// otherwise an explicit zs_set_write_window decides (no windows: per-tile
+// stores; a window: the windowed kernel); otherwise the phased kernel for
+// N >= kPhasedMinReplicas (32) on shards of at least kPhasedMinParams, and
+// per-tile stores below.  The windowed kernel's default window is a
+// 4096-tick (41 us) period with 640 ticks open for N < 64, 512 up to 128 and
+// 384 above: the writes' share of the bytes shrinks as N grows.
 zs::FlatSchedule flat_schedule(int32_t N, int64_t n, zs::WriteWindow* win) {
   const int32_t forced = g_flat_schedule.load(std::memory_order_relaxed);
   const uint64_t word = g_window.load(std::memory_order_relaxed);
@@ -679,12 +667,10 @@ zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* period_
   if (n < 0) return fail(ZS_ERR_RANGE, "n must be >= 0");
   const bool flat = kernel != ZS_WINDOW_REDUCE_PASS;  // the flat step and list plans: 512-parameter tiles
   zs::WriteWindow w{};
-  if (kernel == ZS_WINDOW_FLAT_STEP)
-    (void)flat_schedule(N, n, &w);
-  else if (kernel == ZS_WINDOW_LIST_PLAN)
-    w = write_window(N);
-  else
+  if (kernel == ZS_WINDOW_REDUCE_PASS)
     (void)reduce_schedule(N, n, &w);
+  else  // list plans take the flat step's schedule for a shard of their size
+    (void)flat_schedule(N, n, &w);
   const bool big = flat ? n / 8 / zs::kFlatBlock >= zs::kWindowMinTiles
                         : n / kTileElems >= zs::kReduceWindowMinTiles;
   const bool used = w.period_mask != 0 && big;
@@ -837,11 +823,13 @@ zs_status launch_list_table(const int32_t* items, int32_t n_items, const zs::Lis
                             const uint16_t* const* gptrs, int32_t N, int64_t n_params, const zs::Scalars* cs,
                             int32_t n_sets, const zs::StepRef& ref, zs_stream stream) {
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  // write windows for plans of at least 2^25 parameters, as for flat shards
-  const zs::WriteWindow win =
-      n_params >= ((int64_t)zs::kWindowMinTiles << 9) ? write_window(N) : zs::WriteWindow{0, 0};
-  return after_launch(zs::launch_list(items, n_items, tensors, gptrs, cs, n_sets, ref, auto_blocks(), win, hs), hs,
-                      "zs_reduce_adam_list launch");
+  // the flat step's schedule for a shard of the plan's size; windows for plans of at least 2^25 parameters
+  zs::WriteWindow win{};
+  const zs::FlatSchedule sched = flat_schedule(N, n_params, &win);
+  if (n_params < ((int64_t)zs::kWindowMinTiles << 9)) win = zs::WriteWindow{0, 0};
+  return after_launch(zs::launch_list(items, n_items, tensors, gptrs, cs, n_sets, ref, auto_blocks(), sched, win,
+                                      phased_ctl(), hs),
+                      hs, "zs_reduce_adam_list launch");
 }
 
 // The step with `n` hyperparameter sets (one for every tensor, n == 1, or one

@@ -123,12 +123,13 @@ hipError_t launch_step_advance(int64_t* step, hipStream_t stream);
 // cs: n_sets folded scalar sets, one per hyperparameter group (1 <= n_sets <=
 // kMaxGroups); with a device step (ref.table set) n_sets is 1 and the table
 // supplies the folded scalars.
-// win: write windows (list_window_kernel) when period_mask != 0.
+// sched: the schedule (list_phased_kernel, list_window_kernel with `win`, or
+// list_kernel), as for a flat shard of the plan's size.
 // items: n_items tensor indices, one per work item (a wave tile), tensor by
 // tensor in order.
 hipError_t launch_list(const int32_t* items, int32_t n_items, const ListTensor* tensors,
                        const uint16_t* const* gptrs, const Scalars* cs, int n_sets, const StepRef& ref, int blocks,
-                       const WriteWindow& win, hipStream_t stream);
+                       FlatSchedule sched, const WriteWindow& win, const PhasedCtl& ctl, hipStream_t stream);
 
 // Threads per workgroup of the fused step's kernels; each thread owns one
 // 8-parameter group, so a tile is 8x this many parameters.  One wave: a

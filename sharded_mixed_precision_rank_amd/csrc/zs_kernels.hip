@@ -347,8 +347,10 @@ __global__ __launch_bounds__(kFlatBlock) void flat_window_kernel(const FlatArgs<
 // parameter of writes go out together instead of trickling out beside the
 // replica reads.  Slot k of wave w in super-chunk c is tile
 // c*T + k*W + w (T tiles per super-chunk, W waves in the grid): in phase B
-// the grid walks each array in one contiguous front.  The last super-chunk
-// may be partial: a wave then owns a prefix of its slots (possibly none).
+// the grid walks each array in one contiguous front.  Only whole super-chunks
+// run phased; the whole tiles after them go one per wave, stored as each is
+// done, and the last workgroup's first wave takes the partial tile and the
+// head and tail elements.
 //
 // The barriers only shape the timing.  Every tile's outputs are formed by the
 // same operations as in flat_kernel and stored to its own addresses, so the
@@ -468,6 +470,31 @@ __device__ __forceinline__ ListWork list_work(const int32_t* __restrict__ items,
   return w;
 }
 
+// One work item of a list plan (see list_work), by one wave of any workgroup:
+// a whole tile (the split layout), a partial tile, or 512 elements of a
+// scalar-only tensor, and for a tensor's first item its head and tail elements.
+template <int NT>
+__device__ __forceinline__ void list_item_step(const ListWork& w, int N, const Scalars& c) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const FlatShape& s = w.s;
+  auto G0 = [&](int r) { return uniform_ptr(w.gp[r]); };
+  if (s.scalar_only) {
+    for (int64_t i = w.lo + lane; i < w.hi; i += kFlatBlock) elem_step(G0, N, i, s, c);
+    return;
+  }
+  const int64_t e0 = s.head + 8 * w.lo;
+  auto G = [&](int r) { return tile_base(G0(r) + e0); };
+  if (w.hi - w.lo == kFlatBlock)
+    group_step_at<NT, true>(G, N, e0, 4u * lane, s, c);
+  else
+    partial_step<NT>(G, N, e0, w.hi - w.lo, s, c);
+  if (w.first) {
+    const int64_t tail = s.n - s.head - 8 * s.nvec;
+    for (int64_t t = lane; t < s.head + tail; t += kFlatBlock)
+      elem_step(G0, N, t < s.head ? t : s.head + 8 * s.nvec + (t - s.head), s, c);
+  }
+}
+
 // The ragged-list step: one-wave workgroups, one work item each, as
 // flat_kernel takes one tile: the plan's table holds one entry per wave tile
 // of every tensor (its tensor's index), tensor by tensor, so every workgroup
@@ -490,20 +517,7 @@ __global__ __launch_bounds__(kFlatBlock) void list_kernel(const int32_t* __restr
   }
   for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
     const ListWork w = list_work(items, it, i0, tensors, gptrs, N);
-    const FlatShape& s = w.s;
-    const Scalars& c = NG == 1 ? one : sc.c[w.grp];
-    auto G0 = [&](int r) { return uniform_ptr(w.gp[r]); };
-    if (s.scalar_only) {
-      for (int64_t i = w.lo + threadIdx.x; i < w.hi; i += kFlatBlock) elem_step(G0, N, i, s, c);
-      continue;
-    }
-    const int64_t e0 = s.head + 8 * w.lo;
-    auto G = [&](int r) { return tile_base(G0(r) + e0); };
-    if (w.hi - w.lo == kFlatBlock)
-      group_step<NT, true>(G, N, e0, s, c);
-    else
-      partial_step<NT>(G, N, e0, w.hi - w.lo, s, c);
-    if (w.first) edge_step<kFlatBlock>(G0, N, s, c);
+    list_item_step<NT>(w, N, NG == 1 ? one : sc.c[w.grp]);
   }
 }
 
@@ -621,6 +635,115 @@ __global__ __launch_bounds__(kFlatBlock) void list_window_kernel(const int32_t* 
   held.flush();
 }
 
+// List plans on the phased schedule (see flat_phased_kernel): one workgroup of
+// kPhasedWaves waves per compute unit; super-chunk c gives wave w the
+// kPhasedTiles consecutive items from (c*W + w)*kPhasedTiles (W waves in the
+// grid).  When they are whole tiles of one tensor (all but a few waves in a
+// list of large tensors), the wave streams their replicas into its
+// accumulators in phase A (the flat step's own code; the tensor's replica
+// pointers come from the plan's table, one scalar load per replica) and
+// updates them in phase B after the grid barrier.  Otherwise the wave reads
+// nothing in phase A, meets the same barriers, and takes its items one at a
+// time in phase B.  Items after the last whole super-chunk go one per wave.
+// Every element goes through the same operations as in list_kernel.
+template <int NT, int NG>
+__global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void list_phased_kernel(
+    const int32_t* __restrict__ items, int32_t n_items, const ListTensor* __restrict__ tensors,
+    const uint16_t* const* __restrict__ gptrs, const ListScalars<NG> sc, const StepRef ref, const PhasedCtl ctl) {
+  constexpr int K = kPhasedTiles;
+  constexpr int64_t kGroups = kTileElemsWave / 8;
+  const int N = NT > 0 ? NT : sc.c[0].n_rep;
+  Scalars one = sc.c[0];
+  if constexpr (NG == 1) {
+    if (!step_scalars(ref, one)) return;  // the same decision in every workgroup
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t e = 4u * lane;
+  const int64_t nw = (int64_t)gridDim.x * kPhasedWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kPhasedWaves + wave;
+  const int64_t per = nw * K;
+  const int64_t nsup = n_items / per;
+  uint32_t* counter = &g_phased_counters[32 * ctl.slot];
+  // the wave's K items of super-chunk c: their tensor, its descriptor as a shard, the first item's
+  // place in it and first 8-group, and whether all K are whole tiles of that tensor
+  struct Octet {
+    int32_t t;
+    FlatShape s;
+    int64_t k0, g0;
+    bool whole;
+  };
+  auto octet = [&](int64_t c) {
+    Octet o;
+    const int64_t it0 = (c * nw + gw) * K;
+    o.t = items[it0];
+    const ListTensor& T = tensors[o.t];
+    o.s.p = uniform_fptr(T.p);
+    o.s.m = uniform_fptr(T.m);
+    o.s.v = uniform_fptr(T.v);
+    o.s.b = uniform_fptr(T.b);
+    o.s.n = uniform_i64(T.n);
+    const int32_t hl = T.head_lead;
+    const int32_t lead = hl >> 8;
+    o.s.head = hl & 0xFF;
+    o.s.nvec = uniform_i64(T.nvec);
+    o.s.scalar_only = T.scalar_only;
+    o.k0 = it0 - T.item0;
+    o.g0 = (lead > 0 ? lead - kGroups : 0) + o.k0 * kGroups;
+    o.whole = !o.s.scalar_only && items[it0 + K - 1] == o.t && o.g0 >= 0 && o.g0 + K * kGroups <= o.s.nvec;
+    return o;
+  };
+  for (int64_t c = 0; c < nsup; ++c) {
+    const Octet o = octet(c);
+    const FlatShape& s = o.s;
+    int64_t es[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) es[k] = s.head + 8 * (o.g0 + k * kGroups);
+    const uint16_t* const* gpt = gptrs + (int64_t)o.t * N;
+    auto gp = [&](int r) { return uniform_ptr(gpt[r]); };
+    float acc[K][8];
+    phased_accumulate<NT, kBF16, K>(gp, N, es, e, acc, o.whole);
+    f32x4 st[2][6];
+    if (o.whole) phased_state_load(s, es, 0, e, st[0]);
+    phased_grid_barrier(counter, (uint32_t)c * gridDim.x + phased_quorum(gridDim.x), ctl.max_polls);
+    if (o.whole) {
+      const Scalars& cs = NG == 1 ? one : sc.c[tensors[o.t].group];
+      phased_update(s, es, e, acc, st, [&](const float(&a)[8], float(&p)[8], float(&m)[8], float(&v)[8]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) adam(mean_of<NT>(a[j], cs), p[j], m[j], v[j], cs);
+      });
+    }
+  }
+  // after the super-chunks: the items of the wave's octets that were not whole tiles of one tensor, one
+  // at a time; the head and tail elements of a tensor whose first item led a whole octet; then the items
+  // after the last whole super-chunk, one per wave
+  for (int64_t c = 0; c < nsup; ++c) {
+    const Octet o = octet(c);
+    if (o.whole) {
+      if (o.k0 == 0) {
+        const FlatShape& s = o.s;
+        const uint16_t* const* gpt = gptrs + (int64_t)o.t * N;
+        auto gp = [&](int r) { return uniform_ptr(gpt[r]); };
+        const Scalars& cs = NG == 1 ? one : sc.c[tensors[o.t].group];
+        const int64_t tail = s.n - s.head - 8 * s.nvec;
+        for (int64_t i = lane; i < s.head + tail; i += kFlatBlock)
+          elem_step(gp, N, i < s.head ? i : s.head + 8 * s.nvec + (i - s.head), s, cs);
+      }
+    } else {
+      const int64_t it0 = (c * nw + gw) * K;
+      for (int k = 0; k < K; ++k) {
+        const ListWork w = list_work(items, it0 + k, 0, tensors, gptrs, N);
+        list_item_step<NT>(w, N, NG == 1 ? one : sc.c[w.grp]);
+      }
+    }
+  }
+  for (int64_t it = nsup * per + gw; it < n_items; it += nw) {
+    // the index is the wave's own (wave-uniform): say so, or the descriptor's pointers land in vector registers
+    const ListWork w = list_work(items, uniform_i64(it), 0, tensors, gptrs, N);
+    list_item_step<NT>(w, N, NG == 1 ? one : sc.c[w.grp]);
+  }
+}
+
 // Flat-kernel grid: `blocks`, but no more workgroups than tiles.
 int clamp_grid(int blocks, int64_t work) {
   int64_t need = (work + kFlatBlock - 1) / kFlatBlock;
@@ -726,32 +849,56 @@ hipError_t go_list_window(const int32_t* items, int32_t n_items, const ListTenso
   return hipGetLastError();
 }
 
+template <int NT, int NG>
+hipError_t go_list_phased(const int32_t* items, int32_t n_items, const ListTensor* tensors,
+                          const uint16_t* const* gptrs, const ListScalars<NG>& sc, const StepRef& ref, int blocks,
+                          const PhasedCtl& ctl, hipStream_t stream, bool* launched) {
+  // templated for 64 replicas; other counts take the run-time instance
+  constexpr int KT = NT == 64 ? 64 : 0;
+  static std::atomic<int> cache[kMaxDevices];
+  *launched = false;
+  int grid = resident_grid(list_phased_kernel<KT, NG>, kFlatBlock * kPhasedWaves, cache);
+  if (grid <= 0) {
+    (void)hipGetLastError();  // no occupancy figure: the caller takes the one-tile kernel
+    return hipSuccess;
+  }
+  if (blocks < grid) grid = blocks;
+  (void)hipGetLastError();
+  phased_clear_kernel<<<dim3(1), dim3(64), 0, stream>>>(ctl.slot);
+  list_phased_kernel<KT, NG><<<dim3(grid), dim3(kFlatBlock * kPhasedWaves), 0, stream>>>(items, n_items, tensors,
+                                                                                        gptrs, sc, ref, ctl);
+  *launched = true;
+  return hipGetLastError();
+}
+
 template <int NT>
 hipError_t go_list(const int32_t* items, int32_t n_items, const ListTensor* tensors,
                    const uint16_t* const* gptrs, const Scalars* cs, int n_sets, const StepRef& ref, int blocks,
-                   const WriteWindow& win, hipStream_t stream) {
-  if (win.period_mask != 0) {
+                   FlatSchedule sched, const WriteWindow& win, const PhasedCtl& ctl, hipStream_t stream) {
+  ListScalars<1> sc1;
+  ListScalars<kMaxGroups> scg;
+  sc1.c[0] = cs[0];
+  for (int k = 0; k < kMaxGroups; ++k) scg.c[k] = cs[k < n_sets ? k : 0];
+  if (sched == FlatSchedule::kPhased) {
     bool launched = false;
-    hipError_t e;
-    if (n_sets <= 1) {
-      ListScalars<1> sc;
-      sc.c[0] = cs[0];
-      e = go_list_window<NT, 1>(items, n_items, tensors, gptrs, sc, ref, blocks, win, stream, &launched);
-    } else {
-      ListScalars<kMaxGroups> sc;
-      for (int k = 0; k < kMaxGroups; ++k) sc.c[k] = cs[k < n_sets ? k : 0];
-      e = go_list_window<NT, kMaxGroups>(items, n_items, tensors, gptrs, sc, ref, blocks, win, stream, &launched);
-    }
+    const hipError_t e =
+        n_sets <= 1 ? go_list_phased<NT, 1>(items, n_items, tensors, gptrs, sc1, ref, blocks, ctl, stream, &launched)
+                    : go_list_phased<NT, kMaxGroups>(items, n_items, tensors, gptrs, scg, ref, blocks, ctl, stream,
+                                                     &launched);
+    if (launched || e != hipSuccess) return e;
+  }
+  if (sched == FlatSchedule::kWindowed && win.period_mask != 0) {
+    bool launched = false;
+    const hipError_t e =
+        n_sets <= 1
+            ? go_list_window<NT, 1>(items, n_items, tensors, gptrs, sc1, ref, blocks, win, stream, &launched)
+            : go_list_window<NT, kMaxGroups>(items, n_items, tensors, gptrs, scg, ref, blocks, win, stream, &launched);
     if (launched || e != hipSuccess) return e;
   }
   // consecutive launches over the item table, each at most launch_bytes()
   // (an item is at most one wave tile; every item is complete in itself, its
   // tensor's head and tail included)
   const int64_t per = units_per_launch(kTileElemsWave * (2 * (int64_t)cs[0].n_rep + 26), 1);
-  ListScalars<1> sc1;
-  ListScalars<kMaxGroups> scg;
-  sc1.c[0] = cs[0];
-  for (int k = 0; k < kMaxGroups; ++k) scg.c[k] = cs[k < n_sets ? k : 0];
   for (int64_t i0 = 0; i0 < n_items; i0 += per) {
     const int32_t cnt = (int32_t)(n_items - i0 > per ? per : n_items - i0);
     const int grid = blocks < cnt ? blocks : cnt;
@@ -792,16 +939,16 @@ hipError_t launch_step_advance(int64_t* step, hipStream_t stream) {
 
 hipError_t launch_list(const int32_t* items, int32_t n_items, const ListTensor* tensors,
                        const uint16_t* const* gptrs, const Scalars* cs, int n_sets, const StepRef& ref, int blocks,
-                       const WriteWindow& win, hipStream_t stream) {
+                       FlatSchedule sched, const WriteWindow& win, const PhasedCtl& ctl, hipStream_t stream) {
   switch (cs[0].n_rep) {
-    case 1: return go_list<1>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    case 2: return go_list<2>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    case 4: return go_list<4>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    case 8: return go_list<8>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    case 16: return go_list<16>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    case 32: return go_list<32>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    case 64: return go_list<64>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
-    default: return go_list<0>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, win, stream);
+    case 1: return go_list<1>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, sched, win, ctl, stream);
+    case 2: return go_list<2>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, sched, win, ctl, stream);
+    case 4: return go_list<4>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, sched, win, ctl, stream);
+    case 8: return go_list<8>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, sched, win, ctl, stream);
+    case 16: return go_list<16>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, sched, win, ctl, stream);
+    case 32: return go_list<32>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, sched, win, ctl, stream);
+    case 64: return go_list<64>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, sched, win, ctl, stream);
+    default: return go_list<0>(items, n_items, tensors, gptrs, cs, n_sets, ref, blocks, sched, win, ctl, stream);
   }
 }
 

@@ -44,12 +44,15 @@ __device__ __forceinline__ uint32_t phased_quorum(uint32_t grid) {
 // workgroup's waves meeting at a workgroup barrier every two replicas so that
 // they read the same replicas at about the same time.  gp(r) is replica r's
 // gradient pointer (bf16 or fp16 bits per FMT).
+//  A wave with `active` false (wave-uniform) issues no loads and leaves acc
+// undefined, but meets every workgroup barrier with the others.
 template <int NT, int FMT, int K, class GP>
 __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&es)[K], uint32_t e,
-                                                  float (&acc)[K][8]) {
+                                                  float (&acc)[K][8], bool active = true) {
   constexpr uint32_t q2 = Layout<true>::kSecond / 4;
   u32x2 w0[K][2], w1[K][2];
   auto load = [&](int r, u32x2(&w)[K][2]) {
+    if (!active) return;
     const uint16_t* g = gp(r);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -101,6 +104,57 @@ __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&
   }
 }
 
+// Phase B's state loads of a wave's tile k: master, m and v at element es[k].
+template <int K>
+__device__ __forceinline__ void phased_state_load(const FlatShape& s, const int64_t (&es)[K], int k, uint32_t e,
+                                                  f32x4 (&q)[6]) {
+  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  const uint32_t o = here(e) * 4u;
+  const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(s.p + es[k]), o);
+  const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(s.m + es[k]), o);
+  const GLB f32x4* V4 = (const GLB f32x4*)at(tile_base(s.v + es[k]), o);
+  q[0] = ld_g(P4);
+  q[1] = ld_g(P4 + q2);
+  q[2] = ld_g(M4);
+  q[3] = ld_g(M4 + q2);
+  q[4] = ld_g(V4);
+  q[5] = ld_g(V4 + q2);
+}
+
+// Phase B after the grid barrier, tile by tile with the next tile's state in
+// flight (tile 0's state already requested into st[0]): upd(acc, p, m, v)
+// turns a lane's 8 rank-ordered replica sums and its 8 master, m and v values
+// into the new master, m and v, and the four outputs are stored.
+template <int K, class UPD>
+__device__ __forceinline__ void phased_update(const FlatShape& s, const int64_t (&es)[K], uint32_t e,
+                                              float (&acc)[K][8], f32x4 (&st)[2][6], UPD&& upd) {
+  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (k + 1 < K) phased_state_load(s, es, k + 1, e, st[(k + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x4* q = st[k & 1];
+    float p[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
+    float m[8] = {q[2].x, q[2].y, q[2].z, q[2].w, q[3].x, q[3].y, q[3].z, q[3].w};
+    float v[8] = {q[4].x, q[4].y, q[4].z, q[4].w, q[5].x, q[5].y, q[5].z, q[5].w};
+    upd(acc[k], p, m, v);
+    const TileOut h = tile_outputs(p, m, v);
+    const uint32_t o = here(e) * 4u;
+    GLB f32x4* P4 = (GLB f32x4*)at(tile_base(s.p + es[k]), o);
+    GLB f32x4* M4 = (GLB f32x4*)at(tile_base(s.m + es[k]), o);
+    GLB f32x4* V4 = (GLB f32x4*)at(tile_base(s.v + es[k]), o);
+    st_g(P4, h.p0);
+    st_g(P4 + q2, h.p1);
+    st_g(M4, h.m0);
+    st_g(M4 + q2, h.m1);
+    st_g(V4, h.v0);
+    st_g(V4 + q2, h.v1);
+    GLB u32x2* B2 = (GLB u32x2*)at(tile_base(s.b + es[k]), here(e) * 2u);
+    st_g(B2, h.b0);
+    st_g(B2 + q2, h.b1);
+  }
+}
+
 // The whole super-chunks of a flat shard (tiles of 512 parameters from element
 // s.head; s.nvec 8-element groups on the vector path): phase A, the grid
 // barrier, phase B, for each.  gp(r) is replica r's gradient pointer (the
@@ -112,7 +166,6 @@ template <int NT, class GP, class UPD>
 __device__ __forceinline__ int64_t phased_super_chunks(GP gp, int N, const FlatShape& s, int32_t slot,
                                                       int32_t max_polls, UPD&& upd) {
   constexpr int K = kPhasedTiles;
-  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t e = 4u * (threadIdx.x & 63u);  // the split lane layout inside a tile
   const int64_t nw = (int64_t)gridDim.x * kPhasedWaves;
@@ -132,50 +185,11 @@ __device__ __forceinline__ int64_t phased_super_chunks(GP gp, int N, const FlatS
     // ---- phase B: state, AdamW, outputs, tile by tile (the next tile's state in flight).  The first
     // tile's state is requested before the barrier: reads, like the stragglers' replica reads.
     f32x4 st[2][6];
-    auto sload = [&](int k, f32x4(&q)[6]) {
-        const uint32_t o = here(e) * 4u;
-        const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(s.p + es[k]), o);
-        const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(s.m + es[k]), o);
-        const GLB f32x4* V4 = (const GLB f32x4*)at(tile_base(s.v + es[k]), o);
-        q[0] = ld_g(P4);
-        q[1] = ld_g(P4 + q2);
-        q[2] = ld_g(M4);
-        q[3] = ld_g(M4 + q2);
-        q[4] = ld_g(V4);
-        q[5] = ld_g(V4 + q2);
-      };
-    sload(0, st[0]);
+    phased_state_load(s, es, 0, e, st[0]);
     // the grid barrier lets the workgroups go once kPhasedQuorum of them have arrived: waiting for the
     // last few costs more than their reads overlapping the others' writes
     phased_grid_barrier(counter, (uint32_t)sc * gridDim.x + phased_quorum(gridDim.x), max_polls);
-    {
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        {
-          if (k + 1 < K) sload(k + 1, st[(k + 1) & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-          const f32x4* q = st[k & 1];
-          float p[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
-          float m[8] = {q[2].x, q[2].y, q[2].z, q[2].w, q[3].x, q[3].y, q[3].z, q[3].w};
-          float v[8] = {q[4].x, q[4].y, q[4].z, q[4].w, q[5].x, q[5].y, q[5].z, q[5].w};
-          upd(acc[k], p, m, v);
-          const TileOut h = tile_outputs(p, m, v);
-          const uint32_t o = here(e) * 4u;
-          GLB f32x4* P4 = (GLB f32x4*)at(tile_base(s.p + es[k]), o);
-          GLB f32x4* M4 = (GLB f32x4*)at(tile_base(s.m + es[k]), o);
-          GLB f32x4* V4 = (GLB f32x4*)at(tile_base(s.v + es[k]), o);
-          st_g(P4, h.p0);
-          st_g(P4 + q2, h.p1);
-          st_g(M4, h.m0);
-          st_g(M4 + q2, h.m1);
-          st_g(V4, h.v0);
-          st_g(V4 + q2, h.v1);
-          GLB u32x2* B2 = (GLB u32x2*)at(tile_base(s.b + es[k]), here(e) * 2u);
-          st_g(B2, h.b0);
-          st_g(B2 + q2, h.b1);
-        }
-      }
-    }
+    phased_update(s, es, e, acc, st, upd);
   }
   return nsup * per;
 }

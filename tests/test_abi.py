@@ -312,7 +312,7 @@ def test_write_window_query():
     (flat, N = 64) and 4096 / 256 (pass 1), on shards of at least 2^25 parameters."""
     assert zs.write_window("flat", 64, 1_093_750_000) == (0, 0)
     assert zs.write_window("reduce", 64, 1_093_750_000) == (0, 0)
-    assert zs.write_window("list", 64, 1_093_750_000) == (4096, 512)   # list plans keep the windows
+    assert zs.write_window("list", 64, 1_093_750_000) == (0, 0)   # list plans: the flat step's schedule
     assert zs.write_window("list", 64, (1 << 25) - 1) == (0, 0)
     assert zs.write_window("list", 8, 1 << 30) == (0, 0)
     try:
@@ -331,6 +331,8 @@ def test_write_window_query():
             assert zs.write_window(kernel, 16, 1 << 30) == (1024, 128)
             assert zs.write_window(kernel, 5, 1 << 30) == (1024, 128)
             zs.set_write_window(0)
+        assert zs.write_window("list", 64, 1 << 30) == (4096, 512)   # a list plan as a flat shard of its size
+        assert zs.write_window("list", 64, (1 << 25) - 1) == (0, 0)
         # the flat step's open length follows the writes' share of the bytes
         assert zs.write_window("flat", 48, 1 << 30) == (4096, 640)
         assert zs.write_window("flat", 128, 1 << 30) == (4096, 512)

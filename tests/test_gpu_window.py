@@ -203,9 +203,10 @@ LIST_SIZES = (1, 9, 0, 5_000, 4_097, 70_001, (1 << 20) + 3, 3_000_001, 10_000_00
 
 @pytest.mark.parametrize("N,window", [(64, (0, 0)), (50, (0, 0)), (8, (256, 32))])
 def test_windowed_list_plan_matches_oracle(env, orc, N, window):
-    """List plans under write windows (the library default at N = 64 and at the run-time count 50, a forced
-    window at N = 8): one set for every tensor, then hyperparameter groups, then the device step, each
-    bit-identical to the oracle applied tensor by tensor (the gaps between tensors untouched)."""
+    """List plans under write windows (the windowed schedule's default window at N = 64 and at the
+    run-time count 50, a forced window at N = 8): one set for every tensor, then hyperparameter groups, then
+    the device step, each bit-identical to the oracle applied tensor by tensor (the gaps between tensors
+    untouched)."""
     from synth import workloads as W
     from tests.test_gpu_list import arena_case, oracle_list, oracle_list_groups
 
@@ -219,10 +220,12 @@ def test_windowed_list_plan_matches_oracle(env, orc, N, window):
                     B=d["B"].cpu().numpy().view(np.uint16))
 
     zs.set_write_window(*window)
+    zs.set_flat_schedule("windowed")
     try:
         with zs.ListPlan.from_arenas(w.sizes, offsets, d["G"], d["P"], d["M"], d["V"], d["B"]) as plan:
-            print(f"windowed list: N={N} window={window} (flat step takes {zs.write_window('flat', N, w.n_params)})",
+            print(f"windowed list: N={N} window={window} (takes {zs.write_window('list', N, w.n_params)})",
                   flush=True)
+            assert zs.write_window("list", N, w.n_params) != (0, 0)
             plan.step(w.hp(), w.step)
             torch.cuda.synchronize()
             ref = oracle_list(orc, w, host, offsets, w.step, w.hp())
@@ -245,11 +248,14 @@ def test_windowed_list_plan_matches_oracle(env, orc, N, window):
             assert src.status == 0
     finally:
         zs.set_write_window(0)
+        zs.set_flat_schedule("auto")
 
 
-@pytest.mark.parametrize("N,window", [(64, (0, 0)), (8, (256, 32))])
-def test_windowed_list_plan_with_peels_and_scalar_tensors(env, orc, N, window):
-    """List plans under write windows on tensors in buffers of their own: 2^25 + 1,003 parameters whose
+@pytest.mark.parametrize("N,window,schedule", [(64, (0, 0), "windowed"), (8, (256, 32), "windowed"),
+                                               (64, (0, 0), "phased"), (50, (0, 0), "phased")])
+def test_windowed_list_plan_with_peels_and_scalar_tensors(env, orc, N, window, schedule):
+    """List plans under write windows (and on the phased schedule) on tensors in buffers of their own:
+    2^25 + 1,003 parameters whose
     arrays all start 3 elements past a 16-byte boundary (a 5-element head peel, whole tiles, a partial
     tile and tail elements), 100 parameters with that phase, and 10,000 parameters whose arrays share no
     16-byte phase (stepped element by element).  Bit-identical to the oracle per tensor, over two steps."""
@@ -280,10 +286,14 @@ def test_windowed_list_plan_with_peels_and_scalar_tensors(env, orc, N, window):
         tensors.append(zs.ShardTensor(g, p, m, v, b))
     assert sum(n_of) >= 1 << 25
     zs.set_write_window(*window)
+    zs.set_flat_schedule(schedule)
     try:
-        assert zs.write_window("list", N, sum(n_of))[0] > 0, "the plan takes write windows"
+        if schedule == "windowed":
+            assert zs.write_window("list", N, sum(n_of))[0] > 0, "the plan takes write windows"
+        else:
+            assert zs.flat_schedule(N, sum(n_of)) == "phased"
         with zs.ListPlan(tensors, N) as plan:
-            print(f"windowed list, peels and scalar tensors: N={N} window={window}", flush=True)
+            print(f"list, peels and scalar tensors: N={N} window={window} schedule={schedule}", flush=True)
             for t in (3, 4):
                 plan.step(HP_WD, t)
                 torch.cuda.synchronize()
@@ -295,3 +305,4 @@ def test_windowed_list_plan_with_peels_and_scalar_tensors(env, orc, N, window):
                     h.update(P=rP, M=rM, V=rV)
     finally:
         zs.set_write_window(0)
+        zs.set_flat_schedule("auto")
