@@ -45,9 +45,9 @@ struct ProbeArgs {
 
 template <int NT, bool WRITE>
 __global__ __launch_bounds__(kFlatBlock) void pattern_kernel(const ProbeArgs<NT> a) {
-  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  constexpr uint32_t q2 = Layout::kSecond / 4;
   const int64_t e0 = (int64_t)blockIdx.x * (kFlatBlock * 8);
-  const uint32_t e = Layout<true>::first();
+  const uint32_t e = Layout::first();
   f32x4 pa, pb, ma, mb, va, vb;
   {
     const uint32_t o = here(e) * 4u;
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kFlatBlock) void pattern_kernel(const ProbeArgs<NT>
   }
   auto G = [&](int r) { return tile_base(a.g[r] + e0); };
   float acc[8];
-  reduce_replicas<NT, true>(G, NT, e, acc);
+  reduce_replicas<NT>(G, NT, e, acc);
   float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
   float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
   float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kFlatBlock) void pattern_kernel(const ProbeArgs<NT>
     st_g(V4 + q2, (f32x4){v[4] + m[4], v[5] + m[5], v[6] + m[6], v[7] + m[7]});
     GLB u32x2* B2 = (GLB u32x2*)at(tile_base(a.b + e0), here(e) * 2u);
     st_g(B2, (u32x2){pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])});
-    st_g(B2 + Layout<true>::kSecond / 4, (u32x2){pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])});
+    st_g(B2 + Layout::kSecond / 4, (u32x2){pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])});
   } else {
     float x = 0.0f;
 #pragma unroll
@@ -98,8 +98,8 @@ __global__ __launch_bounds__(kFlatBlock) void pattern_kernel(const ProbeArgs<NT>
 template <int NT>
 __global__ __launch_bounds__(kFlatBlock) void pattern_window_kernel(const ProbeArgs<NT> a, int64_t tiles,
                                                                     const WriteWindow w) {
-  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
-  const uint32_t e = Layout<true>::first();
+  constexpr uint32_t q2 = Layout::kSecond / 4;
+  const uint32_t e = Layout::first();
   FlatShape s{};
   s.p = a.p;
   s.m = a.m;
@@ -181,11 +181,11 @@ hipError_t go(const uint16_t* const* g, int64_t tiles, float* p, float* m, float
 // the workgroup holding the last tile also copies the tail elements.
 __global__ __launch_bounds__(kFlatBlock) void copy_kernel(const float* __restrict__ src, float* __restrict__ dst,
                                                           int64_t t0, int64_t n) {
-  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  constexpr uint32_t q2 = Layout::kSecond / 4;
   const int64_t t = t0 + blockIdx.x;
   const int64_t e0 = t * (kFlatBlock * 8);
   if (e0 + kFlatBlock * 8 <= n) {
-    const uint32_t o = here(Layout<true>::first()) * 4u;
+    const uint32_t o = here(Layout::first()) * 4u;
     const GLB f32x4* S = (const GLB f32x4*)at(tile_base(src + e0), o);
     GLB f32x4* D = (GLB f32x4*)at(tile_base(dst + e0), o);
     const f32x4 x = ld_g(S), y = ld_g(S + q2);

@@ -193,41 +193,33 @@ __device__ __forceinline__ void widen_first(float (&acc)[8], const u32x4 w) {
   acc[7] = h_hi<FMT>(w.w);
 }
 
-// Lane layouts of an 8-parameter group inside a tile (one group per thread).
-//  Split (full tiles): lane l of wave q owns the quads at tile elements
-//    512q + 4l and 512q + 256 + 4l.  Every access instruction of a wave then
-//    covers whole contiguous lines: 1 KiB per fp32 access, 512 B per bf16
-//    access (8 bytes per lane).  Writes in particular go out as full lines.
-//  Contiguous (the one partial tile of a shard): thread t owns the 8
-//    elements 8t..8t+7; used where only a prefix of the tile's groups exists.
-template <bool SPLIT>
+// Lane layout of a wave tile (one 8-parameter group per thread): lane l of
+// wave q owns the quads at tile elements 512q + 4l and 512q + 256 + 4l.  Every
+// access instruction of a wave then covers whole contiguous lines: 1 KiB per
+// fp32 access, 512 B per bf16 access (8 bytes per lane).  Writes in particular
+// go out as full lines.  A partial tile keeps the layout, with a predicate per
+// quad (partial_step).
 struct Layout {
-  static __device__ __forceinline__ uint32_t first() {
-    return SPLIT ? 512u * (threadIdx.x >> 6) + 4u * (threadIdx.x & 63u) : 8u * threadIdx.x;
-  }
-  static constexpr uint32_t kSecond = SPLIT ? 256u : 4u;  // element distance to the 2nd quad
+  static __device__ __forceinline__ uint32_t first() { return 512u * (threadIdx.x >> 6) + 4u * (threadIdx.x & 63u); }
+  static constexpr uint32_t kSecond = 256u;  // element distance to the 2nd quad
 };
 
 
 // Replica r's 8 gradient values (bf16 or fp16 bits) of this lane's group.  G(r) is replica r's
 // gradient pointer advanced to the tile (wave-uniform, SGPRs); `e` is the
 // lane's first element in the tile.
-template <bool SPLIT, class GP>
+template <class GP>
 __device__ __forceinline__ u32x4 ld_grad(GP G, int r, uint32_t e) {
-  if constexpr (SPLIT) {
-    const GLB u32x2* a = (const GLB u32x2*)at(G(r), here(e) * 2u);
-    const u32x2 x = ld_g(a), y = ld_g(a + Layout<true>::kSecond / 4);
-    return (u32x4){x.x, x.y, y.x, y.y};
-  } else {
-    return ld_g((const GLB u32x4*)at(G(r), here(e) * 2u));
-  }
+  const GLB u32x2* a = (const GLB u32x2*)at(G(r), here(e) * 2u);
+  const u32x2 x = ld_g(a), y = ld_g(a + Layout::kSecond / 4);
+  return (u32x4){x.x, x.y, y.x, y.y};
 }
 
-template <bool SPLIT, class GP>
+template <class GP>
 __device__ __forceinline__ void load_batch(GP G, int r, int N, uint32_t e, u32x4 (&w)[kBatch]) {
 #pragma unroll
   for (int j = 0; j < kBatch; ++j)
-    if (r + j < N) w[j] = ld_grad<SPLIT>(G, r + j, e);
+    if (r + j < N) w[j] = ld_grad(G, r + j, e);
 }
 
 // Adds a batch, then pins the accumulators: the sums must be formed here, not
@@ -247,31 +239,31 @@ __device__ __forceinline__ void add_batch(float (&acc)[8], const u32x4 (&w)[kBat
 // batch is in flight while the current one is added (two register buffers),
 // and scheduling barriers stop the compiler from hoisting later batches,
 // which would buy nothing but registers.
-template <int NT, bool SPLIT, int FMT = kBF16, class GP>
+template <int NT, int FMT = kBF16, class GP>
 __device__ __forceinline__ void reduce_replicas(GP G, int N, uint32_t e, float (&acc)[8]) {
-  widen_first<FMT>(acc, ld_grad<SPLIT>(G, 0, e));
+  widen_first<FMT>(acc, ld_grad(G, 0, e));
   if constexpr (NT > 0) {
     constexpr int NB = (NT - 1 + kBatch - 1) / kBatch;
     u32x4 w[2][kBatch];
-    if constexpr (NB > 0) load_batch<SPLIT>(G, 1, NT, e, w[0]);
+    if constexpr (NB > 0) load_batch(G, 1, NT, e, w[0]);
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      if (k + 1 < NB) load_batch<SPLIT>(G, 1 + (k + 1) * kBatch, NT, e, w[(k + 1) & 1]);
+      if (k + 1 < NB) load_batch(G, 1 + (k + 1) * kBatch, NT, e, w[(k + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
       add_batch<FMT>(acc, w[k & 1], 1 + k * kBatch, NT);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     u32x4 wa[kBatch], wb[kBatch];
-    if (N > 1) load_batch<SPLIT>(G, 1, N, e, wa);
+    if (N > 1) load_batch(G, 1, N, e, wa);
 #pragma unroll 1
     for (int r0 = 1; r0 < N; r0 += 2 * kBatch) {
       const int r1 = r0 + kBatch, r2 = r1 + kBatch;
-      if (r1 < N) load_batch<SPLIT>(G, r1, N, e, wb);
+      if (r1 < N) load_batch(G, r1, N, e, wb);
       __builtin_amdgcn_sched_barrier(0);
       add_batch<FMT>(acc, wa, r0, N);
       __builtin_amdgcn_sched_barrier(0);
-      if (r2 < N) load_batch<SPLIT>(G, r2, N, e, wa);
+      if (r2 < N) load_batch(G, r2, N, e, wa);
       __builtin_amdgcn_sched_barrier(0);
       if (r1 < N) add_batch<FMT>(acc, wb, r1, N);
       __builtin_amdgcn_sched_barrier(0);
@@ -302,8 +294,8 @@ __device__ __forceinline__ TileOut tile_outputs(const float (&p)[8], const float
 
 // Stores a full tile's outputs at tile element e0 (split layout).
 __device__ __forceinline__ void store_tile(const FlatShape& s, int64_t e0, const TileOut& h) {
-  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
-  const uint32_t e = Layout<true>::first();
+  constexpr uint32_t q2 = Layout::kSecond / 4;
+  const uint32_t e = Layout::first();
   const uint32_t o = here(e) * 4u;
   GLB f32x4* P4 = (GLB f32x4*)at(tile_base(s.p + e0), o);
   GLB f32x4* M4 = (GLB f32x4*)at(tile_base(s.m + e0), o);
@@ -316,7 +308,7 @@ __device__ __forceinline__ void store_tile(const FlatShape& s, int64_t e0, const
   st_g(V4 + q2, h.v1);
   GLB u32x2* B2 = (GLB u32x2*)at(tile_base(s.b + e0), here(e) * 2u);
   st_g(B2, h.b0);
-  st_g(B2 + Layout<true>::kSecond / 4, h.b1);
+  st_g(B2 + Layout::kSecond / 4, h.b1);
 }
 
 // The device's 100 MHz real-time counter, one clock for the whole chip.
@@ -383,10 +375,10 @@ struct HeldMeans {
   f32x4 g0[K], g1[K];
 
   __device__ __forceinline__ static void store(float* gbar, int64_t e0, f32x4 a, f32x4 b) {
-    const uint32_t o = here(Layout<true>::first()) * 4u;
+    const uint32_t o = here(Layout::first()) * 4u;
     GLB f32x4* O = (GLB f32x4*)at(tile_base(gbar + e0), o);
     st_g(O, a);
-    st_g(O + Layout<true>::kSecond / 4, b);
+    st_g(O + Layout::kSecond / 4, b);
   }
   __device__ __forceinline__ void flush(float* gbar) {
 #pragma unroll
@@ -426,20 +418,20 @@ struct HeldMeans {
 template <int NT, int CHK, int FMT = kBF16, class GP, class HOOK>
 __device__ __forceinline__ void reduce_replicas_hooked(GP G, uint32_t e, float (&acc)[8], HOOK&& hook) {
   static_assert(NT > 0 && kBatch % CHK == 0, "templated replica count, CHK divides the batch");
-  widen_first<FMT>(acc, ld_grad<true>(G, 0, e));
+  widen_first<FMT>(acc, ld_grad(G, 0, e));
   constexpr int NB = (NT - 1 + kBatch - 1) / kBatch;
   if constexpr (NB == 0) {
     hook();
   } else {
     u32x4 w[2][kBatch];
-    load_batch<true>(G, 1, NT, e, w[0]);
+    load_batch(G, 1, NT, e, w[0]);
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       if (k + 1 < NB) {
         const int r0 = 1 + (k + 1) * kBatch;
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-          if (r0 + j < NT) w[(k + 1) & 1][j] = ld_grad<true>(G, r0 + j, e);
+          if (r0 + j < NT) w[(k + 1) & 1][j] = ld_grad(G, r0 + j, e);
           if (CHK > 1 && (j + 1) % (kBatch / CHK) == 0 && j + 1 < kBatch) {
             __builtin_amdgcn_sched_barrier(0);
             hook();
@@ -461,20 +453,20 @@ __device__ __forceinline__ void reduce_replicas_hooked(GP G, uint32_t e, float (
 // with hook() after each batch's loads are issued.
 template <int FMT = kBF16, class GP, class HOOK>
 __device__ __forceinline__ void reduce_replicas_hooked_rt(GP G, int N, uint32_t e, float (&acc)[8], HOOK&& hook) {
-  widen_first<FMT>(acc, ld_grad<true>(G, 0, e));
+  widen_first<FMT>(acc, ld_grad(G, 0, e));
   u32x4 wa[kBatch], wb[kBatch];
-  if (N > 1) load_batch<true>(G, 1, N, e, wa);
+  if (N > 1) load_batch(G, 1, N, e, wa);
   hook();
 #pragma unroll 1
   for (int r0 = 1; r0 < N; r0 += 2 * kBatch) {
     const int r1 = r0 + kBatch, r2 = r1 + kBatch;
-    if (r1 < N) load_batch<true>(G, r1, N, e, wb);
+    if (r1 < N) load_batch(G, r1, N, e, wb);
     __builtin_amdgcn_sched_barrier(0);
     hook();
     __builtin_amdgcn_sched_barrier(0);
     add_batch<FMT>(acc, wa, r0, N);
     __builtin_amdgcn_sched_barrier(0);
-    if (r2 < N) load_batch<true>(G, r2, N, e, wa);
+    if (r2 < N) load_batch(G, r2, N, e, wa);
     __builtin_amdgcn_sched_barrier(0);
     hook();
     __builtin_amdgcn_sched_barrier(0);

@@ -56,13 +56,14 @@ namespace {
 
 using namespace dev;
 
-// One 8-parameter group of the tile starting at element e0 (wave-uniform,
-// 16-byte aligned in every array).  G(r) returns replica r's gradient pointer
-// advanced to e0.
-template <int NT, bool SPLIT, class GP>
+// One 8-parameter group of the whole wave tile starting at element e0
+// (wave-uniform, 16-byte aligned in every array): the lane's quads at tile
+// elements e and e + 256 (see Layout).  G(r) returns replica r's gradient
+// pointer advanced to e0.
+template <int NT, class GP>
 __device__ __forceinline__ void group_step_at(GP G, int N, int64_t e0, uint32_t e, const FlatShape& s,
                                               const Scalars& c) {
-  constexpr uint32_t q2 = Layout<SPLIT>::kSecond / 4;  // second quad, in f32x4 units
+  constexpr uint32_t q2 = Layout::kSecond / 4;  // second quad, in f32x4 units
   f32x4 pa, pb, ma, mb, va, vb;
   {
     const uint32_t o = here(e) * 4u;  // byte offset in fp32 arrays
@@ -78,7 +79,7 @@ __device__ __forceinline__ void group_step_at(GP G, int N, int64_t e0, uint32_t 
   }
 
   float acc[8];
-  reduce_replicas<NT, SPLIT>(G, N, e, acc);
+  reduce_replicas<NT>(G, N, e, acc);
 
   float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
   float m[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
@@ -97,21 +98,16 @@ __device__ __forceinline__ void group_step_at(GP G, int N, int64_t e0, uint32_t 
   st_g(M4 + q2, (f32x4){m[4], m[5], m[6], m[7]});
   st_g(V4, (f32x4){v[0], v[1], v[2], v[3]});
   st_g(V4 + q2, (f32x4){v[4], v[5], v[6], v[7]});
-  if constexpr (SPLIT) {
-    GLB u32x2* B2 = (GLB u32x2*)at(tile_base(s.b + e0), here(e) * 2u);
-    st_g(B2, (u32x2){pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])});
-    st_g(B2 + Layout<true>::kSecond / 4, (u32x2){pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])});
-  } else {
-    st_g((GLB u32x4*)at(tile_base(s.b + e0), here(e) * 2u),
-         (u32x4){pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])});
-  }
+  GLB u32x2* B2 = (GLB u32x2*)at(tile_base(s.b + e0), here(e) * 2u);
+  st_g(B2, (u32x2){pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])});
+  st_g(B2 + Layout::kSecond / 4, (u32x2){pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])});
 }
 
 // The same with the lane's offset in the tile taken from the workgroup's
 // layout (one tile per workgroup).
-template <int NT, bool SPLIT, class GP>
+template <int NT, class GP>
 __device__ __forceinline__ void group_step(GP G, int N, int64_t e0, const FlatShape& s, const Scalars& c) {
-  group_step_at<NT, SPLIT>(G, N, e0, Layout<SPLIT>::first(), s, c);
+  group_step_at<NT>(G, N, e0, Layout::first(), s, c);
 }
 
 // A partial wave tile: `groups` (1..63) 8-groups from element e0, in the split
@@ -127,7 +123,7 @@ __device__ __forceinline__ void group_step(GP G, int N, int64_t e0, const FlatSh
 template <int NT, class GP>
 __device__ __forceinline__ void partial_step(GP G, int N, int64_t e0, int64_t groups, const FlatShape& s,
                                              const Scalars& c) {
-  constexpr uint32_t q2 = Layout<true>::kSecond / 4;  // second quad, in f32x4 units
+  constexpr uint32_t q2 = Layout::kSecond / 4;  // second quad, in f32x4 units
   const uint32_t t = threadIdx.x & 63u;
   const uint32_t e = 4u * t;
   const bool qa = (int64_t)t < 2 * groups, qb = (int64_t)t + 64 < 2 * groups;
@@ -205,7 +201,7 @@ __device__ __forceinline__ void tiles(GP0 G0, int N, int64_t g_begin, int64_t g_
     const int64_t e0 = s.head + 8 * gt;
     auto G = [&](int r) { return tile_base(G0(r) + e0); };
     if (gt + BLOCK <= g_end)
-      group_step<NT, true>(G, N, e0, s, c);
+      group_step<NT>(G, N, e0, s, c);
     else
       partial_step<NT>(G, N, e0, g_end - gt, s, c);
   }
@@ -285,8 +281,8 @@ __global__ __launch_bounds__(kFlatBlock) void flat_window_kernel(const FlatArgs<
   if (!step_scalars(a.r, c)) return;
   const int N = NT > 0 ? NT : c.n_rep;
   const FlatShape& s = a.s;
-  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
-  const uint32_t e = Layout<true>::first();
+  constexpr uint32_t q2 = Layout::kSecond / 4;
+  const uint32_t e = Layout::first();
   const int64_t full = s.nvec / kFlatBlock;  // whole tiles
   HeldTiles held;
   auto check = [&]() { held.check(s, w); };
@@ -380,7 +376,7 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void flat_phased_kernel(c
   for (int64_t t = covered + gw; t < full; t += nw) {
     const int64_t e0 = s.head + 8 * kFlatBlock * t;
     auto G = [&](int r) { return tile_base(a.g[r] + e0); };
-    group_step_at<NT, true>(G, N, e0, e, s, c);
+    group_step_at<NT>(G, N, e0, e, s, c);
   }
   // the one partial tile and the head and tail elements: the last workgroup's first wave
   if (blockIdx.x == gridDim.x - 1 && wave == 0) {
@@ -485,7 +481,7 @@ __device__ __forceinline__ void list_item_step(const ListWork& w, int N, const S
   const int64_t e0 = s.head + 8 * w.lo;
   auto G = [&](int r) { return tile_base(G0(r) + e0); };
   if (w.hi - w.lo == kFlatBlock)
-    group_step_at<NT, true>(G, N, e0, 4u * lane, s, c);
+    group_step_at<NT>(G, N, e0, 4u * lane, s, c);
   else
     partial_step<NT>(G, N, e0, w.hi - w.lo, s, c);
   if (w.first) {
@@ -580,13 +576,13 @@ __global__ __launch_bounds__(kFlatBlock) void list_window_kernel(const int32_t* 
                                                              const uint16_t* const* __restrict__ gptrs,
                                                              const ListScalars<NG> sc, const StepRef ref,
                                                              const WriteWindow w) {
-  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  constexpr uint32_t q2 = Layout::kSecond / 4;
   const int N = NT > 0 ? NT : sc.c[0].n_rep;
   Scalars one = sc.c[0];
   if constexpr (NG == 1) {
     if (!step_scalars(ref, one)) return;
   }
-  const uint32_t e = Layout<true>::first();
+  const uint32_t e = Layout::first();
   HeldListTiles held;
   auto check = [&]() { held.check(w); };
   for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {

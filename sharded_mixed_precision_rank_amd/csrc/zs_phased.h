@@ -49,7 +49,7 @@ __device__ __forceinline__ uint32_t phased_quorum(uint32_t grid) {
 template <int NT, int FMT, int K, class GP>
 __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&es)[K], uint32_t e,
                                                   float (&acc)[K][8], bool active = true) {
-  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  constexpr uint32_t q2 = Layout::kSecond / 4;
   u32x2 w0[K][2], w1[K][2];
   auto load = [&](int r, u32x2(&w)[K][2]) {
     if (!active) return;
@@ -108,7 +108,7 @@ __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&
 template <int K>
 __device__ __forceinline__ void phased_state_load(const FlatShape& s, const int64_t (&es)[K], int k, uint32_t e,
                                                   f32x4 (&q)[6]) {
-  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  constexpr uint32_t q2 = Layout::kSecond / 4;
   const uint32_t o = here(e) * 4u;
   const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(s.p + es[k]), o);
   const GLB f32x4* M4 = (const GLB f32x4*)at(tile_base(s.m + es[k]), o);
@@ -128,7 +128,7 @@ __device__ __forceinline__ void phased_state_load(const FlatShape& s, const int6
 template <int K, class UPD>
 __device__ __forceinline__ void phased_update(const FlatShape& s, const int64_t (&es)[K], uint32_t e,
                                               float (&acc)[K][8], f32x4 (&st)[2][6], UPD&& upd) {
-  constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+  constexpr uint32_t q2 = Layout::kSecond / 4;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     if (k + 1 < K) phased_state_load(s, es, k + 1, e, st[(k + 1) & 1]);

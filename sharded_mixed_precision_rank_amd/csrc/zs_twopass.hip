@@ -121,15 +121,15 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs<NT> a) 
     if (!a.scalar_only && e0 + kTile <= a.n) {
       // full tile, whole-line layout
       auto G = [&](int r) { return tile_base(G0(r) + e0); };
-      const uint32_t e = Layout<true>::first();
+      const uint32_t e = Layout::first();
       float acc[8];
-      reduce_replicas<NT, true, FMT>(G, N, e, acc);
+      reduce_replicas<NT, FMT>(G, N, e, acc);
       float g[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) g[k] = mean_of<NT>(acc[k], c) * inv;
       GLB f32x4* O = (GLB f32x4*)at(tile_base(a.gbar + e0), here(e) * 4u);
       st_g(O, (f32x4){g[0], g[1], g[2], g[3]});
-      st_g(O + Layout<true>::kSecond / 4, (f32x4){g[4], g[5], g[6], g[7]});
+      st_g(O + Layout::kSecond / 4, (f32x4){g[4], g[5], g[6], g[7]});
 #pragma unroll
       for (int k = 0; k < 8; ++k) sq += (double)g[k] * (double)g[k];
     } else {
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kBlock) void reduce_window_kernel(const ReduceArgs<
   const float inv = unscale_factor(a);
   auto G0 = [&](int r) { return a.g[r]; };
   const int64_t full = (a.n - a.head) / kTile;  // whole tiles (the shard has a common alignment)
-  const uint32_t e = Layout<true>::first();
+  const uint32_t e = Layout::first();
   HeldMeans<kHeldMeans> held;
   auto check = [&]() { held.check(a.gbar, w); };
   for (int64_t t = blockIdx.x; t < full; t += gridDim.x) {
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void reduce_phased_kernel
       for (int j = 0; j < 8; ++j) g[j] = mean_of<NT>(acc[k][j], c) * inv;
       GLB f32x4* O = (GLB f32x4*)at(tile_base(a.gbar + es[k]), here(e) * 4u);
       st_g(O, (f32x4){g[0], g[1], g[2], g[3]});
-      st_g(O + Layout<true>::kSecond / 4, (f32x4){g[4], g[5], g[6], g[7]});
+      st_g(O + Layout::kSecond / 4, (f32x4){g[4], g[5], g[6], g[7]});
       double sq = 0.0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) sq += (double)g[j] * (double)g[j];
@@ -332,8 +332,8 @@ __global__ __launch_bounds__(BLK) void gbar_kernel(const GbarArgs a) {
   for (int64_t t = a.t_lo + blockIdx.x; t < a.t_hi; t += gridDim.x) {
     if (!s.scalar_only && (t + 1) * BLK <= s.nvec) {
       const int64_t e0 = s.head + t * kT;
-      const uint32_t e = Layout<true>::first();
-      constexpr uint32_t q2 = Layout<true>::kSecond / 4;
+      const uint32_t e = Layout::first();
+      constexpr uint32_t q2 = Layout::kSecond / 4;
       const uint32_t o = here(e) * 4u;
       const GLB f32x4* G4 = (const GLB f32x4*)at(tile_base(a.gbar + e0), o);
       const GLB f32x4* P4 = (const GLB f32x4*)at(tile_base(s.p + e0), o);
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(BLK) void gbar_kernel(const GbarArgs a) {
       st_g(Vo + q2, (f32x4){v[4], v[5], v[6], v[7]});
       GLB u32x2* B2 = (GLB u32x2*)at(tile_base(s.b + e0), here(e) * 2u);
       st_g(B2, (u32x2){pack_half<OFMT>(p[0], p[1]), pack_half<OFMT>(p[2], p[3])});
-      st_g(B2 + Layout<true>::kSecond / 4, (u32x2){pack_half<OFMT>(p[4], p[5]), pack_half<OFMT>(p[6], p[7])});
+      st_g(B2 + Layout::kSecond / 4, (u32x2){pack_half<OFMT>(p[4], p[5]), pack_half<OFMT>(p[6], p[7])});
     } else {
       // partial tile (vector shards) or any tile of a shard without common alignment
       const int64_t e0 = s.scalar_only ? t * kT : s.head + t * kT;
