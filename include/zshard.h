@@ -501,12 +501,15 @@ ZS_API zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* 
                            was set), on shards of at least 2^25 parameters
                            (ZS_SCHEDULE_STREAM below).
      ZS_SCHEDULE_PHASED:   one persistent workgroup of 12 waves per compute
-                           unit; the shard goes in super-chunks of 8 tiles per
+                           unit; the shard goes in super-chunks of 12 tiles
+                           per wave (pass 1: 10), then a part super-chunk of
+                           fewer tiles per wave when at least half a
+                           super-chunk's tiles are left, the rest one tile per
                            wave.  First every wave reads all N replicas of its
                            tiles into register accumulators, the workgroup's
                            waves kept on the same replicas, so the device
-                           reads one or two replica streams at a time over one
-                           contiguous region each; then, after a grid barrier
+                           reads one replica stream at a time over one
+                           contiguous region; then, after a grid barrier
                            (released once 95% of the workgroups have
                            arrived), it reads master, m and v and writes the
                            four outputs of the super-chunk.  Any shard of at least

@@ -193,6 +193,31 @@ __device__ __forceinline__ void widen_first(float (&acc)[8], const u32x4 w) {
   acc[7] = h_hi<FMT>(w.w);
 }
 
+// A value every lane of the wave holds, moved to scalar registers.  The
+// compiler computes some wave-uniform values (64-bit divisions, loads through
+// a vector index) in vector registers; where one feeds an SGPR-pinned tile
+// base it must be read back into scalar registers first.
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+}
+
+template <class T>
+__device__ __forceinline__ T* uniform_fptr(T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Lane layout of a wave tile (one 8-parameter group per thread): lane l of
 // wave q owns the quads at tile elements 512q + 4l and 512q + 256 + 4l.  Every
 // access instruction of a wave then covers whole contiguous lines: 1 KiB per

@@ -331,22 +331,27 @@ __global__ __launch_bounds__(kFlatBlock) void flat_window_kernel(const FlatArgs<
 // ---------------------------------------------------------------- phased schedule
 // The flat step in super-chunks of (workgroups x kPhasedWaves x kPhasedTiles)
 // whole tiles.  Phase A: every wave streams replicas 0..N-1 (rank order) of
-// its kPhasedTiles tiles into fp32 register accumulators; the waves of a
-// workgroup meet at a workgroup barrier every two replicas, and all
-// workgroups start the phase together, so at any moment the chip reads one or
-// two replica streams, each over one contiguous region, instead of all N
-// interleaved (on this memory system reading 2 streams at once runs about 9%
-// faster than reading 64).  The workgroups then meet at a grid barrier, which
-// lets them go once kPhasedQuorumPct percent of them have arrived.
+// its kPhasedTiles tiles into fp32 register accumulators, one replica's tiles
+// in flight at a time; the waves of a workgroup meet at a workgroup barrier
+// every two replicas, and all workgroups start the phase together, so at any
+// moment the chip reads one or two replica streams, each over one contiguous
+// region, instead of all N interleaved (on this memory system reading 2
+// streams at once runs about 9% faster than reading 64).  The workgroups then
+// meet at a grid barrier, which lets them go once kPhasedQuorumPct percent of
+// them have arrived.  Each super-chunk costs about 8 us beyond its bytes (the
+// barrier and the phases' ramps), so the super-chunk is as large as the
+// registers allow: 12 tiles per wave, 18.9M parameters on 256 compute units.
 // Phase B: each wave reads its tiles' master, m and v, applies AdamW and
 // writes master, m, v and the bf16 copy, so the super-chunk's 14 bytes per
 // parameter of writes go out together instead of trickling out beside the
 // replica reads.  Slot k of wave w in super-chunk c is tile
 // c*T + k*W + w (T tiles per super-chunk, W waves in the grid): in phase B
-// the grid walks each array in one contiguous front.  Only whole super-chunks
-// run phased; the whole tiles after them go one per wave, stored as each is
-// done, and the last workgroup's first wave takes the partial tile and the
-// head and tail elements.
+// the grid walks each array in one contiguous front.  After the whole
+// super-chunks, a part super-chunk of fewer tiles per wave runs phased when at
+// least half a super-chunk's tiles are left (phased_part_tiles); the whole
+// tiles after that go one per wave, stored as each is done, and the last
+// workgroup's first wave takes the partial tile and the head and tail
+// elements.
 //
 // The barriers only shape the timing.  Every tile's outputs are formed by the
 // same operations as in flat_kernel and stored to its own addresses, so the
@@ -393,27 +398,6 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void flat_phased_kernel(c
 
 __global__ void step_advance_kernel(int64_t* step) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *step = *step + 1;
-}
-
-__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
-  const uint64_t u = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
-}
-
-template <class T>
-__device__ __forceinline__ T* uniform_fptr(T* p) {
-  const uint64_t u = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // NG sets of folded scalars: one for every tensor (NG = 1), or one per
@@ -633,11 +617,14 @@ __global__ __launch_bounds__(kFlatBlock) void list_window_kernel(const int32_t* 
 
 // List plans on the phased schedule (see flat_phased_kernel): one workgroup of
 // kPhasedWaves waves per compute unit; super-chunk c gives wave w the
-// kPhasedTiles consecutive items from (c*W + w)*kPhasedTiles (W waves in the
+// kListPhasedTiles (8) consecutive items from (c*W + w)*8 (W waves in the
 // grid).  When they are whole tiles of one tensor (all but a few waves in a
 // list of large tensors), the wave streams their replicas into its
-// accumulators in phase A (the flat step's own code; the tensor's replica
-// pointers come from the plan's table, one scalar load per replica) and
+// accumulators in phase A (the flat step's own code, with two replicas in
+// flight: with one, the per-wave descriptors and the fully known replica
+// count left too few registers and the kernel spilled inside phase A; the
+// tensor's replica pointers come from the plan's table, one scalar load per
+// replica) and
 // updates them in phase B after the grid barrier.  Otherwise the wave reads
 // nothing in phase A, meets the same barriers, and takes its items one at a
 // time in phase B.  Items after the last whole super-chunk go one per wave.
@@ -646,7 +633,7 @@ template <int NT, int NG>
 __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void list_phased_kernel(
     const int32_t* __restrict__ items, int32_t n_items, const ListTensor* __restrict__ tensors,
     const uint16_t* const* __restrict__ gptrs, const ListScalars<NG> sc, const StepRef ref, const PhasedCtl ctl) {
-  constexpr int K = kPhasedTiles;
+  constexpr int K = kListPhasedTiles;
   constexpr int64_t kGroups = kTileElemsWave / 8;
   const int N = NT > 0 ? NT : sc.c[0].n_rep;
   Scalars one = sc.c[0];
@@ -698,7 +685,7 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void list_phased_kernel(
     const uint16_t* const* gpt = gptrs + (int64_t)o.t * N;
     auto gp = [&](int r) { return uniform_ptr(gpt[r]); };
     float acc[K][8];
-    phased_accumulate<NT, kBF16, K>(gp, N, es, e, acc, o.whole);
+    phased_accumulate<NT, kBF16, K, 2>(gp, N, es, e, acc, o.whole);
     f32x4 st[2][6];
     if (o.whole) phased_state_load(s, es, 0, e, st[0]);
     phased_grid_barrier(counter, (uint32_t)c * gridDim.x + phased_quorum(gridDim.x), ctl.max_polls);

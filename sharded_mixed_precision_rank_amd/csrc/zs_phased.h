@@ -40,22 +40,30 @@ __device__ __forceinline__ uint32_t phased_quorum(uint32_t grid) {
 
 // Phase A of a super-chunk: replicas 0..N-1 (rank order) of a wave's K tiles
 // (tile k from element es[k], wave-uniform; the split lane layout, lane
-// offset e) into fp32 register accumulators, two replicas in flight, the
-// workgroup's waves meeting at a workgroup barrier every two replicas so that
-// they read the same replicas at about the same time.  gp(r) is replica r's
-// gradient pointer (bf16 or fp16 bits per FMT).
+// offset e) into fp32 register accumulators, the workgroup's waves meeting at
+// a workgroup barrier every two replicas so that they read the same replicas
+// at about the same time.  gp(r) is replica r's gradient pointer (bf16 or
+// fp16 bits per FMT).  DB = 1: one replica's K tiles in flight per wave;
+// DB = 2: two (replica r + 1 requested before replica r is added).  With 12
+// waves per compute unit the second buffer measured no faster, and one buffer
+// leaves the registers for more tiles per super-chunk; the list kernel, whose
+// per-wave descriptors take registers of their own, keeps two buffers of
+// fewer tiles.
 //  A wave with `active` false (wave-uniform) issues no loads and leaves acc
-// undefined, but meets every workgroup barrier with the others.
-template <int NT, int FMT, int K, class GP>
+// undefined, but meets every workgroup barrier with the others.  With PART
+// (DB = 1 only), only tiles 0..kk-1 (kk wave-uniform) are read; the others'
+// accumulators are left undefined.
+template <int NT, int FMT, int K, int DB = 1, bool PART = false, class GP>
 __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&es)[K], uint32_t e,
-                                                  float (&acc)[K][8], bool active = true) {
+                                                  float (&acc)[K][8], bool active = true, int kk = K) {
+  static_assert(DB == 1 || (DB == 2 && !PART), "one or two replica buffers; parts on one");
   constexpr uint32_t q2 = Layout::kSecond / 4;
-  u32x2 w0[K][2], w1[K][2];
   auto load = [&](int r, u32x2(&w)[K][2]) {
     if (!active) return;
     const uint16_t* g = gp(r);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
+      if (PART && k >= kk) continue;
       const GLB u32x2* q = (const GLB u32x2*)at(tile_base(g + es[k]), here(e) * 2u);
       w[k][0] = ld_g(q);
       w[k][1] = ld_g(q + q2);  // the second quad: 256 elements on (64 u32x2)
@@ -64,42 +72,69 @@ __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&
   auto add = [&](const u32x2(&w)[K][2], bool first) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
+      if (PART && k >= kk) continue;
       const float x[8] = {h_lo<FMT>(w[k][0].x), h_hi<FMT>(w[k][0].x), h_lo<FMT>(w[k][0].y), h_hi<FMT>(w[k][0].y),
                           h_lo<FMT>(w[k][1].x), h_hi<FMT>(w[k][1].x), h_lo<FMT>(w[k][1].y), h_hi<FMT>(w[k][1].y)};
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[k][j] = first ? x[j] : acc[k][j] + x[j];
     }
 #pragma unroll
-    for (int k = 0; k < K; ++k)
+    for (int k = 0; k < K; ++k) {
+      if (PART && k >= kk) continue;
 #pragma unroll
       for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(acc[k][j]));
+    }
   };
-  load(0, w0);
-  if constexpr (NT > 0) {
-#pragma unroll
-    for (int r = 0; r < NT; r += 2) {
-      if (r + 1 < NT) load(r + 1, w1);
+  if constexpr (DB == 1) {
+    u32x2 w[K][2];
+    // replica 0 initialises the accumulators; replicas 1..N-1 are added in rank order
+    load(0, w);
+    __builtin_amdgcn_sched_barrier(0);
+    add(w, true);
+    __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](int r) {
+      load(r, w);
       __builtin_amdgcn_sched_barrier(0);
-      add(w0, r == 0);
+      add(w, false);
       __builtin_amdgcn_sched_barrier(0);
-      if (r + 2 < NT) load(r + 2, w0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (r + 1 < NT) add(w1, false);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();  // keep the workgroup's waves on the same replicas
+      if (r & 1) __syncthreads();  // keep the workgroup's waves on the same replicas
+    };
+    if constexpr (NT > 0) {
+#pragma unroll 2
+      for (int r = 1; r < NT; ++r) step(r);
+    } else {
+#pragma unroll 1
+      for (int r = 1; r < N; ++r) step(r);
     }
   } else {
+    u32x2 w0[K][2], w1[K][2];
+    load(0, w0);
+    if constexpr (NT > 0) {
+#pragma unroll
+      for (int r = 0; r < NT; r += 2) {
+        if (r + 1 < NT) load(r + 1, w1);
+        __builtin_amdgcn_sched_barrier(0);
+        add(w0, r == 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (r + 2 < NT) load(r + 2, w0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (r + 1 < NT) add(w1, false);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();  // keep the workgroup's waves on the same replicas
+      }
+    } else {
 #pragma unroll 1
-    for (int r = 0; r < N; r += 2) {
-      if (r + 1 < N) load(r + 1, w1);
-      __builtin_amdgcn_sched_barrier(0);
-      add(w0, r == 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (r + 2 < N) load(r + 2, w0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (r + 1 < N) add(w1, false);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
+      for (int r = 0; r < N; r += 2) {
+        if (r + 1 < N) load(r + 1, w1);
+        __builtin_amdgcn_sched_barrier(0);
+        add(w0, r == 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (r + 2 < N) load(r + 2, w0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (r + 1 < N) add(w1, false);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+      }
     }
   }
 }
@@ -124,14 +159,16 @@ __device__ __forceinline__ void phased_state_load(const FlatShape& s, const int6
 // Phase B after the grid barrier, tile by tile with the next tile's state in
 // flight (tile 0's state already requested into st[0]): upd(acc, p, m, v)
 // turns a lane's 8 rank-ordered replica sums and its 8 master, m and v values
-// into the new master, m and v, and the four outputs are stored.
-template <int K, class UPD>
+// into the new master, m and v, and the four outputs are stored.  With PART,
+// tiles 0..kk-1 only.
+template <int K, bool PART = false, class UPD>
 __device__ __forceinline__ void phased_update(const FlatShape& s, const int64_t (&es)[K], uint32_t e,
-                                              float (&acc)[K][8], f32x4 (&st)[2][6], UPD&& upd) {
+                                              float (&acc)[K][8], f32x4 (&st)[2][6], UPD&& upd, int kk = K) {
   constexpr uint32_t q2 = Layout::kSecond / 4;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    if (k + 1 < K) phased_state_load(s, es, k + 1, e, st[(k + 1) & 1]);
+    if (PART && k >= kk) continue;
+    if (k + 1 < K && (!PART || k + 1 < kk)) phased_state_load(s, es, k + 1, e, st[(k + 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
     const f32x4* q = st[k & 1];
     float p[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
@@ -155,13 +192,47 @@ __device__ __forceinline__ void phased_update(const FlatShape& s, const int64_t 
   }
 }
 
-// The whole super-chunks of a flat shard (tiles of 512 parameters from element
-// s.head; s.nvec 8-element groups on the vector path): phase A, the grid
-// barrier, phase B, for each.  gp(r) is replica r's gradient pointer (the
-// shard's element 0); upd(acc, p, m, v) turns the 8 rank-ordered replica sums
-// of a lane and its 8 master, m and v values into the new master, m and v.
-// Returns the number of whole tiles covered; the caller takes the rest.
-// Launched as one workgroup of kPhasedWaves waves per compute unit.
+// Tiles per wave of the part super-chunk after the whole ones (of `tiles`
+// tiles per wave), out of `rest` tiles left: the part runs phased only with at
+// least half a super-chunk's tiles per wave (fewer keep too few loads in
+// flight per compute unit; they go one tile per wave); 0 otherwise.
+__device__ __host__ inline int phased_part_tiles(int64_t rest, int64_t waves, int tiles = kPhasedTiles) {
+  const int64_t kk = rest / waves;
+  return 2 * kk >= tiles ? (int)(kk < tiles ? kk : tiles - 1) : 0;
+}
+
+// One super-chunk of a flat shard: phase A, the grid barrier (release number
+// `c` of the slot's counter), phase B.  Slot k of the wave is tile t0 + k*nw +
+// gw (nw waves in the grid, gw the wave's index); with PART, slots 0..kk-1.
+template <int NT, bool PART, class GP, class UPD>
+__device__ __forceinline__ void phased_super_chunk(GP gp, int N, const FlatShape& s, int64_t t0, int64_t nw,
+                                                   int64_t gw, uint32_t e, uint32_t* counter, int64_t c,
+                                                   int32_t max_polls, UPD&& upd, int kk) {
+  constexpr int K = kPhasedTiles;
+  int64_t es[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) es[k] = s.head + 8 * kFlatBlock * (t0 + k * nw + gw);
+  // ---- phase A: the replicas, in rank order, into the accumulators
+  float acc[K][8];
+  phased_accumulate<NT, kBF16, K, 1, PART>(gp, N, es, e, acc, true, kk);
+  // ---- phase B: state, AdamW, outputs, tile by tile (the next tile's state in flight).  The first
+  // tile's state is requested before the barrier: reads, like the stragglers' replica reads.
+  f32x4 st[2][6];
+  phased_state_load(s, es, 0, e, st[0]);
+  // the grid barrier lets the workgroups go once kPhasedQuorum of them have arrived: waiting for the
+  // last few costs more than their reads overlapping the others' writes
+  phased_grid_barrier(counter, (uint32_t)c * gridDim.x + phased_quorum(gridDim.x), max_polls);
+  phased_update<K, PART>(s, es, e, acc, st, upd, kk);
+}
+
+// The super-chunks of a flat shard (tiles of 512 parameters from element
+// s.head; s.nvec 8-element groups on the vector path): the whole ones, then
+// the part-super-chunk of phased_part_tiles tiles per wave.  gp(r) is
+// replica r's gradient pointer (the shard's element 0); upd(acc, p, m, v)
+// turns the 8 rank-ordered replica sums of a lane and its 8 master, m and v
+// values into the new master, m and v.  Returns the number of whole tiles
+// covered; the caller takes the rest.  Launched as one workgroup of
+// kPhasedWaves waves per compute unit.
 template <int NT, class GP, class UPD>
 __device__ __forceinline__ int64_t phased_super_chunks(GP gp, int N, const FlatShape& s, int32_t slot,
                                                       int32_t max_polls, UPD&& upd) {
@@ -172,26 +243,13 @@ __device__ __forceinline__ int64_t phased_super_chunks(GP gp, int N, const FlatS
   const int64_t gw = (int64_t)blockIdx.x * kPhasedWaves + wave;
   const int64_t full = s.nvec / kFlatBlock;  // whole tiles
   const int64_t per = nw * K;                // tiles per super-chunk
-  const int64_t nsup = full / per;           // whole super-chunks; the rest of the tiles after them
+  const int64_t nsup = uniform_i64(full / per);  // whole super-chunks
   uint32_t* counter = &g_phased_counters[32 * slot];
-  for (int64_t sc = 0; sc < nsup; ++sc) {
-    // slot k of this wave: tile sc*per + k*nw + gw, from element es[k] (wave-uniform)
-    int64_t es[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) es[k] = s.head + 8 * kFlatBlock * (sc * per + k * nw + gw);
-    // ---- phase A: the replicas, in rank order, into the accumulators
-    float acc[K][8];
-    phased_accumulate<NT, kBF16, K>(gp, N, es, e, acc);
-    // ---- phase B: state, AdamW, outputs, tile by tile (the next tile's state in flight).  The first
-    // tile's state is requested before the barrier: reads, like the stragglers' replica reads.
-    f32x4 st[2][6];
-    phased_state_load(s, es, 0, e, st[0]);
-    // the grid barrier lets the workgroups go once kPhasedQuorum of them have arrived: waiting for the
-    // last few costs more than their reads overlapping the others' writes
-    phased_grid_barrier(counter, (uint32_t)sc * gridDim.x + phased_quorum(gridDim.x), max_polls);
-    phased_update(s, es, e, acc, st, upd);
-  }
-  return nsup * per;
+  for (int64_t c = 0; c < nsup; ++c)
+    phased_super_chunk<NT, false>(gp, N, s, c * per, nw, gw, e, counter, c, max_polls, upd, K);
+  const int kk = __builtin_amdgcn_readfirstlane(phased_part_tiles(full - nsup * per, nw));
+  if (kk > 0) phased_super_chunk<NT, true>(gp, N, s, nsup * per, nw, gw, e, counter, nsup, max_polls, upd, kk);
+  return nsup * per + kk * nw;
 }
 
 }  // namespace

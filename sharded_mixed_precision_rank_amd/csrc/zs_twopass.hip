@@ -191,10 +191,55 @@ __global__ __launch_bounds__(kBlock) void reduce_window_kernel(const ReduceArgs<
   if (blockIdx.x == 0) head_partial<NT, FMT>(a, G0, N, inv, lds4);
 }
 
+// One super-chunk of pass 1 on the phased schedule: slot k of the wave is
+// wave tile t0 + k*nw + gw (with PART, slots 0..kk-1); `c` numbers the grid
+// barrier.
+template <int NT, int FMT, bool PART>
+__device__ __forceinline__ void reduce_super_chunk(const ReduceArgs<NT>& a, int N, const Scalars& c, float inv,
+                                                   int64_t t0, int64_t nw, int64_t gw, int wave, uint32_t e,
+                                                   uint32_t* counter, int64_t cnum, int32_t max_polls,
+                                                   double (&wsum)[kReducePhasedTiles][kPhasedWaves], int kk) {
+  constexpr int K = kReducePhasedTiles;
+  constexpr int kQuarters = kTile / (8 * kFlatBlock);   // wave tiles per norm tile
+  constexpr int kNormTiles = kPhasedWaves / kQuarters;  // per slot per workgroup
+  auto gp = [&](int r) { return a.g[r]; };
+  int64_t es[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) es[k] = a.head + 8 * kFlatBlock * (t0 + k * nw + gw);
+  float acc[K][8];
+  phased_accumulate<NT, FMT, K, 1, PART>(gp, N, es, e, acc, true, kk);
+  phased_grid_barrier(counter, (uint32_t)cnum * gridDim.x + phased_quorum(gridDim.x), max_polls);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (PART && k >= kk) continue;
+    float g[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) g[j] = mean_of<NT>(acc[k][j], c) * inv;
+    GLB f32x4* O = (GLB f32x4*)at(tile_base(a.gbar + es[k]), here(e) * 4u);
+    st_g(O, (f32x4){g[0], g[1], g[2], g[3]});
+    st_g(O + Layout::kSecond / 4, (f32x4){g[4], g[5], g[6], g[7]});
+    double sq = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sq += (double)g[j] * (double)g[j];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, 64);
+    if ((threadIdx.x & 63) == 0) wsum[k][wave] = sq;
+  }
+  __syncthreads();
+  if (threadIdx.x < (PART ? kk : K) * kNormTiles) {
+    const int k = threadIdx.x / kNormTiles, i = threadIdx.x % kNormTiles;
+    const double* q = &wsum[k][kQuarters * i];
+    const int64_t w0 = t0 + k * nw + (int64_t)blockIdx.x * kPhasedWaves + kQuarters * i;
+    a.partials[w0 / kQuarters] = (q[0] + q[1]) + (q[2] + q[3]);
+  }
+  __syncthreads();
+}
+
 // Pass 1 on the phased schedule of the flat step (flat_phased_kernel): one
 // workgroup of kPhasedWaves waves per compute unit; for each of `nsup` whole
 // super-chunks of wave tiles (512 parameters from `head`, kPhasedTiles per
-// wave, slot k of wave w at tile sc*per + k*waves + w), phase A streams the
+// wave, slot k of wave w at tile sc*per + k*waves + w), and then a part
+// super-chunk of `kk` tiles per wave when kk > 0, phase A streams the
 // replicas in rank order into register accumulators (phased_accumulate, the
 // flat step's own code), the grid barrier follows, and phase B writes the
 // means and the norm partials.  A 2048-parameter norm tile is four
@@ -206,12 +251,11 @@ __global__ __launch_bounds__(kBlock) void reduce_window_kernel(const ReduceArgs<
 // tiles after the super-chunks and the head elements.
 template <int NT, int FMT>
 __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void reduce_phased_kernel(const ReduceArgs<NT> a,
-                                                                                 const PhasedCtl ctl, int64_t nsup) {
-  constexpr int K = kPhasedTiles;
+                                                                                 const PhasedCtl ctl, int64_t nsup,
+                                                                                 int32_t kk) {
   constexpr int kQuarters = kTile / (8 * kFlatBlock);  // wave tiles per norm tile
   static_assert(kQuarters == 4 && kPhasedWaves % kQuarters == 0, "norm tiles of whole waves of one workgroup");
-  constexpr int kNormTiles = kPhasedWaves / kQuarters;  // per slot per workgroup
-  __shared__ double wsum[K][kPhasedWaves];
+  __shared__ double wsum[kReducePhasedTiles][kPhasedWaves];
   const int N = NT > 0 ? NT : a.n_rep;
   Scalars c{};
   c.n_rep = N;
@@ -220,40 +264,14 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void reduce_phased_kernel
   const uint32_t e = 4u * (threadIdx.x & 63u);
   const int64_t nw = (int64_t)gridDim.x * kPhasedWaves;
   const int64_t gw = (int64_t)blockIdx.x * kPhasedWaves + wave;
-  const int64_t per = nw * K;
+  const int64_t per = nw * kReducePhasedTiles;
   uint32_t* counter = &g_phased_counters[32 * ctl.slot];
-  auto gp = [&](int r) { return a.g[r]; };
-  for (int64_t sc = 0; sc < nsup; ++sc) {
-    int64_t es[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) es[k] = a.head + 8 * kFlatBlock * (sc * per + k * nw + gw);
-    float acc[K][8];
-    phased_accumulate<NT, FMT, K>(gp, N, es, e, acc);
-    phased_grid_barrier(counter, (uint32_t)sc * gridDim.x + phased_quorum(gridDim.x), ctl.max_polls);
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      float g[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) g[j] = mean_of<NT>(acc[k][j], c) * inv;
-      GLB f32x4* O = (GLB f32x4*)at(tile_base(a.gbar + es[k]), here(e) * 4u);
-      st_g(O, (f32x4){g[0], g[1], g[2], g[3]});
-      st_g(O + Layout::kSecond / 4, (f32x4){g[4], g[5], g[6], g[7]});
-      double sq = 0.0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sq += (double)g[j] * (double)g[j];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, 64);
-      if ((threadIdx.x & 63) == 0) wsum[k][wave] = sq;
-    }
-    __syncthreads();
-    if (threadIdx.x < K * kNormTiles) {
-      const int k = threadIdx.x / kNormTiles, i = threadIdx.x % kNormTiles;
-      const double* q = &wsum[k][kQuarters * i];
-      const int64_t w0 = sc * per + k * nw + (int64_t)blockIdx.x * kPhasedWaves + kQuarters * i;
-      a.partials[w0 / kQuarters] = (q[0] + q[1]) + (q[2] + q[3]);
-    }
-    __syncthreads();
-  }
+  for (int64_t sc = 0; sc < nsup; ++sc)
+    reduce_super_chunk<NT, FMT, false>(a, N, c, inv, sc * per, nw, gw, wave, e, counter, sc, ctl.max_polls, wsum,
+                                       kReducePhasedTiles);
+  if (kk > 0)
+    reduce_super_chunk<NT, FMT, true>(a, N, c, inv, nsup * per, nw, gw, wave, e, counter, nsup, ctl.max_polls, wsum,
+                                      kk);
 }
 
 // First stage of the norm: workgroup b takes partials [b*kFinalSeg,
@@ -410,13 +428,16 @@ hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int b
                    : resident_grid(reduce_phased_kernel<0, FMT>, kFlatBlock * kPhasedWaves, cache);
     if (grid > 0) {
       if (blocks < grid) grid = blocks;
-      const int64_t per = (int64_t)grid * kPhasedWaves * kPhasedTiles;  // wave tiles per super-chunk
-      const int64_t nsup = (sh.n - sh.head) / (8 * kFlatBlock) / per;
+      const int64_t nw = (int64_t)grid * kPhasedWaves;
+      const int64_t per = nw * kReducePhasedTiles;  // wave tiles per super-chunk
+      const int64_t full = (sh.n - sh.head) / (8 * kFlatBlock);
+      const int64_t nsup = full / per;
+      const int32_t kk = phased_part_tiles(full - nsup * per, nw, kReducePhasedTiles);
       if (nsup > 0) {
         (void)hipGetLastError();
         phased_clear_kernel<<<dim3(1), dim3(64), 0, stream>>>(sh.ctl.slot);
         if constexpr (NT == 64) {
-          reduce_phased_kernel<64, FMT><<<dim3(grid), dim3(kFlatBlock * kPhasedWaves), 0, stream>>>(a, sh.ctl, nsup);
+          reduce_phased_kernel<64, FMT><<<dim3(grid), dim3(kFlatBlock * kPhasedWaves), 0, stream>>>(a, sh.ctl, nsup, kk);
         } else {
           ReduceArgs<0> b;
           for (int r = 0; r < sh.n_rep; ++r) b.g[r] = grads[r];
@@ -432,11 +453,11 @@ hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int b
           b.t_lo = a.t_lo;
           b.t_hi = a.t_hi;
           b.head_here = a.head_here;
-          reduce_phased_kernel<0, FMT><<<dim3(grid), dim3(kFlatBlock * kPhasedWaves), 0, stream>>>(b, sh.ctl, nsup);
+          reduce_phased_kernel<0, FMT><<<dim3(grid), dim3(kFlatBlock * kPhasedWaves), 0, stream>>>(b, sh.ctl, nsup, kk);
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        t_first = nsup * per / 4;  // four wave tiles per norm tile
+        t_first = (nsup * per + kk * nw) / 4;  // four wave tiles per norm tile
       }
     } else {
       (void)hipGetLastError();  // no occupancy figure: the one-tile kernel takes the shard

@@ -1,14 +1,16 @@
 """GPU parity of the phased schedule of the flat step (flat_phased_kernel)
 against the oracle, and against the other two schedules.
 
-The phased kernel cuts a shard into super-chunks of (workgroups x 12 waves x 8
-tiles) whole tiles, then the whole tiles after the last super-chunk, then the
-one partial tile and the head and tail elements.  A forced small grid (1 to 3
-workgroups: super-chunks of 49,152 to 147,456 parameters) puts every one of
-those parts in shards the oracle checks in full; the library's own grid is
-checked on a shard of 2^25 + 3,707 parameters (two super-chunks and a
-remainder).  The grid barrier only shapes timing: the same results must come
-out when a workgroup gives up waiting after a single poll."""
+The phased kernel cuts a shard into super-chunks of (workgroups x 12 waves x 12
+tiles) whole tiles, then a part super-chunk of 6 to 11 tiles per wave when at
+least half a super-chunk's tiles are left, then the whole tiles after those
+one per wave, then the one partial tile and the head and tail elements.  A
+forced small grid (1 to 3 workgroups: super-chunks of 73,728 to 221,184
+parameters) puts every one of those parts in shards the oracle checks in full;
+the library's own grid is checked on a shard of 2^25 + 3,707 parameters (one
+super-chunk, a part super-chunk of 9 tiles per wave and a remainder).  The
+grid barrier only shapes timing: the same results must come out when a
+workgroup gives up waiting after a single poll."""
 import numpy as np
 import pytest
 
@@ -18,7 +20,8 @@ from tests.test_gpu_flat import HP, download, rand_host, upload
 pytestmark = pytest.mark.gpu
 
 HP_WD = dict(HP, weight_decay=0.1)
-SUPER = 12 * 8 * 512  # parameters per super-chunk per workgroup
+SUPER = 12 * 12 * 512  # parameters per super-chunk per workgroup
+ROW = 12 * 512  # parameters of one tile per wave of one workgroup
 
 
 @pytest.fixture
@@ -64,7 +67,12 @@ def check(env, orc, host, hp, t, what, offset=0):
     (2, 64, 3 * 2 * SUPER, 0),              # whole super-chunks only
     (3, 50, 2 * 3 * SUPER + 512 * 40 + 9, 0),   # run-time replica count
     (2, 8, 4 * 2 * SUPER + 3, 61),          # few replicas, a 61-element offset
-    (2, 3, 2 * SUPER - 1, 0),               # less than one super-chunk: remainder tiles only
+    (2, 3, 2 * SUPER - 1, 0),               # less than one super-chunk: a part super-chunk of 11 tiles per wave
+    (1, 64, 2 * SUPER + 7 * ROW + 777, 0),  # a part super-chunk of 7 tiles per wave, remainder, partial tile
+    (2, 64, 2 * SUPER + 22 * ROW + 515, 3), # a part of 11 tiles per wave behind a 3-element peel
+    (3, 50, 3 * SUPER + 18 * ROW + 5, 0),   # a part of 6 tiles per wave at a run-time replica count
+    (1, 64, 2 * SUPER + 5 * ROW + 9, 0),    # 5 tiles per wave left: below a part, one tile per wave
+    (2, 3, 10 * ROW + 7, 0),                # less than half a super-chunk: remainder tiles only
     (1, 64, 512, 0),                        # one tile
     (1, 65, 1300, 3),                       # one tile, a partial one, head and tail
 ])
@@ -103,8 +111,9 @@ def env_torch():
 
 
 def test_phased_library_grid_multi_super_chunk(env, orc):
-    """The library's own grid (one workgroup per compute unit) on 2^25 + 3,707 parameters at N = 64,
-    every position against the oracle (the host redraws the same inputs)."""
+    """The library's own grid (one workgroup per compute unit) on 2^25 + 3,707 parameters at N = 64 (a
+    super-chunk and a part super-chunk), every position against the oracle (the host redraws the same
+    inputs)."""
     from synth import workloads as W
 
     torch = env["torch"]

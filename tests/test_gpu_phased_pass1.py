@@ -2,10 +2,14 @@
 (reduce_phased_kernel): the mean gradient bit for bit and the squared norm
 against the oracle, and both the same bits as on the one-tile schedule.
 
-Forced small grids (1 to 3 workgroups: super-chunks of 49,152 to 147,456
-parameters) put whole super-chunks, the norm tiles after them, the partial
-tile and the head elements in shards the oracle checks in full; the library's
-own grid is checked on 2^25 + 3,707 parameters at N = 64."""
+Pass 1 takes super-chunks of (workgroups x 12 waves x 10 tiles) whole wave
+tiles, then a part super-chunk of 5 to 9 tiles per wave when at least half a
+super-chunk's tiles are left.  Forced small grids (1 to 3 workgroups:
+super-chunks of 61,440 to 184,320 parameters) put whole super-chunks, part
+super-chunks, the norm tiles after them, the partial tile and the head
+elements in shards the oracle checks in full; the library's own grid is
+checked on 40,898,171 parameters at N = 64 (two super-chunks and a part of 6
+tiles per wave)."""
 import numpy as np
 import pytest
 
@@ -13,7 +17,8 @@ from tests.test_gpu_twopass import HP, rand_case
 
 pytestmark = pytest.mark.gpu
 
-SUPER = 12 * 8 * 512  # parameters per super-chunk per workgroup
+SUPER = 12 * 10 * 512  # parameters per super-chunk per workgroup
+ROW = 12 * 512  # parameters of one tile per wave of one workgroup
 
 
 @pytest.fixture
@@ -59,6 +64,10 @@ def device_replicas(env, host, offset):
     (3, 32, 2 * 3 * SUPER, 0, "fp16", 256.0),             # whole super-chunks only; fp16, loss-scaled
     (2, 64, 2 * 2 * SUPER + 9, 61, "fp16", 65536.0),      # a 61-element offset, fp16
     (1, 8, SUPER - 1, 0, "bf16", 1.0),                    # less than one super-chunk: the one-tile kernel
+    (1, 64, 2 * SUPER + 7 * ROW + 2048 + 5, 0, "bf16", 1.0),   # a part super-chunk of 7 tiles per wave
+    (2, 64, 2 * SUPER + 18 * ROW + 777, 3, "fp16", 1024.0),    # a part of 9 tiles per wave behind a peel
+    (3, 50, 3 * SUPER + 15 * ROW + 11, 0, "bf16", 1.0),        # a part of 5 tiles per wave, run-time N
+    (1, 64, 2 * SUPER + 4 * ROW + 100, 0, "bf16", 1.0),        # 4 tiles per wave left: no part
 ])
 def test_phased_pass1_matches_oracle_and_stream(env, orc, grid, N, n, offset, gfmt, scale):
     zs = env["zs"]
@@ -95,13 +104,14 @@ def test_phased_pass1_one_poll_per_barrier(env, orc):
 
 
 def test_phased_pass1_library_grid(env, orc):
-    """The library's own grid at N = 64 on 2^25 + 3,707 parameters (the automatic schedule): the mean
-    gradient and the norm are the bits of the one-tile schedule, and the mean gradient is the oracle's
-    at 100,000 sampled positions (the host redraws the same inputs there)."""
+    """The library's own grid at N = 64 on 40,898,171 parameters (the automatic schedule: two
+    super-chunks and a part super-chunk of 6 tiles per wave on 256 compute units): the mean gradient and
+    the norm are the bits of the one-tile schedule, and the mean gradient is the oracle's at 100,000
+    sampled positions (the host redraws the same inputs there)."""
     from synth import workloads as W
 
     torch, zs = env["torch"], env["zs"]
-    n = (1 << 25) + 3_707
+    n = 2 * 256 * SUPER + 6 * 256 * ROW + 3_707
     assert zs.reduce_schedule(64, n) == "phased"
     w = W.FLAT_70B_DP64_N64.with_(name="pass1", n_flat=n)
     d = W.device_inputs(w)
