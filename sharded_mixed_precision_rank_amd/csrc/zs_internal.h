@@ -152,20 +152,19 @@ constexpr int kMaxGroups = ZS_MAX_GROUPS;
 constexpr int kWindowChecks = 4;
 constexpr int64_t kWindowMinTiles = 65536;
 constexpr int kMaxDevices = 64;
-// Phased flat step: 512-parameter tiles per wave in one super-chunk (their
-// fp32 accumulators take 96 VGPRs, one replica's loads in flight 48 more),
-// waves per workgroup (one workgroup per compute unit at 3 waves per SIMD),
-// the fewest tiles per wave for which the part of a super-chunk left after
-// the whole ones runs phased (fewer keep too few loads in flight per compute
-// unit; they go one tile per wave), barrier counter slots, the default
+// Phased schedule: 512-parameter tiles per wave in one super-chunk of the
+// flat step and of pass 1 (their fp32 accumulators take 96 VGPRs, one
+// replica's loads in flight 48 more) and of a list plan (10: its per-wave
+// descriptor takes registers of its own), waves per workgroup (one workgroup
+// per compute unit at 3 waves per SIMD), barrier counter slots, the default
 // longest wait at one barrier (polls of about 50 ns: about 3 ms), and the
 // fewest parameters and replicas for which the automatic schedule takes it.
-// Measured on 2^28-2^30-parameter shards against per-tile stores: 63% / 74%
-// of 8 TB/s at N = 8, 70% / 74% at 16, 76% / 74% at 32, 78% / 71% at 48, 82% /
-// 74% at 64, 82% / 69% at 128, 83% / 71% at 256.
+// With 8 tiles per wave, measured on 2^28-2^30-parameter shards against
+// per-tile stores: 63% / 74% of 8 TB/s at N = 8, 70% / 74% at 16, 76% / 74% at
+// 32, 78% / 71% at 48, 82% / 74% at 64, 82% / 69% at 128, 83% / 71% at 256;
+// 12 tiles took another 1.3-1.5% at N = 48 and 64.
 constexpr int kPhasedTiles = 12;
-constexpr int kReducePhasedTiles = 10;
-constexpr int kListPhasedTiles = 8;
+constexpr int kListPhasedTiles = 10;
 constexpr int kPhasedWaves = 12;
 constexpr int kPhasedSlots = 16;
 constexpr int32_t kPhasedMaxPolls = 1 << 16;

@@ -617,14 +617,13 @@ __global__ __launch_bounds__(kFlatBlock) void list_window_kernel(const int32_t* 
 
 // List plans on the phased schedule (see flat_phased_kernel): one workgroup of
 // kPhasedWaves waves per compute unit; super-chunk c gives wave w the
-// kListPhasedTiles (8) consecutive items from (c*W + w)*8 (W waves in the
-// grid).  When they are whole tiles of one tensor (all but a few waves in a
-// list of large tensors), the wave streams their replicas into its
-// accumulators in phase A (the flat step's own code, with two replicas in
-// flight: with one, the per-wave descriptors and the fully known replica
-// count left too few registers and the kernel spilled inside phase A; the
-// tensor's replica pointers come from the plan's table, one scalar load per
-// replica) and
+// kListPhasedTiles (10) consecutive items from (c*W + w)*10 (W waves in the
+// grid; the per-wave descriptor leaves registers for 10 accumulator tiles,
+// not the flat step's 12).  When they are whole tiles of one tensor (all but
+// a few waves in a list of large tensors), the wave streams their replicas
+// into its accumulators in phase A (the flat step's own code; the tensor's
+// replica pointers come from the plan's table, one scalar load per replica)
+// and
 // updates them in phase B after the grid barrier.  Otherwise the wave reads
 // nothing in phase A, meets the same barriers, and takes its items one at a
 // time in phase B.  Items after the last whole super-chunk go one per wave.
@@ -650,14 +649,14 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void list_phased_kernel(
   uint32_t* counter = &g_phased_counters[32 * ctl.slot];
   // the wave's K items of super-chunk c: their tensor, its descriptor as a shard, the first item's
   // place in it and first 8-group, and whether all K are whole tiles of that tensor
-  struct Octet {
+  struct Span {
     int32_t t;
     FlatShape s;
     int64_t k0, g0;
     bool whole;
   };
-  auto octet = [&](int64_t c) {
-    Octet o;
+  auto span = [&](int64_t c) {
+    Span o;
     const int64_t it0 = (c * nw + gw) * K;
     o.t = items[it0];
     const ListTensor& T = tensors[o.t];
@@ -677,7 +676,7 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void list_phased_kernel(
     return o;
   };
   for (int64_t c = 0; c < nsup; ++c) {
-    const Octet o = octet(c);
+    const Span o = span(c);
     const FlatShape& s = o.s;
     int64_t es[K];
 #pragma unroll
@@ -685,7 +684,7 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void list_phased_kernel(
     const uint16_t* const* gpt = gptrs + (int64_t)o.t * N;
     auto gp = [&](int r) { return uniform_ptr(gpt[r]); };
     float acc[K][8];
-    phased_accumulate<NT, kBF16, K, 2>(gp, N, es, e, acc, o.whole);
+    phased_accumulate<NT, kBF16, K>(gp, N, es, e, acc, o.whole);
     f32x4 st[2][6];
     if (o.whole) phased_state_load(s, es, 0, e, st[0]);
     phased_grid_barrier(counter, (uint32_t)c * gridDim.x + phased_quorum(gridDim.x), ctl.max_polls);
@@ -697,11 +696,11 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void list_phased_kernel(
       });
     }
   }
-  // after the super-chunks: the items of the wave's octets that were not whole tiles of one tensor, one
-  // at a time; the head and tail elements of a tensor whose first item led a whole octet; then the items
+  // after the super-chunks: the items of the wave's spans that were not whole tiles of one tensor, one
+  // at a time; the head and tail elements of a tensor whose first item led a whole span; then the items
   // after the last whole super-chunk, one per wave
   for (int64_t c = 0; c < nsup; ++c) {
-    const Octet o = octet(c);
+    const Span o = span(c);
     if (o.whole) {
       if (o.k0 == 0) {
         const FlatShape& s = o.s;

@@ -53,7 +53,7 @@ __device__ __forceinline__ uint32_t phased_quorum(uint32_t grid) {
 // undefined, but meets every workgroup barrier with the others.  With PART
 // (DB = 1 only), only tiles 0..kk-1 (kk wave-uniform) are read; the others'
 // accumulators are left undefined.
-template <int NT, int FMT, int K, int DB = 1, bool PART = false, class GP>
+template <int NT, int FMT, int K, int DB = 1, bool PART = false, int UNROLL = 1, class GP>
 __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&es)[K], uint32_t e,
                                                   float (&acc)[K][8], bool active = true, int kk = K) {
   static_assert(DB == 1 || (DB == 2 && !PART), "one or two replica buffers; parts on one");
@@ -100,7 +100,7 @@ __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&
       if (r & 1) __syncthreads();  // keep the workgroup's waves on the same replicas
     };
     if constexpr (NT > 0) {
-#pragma unroll 2
+#pragma unroll UNROLL
       for (int r = 1; r < NT; ++r) step(r);
     } else {
 #pragma unroll 1
@@ -214,7 +214,7 @@ __device__ __forceinline__ void phased_super_chunk(GP gp, int N, const FlatShape
   for (int k = 0; k < K; ++k) es[k] = s.head + 8 * kFlatBlock * (t0 + k * nw + gw);
   // ---- phase A: the replicas, in rank order, into the accumulators
   float acc[K][8];
-  phased_accumulate<NT, kBF16, K, 1, PART>(gp, N, es, e, acc, true, kk);
+  phased_accumulate<NT, kBF16, K, 1, PART, 2>(gp, N, es, e, acc, true, kk);
   // ---- phase B: state, AdamW, outputs, tile by tile (the next tile's state in flight).  The first
   // tile's state is requested before the barrier: reads, like the stragglers' replica reads.
   f32x4 st[2][6];

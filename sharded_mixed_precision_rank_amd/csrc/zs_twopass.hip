@@ -198,8 +198,8 @@ template <int NT, int FMT, bool PART>
 __device__ __forceinline__ void reduce_super_chunk(const ReduceArgs<NT>& a, int N, const Scalars& c, float inv,
                                                    int64_t t0, int64_t nw, int64_t gw, int wave, uint32_t e,
                                                    uint32_t* counter, int64_t cnum, int32_t max_polls,
-                                                   double (&wsum)[kReducePhasedTiles][kPhasedWaves], int kk) {
-  constexpr int K = kReducePhasedTiles;
+                                                   double (&wsum)[kPhasedTiles][kPhasedWaves], int kk) {
+  constexpr int K = kPhasedTiles;
   constexpr int kQuarters = kTile / (8 * kFlatBlock);   // wave tiles per norm tile
   constexpr int kNormTiles = kPhasedWaves / kQuarters;  // per slot per workgroup
   auto gp = [&](int r) { return a.g[r]; };
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void reduce_phased_kernel
                                                                                  int32_t kk) {
   constexpr int kQuarters = kTile / (8 * kFlatBlock);  // wave tiles per norm tile
   static_assert(kQuarters == 4 && kPhasedWaves % kQuarters == 0, "norm tiles of whole waves of one workgroup");
-  __shared__ double wsum[kReducePhasedTiles][kPhasedWaves];
+  __shared__ double wsum[kPhasedTiles][kPhasedWaves];
   const int N = NT > 0 ? NT : a.n_rep;
   Scalars c{};
   c.n_rep = N;
@@ -264,11 +264,11 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void reduce_phased_kernel
   const uint32_t e = 4u * (threadIdx.x & 63u);
   const int64_t nw = (int64_t)gridDim.x * kPhasedWaves;
   const int64_t gw = (int64_t)blockIdx.x * kPhasedWaves + wave;
-  const int64_t per = nw * kReducePhasedTiles;
+  const int64_t per = nw * kPhasedTiles;
   uint32_t* counter = &g_phased_counters[32 * ctl.slot];
   for (int64_t sc = 0; sc < nsup; ++sc)
     reduce_super_chunk<NT, FMT, false>(a, N, c, inv, sc * per, nw, gw, wave, e, counter, sc, ctl.max_polls, wsum,
-                                       kReducePhasedTiles);
+                                       kPhasedTiles);
   if (kk > 0)
     reduce_super_chunk<NT, FMT, true>(a, N, c, inv, nsup * per, nw, gw, wave, e, counter, nsup, ctl.max_polls, wsum,
                                       kk);
@@ -429,11 +429,11 @@ hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int b
     if (grid > 0) {
       if (blocks < grid) grid = blocks;
       const int64_t nw = (int64_t)grid * kPhasedWaves;
-      const int64_t per = nw * kReducePhasedTiles;  // wave tiles per super-chunk
+      const int64_t per = nw * kPhasedTiles;  // wave tiles per super-chunk
       const int64_t full = (sh.n - sh.head) / (8 * kFlatBlock);
       const int64_t nsup = full / per;
-      const int32_t kk = phased_part_tiles(full - nsup * per, nw, kReducePhasedTiles);
-      if (nsup > 0) {
+      const int32_t kk = phased_part_tiles(full - nsup * per, nw);
+      if (nsup > 0 || kk > 0) {
         (void)hipGetLastError();
         phased_clear_kernel<<<dim3(1), dim3(64), 0, stream>>>(sh.ctl.slot);
         if constexpr (NT == 64) {

@@ -1,10 +1,10 @@
 """GPU parity of list plans on the phased schedule (list_phased_kernel) against the oracle, tensor by
 tensor.
 
-A wave takes 8 consecutive work items per super-chunk: whole tiles of one tensor go through phase A and B,
-any other octet (near a tensor's ends, scalar-only tensors) goes one item at a time after the
+A wave takes 10 consecutive work items per super-chunk: whole tiles of one tensor go through phase A and
+B, any other span (near a tensor's ends, scalar-only tensors) goes one item at a time after the
 super-chunks, and the items after the last whole super-chunk go one per wave.  Forced grids of 1 to 3
-workgroups (super-chunks of 96 to 288 items) put every case in lists the oracle checks in full."""
+workgroups (super-chunks of 120 to 360 items) put every case in lists the oracle checks in full."""
 import numpy as np
 import pytest
 
@@ -35,10 +35,10 @@ def got_of(d):
 
 
 @pytest.mark.parametrize("grid,N,count,hi", [
-    (1, 64, 60, 70_000),     # tensors of a few to ~140 tiles, every octet kind, many super-chunks
+    (1, 64, 60, 70_000),     # tensors of a few to ~140 tiles, every span kind, many super-chunks
     (2, 50, 60, 70_000),     # the run-time replica count
     (3, 8, 200, 200_000),    # few replicas (phased only on request)
-    (2, 64, 12, 2_000_000),  # long tensors: almost every octet whole
+    (2, 64, 12, 2_000_000),  # long tensors: almost every span whole
 ])
 def test_phased_list_matches_oracle(env, orc, grid, N, count, hi):
     """One set for every tensor, then three hyperparameter groups, then the device step."""
