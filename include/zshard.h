@@ -481,14 +481,15 @@ ZS_API zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* 
    pass 1's norm partials in the same order, so results do not depend on it;
    only when the bytes move does.  For pass 1 the phased schedule writes the
    mean gradient and the norm partials after the grid barrier, and its
-   windowed default is 4096 / 256 ticks.  A list plan on the phased schedule
-   gives each wave 8 consecutive wave tiles per super-chunk; when they are not
+   windowed default is 4096 / 256 ticks, and the automatic schedule takes the
+   phased one from N = 12 replicas on.  A list plan on the phased schedule
+   gives each wave 10 consecutive wave tiles per super-chunk; when they are not
    whole tiles of one tensor (near a tensor's ends) the wave takes them one at
    a time after the barrier.
      ZS_SCHEDULE_AUTO:     the default.  An explicit zs_set_write_window
                            decides when one was made (no windows:
                            ZS_SCHEDULE_STREAM; a window: ZS_SCHEDULE_WINDOWED);
-                           otherwise ZS_SCHEDULE_PHASED for N >= 32 replicas on
+                           otherwise ZS_SCHEDULE_PHASED for N >= 18 replicas on
                            shards of at least 2^25 parameters, and
                            ZS_SCHEDULE_STREAM below (at N = 8 and 16 per-tile
                            stores measured faster).

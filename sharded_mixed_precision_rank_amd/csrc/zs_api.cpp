@@ -188,7 +188,7 @@ int auto_blocks() {
 // (period_mask 0 unless windowed).  An explicit zs_set_flat_schedule wins;
 // otherwise an explicit zs_set_write_window decides (no windows: per-tile
 // stores; a window: the windowed kernel); otherwise the phased kernel for
-// N >= kPhasedMinReplicas (32) on shards of at least kPhasedMinParams, and
+// N >= kPhasedMinReplicas (18) on shards of at least kPhasedMinParams, and
 // per-tile stores below.  The windowed kernel's default window is a
 // 4096-tick (41 us) period with 640 ticks open for N < 64, 512 up to 128 and
 // 384 above: the writes' share of the bytes shrinks as N grows.
@@ -227,9 +227,9 @@ zs::PhasedCtl phased_ctl() {
 
 // Pass 1 of the two-pass form (2N bytes read and 4 written per parameter)
 // follows the same setting: an explicit schedule, else an explicit window
-// (1: none, > 1: windowed), else phased for N >= kPhasedMinReplicas on shards
-// of at least kPhasedMinParams, else one tile per workgroup.  Its windowed
-// default is 4096 / 256.
+// (1: none, > 1: windowed), else phased for N >= kReducePhasedMinReplicas
+// (12) on shards of at least kPhasedMinParams, else one tile per workgroup.
+// Its windowed default is 4096 / 256.
 zs::FlatSchedule reduce_schedule(int32_t N, int64_t n, zs::WriteWindow* win) {
   const int32_t forced = g_flat_schedule.load(std::memory_order_relaxed);
   const uint64_t word = g_window.load(std::memory_order_relaxed);
@@ -242,8 +242,8 @@ zs::FlatSchedule reduce_schedule(int32_t N, int64_t n, zs::WriteWindow* win) {
   else if (period > 1)
     sched = zs::FlatSchedule::kWindowed;
   else
-    sched = N >= zs::kPhasedMinReplicas && n >= zs::kPhasedMinParams ? zs::FlatSchedule::kPhased
-                                                                      : zs::FlatSchedule::kStream;
+    sched = N >= zs::kReducePhasedMinReplicas && n >= zs::kPhasedMinParams ? zs::FlatSchedule::kPhased
+                                                                            : zs::FlatSchedule::kStream;
   zs::WriteWindow w{0, 0};
   if (sched == zs::FlatSchedule::kWindowed) {
     if (period > 1)

@@ -52,7 +52,9 @@ __device__ __forceinline__ uint32_t phased_quorum(uint32_t grid) {
 //  A wave with `active` false (wave-uniform) issues no loads and leaves acc
 // undefined, but meets every workgroup barrier with the others.  With PART
 // (DB = 1 only), only tiles 0..kk-1 (kk wave-uniform) are read; the others'
-// accumulators are left undefined.
+// accumulators are left undefined.  The tile loops skip the others with
+// `continue` (the same tiles as a `break`): with `break` this compiler turned
+// a tile base into a vector value and failed ("illegal VGPR to SGPR copy").
 template <int NT, int FMT, int K, int DB = 1, bool PART = false, int UNROLL = 1, class GP>
 __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&es)[K], uint32_t e,
                                                   float (&acc)[K][8], bool active = true, int kk = K) {

@@ -468,11 +468,12 @@ def test_tuning_knobs_check_their_ranges():
 
 
 def test_reduce_schedule_query():
-    """Pass 1 of the two-pass form follows the same setting: phased for N >= 32 on shards of at least
+    """Pass 1 of the two-pass form follows the same setting: phased for N >= 12 on shards of at least
     2^25 parameters, one tile per workgroup otherwise; windowed only on request."""
     assert zs.reduce_schedule(64, 1_093_750_000) == "phased"
-    assert zs.reduce_schedule(32, 1 << 25) == "phased"
-    assert zs.reduce_schedule(31, 1 << 30) == "stream"
+    assert zs.reduce_schedule(12, 1 << 25) == "phased"
+    assert zs.reduce_schedule(16, 1 << 30) == "phased"
+    assert zs.reduce_schedule(11, 1 << 30) == "stream"
     assert zs.reduce_schedule(8, 124_000_000) == "stream"
     assert zs.reduce_schedule(64, (1 << 25) - 1) == "stream"
     try:
@@ -497,12 +498,12 @@ def test_reduce_schedule_query():
 
 
 def test_flat_schedule_query_and_setting():
-    """The automatic schedule: phased for N >= 32 on shards of at least 2^25 parameters, per-tile stores
+    """The automatic schedule: phased for N >= 18 on shards of at least 2^25 parameters, per-tile stores
     otherwise; an explicit schedule wins (each kernel's own size conditions aside)."""
     assert zs.flat_schedule(64, 1_093_750_000) == "phased"
-    assert zs.flat_schedule(32, 1 << 25) == "phased"
+    assert zs.flat_schedule(18, 1 << 25) == "phased"
     assert zs.flat_schedule(256, 1 << 30) == "phased"
-    assert zs.flat_schedule(31, 1 << 30) == "stream"
+    assert zs.flat_schedule(17, 1 << 30) == "stream"
     assert zs.flat_schedule(16, 1 << 30) == "stream"
     assert zs.flat_schedule(8, 124_000_000) == "stream"
     assert zs.flat_schedule(64, (1 << 25) - 1) == "stream"
