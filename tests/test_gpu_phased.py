@@ -179,11 +179,12 @@ def test_phased_device_step(env, orc):
 
 def test_phased_in_a_graph(env, orc):
     """Captured once in a HIP graph (the barrier counter's clear is a kernel node), replayed four times
-    with eager work and synchronisation between replays; every replay equals the eager step."""
+    with eager work and synchronisation between replays; every replay equals the eager step.  The shard
+    has three super-chunks, a part super-chunk of 7 tiles per wave and a partial tile."""
     torch, zs, dev = env["torch"], env["zs"], env["dev"]
     zs.set_grid_blocks(2)
     rng = np.random.default_rng(41)
-    n = 3 * 2 * SUPER + 100
+    n = 3 * 2 * SUPER + 2 * 7 * ROW + 100
     host = rand_host(rng, 64, n)
     P, M, V, B = orc.step(host["G"], host["P"], host["M"], host["V"], HP_WD, 7)
     ref = dict(P=P, M=M, V=V, B=B)
