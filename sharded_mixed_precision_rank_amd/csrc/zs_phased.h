@@ -40,27 +40,27 @@ __device__ __forceinline__ uint32_t phased_quorum(uint32_t grid) {
 
 // Phase A of a super-chunk: replicas 0..N-1 (rank order) of a wave's K tiles
 // (tile k from element es[k], wave-uniform; the split lane layout, lane
-// offset e) into fp32 register accumulators, the workgroup's waves meeting at
-// a workgroup barrier every two replicas so that they read the same replicas
-// at about the same time.  gp(r) is replica r's gradient pointer (bf16 or
-// fp16 bits per FMT).  DB = 1: one replica's K tiles in flight per wave;
-// DB = 2: two (replica r + 1 requested before replica r is added).  With 12
-// waves per compute unit the second buffer measured no faster, and one buffer
-// leaves the registers for more tiles per super-chunk; the list kernel, whose
-// per-wave descriptors take registers of their own, keeps two buffers of
-// fewer tiles.
+// offset e) into fp32 register accumulators, one replica's K tiles in flight
+// per wave, the workgroup's waves meeting at a workgroup barrier after every
+// replica so that they read the same replica at about the same time.  gp(r)
+// is replica r's gradient pointer (bf16 or fp16 bits per FMT).  A second
+// replica buffer (replica r + 1 requested before r is added) measured no
+// faster with 12 waves per compute unit; its registers go to more tiles per
+// super-chunk instead.  A barrier after every replica measured 0.2-0.4%
+// faster than after every two, and after every four 0.1% slower.
 //  A wave with `active` false (wave-uniform) issues no loads and leaves acc
-// undefined, but meets every workgroup barrier with the others.  With PART
-// (DB = 1 only), only tiles 0..kk-1 (kk wave-uniform) are read; the others'
-// accumulators are left undefined.  The tile loops skip the others with
-// `continue` (the same tiles as a `break`): with `break` this compiler turned
-// a tile base into a vector value and failed ("illegal VGPR to SGPR copy").
-template <int NT, int FMT, int K, int DB = 1, bool PART = false, int UNROLL = 1, class GP>
+// undefined, but meets every workgroup barrier with the others.  With PART,
+// only tiles 0..kk-1 (kk wave-uniform) are read; the others' accumulators are
+// left undefined.  The tile loops skip the others with `continue` (the same
+// tiles as a `break`): with `break` this compiler turned a tile base into a
+// vector value and failed ("illegal VGPR to SGPR copy").  UNROLL unrolls the
+// replica loop of a fixed replica count.
+template <int NT, int FMT, int K, bool PART = false, int UNROLL = 1, class GP>
 __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&es)[K], uint32_t e,
                                                   float (&acc)[K][8], bool active = true, int kk = K) {
-  static_assert(DB == 1 || (DB == 2 && !PART), "one or two replica buffers; parts on one");
   constexpr uint32_t q2 = Layout::kSecond / 4;
-  auto load = [&](int r, u32x2(&w)[K][2]) {
+  u32x2 w[K][2];
+  auto load = [&](int r) {
     if (!active) return;
     const uint16_t* g = gp(r);
 #pragma unroll
@@ -71,7 +71,7 @@ __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&
       w[k][1] = ld_g(q + q2);  // the second quad: 256 elements on (64 u32x2)
     }
   };
-  auto add = [&](const u32x2(&w)[K][2], bool first) {
+  auto add = [&](bool first) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       if (PART && k >= kk) continue;
@@ -87,57 +87,25 @@ __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&
       for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(acc[k][j]));
     }
   };
-  if constexpr (DB == 1) {
-    u32x2 w[K][2];
-    // replica 0 initialises the accumulators; replicas 1..N-1 are added in rank order
-    load(0, w);
+  // replica 0 initialises the accumulators; replicas 1..N-1 are added in rank order
+  load(0);
+  __builtin_amdgcn_sched_barrier(0);
+  add(true);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();  // keep the workgroup's waves on the same replica
+  auto step = [&](int r) {
+    load(r);
     __builtin_amdgcn_sched_barrier(0);
-    add(w, true);
+    add(false);
     __builtin_amdgcn_sched_barrier(0);
-    auto step = [&](int r) {
-      load(r, w);
-      __builtin_amdgcn_sched_barrier(0);
-      add(w, false);
-      __builtin_amdgcn_sched_barrier(0);
-      if (r & 1) __syncthreads();  // keep the workgroup's waves on the same replicas
-    };
-    if constexpr (NT > 0) {
+    __syncthreads();
+  };
+  if constexpr (NT > 0) {
 #pragma unroll UNROLL
-      for (int r = 1; r < NT; ++r) step(r);
-    } else {
-#pragma unroll 1
-      for (int r = 1; r < N; ++r) step(r);
-    }
+    for (int r = 1; r < NT; ++r) step(r);
   } else {
-    u32x2 w0[K][2], w1[K][2];
-    load(0, w0);
-    if constexpr (NT > 0) {
-#pragma unroll
-      for (int r = 0; r < NT; r += 2) {
-        if (r + 1 < NT) load(r + 1, w1);
-        __builtin_amdgcn_sched_barrier(0);
-        add(w0, r == 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (r + 2 < NT) load(r + 2, w0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (r + 1 < NT) add(w1, false);
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();  // keep the workgroup's waves on the same replicas
-      }
-    } else {
 #pragma unroll 1
-      for (int r = 0; r < N; r += 2) {
-        if (r + 1 < N) load(r + 1, w1);
-        __builtin_amdgcn_sched_barrier(0);
-        add(w0, r == 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (r + 2 < N) load(r + 2, w0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (r + 1 < N) add(w1, false);
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-      }
-    }
+    for (int r = 1; r < N; ++r) step(r);
   }
 }
 
@@ -216,7 +184,7 @@ __device__ __forceinline__ void phased_super_chunk(GP gp, int N, const FlatShape
   for (int k = 0; k < K; ++k) es[k] = s.head + 8 * kFlatBlock * (t0 + k * nw + gw);
   // ---- phase A: the replicas, in rank order, into the accumulators
   float acc[K][8];
-  phased_accumulate<NT, kBF16, K, 1, PART, 2>(gp, N, es, e, acc, true, kk);
+  phased_accumulate<NT, kBF16, K, PART, 2>(gp, N, es, e, acc, true, kk);
   // ---- phase B: state, AdamW, outputs, tile by tile (the next tile's state in flight).  The first
   // tile's state is requested before the barrier: reads, like the stragglers' replica reads.
   f32x4 st[2][6];

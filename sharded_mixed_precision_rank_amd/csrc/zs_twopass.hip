@@ -207,7 +207,7 @@ __device__ __forceinline__ void reduce_super_chunk(const ReduceArgs<NT>& a, int 
 #pragma unroll
   for (int k = 0; k < K; ++k) es[k] = a.head + 8 * kFlatBlock * (t0 + k * nw + gw);
   float acc[K][8];
-  phased_accumulate<NT, FMT, K, 1, PART>(gp, N, es, e, acc, true, kk);
+  phased_accumulate<NT, FMT, K, PART>(gp, N, es, e, acc, true, kk);
   phased_grid_barrier(counter, (uint32_t)cnum * gridDim.x + phased_quorum(gridDim.x), max_polls);
 #pragma unroll
   for (int k = 0; k < K; ++k) {
