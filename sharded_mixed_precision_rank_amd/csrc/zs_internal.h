@@ -153,9 +153,10 @@ constexpr int kWindowChecks = 4;
 constexpr int64_t kWindowMinTiles = 65536;
 constexpr int kMaxDevices = 64;
 // Phased schedule: 512-parameter tiles per wave in one super-chunk of the
-// flat step and of pass 1 (their fp32 accumulators take 96 VGPRs, one
-// replica's loads in flight 48 more) and of a list plan (10: its per-wave
-// descriptor takes registers of its own), waves per workgroup (one workgroup
+// flat step (their fp32 accumulators take 96 VGPRs, one replica's loads in
+// flight 48 more), of pass 1 (10 in registers and 4 in LDS, 96 KB per
+// workgroup) and of a list plan (10: its per-wave descriptor takes registers
+// of its own), waves per workgroup (one workgroup
 // per compute unit at 3 waves per SIMD), barrier counter slots, the default
 // longest wait at one barrier (polls of about 50 ns: about 3 ms), and the
 // fewest parameters and replicas for which the automatic schedule takes it.
@@ -169,6 +170,9 @@ constexpr int kMaxDevices = 64;
 // 4-byte means alone, gains from fewer replicas: 75% / 75% at N = 8, 73.5% /
 // 71.5% at 12, 77% / 72% at 16, 77% / 71% at 18, 79% / 71% at 24.
 constexpr int kPhasedTiles = 12;
+constexpr int kReduceRegTiles = 10;
+constexpr int kReduceLdsTiles = 4;
+constexpr int kReducePhasedTiles = kReduceRegTiles + kReduceLdsTiles;
 constexpr int kListPhasedTiles = 10;
 constexpr int kPhasedWaves = 12;
 constexpr int kPhasedSlots = 16;

@@ -688,13 +688,13 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void list_phased_kernel(
     const uint16_t* const* gpt = gptrs + (int64_t)o.t * N;
     auto gp = [&](int r) { return uniform_ptr(gpt[r]); };
     float acc[K][8];
-    phased_accumulate<NT, kBF16, K>(gp, N, es, e, acc, o.whole);
+    phased_accumulate<NT, kBF16, K, 0>(gp, N, es, e, acc, nullptr, o.whole);
     f32x4 st[2][6];
     if (o.whole) phased_state_load(s, es, 0, e, st[0]);
     phased_grid_barrier(counter, (uint32_t)c * gridDim.x + phased_quorum(gridDim.x), ctl.max_polls);
     if (o.whole) {
       const Scalars& cs = NG == 1 ? one : sc.c[tensors[o.t].group];
-      phased_update(s, es, e, acc, st, [&](const float(&a)[8], float(&p)[8], float(&m)[8], float(&v)[8]) {
+      phased_update<K, 0>(s, es, e, acc, nullptr, st, [&](const float(&a)[8], float(&p)[8], float(&m)[8], float(&v)[8]) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) adam(mean_of<NT>(a[j], cs), p[j], m[j], v[j], cs);
       });

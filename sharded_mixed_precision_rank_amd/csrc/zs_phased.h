@@ -55,10 +55,13 @@ __device__ __forceinline__ uint32_t phased_quorum(uint32_t grid) {
 // tiles as a `break`): with `break` this compiler turned a tile base into a
 // vector value and failed ("illegal VGPR to SGPR copy").  UNROLL unrolls the
 // replica loop of a fixed replica count.
-template <int NT, int FMT, int K, bool PART = false, int UNROLL = 1, class GP>
-__device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&es)[K], uint32_t e,
-                                                  float (&acc)[K][8], bool active = true, int kk = K) {
+template <int NT, int FMT, int KR, int KL, bool PART = false, int UNROLL = 1, class GP>
+__device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&es)[KR + KL], uint32_t e,
+                                                  float (&acc)[KR][8], f32x4 (*la)[2][64], bool active = true,
+                                                  int kk = KR + KL) {
+  constexpr int K = KR + KL;
   constexpr uint32_t q2 = Layout::kSecond / 4;
+  const uint32_t lane = threadIdx.x & 63u;
   u32x2 w[K][2];
   auto load = [&](int r) {
     if (!active) return;
@@ -71,20 +74,55 @@ __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&
       w[k][1] = ld_g(q + q2);  // the second quad: 256 elements on (64 u32x2)
     }
   };
+  auto widen = [&](int k, float (&x)[8]) {
+    x[0] = h_lo<FMT>(w[k][0].x);
+    x[1] = h_hi<FMT>(w[k][0].x);
+    x[2] = h_lo<FMT>(w[k][0].y);
+    x[3] = h_hi<FMT>(w[k][0].y);
+    x[4] = h_lo<FMT>(w[k][1].x);
+    x[5] = h_hi<FMT>(w[k][1].x);
+    x[6] = h_lo<FMT>(w[k][1].y);
+    x[7] = h_hi<FMT>(w[k][1].y);
+  };
   auto add = [&](bool first) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
+    for (int k = 0; k < KR; ++k) {
       if (PART && k >= kk) continue;
-      const float x[8] = {h_lo<FMT>(w[k][0].x), h_hi<FMT>(w[k][0].x), h_lo<FMT>(w[k][0].y), h_hi<FMT>(w[k][0].y),
-                          h_lo<FMT>(w[k][1].x), h_hi<FMT>(w[k][1].x), h_lo<FMT>(w[k][1].y), h_hi<FMT>(w[k][1].y)};
+      float x[8];
+      widen(k, x);
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[k][j] = first ? x[j] : acc[k][j] + x[j];
     }
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
+    for (int k = 0; k < KR; ++k) {
       if (PART && k >= kk) continue;
 #pragma unroll
       for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(acc[k][j]));
+    }
+    // the tiles kept in LDS: the wave's own region, so no other wave reads or writes it
+#pragma unroll
+    for (int l = 0; l < KL; ++l) {
+      if (PART && KR + l >= kk) continue;
+      float x[8];
+      widen(KR + l, x);
+      f32x4 a0, a1;
+      if (first) {
+        a0 = (f32x4){x[0], x[1], x[2], x[3]};
+        a1 = (f32x4){x[4], x[5], x[6], x[7]};
+      } else {
+        a0 = la[l][0][lane];
+        a1 = la[l][1][lane];
+        a0.x = a0.x + x[0];
+        a0.y = a0.y + x[1];
+        a0.z = a0.z + x[2];
+        a0.w = a0.w + x[3];
+        a1.x = a1.x + x[4];
+        a1.y = a1.y + x[5];
+        a1.z = a1.z + x[6];
+        a1.w = a1.w + x[7];
+      }
+      la[l][0][lane] = a0;
+      la[l][1][lane] = a1;
     }
   };
   // replica 0 initialises the accumulators; replicas 1..N-1 are added in rank order
@@ -106,6 +144,28 @@ __device__ __forceinline__ void phased_accumulate(GP gp, int N, const int64_t (&
   } else {
 #pragma unroll 1
     for (int r = 1; r < N; ++r) step(r);
+  }
+}
+
+// Tile k's 8 rank-ordered sums of a lane after phase A: from the registers
+// (k < KR) or from the wave's LDS tiles.
+template <int KR, int KL>
+__device__ __forceinline__ void phased_sums(const float (&acc)[KR][8], f32x4 (*la)[2][64], int k, float (&g)[8]) {
+  if (k < KR) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) g[j] = acc[k < KR ? k : 0][j];
+  } else {
+    const uint32_t lane = threadIdx.x & 63u;
+    const int l = k >= KR ? k - KR : 0;
+    const f32x4 a0 = la[l][0][lane], a1 = la[l][1][lane];
+    g[0] = a0.x;
+    g[1] = a0.y;
+    g[2] = a0.z;
+    g[3] = a0.w;
+    g[4] = a1.x;
+    g[5] = a1.y;
+    g[6] = a1.z;
+    g[7] = a1.w;
   }
 }
 
@@ -131,9 +191,11 @@ __device__ __forceinline__ void phased_state_load(const FlatShape& s, const int6
 // turns a lane's 8 rank-ordered replica sums and its 8 master, m and v values
 // into the new master, m and v, and the four outputs are stored.  With PART,
 // tiles 0..kk-1 only.
-template <int K, bool PART = false, class UPD>
-__device__ __forceinline__ void phased_update(const FlatShape& s, const int64_t (&es)[K], uint32_t e,
-                                              float (&acc)[K][8], f32x4 (&st)[2][6], UPD&& upd, int kk = K) {
+template <int KR, int KL, bool PART = false, class UPD>
+__device__ __forceinline__ void phased_update(const FlatShape& s, const int64_t (&es)[KR + KL], uint32_t e,
+                                              float (&acc)[KR][8], f32x4 (*la)[2][64], f32x4 (&st)[2][6],
+                                              UPD&& upd, int kk = KR + KL) {
+  constexpr int K = KR + KL;
   constexpr uint32_t q2 = Layout::kSecond / 4;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
@@ -144,7 +206,9 @@ __device__ __forceinline__ void phased_update(const FlatShape& s, const int64_t 
     float p[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
     float m[8] = {q[2].x, q[2].y, q[2].z, q[2].w, q[3].x, q[3].y, q[3].z, q[3].w};
     float v[8] = {q[4].x, q[4].y, q[4].z, q[4].w, q[5].x, q[5].y, q[5].z, q[5].w};
-    upd(acc[k], p, m, v);
+    float g[8];
+    phased_sums<KR, KL>(acc, la, k, g);
+    upd(g, p, m, v);
     const TileOut h = tile_outputs(p, m, v);
     const uint32_t o = here(e) * 4u;
     GLB f32x4* P4 = (GLB f32x4*)at(tile_base(s.p + es[k]), o);
@@ -178,13 +242,14 @@ template <int NT, bool PART, class GP, class UPD>
 __device__ __forceinline__ void phased_super_chunk(GP gp, int N, const FlatShape& s, int64_t t0, int64_t nw,
                                                    int64_t gw, uint32_t e, uint32_t* counter, int64_t c,
                                                    int32_t max_polls, UPD&& upd, int kk) {
-  constexpr int K = kPhasedTiles;
+  constexpr int KR = kPhasedTiles, KL = 0, K = KR;
+  f32x4(*la)[2][64] = nullptr;  // every accumulator in registers
   int64_t es[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) es[k] = s.head + 8 * kFlatBlock * (t0 + k * nw + gw);
   // ---- phase A: the replicas, in rank order, into the accumulators
-  float acc[K][8];
-  phased_accumulate<NT, kBF16, K, PART, 2>(gp, N, es, e, acc, true, kk);
+  float acc[KR][8];
+  phased_accumulate<NT, kBF16, KR, KL, PART, 2>(gp, N, es, e, acc, la, true, kk);
   // ---- phase B: state, AdamW, outputs, tile by tile (the next tile's state in flight).  The first
   // tile's state is requested before the barrier: reads, like the stragglers' replica reads.
   f32x4 st[2][6];
@@ -192,7 +257,7 @@ __device__ __forceinline__ void phased_super_chunk(GP gp, int N, const FlatShape
   // the grid barrier lets the workgroups go once kPhasedQuorum of them have arrived: waiting for the
   // last few costs more than their reads overlapping the others' writes
   phased_grid_barrier(counter, (uint32_t)c * gridDim.x + phased_quorum(gridDim.x), max_polls);
-  phased_update<K, PART>(s, es, e, acc, st, upd, kk);
+  phased_update<KR, KL, PART>(s, es, e, acc, la, st, upd, kk);
 }
 
 // The super-chunks of a flat shard (tiles of 512 parameters from element

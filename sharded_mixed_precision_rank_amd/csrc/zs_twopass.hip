@@ -198,23 +198,25 @@ template <int NT, int FMT, bool PART>
 __device__ __forceinline__ void reduce_super_chunk(const ReduceArgs<NT>& a, int N, const Scalars& c, float inv,
                                                    int64_t t0, int64_t nw, int64_t gw, int wave, uint32_t e,
                                                    uint32_t* counter, int64_t cnum, int32_t max_polls,
-                                                   double (&wsum)[kPhasedTiles][kPhasedWaves], int kk) {
-  constexpr int K = kPhasedTiles;
+                                                   double (&wsum)[kReducePhasedTiles][kPhasedWaves], int kk,
+                                                   f32x4 (*la)[2][64]) {
+  constexpr int KR = kReduceRegTiles, KL = kReduceLdsTiles, K = KR + KL;
   constexpr int kQuarters = kTile / (8 * kFlatBlock);   // wave tiles per norm tile
   constexpr int kNormTiles = kPhasedWaves / kQuarters;  // per slot per workgroup
   auto gp = [&](int r) { return a.g[r]; };
   int64_t es[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) es[k] = a.head + 8 * kFlatBlock * (t0 + k * nw + gw);
-  float acc[K][8];
-  phased_accumulate<NT, FMT, K, PART>(gp, N, es, e, acc, true, kk);
+  float acc[KR][8];
+  phased_accumulate<NT, FMT, KR, KL, PART>(gp, N, es, e, acc, la, true, kk);
   phased_grid_barrier(counter, (uint32_t)cnum * gridDim.x + phased_quorum(gridDim.x), max_polls);
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     if (PART && k >= kk) continue;
     float g[8];
+    phased_sums<KR, KL>(acc, la, k, g);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) g[j] = mean_of<NT>(acc[k][j], c) * inv;
+    for (int j = 0; j < 8; ++j) g[j] = mean_of<NT>(g[j], c) * inv;
     GLB f32x4* O = (GLB f32x4*)at(tile_base(a.gbar + es[k]), here(e) * 4u);
     st_g(O, (f32x4){g[0], g[1], g[2], g[3]});
     st_g(O + Layout::kSecond / 4, (f32x4){g[4], g[5], g[6], g[7]});
@@ -237,12 +239,16 @@ __device__ __forceinline__ void reduce_super_chunk(const ReduceArgs<NT>& a, int 
 
 // Pass 1 on the phased schedule of the flat step (flat_phased_kernel): one
 // workgroup of kPhasedWaves waves per compute unit; for each of `nsup` whole
-// super-chunks of wave tiles (512 parameters from `head`, kPhasedTiles per
-// wave, slot k of wave w at tile sc*per + k*waves + w), and then a part
+// super-chunks of wave tiles (512 parameters from `head`, kReducePhasedTiles
+// per wave, slot k of wave w at tile sc*per + k*waves + w), and then a part
 // super-chunk of `kk` tiles per wave when kk > 0, phase A streams the
-// replicas in rank order into register accumulators (phased_accumulate, the
-// flat step's own code), the grid barrier follows, and phase B writes the
-// means and the norm partials.  A 2048-parameter norm tile is four
+// replicas in rank order into fp32 accumulators (phased_accumulate, the flat
+// step's own code; kReduceRegTiles tiles in registers, kReduceLdsTiles in the
+// wave's own LDS region), the grid barrier follows, and phase B writes the
+// means and the norm partials.  Pass 1's phase B writes only its 4-byte
+// means, so its super-chunks pay for more of their fixed cost than the flat
+// step's: the LDS tiles' longer super-chunks measured 1% faster here and no
+// faster (0.4% slower) on the flat step.  A 2048-parameter norm tile is four
 // consecutive wave tiles, held by four consecutive waves of one workgroup in
 // the same slot: each wave forms its sum of squares as reduce_kernel's wave
 // does for that quarter (per thread in element order, then the same
@@ -255,7 +261,8 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void reduce_phased_kernel
                                                                                  int32_t kk) {
   constexpr int kQuarters = kTile / (8 * kFlatBlock);  // wave tiles per norm tile
   static_assert(kQuarters == 4 && kPhasedWaves % kQuarters == 0, "norm tiles of whole waves of one workgroup");
-  __shared__ double wsum[kPhasedTiles][kPhasedWaves];
+  __shared__ double wsum[kReducePhasedTiles][kPhasedWaves];
+  __shared__ f32x4 lds[kPhasedWaves][kReduceLdsTiles][2][64];  // the waves' accumulator tiles beyond registers
   const int N = NT > 0 ? NT : a.n_rep;
   Scalars c{};
   c.n_rep = N;
@@ -264,14 +271,14 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void reduce_phased_kernel
   const uint32_t e = 4u * (threadIdx.x & 63u);
   const int64_t nw = (int64_t)gridDim.x * kPhasedWaves;
   const int64_t gw = (int64_t)blockIdx.x * kPhasedWaves + wave;
-  const int64_t per = nw * kPhasedTiles;
+  const int64_t per = nw * kReducePhasedTiles;
   uint32_t* counter = &g_phased_counters[32 * ctl.slot];
   for (int64_t sc = 0; sc < nsup; ++sc)
     reduce_super_chunk<NT, FMT, false>(a, N, c, inv, sc * per, nw, gw, wave, e, counter, sc, ctl.max_polls, wsum,
-                                       kPhasedTiles);
+                                       kReducePhasedTiles, lds[wave]);
   if (kk > 0)
     reduce_super_chunk<NT, FMT, true>(a, N, c, inv, nsup * per, nw, gw, wave, e, counter, nsup, ctl.max_polls, wsum,
-                                      kk);
+                                      kk, lds[wave]);
 }
 
 // First stage of the norm: workgroup b takes partials [b*kFinalSeg,
@@ -429,10 +436,10 @@ hipError_t go_reduce(const uint16_t* const* grads, const TwoPassShape& sh, int b
     if (grid > 0) {
       if (blocks < grid) grid = blocks;
       const int64_t nw = (int64_t)grid * kPhasedWaves;
-      const int64_t per = nw * kPhasedTiles;  // wave tiles per super-chunk
+      const int64_t per = nw * kReducePhasedTiles;  // wave tiles per super-chunk
       const int64_t full = (sh.n - sh.head) / (8 * kFlatBlock);
       const int64_t nsup = full / per;
-      const int32_t kk = phased_part_tiles(full - nsup * per, nw);
+      const int32_t kk = phased_part_tiles(full - nsup * per, nw, kReducePhasedTiles);
       if (nsup > 0 || kk > 0) {
         (void)hipGetLastError();
         phased_clear_kernel<<<dim3(1), dim3(64), 0, stream>>>(sh.ctl.slot);
