@@ -38,12 +38,16 @@ __device__ __forceinline__ uint32_t phased_quorum(uint32_t grid) {
   return (grid * kPhasedQuorumPct + 99u) / 100u;
 }
 
-// Phase A of a super-chunk: replicas 0..N-1 (rank order) of a wave's K tiles
-// (tile k from element es[k], wave-uniform; the split lane layout, lane
-// offset e) into fp32 register accumulators, one replica's K tiles in flight
-// per wave, the workgroup's waves meeting at a workgroup barrier after every
-// replica so that they read the same replica at about the same time.  gp(r)
-// is replica r's gradient pointer (bf16 or fp16 bits per FMT).  A second
+// Phase A of a super-chunk: replicas 0..N-1 (rank order) of a wave's
+// K = KR + KL tiles (tile k from element es[k], wave-uniform; the split lane
+// layout, lane offset e) into fp32 accumulators, tiles 0..KR-1 in registers
+// (acc) and tiles KR..K-1 in the wave's own LDS region `la` (tile l at la[l],
+// lane t's quads at la[l][0][t] and la[l][1][t]; each replica's values read,
+// added in the same fp32 order and written back, so the sums are the same
+// bits), one replica's K tiles in flight per wave, the workgroup's waves
+// meeting at a workgroup barrier after every replica so that they read the
+// same replica at about the same time.  gp(r) is replica r's gradient
+// pointer (bf16 or fp16 bits per FMT).  A second
 // replica buffer (replica r + 1 requested before r is added) measured no
 // faster with 12 waves per compute unit; its registers go to more tiles per
 // super-chunk instead.  A barrier after every replica measured 0.2-0.4%
