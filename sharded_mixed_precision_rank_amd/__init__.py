@@ -330,6 +330,49 @@ def reduce_adam_flat_ptrs(grad_ptrs: Sequence[int], n: int, master: int, m: int,
            "zs_reduce_adam_flat")
 
 
+class FlatStep:
+    """:func:`reduce_adam_flat` on fixed tensors, prepared once: the argument
+    checks, the device and the replica pointer table are done at construction,
+    so a call only packs the hyperparameters (kept while the same frozen
+    :class:`AdamHP` comes back; a dict is packed on every call, since it may
+    have changed) and enqueues the step.  For small shards, where the per-call
+    checks cost more than the device time.  The object holds references to the
+    tensors; it reads their addresses once, so re-pointing a tensor at new
+    storage (``Tensor.set_``) after construction is not seen.  ``stream`` fixed
+    here (a torch stream or a raw handle) saves looking up torch's current
+    stream on every call."""
+
+    def __init__(self, grads: Sequence, master, m, v, param, stream=None):
+        self._tensors = (tuple(grads), master, m, v, param)
+        self._N = len(grads)
+        self._n = _tensor_args(grads, master, m, v, param)
+        self._dev = _one_device(master, m, v, param, *grads)
+        self._dev_index = self._dev.index if self._dev.index is not None else torch.cuda.current_device()
+        self._tab = (_vp * max(self._N, 1))(*[g.data_ptr() for g in grads])
+        self._ptrs = (master.data_ptr(), m.data_ptr(), v.data_ptr(), param.data_ptr())
+        self._stream = None if stream is None else _stream_handle(stream, self._dev)
+        self._hp_obj = None
+        self._hp = None
+
+    def __call__(self, hp, step: int, stream=None) -> None:
+        if hp is not self._hp_obj:
+            self._hp = _hp(hp)
+            self._hp_obj = hp if isinstance(hp, AdamHP) else None
+        if stream is not None:
+            s = _stream_handle(stream, self._dev)
+        elif self._stream is not None:
+            s = self._stream
+        else:
+            s = torch.cuda.current_stream(self._dev).cuda_stream
+        args = (self._tab, self._N, self._n, *self._ptrs, ctypes.byref(self._hp), step, s)
+        if torch.cuda.current_device() == self._dev_index:
+            st = _lib.zs_reduce_adam_flat(*args)
+        else:
+            with torch.cuda.device(self._dev):
+                st = _lib.zs_reduce_adam_flat(*args)
+        _check(st, "zs_reduce_adam_flat")
+
+
 # ------------------------------------------------------------ device-resident step index
 def fold_table(hp, t0: int, count: int):
     """The folded scalars of steps t0 .. t0+count-1: a (count, 8) float32 array, rows as :func:`fold`."""
