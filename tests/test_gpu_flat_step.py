@@ -36,3 +36,23 @@ def test_flat_step_matches_the_plain_call_and_the_oracle(orc, N, n, fixed_stream
         ref = dict(P=P, M=M, V=V, B=B)
         assert parity.bit_identical(download(b), download(a)), f"step {t}: prepared against plain"
         assert parity.bit_identical(download(b), ref), f"step {t}: prepared against the oracle"
+
+
+def test_flat_step_checks_its_arguments_once():
+    """The checks of reduce_adam_flat run at construction: wrong dtypes and sizes are refused there."""
+    import torch
+
+    import sharded_mixed_precision_rank_amd as zs
+
+    dev = torch.device("cuda:0")
+    n = 1000
+    G = [torch.zeros(n, dtype=torch.int16, device=dev) for _ in range(2)]
+    P, M, V = (torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(3))
+    B = torch.zeros(n, dtype=torch.int16, device=dev)
+    zs.FlatStep(G, P, M, V, B)
+    with pytest.raises(TypeError):
+        zs.FlatStep(G, P.double(), M, V, B)
+    with pytest.raises(ValueError):
+        zs.FlatStep(G, P, M[:-1], V, B)
+    with pytest.raises(ValueError):
+        zs.FlatStep([G[0], G[1][:-1]], P, M, V, B)
