@@ -474,7 +474,9 @@ ZS_API zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* 
 
 /* The schedule of the flat step (zs_reduce_adam_flat and its device-step
    form), of list plans (every zs_reduce_adam_list* call, taking the schedule
-   of a flat shard of the plan's total size) and of pass 1 of the two-pass
+   of a flat shard of the plan's total size, except that the automatic
+   schedule takes the phased one from N = 32 replicas on: zs_list_schedule)
+   and of pass 1 of the two-pass
    form (zs_reduce_grads_flat and its device-scale form), for all later calls
    in this process.  Every schedule
    computes every parameter by the same operations in the same order, and
@@ -538,6 +540,13 @@ ZS_API zs_status zs_flat_schedule(int32_t N, int64_t n, int32_t* schedule);
    of n parameters whose replicas and fp32 workspace share a 128-byte line
    phase.  No GPU call.  Errors: ZS_ERR_NULL, ZS_ERR_RANGE. */
 ZS_API zs_status zs_reduce_schedule(int32_t N, int64_t n, int32_t* schedule);
+
+/* The same for a list plan of n parameters in all over N replicas (any
+   tensor layout): the flat step's rule, the automatic schedule taking
+   ZS_SCHEDULE_PHASED from N = 32 on (at N = 18 per-tile stores measured
+   faster on lists, at N = 24 it depended on the list).  No GPU call.
+   Errors: ZS_ERR_NULL, ZS_ERR_RANGE. */
+ZS_API zs_status zs_list_schedule(int32_t N, int64_t n, int32_t* schedule);
 
 /* The longest a workgroup of the phased schedule waits at a grid barrier, in
    polls of about 50 ns (0: the default, 2^16, about 3 ms).  Past it the

@@ -106,6 +106,8 @@ _lib.zs_flat_schedule.restype = ctypes.c_int
 _lib.zs_flat_schedule.argtypes = [_i32, _i64, ctypes.POINTER(_i32)]
 _lib.zs_reduce_schedule.restype = ctypes.c_int
 _lib.zs_reduce_schedule.argtypes = [_i32, _i64, ctypes.POINTER(_i32)]
+_lib.zs_list_schedule.restype = ctypes.c_int
+_lib.zs_list_schedule.argtypes = [_i32, _i64, ctypes.POINTER(_i32)]
 _lib.zs_set_phased_max_polls.restype = ctypes.c_int
 _lib.zs_set_phased_max_polls.argtypes = [_i32]
 SCHEDULES = {"auto": 0, "stream": 1, "windowed": 2, "phased": 3}
@@ -243,6 +245,14 @@ def reduce_schedule(N: int, n: int) -> str:
     on n parameters."""
     out = _i32()
     _check(_lib.zs_reduce_schedule(N, n, ctypes.byref(out)), "zs_reduce_schedule")
+    return {v: k for k, v in SCHEDULES.items()}[out.value]
+
+
+def list_schedule(N: int, n: int) -> str:
+    """The schedule ("stream", "windowed" or "phased") a list plan of n parameters in all over N replicas
+    takes."""
+    out = _i32()
+    _check(_lib.zs_list_schedule(N, n, ctypes.byref(out)), "zs_list_schedule")
     return {v: k for k, v in SCHEDULES.items()}[out.value]
 
 

@@ -192,7 +192,14 @@ int auto_blocks() {
 // per-tile stores below.  The windowed kernel's default window is a
 // 4096-tick (41 us) period with 640 ticks open for N < 64, 512 up to 128 and
 // 384 above: the writes' share of the bytes shrinks as N grows.
-zs::FlatSchedule flat_schedule(int32_t N, int64_t n, zs::WriteWindow* win) {
+// List plans take the phased kernel from more replicas than flat shards: with
+// spans of consecutive items and the per-span descriptors, per-tile stores
+// measured faster at N = 18 (4.5-6%), the two drawn lists split at N = 24
+// (ragged +3.4% phased, llama7b -1.4%), and the phased kernel won at N = 32.
+constexpr int32_t kListPhasedMinReplicas = 32;
+
+zs::FlatSchedule flat_schedule(int32_t N, int64_t n, zs::WriteWindow* win,
+                               int32_t min_replicas = zs::kPhasedMinReplicas) {
   const int32_t forced = g_flat_schedule.load(std::memory_order_relaxed);
   const uint64_t word = g_window.load(std::memory_order_relaxed);
   const int32_t period = (int32_t)(word >> 32);
@@ -204,8 +211,7 @@ zs::FlatSchedule flat_schedule(int32_t N, int64_t n, zs::WriteWindow* win) {
   else if (period > 1)
     sched = zs::FlatSchedule::kWindowed;
   else
-    sched = N >= zs::kPhasedMinReplicas && n >= zs::kPhasedMinParams ? zs::FlatSchedule::kPhased
-                                                                      : zs::FlatSchedule::kStream;
+    sched = N >= min_replicas && n >= zs::kPhasedMinParams ? zs::FlatSchedule::kPhased : zs::FlatSchedule::kStream;
   zs::WriteWindow w{0, 0};
   if (sched == zs::FlatSchedule::kWindowed) {
     // an explicit window, none when windows were switched off, else the default for N (any N)
@@ -669,7 +675,9 @@ zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* period_
   zs::WriteWindow w{};
   if (kernel == ZS_WINDOW_REDUCE_PASS)
     (void)reduce_schedule(N, n, &w);
-  else  // list plans take the flat step's schedule for a shard of their size
+  else if (kernel == ZS_WINDOW_LIST_PLAN)  // a flat shard's schedule for the plan's size, with the list threshold
+    (void)flat_schedule(N, n, &w, kListPhasedMinReplicas);
+  else
     (void)flat_schedule(N, n, &w);
   const bool big = flat ? n / 8 / zs::kFlatBlock >= zs::kWindowMinTiles
                         : n / kTileElems >= zs::kReduceWindowMinTiles;
@@ -714,6 +722,20 @@ zs_status zs_flat_schedule(int32_t N, int64_t n, int32_t* schedule) {
   if (sched == zs::FlatSchedule::kWindowed && (w.period_mask == 0 || tiles < zs::kWindowMinTiles))
     sched = zs::FlatSchedule::kStream;
   if (sched == zs::FlatSchedule::kPhased && tiles < 1) sched = zs::FlatSchedule::kStream;
+  *schedule = (int32_t)sched;
+  return ZS_OK;
+}
+
+zs_status zs_list_schedule(int32_t N, int64_t n, int32_t* schedule) {
+  g_last_error.clear();
+  if (!schedule) return fail(ZS_ERR_NULL, "schedule is NULL");
+  if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
+  if (n < 0) return fail(ZS_ERR_RANGE, "n must be >= 0");
+  zs::WriteWindow w{};
+  zs::FlatSchedule sched = flat_schedule(N, n, &w, kListPhasedMinReplicas);
+  // the windowed list kernel's size condition
+  if (sched == zs::FlatSchedule::kWindowed && (w.period_mask == 0 || n / 8 / zs::kFlatBlock < zs::kWindowMinTiles))
+    sched = zs::FlatSchedule::kStream;
   *schedule = (int32_t)sched;
   return ZS_OK;
 }
@@ -823,9 +845,10 @@ zs_status launch_list_table(const int32_t* items, int32_t n_items, const zs::Lis
                             const uint16_t* const* gptrs, int32_t N, int64_t n_params, const zs::Scalars* cs,
                             int32_t n_sets, const zs::StepRef& ref, zs_stream stream) {
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  // the flat step's schedule for a shard of the plan's size; windows for plans of at least 2^25 parameters
+  // the flat step's schedule for a shard of the plan's size, phased from kListPhasedMinReplicas on; windows
+  // for plans of at least 2^25 parameters
   zs::WriteWindow win{};
-  const zs::FlatSchedule sched = flat_schedule(N, n_params, &win);
+  const zs::FlatSchedule sched = flat_schedule(N, n_params, &win, kListPhasedMinReplicas);
   if (n_params < ((int64_t)zs::kWindowMinTiles << 9)) win = zs::WriteWindow{0, 0};
   return after_launch(zs::launch_list(items, n_items, tensors, gptrs, cs, n_sets, ref, auto_blocks(), sched, win,
                                       phased_ctl(), hs),

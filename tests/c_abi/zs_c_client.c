@@ -224,6 +224,16 @@ int main(void) {
       fprintf(stderr, "default flat schedule for N = 64 on 2^30 parameters: %d\n", sched);
       bad = 1;
     }
+    CHECK_ZS(zs_list_schedule(24, (int64_t)1 << 30, &sched));
+    if (sched != ZS_SCHEDULE_STREAM) {
+      fprintf(stderr, "default list schedule for N = 24 on 2^30 parameters: %d\n", sched);
+      bad = 1;
+    }
+    CHECK_ZS(zs_list_schedule(32, (int64_t)1 << 30, &sched));
+    if (sched != ZS_SCHEDULE_PHASED) {
+      fprintf(stderr, "default list schedule for N = 32 on 2^30 parameters: %d\n", sched);
+      bad = 1;
+    }
     CHECK_ZS(zs_set_flat_schedule(ZS_SCHEDULE_WINDOWED));
     CHECK_ZS(zs_write_window(ZS_WINDOW_FLAT_STEP, 64, (int64_t)1 << 30, &per, &open));
     if (per != 4096 || open != 512) {

@@ -497,6 +497,32 @@ def test_reduce_schedule_query():
         zs.set_write_window(0)
 
 
+def test_list_schedule_query():
+    """List plans: the flat step's rule, the automatic schedule phased from N = 32 (not 18) on plans of at
+    least 2^25 parameters; an explicit schedule or window wins as for flat shards."""
+    assert zs.list_schedule(64, 1_069_568_000) == "phased"
+    assert zs.list_schedule(32, 1 << 25) == "phased"
+    assert zs.list_schedule(31, 1 << 30) == "stream"
+    assert zs.list_schedule(24, 1 << 30) == "stream"
+    assert zs.list_schedule(16, 2_154_298_847) == "stream"
+    assert zs.list_schedule(64, (1 << 25) - 1) == "stream"
+    assert zs.flat_schedule(24, 1 << 30) == "phased"   # the flat step takes it from 18
+    try:
+        zs.set_flat_schedule("phased")
+        assert zs.list_schedule(8, 1 << 20) == "phased"
+        zs.set_flat_schedule("auto")
+        zs.set_write_window(2048, 256)
+        assert zs.list_schedule(8, 1 << 30) == "windowed"
+        assert zs.list_schedule(8, 1 << 20) == "stream"   # below the windowed kernel's size
+    finally:
+        zs.set_flat_schedule("auto")
+        zs.set_write_window(0)
+    with pytest.raises(zs.ZShardError):
+        zs.list_schedule(0, 1 << 20)
+    with pytest.raises(zs.ZShardError):
+        zs.list_schedule(8, -1)
+
+
 def test_flat_schedule_query_and_setting():
     """The automatic schedule: phased for N >= 18 on shards of at least 2^25 parameters, per-tile stores
     otherwise; an explicit schedule wins (each kernel's own size conditions aside)."""
