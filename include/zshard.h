@@ -474,27 +474,26 @@ ZS_API zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* 
 
 /* The schedule of the flat step (zs_reduce_adam_flat and its device-step
    form), of list plans (every zs_reduce_adam_list* call, taking the schedule
-   of a flat shard of the plan's total size, except that the automatic
-   schedule takes the phased one from N = 32 replicas on: zs_list_schedule)
-   and of pass 1 of the two-pass
+   of a flat shard of the plan's total size by the list rules of
+   ZS_SCHEDULE_AUTO below: zs_list_schedule) and of pass 1 of the two-pass
    form (zs_reduce_grads_flat and its device-scale form), for all later calls
    in this process.  Every schedule
    computes every parameter by the same operations in the same order, and
    pass 1's norm partials in the same order, so results do not depend on it;
    only when the bytes move does.  For pass 1 the phased schedule writes the
    mean gradient and the norm partials after the grid barrier, and its
-   windowed default is 4096 / 256 ticks, and the automatic schedule takes the
-   phased one from N = 12 replicas on.  A list plan on the phased schedule
+   windowed default is 4096 / 256 ticks.  A list plan on the phased schedule
    gives each wave 10 consecutive wave tiles per super-chunk; when they are not
    whole tiles of one tensor (near a tensor's ends) the wave takes them one at
    a time after the barrier.
      ZS_SCHEDULE_AUTO:     the default.  An explicit zs_set_write_window
                            decides when one was made (no windows:
                            ZS_SCHEDULE_STREAM; a window: ZS_SCHEDULE_WINDOWED);
-                           otherwise ZS_SCHEDULE_PHASED for N >= 18 replicas on
-                           shards of at least 2^25 parameters, and
-                           ZS_SCHEDULE_STREAM below (at N = 8 and 16 per-tile
-                           stores measured faster).
+                           otherwise ZS_SCHEDULE_PHASED for N >= 40 replicas on
+                           shards of at least 2^25 parameters and for N >= 24
+                           on at least 2^27, and ZS_SCHEDULE_STREAM elsewhere
+                           (where per-tile stores measured faster).  List
+                           plans: zs_list_schedule; pass 1: N >= 12 on 2^25.
      ZS_SCHEDULE_STREAM:   one 512-parameter tile per workgroup, its outputs
                            stored as soon as it is done; consecutive launches
                            of at most zs_launch_bytes() each.
@@ -541,12 +540,18 @@ ZS_API zs_status zs_flat_schedule(int32_t N, int64_t n, int32_t* schedule);
    phase.  No GPU call.  Errors: ZS_ERR_NULL, ZS_ERR_RANGE. */
 ZS_API zs_status zs_reduce_schedule(int32_t N, int64_t n, int32_t* schedule);
 
-/* The same for a list plan of n parameters in all over N replicas (any
-   tensor layout): the flat step's rule, the automatic schedule taking
-   ZS_SCHEDULE_PHASED from N = 32 on (at N = 18 per-tile stores measured
-   faster on lists, at N = 24 it depended on the list).  No GPU call.
-   Errors: ZS_ERR_NULL, ZS_ERR_RANGE. */
-ZS_API zs_status zs_list_schedule(int32_t N, int64_t n, int32_t* schedule);
+/* The schedule a list plan of these T tensors over N replicas
+   (zs_list_plan_create's arguments, validated as there) takes under the
+   current settings.  By the list rules of ZS_SCHEDULE_AUTO: the phased kernel
+   needs N >= 64 on 3 * 2^24 parameters in all, N >= 40 on 3 * 2^25 or
+   N >= 32 on 3 * 2^26, and at most 1 in 20 of the plan's wave tiles outside
+   whole spans (10
+   consecutive tiles of one tensor, counted from the list's first tile); lists
+   of many small tensors, whose tiles the phased kernel takes one at a time,
+   keep per-tile stores.  The pointers are only read for their alignment.
+   No GPU call.  Errors: ZS_ERR_NULL, ZS_ERR_RANGE, ZS_ERR_ALIGN, ZS_ERR_ALIAS,
+   ZS_ERR_NOMEM. */
+ZS_API zs_status zs_list_schedule(const zs_tensor* tensors, int32_t T, int32_t N, int32_t* schedule);
 
 /* The longest a workgroup of the phased schedule waits at a grid barrier, in
    polls of about 50 ns (0: the default, 2^16, about 3 ms).  Past it the

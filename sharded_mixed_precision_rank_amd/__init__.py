@@ -107,7 +107,7 @@ _lib.zs_flat_schedule.argtypes = [_i32, _i64, ctypes.POINTER(_i32)]
 _lib.zs_reduce_schedule.restype = ctypes.c_int
 _lib.zs_reduce_schedule.argtypes = [_i32, _i64, ctypes.POINTER(_i32)]
 _lib.zs_list_schedule.restype = ctypes.c_int
-_lib.zs_list_schedule.argtypes = [_i32, _i64, ctypes.POINTER(_i32)]
+_lib.zs_list_schedule.argtypes = [ctypes.POINTER(TensorStruct), _i32, _i32, ctypes.POINTER(_i32)]
 _lib.zs_set_phased_max_polls.restype = ctypes.c_int
 _lib.zs_set_phased_max_polls.argtypes = [_i32]
 SCHEDULES = {"auto": 0, "stream": 1, "windowed": 2, "phased": 3}
@@ -248,11 +248,25 @@ def reduce_schedule(N: int, n: int) -> str:
     return {v: k for k, v in SCHEDULES.items()}[out.value]
 
 
-def list_schedule(N: int, n: int) -> str:
-    """The schedule ("stream", "windowed" or "phased") a list plan of n parameters in all over N replicas
-    takes."""
+def list_schedule(sizes, N: int, offsets=None) -> str:
+    """The schedule ("stream", "windowed" or "phased") a list plan over tensors of these sizes takes with N
+    replicas: the tensors in per-array arenas at ``offsets`` (by default back to back on 8-element
+    boundaries), each arena on a 2 MiB boundary, as the caching allocator places large blocks.  No GPU
+    call: the addresses only stand for their alignment."""
+    sizes = np.asarray(sizes, dtype=np.int64)
+    if offsets is None:
+        padded = (sizes + 7) // 8 * 8
+        offsets = np.concatenate([[0], np.cumsum(padded)[:-1]]) if sizes.size else sizes
+    offsets = np.asarray(offsets, dtype=np.int64)
+    L = int((offsets + sizes).max()) if sizes.size else 0
+    step2 = -(-max(L, 1) * 4 // (1 << 21)) * (1 << 21)   # every arena's span, 2 MiB-rounded
+    base = 1 << 40
+    rec, gtab = _arena_records(sizes, offsets, [base + step2 * (4 + r) for r in range(N)], base, base + step2,
+                               base + 2 * step2, base + 3 * step2)
     out = _i32()
-    _check(_lib.zs_list_schedule(N, n, ctypes.byref(out)), "zs_list_schedule")
+    _check(_lib.zs_list_schedule(ctypes.cast(rec.ctypes.data, ctypes.POINTER(TensorStruct)), sizes.size, N,
+                                 ctypes.byref(out)), "zs_list_schedule")
+    del gtab
     return {v: k for k, v in SCHEDULES.items()}[out.value]
 
 
@@ -457,6 +471,24 @@ def _tensor_table(tensors: Sequence[ShardTensor], N: int):
     return tab, keep
 
 
+def _arena_records(sizes, offsets, gbases, pbase, mbase, vbase, bbase):
+    """zs_tensor records (and the replica-pointer table they point into, which the caller keeps alive) for
+    tensors at ``offsets`` of arenas starting at the given addresses."""
+    T, N = sizes.size, len(gbases)
+    gtab = np.empty((max(T, 1), N), dtype=np.uint64)
+    for r, gb in enumerate(gbases):
+        gtab[:T, r] = np.uint64(gb) + (offsets * 2).astype(np.uint64)
+    rec = np.zeros((max(T, 1), 6), dtype=np.uint64)
+    rec[:T, 0] = sizes.astype(np.uint64)
+    rec[:T, 1] = np.uint64(pbase) + (offsets * 4).astype(np.uint64)
+    rec[:T, 2] = np.uint64(mbase) + (offsets * 4).astype(np.uint64)
+    rec[:T, 3] = np.uint64(vbase) + (offsets * 4).astype(np.uint64)
+    rec[:T, 4] = np.uint64(bbase) + (offsets * 2).astype(np.uint64)
+    rec[:T, 5] = np.uint64(gtab.ctypes.data) + np.arange(max(T, 1), dtype=np.uint64) * np.uint64(8 * N)
+    assert ctypes.sizeof(TensorStruct) == 48
+    return rec, gtab
+
+
 class ListPlan:
     """A device-resident chunk table for a fixed ragged list of tensors; each
     :meth:`step` is one kernel covering every tensor (in consecutive launches of a few GB each on long
@@ -488,17 +520,8 @@ class ListPlan:
         if sizes.shape != offsets.shape or (sizes.size and (offsets.min() < 0 or (offsets + sizes).max() > L)):
             raise ValueError("tensor ranges must lie inside the arenas")
         T = sizes.size
-        gtab = np.empty((max(T, 1), N), dtype=np.uint64)
-        for r, g in enumerate(grads):
-            gtab[:T, r] = np.uint64(g.data_ptr()) + (offsets * 2).astype(np.uint64)
-        rec = np.zeros((max(T, 1), 6), dtype=np.uint64)
-        rec[:T, 0] = sizes.astype(np.uint64)
-        rec[:T, 1] = np.uint64(master.data_ptr()) + (offsets * 4).astype(np.uint64)
-        rec[:T, 2] = np.uint64(m.data_ptr()) + (offsets * 4).astype(np.uint64)
-        rec[:T, 3] = np.uint64(v.data_ptr()) + (offsets * 4).astype(np.uint64)
-        rec[:T, 4] = np.uint64(param.data_ptr()) + (offsets * 2).astype(np.uint64)
-        rec[:T, 5] = np.uint64(gtab.ctypes.data) + np.arange(max(T, 1), dtype=np.uint64) * np.uint64(8 * N)
-        assert ctypes.sizeof(TensorStruct) == 48
+        rec, gtab = _arena_records(sizes, offsets, [g.data_ptr() for g in grads], master.data_ptr(), m.data_ptr(),
+                                   v.data_ptr(), param.data_ptr())
         self = cls.__new__(cls)
         h = _vp()
         with torch.cuda.device(dev):

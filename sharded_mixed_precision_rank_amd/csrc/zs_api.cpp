@@ -183,23 +183,66 @@ int auto_blocks() {
   return forced > 0 ? forced : 1 << 30;
 }
 
-// The flat step's schedule for N replicas on a shard of n parameters (and a
-// list plan's, for n parameters in all), and the write window it takes
-// (period_mask 0 unless windowed).  An explicit zs_set_flat_schedule wins;
-// otherwise an explicit zs_set_write_window decides (no windows: per-tile
-// stores; a window: the windowed kernel); otherwise the phased kernel for
-// N >= kPhasedMinReplicas (18) on shards of at least kPhasedMinParams, and
-// per-tile stores below.  The windowed kernel's default window is a
-// 4096-tick (41 us) period with 640 ticks open for N < 64, 512 up to 128 and
-// 384 above: the writes' share of the bytes shrinks as N grows.
-// List plans take the phased kernel from more replicas than flat shards: with
-// spans of consecutive items and the per-span descriptors, per-tile stores
-// measured faster at N = 18 (4.5-6%), the two drawn lists split at N = 24
-// (ragged +3.4% phased, llama7b -1.4%), and the phased kernel won at N = 32.
-constexpr int32_t kListPhasedMinReplicas = 32;
+// When the automatic schedule takes the phased kernel: for N replicas on n
+// parameters, when some rule {replicas, params} has N >= replicas and
+// n >= params.  The rules follow the crossings measured against per-tile
+// stores (one process per point, % of 8 TB/s by the byte model, phased /
+// per-tile):
+//  - the flat step: from 2^25 parameters at N >= 40 (N = 40: 73% / 70% at
+//    2^25; 48: 72% / 68%; 64: 74% / 70.5%), from 2^27 at N = 24-39 (N = 24:
+//    67% / 70% at 2^25, 72.5% / 71.6% at 2^27, 77.5% / 74% at 2^30; N = 32:
+//    70% / 71.6% at 2^25, 74% / 70% at 2^27).  Below 24 replicas it gains at
+//    most 1.4% on 2^29-2^30 parameters and loses on smaller shards (N = 18:
+//    67% / 72% at 2^25, 73% / 72% at 2^30; N = 8: 66% / 74% at 2^30);
+//  - list plans (spans of 10 consecutive items, per-span descriptors), on
+//    lists of large tensors (the llama7b shapes scaled to 2^25-2^29.6
+//    parameters, 1-4% of items outside whole spans): from 2^26 at N >= 64
+//    (74% / 70.6%; 71% / 71% at 2^25), from 2^27 at N = 40-63 (71% / 66.4%;
+//    69% / 69.3% at 2^26), from 2^28 at N = 32-39 (72% / 67.8%; 69.7% /
+//    69.6% at 2^27); per-tile stores won at N = 18 and 24 on 2^29.6.  Items
+//    outside whole spans go one at a time after the super-chunks: the ragged
+//    list of 20,000 tensors lost phased at every N from 32 to 64 when scaled
+//    to 2^25-2^27 parameters (33-76% of its items loose; 48-62% / 65-70%),
+//    lost at N = 32 and 40 on 2^28 (20% loose; 63% / 66-69%), and won at
+//    N = 24 and 32 on 2^31 (3.5% loose; 73.6% / 71.2%).  So lists take it
+//    from 1.5x the power of two where it first won (3 * 2^24 at N >= 64,
+//    3 * 2^25 at N >= 40, 3 * 2^26 at N >= 32: halfway to the tie below in
+//    log terms) with at most 1 item in 20 outside whole spans;
+//  - pass 1 of the two-pass form, whose write phase is its 4-byte means
+//    alone: phased wins or ties from N = 12 on 2^25 parameters and more
+//    (N = 12: 65.5% / 65.1% at 2^25, 74% / 71% at 2^27; N = 16: 66% / 66.6%
+//    at 2^25, 73.6% / 69.6% at 2^26, 77% / 72% at 2^30; N = 8: 74.7% / 75.4%
+//    at 2^30).
+struct PhasedRule {
+  int32_t replicas;
+  int64_t params;
+};
+constexpr PhasedRule kFlatPhased[] = {{40, (int64_t)1 << 25}, {24, (int64_t)1 << 27}};
+constexpr PhasedRule kListPhased[] = {{64, (int64_t)3 << 24}, {40, (int64_t)3 << 25}, {32, (int64_t)3 << 26}};
+// ... and list plans only when at most 1/20 of their items lie outside whole spans (kLooseShareMax)
+constexpr int64_t kLooseShareMax = 20;
+constexpr PhasedRule kReducePhased[] = {{12, (int64_t)1 << 25}};
 
-zs::FlatSchedule flat_schedule(int32_t N, int64_t n, zs::WriteWindow* win,
-                               int32_t min_replicas = zs::kPhasedMinReplicas) {
+template <size_t R>
+bool phased_by_rule(const PhasedRule (&rules)[R], int32_t N, int64_t n) {
+  for (const PhasedRule& r : rules)
+    if (N >= r.replicas && n >= r.params) return true;
+  return false;
+}
+
+// The flat step's schedule for N replicas on a shard of n parameters (and a
+// list plan's, for n parameters in all, with `list_items` >= 0: its items, of
+// which `loose_items` lie outside whole spans), and the write window it takes
+// (period_mask 0 unless windowed).  An explicit zs_set_flat_schedule
+// wins; otherwise an explicit zs_set_write_window decides (no windows:
+// per-tile stores; a window: the windowed kernel); otherwise the phased
+// kernel where its rules say (above), and per-tile stores elsewhere.  The
+// windowed kernel's default window is a 4096-tick (41 us) period with 640
+// ticks open for N < 64, 512 up to 128 and 384 above: the writes' share of
+// the bytes shrinks as N grows.
+zs::FlatSchedule flat_schedule(int32_t N, int64_t n, zs::WriteWindow* win, int64_t list_items = -1,
+                               int64_t loose_items = 0) {
+  const bool list = list_items >= 0;
   const int32_t forced = g_flat_schedule.load(std::memory_order_relaxed);
   const uint64_t word = g_window.load(std::memory_order_relaxed);
   const int32_t period = (int32_t)(word >> 32);
@@ -211,7 +254,10 @@ zs::FlatSchedule flat_schedule(int32_t N, int64_t n, zs::WriteWindow* win,
   else if (period > 1)
     sched = zs::FlatSchedule::kWindowed;
   else
-    sched = N >= min_replicas && n >= zs::kPhasedMinParams ? zs::FlatSchedule::kPhased : zs::FlatSchedule::kStream;
+    sched = (list ? phased_by_rule(kListPhased, N, n) && loose_items * kLooseShareMax <= list_items
+                  : phased_by_rule(kFlatPhased, N, n))
+                ? zs::FlatSchedule::kPhased
+                : zs::FlatSchedule::kStream;
   zs::WriteWindow w{0, 0};
   if (sched == zs::FlatSchedule::kWindowed) {
     // an explicit window, none when windows were switched off, else the default for N (any N)
@@ -233,9 +279,8 @@ zs::PhasedCtl phased_ctl() {
 
 // Pass 1 of the two-pass form (2N bytes read and 4 written per parameter)
 // follows the same setting: an explicit schedule, else an explicit window
-// (1: none, > 1: windowed), else phased for N >= kReducePhasedMinReplicas
-// (12) on shards of at least kPhasedMinParams, else one tile per workgroup.
-// Its windowed default is 4096 / 256.
+// (1: none, > 1: windowed), else phased where its rules say (above), else
+// one tile per workgroup.  Its windowed default is 4096 / 256.
 zs::FlatSchedule reduce_schedule(int32_t N, int64_t n, zs::WriteWindow* win) {
   const int32_t forced = g_flat_schedule.load(std::memory_order_relaxed);
   const uint64_t word = g_window.load(std::memory_order_relaxed);
@@ -248,8 +293,7 @@ zs::FlatSchedule reduce_schedule(int32_t N, int64_t n, zs::WriteWindow* win) {
   else if (period > 1)
     sched = zs::FlatSchedule::kWindowed;
   else
-    sched = N >= zs::kReducePhasedMinReplicas && n >= zs::kPhasedMinParams ? zs::FlatSchedule::kPhased
-                                                                            : zs::FlatSchedule::kStream;
+    sched = phased_by_rule(kReducePhased, N, n) ? zs::FlatSchedule::kPhased : zs::FlatSchedule::kStream;
   zs::WriteWindow w{0, 0};
   if (sched == zs::FlatSchedule::kWindowed) {
     if (period > 1)
@@ -453,6 +497,7 @@ struct ListTable {
   std::vector<unsigned char> bytes;
   size_t off_tensors = 0, off_gptrs = 0;
   int32_t n_items = 0;
+  int32_t loose_items = 0;  // items outside whole spans of the phased list kernel
   int64_t n_params = 0;
 };
 
@@ -478,6 +523,8 @@ zs_status build_list_table(const zs_tensor* tensors, int32_t T, int32_t N, ListT
   if (st) return st;
 
   constexpr int64_t kGroupsPerTile = zs::kTileElemsWave / 8;
+  constexpr int64_t K = zs::kListPhasedTiles;
+  int64_t whole = 0;  // items in whole spans: K consecutive items from a multiple of K, all whole tiles of one tensor
   std::vector<zs::ListTensor> ht;
   std::vector<int32_t> hi;
   std::vector<const uint16_t*> hg;
@@ -509,6 +556,11 @@ zs_status build_list_table(const zs_tensor* tensors, int32_t T, int32_t N, ListT
         d.head_lead |= (int32_t)lead << 8;
         const int64_t gofs = lead > 0 ? lead - kGroupsPerTile : 0;
         items = (s.nvec - gofs + kGroupsPerTile - 1) / kGroupsPerTile;
+        const int64_t i0 = (int64_t)hi.size();
+        for (int64_t j = (i0 + K - 1) / K; (j + 1) * K <= i0 + items; ++j) {
+          const int64_t g0 = gofs + (j * K - i0) * kGroupsPerTile;
+          if (g0 >= 0 && g0 + K * kGroupsPerTile <= s.nvec) whole += K;
+        }
       } else {
         items = (s.n + zs::kTileElemsWave - 1) / zs::kTileElemsWave;
       }
@@ -528,6 +580,7 @@ zs_status build_list_table(const zs_tensor* tensors, int32_t T, int32_t N, ListT
   out.off_tensors = bi;
   out.off_gptrs = bi + bt;
   out.n_items = (int32_t)hi.size();
+  out.loose_items = (int32_t)((int64_t)hi.size() - whole);
   out.n_params = total;
   return ZS_OK;
 }
@@ -539,6 +592,7 @@ struct zs_list_plan {
   int32_t N;
   int32_t T;
   int32_t n_items;
+  int32_t loose_items;  // items outside whole spans (the automatic schedule's list rule)
   int64_t n_params;
   int32_t n_groups;  // hyperparameter groups set by zs_list_plan_set_groups (1 until then)
   void* table;  // device: items | tensors | grad pointers
@@ -675,8 +729,8 @@ zs_status zs_write_window(int32_t kernel, int32_t N, int64_t n, int32_t* period_
   zs::WriteWindow w{};
   if (kernel == ZS_WINDOW_REDUCE_PASS)
     (void)reduce_schedule(N, n, &w);
-  else if (kernel == ZS_WINDOW_LIST_PLAN)  // a flat shard's schedule for the plan's size, with the list threshold
-    (void)flat_schedule(N, n, &w, kListPhasedMinReplicas);
+  else if (kernel == ZS_WINDOW_LIST_PLAN)  // a flat shard's schedule for the plan's size, by the list rules
+    (void)flat_schedule(N, n, &w, 0);
   else
     (void)flat_schedule(N, n, &w);
   const bool big = flat ? n / 8 / zs::kFlatBlock >= zs::kWindowMinTiles
@@ -726,18 +780,24 @@ zs_status zs_flat_schedule(int32_t N, int64_t n, int32_t* schedule) {
   return ZS_OK;
 }
 
-zs_status zs_list_schedule(int32_t N, int64_t n, int32_t* schedule) {
-  g_last_error.clear();
-  if (!schedule) return fail(ZS_ERR_NULL, "schedule is NULL");
-  if (N < 1 || N > ZS_MAX_REPLICAS) return fail(ZS_ERR_RANGE, "N must be in [1, %d] (got %d)", ZS_MAX_REPLICAS, N);
-  if (n < 0) return fail(ZS_ERR_RANGE, "n must be >= 0");
-  zs::WriteWindow w{};
-  zs::FlatSchedule sched = flat_schedule(N, n, &w, kListPhasedMinReplicas);
-  // the windowed list kernel's size condition
-  if (sched == zs::FlatSchedule::kWindowed && (w.period_mask == 0 || n / 8 / zs::kFlatBlock < zs::kWindowMinTiles))
-    sched = zs::FlatSchedule::kStream;
-  *schedule = (int32_t)sched;
-  return ZS_OK;
+zs_status zs_list_schedule(const zs_tensor* tensors, int32_t T, int32_t N, int32_t* schedule) {
+  try {
+    g_last_error.clear();
+    if (!schedule) return fail(ZS_ERR_NULL, "schedule is NULL");
+    ListTable tab;
+    zs_status st = build_list_table(tensors, T, N, tab);
+    if (st) return st;
+    zs::WriteWindow w{};
+    zs::FlatSchedule sched = flat_schedule(N, tab.n_params, &w, tab.n_items, tab.loose_items);
+    // the windowed list kernel's size condition
+    if (sched == zs::FlatSchedule::kWindowed &&
+        (w.period_mask == 0 || tab.n_params < ((int64_t)zs::kWindowMinTiles << 9)))
+      sched = zs::FlatSchedule::kStream;
+    *schedule = (int32_t)sched;
+    return ZS_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(ZS_ERR_NOMEM, "host allocation failed");
+  }
 }
 
 zs_status zs_set_phased_max_polls(int32_t polls) {
@@ -793,6 +853,7 @@ zs_status zs_list_plan_create(const zs_tensor* tensors, int32_t T, int32_t N, zs
     plan->N = N;
     plan->T = T;
     plan->n_items = tab.n_items;
+    plan->loose_items = tab.loose_items;
     plan->n_params = tab.n_params;
     plan->n_groups = 1;
     plan->table = nullptr;
@@ -841,14 +902,14 @@ zs_status plan_on_current_device(zs_list_plan_t plan) {
 }
 
 // The list step over a device table (a plan's, or the fixed array of zs_reduce_adam_list_static).
-zs_status launch_list_table(const int32_t* items, int32_t n_items, const zs::ListTensor* tensors,
-                            const uint16_t* const* gptrs, int32_t N, int64_t n_params, const zs::Scalars* cs,
-                            int32_t n_sets, const zs::StepRef& ref, zs_stream stream) {
+zs_status launch_list_table(const int32_t* items, int32_t n_items, int32_t loose_items,
+                            const zs::ListTensor* tensors, const uint16_t* const* gptrs, int32_t N, int64_t n_params,
+                            const zs::Scalars* cs, int32_t n_sets, const zs::StepRef& ref, zs_stream stream) {
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  // the flat step's schedule for a shard of the plan's size, phased from kListPhasedMinReplicas on; windows
-  // for plans of at least 2^25 parameters
+  // the flat step's schedule for a shard of the plan's size, by the list rules; windows for plans of at
+  // least 2^25 parameters
   zs::WriteWindow win{};
-  const zs::FlatSchedule sched = flat_schedule(N, n_params, &win, kListPhasedMinReplicas);
+  const zs::FlatSchedule sched = flat_schedule(N, n_params, &win, n_items, loose_items);
   if (n_params < ((int64_t)zs::kWindowMinTiles << 9)) win = zs::WriteWindow{0, 0};
   return after_launch(zs::launch_list(items, n_items, tensors, gptrs, cs, n_sets, ref, auto_blocks(), sched, win,
                                       phased_ctl(), hs),
@@ -877,8 +938,8 @@ zs_status run_plan(zs_list_plan_t plan, const zs_adam_hp* hps, int32_t n, int64_
   if (plan->n_items == 0) return ZS_OK;
   zs_status st = plan_on_current_device(plan);
   if (st) return st;
-  return launch_list_table(plan->items, plan->n_items, plan->tensors, plan->gptrs, plan->N, plan->n_params, cs, n,
-                           ref, stream);
+  return launch_list_table(plan->items, plan->n_items, plan->loose_items, plan->tensors, plan->gptrs, plan->N,
+                           plan->n_params, cs, n, ref, stream);
 }
 
 }  // namespace
@@ -1034,7 +1095,7 @@ zs_status zs_reduce_adam_list_static(const zs_tensor* tensors, int32_t T, int32_
     if (e != hipSuccess) return hip_fail(e, "table upload");
     unsigned char* b = static_cast<unsigned char*>(base);
     const zs::Scalars c = make_scalars(*hp, step, N);
-    st = launch_list_table(reinterpret_cast<const int32_t*>(b), tab.n_items,
+    st = launch_list_table(reinterpret_cast<const int32_t*>(b), tab.n_items, tab.loose_items,
                            reinterpret_cast<const zs::ListTensor*>(b + tab.off_tensors),
                            reinterpret_cast<const uint16_t* const*>(b + tab.off_gptrs), N, tab.n_params, &c, 1,
                            zs::StepRef{}, stream);

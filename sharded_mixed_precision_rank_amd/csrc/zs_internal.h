@@ -157,18 +157,10 @@ constexpr int kMaxDevices = 64;
 // flight 48 more), of pass 1 (10 in registers and 4 in LDS, 96 KB per
 // workgroup) and of a list plan (10: its per-wave descriptor takes registers
 // of its own), waves per workgroup (one workgroup
-// per compute unit at 3 waves per SIMD), barrier counter slots, the default
-// longest wait at one barrier (polls of about 50 ns: about 3 ms), and the
-// fewest parameters and replicas for which the automatic schedule takes it.
-// With 8 tiles per wave, measured on 2^28-2^30-parameter shards against
-// per-tile stores: 63% / 74% of 8 TB/s at N = 8, 70% / 74% at 16, 76% / 74% at
-// 32, 78% / 71% at 48, 82% / 74% at 64, 82% / 69% at 128, 83% / 71% at 256;
-// 12 tiles took another 1.3-1.5% at N = 48 and 64.  With 12 tiles, on 2^29-
-// 2^30-parameter shards: 66% / 74% at N = 8, 70% / 73% at 16, 73% / 72% at
-// 18, 77% / 76% at 20, 73% / 72% at 22, 77.5% / 74% at 24, 74% / 72% at 28,
-// 76% / 70.5% at 32.  Pass 1 of the two-pass form, whose write phase is its
-// 4-byte means alone, gains from fewer replicas: 75% / 75% at N = 8, 73.5% /
-// 71.5% at 12, 77% / 72% at 16, 77% / 71% at 18, 79% / 71% at 24.
+// per compute unit at 3 waves per SIMD), barrier counter slots and the
+// default longest wait at one barrier (polls of about 50 ns: about 3 ms).
+// When the automatic schedule takes the phased kernel is a host decision
+// (zs_api.cpp, with its measurements).
 constexpr int kPhasedTiles = 12;
 constexpr int kReduceRegTiles = 10;
 constexpr int kReduceLdsTiles = 4;
@@ -177,13 +169,10 @@ constexpr int kListPhasedTiles = 10;
 constexpr int kPhasedWaves = 12;
 constexpr int kPhasedSlots = 16;
 constexpr int32_t kPhasedMaxPolls = 1 << 16;
-constexpr int64_t kPhasedMinParams = (int64_t)1 << 25;
 // The share of the grid, in percent, whose arrival at a grid barrier releases it.  On the 70B/64 shard
 // the workgroups reach the barrier over about 26 us of a 297 us super-chunk; releasing at 92-96% was
 // 0.6-1% faster than waiting for all (releasing at 88% let stragglers fall a super-chunk behind).
 constexpr uint32_t kPhasedQuorumPct = 95;
-constexpr int32_t kPhasedMinReplicas = 18;
-constexpr int32_t kReducePhasedMinReplicas = 12;
 // Write-window bounds, in ticks of the 100 MHz device clock: the period a
 // power of two in [kWindowMinPeriod, kWindowMaxPeriod], the open part at most
 // kWindowMaxOpen; a wave's wait in a window is capped at kWindowMaxSleeps

@@ -224,15 +224,33 @@ int main(void) {
       fprintf(stderr, "default flat schedule for N = 64 on 2^30 parameters: %d\n", sched);
       bad = 1;
     }
-    CHECK_ZS(zs_list_schedule(24, (int64_t)1 << 30, &sched));
-    if (sched != ZS_SCHEDULE_STREAM) {
-      fprintf(stderr, "default list schedule for N = 24 on 2^30 parameters: %d\n", sched);
-      bad = 1;
-    }
-    CHECK_ZS(zs_list_schedule(32, (int64_t)1 << 30, &sched));
-    if (sched != ZS_SCHEDULE_PHASED) {
-      fprintf(stderr, "default list schedule for N = 32 on 2^30 parameters: %d\n", sched);
-      bad = 1;
+    {
+      /* 64 tensors of 2^24 parameters in arenas on 2 MiB boundaries: addresses that only stand for their
+         alignment (the query reads none of them) */
+      enum { LT = 64, LN = 32 };
+      const uintptr_t base = (uintptr_t)1 << 40, span = (uintptr_t)1 << 32;
+      static const uint16_t* lg[LT][LN];
+      static zs_tensor lt[LT];
+      for (int t = 0; t < LT; ++t) {
+        const uintptr_t o = (uintptr_t)t << 24;
+        for (int r = 0; r < LN; ++r) lg[t][r] = (const uint16_t*)(base + (4 + (uintptr_t)r) * span + 2 * o);
+        lt[t].n = (int64_t)1 << 24;
+        lt[t].master = (float*)(base + 4 * o);
+        lt[t].m = (float*)(base + span + 4 * o);
+        lt[t].v = (float*)(base + 2 * span + 4 * o);
+        lt[t].param_bf16 = (uint16_t*)(base + 3 * span + 2 * o);
+        lt[t].grad_chunks = lg[t];
+      }
+      CHECK_ZS(zs_list_schedule(lt, LT, 24, &sched));
+      if (sched != ZS_SCHEDULE_STREAM) {
+        fprintf(stderr, "default list schedule for N = 24 on 2^30 parameters: %d\n", sched);
+        bad = 1;
+      }
+      CHECK_ZS(zs_list_schedule(lt, LT, 32, &sched));
+      if (sched != ZS_SCHEDULE_PHASED) {
+        fprintf(stderr, "default list schedule for N = 32 on 2^30 parameters: %d\n", sched);
+        bad = 1;
+      }
     }
     CHECK_ZS(zs_set_flat_schedule(ZS_SCHEDULE_WINDOWED));
     CHECK_ZS(zs_write_window(ZS_WINDOW_FLAT_STEP, 64, (int64_t)1 << 30, &per, &open));

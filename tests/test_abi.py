@@ -498,38 +498,67 @@ def test_reduce_schedule_query():
 
 
 def test_list_schedule_query():
-    """List plans: the flat step's rule, the automatic schedule phased from N = 32 (not 18) on plans of at
-    least 2^25 parameters; an explicit schedule or window wins as for flat shards."""
-    assert zs.list_schedule(64, 1_069_568_000) == "phased"
-    assert zs.list_schedule(32, 1 << 25) == "phased"
-    assert zs.list_schedule(31, 1 << 30) == "stream"
-    assert zs.list_schedule(24, 1 << 30) == "stream"
-    assert zs.list_schedule(16, 2_154_298_847) == "stream"
-    assert zs.list_schedule(64, (1 << 25) - 1) == "stream"
-    assert zs.flat_schedule(24, 1 << 30) == "phased"   # the flat step takes it from 18
+    """List plans: phased for N >= 64 from 3 * 2^24 parameters in all, N >= 40 from 3 * 2^25 and N >= 32
+    from 3 * 2^26, when at most 1 in 20 wave tiles lies outside whole spans; an explicit schedule or window
+    wins as for flat shards."""
+    big = [1 << 22] * 64                                    # 2^28 in tensors of 8,192 tiles
+    assert zs.list_schedule(big, 32) == "phased"
+    assert zs.list_schedule(big, 31) == "stream"
+    assert zs.list_schedule(big[:32], 40) == "phased"       # 2^27
+    assert zs.list_schedule(big[:32], 39) == "stream"
+    assert zs.list_schedule(big[:32], 32) == "stream"
+    assert zs.list_schedule(big[:16], 64) == "phased"       # 2^26
+    assert zs.list_schedule(big[:16], 63) == "stream"
+    assert zs.list_schedule(big[:8], 64) == "stream"        # 2^25
+    three = [3 << 21] * 64                                  # 3 * 2^27, in tensors of 12,288 tiles
+    assert zs.list_schedule(three[:8], 64) == "phased"      # 3 * 2^24
+    assert zs.list_schedule(three[:7] + [(3 << 21) - 8], 64) == "stream"
+    assert zs.list_schedule(three[:16], 40) == "phased"     # 3 * 2^25
+    assert zs.list_schedule(three[:15] + [(3 << 21) - 8], 40) == "stream"
+    assert zs.list_schedule(three[:32], 32) == "phased"     # 3 * 2^26
+    assert zs.list_schedule(three[:31] + [(3 << 21) - 8], 32) == "stream"
+    assert zs.list_schedule(big[:16], 24) == "stream"
+    assert zs.list_schedule(big * 4, 24) == "stream"        # 2^30 at N = 24: per-tile stores on lists
+    assert zs.flat_schedule(24, 1 << 30) == "phased"        # the flat step takes it from 24 on 2^27 and more
+    # 20,000 tensors of 32 tiles: spans of 10 tiles from a multiple of 10 leave 2-12 of each tensor's 32
+    # tiles outside whole spans, far above 1 in 20
+    small = [1 << 14] * 20000
+    assert sum(small) > 1 << 28
+    assert zs.list_schedule(small, 64) == "stream"
+    # 2,000 tensors of 320 tiles, each starting on a multiple of 10 tiles: every tile in a whole span
+    assert zs.list_schedule([320 * 512] * 2000, 64) == "phased"
+    # the same with a 1-element tensor before each: the large tensors move off the tile grid (a partial
+    # first and last tile, 321 in all) and 31 whole spans fit in each, so 11 of its tiles and the scalar
+    # tensor's one are loose: 12 in 322, under 1 in 20
+    mixed = [x for _ in range(2000) for x in (1, 320 * 512)]
+    assert zs.list_schedule(mixed, 64) == "phased"
     try:
         zs.set_flat_schedule("phased")
-        assert zs.list_schedule(8, 1 << 20) == "phased"
+        assert zs.list_schedule(small, 8) == "phased"
         zs.set_flat_schedule("auto")
         zs.set_write_window(2048, 256)
-        assert zs.list_schedule(8, 1 << 30) == "windowed"
-        assert zs.list_schedule(8, 1 << 20) == "stream"   # below the windowed kernel's size
+        assert zs.list_schedule(big, 8) == "windowed"
+        assert zs.list_schedule([1 << 20], 8) == "stream"   # below the windowed kernel's size
     finally:
         zs.set_flat_schedule("auto")
         zs.set_write_window(0)
     with pytest.raises(zs.ZShardError):
-        zs.list_schedule(0, 1 << 20)
+        zs.list_schedule(big, 0)
     with pytest.raises(zs.ZShardError):
-        zs.list_schedule(8, -1)
+        zs.list_schedule([-1], 8)
 
 
 def test_flat_schedule_query_and_setting():
-    """The automatic schedule: phased for N >= 18 on shards of at least 2^25 parameters, per-tile stores
-    otherwise; an explicit schedule wins (each kernel's own size conditions aside)."""
+    """The automatic schedule: phased for N >= 40 on shards of at least 2^25 parameters and for N >= 24
+    on at least 2^27, per-tile stores otherwise; an explicit schedule wins (each kernel's own size
+    conditions aside)."""
     assert zs.flat_schedule(64, 1_093_750_000) == "phased"
-    assert zs.flat_schedule(18, 1 << 25) == "phased"
+    assert zs.flat_schedule(40, 1 << 25) == "phased"
+    assert zs.flat_schedule(39, 1 << 25) == "stream"
+    assert zs.flat_schedule(24, 1 << 27) == "phased"
+    assert zs.flat_schedule(24, (1 << 27) - 1) == "stream"
     assert zs.flat_schedule(256, 1 << 30) == "phased"
-    assert zs.flat_schedule(17, 1 << 30) == "stream"
+    assert zs.flat_schedule(23, 1 << 30) == "stream"
     assert zs.flat_schedule(16, 1 << 30) == "stream"
     assert zs.flat_schedule(8, 124_000_000) == "stream"
     assert zs.flat_schedule(64, (1 << 25) - 1) == "stream"
