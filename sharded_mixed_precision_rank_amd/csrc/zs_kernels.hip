@@ -686,7 +686,25 @@ __global__ __launch_bounds__(kFlatBlock* kPhasedWaves) void list_phased_kernel(
 #pragma unroll
     for (int k = 0; k < K; ++k) es[k] = s.head + 8 * (o.g0 + k * kGroups);
     const uint16_t* const* gpt = gptrs + (int64_t)o.t * N;
-    auto gp = [&](int r) { return uniform_ptr(gpt[r]); };
+    // up to 64 replicas: lane r holds replica r's pointer, one vector load per span, and each replica
+    // step takes its pointer by v_readlane instead of a scalar load that its gradient loads wait on
+    // (0.2-0.4% faster on the llama70b/64 list)
+    uint32_t plo = 0u, phi = 0u;
+    if constexpr (NT > 0 && NT <= 64) {
+      if ((int)lane < N) {
+        const uint64_t u = reinterpret_cast<uint64_t>(gpt[lane]);
+        plo = (uint32_t)u;
+        phi = (uint32_t)(u >> 32);
+      }
+    }
+    auto gp = [&](int r) {
+      if constexpr (NT > 0 && NT <= 64) {
+        const uint32_t lo = __builtin_amdgcn_readlane(plo, r), hi = __builtin_amdgcn_readlane(phi, r);
+        return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+      } else {
+        return uniform_ptr(gpt[r]);
+      }
+    };
     float acc[K][8];
     phased_accumulate<NT, kBF16, K, 0>(gp, N, es, e, acc, nullptr, o.whole);
     f32x4 st[2][6];
