@@ -626,9 +626,9 @@ __global__ __launch_bounds__(kFlatBlock) void list_window_kernel(const int32_t* 
 // not the flat step's 12).  When they are whole tiles of one tensor (all but
 // a few waves in a list of large tensors), the wave streams their replicas
 // into its accumulators in phase A (the flat step's own code; the tensor's
-// replica pointers come from the plan's table, one scalar load per replica)
-// and
-// updates them in phase B after the grid barrier.  Otherwise the wave reads
+// replica pointers come from the plan's table, one per lane for up to 64
+// replicas, else one scalar load per replica) and updates them in phase B
+// after the grid barrier.  Otherwise the wave reads
 // nothing in phase A, meets the same barriers, and takes its items one at a
 // time in phase B.  Items after the last whole super-chunk go one per wave.
 // Every element goes through the same operations as in list_kernel.
