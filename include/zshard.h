@@ -418,12 +418,14 @@ ZS_API zs_status zs_set_grid_blocks(int32_t blocks);
    one tile.  On this memory system one long launch lost up to 13% against
    the same work cut into launches of 1.3-5 GB.  The windowed kernels are
    persistent and always one launch.  Results do not depend on the setting.
-     bytes = 0: the default, 3e9;
+     bytes = 0: the defaults: 3e9, and 1e9 for pass 2 of the two-pass form
+                (zs_adam_from_grads_flat and its device-step form), which ran
+                2.5% faster at 0.75-1 GB than at 3 GB;
      bytes > 0: that limit (a value below one tile's bytes gives one tile per
                 launch; INT64_MAX gives one launch per call).
    Errors: ZS_ERR_RANGE (bytes < 0). */
 ZS_API zs_status zs_set_launch_bytes(int64_t bytes);
-/* The limit in force (the default when none was set). */
+/* The limit in force (3e9 when none was set; pass 2 then takes 1e9). */
 ZS_API int64_t zs_launch_bytes(void);
 
 /* Write windows of the flat step (zs_reduce_adam_flat and its device-step

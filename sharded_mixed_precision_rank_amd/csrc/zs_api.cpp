@@ -342,9 +342,9 @@ zs_status step_ref_of(const zs_step_source* src, std::vector<Range>& rs, zs::Ste
 
 namespace zs {
 
-int64_t launch_bytes() {
+int64_t launch_bytes(int64_t fallback) {
   const int64_t b = g_launch_bytes.load(std::memory_order_relaxed);
-  return b > 0 ? b : kLaunchBytes;
+  return b > 0 ? b : fallback;
 }
 
 // Tiles that start on a cache-line boundary in every array keep every wave

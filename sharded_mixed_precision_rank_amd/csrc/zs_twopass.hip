@@ -590,8 +590,9 @@ hipError_t launch_gbar(const float* gbar, const FlatShape& s, const Scalars& c, 
   constexpr int64_t kT = 8 * BLK;
   const int64_t ntiles = s.scalar_only ? (s.n + kT - 1) / kT : (s.nvec + BLK - 1) / BLK;
   // consecutive launches of at most launch_bytes() each (30 bytes per
-  // parameter); the first also takes the head and tail elements
-  const int64_t per = units_per_launch(30 * kT, 1);
+  // parameter; 1 GB unless set, kPass2LaunchBytes); the first also takes the
+  // head and tail elements
+  const int64_t per = units_per_launch(30 * kT, 1, kPass2LaunchBytes);
   int64_t lo = 0;
   do {
     const int64_t hi = ntiles - lo > per ? lo + per : ntiles;
